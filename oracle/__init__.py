@@ -1,0 +1,6 @@
+"""Float64 CPU reference of the CARVE key-axis gated delta rule.
+
+Test infrastructure only: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library's product path.
+"""
+from .carve_oracle import forward, backward  # noqa: F401

@@ -1,0 +1,393 @@
+"""Pins for the float64 reference (CPU only).
+
+Each test checks the reference against something other than its own loop:
+hand-worked values, closed forms of special cases, exact identities of the
+recurrence, or finite differences.  The pins are chosen so that a plausible
+slip (decay applied after the write instead of before, pre-update readout,
+decay on the value axis instead of the key axis, a transposed product, an
+off-by-one chunk mean, a dropped gradient term) fails at least one of them.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import forward, backward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(rng, B=1, H=2, T=12, Dk=5, Dv=4, unit_keys=True, with_b=True):
+    q = rng.standard_normal((B, H, T, Dk))
+    k = rng.standard_normal((B, H, T, Dk))
+    if unit_keys:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, H, T, Dv))
+    log_g = rng.uniform(np.log(0.5), 0.0, (B, H, T, Dk))
+    b = rng.uniform(0.3, 1.0, (B, H, T, Dk)) if with_b else None
+    w = rng.uniform(0.05, 0.95, (B, H, T))
+    S0 = rng.standard_normal((B, H, Dv, Dk))
+    return dict(q=q, k=k, v=v, log_g=log_g, b=b, w=w, S0=S0)
+
+
+# ---------------------------------------------------------------- forward pins
+
+def test_golden_two_tokens():
+    """Hand-worked two-token example (fixture cites the update and readout legends)."""
+    with open(os.path.join(GOLDEN, "worked_two_tokens.json")) as f:
+        g = json.load(f)
+    inp = g["inputs"]
+    k = np.array(inp["k"], float)[None, None]
+    v = np.array(inp["v"], float)[None, None]
+    q = np.array(inp["q"], float)[None, None]
+    log_g = np.log(np.array(inp["a"], float))[None, None]
+    w = np.array(inp["w"], float)[None, None]
+    S0 = np.array(inp["S0"], float)[None, None]
+    o, S_T, _ = forward(q, k, v, log_g, w, S0=S0)
+    np.testing.assert_allclose(o[0, 0], np.array(g["expected"]["o"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S_T[0, 0], np.array(g["expected"]["S_T"]), rtol=0, atol=1e-14)
+
+
+def test_readout_is_post_update():
+    """T=1 from a zero state: o_0 = w_0 v_0 (k_0 . q_0); a pre-update readout would give 0."""
+    rng = np.random.default_rng(1)
+    c = rand_case(rng, T=1)
+    o, _, _ = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"])
+    kq = np.einsum("bhtk,bhtk->bht", c["k"], c["q"])
+    np.testing.assert_allclose(o, c["w"][..., None] * c["v"] * kq[..., None], rtol=1e-13, atol=1e-15)
+
+
+def test_unrolled_product():
+    """S_T = S0 M_1...M_T + sum_t w_t v_t k_t^T M_{t+1}...M_T with M_t = Diag(a_t)(I - w_t k_t k_t^T),
+    and o_t = S_t q_t, computed with explicit d_k x d_k matrix products."""
+    rng = np.random.default_rng(2)
+    c = rand_case(rng, B=2, H=2, T=9, Dk=5, Dv=3)
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"], S0=c["S0"])
+    B, H, T, Dk = c["k"].shape
+    for bi in range(B):
+        for hi in range(H):
+            a = np.exp(c["log_g"][bi, hi]) * c["b"][bi, hi]
+            M = [np.diag(a[t]) @ (np.eye(Dk) - c["w"][bi, hi, t] * np.outer(c["k"][bi, hi, t], c["k"][bi, hi, t]))
+                 for t in range(T)]
+            for t_end in range(1, T + 1):
+                prod = np.eye(Dk)
+                for t in range(t_end):
+                    prod = prod @ M[t]
+                S = c["S0"][bi, hi] @ prod
+                for t in range(t_end):
+                    tail = np.eye(Dk)
+                    for s in range(t + 1, t_end):
+                        tail = tail @ M[s]
+                    S = S + c["w"][bi, hi, t] * np.outer(c["v"][bi, hi, t], c["k"][bi, hi, t]) @ tail
+                np.testing.assert_allclose(o[bi, hi, t_end - 1], S @ c["q"][bi, hi, t_end - 1], rtol=1e-11, atol=1e-12)
+            np.testing.assert_allclose(S_T[bi, hi], S, rtol=1e-11, atol=1e-12)
+
+
+def test_one_hot_keys_decouple_columns():
+    """k_t = e_{i_t}: column j != i_t only decays (col_j <- a_j col_j); column i_t becomes
+    (1 - w) a_i col_i + w v_t.  Decay on the value axis or a transposed state fails this."""
+    rng = np.random.default_rng(3)
+    B, H, T, Dk, Dv = 1, 3, 20, 4, 3
+    idx = rng.integers(0, Dk, (B, H, T))
+    k = np.zeros((B, H, T, Dk))
+    np.put_along_axis(k, idx[..., None], 1.0, axis=-1)
+    q = rng.standard_normal((B, H, T, Dk))
+    v = rng.standard_normal((B, H, T, Dv))
+    log_g = rng.uniform(-0.7, 0.0, (B, H, T, Dk))
+    b = rng.uniform(0.2, 1.0, (B, H, T, Dk))
+    w = rng.uniform(0, 1, (B, H, T))
+    S0 = rng.standard_normal((B, H, Dv, Dk))
+    o, S_T, _ = forward(q, k, v, log_g, w, b=b, S0=S0)
+    for h in range(H):
+        cols = S0[0, h].copy()  # [Dv, Dk]
+        for t in range(T):
+            a = np.exp(log_g[0, h, t]) * b[0, h, t]
+            i = idx[0, h, t]
+            new = cols * a[None, :]
+            new[:, i] = (1 - w[0, h, t]) * a[i] * cols[:, i] + w[0, h, t] * v[0, h, t]
+            cols = new
+            np.testing.assert_allclose(o[0, h, t], cols @ q[0, h, t], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(S_T[0, h], cols, rtol=1e-12, atol=1e-13)
+
+
+def test_orthonormal_keys_no_decay_is_linear_attention():
+    """a = 1 and orthonormal keys: S_T = S0 (I - sum w_t k_t k_t^T) + sum w_t v_t k_t^T;
+    with S0 = 0 and w = 1 the outputs are causal linear attention o_t = sum_{s<=t} v_s (k_s . q_t)."""
+    rng = np.random.default_rng(4)
+    B, H, T, D = 1, 2, 6, 8
+    Qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    k = np.broadcast_to(Qm[:T][None, None], (B, H, T, D)).copy()
+    q = rng.standard_normal((B, H, T, D))
+    v = rng.standard_normal((B, H, T, D))
+    zero = np.zeros((B, H, T, D))
+    w = rng.uniform(0.1, 0.9, (B, H, T))
+    S0 = rng.standard_normal((B, H, D, D))
+    _, S_T, _ = forward(q, k, v, zero, w, S0=S0)
+    for h in range(H):
+        proj = sum(w[0, h, t] * np.outer(k[0, h, t], k[0, h, t]) for t in range(T))
+        write = sum(w[0, h, t] * np.outer(v[0, h, t], k[0, h, t]) for t in range(T))
+        np.testing.assert_allclose(S_T[0, h], S0[0, h] @ (np.eye(D) - proj) + write, rtol=1e-12, atol=1e-12)
+    o, _, _ = forward(q, k, v, zero, np.ones((B, H, T)))
+    scores = np.einsum("bhsk,bhtk->bhts", k, q)
+    causal = np.tril(np.ones((T, T)))
+    np.testing.assert_allclose(o, np.einsum("bhts,bhsv->bhtv", scores * causal, v), rtol=1e-12, atol=1e-12)
+
+
+def test_no_write_is_pure_key_axis_decay():
+    """w = 0: S_t = S0 Diag(prod_{s<=t} a_s) (inclusive product), o_t = S_t q_t."""
+    rng = np.random.default_rng(5)
+    c = rand_case(rng, B=2, H=1, T=10)
+    w0 = np.zeros_like(c["w"])
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], c["log_g"], w0, b=c["b"], S0=c["S0"])
+    cum = np.cumprod(np.exp(c["log_g"]) * c["b"], axis=2)  # [B,H,T,Dk]
+    St = c["S0"][:, :, None] * cum[:, :, :, None, :]        # [B,H,T,Dv,Dk]
+    np.testing.assert_allclose(o, np.einsum("bhtvk,bhtk->bhtv", St, c["q"]), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S_T, St[:, :, -1], rtol=1e-12, atol=1e-14)
+
+
+def test_delta_rule_retrieval_identity():
+    """After each update S_t k_t = (1 - w_t|k_t|^2) P_t k_t + w_t |k_t|^2 v_t with P_t = S_{t-1}Diag(a_t);
+    with w = 1 and unit keys the state maps k_t exactly to v_t (the delta rule's defining property)."""
+    rng = np.random.default_rng(6)
+    c = rand_case(rng, B=1, H=2, T=15, unit_keys=False)
+    _, _, _, states = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"], S0=c["S0"], return_states=True)
+    a = np.exp(c["log_g"]) * c["b"]
+    for t in range(c["k"].shape[2]):
+        kt = c["k"][:, :, t]
+        P = states[t] * a[:, :, t][:, :, None, :]
+        nk = np.sum(kt * kt, axis=-1)
+        lhs = np.einsum("bhvk,bhk->bhv", states[t + 1], kt)
+        Pk = np.einsum("bhvk,bhk->bhv", P, kt)
+        wt = c["w"][:, :, t]
+        rhs = (1 - wt * nk)[..., None] * Pk + (wt * nk)[..., None] * c["v"][:, :, t]
+        np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+    c2 = rand_case(rng, B=1, H=2, T=15, unit_keys=True)
+    _, _, _, states = forward(c2["q"], c2["k"], c2["v"], c2["log_g"], np.ones_like(c2["w"]), b=c2["b"],
+                              S0=c2["S0"], return_states=True)
+    for t in range(15):
+        np.testing.assert_allclose(np.einsum("bhvk,bhk->bhv", states[t + 1], c2["k"][:, :, t]), c2["v"][:, :, t],
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_scalar_decay_reduces_to_rescaled_delta_rule():
+    """b = 1 and a_t = alpha_t 1 (one decay per head): with S0 = 0 the decayed run equals
+    (prod_{s<=t} alpha_s) times an undecayed delta-rule run on values v_t / prod_{s<=t} alpha_s."""
+    rng = np.random.default_rng(7)
+    c = rand_case(rng, B=1, H=2, T=14, with_b=False)
+    alpha = rng.uniform(0.6, 1.0, (1, 2, 14))
+    log_g = np.broadcast_to(np.log(alpha)[..., None], c["k"].shape).copy()
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], log_g, c["w"])
+    cum = np.cumprod(alpha, axis=-1)
+    o_hat, S_hat, _ = forward(c["q"], c["k"], c["v"] / cum[..., None], np.zeros_like(log_g), c["w"])
+    np.testing.assert_allclose(o, cum[..., None] * o_hat, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(S_T, cum[..., -1][..., None, None] * S_hat, rtol=1e-11, atol=1e-13)
+
+
+def test_frobenius_bound():
+    """|S_t|_F <= max_i a_{t,i} |S_{t-1}|_F + w_t |v_t| |k_t| whenever w_t |k_t|^2 <= 2 (stability)."""
+    rng = np.random.default_rng(8)
+    c = rand_case(rng, B=2, H=2, T=64, Dk=16, Dv=16, unit_keys=False)
+    c["k"] /= np.linalg.norm(c["k"], axis=-1, keepdims=True)
+    c["k"] *= rng.uniform(0.5, 1.4, c["k"].shape[:-1])[..., None]  # w |k|^2 <= 0.95 * 1.96 < 2
+    _, _, _, states = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"], S0=c["S0"], return_states=True)
+    a = np.exp(c["log_g"]) * c["b"]
+    for t in range(64):
+        assert np.all(c["w"][:, :, t] * np.sum(c["k"][:, :, t] ** 2, -1) <= 2)
+        lhs = np.linalg.norm(states[t + 1], axis=(-2, -1))
+        rhs = (a[:, :, t].max(-1) * np.linalg.norm(states[t], axis=(-2, -1))
+               + c["w"][:, :, t] * np.linalg.norm(c["v"][:, :, t], axis=-1) * np.linalg.norm(c["k"][:, :, t], axis=-1))
+        assert np.all(lhs <= rhs * (1 + 1e-12))
+
+
+def test_linear_in_values_and_initial_state():
+    """o and S_T are jointly linear in (v, S0)."""
+    rng = np.random.default_rng(9)
+    c1 = rand_case(rng, T=11)
+    v2 = rng.standard_normal(c1["v"].shape)
+    S02 = rng.standard_normal(c1["S0"].shape)
+    args = (c1["q"], c1["k"])
+    o1, s1, _ = forward(*args, c1["v"], c1["log_g"], c1["w"], b=c1["b"], S0=c1["S0"])
+    o2, s2, _ = forward(*args, v2, c1["log_g"], c1["w"], b=c1["b"], S0=S02)
+    o3, s3, _ = forward(*args, 2 * c1["v"] - 3 * v2, c1["log_g"], c1["w"], b=c1["b"], S0=2 * c1["S0"] - 3 * S02)
+    np.testing.assert_allclose(o3, 2 * o1 - 3 * o2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s3, 2 * s1 - 3 * s2, rtol=1e-11, atol=1e-12)
+
+
+def test_causality_and_state_carry():
+    rng = np.random.default_rng(10)
+    c = rand_case(rng, B=1, H=2, T=20)
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"], S0=c["S0"])
+    c2 = {k_: (None if x is None else x.copy()) for k_, x in c.items()}
+    for key in ("q", "k", "v", "log_g", "b"):
+        c2[key][:, :, 13:] = rng.standard_normal(c2[key][:, :, 13:].shape) * 0.1 + (1 if key == "b" else 0)
+    c2["w"][:, :, 13:] = 0.3
+    o2, _, _ = forward(c2["q"], c2["k"], c2["v"], c2["log_g"], c2["w"], b=c2["b"], S0=c2["S0"])
+    assert np.array_equal(o[:, :, :13], o2[:, :, :13])
+    sl = lambda x, a_, b_: x[:, :, a_:b_]
+    oa, Sa, _ = forward(*(sl(c[n], 0, 7) for n in ("q", "k", "v", "log_g", "w")), b=sl(c["b"], 0, 7), S0=c["S0"])
+    ob, Sb, _ = forward(*(sl(c[n], 7, 20) for n in ("q", "k", "v", "log_g", "w")), b=sl(c["b"], 7, 20), S0=Sa)
+    np.testing.assert_allclose(np.concatenate([oa, ob], axis=2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sb, S_T, rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------------ content-path pins
+
+def content_case(rng, B=1, H=2, T=12, D=3, R=2):
+    c = rand_case(rng, B=B, H=H, T=T, Dk=D, Dv=D, with_b=False)
+    c["b_x"] = rng.normal(1.0, 1.0, (B, H, T, D))
+    c["U1"] = rng.normal(0, 0.5, (H, R, D))
+    c["U2"] = rng.normal(0, 0.5, (H, D, R))
+    return c
+
+
+def _sig(x):
+    return 1 / (1 + np.exp(-x))
+
+
+def test_content_zero_projection_is_token_only():
+    """U_b = 0 gives b = sigmoid(b_x) everywhere: bit-identical to U_b absent, and equal to the
+    token-only path fed b = sigmoid(b_x) (zero-initialised projection reproduces the baseline)."""
+    rng = np.random.default_rng(11)
+    c = content_case(rng, T=12)
+    base = (c["q"], c["k"], c["v"], c["log_g"], c["w"])
+    zero = dict(b_x=c["b_x"], U1=np.zeros_like(c["U1"]), U2=np.zeros_like(c["U2"]))
+    absent = dict(b_x=c["b_x"], U1=None, U2=None)
+    oz, sz, mz = forward(*base, S0=c["S0"], L=4, content=zero)
+    oa, sa, ma = forward(*base, S0=c["S0"], L=4, content=absent)
+    assert np.array_equal(oz, oa) and np.array_equal(sz, sa) and np.array_equal(mz, ma)
+    ot, st, _ = forward(*base, b=_sig(c["b_x"]), S0=c["S0"])
+    assert np.array_equal(oz, ot) and np.array_equal(sz, st)
+
+
+def test_content_chunk_composition():
+    """Two chunks of L=3: chunk 0 is the token-only run with b = sigmoid(b_x); chunk 1 is the token-only
+    run from the carried state with b = sigmoid(b_x + U2 U1 m_0), m_0 the mean of chunk 0's outputs;
+    m_out is the mean of chunk 1's outputs.  An off-by-one in the averaged window or in the chunk that
+    receives the signal fails this."""
+    rng = np.random.default_rng(12)
+    L = 3
+    c = content_case(rng, T=2 * L)
+    cont = dict(b_x=c["b_x"], U1=c["U1"], U2=c["U2"])
+    o, S_T, m_out = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], S0=c["S0"], L=L, content=cont)
+    s0 = lambda x: x[:, :, :L]
+    s1 = lambda x: x[:, :, L:]
+    names = ("q", "k", "v", "log_g", "w")
+    o0, S1, _ = forward(*(s0(c[n]) for n in names), b=_sig(s0(c["b_x"])), S0=c["S0"])
+    m0 = o0.mean(axis=2)                                          # [B,H,Dv]
+    z = np.einsum("hkr,hrv,bhv->bhk", c["U2"], c["U1"], m0)
+    o1, S2, _ = forward(*(s1(c[n]) for n in names), b=_sig(s1(c["b_x"]) + z[:, :, None, :]), S0=S1)
+    np.testing.assert_allclose(o, np.concatenate([o0, o1], axis=2), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(S_T, S2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(m_out, o1.mean(axis=2), rtol=1e-13, atol=1e-14)
+
+
+def test_content_first_chunk_has_no_signal_and_carry():
+    rng = np.random.default_rng(13)
+    L = 4
+    c = content_case(rng, T=3 * L)
+    names = ("q", "k", "v", "log_g", "w")
+    cont = dict(b_x=c["b_x"], U1=c["U1"], U2=c["U2"])
+    o, S_T, m_out = forward(*(c[n] for n in names), S0=c["S0"], L=L, content=cont)
+    cont2 = dict(cont, U1=3 * c["U1"] + 1.0, U2=c["U2"] - 0.5)
+    o2, _, _ = forward(*(c[n] for n in names), S0=c["S0"], L=L, content=cont2)
+    assert np.array_equal(o[:, :, :L], o2[:, :, :L])
+    assert not np.allclose(o[:, :, L:], o2[:, :, L:])
+    # split at a chunk boundary, carrying both S and m
+    cut = 2 * L
+    sl = lambda x, a_, b_: x[:, :, a_:b_]
+    oa, Sa, ma = forward(*(sl(c[n], 0, cut) for n in names), S0=c["S0"], L=L,
+                         content=dict(cont, b_x=sl(c["b_x"], 0, cut)))
+    ob, Sb, mb = forward(*(sl(c[n], cut, 3 * L) for n in names), S0=Sa, L=L,
+                         content=dict(cont, b_x=sl(c["b_x"], cut, 3 * L), m0=ma))
+    np.testing.assert_allclose(np.concatenate([oa, ob], 2), o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sb, S_T, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(mb, m_out, rtol=1e-13, atol=1e-14)
+
+
+def test_content_ragged_tail_mean():
+    """A final partial chunk averages over the tokens it holds."""
+    rng = np.random.default_rng(14)
+    L = 4
+    c = content_case(rng, T=10)
+    names = ("q", "k", "v", "log_g", "w")
+    o, _, m_out = forward(*(c[n] for n in names), S0=c["S0"], L=L, content=dict(b_x=c["b_x"], U1=c["U1"], U2=c["U2"]))
+    np.testing.assert_allclose(m_out, o[:, :, 8:10].mean(axis=2), rtol=1e-13, atol=1e-14)
+
+
+# ----------------------------------------------------------------- backward pins
+
+def _loss(c, dO, dS_T, b_key="b"):
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c.get(b_key), S0=c["S0"])
+    return np.sum(o * dO) + np.sum(S_T * dS_T)
+
+
+@pytest.mark.parametrize("seed", [20, 21])
+def test_backward_matches_finite_differences(seed):
+    rng = np.random.default_rng(seed)
+    c = rand_case(rng, B=1, H=2, T=7, Dk=3, Dv=2, unit_keys=False)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+    g = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], dS_T=dS_T, segment=3)
+    eps = 1e-6
+    for name, gname in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_g", "dlog_g"), ("b", "db"),
+                        ("w", "dw"), ("S0", "dS0")]:
+        x = c[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = _loss(c, dO, dS_T)
+            x[i] = old - eps
+            lm = _loss(c, dO, dS_T)
+            x[i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+def test_backward_directional_derivative_larger():
+    """Directional finite differences at T=64, d=16 (several random directions)."""
+    rng = np.random.default_rng(22)
+    c = rand_case(rng, B=1, H=2, T=64, Dk=16, Dv=16)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+    g = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], dS_T=dS_T, segment=16)
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_g", "dlog_g"), ("b", "db"), ("w", "dw"), ("S0", "dS0")]
+    for trial in range(6):
+        dirs = {n: rng.standard_normal(c[n].shape) for n, _ in names}
+        eps = 1e-5
+        cp = {n: (c[n] + eps * dirs[n] if n in dirs else c[n]) for n in c}
+        cm = {n: (c[n] - eps * dirs[n] if n in dirs else c[n]) for n in c}
+        fd = (_loss(cp, dO, dS_T) - _loss(cm, dO, dS_T)) / (2 * eps)
+        an = sum(np.sum(g[gn] * dirs[n]) for n, gn in names)
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (trial, fd, an)
+
+
+def test_backward_homogeneity_identities():
+    """o is linear in q: <dq,q> = <dO,o>.  (o, S_T) are jointly linear in (v, S0):
+    <dv,v> + <dS0,S0> = <dO,o> + <dS_T,S_T>.  log a = log g + log b: dlog_g = b * db."""
+    rng = np.random.default_rng(23)
+    c = rand_case(rng, B=2, H=2, T=40, Dk=8, Dv=6)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"], S0=c["S0"])
+    g = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], dS_T=dS_T, segment=8)
+    lo = np.sum(dO * o)
+    ls = np.sum(dS_T * S_T)
+    assert abs(np.sum(g["dq"] * c["q"]) - lo) <= 1e-11 * max(1, abs(lo))
+    assert abs(np.sum(g["dv"] * c["v"]) + np.sum(g["dS0"] * c["S0"]) - lo - ls) <= 1e-11 * max(1, abs(lo + ls))
+    np.testing.assert_allclose(g["dlog_g"], c["b"] * g["db"], rtol=1e-12, atol=1e-14)
+
+
+def test_backward_segmenting_is_invisible():
+    rng = np.random.default_rng(24)
+    c = rand_case(rng, B=1, H=2, T=23, Dk=4, Dv=3)
+    dO = rng.standard_normal(c["v"].shape)
+    g1 = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], segment=5)
+    g2 = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], segment=64)
+    for key in g1:
+        np.testing.assert_allclose(g1[key], g2[key], rtol=1e-13, atol=1e-14)
