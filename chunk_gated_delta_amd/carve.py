@@ -1,0 +1,200 @@
+"""Python binding of libcarve.so (ctypes).
+
+Argument marshalling only: every step of the operation runs in the HIP
+kernels behind the C ABI (include/carve.h).  PyTorch supplies device memory
+(outputs and workspace are allocated with torch on the inputs' device) and
+the current HIP stream.  There is no CPU fallback: if the library is missing
+or a call is rejected, a RuntimeError is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcarve.so")
+
+CARVE_F32 = 0
+CARVE_BF16 = 1
+
+
+class carve_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("T", ctypes.c_int),
+                ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("L", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
+class carve_content(ctypes.Structure):
+    _fields_ = [("b_x", ctypes.c_void_p), ("U1", ctypes.c_void_p), ("U2", ctypes.c_void_p),
+                ("R", ctypes.c_int), ("m0", ctypes.c_void_p), ("m_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libcarve.so (built in-tree by chunk_gated_delta_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m chunk_gated_delta_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    sp = ctypes.POINTER(carve_shape)
+    cp = ctypes.POINTER(carve_content)
+    lib.carve_fwd_workspace_size.argtypes = [sp, cp]
+    lib.carve_fwd_workspace_size.restype = sz
+    lib.carve_bwd_workspace_size.argtypes = [sp]
+    lib.carve_bwd_workspace_size.restype = sz
+    lib.carve_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp]
+    lib.carve_fwd.restype = i
+    lib.carve_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.carve_bwd.restype = i
+    lib.carve_status_string.argtypes = [i]
+    lib.carve_status_string.restype = ctypes.c_char_p
+    lib.carve_abi_version.argtypes = []
+    lib.carve_abi_version.restype = i
+    _lib = lib
+    return lib
+
+
+def status_string(code):
+    return load_library().carve_status_string(code).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return CARVE_BF16
+    if t.dtype == torch.float32:
+        return CARVE_F32
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _raise(code, what):
+    if code != 0:
+        raise RuntimeError(f"{what}: {status_string(code)}")
+
+
+def make_shape(q, v, L):
+    B, H, T, Dk = q.shape
+    return carve_shape(B, H, T, Dk, v.shape[-1], L, _dtype_code(q))
+
+
+def fwd_workspace_bytes(q, v, L=64, content=False):
+    lib = load_library()
+    s = make_shape(q, v, L)
+    c = carve_content() if content else None
+    return lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(c) if c is not None else None)
+
+
+def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None, workspace=None,
+        want_state=True):
+    """o, S_T, m_out = fwd(...).
+
+    q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, one dtype); log_g, b [B,H,T,Dk]
+    float32; w [B,H,T] float32; S0 [B,H,Dv,Dk] float32 or None.  content is None or a dict
+    with b_x [B,H,T,Dk], U1 [H,R,Dv] / U2 [H,Dk,R] (or None), m0 [B,H,Dv] (or None).
+    Outputs may be passed preallocated (o, S_T, workspace)."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(log_g, "log_g", (B, H, T, Dk), torch.float32, dev)
+    _check(b, "b", (B, H, T, Dk), torch.float32, dev)
+    _check(w, "w", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    s = make_shape(q, v, L)
+    cs = None
+    m_out = None
+    keep = []
+    if content is not None:
+        bx = content["b_x"]
+        U1 = content.get("U1")
+        U2 = content.get("U2")
+        m0 = content.get("m0")
+        _check(bx, "b_x", (B, H, T, Dk), torch.float32, dev)
+        R = 0
+        if U1 is not None:
+            R = U1.shape[1]
+            _check(U1, "U1", (H, R, Dv), torch.float32, dev)
+            _check(U2, "U2", (H, Dk, R), torch.float32, dev)
+        _check(m0, "m0", (B, H, Dv), torch.float32, dev)
+        m_out = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+        cs = carve_content(bx.data_ptr(), None if U1 is None else U1.data_ptr(),
+                           None if U2 is None else U2.data_ptr(), R,
+                           None if m0 is None else m0.data_ptr(), m_out.data_ptr())
+        keep.append(cs)
+    if o is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    need = lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(cs) if cs is not None else None)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
+                         ctypes.byref(cs) if cs is not None else None, _ptr(o), _ptr(S_T),
+                         _ptr(workspace), workspace.numel(), _stream(dev))
+    _raise(code, "carve_fwd")
+    return o, S_T, m_out
+
+
+def bwd(q, k, v, log_g, w, dO, b=None, S0=None, dS_T=None, L=64, want_dS0=True, workspace=None, out=None):
+    """Gradients of the token-only forward: dict with dq, dk, dv, dlog_g, db (None if b is None),
+    dw and dS0 (None unless want_dS0)."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(dO, "dO", (B, H, T, Dv), dt, dev)
+    _check(log_g, "log_g", (B, H, T, Dk), torch.float32, dev)
+    _check(b, "b", (B, H, T, Dk), torch.float32, dev)
+    _check(w, "w", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    s = make_shape(q, v, L)
+    g = out if out is not None else {}
+    if out is None:
+        g["dq"] = torch.empty_like(q)
+        g["dk"] = torch.empty_like(k)
+        g["dv"] = torch.empty_like(v)
+        g["dlog_g"] = torch.empty_like(log_g)
+        g["db"] = None if b is None else torch.empty_like(b)
+        g["dw"] = torch.empty_like(w)
+        g["dS0"] = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = lib.carve_bwd_workspace_size(ctypes.byref(s))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
+                         _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]),
+                         _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel(),
+                         _stream(dev))
+    _raise(code, "carve_bwd")
+    return g

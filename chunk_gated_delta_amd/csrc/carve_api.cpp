@@ -1,0 +1,232 @@
+// C ABI of the CARVE key-axis gated delta rule: argument checks, workspace
+// sizing and kernel dispatch.  Checks run on the host before any launch, so a
+// rejected call touches nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/carve.h"
+#include "carve_internal.h"
+
+namespace {
+
+struct Plan {
+  int BH;      // B * H
+  int D;       // Dk == Dv
+  int LC;      // token tile of the chunk kernels (32 or 64)
+  int NC;      // number of token tiles, ceil(T / LC)
+  int VS;      // value rows per state workgroup
+  bool empty;  // no token to process
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// token tile of the chunk kernels: 32 for short chunks and for fp32 at width 128
+// (LDS limit), else 64
+int tile_for(int L, int dtype, int D) { return (L <= 32 || (dtype == CARVE_F32 && D == 128)) ? 32 : 64; }
+
+// value rows per state workgroup: enough workgroups to cover the 256 compute units
+int value_slice(int BH, int D) {
+  for (int vs : {64, 32, 16}) {
+    if (vs <= D && (long long)BH * (D / vs) >= 256) return vs;
+  }
+  return 16;
+}
+
+carve_status check_shape(const carve_shape* s, Plan* p) {
+  if (!s) return CARVE_ERR_INVALID_ARG;
+  if (s->B < 0 || s->H < 0 || s->T < 0 || s->L < 1) return CARVE_ERR_INVALID_ARG;
+  if (s->dtype != CARVE_F32 && s->dtype != CARVE_BF16) return CARVE_ERR_INVALID_ARG;
+  if (s->Dk != s->Dv) return CARVE_ERR_UNSUPPORTED;
+  if (s->Dk != 64 && s->Dk != 128) return CARVE_ERR_UNSUPPORTED;
+  if ((long long)s->B * s->H > 65535 || s->T > (1 << 30)) return CARVE_ERR_UNSUPPORTED;  // grid y = B*H
+  p->BH = s->B * s->H;
+  p->D = s->Dk;
+  p->LC = tile_for(s->L, s->dtype, s->Dk);
+  p->NC = (s->T + p->LC - 1) / p->LC;
+  p->VS = value_slice(p->BH, p->D);
+  p->empty = (p->BH == 0 || s->T == 0);
+  return CARVE_OK;
+}
+
+carve_status check_content(const carve_shape* s, const Plan& p, const carve_content* c, const float* b) {
+  if (!c) return CARVE_OK;
+  if (b) return CARVE_ERR_INVALID_ARG;                       // erase comes from the content gate
+  if ((c->U1 == nullptr) != (c->U2 == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (c->U1 && (c->R < 1 || c->R > 64)) return CARVE_ERR_INVALID_ARG;
+  if (s->L % p.LC != 0) return CARVE_ERR_UNSUPPORTED;        // content period must be whole tiles
+  if (!p.empty && !c->b_x) return CARVE_ERR_INVALID_ARG;
+  for (const void* q : {(const void*)c->b_x, (const void*)c->U1, (const void*)c->U2, (const void*)c->m0,
+                        (const void*)c->m_out})
+    if (q && !aligned16(q)) return CARVE_ERR_INVALID_ARG;
+  return CARVE_OK;
+}
+
+size_t fwd_ws(const carve_shape* s, const Plan& p, const carve_content* c) {
+  if (p.empty) return 0;
+  const int slots = c ? 1 : p.NC;   // the content kernel reuses one factor slot per head
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, slots, p.LC, p.D);
+}
+
+size_t bwd_ws(const carve_shape* s, const Plan& p) {
+  if (p.empty) return 0;
+  const size_t states = (size_t)p.BH * p.NC * p.D * p.D * sizeof(float);
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D) + 2 * (states + 256);
+}
+
+carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, const void* k, const void* v,
+                        const float* log_g, const float* b, const float* w, const float* S0, void* o,
+                        float* S_T) {
+  carve::FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = s->B;
+  a.H = s->H;
+  a.T = s->T;
+  a.D = p.D;
+  a.LC = p.LC;
+  a.NC = p.NC;
+  a.VS = p.VS;
+  a.dtype = s->dtype == CARVE_BF16 ? 1 : 0;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_g = log_g;
+  a.b = b;
+  a.w = w;
+  a.S0 = S0;
+  a.o = o;
+  a.S_T = S_T;
+  return a;
+}
+
+char* align_up(void* p) {
+  return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t carve_fwd_workspace_size(const carve_shape* s, const carve_content* content) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK) return 0;
+  return fwd_ws(s, p, content);
+}
+
+size_t carve_bwd_workspace_size(const carve_shape* s) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK) return 0;
+  return bwd_ws(s, p);
+}
+
+carve_status carve_fwd(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                       const float* b, const float* w, const float* S0, const carve_content* content, void* o,
+                       float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  st = check_content(s, p, content, b);
+  if (st != CARVE_OK) return st;
+  if (!p.empty) {
+    if (!q || !k || !v || !log_g || !w || !o) return CARVE_ERR_INVALID_ARG;
+  }
+  for (const void* ptr : {q, k, v, (const void*)log_g, (const void*)b, (const void*)w, (const void*)S0,
+                          (const void*)o, (const void*)S_T})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need = fwd_ws(s, p, content);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = hipSuccess;
+    if (S_T) e = carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * p.D * p.D, hs);
+    if (e == hipSuccess && content && content->m_out)
+      e = carve::launch_copy_or_zero(content->m_out, content->m0, (size_t)p.BH * p.D, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::FwdArgs a = fwd_args(s, p, q, k, v, log_g, b, w, S0, o, S_T);
+  hipError_t e;
+  if (content) {
+    a.f = carve::carve_factors(workspace, a.dtype, p.BH, 1, p.LC, p.D);
+    carve::ContentArgs cg;
+    cg.b_x = content->b_x;
+    cg.U1 = content->U1;
+    cg.U2 = content->U2;
+    cg.R = content->U1 ? content->R : 0;
+    cg.m0 = content->m0;
+    cg.m_out = content->m_out;
+    cg.period = s->L;
+    e = carve::launch_fwd_content(a, cg, hs);
+  } else {
+    a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D);
+    e = carve::launch_fwd_prep(a, hs);
+    if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
+  }
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+carve_status carve_bwd(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                       const float* b, const float* w, const float* S0, const void* dO, const float* dS_T,
+                       void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  if ((b == nullptr) != (db == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty) {
+    if (!q || !k || !v || !log_g || !w || !dO || !dq || !dk || !dv || !dlog_g || !dw)
+      return CARVE_ERR_INVALID_ARG;
+  }
+  for (const void* ptr : {q, k, v, (const void*)log_g, (const void*)b, (const void*)w, (const void*)S0, dO,
+                          (const void*)dS_T, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)dlog_g, (const void*)db, (const void*)dw, (const void*)dS0})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need = bwd_ws(s, p);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = hipSuccess;
+    if (dS0) e = carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * p.D * p.D, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fwd = fwd_args(s, p, q, k, v, log_g, b, w, S0, nullptr, nullptr);
+  a.fwd.f = carve::carve_factors(workspace, a.fwd.dtype, p.BH, p.NC, p.LC, p.D);
+  char* base = align_up(static_cast<char*>(workspace) +
+                        carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D));
+  const size_t states = (size_t)p.BH * p.NC * p.D * p.D * sizeof(float);
+  a.fwd.S_chunk = reinterpret_cast<float*>(base);
+  a.dS_chunk = reinterpret_cast<float*>(align_up(base + states));
+  a.dO = dO;
+  a.dS_T = dS_T;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_g = dlog_g;
+  a.db = db;
+  a.dw = dw;
+  a.dS0 = dS0;
+  hipError_t e = carve::launch_fwd_prep(a.fwd, hs);
+  if (e == hipSuccess) e = carve::launch_fwd_state(a.fwd, hs);
+  if (e == hipSuccess) e = carve::launch_bwd_state(a, hs);
+  if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+const char* carve_status_string(carve_status st) {
+  switch (st) {
+    case CARVE_OK: return "CARVE_OK";
+    case CARVE_ERR_INVALID_ARG: return "CARVE_ERR_INVALID_ARG: invalid argument";
+    case CARVE_ERR_UNSUPPORTED: return "CARVE_ERR_UNSUPPORTED: shape or option not supported";
+    case CARVE_ERR_WORKSPACE: return "CARVE_ERR_WORKSPACE: workspace too small";
+    case CARVE_ERR_HIP: return "CARVE_ERR_HIP: kernel launch failed";
+  }
+  return "CARVE_ERR_UNKNOWN";
+}
+
+int carve_abi_version(void) { return CARVE_ABI_VERSION; }
+
+}  // extern "C"

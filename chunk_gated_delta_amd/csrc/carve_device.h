@@ -1,0 +1,122 @@
+// Device-side building blocks shared by the CARVE kernels (gfx950 / CDNA4).
+//
+// Matrix products run on the 16x16 MFMA tiles of CDNA4:
+//   * bf16 operands: v_mfma_f32_16x16x32_bf16 (one instruction per 32-deep k block)
+//   * fp32 operands: v_mfma_f32_16x16x4_f32   (eight instructions per 32-deep k block)
+// Both consume a per-lane "fragment" of 8 consecutive k values:
+//   A operand (16 x 32):  lane l holds A[l % 16][8 * (l / 16) + j], j = 0..7
+//   B operand (32 x 16):  lane l holds B[8 * (l / 16) + j][l % 16]
+// and produce the same accumulator layout:
+//   C (16 x 16):          lane l holds C[4 * (l / 16) + i][l % 16], i = 0..3
+// For the fp32 instruction the eight values of a fragment are fed as eight
+// k=4 steps; because A and B fragments use the same k permutation the sum is
+// unchanged.  These layouts were checked on gfx950 with a lane-layout probe.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace carve {
+
+typedef __bf16 bf16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;   // four wave64 waves per workgroup
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ------------------------------------------------------------------ fragments
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 lo, hi; };
+
+// 8 consecutive elements starting at p (16-byte aligned for bf16, 32 for f32)
+__device__ __forceinline__ Frag<bf16> load_frag(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag<float> load_frag(const float* p) {
+  Frag<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+// 8 elements with a stride (used for operands stored with k along rows)
+__device__ __forceinline__ Frag<bf16> load_frag_strided(const bf16* p, int stride) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = p[j * stride];
+  return f;
+}
+__device__ __forceinline__ Frag<float> load_frag_strided(const float* p, int stride) {
+  Frag<float> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { f.lo[j] = p[j * stride]; f.hi[j] = p[(j + 4) * stride]; }
+  return f;
+}
+__device__ __forceinline__ Frag<bf16> zero_frag(bf16) {
+  Frag<bf16> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = (bf16)0.0f;
+  return f;
+}
+__device__ __forceinline__ Frag<float> zero_frag(float) {
+  Frag<float> f;
+  f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+  f.hi = f.lo;
+  return f;
+}
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[j], b.lo[j], c, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[j], b.hi[j], c, 0, 0, 0);
+}
+
+// single fp32 MFMA step (k = 4): lane l supplies A[l%16][l/16] and B[l/16][l%16]
+__device__ __forceinline__ void mma_k4(f32x4& c, float a, float b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------- conversions
+template <typename T> __device__ __forceinline__ T to(float x);
+template <> __device__ __forceinline__ float to<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 to<bf16>(float x) { return (bf16)x; }
+__device__ __forceinline__ float tof(float x) { return x; }
+__device__ __forceinline__ float tof(bf16 x) { return (float)x; }
+
+// 4 accumulator values written as 4 consecutive elements
+__device__ __forceinline__ void store4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(bf16* p, f32x4 v) {
+  bf16x4 b;
+  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+__device__ __forceinline__ f32x4 load4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4f(const bf16* p) {
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+
+// wave-local ordering of LDS traffic between lanes of one wave
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// padded leading dimensions for LDS tiles: rows shifted by 16 bytes to spread banks
+template <typename T> struct Pad;
+template <> struct Pad<bf16> { static constexpr int v = 8; };
+template <> struct Pad<float> { static constexpr int v = 4; };
+
+}  // namespace carve

@@ -1,0 +1,78 @@
+// Internal launch interface between the C ABI (carve_api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace carve {
+
+// Per-chunk factors produced by the chunk-parallel prep kernel and consumed by
+// the sequential state kernels.  Chunk index ci = (b*H + h) * NC + c.
+//   Wn  [ci][LC][D]  -W      with W  = T diag(w) (K .* Gamma)        (dtype)
+//   Qt  [ci][LC][D]  Q~      = (Q .* Gamma) - P W                    (dtype)
+//   KfT [ci][D][LC]  (K .* Gamma_L / Gamma)^T                        (dtype)
+//   UbT [ci][D][LC]  Ubar^T  with Ubar = T diag(w) V                 (dtype)
+//   OiT [ci][D][LC]  (P Ubar)^T, the intra-chunk output              (dtype)
+//   gL  [ci][D]      Gamma_L, the chunk's total key-axis retention   (float)
+// where Gamma is the inclusive cumulative product of a inside the chunk,
+// T = (I + A)^-1, A = strict_tril(diag(w) (K.*Gamma)(K./Gamma)^T) and
+// P = tril((Q.*Gamma)(K./Gamma)^T).
+struct ChunkFactors {
+  void* Wn;
+  void* Qt;
+  void* KfT;
+  void* UbT;
+  void* OiT;
+  float* gL;
+};
+
+struct FwdArgs {
+  int B, H, T, D, LC, NC, VS;
+  int dtype;              // 0 f32, 1 bf16
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_g;
+  const float* b;         // may be null (= 1)
+  const float* w;
+  const float* S0;        // may be null
+  void* o;                // may be null (state-only pass)
+  float* S_T;             // may be null
+  float* S_chunk;         // may be null: state at the start of every chunk, [ci][D][D] float
+  ChunkFactors f;
+};
+
+struct ContentArgs {
+  const float* b_x;
+  const float* U1;        // may be null
+  const float* U2;        // may be null
+  int R;
+  const float* m0;        // may be null
+  float* m_out;           // may be null
+  int period;             // content period in tokens (the chunk length L), multiple of LC
+};
+
+struct BwdArgs {
+  FwdArgs fwd;            // forward inputs, factors and S_chunk (all required)
+  const void* dO;
+  const float* dS_T;      // may be null
+  float* dS_chunk;        // [ci][D][D] float: gradient w.r.t. the state at the END of chunk ci
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dlog_g;
+  float* db;              // may be null (iff b is null)
+  float* dw;
+  float* dS0;             // may be null
+};
+
+size_t factors_bytes(int dtype, int BH, int NC, int LC, int D);
+ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D);
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
+hipError_t launch_fwd_prep(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_state(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_content(const FwdArgs& a, const ContentArgs& c, hipStream_t st);
+hipError_t launch_bwd_state(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
+
+}  // namespace carve

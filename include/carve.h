@@ -1,0 +1,148 @@
+/*
+ * carve.h -- C ABI of the MI355X (gfx950) CARVE key-axis gated delta rule.
+ *
+ * The operation (CARVE pages: liuzhao09.github.io CARVE notes, sections 2.1-2.3;
+ * gist.science technical summary, section 2):  per batch b and head h, with a
+ * state S in R^{Dv x Dk} (rows: value index, columns: key index),
+ *
+ *     a_t = exp(log_g_t) * b_t                      key-axis retention x erase, in (0,1]^Dk
+ *     P_t = S_{t-1} Diag(a_t)                       decay and erase right-multiply the key axis
+ *     S_t = P_t + w_t (v_t - P_t k_t) k_t^T         delta-rule write of the prediction error,
+ *                                                   one scalar write strength w_t per head
+ *     o_t = S_t q_t                                 readout of the updated state
+ *
+ * computed chunk-parallel in WY form: within a chunk of tokens one strictly
+ * lower-triangular coupling matrix, shared by every value channel because all
+ * gating sits on the key axis, is inverted once (section 2.3 of the notes: the
+ * coupling does not depend on the value index, so a single triangular solve
+ * serves all d_v columns).  Optionally the erase gate is content-aware
+ * (section 2.2): for chunk c of L tokens
+ *
+ *     b_{c,t} = sigmoid(b_x_t + U2 (U1 m_{c-1})),   m_{c-1} = mean of chunk c-1's outputs o,
+ *
+ * with m_{-1} = m0 (zero when not given), a zero-initialised low-rank projection
+ * U_b = U2 U1 per head.
+ *
+ * No query scaling and no normalisation are applied; callers L2-normalise q, k.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) are HIP device pointers; structs are host memory.
+ *   - All tensors are dense, row-major, with the shapes given below, and
+ *     16-byte aligned.  "dtype" tensors are float32 or bfloat16 per shape->dtype;
+ *     gates, states, workspace-independent outputs marked float are float32.
+ *   - The caller owns every buffer, including the workspace, which must hold at
+ *     least *_workspace_size() bytes.  The library never allocates or frees
+ *     device memory and keeps no mutable global state; calls on different
+ *     streams may run concurrently as long as they use different workspaces.
+ *   - Every launch is enqueued on `stream` (a hipStream_t; NULL = default
+ *     stream) and the call returns without synchronising.
+ *   - Argument checks run on the host before any launch.  On a non-OK status
+ *     nothing has been launched and no output was touched, except
+ *     CARVE_ERR_HIP, which reports a launch error (hipGetLastError) after the
+ *     launches were issued.  Device faults surface at the caller's next
+ *     synchronisation.  NaN/Inf inputs propagate unchecked.
+ *   - Supported: Dk == Dv in {64, 128}; any T >= 0 (a final partial chunk is
+ *     handled); B, H >= 0 (an empty batch, head or token axis is a no-op that
+ *     still writes S_T = S0 and m_out = m0).  Chunk length L: any L >= 1 for
+ *     token-only gates (the result does not depend on L; the kernels tile
+ *     tokens in blocks of 32 when L <= 32 and of 64 otherwise); for the content
+ *     path L must be a multiple of that tile (32, 64, 128, ...).
+ *   - Numerical range: the chunk kernels form products exp(G_r) and exp(-G_s)
+ *     of the cumulative log-retention G inside one tile of tokens, so every
+ *     key channel's retention accumulated over one tile must stay above about
+ *     1e-30 (|sum of log a| < ~69 per 64 tokens); beyond that outputs are NaN.
+ */
+#ifndef CARVE_H
+#define CARVE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CARVE_ABI_VERSION 1
+
+typedef enum {
+  CARVE_OK = 0,
+  CARVE_ERR_INVALID_ARG = 1,   /* null required pointer, negative size, b given together with content, ... */
+  CARVE_ERR_UNSUPPORTED = 2,   /* shape or option outside the supported set above                    */
+  CARVE_ERR_WORKSPACE = 3,     /* workspace smaller than *_workspace_size()                          */
+  CARVE_ERR_HIP = 4            /* a kernel launch failed                                             */
+} carve_status;
+
+typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;   /* dtype of q, k, v, o, dO, dq, dk, dv */
+
+typedef struct {
+  int B, H, T;     /* batch, heads, tokens                         */
+  int Dk, Dv;      /* key and value widths (equal, 64 or 128)      */
+  int L;           /* chunk length                                  */
+  carve_dtype dtype;
+} carve_shape;
+
+/* Content-aware erase (notes section 2.2).  Pass NULL to carve_fwd for token-only gates. */
+typedef struct {
+  const float* b_x;  /* (device) [B,H,T,Dk] erase pre-activation (required)                     */
+  const float* U1;   /* (device) [H,R,Dv] or NULL;  U1 and U2 both NULL = no projection,        */
+  const float* U2;   /* (device) [H,Dk,R] or NULL;  then b = sigmoid(b_x) exactly               */
+  int R;             /* rank of the projection, 1..64 (ignored when U1 = U2 = NULL)             */
+  const float* m0;   /* (device) [B,H,Dv] mean output of the chunk before this call, or NULL (= 0) */
+  float* m_out;      /* (device) [B,H,Dv] mean output of this call's last chunk, or NULL         */
+} carve_content;
+
+/* Bytes of device workspace carve_fwd needs for this shape (0 is a valid answer). */
+size_t carve_fwd_workspace_size(const carve_shape* s, const carve_content* content);
+
+/*
+ * Forward pass.
+ *   q, k   (device) [B,H,T,Dk] dtype          v (device) [B,H,T,Dv] dtype
+ *   log_g  (device) [B,H,T,Dk] float, <= 0    log of the key-axis retention
+ *   b      (device) [B,H,T,Dk] float in (0,1] erase gate, or NULL (= 1); must be NULL with content
+ *   w      (device) [B,H,T]    float          scalar write strength per head and token
+ *   S0     (device) [B,H,Dv,Dk] float         initial state, or NULL (= 0)
+ *   content                                    NULL (token-only gates) or content-aware erase
+ *   o      (device) [B,H,T,Dv] dtype          output (written)
+ *   S_T    (device) [B,H,Dv,Dk] float         final state (written), or NULL
+ */
+carve_status carve_fwd(const carve_shape* s,
+                       const void* q, const void* k, const void* v,
+                       const float* log_g, const float* b, const float* w,
+                       const float* S0, const carve_content* content,
+                       void* o, float* S_T,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace carve_bwd needs for this shape. */
+size_t carve_bwd_workspace_size(const carve_shape* s);
+
+/*
+ * Backward pass of the token-only forward (content-aware backward is not
+ * provided: CARVE_ERR_UNSUPPORTED is never needed because there is no content
+ * argument).  Recomputes the forward internally.
+ *   q, k, v, log_g, b, w, S0   as for carve_fwd
+ *   dO     (device) [B,H,T,Dv] dtype          gradient of the loss w.r.t. o
+ *   dS_T   (device) [B,H,Dv,Dk] float         gradient w.r.t. S_T, or NULL (= 0)
+ * Outputs (all written, shapes as the matching input):
+ *   dq, dk (dtype) [B,H,T,Dk]; dv (dtype) [B,H,T,Dv];
+ *   dlog_g (float) [B,H,T,Dk]: derivative w.r.t. log g;
+ *   db     (float) [B,H,T,Dk]: derivative w.r.t. the erase probability b; must be NULL iff b is NULL;
+ *   dw     (float) [B,H,T]:    derivative w.r.t. w;
+ *   dS0    (float) [B,H,Dv,Dk] derivative w.r.t. S0, or NULL (not written).
+ */
+carve_status carve_bwd(const carve_shape* s,
+                       const void* q, const void* k, const void* v,
+                       const float* log_g, const float* b, const float* w,
+                       const float* S0, const void* dO, const float* dS_T,
+                       void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* carve_status_string(carve_status st);
+
+/* CARVE_ABI_VERSION of the built library. */
+int carve_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CARVE_H */

@@ -1,0 +1,114 @@
+"""The C ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before any launch (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunk_gated_delta_amd import carve
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "carve.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+FAKE = 0x100000  # 16-byte aligned placeholder address; never dereferenced on a rejected call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(carve_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return carve.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"carve_fwd", "carve_bwd", "carve_fwd_workspace_size", "carve_bwd_workspace_size",
+            "carve_status_string", "carve_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.carve_abi_version() == 1
+    for code in range(5):
+        assert carve.status_string(code).startswith("CARVE_")
+
+
+def shape(B=2, H=2, T=128, D=128, L=64, dtype=carve.CARVE_BF16, Dv=None):
+    return carve.carve_shape(B, H, T, D, D if Dv is None else Dv, L, dtype)
+
+
+def call_fwd(lib, s, q=FAKE, k=FAKE, v=FAKE, log_g=FAKE, b=None, w=FAKE, S0=None, content=None, o=FAKE,
+             S_T=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.carve_fwd(ctypes.byref(s), q, k, v, log_g, b, w, S0,
+                         ctypes.byref(content) if content is not None else None, o, S_T, ws, ws_bytes, None)
+
+
+def test_fwd_rejects_bad_shapes(lib):
+    assert call_fwd(lib, shape(D=96)) == UNSUPPORTED
+    assert call_fwd(lib, shape(D=128, Dv=64)) == UNSUPPORTED
+    assert call_fwd(lib, shape(B=-1)) == INVALID
+    assert call_fwd(lib, shape(T=-5)) == INVALID
+    assert call_fwd(lib, shape(L=0)) == INVALID
+    assert call_fwd(lib, shape(dtype=7)) == INVALID
+    assert call_fwd(lib, None if False else shape(), q=None) == INVALID
+    assert call_fwd(lib, shape(), w=None) == INVALID
+    assert call_fwd(lib, shape(), o=None) == INVALID
+    assert call_fwd(lib, shape(), k=FAKE + 4) == INVALID          # misaligned
+
+
+def test_fwd_workspace_checks(lib):
+    s = shape()
+    need = lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+    assert need > 0
+    assert call_fwd(lib, s, ws_bytes=need - 1) == WORKSPACE
+    assert call_fwd(lib, s, ws=None, ws_bytes=need) == WORKSPACE
+    # the factor workspace scales with the token count
+    s2 = shape(T=256)
+    assert lib.carve_fwd_workspace_size(ctypes.byref(s2), None) > need
+    # an empty problem needs no workspace and, with no outputs to fill, launches nothing
+    s0 = shape(T=0)
+    assert lib.carve_fwd_workspace_size(ctypes.byref(s0), None) == 0
+    assert call_fwd(lib, s0, q=None, k=None, v=None, log_g=None, w=None, o=None, ws=None, ws_bytes=0) == OK
+    sb = shape(B=0)
+    assert call_fwd(lib, sb, q=None, k=None, v=None, log_g=None, w=None, o=None, ws=None, ws_bytes=0) == OK
+
+
+def test_fwd_content_checks(lib):
+    c = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
+    assert call_fwd(lib, shape(), b=FAKE, content=c) == INVALID               # b together with content
+    c_half = carve.carve_content(FAKE, FAKE, None, 16, None, None)
+    assert call_fwd(lib, shape(), content=c_half) == INVALID                 # U1 without U2
+    c_rank = carve.carve_content(FAKE, FAKE, FAKE, 0, None, None)
+    assert call_fwd(lib, shape(), content=c_rank) == INVALID                 # rank 0
+    c_nobx = carve.carve_content(None, None, None, 0, None, None)
+    assert call_fwd(lib, shape(), content=c_nobx) == INVALID                 # b_x required
+    assert call_fwd(lib, shape(L=16), content=c) == UNSUPPORTED               # period not whole tiles
+    assert call_fwd(lib, shape(L=96), content=c) == UNSUPPORTED
+    s = shape()
+    assert lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(c)) < \
+        lib.carve_fwd_workspace_size(ctypes.byref(s), None)                  # one factor slot per head
+    assert call_fwd(lib, s, content=c, ws_bytes=0) == WORKSPACE
+
+
+def call_bwd(lib, s, b=None, db=None, dq=FAKE, dO=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.carve_bwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, b, FAKE, None, dO, None,
+                         dq, FAKE, FAKE, FAKE, db, FAKE, None, ws, ws_bytes, None)
+
+
+def test_bwd_checks(lib):
+    s = shape()
+    assert call_bwd(lib, s, b=FAKE, db=None) == INVALID        # db must be given iff b is
+    assert call_bwd(lib, s, b=None, db=FAKE) == INVALID
+    assert call_bwd(lib, s, dq=None) == INVALID
+    assert call_bwd(lib, s, dO=None) == INVALID
+    assert call_bwd(lib, shape(D=32)) == UNSUPPORTED
+    need = lib.carve_bwd_workspace_size(ctypes.byref(s))
+    assert need > lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+    assert call_bwd(lib, s, ws_bytes=need - 1) == WORKSPACE
