@@ -1,0 +1,244 @@
+"""Benchmark of the CARVE key-axis gated delta rule on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--pass fwd+bwd|fwd] [--no-cpu-baseline]
+
+One step = one pass of the hot path over one batch of the 1.3B-head-shape
+workload (B4 H16 T4096 d128 L64, bf16 q/k/v, fp32 gates and state): the
+token-only forward (chunk prep + state pass) followed by the backward
+(recompute, reverse state pass, chunk gradients).  Inputs are synthetic and
+seeded, already resident in HBM when the timed region starts.  Prints ONE JSON
+line.  The content-aware forward of the same shape is timed separately and
+reported under "extra".
+
+Roofline: every stage is bracketed with HIP events on the stream it runs on
+(carve_fwd_ex / carve_bwd_ex) inside the timed region; the stage with the
+largest mean duration is the dominant kernel, and its achieved bandwidth is
+its algorithmic bytes (inputs it must read plus outputs it must write, per
+token-head, times the token-heads of one launch) over that mean duration.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--pass", dest="passes", default="fwd+bwd", choices=["fwd+bwd", "fwd"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=512)
+    p.add_argument("--no-content", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic(wl, with_bwd):
+    """Algorithmic bytes and flops per token-head (inputs read once, outputs written once;
+    triangle-aware flop count, 2 per multiply-add)."""
+    d, L = wl.Dk, wl.L
+    es = 2 if wl.dtype == "bf16" else 4
+    gates = 4 * d * (2 if wl.erase in ("sigmoid", "ones") else 1) + 4       # log_g (+ b) + w
+    fwd_in = 3 * es * d + gates                                                # q, k, v, gates
+    fwd_out = es * d                                                           # o
+    flops_fwd = 2 * ((L - 1) / 2 * (2 * d + d) + (L + 1) / 2 * (d + d) + 3 * d * d + L * L / 6)
+    out = {"fwd_in": fwd_in, "fwd_out": fwd_out, "fwd": fwd_in + fwd_out, "flops_fwd": flops_fwd}
+    if with_bwd:
+        bwd_in = fwd_in + es * d                                               # inputs again + dO
+        bwd_out = 3 * es * d + gates                                           # dq dk dv + dlog_g (+ db) + dw
+        out.update(bwd_in=bwd_in, bwd_out=bwd_out, bwd=bwd_in + bwd_out, flops_bwd=2 * flops_fwd)
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the CARVE kernels run on a single MI355X in this build "
+              f"(--gpus {args.gpus} is not supported; heads would shard across GPUs with no communication, "
+              f"see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from chunk_gated_delta_amd import carve
+    from chunk_gated_delta_amd.synth import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["head1p3b_fwd"]
+    with_bwd = args.passes == "fwd+bwd"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(wl, with_dO=True)
+
+    def t_bf16(key):
+        return torch.from_numpy(np.ascontiguousarray(inp[key + "_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def t_f32(key):
+        return torch.from_numpy(np.ascontiguousarray(inp[key], dtype=np.float32)).to(dev)
+
+    q, k, v, dO = t_bf16("q"), t_bf16("k"), t_bf16("v"), t_bf16("dO")
+    log_g, b, w = t_f32("log_g"), t_f32("b"), t_f32("w")
+    B, H, T, D = wl.B, wl.H, wl.T, wl.Dk
+    o = torch.empty_like(v)
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws_f = torch.empty(max(1, carve.fwd_workspace_bytes(q, v, wl.L)), dtype=torch.uint8, device=dev)
+    lib = carve.load_library()
+    shape = carve.make_shape(q, v, wl.L)
+    import ctypes
+    ws_b = torch.empty(max(1, lib.carve_bwd_workspace_size(ctypes.byref(shape))), dtype=torch.uint8, device=dev)
+    grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+             "dlog_g": torch.empty_like(log_g), "db": torch.empty_like(b), "dw": torch.empty_like(w), "dS0": None}
+
+    n_fwd_stages, n_bwd_stages = 2, 4
+    fwd_names = ["fwd_prep", "fwd_state"]
+    bwd_names = ["bwd_prep", "bwd_state_fwd", "bwd_state_rev", "bwd_chunk_grads"]
+
+    def new_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        for e in evs:
+            e.record()          # materialise the underlying hipEvent_t
+        return evs
+
+    def step(fe, be):
+        carve.fwd(q, k, v, log_g, w, b=b, L=wl.L, o=o, S_T=S_T, workspace=ws_f,
+                  profile=carve.make_profile(fe) if fe is not None else None)
+        if with_bwd:
+            carve.bwd(q, k, v, log_g, w, dO, b=b, L=wl.L, want_dS0=False, workspace=ws_b, out=grads,
+                      profile=carve.make_profile(be) if be is not None else None)
+
+    for _ in range(args.warmup):
+        step(None, None)
+    torch.cuda.synchronize()
+
+    stage_evs = [(new_events(n_fwd_stages), new_events(n_bwd_stages) if with_bwd else None)
+                 for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(*stage_evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    stage_ms = {}
+    for fe, be in stage_evs:
+        for j, name in enumerate(fwd_names):
+            stage_ms.setdefault(name, []).append(fe[j].elapsed_time(fe[j + 1]))
+        if be is not None:
+            for j, name in enumerate(bwd_names):
+                stage_ms.setdefault(name, []).append(be[j].elapsed_time(be[j + 1]))
+    stage_mean = {k_: float(np.mean(v_)) for k_, v_ in stage_ms.items()}
+    fwd_ms = sum(stage_mean[n] for n in fwd_names)
+
+    # content-aware forward of the same shape (separate timing, not part of the step)
+    extra = {"stage_ms": {k_: round(v_, 4) for k_, v_ in stage_mean.items()},
+             "fwd_tokens_per_s": B * T / (fwd_ms * 1e-3)}
+    if not args.no_content:
+        wc = WORKLOADS["content_fwd"]
+        cin = make_inputs(wc)
+        cq = torch.from_numpy(np.ascontiguousarray(cin["q_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+        ck = torch.from_numpy(np.ascontiguousarray(cin["k_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+        cv = torch.from_numpy(np.ascontiguousarray(cin["v_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+        cf = {key: torch.from_numpy(np.ascontiguousarray(cin[key], dtype=np.float32)).to(dev)
+              for key in ("log_g", "w", "b_x", "U1", "U2")}
+        cont = {"b_x": cf["b_x"], "U1": cf["U1"], "U2": cf["U2"]}
+        ws_c = torch.empty(max(1, carve.fwd_workspace_bytes(cq, cv, wc.L, content=True)), dtype=torch.uint8,
+                           device=dev)
+        co = torch.empty_like(cv)
+        for _ in range(2):
+            carve.fwd(cq, ck, cv, cf["log_g"], cf["w"], L=wc.L, content=cont, o=co, workspace=ws_c)
+        torch.cuda.synchronize()
+        ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nrep = 5
+        ce0.record()
+        for _ in range(nrep):
+            carve.fwd(cq, ck, cv, cf["log_g"], cf["w"], L=wc.L, content=cont, o=co, workspace=ws_c)
+        ce1.record()
+        torch.cuda.synchronize()
+        cms = ce0.elapsed_time(ce1) / nrep
+        extra["content_fwd_ms"] = round(cms, 4)
+        extra["content_fwd_tokens_per_s"] = wc.B * wc.T / (cms * 1e-3)
+        del cq, ck, cv, cf, cont, ws_c, co
+
+    # roofline of the dominant stage
+    alg = algorithmic(wl, with_bwd)
+    units = B * H * T
+    stage_bytes = {
+        "fwd_prep": alg["fwd_in"], "fwd_state": alg["fwd_out"],
+        "bwd_prep": alg["fwd_in"], "bwd_state_fwd": 0, "bwd_state_rev": es_do(wl),
+        "bwd_chunk_grads": alg.get("bwd_in", 0) + alg.get("bwd_out", 0),
+    }
+    dom = max(stage_mean, key=stage_mean.get)
+    dom_ms = stage_mean[dom]
+    ach = stage_bytes[dom] * units / (dom_ms * 1e-3) / 1e9
+    path_bytes = alg["fwd"] + (alg["bwd"] if with_bwd else 0)
+    path_flops = alg["flops_fwd"] + (alg["flops_bwd"] if with_bwd else 0)
+    extra["path_hbm_frac"] = path_bytes * units / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    extra["path_mfma_frac"] = path_flops * units / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS
+    extra["algorithmic_bytes_per_token_head"] = path_bytes
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_token_head": stage_bytes[dom], "launch_ms": round(dom_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, wl, args.cpu_sample_tokens, with_bwd)
+
+    tokens = B * T
+    line = {
+        "metric": "tokens/s (fwd, fwd+bwd) at B4 H16 T4096 d128 L64; % MFMA peak",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "head1p3b_" + args.passes.replace("+", "_"), "B": B, "H": H, "T": T, "d": D,
+                   "L": wl.L, "pass": args.passes, "parallelism": "single-gpu"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+def es_do(wl):
+    """dO bytes per token-head read by the reverse state pass."""
+    return (2 if wl.dtype == "bf16" else 4) * wl.Dv
+
+
+def cpu_baseline(inp, wl, t_sample, with_bwd):
+    """The float64 reference timed on the host on the first t_sample tokens of every head."""
+    import oracle
+    sl = {k_: v_[:, :, :t_sample] for k_, v_ in inp.items() if not k_.endswith("_bits") and np.ndim(v_) >= 3}
+    t0 = time.perf_counter()
+    oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_g"], sl["w"], b=sl.get("b"), L=wl.L)
+    if with_bwd:
+        oracle.backward(sl["q"], sl["k"], sl["v"], sl["log_g"], sl["w"], sl["dO"], b=sl.get("b"))
+    dt = time.perf_counter() - t0
+    return {"value": wl.B * t_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"all {wl.B}x{wl.H} heads, first {t_sample} of {wl.T} tokens, "
+                      f"{'forward+backward' if with_bwd else 'forward'}, float64 numpy, single process",
+            "seconds": round(dt, 2), "cpu": platform.processor() or platform.machine(),
+            "numpy": np.__version__}
+
+
+if __name__ == "__main__":
+    main()

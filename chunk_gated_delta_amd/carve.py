@@ -29,6 +29,19 @@ class carve_content(ctypes.Structure):
                 ("R", ctypes.c_int), ("m0", ctypes.c_void_p), ("m_out", ctypes.c_void_p)]
 
 
+class carve_profile(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p * 9), ("n_events", ctypes.c_int)]
+
+
+def make_profile(events):
+    """carve_profile from torch.cuda.Event objects (each recorded once so its handle exists)."""
+    prof = carve_profile()
+    for i, ev in enumerate(events):
+        prof.events[i] = ev.cuda_event
+    prof.n_events = len(events)
+    return prof
+
+
 _lib = None
 
 
@@ -49,6 +62,11 @@ def load_library():
     lib.carve_bwd_workspace_size.restype = sz
     lib.carve_fwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp]
     lib.carve_fwd.restype = i
+    pp = ctypes.POINTER(carve_profile)
+    lib.carve_fwd_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp, pp]
+    lib.carve_fwd_ex.restype = i
+    lib.carve_bwd_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
+    lib.carve_bwd_ex.restype = i
     lib.carve_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.carve_bwd.restype = i
     lib.carve_status_string.argtypes = [i]
@@ -110,7 +128,7 @@ def fwd_workspace_bytes(q, v, L=64, content=False):
 
 
 def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None, workspace=None,
-        want_state=True):
+        want_state=True, profile=None):
     """o, S_T, m_out = fwd(...).
 
     q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, one dtype); log_g, b [B,H,T,Dk]
@@ -156,14 +174,16 @@ def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None
     need = lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(cs) if cs is not None else None)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    code = lib.carve_fwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
-                         ctypes.byref(cs) if cs is not None else None, _ptr(o), _ptr(S_T),
-                         _ptr(workspace), workspace.numel(), _stream(dev))
+    code = lib.carve_fwd_ex(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
+                            ctypes.byref(cs) if cs is not None else None, _ptr(o), _ptr(S_T),
+                            _ptr(workspace), workspace.numel(), _stream(dev),
+                            ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_fwd")
     return o, S_T, m_out
 
 
-def bwd(q, k, v, log_g, w, dO, b=None, S0=None, dS_T=None, L=64, want_dS0=True, workspace=None, out=None):
+def bwd(q, k, v, log_g, w, dO, b=None, S0=None, dS_T=None, L=64, want_dS0=True, workspace=None, out=None,
+        profile=None):
     """Gradients of the token-only forward: dict with dq, dk, dv, dlog_g, db (None if b is None),
     dw and dS0 (None unless want_dS0)."""
     lib = load_library()
@@ -192,9 +212,9 @@ def bwd(q, k, v, log_g, w, dO, b=None, S0=None, dS_T=None, L=64, want_dS0=True, 
     need = lib.carve_bwd_workspace_size(ctypes.byref(s))
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    code = lib.carve_bwd(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
-                         _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]),
-                         _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel(),
-                         _stream(dev))
+    code = lib.carve_bwd_ex(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
+                            _ptr(dO), _ptr(dS_T), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]),
+                            _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel(),
+                            _stream(dev), ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_bwd")
     return g

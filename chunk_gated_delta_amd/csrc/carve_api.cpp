@@ -22,9 +22,12 @@ struct Plan {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// token tile of the chunk kernels: 32 for short chunks and for fp32 at width 128
-// (LDS limit), else 64
-int tile_for(int L, int dtype, int D) { return (L <= 32 || (dtype == CARVE_F32 && D == 128)) ? 32 : 64; }
+// token tile of the chunk kernels: 32 for short chunks and for float32 inputs
+// (LDS budget of the backward chunk kernel), else 64
+int tile_for(int L, int dtype, int D) {
+  (void)D;
+  return (L <= 32 || dtype == CARVE_F32) ? 32 : 64;
+}
 
 // value rows per state workgroup: enough workgroups to cover the 256 compute units
 int value_slice(int BH, int D) {
@@ -66,13 +69,13 @@ carve_status check_content(const carve_shape* s, const Plan& p, const carve_cont
 size_t fwd_ws(const carve_shape* s, const Plan& p, const carve_content* c) {
   if (p.empty) return 0;
   const int slots = c ? 1 : p.NC;   // the content kernel reuses one factor slot per head
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, slots, p.LC, p.D);
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, slots, p.LC, p.D, false);
 }
 
 size_t bwd_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
   const size_t states = (size_t)p.BH * p.NC * p.D * p.D * sizeof(float);
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D) + 2 * (states + 256);
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, true) + 2 * (states + 256) + 256;
 }
 
 carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, const void* k, const void* v,
@@ -100,6 +103,11 @@ carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, cons
   return a;
 }
 
+void mark(const carve_profile* prof, int i, hipStream_t st) {
+  if (prof && i >= 0 && i < prof->n_events && i <= CARVE_MAX_STAGES && prof->events[i])
+    (void)hipEventRecord(reinterpret_cast<hipEvent_t>(prof->events[i]), st);
+}
+
 char* align_up(void* p) {
   return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255));
 }
@@ -123,6 +131,13 @@ size_t carve_bwd_workspace_size(const carve_shape* s) {
 carve_status carve_fwd(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
                        const float* b, const float* w, const float* S0, const carve_content* content, void* o,
                        float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+  return carve_fwd_ex(s, q, k, v, log_g, b, w, S0, content, o, S_T, workspace, workspace_bytes, stream, nullptr);
+}
+
+carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                          const float* b, const float* w, const float* S0, const carve_content* content, void* o,
+                          float* S_T, void* workspace, size_t workspace_bytes, void* stream,
+                          const carve_profile* prof) {
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -148,7 +163,7 @@ carve_status carve_fwd(const carve_shape* s, const void* q, const void* k, const
   carve::FwdArgs a = fwd_args(s, p, q, k, v, log_g, b, w, S0, o, S_T);
   hipError_t e;
   if (content) {
-    a.f = carve::carve_factors(workspace, a.dtype, p.BH, 1, p.LC, p.D);
+    a.f = carve::carve_factors(workspace, a.dtype, p.BH, 1, p.LC, p.D, false);
     carve::ContentArgs cg;
     cg.b_x = content->b_x;
     cg.U1 = content->U1;
@@ -157,11 +172,16 @@ carve_status carve_fwd(const carve_shape* s, const void* q, const void* k, const
     cg.m0 = content->m0;
     cg.m_out = content->m_out;
     cg.period = s->L;
+    mark(prof, 0, hs);
     e = carve::launch_fwd_content(a, cg, hs);
+    mark(prof, 1, hs);
   } else {
-    a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D);
+    a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, false);
+    mark(prof, 0, hs);
     e = carve::launch_fwd_prep(a, hs);
+    mark(prof, 1, hs);
     if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
+    mark(prof, 2, hs);
   }
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
@@ -170,6 +190,14 @@ carve_status carve_bwd(const carve_shape* s, const void* q, const void* k, const
                        const float* b, const float* w, const float* S0, const void* dO, const float* dS_T,
                        void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
                        void* workspace, size_t workspace_bytes, void* stream) {
+  return carve_bwd_ex(s, q, k, v, log_g, b, w, S0, dO, dS_T, dq, dk, dv, dlog_g, db, dw, dS0, workspace,
+                      workspace_bytes, stream, nullptr);
+}
+
+carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                          const float* b, const float* w, const float* S0, const void* dO, const float* dS_T,
+                          void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* stream, const carve_profile* prof) {
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -194,9 +222,10 @@ carve_status carve_bwd(const carve_shape* s, const void* q, const void* k, const
   carve::BwdArgs a;
   memset(&a, 0, sizeof(a));
   a.fwd = fwd_args(s, p, q, k, v, log_g, b, w, S0, nullptr, nullptr);
-  a.fwd.f = carve::carve_factors(workspace, a.fwd.dtype, p.BH, p.NC, p.LC, p.D);
+  a.fwd.bwd = 1;
+  a.fwd.f = carve::carve_factors(workspace, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, true);
   char* base = align_up(static_cast<char*>(workspace) +
-                        carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D));
+                        carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, true));
   const size_t states = (size_t)p.BH * p.NC * p.D * p.D * sizeof(float);
   a.fwd.S_chunk = reinterpret_cast<float*>(base);
   a.dS_chunk = reinterpret_cast<float*>(align_up(base + states));
@@ -209,10 +238,15 @@ carve_status carve_bwd(const carve_shape* s, const void* q, const void* k, const
   a.db = db;
   a.dw = dw;
   a.dS0 = dS0;
+  mark(prof, 0, hs);
   hipError_t e = carve::launch_fwd_prep(a.fwd, hs);
+  mark(prof, 1, hs);
   if (e == hipSuccess) e = carve::launch_fwd_state(a.fwd, hs);
+  mark(prof, 2, hs);
   if (e == hipSuccess) e = carve::launch_bwd_state(a, hs);
+  mark(prof, 3, hs);
   if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
+  mark(prof, 4, hs);
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 

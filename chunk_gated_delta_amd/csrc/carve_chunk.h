@@ -1,0 +1,345 @@
+// Per-chunk factor preparation shared by the forward and backward kernels.
+//
+// Chunk algebra (rows = tokens of one chunk, S = state entering the chunk,
+// Gamma_r = prod_{i<=r} a_i per key channel, Gamma_L its value at the chunk end):
+//   K+ = K .* Gamma, K- = K ./ Gamma, Q+ = Q .* Gamma, K-> = K .* Gamma_L ./ Gamma
+//   A  = strict_tril(diag(w) K+ K-^T)       shared by every value channel
+//   T  = (I + A)^-1                          (one triangular solve per chunk)
+//   U  = T diag(w) V - T diag(w) K+ S^T = Ubar - W S^T
+//   O  = Q+ S^T + tril(Q+ K-^T) U = (P Ubar) + Q~ S^T
+//   S' = S Diag(Gamma_L) + U^T K->
+// This is the token recurrence of the CARVE notes (sections 2.1-2.3) unrolled
+// over one chunk: the shared coupling is what the notes call the single WY-form
+// triangular solve that key-axis-only gating keeps valid.
+#pragma once
+#include "carve_device.h"
+#include "carve_internal.h"
+
+namespace carve {
+
+// ------------------------------------------------------------------ helpers
+template <typename T, int LC, int D>
+struct PrepLayout {
+  static constexpr int LDD = D + Pad<T>::v;      // [LC][D] row stride (elements)
+  static constexpr int LDL = LC + Pad<T>::v;     // [D][LC] and [LC][LC] row stride
+  static constexpr int LDF = LC + 4;             // fp32 [LC][LC] row stride
+  static constexpr int P = kThreads / D;         // token parts per key channel in the gate pass
+  static constexpr int RP = LC / P;              // tokens per part
+  static constexpr size_t szLD = sizeof(T) * LC * LDD;
+  static constexpr size_t szDL = sizeof(T) * D * LDL;
+  static constexpr size_t szLLf = sizeof(float) * LC * LDF;
+  static constexpr size_t szLL = sizeof(T) * LC * LDL;
+  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+  // region 1: K+ and K- (gate pass .. coupling), then T (fp32) and Tb (dtype)
+  static constexpr size_t R1 = 0;
+  static constexpr size_t R1sz = al(cmax(2 * szLD, szLLf + szLL));
+  static constexpr size_t R2 = R1 + R1sz;                 // Q+           (gate pass .. Q~)
+  static constexpr size_t R3 = R2 + al(szLD);             // Kw^T, Vw^T   (gate pass .. WY factors)
+  static constexpr size_t R4 = R3 + al(2 * szDL);         // A (fp32), then (-W)^T
+  static constexpr size_t R5 = R4 + al(cmax(szLLf, szDL)); // P (dtype)
+  static constexpr size_t R6 = R5 + al(szLL);             // Ubar^T
+  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [P][D], T-solve scratch
+  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D + kWaves * 16 * 20));
+};
+
+// lower-triangular block index -> (i, j), j <= i
+__device__ __forceinline__ void tri_index(int t, int& i, int& j) {
+  i = 0;
+  while ((i + 1) * (i + 2) / 2 <= t) ++i;
+  j = t - i * (i + 1) / 2;
+}
+
+// T = (I + A)^-1 for strictly lower-triangular A (fp32 in LDS), LC = 16 * NB.
+// Diagonal 16x16 blocks by column-parallel forward substitution, then the
+// off-diagonal blocks by block forward substitution on fp32 MFMA:
+//   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj,   processed by increasing i - j.
+template <int LC, int LDF>
+__device__ void triangular_inverse(const float* Af, float* Tf, float* scratch) {
+  constexpr int NB = LC / 16;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  if (tid < 16 * NB) {
+    const int base = 16 * (tid / 16), j = tid % 16;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s -= Af[(base + r) * LDF + base + m] * x[m];
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Tf[(base + r) * LDF + base + j] = x[r];
+  }
+  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+    const int r = idx / LC, s = idx % LC;
+    if ((s >> 4) > (r >> 4)) Tf[r * LDF + s] = 0.f;
+  }
+  __syncthreads();
+  for (int d = 1; d < NB; ++d) {
+    if (wave < NB - d) {
+      const int j = wave, i = wave + d;
+      const int lr = lane & 15, lg = lane >> 4;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int m = j; m < i; ++m) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const float a = Af[(16 * i + lr) * LDF + 16 * m + 4 * s4 + lg];
+          const float b = Tf[(16 * m + 4 * s4 + lg) * LDF + 16 * j + lr];
+          mma_k4(y, a, b);
+        }
+      }
+      float* Y = scratch + wave * 16 * 20;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Y[(4 * lg + ii) * 20 + lr] = y[ii];
+      wave_lds_sync();
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float a = Tf[(16 * i + lr) * LDF + 16 * i + 4 * s4 + lg];
+        const float b = Y[(4 * s4 + lg) * 20 + lr];
+        mma_k4(x, a, b);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) Tf[(16 * i + 4 * lg + ii) * LDF + 16 * j + lr] = -x[ii];
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ gate sources
+// Erase gate of one element, split into a raw load (issued early, branch-free)
+// and its activation: token-only with b given, token-only with b = 1, or
+// content-aware b = sigmoid(b_x + z) with the chunk's content signal z (per key
+// channel, in LDS).
+struct TokenGatesB {
+  const float* b;
+  __device__ __forceinline__ float load(size_t idx) const { return b[idx]; }
+  __device__ __forceinline__ float act(float x, int) const { return x; }
+};
+struct TokenGates1 {
+  __device__ __forceinline__ float load(size_t) const { return 1.f; }
+  __device__ __forceinline__ float act(float x, int) const { return x; }
+};
+struct ContentGates {
+  const float* b_x;
+  const float* z;
+  __device__ __forceinline__ float load(size_t idx) const { return b_x[idx]; }
+  __device__ __forceinline__ float act(float x, int ch) const { return 1.f / (1.f + __expf(-(x + z[ch]))); }
+};
+
+// ------------------------------------------------------------------ per-chunk prep
+// Computes the factors of chunk c of head bh and writes them to slot `ci` of
+// the factor arrays.  Uses PrepLayout<T, LC, D>::bytes of LDS at `smem`.
+// With BWD the chunk's factors are written in the layouts the backward passes
+// need: (-W)^T, Q~^T and row-major K-> in addition to -W, K->^T, Ubar^T, Gamma_L
+// (and no Q~ / P Ubar, which only the forward output uses).
+template <typename T, int LC, int D, typename Gates, bool BWD = false>
+__device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
+                           unsigned char* smem) {
+  using Lay = PrepLayout<T, LC, D>;
+  constexpr int NB = LC / 16, NCT = D / 16;
+  constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF, P = Lay::P, RP = Lay::RP;
+  T* Kp = reinterpret_cast<T*>(smem + Lay::R1);
+  T* Km = Kp + LC * LDD;
+  float* Tf = reinterpret_cast<float*>(smem + Lay::R1);
+  T* Tb = reinterpret_cast<T*>(smem + Lay::R1 + Lay::szLLf);
+  T* Qp = reinterpret_cast<T*>(smem + Lay::R2);
+  T* KwT = reinterpret_cast<T*>(smem + Lay::R3);
+  T* VwT = KwT + D * LDL;
+  float* Af = reinterpret_cast<float*>(smem + Lay::R4);
+  T* WnT = reinterpret_cast<T*>(smem + Lay::R4);
+  T* Pb = reinterpret_cast<T*>(smem + Lay::R5);
+  T* UbTs = reinterpret_cast<T*>(smem + Lay::R6);
+  float* wL = reinterpret_cast<float*>(smem + Lay::R7);
+  float* part = wL + LC;
+  float* scratch = part + P * D;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const int t0 = c * LC;
+  const int n = min(LC, a.T - t0);
+  const size_t row0 = (size_t)bh * a.T + t0;   // global token row of the chunk's first token
+  const T* q = reinterpret_cast<const T*>(a.q);
+  const T* k = reinterpret_cast<const T*>(a.k);
+  const T* v = reinterpret_cast<const T*>(a.v);
+  T* gWn = reinterpret_cast<T*>(a.f.Wn) + ci * LC * D;
+  T* gQt = reinterpret_cast<T*>(a.f.Qt) + ci * LC * D;
+  T* gKfT = reinterpret_cast<T*>(a.f.KfT) + ci * D * LC;
+  T* gUbT = reinterpret_cast<T*>(a.f.UbT) + ci * D * LC;
+  T* gOiT = reinterpret_cast<T*>(a.f.OiT) + ci * D * LC;
+  T* gWnT = BWD ? reinterpret_cast<T*>(a.f.WnT) + ci * D * LC : nullptr;
+  T* gQtT = BWD ? reinterpret_cast<T*>(a.f.QtT) + ci * D * LC : nullptr;
+  T* gKf = BWD ? reinterpret_cast<T*>(a.f.Kf) + ci * LC * D : nullptr;
+
+  // ---- gate pass: cumulative key-axis retention Gamma (thread = key channel x token part).
+  // All global loads are issued up front from clamped rows (n >= 1), then masked.
+  const int ch = tid % D, pid = tid / D, r0 = pid * RP;
+  if (tid < LC) wL[tid] = (tid < n) ? a.w[row0 + min(tid, n - 1)] : 0.f;
+  float lgv[RP], gv[RP];
+  T kr[RP], qr[RP], vr[RP];
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const size_t idx = (row0 + min(r0 + i, n - 1)) * D + ch;
+    lgv[i] = a.log_g[idx];
+    gv[i] = gates.load(idx);
+  }
+#pragma unroll
+  for (int i = 0; i < RP; ++i) {
+    const size_t idx = (row0 + min(r0 + i, n - 1)) * D + ch;
+    kr[i] = k[idx];
+    qr[i] = q[idx];
+    vr[i] = v[idx];
+  }
+  float G[RP];
+  {
+    float run = 1.f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      const float av = (r0 + i < n) ? __expf(lgv[i]) * gates.act(gv[i], ch) : 1.f;
+      run *= av;
+      G[i] = run;
+    }
+    part[pid * D + ch] = run;
+  }
+  __syncthreads();
+  float pre = 1.f, tot = 1.f;
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {
+    const float pt = part[pp * D + ch];
+    if (pp < pid) pre *= pt;
+    tot *= pt;
+  }
+  {
+    T kf[RP];
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      const int r = r0 + i;
+      const float gam = pre * G[i];
+      const float inv = 1.f / gam;
+      const bool valid = r < n;
+      const float kv = valid ? tof(kr[i]) : 0.f;
+      const float qv = valid ? tof(qr[i]) : 0.f;
+      const float vv = valid ? tof(vr[i]) : 0.f;
+      const float wr = wL[r];
+      Kp[r * LDD + ch] = to<T>(kv * gam);
+      Km[r * LDD + ch] = to<T>(kv * inv);
+      Qp[r * LDD + ch] = to<T>(qv * gam);
+      KwT[ch * LDL + r] = to<T>(wr * (kv * gam));
+      VwT[ch * LDL + r] = to<T>(wr * vv);
+      kf[i] = to<T>(kv * (tot * inv));
+    }
+#pragma unroll
+    for (int i = 0; i < RP; ++i) gKfT[ch * LC + r0 + i] = kf[i];
+    if (BWD) {
+#pragma unroll
+      for (int i = 0; i < RP; ++i) gKf[(r0 + i) * D + ch] = kf[i];
+    }
+    if (pid == 0) a.f.gL[ci * D + ch] = tot;
+  }
+  __syncthreads();
+
+  // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
+  constexpr int NTRI = NB * (NB + 1) / 2;
+  for (int t = wave; t < 2 * NTRI; t += kWaves) {
+    const bool isA = t < NTRI;
+    int i, j;
+    tri_index(isA ? t : t - NTRI, i, j);
+    const T* Ar = isA ? Kp : Qp;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D; kk += 32) {
+      const Frag<T> fa = load_frag(Ar + (16 * i + lr) * LDD + kk + 8 * lg);
+      const Frag<T> fb = load_frag(Km + (16 * j + lr) * LDD + kk + 8 * lg);
+      mma(acc, fa, fb);
+    }
+    const int s = 16 * j + lr;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const int r = 16 * i + 4 * lg + ii;
+      if (isA) Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
+      else Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
+    }
+  }
+  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+    const int r = idx / LC, s = idx % LC;
+    if ((s >> 4) > (r >> 4)) Pb[r * LDL + s] = to<T>(0.f);
+  }
+  __syncthreads();
+
+  // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products
+  triangular_inverse<LC, LDF>(Af, Tf, scratch);
+  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+    const int r = idx / LC, s = idx % LC;
+    Tb[r * LDL + s] = to<T>(Tf[r * LDF + s]);
+  }
+  __syncthreads();
+
+  // ---- WY factors: W = T Kw, Ubar = T Vw  (Kw = diag(w) K+, Vw = diag(w) V)
+  for (int t = wave; t < 2 * NB * NCT; t += kWaves) {
+    const bool isW = t < NB * NCT;
+    const int tt = isW ? t : t - NB * NCT;
+    const int i = tt / NCT, ct = tt % NCT;
+    const T* Bs = isW ? KwT : VwT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kk = 0; kk < 16 * (i + 1); kk += 32) {
+      const Frag<T> fa = load_frag(Tb + (16 * i + lr) * LDL + kk + 8 * lg);
+      const Frag<T> fb = load_frag(Bs + (16 * ct + lr) * LDL + kk + 8 * lg);
+      mma(acc, fa, fb);
+    }
+    const int col = 16 * ct + lr, r = 16 * i + 4 * lg;
+    if (isW) {
+      const f32x4 neg = -acc;
+      store4(WnT + col * LDL + r, neg);
+      if (BWD) store4(gWnT + col * LC + r, neg);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) gWn[(r + ii) * D + col] = to<T>(neg[ii]);
+    } else {
+      store4(UbTs + col * LDL + r, acc);
+      store4(gUbT + col * LC + r, acc);
+    }
+  }
+  __syncthreads();
+
+  // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
+  for (int t = BWD ? wave + NB * NCT : wave; t < 2 * NB * NCT; t += kWaves) {
+    const bool isO = t < NB * NCT;
+    const int tt = isO ? t : t - NB * NCT;
+    const int i = tt / NCT, ct = tt % NCT;
+    const int col = 16 * ct + lr, r = 16 * i + 4 * lg;
+    f32x4 acc;
+    if (isO) {
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) acc[ii] = tof(Qp[(r + ii) * LDD + col]);
+    }
+    const T* Bs = isO ? UbTs : WnT;
+    for (int kk = 0; kk < 16 * (i + 1); kk += 32) {
+      const Frag<T> fa = load_frag(Pb + (16 * i + lr) * LDL + kk + 8 * lg);
+      const Frag<T> fb = load_frag(Bs + (16 * ct + lr) * LDL + kk + 8 * lg);
+      mma(acc, fa, fb);
+    }
+    if (isO) {
+      store4(gOiT + col * LC + r, acc);
+    } else if (BWD) {
+      store4(gQtT + col * LC + r, acc);
+    } else {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) gQt[(r + ii) * D + col] = to<T>(acc[ii]);
+    }
+  }
+}
+
+
+// State tiles of a workgroup holding VS value rows of a D x D state: lane l of
+// tile (ct, vt) holds S[16 vt + l%16][16 ct + 4 (l/16) + i], i = 0..3
+// (accumulator layout of S^T); wave w owns tiles w*SPW .. w*SPW+SPW-1.
+template <int D, int VS>
+struct StateTiles {
+  static constexpr int NVT = VS / 16, NCT = D / 16;
+  static constexpr int SPW = NCT * NVT / kWaves;   // state tiles per wave
+  static_assert(NCT * NVT % kWaves == 0, "state tiles must split evenly over waves");
+};
+
+}  // namespace carve

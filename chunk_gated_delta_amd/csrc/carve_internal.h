@@ -16,6 +16,10 @@ namespace carve {
 // where Gamma is the inclusive cumulative product of a inside the chunk,
 // T = (I + A)^-1, A = strict_tril(diag(w) (K.*Gamma)(K./Gamma)^T) and
 // P = tril((Q.*Gamma)(K./Gamma)^T).
+// Backward mode adds, in the same slots where the forward-only factors would be:
+//   QtT [ci][D][LC]  Q~^T   (slot of Qt)
+//   WnT [ci][D][LC]  (-W)^T (slot of OiT)
+//   Kf  [ci][LC][D]  K->    (an extra slot)
 struct ChunkFactors {
   void* Wn;
   void* Qt;
@@ -23,10 +27,14 @@ struct ChunkFactors {
   void* UbT;
   void* OiT;
   float* gL;
+  void* QtT;
+  void* WnT;
+  void* Kf;
 };
 
 struct FwdArgs {
   int B, H, T, D, LC, NC, VS;
+  int bwd;                // prep writes the backward layouts
   int dtype;              // 0 f32, 1 bf16
   const void* q;
   const void* k;
@@ -65,8 +73,8 @@ struct BwdArgs {
   float* dS0;             // may be null
 };
 
-size_t factors_bytes(int dtype, int BH, int NC, int LC, int D);
-ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D);
+size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, bool bwd);
+ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, bool bwd);
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
 hipError_t launch_fwd_prep(const FwdArgs& a, hipStream_t st);

@@ -18,303 +18,16 @@
 // This is the token recurrence of the CARVE notes (sections 2.1-2.3) unrolled
 // over one chunk: the shared coupling is what the notes call the single WY-form
 // triangular solve that key-axis-only gating keeps valid.
-#include "carve_device.h"
-#include "carve_internal.h"
+#include "carve_chunk.h"
 
 namespace carve {
 
-// ------------------------------------------------------------------ helpers
-template <typename T, int LC, int D>
-struct PrepLayout {
-  static constexpr int LDD = D + Pad<T>::v;      // [LC][D] row stride (elements)
-  static constexpr int LDL = LC + Pad<T>::v;     // [D][LC] and [LC][LC] row stride
-  static constexpr int LDF = LC + 4;             // fp32 [LC][LC] row stride
-  static constexpr int P = kThreads / D;         // token parts per key channel in the gate pass
-  static constexpr int RP = LC / P;              // tokens per part
-  static constexpr size_t szLD = sizeof(T) * LC * LDD;
-  static constexpr size_t szDL = sizeof(T) * D * LDL;
-  static constexpr size_t szLLf = sizeof(float) * LC * LDF;
-  static constexpr size_t szLL = sizeof(T) * LC * LDL;
-  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
-  static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
-  // region 1: K+ and K- (gate pass .. coupling), then T (fp32) and Tb (dtype)
-  static constexpr size_t R1 = 0;
-  static constexpr size_t R1sz = al(cmax(2 * szLD, szLLf + szLL));
-  static constexpr size_t R2 = R1 + R1sz;                 // Q+           (gate pass .. Q~)
-  static constexpr size_t R3 = R2 + al(szLD);             // Kw^T, Vw^T   (gate pass .. WY factors)
-  static constexpr size_t R4 = R3 + al(2 * szDL);         // A (fp32), then (-W)^T
-  static constexpr size_t R5 = R4 + al(cmax(szLLf, szDL)); // P (dtype)
-  static constexpr size_t R6 = R5 + al(szLL);             // Ubar^T
-  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [P][D], T-solve scratch
-  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D + kWaves * 16 * 20));
-};
-
-// lower-triangular block index -> (i, j), j <= i
-__device__ __forceinline__ void tri_index(int t, int& i, int& j) {
-  i = 0;
-  while ((i + 1) * (i + 2) / 2 <= t) ++i;
-  j = t - i * (i + 1) / 2;
-}
-
-// T = (I + A)^-1 for strictly lower-triangular A (fp32 in LDS), LC = 16 * NB.
-// Diagonal 16x16 blocks by column-parallel forward substitution, then the
-// off-diagonal blocks by block forward substitution on fp32 MFMA:
-//   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj,   processed by increasing i - j.
-template <int LC, int LDF>
-__device__ void triangular_inverse(const float* Af, float* Tf, float* scratch) {
-  constexpr int NB = LC / 16;
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  if (tid < 16 * NB) {
-    const int base = 16 * (tid / 16), j = tid % 16;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-      for (int m = 0; m < r; ++m) s -= Af[(base + r) * LDF + base + m] * x[m];
-      x[r] = s;
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Tf[(base + r) * LDF + base + j] = x[r];
-  }
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
-    const int r = idx / LC, s = idx % LC;
-    if ((s >> 4) > (r >> 4)) Tf[r * LDF + s] = 0.f;
-  }
-  __syncthreads();
-  for (int d = 1; d < NB; ++d) {
-    if (wave < NB - d) {
-      const int j = wave, i = wave + d;
-      const int lr = lane & 15, lg = lane >> 4;
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-      for (int m = j; m < i; ++m) {
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const float a = Af[(16 * i + lr) * LDF + 16 * m + 4 * s4 + lg];
-          const float b = Tf[(16 * m + 4 * s4 + lg) * LDF + 16 * j + lr];
-          mma_k4(y, a, b);
-        }
-      }
-      float* Y = scratch + wave * 16 * 20;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Y[(4 * lg + ii) * 20 + lr] = y[ii];
-      wave_lds_sync();
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const float a = Tf[(16 * i + lr) * LDF + 16 * i + 4 * s4 + lg];
-        const float b = Y[(4 * s4 + lg) * 20 + lr];
-        mma_k4(x, a, b);
-      }
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Tf[(16 * i + 4 * lg + ii) * LDF + 16 * j + lr] = -x[ii];
-    }
-    __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------------ gate sources
-// Erase gate of one element: token-only (b given or 1) or content-aware
-// b = sigmoid(b_x + z) with the chunk's content signal z (per key channel, in LDS).
-struct TokenGates {
-  const float* b;
-  __device__ __forceinline__ float operator()(size_t idx, int) const { return b ? b[idx] : 1.f; }
-};
-struct ContentGates {
-  const float* b_x;
-  const float* z;
-  __device__ __forceinline__ float operator()(size_t idx, int ch) const {
-    return 1.f / (1.f + __expf(-(b_x[idx] + z[ch])));
-  }
-};
-
-// ------------------------------------------------------------------ per-chunk prep
-// Computes the factors of chunk c of head bh and writes them to slot `ci` of
-// the factor arrays.  Uses PrepLayout<T, LC, D>::bytes of LDS at `smem`.
-template <typename T, int LC, int D, typename Gates>
-__device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
-                           unsigned char* smem) {
-  using Lay = PrepLayout<T, LC, D>;
-  constexpr int NB = LC / 16, NCT = D / 16;
-  constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF, P = Lay::P, RP = Lay::RP;
-  T* Kp = reinterpret_cast<T*>(smem + Lay::R1);
-  T* Km = Kp + LC * LDD;
-  float* Tf = reinterpret_cast<float*>(smem + Lay::R1);
-  T* Tb = reinterpret_cast<T*>(smem + Lay::R1 + Lay::szLLf);
-  T* Qp = reinterpret_cast<T*>(smem + Lay::R2);
-  T* KwT = reinterpret_cast<T*>(smem + Lay::R3);
-  T* VwT = KwT + D * LDL;
-  float* Af = reinterpret_cast<float*>(smem + Lay::R4);
-  T* WnT = reinterpret_cast<T*>(smem + Lay::R4);
-  T* Pb = reinterpret_cast<T*>(smem + Lay::R5);
-  T* UbTs = reinterpret_cast<T*>(smem + Lay::R6);
-  float* wL = reinterpret_cast<float*>(smem + Lay::R7);
-  float* part = wL + LC;
-  float* scratch = part + P * D;
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int lr = lane & 15, lg = lane >> 4;
-  const int t0 = c * LC;
-  const int n = min(LC, a.T - t0);
-  const size_t row0 = (size_t)bh * a.T + t0;   // global token row of the chunk's first token
-  const T* q = reinterpret_cast<const T*>(a.q);
-  const T* k = reinterpret_cast<const T*>(a.k);
-  const T* v = reinterpret_cast<const T*>(a.v);
-  T* gWn = reinterpret_cast<T*>(a.f.Wn) + ci * LC * D;
-  T* gQt = reinterpret_cast<T*>(a.f.Qt) + ci * LC * D;
-  T* gKfT = reinterpret_cast<T*>(a.f.KfT) + ci * D * LC;
-  T* gUbT = reinterpret_cast<T*>(a.f.UbT) + ci * D * LC;
-  T* gOiT = reinterpret_cast<T*>(a.f.OiT) + ci * D * LC;
-
-  // ---- gate pass: cumulative key-axis retention Gamma (thread = key channel x token part)
-  const int ch = tid % D, pid = tid / D, r0 = pid * RP;
-  if (tid < LC) wL[tid] = (tid < n) ? a.w[row0 + tid] : 0.f;
-  float G[RP];
-  {
-    float run = 1.f;
-#pragma unroll
-    for (int i = 0; i < RP; ++i) {
-      const int r = r0 + i;
-      float av = 1.f;
-      if (r < n) {
-        const size_t idx = (row0 + r) * D + ch;
-        av = __expf(a.log_g[idx]) * gates(idx, ch);
-      }
-      run *= av;
-      G[i] = run;
-    }
-    part[pid * D + ch] = run;
-  }
-  __syncthreads();
-  float pre = 1.f, tot = 1.f;
-#pragma unroll
-  for (int pp = 0; pp < P; ++pp) {
-    const float pt = part[pp * D + ch];
-    if (pp < pid) pre *= pt;
-    tot *= pt;
-  }
-  {
-    T kf[RP];
-#pragma unroll
-    for (int i = 0; i < RP; ++i) {
-      const int r = r0 + i;
-      const float gam = pre * G[i];
-      const float inv = 1.f / gam;
-      float kv = 0.f, qv = 0.f, vv = 0.f;
-      if (r < n) {
-        const size_t idx = (row0 + r) * D + ch;
-        kv = tof(k[idx]);
-        qv = tof(q[idx]);
-        vv = tof(v[idx]);
-      }
-      const float wr = wL[r];
-      Kp[r * LDD + ch] = to<T>(kv * gam);
-      Km[r * LDD + ch] = to<T>(kv * inv);
-      Qp[r * LDD + ch] = to<T>(qv * gam);
-      KwT[ch * LDL + r] = to<T>(wr * (kv * gam));
-      VwT[ch * LDL + r] = to<T>(wr * vv);
-      kf[i] = to<T>(kv * (tot * inv));
-    }
-#pragma unroll
-    for (int i = 0; i < RP; ++i) gKfT[ch * LC + r0 + i] = kf[i];
-    if (pid == 0) a.f.gL[ci * D + ch] = tot;
-  }
-  __syncthreads();
-
-  // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
-  constexpr int NTRI = NB * (NB + 1) / 2;
-  for (int t = wave; t < 2 * NTRI; t += kWaves) {
-    const bool isA = t < NTRI;
-    int i, j;
-    tri_index(isA ? t : t - NTRI, i, j);
-    const T* Ar = isA ? Kp : Qp;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D; kk += 32) {
-      const Frag<T> fa = load_frag(Ar + (16 * i + lr) * LDD + kk + 8 * lg);
-      const Frag<T> fb = load_frag(Km + (16 * j + lr) * LDD + kk + 8 * lg);
-      mma(acc, fa, fb);
-    }
-    const int s = 16 * j + lr;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 16 * i + 4 * lg + ii;
-      if (isA) Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
-      else Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
-    }
-  }
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
-    const int r = idx / LC, s = idx % LC;
-    if ((s >> 4) > (r >> 4)) Pb[r * LDL + s] = to<T>(0.f);
-  }
-  __syncthreads();
-
-  // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products
-  triangular_inverse<LC, LDF>(Af, Tf, scratch);
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
-    const int r = idx / LC, s = idx % LC;
-    Tb[r * LDL + s] = to<T>(Tf[r * LDF + s]);
-  }
-  __syncthreads();
-
-  // ---- WY factors: W = T Kw, Ubar = T Vw  (Kw = diag(w) K+, Vw = diag(w) V)
-  for (int t = wave; t < 2 * NB * NCT; t += kWaves) {
-    const bool isW = t < NB * NCT;
-    const int tt = isW ? t : t - NB * NCT;
-    const int i = tt / NCT, ct = tt % NCT;
-    const T* Bs = isW ? KwT : VwT;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < 16 * (i + 1); kk += 32) {
-      const Frag<T> fa = load_frag(Tb + (16 * i + lr) * LDL + kk + 8 * lg);
-      const Frag<T> fb = load_frag(Bs + (16 * ct + lr) * LDL + kk + 8 * lg);
-      mma(acc, fa, fb);
-    }
-    const int col = 16 * ct + lr, r = 16 * i + 4 * lg;
-    if (isW) {
-      const f32x4 neg = -acc;
-      store4(WnT + col * LDL + r, neg);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) gWn[(r + ii) * D + col] = to<T>(neg[ii]);
-    } else {
-      store4(UbTs + col * LDL + r, acc);
-      store4(gUbT + col * LC + r, acc);
-    }
-  }
-  __syncthreads();
-
-  // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
-  for (int t = wave; t < 2 * NB * NCT; t += kWaves) {
-    const bool isO = t < NB * NCT;
-    const int tt = isO ? t : t - NB * NCT;
-    const int i = tt / NCT, ct = tt % NCT;
-    const int col = 16 * ct + lr, r = 16 * i + 4 * lg;
-    f32x4 acc;
-    if (isO) {
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) acc[ii] = tof(Qp[(r + ii) * LDD + col]);
-    }
-    const T* Bs = isO ? UbTs : WnT;
-    for (int kk = 0; kk < 16 * (i + 1); kk += 32) {
-      const Frag<T> fa = load_frag(Pb + (16 * i + lr) * LDL + kk + 8 * lg);
-      const Frag<T> fb = load_frag(Bs + (16 * ct + lr) * LDL + kk + 8 * lg);
-      mma(acc, fa, fb);
-    }
-    if (isO) {
-      store4(gOiT + col * LC + r, acc);
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) gQt[(r + ii) * D + col] = to<T>(acc[ii]);
-    }
-  }
-}
-
-template <typename T, int LC, int D>
+template <typename T, int LC, int D, bool BWD>
 __global__ __launch_bounds__(kThreads) void fwd_prep_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, bh = blockIdx.y;
-  prep_chunk<T, LC, D>(a, TokenGates{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
+  if (a.b) prep_chunk<T, LC, D, TokenGatesB, BWD>(a, TokenGatesB{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
+  else prep_chunk<T, LC, D, TokenGates1, BWD>(a, TokenGates1{}, bh, c, (size_t)bh * a.NC + c, smem);
 }
 
 // ------------------------------------------------------------------ state step
@@ -330,11 +43,65 @@ struct StateLayout {
   static constexpr size_t bytes = sizeof(T) * (VS * LDS_ + VS * LDU) + sizeof(float) * NB * VS;
 };
 
-template <int D, int VS>
-struct StateTiles {
-  static constexpr int NVT = VS / 16, NCT = D / 16;
-  static constexpr int SPW = NCT * NVT / kWaves;   // state tiles per wave
-  static_assert(NCT * NVT % kWaves == 0, "state tiles must split evenly over waves");
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> { bf16x4 v; };
+template <> struct Raw4<float> { f32x4 v; };
+__device__ __forceinline__ Raw4<bf16> load_raw4(const bf16* p) { return Raw4<bf16>{*reinterpret_cast<const bf16x4*>(p)}; }
+__device__ __forceinline__ Raw4<float> load_raw4(const float* p) { return Raw4<float>{*reinterpret_cast<const f32x4*>(p)}; }
+__device__ __forceinline__ f32x4 widen(const Raw4<bf16>& r) {
+  return f32x4{(float)r.v[0], (float)r.v[1], (float)r.v[2], (float)r.v[3]};
+}
+__device__ __forceinline__ f32x4 widen(const Raw4<float>& r) { return r.v; }
+
+// The global operands one wave needs for one chunk.  Wave w owns the U/O tiles
+// tix = w*UPW + u (all in one row tile of the chunk) and the state tiles of
+// key tiles ct = w*SCT + j.  Loaded one chunk ahead of their use.
+template <typename T, int LC, int D, int VS, bool HAS_O>
+struct ChunkOps {
+  static constexpr int NVT = VS / 16, NB = LC / 16, NCT = D / 16;
+  static constexpr int NUO = NB * NVT;
+  static constexpr int UPW = (NUO + kWaves - 1) / kWaves;
+  static constexpr int SCT = NCT / kWaves;
+  static constexpr int KD = D / 32, KL = LC / 32;
+  static_assert(NVT % UPW == 0, "a wave's U/O tiles must share one row tile");
+  Frag<T> w[KD];
+  Frag<T> q[HAS_O ? KD : 1];
+  Raw4<T> ub[UPW];
+  Raw4<T> oi[HAS_O ? UPW : 1];
+  Frag<T> kf[SCT][KL];
+  f32x4 gl[SCT];
+
+  __device__ __forceinline__ void load(const FwdArgs& a, size_t ci, int v0) {
+    const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+    const T* Wn = reinterpret_cast<const T*>(a.f.Wn);
+    const T* Qt = reinterpret_cast<const T*>(a.f.Qt);
+    const T* KfT = reinterpret_cast<const T*>(a.f.KfT);
+    const T* UbT = reinterpret_cast<const T*>(a.f.UbT);
+    const T* OiT = reinterpret_cast<const T*>(a.f.OiT);
+    const int t0 = wave * UPW;
+    if (t0 < NUO) {
+      const int rt = t0 / NVT;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        w[kk] = load_frag(Wn + (ci * LC + 16 * rt + lr) * D + 32 * kk + 8 * lg);
+        if (HAS_O) q[kk] = load_frag(Qt + (ci * LC + 16 * rt + lr) * D + 32 * kk + 8 * lg);
+      }
+#pragma unroll
+      for (int u = 0; u < UPW; ++u) {
+        const int vt = (t0 + u) % NVT;
+        const int vg = v0 + 16 * vt + lr, r = 16 * rt + 4 * lg;
+        ub[u] = load_raw4(UbT + (ci * D + vg) * LC + r);
+        if (HAS_O) oi[u] = load_raw4(OiT + (ci * D + vg) * LC + r);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SCT; ++j) {
+      const int ct = wave * SCT + j;
+      gl[j] = load4f(a.f.gL + ci * D + 16 * ct + 4 * lg);
+#pragma unroll
+      for (int kk = 0; kk < KL; ++kk) kf[j][kk] = load_frag(KfT + (ci * D + 16 * ct + lr) * LC + 32 * kk + 8 * lg);
+    }
+  }
 };
 
 // Load the state slice (S0 or zero) into registers and its dtype copy into LDS.
@@ -354,50 +121,41 @@ __device__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTil
 }
 
 // One chunk of the state recurrence for a slice of VS value rows:
-//   U = Ubar + (-W) S^T,  O = (P Ubar) + Q~ S^T  (o written when a.o is set),
+//   U = Ubar + (-W) S^T,  O = (P Ubar) + Q~ S^T  (written when HAS_O),
 //   S^T <- Diag(Gamma_L) S^T + K->^T U.
-// Factors are read from slot ci.  On entry Sb holds the dtype copy of S; on exit
-// S and Sb hold the updated state.  If colsum is given, the per-row-tile column
-// sums of the fp32 outputs (valid tokens only) are written to colsum[NB][VS].
-template <typename T, int LC, int D, int VS>
-__device__ void state_chunk(const FwdArgs& a, int bh, int c, size_t ci, int v0,
+// Operands come from `op` (this chunk's factors).  On entry Sb holds the dtype
+// copy of S; on exit S and Sb hold the updated state.  If colsum is given, the
+// per-row-tile column sums of the fp32 outputs (valid tokens only) are written
+// to colsum[NB][VS].
+template <typename T, int LC, int D, int VS, bool HAS_O>
+__device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const ChunkOps<T, LC, D, VS, HAS_O>& op,
                             f32x4 (&S)[StateTiles<D, VS>::SPW], unsigned char* smem, float* colsum) {
   using Lay = StateLayout<T, LC, D, VS>;
+  using Op = ChunkOps<T, LC, D, VS, HAS_O>;
   using ST = StateTiles<D, VS>;
-  constexpr int NVT = ST::NVT, NB = LC / 16, SPW = ST::SPW;
-  constexpr int NUO = NB * NVT;
-  constexpr int UPW = (NUO + kWaves - 1) / kWaves;
+  constexpr int NVT = ST::NVT, SPW = ST::SPW, UPW = Op::UPW, NUO = Op::NUO;
   constexpr int LDS_ = Lay::LDS_, LDU = Lay::LDU;
   T* Sb = reinterpret_cast<T*>(smem);
   T* UT = Sb + VS * LDS_;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
-  const T* Wn = reinterpret_cast<const T*>(a.f.Wn);
-  const T* Qt = reinterpret_cast<const T*>(a.f.Qt);
-  const T* KfT = reinterpret_cast<const T*>(a.f.KfT);
-  const T* UbT = reinterpret_cast<const T*>(a.f.UbT);
-  const T* OiT = reinterpret_cast<const T*>(a.f.OiT);
   T* o = reinterpret_cast<T*>(a.o);
 
+  const int t0 = wave * UPW;
+  if (t0 < NUO) {
+    const int rt = t0 / NVT;
 #pragma unroll
-  for (int u = 0; u < UPW; ++u) {
-    const int tix = wave + kWaves * u;
-    if (tix < NUO) {
-      const int rt = tix / NVT, vt = tix % NVT;
+    for (int u = 0; u < UPW; ++u) {
+      const int vt = (t0 + u) % NVT;
       const int r = 16 * rt + 4 * lg, vl = 16 * vt + lr, vg = v0 + vl;
-      f32x4 accU = load4f(UbT + (ci * D + vg) * LC + r);
-      f32x4 accO = {0.f, 0.f, 0.f, 0.f};
-      if (a.o) accO = load4f(OiT + (ci * D + vg) * LC + r);
+      f32x4 accU = widen(op.ub[u]);
+      f32x4 accO = HAS_O ? widen(op.oi[u]) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < D; kk += 32) {
-        const Frag<T> fs = load_frag(Sb + vl * LDS_ + kk + 8 * lg);
-        const Frag<T> fw = load_frag(Wn + (ci * LC + 16 * rt + lr) * D + kk + 8 * lg);
-        mma(accU, fw, fs);
-        if (a.o) {
-          const Frag<T> fq = load_frag(Qt + (ci * LC + 16 * rt + lr) * D + kk + 8 * lg);
-          mma(accO, fq, fs);
-        }
+      for (int kk = 0; kk < Op::KD; ++kk) {
+        const Frag<T> fs = load_frag(Sb + vl * LDS_ + 32 * kk + 8 * lg);
+        mma(accU, op.w[kk], fs);
+        if (HAS_O) mma(accO, op.q[kk], fs);
       }
-      if (a.o) {
+      if (HAS_O) {
         float csum = 0.f;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
@@ -419,15 +177,14 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, size_t ci, int v0,
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    const int st = wave * SPW + j, ct = st / NVT, vt = st % NVT;
+    // wave*SPW is a multiple of NVT, so the key tile index within the wave is j / NVT
+    const int jc = j / NVT, ct = wave * Op::SCT + jc, vt = j % NVT;
     const int kc = 16 * ct + 4 * lg, vl = 16 * vt + lr;
-    const f32x4 gl = load4f(a.f.gL + ci * D + kc);
-    S[j] *= gl;
+    S[j] *= op.gl[jc];
 #pragma unroll
-    for (int kk = 0; kk < LC; kk += 32) {
-      const Frag<T> fk = load_frag(KfT + (ci * D + 16 * ct + lr) * LC + kk + 8 * lg);
-      const Frag<T> fu = load_frag(UT + vl * LDU + kk + 8 * lg);
-      mma(S[j], fk, fu);
+    for (int kk = 0; kk < Op::KL; ++kk) {
+      const Frag<T> fu = load_frag(UT + vl * LDU + 32 * kk + 8 * lg);
+      mma(S[j], op.kf[jc][kk], fu);
     }
     store4(Sb + vl * LDS_ + kc, S[j]);
   }
@@ -445,19 +202,24 @@ __device__ void state_store(const FwdArgs& a, int bh, int v0, const f32x4 (&S)[S
   }
 }
 
-template <typename T, int LC, int D, int VS>
+template <typename T, int LC, int D, int VS, bool HAS_O>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   using ST = StateTiles<D, VS>;
+  using Op = ChunkOps<T, LC, D, VS, HAS_O>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int slice = blockIdx.x, bh = blockIdx.y;
   const int v0 = slice * VS;
   f32x4 S[ST::SPW];
+  Op cur, nxt;
+  cur.load(a, (size_t)bh * a.NC, v0);
   state_init<T, D, VS>(a, bh, v0, S, reinterpret_cast<T*>(smem));
   __syncthreads();
   for (int c = 0; c < a.NC; ++c) {
     const size_t ci = (size_t)bh * a.NC + c;
+    if (c + 1 < a.NC) nxt.load(a, ci + 1, v0);
     if (a.S_chunk) state_store<T, D, VS>(a, (int)ci, v0, S, a.S_chunk);
-    state_chunk<T, LC, D, VS>(a, bh, c, ci, v0, S, smem, nullptr);
+    state_chunk<T, LC, D, VS, HAS_O>(a, bh, c, v0, cur, S, smem, nullptr);
+    cur = nxt;
   }
   if (a.S_T) state_store<T, D, VS>(a, bh, v0, S, a.S_T);
 }
@@ -544,7 +306,9 @@ __global__ __launch_bounds__(kThreads) void fwd_content_kernel(FwdArgs a, Conten
       __syncthreads();
     }
     float* cs = reinterpret_cast<float*>(smem + StateLayout<T, LC, D, D>::bytes - sizeof(float) * NB * D);
-    state_chunk<T, LC, D, D>(a, bh, c, (size_t)bh, 0, S, smem, cs);
+    ChunkOps<T, LC, D, D, true> op;
+    op.load(a, (size_t)bh, 0);
+    state_chunk<T, LC, D, D, true>(a, bh, c, 0, op, S, smem, cs);
     // fold this chunk's column sums into the period sum (fixed order over row tiles)
     const int nvalid = min(LC, a.T - c * LC);
     if (tid < D) {
@@ -578,16 +342,17 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream
 }
 
 // ------------------------------------------------------------------ launchers
-size_t factors_bytes(int dtype, int BH, int NC, int LC, int D) {
+static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {
   const size_t es = dtype ? 2 : 4;
-  const size_t nchunk = (size_t)BH * NC;
-  return nchunk * (5 * (size_t)LC * D * es + (size_t)D * 4) + 5 * 256;
+  return ((size_t)BH * NC * LC * D * es + 255) & ~size_t(255);
 }
 
-ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D) {
-  const size_t es = dtype ? 2 : 4;
-  const size_t nchunk = (size_t)BH * NC;
-  const size_t blk = (nchunk * LC * D * es + 255) & ~size_t(255);
+size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, bool bwd) {
+  return (bwd ? 6 : 5) * factor_block(dtype, BH, NC, LC, D) + (size_t)BH * NC * D * sizeof(float);
+}
+
+ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, bool bwd) {
+  const size_t blk = factor_block(dtype, BH, NC, LC, D);
   char* p = static_cast<char*>(ws);
   ChunkFactors f;
   f.Wn = p;
@@ -595,7 +360,10 @@ ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D) {
   f.KfT = p + 2 * blk;
   f.UbT = p + 3 * blk;
   f.OiT = p + 4 * blk;
-  f.gL = reinterpret_cast<float*>(p + 5 * blk);
+  f.QtT = bwd ? f.Qt : nullptr;
+  f.WnT = bwd ? f.OiT : nullptr;
+  f.Kf = bwd ? p + 5 * blk : nullptr;
+  f.gL = reinterpret_cast<float*>(p + (bwd ? 6 : 5) * blk);
   return f;
 }
 
@@ -603,7 +371,7 @@ template <typename T, int LC, int D>
 static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = PrepLayout<T, LC, D>;
   static_assert(Lay::bytes <= 160 * 1024, "prep LDS exceeds 160 KB");
-  auto kern = fwd_prep_kernel<T, LC, D>;
+  auto kern = a.bwd ? fwd_prep_kernel<T, LC, D, true> : fwd_prep_kernel<T, LC, D, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
@@ -616,9 +384,9 @@ template <typename T, int LC, int D, int VS>
 static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = StateLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 64 * 1024, "state LDS exceeds 64 KB");
-  auto kern = fwd_state_kernel<T, LC, D, VS>;
   dim3 grid(D / VS, a.B * a.H);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), Lay::bytes, st, a);
+  if (a.o) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true>), grid, dim3(kThreads), Lay::bytes, st, a);
+  else hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, false>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }
 

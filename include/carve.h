@@ -135,6 +135,40 @@ carve_status carve_bwd(const carve_shape* s,
                        void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Stage timing.  The *_ex variants behave exactly like carve_fwd / carve_bwd and
+ * additionally record caller-created HIP events (hipEvent_t handles) on
+ * `stream` at the stage boundaries: events[i] just before stage i is
+ * launched and events[i+1] just after it, for i < n_events - 1.  Nothing is
+ * synchronised; the caller reads the events afterwards (hipEventElapsedTime).
+ *   carve_fwd  stages: 0 = chunk prep (token-only) or the content-aware
+ *                      kernel (content path, single stage), 1 = state pass
+ *   carve_bwd  stages: 0 = chunk prep, 1 = forward state pass,
+ *                      2 = reverse state pass, 3 = chunk gradients
+ * With profile == NULL they are carve_fwd / carve_bwd.
+ */
+#define CARVE_MAX_STAGES 8
+typedef struct {
+  void* events[CARVE_MAX_STAGES + 1];
+  int n_events;
+} carve_profile;
+
+carve_status carve_fwd_ex(const carve_shape* s,
+                          const void* q, const void* k, const void* v,
+                          const float* log_g, const float* b, const float* w,
+                          const float* S0, const carve_content* content,
+                          void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const carve_profile* profile);
+
+carve_status carve_bwd_ex(const carve_shape* s,
+                          const void* q, const void* k, const void* v,
+                          const float* log_g, const float* b, const float* w,
+                          const float* S0, const void* dO, const float* dS_T,
+                          void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
+                          void* workspace, size_t workspace_bytes, void* stream,
+                          const carve_profile* profile);
+
 /* Human-readable name of a status code (static storage). */
 const char* carve_status_string(carve_status st);
 
