@@ -40,7 +40,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--pass", dest="passes", default="fwd+bwd", choices=["fwd+bwd", "fwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=512)
+    p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--no-content", action="store_true")
     return p.parse_args()
 
