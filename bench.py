@@ -4,11 +4,12 @@
 
 One step = one pass of the hot path over one batch of the 1.3B-head-shape
 workload (B4 H16 T4096 d128 L64, bf16 q/k/v, fp32 gates and state): the
-token-only forward (chunk prep + state pass) followed by the backward
-(recompute, reverse state pass, chunk gradients).  Inputs are synthetic and
-seeded, already resident in HBM when the timed region starts.  Prints ONE JSON
-line.  The content-aware forward of the same shape is timed separately and
-reported under "extra".
+token-only training forward (chunk prep + state pass, keeping the chunk factors
+and chunk-entry states for the backward) followed by the backward (reverse
+state pass, chunk gradients).  Inputs are synthetic and seeded, already
+resident in HBM when the timed region starts.  Prints ONE JSON line.  The plain
+(inference) forward and the content-aware forward of the same shape are timed
+separately and reported under "extra".
 
 Roofline: every stage is bracketed with HIP events on the stream it runs on
 (carve_fwd_ex / carve_bwd_ex) inside the timed region; the stage with the
@@ -95,13 +96,14 @@ def main():
     lib = carve.load_library()
     shape = carve.make_shape(q, v, wl.L)
     import ctypes
-    ws_b = torch.empty(max(1, lib.carve_bwd_workspace_size(ctypes.byref(shape))), dtype=torch.uint8, device=dev)
+    saved = torch.empty(max(1, lib.carve_saved_size(ctypes.byref(shape))), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(1, lib.carve_bwd_saved_workspace_size(ctypes.byref(shape))), dtype=torch.uint8,
+                       device=dev)
     grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
              "dlog_g": torch.empty_like(log_g), "db": torch.empty_like(b), "dw": torch.empty_like(w), "dS0": None}
 
-    n_fwd_stages, n_bwd_stages = 2, 4
     fwd_names = ["fwd_prep", "fwd_state"]
-    bwd_names = ["bwd_prep", "bwd_state_fwd", "bwd_state_rev", "bwd_chunk_grads"]
+    bwd_names = ["bwd_state_rev", "bwd_chunk_grads"]
 
     def new_events(n):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
@@ -110,17 +112,20 @@ def main():
         return evs
 
     def step(fe, be):
-        carve.fwd(q, k, v, log_g, w, b=b, L=wl.L, o=o, S_T=S_T, workspace=ws_f,
-                  profile=carve.make_profile(fe) if fe is not None else None)
         if with_bwd:
-            carve.bwd(q, k, v, log_g, w, dO, b=b, L=wl.L, want_dS0=False, workspace=ws_b, out=grads,
-                      profile=carve.make_profile(be) if be is not None else None)
+            carve.fwd_save(q, k, v, log_g, w, b=b, L=wl.L, o=o, S_T=S_T, saved=saved,
+                           profile=carve.make_profile(fe) if fe is not None else None)
+            carve.bwd_saved(q, k, v, log_g, w, dO, saved, b=b, L=wl.L, want_dS0=False, workspace=ws_b, out=grads,
+                            profile=carve.make_profile(be) if be is not None else None)
+        else:
+            carve.fwd(q, k, v, log_g, w, b=b, L=wl.L, o=o, S_T=S_T, workspace=ws_f,
+                      profile=carve.make_profile(fe) if fe is not None else None)
 
     for _ in range(args.warmup):
         step(None, None)
     torch.cuda.synchronize()
 
-    stage_evs = [(new_events(n_fwd_stages), new_events(n_bwd_stages) if with_bwd else None)
+    stage_evs = [(new_events(len(fwd_names)), new_events(len(bwd_names)) if with_bwd else None)
                  for _ in range(args.steps)]
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -140,10 +145,22 @@ def main():
             for j, name in enumerate(bwd_names):
                 stage_ms.setdefault(name, []).append(be[j].elapsed_time(be[j + 1]))
     stage_mean = {k_: float(np.mean(v_)) for k_, v_ in stage_ms.items()}
-    fwd_ms = sum(stage_mean[n] for n in fwd_names)
+
+    # plain (inference) forward: the fwd part of the metric
+    pf = [new_events(len(fwd_names)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for i in range(args.steps):
+        carve.fwd(q, k, v, log_g, w, b=b, L=wl.L, o=o, S_T=S_T, workspace=ws_f, profile=carve.make_profile(pf[i]))
+    f1.record()
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+    fwd_stage = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in pf])) for j, name in enumerate(fwd_names)}
 
     # content-aware forward of the same shape (separate timing, not part of the step)
     extra = {"stage_ms": {k_: round(v_, 4) for k_, v_ in stage_mean.items()},
+             "fwd_ms": round(fwd_ms, 4), "fwd_stage_ms": {k_: round(v_, 4) for k_, v_ in fwd_stage.items()},
              "fwd_tokens_per_s": B * T / (fwd_ms * 1e-3)}
     if not args.no_content:
         wc = WORKLOADS["content_fwd"]
@@ -177,7 +194,7 @@ def main():
     units = B * H * T
     stage_bytes = {
         "fwd_prep": alg["fwd_in"], "fwd_state": alg["fwd_out"],
-        "bwd_prep": alg["fwd_in"], "bwd_state_fwd": 0, "bwd_state_rev": es_do(wl),
+        "bwd_state_rev": es_do(wl),
         "bwd_chunk_grads": alg.get("bwd_in", 0) + alg.get("bwd_out", 0),
     }
     dom = max(stage_mean, key=stage_mean.get)

@@ -5,6 +5,6 @@
 `fwd` / `bwd` marshal torch tensors into the C ABI of libcarve.so; the
 library is loaded on first use and must be built (chunk_gated_delta_amd.build).
 """
-from .carve import fwd, bwd, load_library, fwd_workspace_bytes  # noqa: F401
+from .carve import fwd, bwd, fwd_save, bwd_saved, load_library, fwd_workspace_bytes  # noqa: F401
 
-__all__ = ["fwd", "bwd", "load_library", "fwd_workspace_bytes"]
+__all__ = ["fwd", "bwd", "fwd_save", "bwd_saved", "load_library", "fwd_workspace_bytes"]

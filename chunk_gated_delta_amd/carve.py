@@ -69,6 +69,15 @@ def load_library():
     lib.carve_bwd_ex.restype = i
     lib.carve_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.carve_bwd.restype = i
+    lib.carve_saved_size.argtypes = [sp]
+    lib.carve_saved_size.restype = sz
+    lib.carve_bwd_saved_workspace_size.argtypes = [sp]
+    lib.carve_bwd_saved_workspace_size.restype = sz
+    lib.carve_fwd_save.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
+    lib.carve_fwd_save.restype = i
+    lib.carve_bwd_saved.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                    vp, pp]
+    lib.carve_bwd_saved.restype = i
     lib.carve_status_string.argtypes = [i]
     lib.carve_status_string.restype = ctypes.c_char_p
     lib.carve_abi_version.argtypes = []
@@ -217,4 +226,71 @@ def bwd(q, k, v, log_g, w, dO, b=None, S0=None, dS_T=None, L=64, want_dS0=True, 
                             _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel(),
                             _stream(dev), ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_bwd")
+    return g
+
+
+def fwd_save(q, k, v, log_g, w, b=None, S0=None, L=64, o=None, S_T=None, saved=None, profile=None):
+    """Forward (token-only gates) that also keeps what bwd_saved needs.
+
+    Returns (o, S_T, saved); `saved` is a uint8 device buffer for bwd_saved."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(log_g, "log_g", (B, H, T, Dk), torch.float32, dev)
+    _check(b, "b", (B, H, T, Dk), torch.float32, dev)
+    _check(w, "w", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    s = make_shape(q, v, L)
+    if o is None:
+        o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    need = lib.carve_saved_size(ctypes.byref(s))
+    if saved is None or saved.numel() < need:
+        saved = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_fwd_save(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(S0),
+                              _ptr(o), _ptr(S_T), _ptr(saved), saved.numel(), _stream(dev),
+                              ctypes.byref(profile) if profile is not None else None)
+    _raise(code, "carve_fwd_save")
+    return o, S_T, saved
+
+
+def bwd_saved(q, k, v, log_g, w, dO, saved, b=None, dS_T=None, L=64, want_dS0=True, workspace=None, out=None,
+              profile=None):
+    """Backward from the buffer of fwd_save (same inputs): dict as bwd()."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(dO, "dO", (B, H, T, Dv), dt, dev)
+    _check(log_g, "log_g", (B, H, T, Dk), torch.float32, dev)
+    _check(b, "b", (B, H, T, Dk), torch.float32, dev)
+    _check(w, "w", (B, H, T), torch.float32, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    s = make_shape(q, v, L)
+    g = out if out is not None else {}
+    if out is None:
+        g["dq"] = torch.empty_like(q)
+        g["dk"] = torch.empty_like(k)
+        g["dv"] = torch.empty_like(v)
+        g["dlog_g"] = torch.empty_like(log_g)
+        g["db"] = None if b is None else torch.empty_like(b)
+        g["dw"] = torch.empty_like(w)
+        g["dS0"] = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev) if want_dS0 else None
+    need = lib.carve_bwd_saved_workspace_size(ctypes.byref(s))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_bwd_saved(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w), _ptr(dO),
+                               _ptr(dS_T), _ptr(saved), saved.numel(), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                               _ptr(g["dlog_g"]), _ptr(g["db"]), _ptr(g["dw"]), _ptr(g["dS0"]), _ptr(workspace),
+                               workspace.numel(), _stream(dev),
+                               ctypes.byref(profile) if profile is not None else None)
+    _raise(code, "carve_bwd_saved")
     return g

@@ -157,11 +157,16 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   for (int c = f.NC - 1; c >= 0; --c) {
     const size_t ci = (size_t)bh * f.NC + c;
     if (c > 0) nxt.load(a, bh, c - 1, v0);
-    // gradient w.r.t. the state leaving chunk c
+    // gradient w.r.t. the state leaving chunk c, in fragment order: scaled by this
+    // chunk's Gamma_L (rows v) and plain (rows k)
+    {
+      T* vk = reinterpret_cast<T*>(a.dSg_vk) + ci * D * D;
+      T* kv = reinterpret_cast<T*>(a.dS_kv) + ci * D * D;
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int st = wave * SPW + j, ct = st / NVT, vt = st % NVT;
-      store4(a.dS_chunk + (ci * D + v0 + 16 * vt + lr) * D + 16 * ct + 4 * lg, dS[j]);
+      for (int j = 0; j < SPW; ++j) {
+        const int jc = j / NVT, ct = wave * Op::SCT + jc, vt = j % NVT;
+        store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, dS[j] * cur.gl[jc], dS[j]);
+      }
     }
     // dO^T slice into LDS
 #pragma unroll
@@ -242,13 +247,71 @@ struct GradLayout {
   static constexpr size_t bytes = small + sizeof(float) * (LC + D + 2 * NB * LC + D);
 };
 
+// Operand sources for the column-owned products below: a fragment of rows
+// row0..row0+15 at k block k0 of a logical [rows][K] matrix.
+template <typename T, bool TR>
+struct LdsSrc {
+  const T* p;
+  int ld;
+  __device__ __forceinline__ Frag<T> operator()(int row0, int k0) const { return frag<TR>(p, ld, row0, k0); }
+};
+
+// acc[rt][j] += A[16 rt .. ][:] * B^T[16 (ct0 + j) .. ][:]  over K (multiple of 32),
+// with B fragments taken from bpre[k block][j] (already in registers).
+template <typename T, int NB, int CPW, int KB, typename ASrc>
+__device__ __forceinline__ void owned_mma(f32x4 (&acc)[NB][CPW], const ASrc& A, const Frag<T> (&bpre)[KB][CPW]) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      const Frag<T> af = A(16 * rt, 32 * kb);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) mma(acc[rt][j], af, bpre[kb][j]);
+    }
+  }
+}
+template <typename T, int NB, int CPW, int KB, typename ASrc, typename BSrc>
+__device__ __forceinline__ void owned_mma(f32x4 (&acc)[NB][CPW], const ASrc& A, const BSrc& B, int ct0) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    Frag<T> bf[CPW];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) bf[j] = B(16 * (ct0 + j), 32 * kb);
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      const Frag<T> af = A(16 * rt, 32 * kb);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) mma(acc[rt][j], af, bf[j]);
+    }
+  }
+}
+// fragments of a fragment-ordered D x D matrix for the wave's row tiles ct0 + j
+template <typename T, int D, int CPW>
+__device__ __forceinline__ void load_state_frags(Frag<T> (&dst)[D / 32][CPW], const T* base, int ct0) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) dst[kb][j] = load_frag(base + frag_offset<D>(ct0 + j, kb, lane));
+}
+template <int NB, int CPW>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[NB][CPW]) {
+#pragma unroll
+  for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
 template <typename T, int LC, int D, bool HAS_B>
-__global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   using Lay = GradLayout<T, LC, D>;
-  constexpr int NB = LC / 16, NCT = D / 16, CPW = NCT / kWaves;
+  // one wave per 16-column tile of the key/value width: NW = D/16 waves
+  constexpr int NW = D / 16, NT = 64 * NW;
+  constexpr int NB = LC / 16, NCT = D / 16, CPW = NCT / NW, KD = D / 32, KL = LC / 32;
   constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF;
   constexpr int NTRI = NB * (NB + 1) / 2;
-  static_assert(NCT % kWaves == 0, "key tiles must split evenly over waves");
+  static_assert(NCT % NW == 0, "key tiles must split evenly over waves");
   extern __shared__ __align__(16) unsigned char smem[];
   T* Kp = reinterpret_cast<T*>(smem + Lay::slot(0));
   T* Km = reinterpret_cast<T*>(smem + Lay::slot(1));
@@ -278,6 +341,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   const FwdArgs& f = a.fwd;
   const int c = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+  const int ct0 = wave * CPW;      // first key/value tile owned by this wave
   const int n = min(LC, f.T - c * LC);
   const size_t ci = (size_t)bh * f.NC + c;
   const size_t row0 = (size_t)bh * f.T + (size_t)c * LC;
@@ -285,38 +349,61 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   const T* k = reinterpret_cast<const T*>(f.k);
   const T* v = reinterpret_cast<const T*>(f.v);
   const T* dO = reinterpret_cast<const T*>(a.dO);
-  const float* S = f.S_chunk + ci * D * D;        // state entering the chunk  [v][k]
-  const float* dS = a.dS_chunk + ci * D * D;      // gradient w.r.t. the state leaving it [v][k]
+  const T* Svk = reinterpret_cast<const T*>(f.S_vk) + ci * D * D;     // state entering the chunk
+  const T* Skv = reinterpret_cast<const T*>(f.S_kv) + ci * D * D;
+  const T* dSgvk = reinterpret_cast<const T*>(a.dSg_vk) + ci * D * D; // gradient w.r.t. the state leaving it
+  const T* dSkv = reinterpret_cast<const T*>(a.dS_kv) + ci * D * D;
 
-  auto zero4 = []() { return f32x4{0.f, 0.f, 0.f, 0.f}; };
-
-  // ---- gate pass in accumulator layout: lane holds rows 16 rt + 4 lg + i of column 16 ct + lr
+  // ---- stage the chunk's raw inputs in LDS with coalesced 16-byte loads:
+  // k, q, v (dtype) in the K+, Q+, V slots; log g in slots 4-5 and b from slot 6 on
+  // (fp32, row stride D+4).  Tokens past the end read as k = q = v = 0, log g = 0, b = 1.
+  constexpr int LDG = D + 4;
+  float* lgS = reinterpret_cast<float*>(smem + Lay::slot(4));
+  float* bS = reinterpret_cast<float*>(smem + Lay::slot(6));
+  static_assert(sizeof(float) * LC * LDG <= 2 * Lay::S1, "log g staging exceeds two slots");
+  static_assert(6 * Lay::S1 + sizeof(float) * LC * LDG <= Lay::small, "b staging exceeds the slots");
   if (tid < LC) wL[tid] = (tid < n) ? f.w[row0 + min(tid, n - 1)] : 0.f;
+  {
+    constexpr int PR = D / 8;                    // 8-element pieces per token row
+    for (int idx = tid; idx < LC * PR; idx += NT) {
+      const int r = idx / PR, g = idx % PR;
+      const size_t src = (row0 + min(r, n - 1)) * D + 8 * g;
+      const bool valid = r < n;
+      const Frag<T> kx = load_frag(k + src), qx = load_frag(q + src), vx = load_frag(v + src);
+      const Frag<float> lx = load_frag(f.log_g + src);
+      Frag<float> bx = lx;
+      if (HAS_B) bx = load_frag(f.b + src);
+      *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = valid ? kx : zero_frag(T());
+      *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = valid ? qx : zero_frag(T());
+      *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? vx : zero_frag(T());
+      *reinterpret_cast<Frag<float>*>(lgS + r * LDG + 8 * g) = valid ? lx : zero_frag(float());
+      if (HAS_B) {
+        Frag<float> one;
+        one.lo = f32x4{1.f, 1.f, 1.f, 1.f};
+        one.hi = one.lo;
+        *reinterpret_cast<Frag<float>*>(bS + r * LDG + 8 * g) = valid ? bx : one;
+      }
+    }
+  }
+  __syncthreads();
+  // ---- gate pass in accumulator layout: lane holds rows 16 rt + 4 lg + i of column 16 (ct0 + j) + lr
   f32x4 gam[NB][CPW];     // cumulative retention Gamma inside the chunk
   float gLc[CPW];         // Gamma_L of the lane's columns
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
-    const int col = 16 * (wave * CPW + j) + lr;
+    const int col = 16 * (ct0 + j) + lr;
     float run = 1.f;
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt) {
-      float av[4];
+      float loc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i;
-        const size_t idx = (row0 + min(r, n - 1)) * D + col;
-        const float lgv = f.log_g[idx];
-        const float bv = HAS_B ? f.b[idx] : 1.f;
-        av[i] = (r < n) ? __expf(lgv) * bv : 1.f;
+        const float av = __expf(lgS[r * LDG + col]) * (HAS_B ? bS[r * LDG + col] : 1.f);
+        loc[i] = (i == 0) ? av : loc[i - 1] * av;
       }
-      float loc[4];
-      loc[0] = av[0];
-      loc[1] = loc[0] * av[1];
-      loc[2] = loc[1] * av[2];
-      loc[3] = loc[2] * av[3];
       // product of the 4-row groups of this row tile held by lanes with smaller lg
-      float pre = run;
-      float tile = 1.f;
+      float pre = run, tile = 1.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float tg = __shfl(loc[3], lr + 16 * g);
@@ -330,36 +417,31 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     gLc[j] = run;
     if (lg == 0) gLs[col] = run;
   }
-  // operand matrices K+, K-, Q+ and raw V in LDS
+  // operand matrices K+ (in place), K-, Q+ (in place); V stays raw
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
-    const int col = 16 * (wave * CPW + j) + lr;
+    const int col = 16 * (ct0 + j) + lr;
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
+    for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i;
-        const size_t idx = (row0 + min(r, n - 1)) * D + col;
-        const bool valid = r < n;
-        const float kv = valid ? tof(k[idx]) : 0.f;
-        const float qv = valid ? tof(q[idx]) : 0.f;
-        const float vv = valid ? tof(v[idx]) : 0.f;
+        const float kv = tof(Kp[r * LDD + col]);
+        const float qv = tof(Qp[r * LDD + col]);
         const float g = gam[rt][j][i];
         Kp[r * LDD + col] = to<T>(kv * g);
-        Km[r * LDD + col] = to<T>(kv / g);
+        Km[r * LDD + col] = to<T>(kv * rcp(g));
         Qp[r * LDD + col] = to<T>(qv * g);
-        Vr[r * LDD + col] = to<T>(vv);
       }
-    }
   }
   __syncthreads();
 
   // ---- A = strict_tril(diag(w) K+ K-^T) (fp32), P = tril(Q+ K-^T)
-  for (int t = wave; t < 2 * NTRI; t += kWaves) {
+  for (int t = wave; t < 2 * NTRI; t += NW) {
     const bool isA = t < NTRI;
     int i, j;
     tri_index(isA ? t : t - NTRI, i, j);
-    f32x4 acc = zero4();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D; kk += 32)
       mma(acc, frag<false>(isA ? Kp : Qp, LDD, 16 * i, kk), frag<false>(Km, LDD, 16 * j, kk));
@@ -371,18 +453,21 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
       else Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
     }
   }
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+  for (int idx = tid; idx < LC * LC; idx += NT) {
     const int r = idx / LC, s = idx % LC;
     if ((s >> 4) > (r >> 4)) {
       Pb[r * LDL + s] = to<T>(0.f);
       dPb[r * LDL + s] = to<T>(0.f);
     }
   }
+  // state fragments for U = Ubar - W S^T, in flight during the solve
+  Frag<T> fS[KD][CPW];
+  load_state_frags<T, D, CPW>(fS, Svk, ct0);
   __syncthreads();
 
   // ---- T = (I + A)^-1; dtype copies T and Tw = T diag(w)
-  triangular_inverse<LC, LDF>(Af, Tf, scratch);
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+  triangular_inverse<LC, LDF, NT>(Af, Tf, scratch);
+  for (int idx = tid; idx < LC * LC; idx += NT) {
     const int r = idx / LC, s = idx % LC;
     const float tv = Tf[r * LDF + s];
     Tb[r * LDL + s] = to<T>(tv);
@@ -390,122 +475,67 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- W = Tw K+ (stored negated), Ubar = Tw V (kept in registers as U's accumulator)
-  f32x4 acc2[NB][CPW];
-#pragma unroll
-  for (int kk = 0; kk < LC; kk += 32) {
-    Frag<T> bk[CPW];
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) bk[j] = frag<true>(Kp, LDD, 16 * (wave * CPW + j), kk);
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      const Frag<T> at = frag<false>(Twb, LDL, 16 * rt, kk);
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        if (kk == 0) acc2[rt][j] = zero4();
-        mma(acc2[rt][j], at, bk[j]);
-      }
-    }
-  }
-#pragma unroll
-  for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        Wn[(16 * rt + 4 * lg + ii) * LDD + 16 * (wave * CPW + j) + lr] = to<T>(-acc2[rt][j][ii]);
-  f32x4 accU[NB][CPW];
-#pragma unroll
-  for (int kk = 0; kk < LC; kk += 32) {
-    Frag<T> bv[CPW];
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) bv[j] = frag<true>(Vr, LDD, 16 * (wave * CPW + j), kk);
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      const Frag<T> at = frag<false>(Twb, LDL, 16 * rt, kk);
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        if (kk == 0) accU[rt][j] = zero4();
-        mma(accU[rt][j], at, bv[j]);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- U = Ubar + (-W) S^T  -> row-major U
-#pragma unroll
-  for (int kk = 0; kk < D; kk += 32) {
-    Frag<T> bs[CPW];
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) bs[j] = frag32<false, T>(S, D, 16 * (wave * CPW + j), kk, nullptr);
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      const Frag<T> at = frag<false>(Wn, LDD, 16 * rt, kk);
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) mma(accU[rt][j], at, bs[j]);
-    }
-  }
-#pragma unroll
-  for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        Ur[(16 * rt + 4 * lg + ii) * LDD + 16 * (wave * CPW + j) + lr] = to<T>(accU[rt][j][ii]);
-  __syncthreads();   // -W no longer needed: its slot takes dO
-
-  // ---- dO into LDS (row-major, zero for tokens past the end)
-  for (int idx = tid; idx < LC * D / 8; idx += kThreads) {
-    const int r = idx / (D / 8), g = idx % (D / 8);
-    Frag<T> x = (r < n) ? load_frag(dO + (row0 + r) * D + 8 * g) : zero_frag(T());
-    *reinterpret_cast<Frag<T>*>(dOr + r * LDD + 8 * g) = x;
-  }
-  __syncthreads();
-
-  // ---- dU = P^T dO + K- (dS' Diag(Gamma_L))^T  -> row-major dU
+  // ---- W = Tw K+ (stored negated), Ubar = Tw V (kept as U's accumulator)
   {
     f32x4 acc[NB][CPW];
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) acc[rt][j] = zero4();
-#pragma unroll
-    for (int kk = 0; kk < LC; kk += 32) {
-      Frag<T> bo[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bo[j] = frag<true>(dOr, LDD, 16 * (wave * CPW + j), kk);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<true>(Pb, LDL, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], at, bo[j]);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < D; kk += 32) {
-      Frag<T> bs[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bs[j] = frag32<false, T>(dS, D, 16 * (wave * CPW + j), kk, gLs);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<false>(Km, LDD, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], at, bs[j]);
-      }
-    }
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, false>{Twb, LDL}, LdsSrc<T, true>{Kp, LDD}, ct0);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
       for (int j = 0; j < CPW; ++j)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          dUr[(16 * rt + 4 * lg + ii) * LDD + 16 * (wave * CPW + j) + lr] = to<T>(acc[rt][j][ii]);
+          Wn[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(-acc[rt][j][ii]);
   }
+  f32x4 accU[NB][CPW];
+  zero_acc(accU);
+  owned_mma<T, NB, CPW, KL>(accU, LdsSrc<T, false>{Twb, LDL}, LdsSrc<T, true>{Vr, LDD}, ct0);
+  __syncthreads();
+
+  // ---- U = Ubar + (-W) S^T  -> row-major U
+  owned_mma<T, NB, CPW, KD>(accU, LdsSrc<T, false>{Wn, LDD}, fS);
+#pragma unroll
+  for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        Ur[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(accU[rt][j][ii]);
+  Frag<T> fG[KD][CPW];                       // dS' Diag(Gamma_L) fragments for dU
+  load_state_frags<T, D, CPW>(fG, dSgvk, ct0);
+  __syncthreads();   // -W no longer needed: its slot takes dO
+
+  // ---- dO into LDS (row-major, zero for tokens past the end)
+  for (int idx = tid; idx < LC * D / 8; idx += NT) {
+    const int r = idx / (D / 8), g = idx % (D / 8);
+    const Frag<T> x = load_frag(dO + (row0 + min(r, n - 1)) * D + 8 * g);
+    *reinterpret_cast<Frag<T>*>(dOr + r * LDD + 8 * g) = (r < n) ? x : zero_frag(T());
+  }
+  __syncthreads();
+
+  // ---- dU = P^T dO + K- (dS' Diag(Gamma_L))^T  -> row-major dU
+  {
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, true>{Pb, LDL}, LdsSrc<T, true>{dOr, LDD}, ct0);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{Km, LDD}, fG);
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          dUr[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(acc[rt][j][ii]);
+  }
+  Frag<T> fSk[KD][CPW], fDk[KD][CPW];        // S and dS' with rows k, for the key-owned products
+  load_state_frags<T, D, CPW>(fSk, Skv, ct0);
+  load_state_frags<T, D, CPW>(fDk, dSkv, ct0);
   // ---- dP = tril(dO U^T)
-  for (int t = wave; t < NTRI; t += kWaves) {
+  for (int t = wave; t < NTRI; t += NW) {
     int i, j;
     tri_index(t, i, j);
-    f32x4 acc = zero4();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D; kk += 32) mma(acc, frag<false>(dOr, LDD, 16 * i, kk), frag<false>(Ur, LDD, 16 * j, kk));
     const int s = 16 * j + lr;
@@ -517,150 +547,107 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- token x key gradients owned by this wave's columns
-  f32x4 dKacc[NB][CPW];   // dk accumulated: Gamma dK+ + dK- / Gamma + (Gamma_L / Gamma) dK->
-  f32x4 dGacc[NB][CPW];   // d G (gradient w.r.t. the cumulative log retention), per element
-  f32x4 dKm[NB][CPW];     // dK- partial
+  // ---- token x key gradients of this wave's columns, folded as they are produced into
+  //   dK = Gamma dK+ + dK- / Gamma + (Gamma_L / Gamma) dK->        (gradient w.r.t. k)
+  //   dG = K+ dK+ - K- dK- + Q+ dQ+ - K-> dK->                        (gradient w.r.t. the
+  //        cumulative log-retention, elementwise; K-> = K- Gamma_L)
+  f32x4 dK[NB][CPW], dG[NB][CPW];
   float gsum[CPW];        // sum over tokens of K-> .* dK-> per column (part of the G_L term)
-  // dQ+ = dO S + dP K-  -> dq = Gamma dQ+, dG += q dq
+  auto lds_el = [&](const T* m, int rt, int j, int ii) {
+    return tof(m[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr]);
+  };
   {
+    // dQ+ = dO S + dP K-  -> dq = Gamma dQ+, dG = Q+ dQ+
     f32x4 acc[NB][CPW];
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) acc[rt][j] = zero4();
-#pragma unroll
-    for (int kk = 0; kk < D; kk += 32) {
-      Frag<T> bs[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bs[j] = frag32<true, T>(S, D, 16 * (wave * CPW + j), kk, nullptr);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<false>(dOr, LDD, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], at, bs[j]);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < LC; kk += 32) {
-      Frag<T> bk[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bk[j] = frag<true>(Km, LDD, 16 * (wave * CPW + j), kk);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<false>(dPb, LDL, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], at, bk[j]);
-      }
-    }
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{dOr, LDD}, fSk);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, false>{dPb, LDL}, LdsSrc<T, true>{Km, LDD}, ct0);
     T* dq = reinterpret_cast<T*>(a.dq);
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int col = 16 * (wave * CPW + j) + lr;
+    for (int j = 0; j < CPW; ++j)
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
-          const float dqv = gam[rt][j][ii] * acc[rt][j][ii];
-          const float qv = (r < n) ? tof(q[(row0 + min(r, n - 1)) * D + col]) : 0.f;
-          dGacc[rt][j][ii] = qv * dqv;
-          if (r < n) dq[(row0 + r) * D + col] = to<T>(dqv);
+          dG[rt][j][ii] = lds_el(Qp, rt, j, ii) * acc[rt][j][ii];
+          if (r < n) dq[(row0 + r) * D + 16 * (ct0 + j) + lr] = to<T>(gam[rt][j][ii] * acc[rt][j][ii]);
         }
-    }
   }
-  // dK-> = U dS'  -> dk += (Gamma_L / Gamma) dK->, dG -= k (Gamma_L / Gamma) dK->
   {
+    // dK-> = U dS'  -> dK = (Gamma_L / Gamma) dK->, dG -= K-> dK->
     f32x4 acc[NB][CPW];
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) acc[rt][j] = zero4();
-#pragma unroll
-    for (int kk = 0; kk < D; kk += 32) {
-      Frag<T> bs[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bs[j] = frag32<true, T>(dS, D, 16 * (wave * CPW + j), kk, nullptr);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<false>(Ur, LDD, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], at, bs[j]);
-      }
-    }
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{Ur, LDD}, fDk);
 #pragma unroll
     for (int j = 0; j < CPW; ++j) {
-      const int col = 16 * (wave * CPW + j) + lr;
       float cs = 0.f;
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const int r = 16 * rt + 4 * lg + ii;
-          const float e3 = gLc[j] / gam[rt][j][ii] * acc[rt][j][ii];
-          const float kv = (r < n) ? tof(k[(row0 + min(r, n - 1)) * D + col]) : 0.f;
-          dKacc[rt][j][ii] = e3;
-          dGacc[rt][j][ii] -= kv * e3;
-          cs += kv * e3;
+          const float kf = lds_el(Km, rt, j, ii) * gLc[j];       // K->
+          dK[rt][j][ii] = gLc[j] * rcp(gam[rt][j][ii]) * acc[rt][j][ii];
+          dG[rt][j][ii] -= kf * acc[rt][j][ii];
+          cs += kf * acc[rt][j][ii];
         }
       gsum[j] = cs;
     }
-  }
-  // dK- (first part) = dP^T Q+
-  {
+    // G_L term of each column: sum_s K->_s dK->_s + Gamma_L sum_v S[v][k] dS'[v][k]
+    // (the lane's fragments hold S and dS' at v = 32 kb + 8 lg + e of column 16 (ct0 + j) + lr)
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
+    for (int j = 0; j < CPW; ++j) {
+      float sd = 0.f;
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) dKm[rt][j] = zero4();
+      for (int kb = 0; kb < KD; ++kb)
 #pragma unroll
-    for (int kk = 0; kk < LC; kk += 32) {
-      Frag<T> bq[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bq[j] = frag<true>(Qp, LDD, 16 * (wave * CPW + j), kk);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<true>(dPb, LDL, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(dKm[rt][j], at, bq[j]);
-      }
+        for (int e = 0; e < 8; ++e) sd += tof(frag_elem(fSk[kb][j], e)) * tof(frag_elem(fDk[kb][j], e));
+      float tot = gLc[j] * sd;
+      tot += __shfl_xor(tot, 16);
+      tot += __shfl_xor(tot, 32);
+      float gs = gsum[j];
+      gs += __shfl_xor(gs, 16);
+      gs += __shfl_xor(gs, 32);
+      if (lg == 0) glt[16 * (ct0 + j) + lr] = tot + gs;
     }
+  }
+  {
+    // dK- (first part) = dP^T Q+  -> dK += dK- / Gamma, dG -= K- dK-
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, true>{dPb, LDL}, LdsSrc<T, true>{Qp, LDD}, ct0);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          dK[rt][j][ii] += rcp(gam[rt][j][ii]) * acc[rt][j][ii];
+          dG[rt][j][ii] -= lds_el(Km, rt, j, ii) * acc[rt][j][ii];
+        }
   }
   __syncthreads();   // Q+ is dead: its slot takes dW
 
   // ---- dW = -dU S  -> row-major dW
   {
     f32x4 acc[NB][CPW];
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) acc[rt][j] = zero4();
-#pragma unroll
-    for (int kk = 0; kk < D; kk += 32) {
-      Frag<T> bs[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) bs[j] = frag32<true, T>(S, D, 16 * (wave * CPW + j), kk, nullptr);
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<false>(dUr, LDD, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], at, bs[j]);
-      }
-    }
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{dUr, LDD}, fSk);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
       for (int j = 0; j < CPW; ++j)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          dWr[(16 * rt + 4 * lg + ii) * LDD + 16 * (wave * CPW + j) + lr] = to<T>(-acc[rt][j][ii]);
+          dWr[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(-acc[rt][j][ii]);
   }
   __syncthreads();
 
   // ---- dT' = dW K+^T + dU V^T (lower tiles); dT = dT' diag(w); dw term sum_i T[i][r] dT'[i][r]
-  for (int t = wave; t < NTRI; t += kWaves) {
+  for (int t = wave; t < NTRI; t += NW) {
     int i, j;
     tri_index(t, i, j);
-    f32x4 acc = zero4();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < D; kk += 32) {
       mma(acc, frag<false>(dWr, LDD, 16 * i, kk), frag<false>(Kp, LDD, 16 * j, kk));
@@ -678,58 +665,39 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     cs += __shfl_xor(cs, 32);
     if (lg == 0) dwp[i * LC + s] = cs;
   }
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+  for (int idx = tid; idx < LC * LC; idx += NT) {
     const int r = idx / LC, s = idx % LC;
     const int it = r >> 4, jt = s >> 4;
     if (jt > it) dTb[r * LDL + s] = to<T>(0.f);
     if (jt > it) dwp[it * LC + s] = 0.f;      // tiles above the diagonal contribute nothing
   }
-  // ---- dV = Tw^T dU (write dv) and dK+ (first part) = Tw^T dW
-  f32x4 dKp[NB][CPW];
+  // ---- dV = Tw^T dU (write dv); dK+ (first part) = Tw^T dW -> dK += Gamma dK+, dG += K+ dK+
   {
-    f32x4 acc[NB][CPW];
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) { acc[rt][j] = zero4(); dKp[rt][j] = zero4(); }
-#pragma unroll
-    for (int kk = 0; kk < LC; kk += 32) {
-      Frag<T> bu[CPW], bw[CPW];
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        bu[j] = frag<true>(dUr, LDD, 16 * (wave * CPW + j), kk);
-        bw[j] = frag<true>(dWr, LDD, 16 * (wave * CPW + j), kk);
-      }
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt) {
-        const Frag<T> at = frag<true>(Twb, LDL, 16 * rt, kk);
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-          mma(acc[rt][j], at, bu[j]);
-          mma(dKp[rt][j], at, bw[j]);
-        }
-      }
-    }
+    f32x4 acc[NB][CPW], acc2[NB][CPW];
+    zero_acc(acc);
+    zero_acc(acc2);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, true>{Twb, LDL}, LdsSrc<T, true>{dUr, LDD}, ct0);
+    owned_mma<T, NB, CPW, KL>(acc2, LdsSrc<T, true>{Twb, LDL}, LdsSrc<T, true>{dWr, LDD}, ct0);
     T* dv = reinterpret_cast<T*>(a.dv);
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int col = 16 * (wave * CPW + j) + lr;
+    for (int j = 0; j < CPW; ++j)
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
-          if (r < n) dv[(row0 + r) * D + col] = to<T>(acc[rt][j][ii]);
+          if (r < n) dv[(row0 + r) * D + 16 * (ct0 + j) + lr] = to<T>(acc[rt][j][ii]);
+          dK[rt][j][ii] += gam[rt][j][ii] * acc2[rt][j][ii];
+          dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * acc2[rt][j][ii];
         }
-    }
   }
   __syncthreads();   // dT complete; dP no longer needed (its slot takes Z)
 
   // ---- Z = dT T^T (lower tiles)
-  for (int t = wave; t < NTRI; t += kWaves) {
+  for (int t = wave; t < NTRI; t += NW) {
     int i, j;
     tri_index(t, i, j);
-    f32x4 acc = zero4();
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < LC; kk += 32) mma(acc, frag<false>(dTb, LDL, 16 * i, kk), frag<false>(Tb, LDL, 16 * j, kk));
     const int s = 16 * j + lr;
@@ -739,18 +707,18 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   __syncthreads();
   // ---- dA = -T^T Z (strictly lower), dB = diag(w) dA; dw term sum_s B_rs dA_rs
   {
-    constexpr int MAXT = (NTRI + kWaves - 1) / kWaves;
+    constexpr int MAXT = (NTRI + NW - 1) / NW;
     f32x4 dA[MAXT];
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
-      const int t = wave + kWaves * u;
-      dA[u] = zero4();
+      const int t = wave + NW * u;
+      dA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (t < NTRI) {
         int i, j;
         tri_index(t, i, j);
 #pragma unroll
         for (int kk = 0; kk < LC; kk += 32) mma(dA[u], frag<true>(Tb, LDL, 16 * i, kk), frag<true>(Zb, LDL, 16 * j, kk));
-        f32x4 bacc = zero4();
+        f32x4 bacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D; kk += 32) mma(bacc, frag<false>(Kp, LDD, 16 * i, kk), frag<false>(Km, LDD, 16 * j, kk));
         const int s = 16 * j + lr;
@@ -771,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();   // every read of Z is done
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) {
-      const int t = wave + kWaves * u;
+      const int t = wave + NW * u;
       if (t < NTRI) {
         int i, j;
         tri_index(t, i, j);
@@ -783,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
         }
       }
     }
-    for (int idx = tid; idx < LC * LC; idx += kThreads) {
+    for (int idx = tid; idx < LC * LC; idx += NT) {
       const int r = idx / LC, s = idx % LC;
       const int it = r >> 4, jt = s >> 4;
       if (jt > it) {
@@ -794,71 +762,51 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- dK+ += dB K-, dK- += dB^T K+; combine everything per element
-#pragma unroll
-  for (int kk = 0; kk < LC; kk += 32) {
-    Frag<T> bm[CPW], bp[CPW];
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      bm[j] = frag<true>(Km, LDD, 16 * (wave * CPW + j), kk);
-      bp[j] = frag<true>(Kp, LDD, 16 * (wave * CPW + j), kk);
-    }
-#pragma unroll
-    for (int rt = 0; rt < NB; ++rt) {
-      const Frag<T> ab = frag<false>(dAb, LDL, 16 * rt, kk);
-      const Frag<T> abt = frag<true>(dAb, LDL, 16 * rt, kk);
-#pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        mma(dKp[rt][j], ab, bm[j]);
-        mma(dKm[rt][j], abt, bp[j]);
-      }
-    }
-  }
-  // G_L term of each column: sum_s K->_s dK->_s + Gamma_L sum_v S[v][k] dS'[v][k]
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int col = 16 * (wave * CPW + j) + lr;
-    float sd = 0.f;
-    for (int vv = lg; vv < D; vv += 4) sd += S[(size_t)vv * D + col] * dS[(size_t)vv * D + col];
-    float tot = gsum[j] + gLc[j] * sd;
-    tot += __shfl_xor(tot, 16);
-    tot += __shfl_xor(tot, 32);
-    if (lg == 0) glt[col] = tot;
-  }
+  // ---- dK+ += dB K-, dK- += dB^T K+; write dk
   {
+    f32x4 accp[NB][CPW], accm[NB][CPW];
+    zero_acc(accp);
+    zero_acc(accm);
+    owned_mma<T, NB, CPW, KL>(accp, LdsSrc<T, false>{dAb, LDL}, LdsSrc<T, true>{Km, LDD}, ct0);
+    owned_mma<T, NB, CPW, KL>(accm, LdsSrc<T, true>{dAb, LDL}, LdsSrc<T, true>{Kp, LDD}, ct0);
     T* dk = reinterpret_cast<T*>(a.dk);
 #pragma unroll
-    for (int j = 0; j < CPW; ++j) {
-      const int col = 16 * (wave * CPW + j) + lr;
+    for (int j = 0; j < CPW; ++j)
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
           const float g = gam[rt][j][ii];
-          const float e1 = g * dKp[rt][j][ii];
-          const float e2 = dKm[rt][j][ii] / g;
-          const float kv = (r < n) ? tof(k[(row0 + min(r, n - 1)) * D + col]) : 0.f;
-          const float dkv = dKacc[rt][j][ii] + e1 + e2;
-          dGacc[rt][j][ii] += kv * (e1 - e2);
-          if (r < n) dk[(row0 + r) * D + col] = to<T>(dkv);
+          dK[rt][j][ii] += g * accp[rt][j][ii] + rcp(g) * accm[rt][j][ii];
+          dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * accp[rt][j][ii] - lds_el(Km, rt, j, ii) * accm[rt][j][ii];
+          if (r < n) dk[(row0 + r) * D + 16 * (ct0 + j) + lr] = to<T>(dK[rt][j][ii]);
         }
-    }
   }
   __syncthreads();   // glt, dwp, dwq complete
 
   // ---- dlog a = reverse cumulative sum of dG over the chunk's tokens + G_L term
+  float binv[CPW][NB][4];
+  if (HAS_B) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          binv[j][rt][ii] = f.b[(row0 + min(16 * rt + 4 * lg + ii, n - 1)) * D + 16 * (ct0 + j) + lr];
+  }
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
-    const int col = 16 * (wave * CPW + j) + lr;
+    const int col = 16 * (ct0 + j) + lr;
     float run = glt[col];
 #pragma unroll
     for (int rt = NB - 1; rt >= 0; --rt) {
       float loc[4];
-      loc[3] = dGacc[rt][j][3];
-      loc[2] = loc[3] + dGacc[rt][j][2];
-      loc[1] = loc[2] + dGacc[rt][j][1];
-      loc[0] = loc[1] + dGacc[rt][j][0];
+      loc[3] = dG[rt][j][3];
+      loc[2] = loc[3] + dG[rt][j][2];
+      loc[1] = loc[2] + dG[rt][j][1];
+      loc[0] = loc[1] + dG[rt][j][0];
       float post = run, tile = 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -873,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chunk_kernel(BwdArgs a) {
           const size_t idx = (row0 + r) * D + col;
           const float dla = post + loc[ii];
           a.dlog_g[idx] = dla;
-          if (HAS_B) a.db[idx] = dla / f.b[idx];
+          if (HAS_B) a.db[idx] = dla * rcp(binv[j][rt][ii]);
         }
       }
       run += tile;
@@ -917,7 +865,7 @@ static hipError_t grad_launch(const BwdArgs& a, hipStream_t st) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
   dim3 grid(a.fwd.NC, a.fwd.B * a.fwd.H);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), Lay::bytes, st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(D * 4), Lay::bytes, st, a);
   return hipGetLastError();
 }
 

@@ -69,13 +69,31 @@ carve_status check_content(const carve_shape* s, const Plan& p, const carve_cont
 size_t fwd_ws(const carve_shape* s, const Plan& p, const carve_content* c) {
   if (p.empty) return 0;
   const int slots = c ? 1 : p.NC;   // the content kernel reuses one factor slot per head
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, slots, p.LC, p.D, false);
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, slots, p.LC, p.D, 1);
+}
+
+// one fragment-order copy of the D x D state for every chunk, in the operand type
+size_t states_bytes(const carve_shape* s, const Plan& p) {
+  return (size_t)p.BH * p.NC * p.D * p.D * (s->dtype == CARVE_BF16 ? 2 : 4);
+}
+
+// saved buffer of carve_fwd_save: factors (forward + backward layouts) and the
+// state entering every chunk (two fragment-order copies)
+size_t saved_bytes(const carve_shape* s, const Plan& p) {
+  if (p.empty) return 0;
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 3) + 2 * (states_bytes(s, p) + 256) + 256;
+}
+
+// workspace of carve_bwd_saved: the state gradients (two copies)
+size_t bwd_saved_ws(const carve_shape* s, const Plan& p) {
+  if (p.empty) return 0;
+  return 2 * (states_bytes(s, p) + 256) + 256;
 }
 
 size_t bwd_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  const size_t states = (size_t)p.BH * p.NC * p.D * p.D * sizeof(float);
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, true) + 2 * (states + 256) + 256;
+  // S and dS per chunk, two fragment-order copies each, in the operand type
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 2) + 4 * (states_bytes(s, p) + 256) + 256;
 }
 
 carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, const void* k, const void* v,
@@ -161,9 +179,10 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
     return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
   }
   carve::FwdArgs a = fwd_args(s, p, q, k, v, log_g, b, w, S0, o, S_T);
+  a.mode = 1;
   hipError_t e;
   if (content) {
-    a.f = carve::carve_factors(workspace, a.dtype, p.BH, 1, p.LC, p.D, false);
+    a.f = carve::carve_factors(workspace, a.dtype, p.BH, 1, p.LC, p.D, 1);
     carve::ContentArgs cg;
     cg.b_x = content->b_x;
     cg.U1 = content->U1;
@@ -176,7 +195,7 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
     e = carve::launch_fwd_content(a, cg, hs);
     mark(prof, 1, hs);
   } else {
-    a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, false);
+    a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, 1);
     mark(prof, 0, hs);
     e = carve::launch_fwd_prep(a, hs);
     mark(prof, 1, hs);
@@ -222,13 +241,15 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
   carve::BwdArgs a;
   memset(&a, 0, sizeof(a));
   a.fwd = fwd_args(s, p, q, k, v, log_g, b, w, S0, nullptr, nullptr);
-  a.fwd.bwd = 1;
-  a.fwd.f = carve::carve_factors(workspace, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, true);
+  a.fwd.mode = 2;
+  a.fwd.f = carve::carve_factors(workspace, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2);
   char* base = align_up(static_cast<char*>(workspace) +
-                        carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, true));
-  const size_t states = (size_t)p.BH * p.NC * p.D * p.D * sizeof(float);
-  a.fwd.S_chunk = reinterpret_cast<float*>(base);
-  a.dS_chunk = reinterpret_cast<float*>(align_up(base + states));
+                        carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2));
+  const size_t states = states_bytes(s, p);
+  a.fwd.S_vk = base;
+  a.fwd.S_kv = align_up(base + states);
+  a.dSg_vk = align_up(static_cast<char*>(a.fwd.S_kv) + states);
+  a.dS_kv = align_up(static_cast<char*>(a.dSg_vk) + states);
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -247,6 +268,105 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
   mark(prof, 3, hs);
   if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
   mark(prof, 4, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+size_t carve_saved_size(const carve_shape* s) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK) return 0;
+  return saved_bytes(s, p);
+}
+
+size_t carve_bwd_saved_workspace_size(const carve_shape* s) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK) return 0;
+  return bwd_saved_ws(s, p);
+}
+
+carve_status carve_fwd_save(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                            const float* b, const float* w, const float* S0, void* o, float* S_T, void* saved,
+                            size_t saved_bytes_given, void* stream, const carve_profile* prof) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  if (!p.empty && (!q || !k || !v || !log_g || !w || !o)) return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, (const void*)log_g, (const void*)b, (const void*)w, (const void*)S0,
+                          (const void*)o, (const void*)S_T, (const void*)saved})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need = saved_bytes(s, p);
+  if (saved_bytes_given < need || (need > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = hipSuccess;
+    if (S_T) e = carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * p.D * p.D, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::FwdArgs a = fwd_args(s, p, q, k, v, log_g, b, w, S0, o, S_T);
+  a.mode = 3;
+  a.f = carve::carve_factors(saved, a.dtype, p.BH, p.NC, p.LC, p.D, 3);
+  char* base = align_up(static_cast<char*>(saved) + carve::factors_bytes(a.dtype, p.BH, p.NC, p.LC, p.D, 3));
+  a.S_vk = base;
+  a.S_kv = align_up(base + states_bytes(s, p));
+  mark(prof, 0, hs);
+  hipError_t e = carve::launch_fwd_prep(a, hs);
+  mark(prof, 1, hs);
+  if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
+  mark(prof, 2, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k, const void* v,
+                             const float* log_g, const float* b, const float* w, const void* dO,
+                             const float* dS_T, const void* saved, size_t saved_bytes_given, void* dq, void* dk,
+                             void* dv, float* dlog_g, float* db, float* dw, float* dS0, void* workspace,
+                             size_t workspace_bytes, void* stream, const carve_profile* prof) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  if ((b == nullptr) != (db == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty) {
+    if (!q || !k || !v || !log_g || !w || !dO || !dq || !dk || !dv || !dlog_g || !dw) return CARVE_ERR_INVALID_ARG;
+  }
+  for (const void* ptr : {q, k, v, (const void*)log_g, (const void*)b, (const void*)w, dO, (const void*)dS_T,
+                          saved, (const void*)dq, (const void*)dk, (const void*)dv, (const void*)dlog_g,
+                          (const void*)db, (const void*)dw, (const void*)dS0})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need_saved = saved_bytes(s, p);
+  if (saved_bytes_given < need_saved || (need_saved > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  const size_t need = bwd_saved_ws(s, p);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = hipSuccess;
+    if (dS0) e = carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * p.D * p.D, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fwd = fwd_args(s, p, q, k, v, log_g, b, w, nullptr, nullptr, nullptr);
+  a.fwd.mode = 3;
+  void* sv = const_cast<void*>(saved);
+  a.fwd.f = carve::carve_factors(sv, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 3);
+  char* base = align_up(static_cast<char*>(sv) + carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 3));
+  const size_t states = states_bytes(s, p);
+  a.fwd.S_vk = base;
+  a.fwd.S_kv = align_up(base + states);
+  a.dSg_vk = align_up(workspace);
+  a.dS_kv = align_up(static_cast<char*>(a.dSg_vk) + states);
+  a.dO = dO;
+  a.dS_T = dS_T;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_g = dlog_g;
+  a.db = db;
+  a.dw = dw;
+  a.dS0 = dS0;
+  mark(prof, 0, hs);
+  hipError_t e = carve::launch_bwd_state(a, hs);
+  mark(prof, 1, hs);
+  if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
+  mark(prof, 2, hs);
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 

@@ -54,9 +54,10 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
 // Diagonal 16x16 blocks by column-parallel forward substitution, then the
 // off-diagonal blocks by block forward substitution on fp32 MFMA:
 //   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj,   processed by increasing i - j.
-template <int LC, int LDF>
+template <int LC, int LDF, int NT = kThreads>
 __device__ void triangular_inverse(const float* Af, float* Tf, float* scratch) {
   constexpr int NB = LC / 16;
+  static_assert(NT / 64 >= NB - 1, "one wave per off-diagonal block of a distance");
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   if (tid < 16 * NB) {
     const int base = 16 * (tid / 16), j = tid % 16;
@@ -71,7 +72,7 @@ __device__ void triangular_inverse(const float* Af, float* Tf, float* scratch) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) Tf[(base + r) * LDF + base + j] = x[r];
   }
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+  for (int idx = tid; idx < LC * LC; idx += NT) {
     const int r = idx / LC, s = idx % LC;
     if ((s >> 4) > (r >> 4)) Tf[r * LDF + s] = 0.f;
   }
@@ -131,10 +132,11 @@ struct ContentGates {
 // ------------------------------------------------------------------ per-chunk prep
 // Computes the factors of chunk c of head bh and writes them to slot `ci` of
 // the factor arrays.  Uses PrepLayout<T, LC, D>::bytes of LDS at `smem`.
-// With BWD the chunk's factors are written in the layouts the backward passes
-// need: (-W)^T, Q~^T and row-major K-> in addition to -W, K->^T, Ubar^T, Gamma_L
-// (and no Q~ / P Ubar, which only the forward output uses).
-template <typename T, int LC, int D, typename Gates, bool BWD = false>
+// MODE bit 1 writes the factors only the forward output uses (Q~ and P Ubar);
+// bit 2 writes the layouts the backward passes need ((-W)^T, Q~^T, row-major K->).
+// -W, K->^T, Ubar^T and Gamma_L are always written.
+constexpr int kPrepFwd = 1, kPrepBwd = 2;
+template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd>
 __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
                            unsigned char* smem) {
   using Lay = PrepLayout<T, LC, D>;
@@ -163,11 +165,12 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
   const T* q = reinterpret_cast<const T*>(a.q);
   const T* k = reinterpret_cast<const T*>(a.k);
   const T* v = reinterpret_cast<const T*>(a.v);
+  constexpr bool FWD = (MODE & kPrepFwd) != 0, BWD = (MODE & kPrepBwd) != 0;
   T* gWn = reinterpret_cast<T*>(a.f.Wn) + ci * LC * D;
-  T* gQt = reinterpret_cast<T*>(a.f.Qt) + ci * LC * D;
+  T* gQt = FWD ? reinterpret_cast<T*>(a.f.Qt) + ci * LC * D : nullptr;
   T* gKfT = reinterpret_cast<T*>(a.f.KfT) + ci * D * LC;
   T* gUbT = reinterpret_cast<T*>(a.f.UbT) + ci * D * LC;
-  T* gOiT = reinterpret_cast<T*>(a.f.OiT) + ci * D * LC;
+  T* gOiT = FWD ? reinterpret_cast<T*>(a.f.OiT) + ci * D * LC : nullptr;
   T* gWnT = BWD ? reinterpret_cast<T*>(a.f.WnT) + ci * D * LC : nullptr;
   T* gQtT = BWD ? reinterpret_cast<T*>(a.f.QtT) + ci * D * LC : nullptr;
   T* gKf = BWD ? reinterpret_cast<T*>(a.f.Kf) + ci * LC * D : nullptr;
@@ -302,7 +305,7 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
   __syncthreads();
 
   // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
-  for (int t = BWD ? wave + NB * NCT : wave; t < 2 * NB * NCT; t += kWaves) {
+  for (int t = FWD ? wave : wave + NB * NCT; t < 2 * NB * NCT; t += kWaves) {
     const bool isO = t < NB * NCT;
     const int tt = isO ? t : t - NB * NCT;
     const int i = tt / NCT, ct = tt % NCT;
@@ -322,11 +325,12 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
     }
     if (isO) {
       store4(gOiT + col * LC + r, acc);
-    } else if (BWD) {
-      store4(gQtT + col * LC + r, acc);
     } else {
+      if (BWD) store4(gQtT + col * LC + r, acc);
+      if (FWD) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) gQt[(r + ii) * D + col] = to<T>(acc[ii]);
+        for (int ii = 0; ii < 4; ++ii) gQt[(r + ii) * D + col] = to<T>(acc[ii]);
+      }
     }
   }
 }
@@ -341,5 +345,27 @@ struct StateTiles {
   static constexpr int SPW = NCT * NVT / kWaves;   // state tiles per wave
   static_assert(NCT * NVT % kWaves == 0, "state tiles must split evenly over waves");
 };
+
+// D x D matrices handed from the state passes to the chunk-gradient kernel are
+// stored in MFMA fragment order: fragment (rt, kb) of a [rows][contraction]
+// matrix M holds, for lane l, M[16 rt + l%16][32 kb + 8 (l/16) + j], j = 0..7, at
+// ((rt * D/32 + kb) * 64 + l) * 8, so one fragment is one coalesced 16-byte
+// (bf16) load per lane.  Two orientations of the state S[v][k] are kept:
+//   "vk": rows v, contraction k;     "kv": rows k, contraction v.
+template <int D>
+__device__ __forceinline__ size_t frag_offset(int rt, int kb, int lane) {
+  return ((size_t)(rt * (D / 32) + kb) * 64 + lane) * 8;
+}
+
+// Scatter one accumulator group (lane (lr, lg) of state tile (vt, ct): the four
+// values M[16 vt + lr][16 ct + 4 lg + i]) into both fragment layouts.
+template <typename T, int D>
+__device__ __forceinline__ void store_state_frags(T* vk, T* kv, int vt, int ct, f32x4 x_vk, f32x4 x_kv) {
+  const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
+  store4(vk + frag_offset<D>(vt, ct >> 1, lr + 16 * (2 * (ct & 1) + (lg >> 1))) + 4 * (lg & 1), x_vk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    kv[frag_offset<D>(ct, vt >> 1, (4 * lg + i) + 16 * (2 * (vt & 1) + (lr >> 3))) + (lr & 7)] = to<T>(x_kv[i]);
+}
 
 }  // namespace carve

@@ -16,10 +16,11 @@ namespace carve {
 // where Gamma is the inclusive cumulative product of a inside the chunk,
 // T = (I + A)^-1, A = strict_tril(diag(w) (K.*Gamma)(K./Gamma)^T) and
 // P = tril((Q.*Gamma)(K./Gamma)^T).
-// Backward mode adds, in the same slots where the forward-only factors would be:
-//   QtT [ci][D][LC]  Q~^T   (slot of Qt)
-//   WnT [ci][D][LC]  (-W)^T (slot of OiT)
-//   Kf  [ci][LC][D]  K->    (an extra slot)
+// The backward layouts (written when the prep mode includes the backward):
+//   QtT [ci][D][LC]  Q~^T
+//   WnT [ci][D][LC]  (-W)^T
+//   Kf  [ci][LC][D]  K->
+// Prep modes: 1 = forward only, 2 = backward only (no Qt / OiT), 3 = both.
 struct ChunkFactors {
   void* Wn;
   void* Qt;
@@ -34,7 +35,7 @@ struct ChunkFactors {
 
 struct FwdArgs {
   int B, H, T, D, LC, NC, VS;
-  int bwd;                // prep writes the backward layouts
+  int mode;               // prep mode: 1 forward, 2 backward, 3 both
   int dtype;              // 0 f32, 1 bf16
   const void* q;
   const void* k;
@@ -45,7 +46,8 @@ struct FwdArgs {
   const float* S0;        // may be null
   void* o;                // may be null (state-only pass)
   float* S_T;             // may be null
-  float* S_chunk;         // may be null: state at the start of every chunk, [ci][D][D] float
+  void* S_vk;             // may be null: state entering every chunk, fragment order, rows v (dtype)
+  void* S_kv;             // ... and rows k (both [ci][D*D], written together)
   ChunkFactors f;
 };
 
@@ -60,10 +62,11 @@ struct ContentArgs {
 };
 
 struct BwdArgs {
-  FwdArgs fwd;            // forward inputs, factors and S_chunk (all required)
+  FwdArgs fwd;            // forward inputs, factors and S_vk / S_kv (all required)
   const void* dO;
   const float* dS_T;      // may be null
-  float* dS_chunk;        // [ci][D][D] float: gradient w.r.t. the state at the END of chunk ci
+  void* dSg_vk;           // [ci][D*D] dtype: dS_{c+1} Diag(Gamma_L of chunk c), fragment order rows v
+  void* dS_kv;            // [ci][D*D] dtype: dS_{c+1}, fragment order rows k
   void* dq;
   void* dk;
   void* dv;
@@ -73,8 +76,8 @@ struct BwdArgs {
   float* dS0;             // may be null
 };
 
-size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, bool bwd);
-ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, bool bwd);
+size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode);
+ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode);
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
 hipError_t launch_fwd_prep(const FwdArgs& a, hipStream_t st);

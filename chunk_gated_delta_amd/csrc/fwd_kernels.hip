@@ -22,12 +22,12 @@
 
 namespace carve {
 
-template <typename T, int LC, int D, bool BWD>
+template <typename T, int LC, int D, int MODE>
 __global__ __launch_bounds__(kThreads) void fwd_prep_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, bh = blockIdx.y;
-  if (a.b) prep_chunk<T, LC, D, TokenGatesB, BWD>(a, TokenGatesB{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
-  else prep_chunk<T, LC, D, TokenGates1, BWD>(a, TokenGates1{}, bh, c, (size_t)bh * a.NC + c, smem);
+  if (a.b) prep_chunk<T, LC, D, TokenGatesB, MODE>(a, TokenGatesB{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
+  else prep_chunk<T, LC, D, TokenGates1, MODE>(a, TokenGates1{}, bh, c, (size_t)bh * a.NC + c, smem);
 }
 
 // ------------------------------------------------------------------ state step
@@ -217,7 +217,16 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   for (int c = 0; c < a.NC; ++c) {
     const size_t ci = (size_t)bh * a.NC + c;
     if (c + 1 < a.NC) nxt.load(a, ci + 1, v0);
-    if (a.S_chunk) state_store<T, D, VS>(a, (int)ci, v0, S, a.S_chunk);
+    if (a.S_vk) {
+      T* vk = reinterpret_cast<T*>(a.S_vk) + ci * D * D;
+      T* kv = reinterpret_cast<T*>(a.S_kv) + ci * D * D;
+      const int wave = wave_id();
+#pragma unroll
+      for (int j = 0; j < ST::SPW; ++j) {
+        const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
+        store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, S[j], S[j]);
+      }
+    }
     state_chunk<T, LC, D, VS, HAS_O>(a, bh, c, v0, cur, S, smem, nullptr);
     cur = nxt;
   }
@@ -342,28 +351,33 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream
 }
 
 // ------------------------------------------------------------------ launchers
-static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {
+static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {  // one [chunk][LC][D] block
   const size_t es = dtype ? 2 : 4;
   return ((size_t)BH * NC * LC * D * es + 255) & ~size_t(255);
 }
 
-size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, bool bwd) {
-  return (bwd ? 6 : 5) * factor_block(dtype, BH, NC, LC, D) + (size_t)BH * NC * D * sizeof(float);
+// Factor blocks in the workspace: -W, K->^T, Ubar^T always; Q~, P Ubar with the
+// forward mode; (-W)^T, Q~^T, K-> with the backward mode; then Gamma_L.
+static int factor_blocks(int mode) { return 3 + ((mode & 1) ? 2 : 0) + ((mode & 2) ? 3 : 0); }
+
+size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode) {
+  return factor_blocks(mode) * factor_block(dtype, BH, NC, LC, D) + (size_t)BH * NC * D * sizeof(float);
 }
 
-ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, bool bwd) {
+ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode) {
   const size_t blk = factor_block(dtype, BH, NC, LC, D);
   char* p = static_cast<char*>(ws);
   ChunkFactors f;
-  f.Wn = p;
-  f.Qt = p + blk;
-  f.KfT = p + 2 * blk;
-  f.UbT = p + 3 * blk;
-  f.OiT = p + 4 * blk;
-  f.QtT = bwd ? f.Qt : nullptr;
-  f.WnT = bwd ? f.OiT : nullptr;
-  f.Kf = bwd ? p + 5 * blk : nullptr;
-  f.gL = reinterpret_cast<float*>(p + (bwd ? 6 : 5) * blk);
+  int i = 0;
+  f.Wn = p + blk * i++;
+  f.KfT = p + blk * i++;
+  f.UbT = p + blk * i++;
+  f.Qt = (mode & 1) ? p + blk * i++ : nullptr;
+  f.OiT = (mode & 1) ? p + blk * i++ : nullptr;
+  f.WnT = (mode & 2) ? p + blk * i++ : nullptr;
+  f.QtT = (mode & 2) ? p + blk * i++ : nullptr;
+  f.Kf = (mode & 2) ? p + blk * i++ : nullptr;
+  f.gL = reinterpret_cast<float*>(p + blk * i);
   return f;
 }
 
@@ -371,7 +385,8 @@ template <typename T, int LC, int D>
 static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = PrepLayout<T, LC, D>;
   static_assert(Lay::bytes <= 160 * 1024, "prep LDS exceeds 160 KB");
-  auto kern = a.bwd ? fwd_prep_kernel<T, LC, D, true> : fwd_prep_kernel<T, LC, D, false>;
+  auto kern = a.mode == 3 ? fwd_prep_kernel<T, LC, D, 3>
+              : (a.mode == 2 ? fwd_prep_kernel<T, LC, D, 2> : fwd_prep_kernel<T, LC, D, 1>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;

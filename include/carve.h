@@ -169,6 +169,39 @@ carve_status carve_bwd_ex(const carve_shape* s,
                           void* workspace, size_t workspace_bytes, void* stream,
                           const carve_profile* profile);
 
+/*
+ * Training pair: a forward that keeps what its backward needs, and a backward
+ * that uses it instead of recomputing the forward (token-only gates).
+ *
+ * carve_fwd_save is carve_fwd (content = NULL) that also fills `saved`
+ * (device, caller-owned, at least carve_saved_size() bytes) with the chunk
+ * factors and the state entering every chunk.  carve_bwd_saved takes the same
+ * inputs (S0 is not needed again: it is in `saved`), dO and dS_T, the `saved`
+ * buffer of a carve_fwd_save call with the same shape and inputs (the library
+ * cannot check that the contents match), and a workspace of
+ * carve_bwd_saved_workspace_size() bytes; outputs as carve_bwd.  Stages for the
+ * profile: carve_fwd_save 0 = chunk prep, 1 = state pass; carve_bwd_saved
+ * 0 = reverse state pass, 1 = chunk gradients.
+ */
+size_t carve_saved_size(const carve_shape* s);
+size_t carve_bwd_saved_workspace_size(const carve_shape* s);
+
+carve_status carve_fwd_save(const carve_shape* s,
+                            const void* q, const void* k, const void* v,
+                            const float* log_g, const float* b, const float* w,
+                            const float* S0, void* o, float* S_T,
+                            void* saved, size_t saved_bytes, void* stream,
+                            const carve_profile* profile);
+
+carve_status carve_bwd_saved(const carve_shape* s,
+                             const void* q, const void* k, const void* v,
+                             const float* log_g, const float* b, const float* w,
+                             const void* dO, const float* dS_T,
+                             const void* saved, size_t saved_bytes,
+                             void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             const carve_profile* profile);
+
 /* Human-readable name of a status code (static storage). */
 const char* carve_status_string(carve_status st);
 

@@ -29,7 +29,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"carve_fwd", "carve_bwd", "carve_fwd_workspace_size", "carve_bwd_workspace_size",
-            "carve_status_string", "carve_abi_version"} <= set(names)
+            "carve_status_string", "carve_abi_version", "carve_fwd_ex", "carve_bwd_ex", "carve_fwd_save",
+            "carve_bwd_saved", "carve_saved_size", "carve_bwd_saved_workspace_size"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -112,3 +113,24 @@ def test_bwd_checks(lib):
     need = lib.carve_bwd_workspace_size(ctypes.byref(s))
     assert need > lib.carve_fwd_workspace_size(ctypes.byref(s), None)
     assert call_bwd(lib, s, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_saved_pair_checks(lib):
+    s = shape()
+    need = lib.carve_saved_size(ctypes.byref(s))
+    assert need > lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+    wsz = lib.carve_bwd_saved_workspace_size(ctypes.byref(s))
+    assert 0 < wsz < lib.carve_bwd_workspace_size(ctypes.byref(s))
+    # fwd_save: short saved buffer, misaligned input, missing output
+    assert lib.carve_fwd_save(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE,
+                              need - 1, None, None) == WORKSPACE
+    assert lib.carve_fwd_save(ctypes.byref(s), FAKE, FAKE + 2, FAKE, FAKE, None, FAKE, None, FAKE, None, FAKE,
+                              need, None, None) == INVALID
+    assert lib.carve_fwd_save(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE,
+                              need, None, None) == INVALID
+    # bwd_saved: short saved buffer, short workspace, db without b
+    args = lambda saved_b, ws_b, db: (ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, saved_b,
+                                      FAKE, FAKE, FAKE, FAKE, db, FAKE, None, FAKE, ws_b, None, None)
+    assert lib.carve_bwd_saved(*args(need - 1, wsz, None)) == WORKSPACE
+    assert lib.carve_bwd_saved(*args(need, wsz - 1, None)) == WORKSPACE
+    assert lib.carve_bwd_saved(*args(need, wsz, FAKE)) == INVALID

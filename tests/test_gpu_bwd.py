@@ -112,3 +112,24 @@ def test_full_train_sampled_heads():
         errs = {key: max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key]) for key in NAMES}
         print(f"  head ({bi},{hi}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
         assert all(v_ <= 2e-2 for v_ in errs.values()), errs
+
+
+def test_saved_pair_matches_recompute_bitwise():
+    """fwd_save gives the same o and S_T as fwd, and bwd_saved the same gradients as bwd
+    (the same arithmetic, only the forward is not recomputed)."""
+    announce("fwd_save / bwd_saved vs fwd / bwd")
+    for (D, dtype, T, erase) in [(128, "bf16", 200, "sigmoid"), (64, "f32", 100, "none")]:
+        inp = random_inputs(2, 2, T, D, D, dtype=dtype, seed=71 + D, erase=erase, dists="softplus_decay",
+                            with_dO=True)
+        d = to_device(inp, dtype)
+        S0 = torch.randn((2, 2, D, D), device="cuda") * 0.3
+        dS_T = torch.randn((2, 2, D, D), device="cuda") * 0.3
+        o1, s1, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d.get("b"), S0=S0)
+        o2, s2, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d.get("b"), S0=S0)
+        g1 = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=d.get("b"), S0=S0, dS_T=dS_T)
+        g2 = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=d.get("b"), dS_T=dS_T)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+        for key in NAMES:
+            if g1[key] is not None:
+                assert torch.equal(g1[key], g2[key]), (D, key)
