@@ -18,12 +18,12 @@
 namespace carve {
 
 // ------------------------------------------------------------------ helpers
-template <typename T, int LC, int D>
+template <typename T, int LC, int D, int NT = kThreads>
 struct PrepLayout {
   static constexpr int LDD = D + Pad<T>::v;      // [LC][D] row stride (elements)
   static constexpr int LDL = LC + Pad<T>::v;     // [D][LC] and [LC][LC] row stride
   static constexpr int LDF = LC + 4;             // fp32 [LC][LC] row stride
-  static constexpr int P = kThreads / D;         // token parts per key channel in the gate pass
+  static constexpr int P = NT / D;               // token parts per key channel in the gate pass
   static constexpr int RP = LC / P;              // tokens per part
   static constexpr size_t szLD = sizeof(T) * LC * LDD;
   static constexpr size_t szDL = sizeof(T) * D * LDL;
@@ -40,7 +40,7 @@ struct PrepLayout {
   static constexpr size_t R5 = R4 + al(cmax(szLLf, szDL)); // P (dtype)
   static constexpr size_t R6 = R5 + al(szLL);             // Ubar^T
   static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [P][D], T-solve scratch
-  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D + kWaves * 16 * 20));
+  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D + (NT / 64) * 16 * 20));
 };
 
 // lower-triangular block index -> (i, j), j <= i
@@ -136,10 +136,11 @@ struct ContentGates {
 // bit 2 writes the layouts the backward passes need ((-W)^T, Q~^T, row-major K->).
 // -W, K->^T, Ubar^T and Gamma_L are always written.
 constexpr int kPrepFwd = 1, kPrepBwd = 2;
-template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd>
+template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
 __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
                            unsigned char* smem) {
-  using Lay = PrepLayout<T, LC, D>;
+  using Lay = PrepLayout<T, LC, D, NT>;
+  constexpr int NW = NT / 64;
   constexpr int NB = LC / 16, NCT = D / 16;
   constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF, P = Lay::P, RP = Lay::RP;
   T* Kp = reinterpret_cast<T*>(smem + Lay::R1);
@@ -244,7 +245,7 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
 
   // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
   constexpr int NTRI = NB * (NB + 1) / 2;
-  for (int t = wave; t < 2 * NTRI; t += kWaves) {
+  for (int t = wave; t < 2 * NTRI; t += NW) {
     const bool isA = t < NTRI;
     int i, j;
     tri_index(isA ? t : t - NTRI, i, j);
@@ -264,22 +265,22 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
       else Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
     }
   }
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+  for (int idx = tid; idx < LC * LC; idx += NT) {
     const int r = idx / LC, s = idx % LC;
     if ((s >> 4) > (r >> 4)) Pb[r * LDL + s] = to<T>(0.f);
   }
   __syncthreads();
 
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products
-  triangular_inverse<LC, LDF>(Af, Tf, scratch);
-  for (int idx = tid; idx < LC * LC; idx += kThreads) {
+  triangular_inverse<LC, LDF, NT>(Af, Tf, scratch);
+  for (int idx = tid; idx < LC * LC; idx += NT) {
     const int r = idx / LC, s = idx % LC;
     Tb[r * LDL + s] = to<T>(Tf[r * LDF + s]);
   }
   __syncthreads();
 
   // ---- WY factors: W = T Kw, Ubar = T Vw  (Kw = diag(w) K+, Vw = diag(w) V)
-  for (int t = wave; t < 2 * NB * NCT; t += kWaves) {
+  for (int t = wave; t < 2 * NB * NCT; t += NW) {
     const bool isW = t < NB * NCT;
     const int tt = isW ? t : t - NB * NCT;
     const int i = tt / NCT, ct = tt % NCT;
@@ -305,7 +306,7 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
   __syncthreads();
 
   // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
-  for (int t = FWD ? wave : wave + NB * NCT; t < 2 * NB * NCT; t += kWaves) {
+  for (int t = FWD ? wave : wave + NB * NCT; t < 2 * NB * NCT; t += NW) {
     const bool isO = t < NB * NCT;
     const int tt = isO ? t : t - NB * NCT;
     const int i = tt / NCT, ct = tt % NCT;

@@ -22,12 +22,16 @@
 
 namespace carve {
 
+// threads of the chunk-prep kernel: one wave per 16 columns of the width
+template <int D> constexpr int prep_threads() { return 8 * D; }
+
 template <typename T, int LC, int D, int MODE>
-__global__ __launch_bounds__(kThreads) void fwd_prep_kernel(FwdArgs a) {
+__global__ __launch_bounds__(8 * D) void fwd_prep_kernel(FwdArgs a) {
+  constexpr int NT = prep_threads<D>();
   extern __shared__ __align__(16) unsigned char smem[];
   const int c = blockIdx.x, bh = blockIdx.y;
-  if (a.b) prep_chunk<T, LC, D, TokenGatesB, MODE>(a, TokenGatesB{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
-  else prep_chunk<T, LC, D, TokenGates1, MODE>(a, TokenGates1{}, bh, c, (size_t)bh * a.NC + c, smem);
+  if (a.b) prep_chunk<T, LC, D, TokenGatesB, MODE, NT>(a, TokenGatesB{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
+  else prep_chunk<T, LC, D, TokenGates1, MODE, NT>(a, TokenGates1{}, bh, c, (size_t)bh * a.NC + c, smem);
 }
 
 // ------------------------------------------------------------------ state step
@@ -383,7 +387,7 @@ ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, i
 
 template <typename T, int LC, int D>
 static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
-  using Lay = PrepLayout<T, LC, D>;
+  using Lay = PrepLayout<T, LC, D, prep_threads<D>()>;
   static_assert(Lay::bytes <= 160 * 1024, "prep LDS exceeds 160 KB");
   auto kern = a.mode == 3 ? fwd_prep_kernel<T, LC, D, 3>
               : (a.mode == 2 ? fwd_prep_kernel<T, LC, D, 2> : fwd_prep_kernel<T, LC, D, 1>);
@@ -391,7 +395,7 @@ static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
   dim3 grid(a.NC, a.B * a.H);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), Lay::bytes, st, a);
+  hipLaunchKernelGGL(kern, grid, dim3(prep_threads<D>()), Lay::bytes, st, a);
   return hipGetLastError();
 }
 
