@@ -138,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   T* XT = dSb + VS * LDS_;
   T* dOT = XT + VS * LDU;
   const FwdArgs& f = a.fwd;
-  const int slice = blockIdx.x, bh = blockIdx.y;
+  int bh, slice;
+  xcd_slice_map(D / VS, f.B * f.H, bh, slice);
   const int v0 = slice * VS;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
 
@@ -841,7 +842,7 @@ template <typename T, int LC, int D, int VS>
 static hipError_t rev_launch(const BwdArgs& a, hipStream_t st) {
   using Lay = RevLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 64 * 1024, "reverse-state LDS exceeds 64 KB");
-  dim3 grid(D / VS, a.fwd.B * a.fwd.H);
+  dim3 grid((D / VS) * a.fwd.B * a.fwd.H);
   hipLaunchKernelGGL((bwd_state_kernel<T, LC, D, VS>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }

@@ -337,6 +337,22 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
 }
 
 
+// Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8), each
+// with its own L2.  The value slices of one (batch, head) read the same chunk
+// factors, so they are mapped to one XCD: block b -> XCD x = b % 8, i = b / 8,
+// head bh = (i / nslices) * 8 + x, slice = i % nslices (when B*H is a multiple of 8).
+__device__ __forceinline__ void xcd_slice_map(int nslices, int BH, int& bh, int& slice) {
+  const int b = blockIdx.x;
+  if (BH % 8 == 0) {
+    const int x = b % 8, i = b / 8;
+    bh = (i / nslices) * 8 + x;
+    slice = i % nslices;
+  } else {
+    bh = b / nslices;
+    slice = b % nslices;
+  }
+}
+
 // State tiles of a workgroup holding VS value rows of a D x D state: lane l of
 // tile (ct, vt) holds S[16 vt + l%16][16 ct + 4 (l/16) + i], i = 0..3
 // (accumulator layout of S^T); wave w owns tiles w*SPW .. w*SPW+SPW-1.

@@ -211,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   using ST = StateTiles<D, VS>;
   using Op = ChunkOps<T, LC, D, VS, HAS_O>;
   extern __shared__ __align__(16) unsigned char smem[];
-  const int slice = blockIdx.x, bh = blockIdx.y;
+  int bh, slice;
+  xcd_slice_map(D / VS, a.B * a.H, bh, slice);
   const int v0 = slice * VS;
   f32x4 S[ST::SPW];
   Op cur, nxt;
@@ -403,7 +404,7 @@ template <typename T, int LC, int D, int VS>
 static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = StateLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 64 * 1024, "state LDS exceeds 64 KB");
-  dim3 grid(D / VS, a.B * a.H);
+  dim3 grid((D / VS) * a.B * a.H);
   if (a.o) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true>), grid, dim3(kThreads), Lay::bytes, st, a);
   else hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, false>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
