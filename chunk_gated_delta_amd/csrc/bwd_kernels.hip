@@ -118,9 +118,8 @@ struct RevOps {
       const int idx = threadIdx.x + kThreads * u;            // piece index: token r, column group g
       const int r = idx / (VS / VEC), g = idx % (VS / VEC);
       if (idx < LC * VS / VEC) {
-        const int rr = min(r, n - 1);
+        const int rr = min(r, n - 1);   // rows past the sequence end are zeroed where they are used
         dov[u] = load_frag(dO + ((size_t)bh * f.T + c * LC + rr) * D + v0 + VEC * g);
-        if (r >= n) dov[u] = zero_frag(T());
       }
     }
   }
@@ -152,12 +151,15 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     else dS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     store4(dSb + vl * LDS_ + kc, dS[j]);
   }
-  Op cur, nxt;
-  cur.load(a, bh, f.NC - 1, v0);
+  // three operand buffers, loaded two chunks ahead (chunks run last to first);
+  // chunks below the last one run in a branch-free main loop with clamped prefetch.
+  constexpr int PF = 3;
+  Op buf[PF];
+#pragma unroll
+  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, bh, max(f.NC - 1 - j, 0), v0);
   __syncthreads();
-  for (int c = f.NC - 1; c >= 0; --c) {
+  auto step = [&](int c, const Op& cur) {
     const size_t ci = (size_t)bh * f.NC + c;
-    if (c > 0) nxt.load(a, bh, c - 1, v0);
     // gradient w.r.t. the state leaving chunk c, in fragment order: scaled by this
     // chunk's Gamma_L (rows v) and plain (rows k)
     {
@@ -175,8 +177,9 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
       const int idx = threadIdx.x + kThreads * u;
       if (idx < LC * VS / VEC) {
         const int r = idx / (VS / VEC), g = idx % (VS / VEC);
+        const bool live = r < f.T - c * LC;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) dOT[(VEC * g + e) * LDU + r] = frag_elem(cur.dov[u], e);
+        for (int e = 0; e < VEC; ++e) dOT[(VEC * g + e) * LDU + r] = live ? frag_elem(cur.dov[u], e) : T(0.f);
       }
     }
     // X^T = K-> dS^T  (tiles [s][v])
@@ -211,7 +214,23 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
       store4(dSb + vl * LDS_ + kc, dS[j]);
     }
     __syncthreads();
-    cur = nxt;
+  };
+  const int nmain = f.NC - (f.NC % PF);     // chunks NC-1 .. NC-nmain in groups of PF
+  for (int g = 0; g < nmain; g += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int c = f.NC - 1 - (g + j);
+      buf[(j + PF - 1) % PF].load(a, bh, max(c - (PF - 1), 0), v0);
+      step(c, buf[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int c = f.NC - 1 - (nmain + j);
+    if (c >= 0) {
+      if (c - (PF - 1) >= 0) buf[(j + PF - 1) % PF].load(a, bh, c - (PF - 1), v0);
+      step(c, buf[j]);
+    }
   }
   if (a.dS0) {
 #pragma unroll

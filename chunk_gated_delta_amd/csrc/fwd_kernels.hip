@@ -131,7 +131,7 @@ __device__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTil
 // copy of S; on exit S and Sb hold the updated state.  If colsum is given, the
 // per-row-tile column sums of the fp32 outputs (valid tokens only) are written
 // to colsum[NB][VS].
-template <typename T, int LC, int D, int VS, bool HAS_O>
+template <typename T, int LC, int D, int VS, bool HAS_O, bool FULL = false>
 __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const ChunkOps<T, LC, D, VS, HAS_O>& op,
                             f32x4 (&S)[StateTiles<D, VS>::SPW], unsigned char* smem, float* colsum) {
   using Lay = StateLayout<T, LC, D, VS>;
@@ -164,7 +164,7 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int t = c * LC + r + ii;
-          if (t < a.T) {
+          if (FULL || t < a.T) {          // FULL: every token of the chunk exists
             o[((size_t)bh * a.T + t) * D + vg] = to<T>(accO[ii]);
             csum += accO[ii];
           }
@@ -206,34 +206,59 @@ __device__ void state_store(const FwdArgs& a, int bh, int v0, const f32x4 (&S)[S
   }
 }
 
-template <typename T, int LC, int D, int VS, bool HAS_O>
+// Store the state entering chunk ci in the two fragment layouts of the backward.
+template <typename T, int D, int VS>
+__device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW]) {
+  using ST = StateTiles<D, VS>;
+  T* vk = reinterpret_cast<T*>(a.S_vk) + ci * D * D;
+  T* kv = reinterpret_cast<T*>(a.S_kv) + ci * D * D;
+  const int wave = wave_id();
+#pragma unroll
+  for (int jj = 0; jj < ST::SPW; ++jj) {
+    const int st = wave * ST::SPW + jj, ct = st / ST::NVT, vt = st % ST::NVT;
+    store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, S[jj], S[jj]);
+  }
+}
+
+// The chunk loop keeps three operand buffers, so chunk c's factors are loaded two
+// chunks ahead.  Full chunks run in a branch-free main loop (prefetch indices are
+// clamped, no token checks), so the compiler's per-wave memory counters only wait
+// for the buffer in use; the last chunks run in a checked tail.
+template <typename T, int LC, int D, int VS, bool HAS_O, bool SAVE>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   using ST = StateTiles<D, VS>;
   using Op = ChunkOps<T, LC, D, VS, HAS_O>;
+  constexpr int PF = 3;
   extern __shared__ __align__(16) unsigned char smem[];
   int bh, slice;
   xcd_slice_map(D / VS, a.B * a.H, bh, slice);
   const int v0 = slice * VS;
+  const size_t c0i = (size_t)bh * a.NC;
   f32x4 S[ST::SPW];
-  Op cur, nxt;
-  cur.load(a, (size_t)bh * a.NC, v0);
+  Op buf[PF];
+#pragma unroll
+  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, c0i + min(j, a.NC - 1), v0);
   state_init<T, D, VS>(a, bh, v0, S, reinterpret_cast<T*>(smem));
   __syncthreads();
-  for (int c = 0; c < a.NC; ++c) {
-    const size_t ci = (size_t)bh * a.NC + c;
-    if (c + 1 < a.NC) nxt.load(a, ci + 1, v0);
-    if (a.S_vk) {
-      T* vk = reinterpret_cast<T*>(a.S_vk) + ci * D * D;
-      T* kv = reinterpret_cast<T*>(a.S_kv) + ci * D * D;
-      const int wave = wave_id();
+  const int nfull = (a.T % LC == 0) ? a.NC : a.NC - 1;
+  const int nmain = nfull - nfull % PF;
+  for (int c0 = 0; c0 < nmain; c0 += PF) {
 #pragma unroll
-      for (int j = 0; j < ST::SPW; ++j) {
-        const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
-        store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, S[j], S[j]);
-      }
+    for (int j = 0; j < PF; ++j) {
+      const int c = c0 + j;
+      buf[(j + PF - 1) % PF].load(a, c0i + min(c + PF - 1, a.NC - 1), v0);
+      if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S);
+      state_chunk<T, LC, D, VS, HAS_O, true>(a, bh, c, v0, buf[j], S, smem, nullptr);
     }
-    state_chunk<T, LC, D, VS, HAS_O>(a, bh, c, v0, cur, S, smem, nullptr);
-    cur = nxt;
+  }
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int c = nmain + j;
+    if (c < a.NC) {
+      if (c + PF - 1 < a.NC) buf[(j + PF - 1) % PF].load(a, c0i + c + PF - 1, v0);
+      if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S);
+      state_chunk<T, LC, D, VS, HAS_O, false>(a, bh, c, v0, buf[j], S, smem, nullptr);
+    }
   }
   if (a.S_T) state_store<T, D, VS>(a, bh, v0, S, a.S_T);
 }
@@ -405,8 +430,10 @@ static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = StateLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 64 * 1024, "state LDS exceeds 64 KB");
   dim3 grid((D / VS) * a.B * a.H);
-  if (a.o) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true>), grid, dim3(kThreads), Lay::bytes, st, a);
-  else hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, false>), grid, dim3(kThreads), Lay::bytes, st, a);
+  if (a.o && a.S_vk) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true, true>), grid, dim3(kThreads), Lay::bytes, st, a);
+  else if (a.o) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true, false>), grid, dim3(kThreads), Lay::bytes, st, a);
+  else if (a.S_vk) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, false, true>), grid, dim3(kThreads), Lay::bytes, st, a);
+  else hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, false, false>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }
 
