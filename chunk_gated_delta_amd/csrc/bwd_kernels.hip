@@ -19,12 +19,14 @@ namespace carve {
 // ------------------------------------------------------------------ fragments
 // Fragment of rows row0..row0+15 of a logical [rows][K] matrix X at k block k0:
 // TR = false: X stored row-major (X[r][k] at base[r*ld + k]);
-// TR = true : X stored transposed (X[r][k] at base[k*ld + r]).
+// TR = true : X stored transposed (X[r][k] at base[k*ld + r]); base must point into
+//             LDS (bf16 uses the LDS transpose read).
 template <bool TR, typename T>
 __device__ __forceinline__ Frag<T> frag(const T* base, int ld, int row0, int k0) {
   const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
-  if (!TR) return load_frag(base + (size_t)(row0 + lr) * ld + k0 + 8 * lg);
-  return load_frag_strided(base + (size_t)(k0 + 8 * lg) * ld + row0 + lr, ld);
+  if constexpr (!TR) return load_frag(base + (size_t)(row0 + lr) * ld + k0 + 8 * lg);
+  else if constexpr (sizeof(T) == 2) return lds_frag_tr(base, ld, row0, k0);
+  else return load_frag_strided(base + (size_t)(k0 + 8 * lg) * ld + row0 + lr, ld);
 }
 
 // Same from an fp32 matrix in global memory, converted to the operand type,

@@ -59,6 +59,29 @@ __device__ __forceinline__ Frag<float> load_frag_strided(const float* p, int str
   for (int j = 0; j < 4; ++j) { f.lo[j] = p[j * stride]; f.hi[j] = p[(j + 4) * stride]; }
   return f;
 }
+
+// Fragment of a bf16 matrix M in LDS (row stride ld elements, ld a multiple of 4,
+// M 8-byte aligned) whose 8 k values run down 8 consecutive rows:
+//   lane l receives M[k0 + 8 (l / 16) + j][c0 + l % 16], j = 0..7.
+// Two LDS transpose reads (ds_read_b64_tr_b16) replace eight 2-byte reads.  Within
+// each 16-lane group the instruction returns to lane 4a + e the element e of the
+// 4-element rows addressed by lanes a, a + 4, a + 8, a + 12 (value i from lane a + 4i);
+// so lane s of the group points at row k0 + 8 g + 4 h + s / 4, columns c0 + 4 (s % 4)
+// (h = 0 for values 0..3, h = 1 for values 4..7).  Layout checked on gfx950 with a
+// lane-layout probe.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ Frag<bf16> lds_frag_tr(const bf16* m, int ld, int c0, int k0) {
+  const int lane = lane_id(), s = lane & 15, g = lane >> 4;
+  bf16* p = const_cast<bf16*>(m) + (k0 + 8 * g + (s >> 2)) * ld + c0 + 4 * (s & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * ld));
+  const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, both);
+  return f;
+}
 __device__ __forceinline__ Frag<bf16> zero_frag(bf16) {
   Frag<bf16> f;
 #pragma unroll
