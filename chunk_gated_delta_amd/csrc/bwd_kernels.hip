@@ -246,8 +246,10 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ chunk gradients
 // LDS slots (reused as the computation proceeds; "row-major" = [token][width]):
 //   s0 K+            s1 K-            s2 Q+ -> dW        s3 V (raw)
-//   s4 A (fp32) -> -W -> dO             s5 T (fp32) -> U    s6 T-solve scratch -> dU
+//   s4 -W -> dO      s5 U             s6 dU
+//   (s4..s6 first stage the fp32 log g and b of the chunk)
 //   p0 P -> dT        p1 T (dtype)     p2 Tw = T diag(w)  p3 dP -> Z -> dA
+// T = (I + A)^-1 itself comes from the prep pass (fp32, one LC x LC block per chunk).
 // Tiles of [token][key] and [token][value] results are owned by column: wave w
 // computes every token tile of key/value tiles ct = w*CPW .. w*CPW+CPW-1, so the
 // cumulative retention Gamma of those columns stays in that wave's registers
@@ -260,8 +262,7 @@ struct GradLayout {
   static constexpr int NB = LC / 16;
   static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t al(size_t x) { return (x + 255) & ~size_t(255); }
-  static constexpr size_t S1 = al(cmax(cmax(sizeof(T) * LC * LDD, sizeof(float) * LC * LDF),
-                                      sizeof(float) * kWaves * 16 * 20));   // also holds the T-solve scratch
+  static constexpr size_t S1 = al(sizeof(T) * LC * LDD);
   static constexpr size_t S2 = al(sizeof(T) * LC * LDL);
   static constexpr size_t slot(int i) { return S1 * i; }
   static constexpr size_t pslot(int i) { return 7 * S1 + S2 * i; }
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   // one wave per 16-column tile of the key/value width: NW = D/16 waves
   constexpr int NW = D / 16, NT = 64 * NW;
   constexpr int NB = LC / 16, NCT = D / 16, CPW = NCT / NW, KD = D / 32, KL = LC / 32;
-  constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF;
+  constexpr int LDD = Lay::LDD, LDL = Lay::LDL;
   constexpr int NTRI = NB * (NB + 1) / 2;
   static_assert(NCT % NW == 0, "key tiles must split evenly over waves");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -340,12 +341,9 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   T* Qp = reinterpret_cast<T*>(smem + Lay::slot(2));
   T* dWr = Qp;
   T* Vr = reinterpret_cast<T*>(smem + Lay::slot(3));
-  float* Af = reinterpret_cast<float*>(smem + Lay::slot(4));
   T* Wn = reinterpret_cast<T*>(smem + Lay::slot(4));
   T* dOr = Wn;
-  float* Tf = reinterpret_cast<float*>(smem + Lay::slot(5));
   T* Ur = reinterpret_cast<T*>(smem + Lay::slot(5));
-  float* scratch = reinterpret_cast<float*>(smem + Lay::slot(6));
   T* dUr = reinterpret_cast<T*>(smem + Lay::slot(6));
   T* Pb = reinterpret_cast<T*>(smem + Lay::pslot(0));
   T* dTb = Pb;
@@ -384,6 +382,22 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   float* bS = reinterpret_cast<float*>(smem + Lay::slot(6));
   static_assert(sizeof(float) * LC * LDG <= 2 * Lay::S1, "log g staging exceeds two slots");
   static_assert(6 * Lay::S1 + sizeof(float) * LC * LDG <= Lay::small, "b staging exceeds the slots");
+  // dO pieces of this thread, loaded now and written to LDS once its slot is free
+  constexpr int NDO = LC * D / 8 / NT;
+  static_assert(NDO * NT * 8 == LC * D, "dO pieces must split evenly over the threads");
+  Frag<T> dOx[NDO];
+#pragma unroll
+  for (int u = 0; u < NDO; ++u) {
+    const int idx = tid + NT * u, r = idx / (D / 8), g = idx % (D / 8);
+    dOx[u] = load_frag(dO + (row0 + min(r, n - 1)) * D + 8 * g);
+  }
+  // the chunk's fp32 inverse T = (I + A)^-1 from the prep pass, 4 consecutive columns
+  // per piece (pieces past the end are clamped and not used)
+  constexpr int TP = LC * LC / 4, NTP = (TP + NT - 1) / NT;
+  f32x4 tpre[NTP];
+#pragma unroll
+  for (int u = 0; u < NTP; ++u)
+    tpre[u] = *reinterpret_cast<const f32x4*>(f.f.Tinv + ci * LC * LC + 4 * min(tid + NT * u, TP - 1));
   if (tid < LC) wL[tid] = (tid < n) ? f.w[row0 + min(tid, n - 1)] : 0.f;
   {
     constexpr int PR = D / 8;                    // 8-element pieces per token row
@@ -458,21 +472,18 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- A = strict_tril(diag(w) K+ K-^T) (fp32), P = tril(Q+ K-^T)
-  for (int t = wave; t < 2 * NTRI; t += NW) {
-    const bool isA = t < NTRI;
+  // ---- P = tril(Q+ K-^T)
+  for (int t = wave; t < NTRI; t += NW) {
     int i, j;
-    tri_index(isA ? t : t - NTRI, i, j);
+    tri_index(t, i, j);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < D; kk += 32)
-      mma(acc, frag<false>(isA ? Kp : Qp, LDD, 16 * i, kk), frag<false>(Km, LDD, 16 * j, kk));
+    for (int kk = 0; kk < D; kk += 32) mma(acc, frag<false>(Qp, LDD, 16 * i, kk), frag<false>(Km, LDD, 16 * j, kk));
     const int s = 16 * j + lr;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int r = 16 * i + 4 * lg + ii;
-      if (isA) Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
-      else Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
+      Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
     }
   }
   for (int idx = tid; idx < LC * LC; idx += NT) {
@@ -482,18 +493,21 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
       dPb[r * LDL + s] = to<T>(0.f);
     }
   }
-  // state fragments for U = Ubar - W S^T, in flight during the solve
+  // state fragments for U = Ubar - W S^T
   Frag<T> fS[KD][CPW];
   load_state_frags<T, D, CPW>(fS, Svk, ct0);
-  __syncthreads();
-
-  // ---- T = (I + A)^-1; dtype copies T and Tw = T diag(w)
-  triangular_inverse<LC, LDF, NT>(Af, Tf, scratch);
-  for (int idx = tid; idx < LC * LC; idx += NT) {
-    const int r = idx / LC, s = idx % LC;
-    const float tv = Tf[r * LDF + s];
-    Tb[r * LDL + s] = to<T>(tv);
-    Twb[r * LDL + s] = to<T>(tv * wL[s]);
+  // dtype copies of T and Tw = T diag(w)
+#pragma unroll
+  for (int u = 0; u < NTP; ++u) {
+    const int idx = tid + NT * u;
+    if (idx < TP) {
+      const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Tb[r * LDL + s + e] = to<T>(tpre[u][e]);
+        Twb[r * LDL + s + e] = to<T>(tpre[u][e] * wL[s + e]);
+      }
+    }
   }
   __syncthreads();
 
@@ -529,10 +543,10 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   __syncthreads();   // -W no longer needed: its slot takes dO
 
   // ---- dO into LDS (row-major, zero for tokens past the end)
-  for (int idx = tid; idx < LC * D / 8; idx += NT) {
-    const int r = idx / (D / 8), g = idx % (D / 8);
-    const Frag<T> x = load_frag(dO + (row0 + min(r, n - 1)) * D + 8 * g);
-    *reinterpret_cast<Frag<T>*>(dOr + r * LDD + 8 * g) = (r < n) ? x : zero_frag(T());
+#pragma unroll
+  for (int u = 0; u < NDO; ++u) {
+    const int idx = tid + NT * u, r = idx / (D / 8), g = idx % (D / 8);
+    *reinterpret_cast<Frag<T>*>(dOr + r * LDD + 8 * g) = (r < n) ? dOx[u] : zero_frag(T());
   }
   __syncthreads();
 
@@ -593,7 +607,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
           dG[rt][j][ii] = lds_el(Qp, rt, j, ii) * acc[rt][j][ii];
-          if (r < n) dq[(row0 + r) * D + 16 * (ct0 + j) + lr] = to<T>(gam[rt][j][ii] * acc[rt][j][ii]);
+          if (r < n) dq[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(gam[rt][j][ii] * acc[rt][j][ii]);
         }
   }
   {
@@ -708,7 +722,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
-          if (r < n) dv[(row0 + r) * D + 16 * (ct0 + j) + lr] = to<T>(acc[rt][j][ii]);
+          if (r < n) dv[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(acc[rt][j][ii]);
           dK[rt][j][ii] += gam[rt][j][ii] * acc2[rt][j][ii];
           dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * acc2[rt][j][ii];
         }
@@ -727,6 +741,18 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     for (int ii = 0; ii < 4; ++ii) Zb[(16 * i + 4 * lg + ii) * LDL + s] = to<T>(acc[ii]);
   }
   __syncthreads();
+  // b at the lane's gradient positions, for db = dlog a / b; loaded here so that the
+  // loads are consumed before the chunk's gradient stores are issued
+  float binv[CPW][NB][4];
+  if (HAS_B) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          binv[j][rt][ii] = f.b[row0 * D + (unsigned)(min(16 * rt + 4 * lg + ii, n - 1) * D + 16 * (ct0 + j) + lr)];
+  }
   // ---- dA = -T^T Z (strictly lower), dB = diag(w) dA; dw term sum_s B_rs dA_rs
   {
     constexpr int MAXT = (NTRI + NW - 1) / NW;
@@ -784,40 +810,35 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // ---- dK+ += dB K-, dK- += dB^T K+; write dk
-  {
-    f32x4 accp[NB][CPW], accm[NB][CPW];
-    zero_acc(accp);
-    zero_acc(accm);
-    owned_mma<T, NB, CPW, KL>(accp, LdsSrc<T, false>{dAb, LDL}, LdsSrc<T, true>{Km, LDD}, ct0);
-    owned_mma<T, NB, CPW, KL>(accm, LdsSrc<T, true>{dAb, LDL}, LdsSrc<T, true>{Kp, LDD}, ct0);
-    T* dk = reinterpret_cast<T*>(a.dk);
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-#pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int r = 16 * rt + 4 * lg + ii;
-          const float g = gam[rt][j][ii];
-          dK[rt][j][ii] += g * accp[rt][j][ii] + rcp(g) * accm[rt][j][ii];
-          dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * accp[rt][j][ii] - lds_el(Km, rt, j, ii) * accm[rt][j][ii];
-          if (r < n) dk[(row0 + r) * D + 16 * (ct0 + j) + lr] = to<T>(dK[rt][j][ii]);
-        }
-  }
-  __syncthreads();   // glt, dwp, dwq complete
-
-  // ---- dlog a = reverse cumulative sum of dG over the chunk's tokens + G_L term
-  float binv[CPW][NB][4];
   if (HAS_B) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          binv[j][rt][ii] = f.b[(row0 + min(16 * rt + 4 * lg + ii, n - 1)) * D + 16 * (ct0 + j) + lr];
+        for (int ii = 0; ii < 4; ++ii) binv[j][rt][ii] = rcp(binv[j][rt][ii]);
   }
+  // ---- dK+ += dB K-, dK- += dB^T K+
+  {
+    f32x4 accp[NB][CPW], accm[NB][CPW];
+    zero_acc(accp);
+    zero_acc(accm);
+    owned_mma<T, NB, CPW, KL>(accp, LdsSrc<T, false>{dAb, LDL}, LdsSrc<T, true>{Km, LDD}, ct0);
+    owned_mma<T, NB, CPW, KL>(accm, LdsSrc<T, true>{dAb, LDL}, LdsSrc<T, true>{Kp, LDD}, ct0);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float g = gam[rt][j][ii];
+          dK[rt][j][ii] += g * accp[rt][j][ii] + rcp(g) * accm[rt][j][ii];
+          dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * accp[rt][j][ii] - lds_el(Km, rt, j, ii) * accm[rt][j][ii];
+        }
+  }
+  __syncthreads();   // glt, dwp, dwq complete
+
+  // ---- dlog a = reverse cumulative sum of dG over the chunk's tokens + G_L term
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int col = 16 * (ct0 + j) + lr;
@@ -840,14 +861,26 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
       for (int ii = 0; ii < 4; ++ii) {
         const int r = 16 * rt + 4 * lg + ii;
         if (r < n) {
-          const size_t idx = (row0 + r) * D + col;
+          const size_t idx = row0 * D + (unsigned)(r * D + col);
           const float dla = post + loc[ii];
           a.dlog_g[idx] = dla;
-          if (HAS_B) a.db[idx] = dla * rcp(binv[j][rt][ii]);
+          if (HAS_B) a.db[idx] = dla * binv[j][rt][ii];
         }
       }
       run += tile;
     }
+  }
+  {
+    T* dk = reinterpret_cast<T*>(a.dk);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * rt + 4 * lg + ii;
+          if (r < n) dk[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(dK[rt][j][ii]);
+        }
   }
   // ---- dw_r = sum_s B_rs dA_rs + sum_i T[i][r] dT'[i][r]
   if (tid < LC && tid < n) {

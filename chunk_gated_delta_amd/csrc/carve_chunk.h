@@ -271,11 +271,15 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
   }
   __syncthreads();
 
-  // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products
+  // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
+  // modes also keep the fp32 T of the chunk
   triangular_inverse<LC, LDF, NT>(Af, Tf, scratch);
-  for (int idx = tid; idx < LC * LC; idx += NT) {
-    const int r = idx / LC, s = idx % LC;
-    Tb[r * LDL + s] = to<T>(Tf[r * LDF + s]);
+  for (int idx = tid; idx < LC * LC / 4; idx += NT) {
+    const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
+    const f32x4 t4 = *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Tb[r * LDL + s + e] = to<T>(t4[e]);
+    if (BWD) *reinterpret_cast<f32x4*>(a.f.Tinv + (ci * LC + r) * LC + s) = t4;
   }
   __syncthreads();
 

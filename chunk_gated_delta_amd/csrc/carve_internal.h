@@ -20,6 +20,7 @@ namespace carve {
 //   QtT [ci][D][LC]  Q~^T
 //   WnT [ci][D][LC]  (-W)^T
 //   Kf  [ci][LC][D]  K->
+//   Tinv [ci][LC][LC] T = (I + A)^-1, fp32
 // Prep modes: 1 = forward only, 2 = backward only (no Qt / OiT), 3 = both.
 struct ChunkFactors {
   void* Wn;
@@ -31,6 +32,7 @@ struct ChunkFactors {
   void* QtT;
   void* WnT;
   void* Kf;
+  float* Tinv;            // [ci][LC][LC] T = (I + A)^-1 in fp32 (backward modes)
 };
 
 struct FwdArgs {
