@@ -382,43 +382,50 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   float* bS = reinterpret_cast<float*>(smem + Lay::slot(6));
   static_assert(sizeof(float) * LC * LDG <= 2 * Lay::S1, "log g staging exceeds two slots");
   static_assert(6 * Lay::S1 + sizeof(float) * LC * LDG <= Lay::small, "b staging exceeds the slots");
-  // dO pieces of this thread, loaded now and written to LDS once its slot is free
-  constexpr int NDO = LC * D / 8 / NT;
-  static_assert(NDO * NT * 8 == LC * D, "dO pieces must split evenly over the threads");
-  Frag<T> dOx[NDO];
+  // All of the chunk's global loads are issued here, from clamped rows (n >= 1), before
+  // anything waits on them: the staged inputs, dO (written to LDS once its slot is
+  // free), the chunk's fp32 inverse T = (I + A)^-1 from the prep pass, and w.
+  constexpr int PR = D / 8;                      // 8-element pieces per token row
+  constexpr int NST = LC * PR / NT;              // pieces per thread
+  static_assert(NST * NT == LC * PR, "pieces must split evenly over the threads");
+  const float wv = f.w[row0 + min(tid, n - 1)];
+  Frag<T> kx[NST], qx[NST], vx[NST], dOx[NST];
+  Frag<float> lx[NST], bx[NST];
 #pragma unroll
-  for (int u = 0; u < NDO; ++u) {
-    const int idx = tid + NT * u, r = idx / (D / 8), g = idx % (D / 8);
-    dOx[u] = load_frag(dO + (row0 + min(r, n - 1)) * D + 8 * g);
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    const size_t src = row0 * D + (unsigned)(min(r, n - 1) * D + 8 * g);
+    kx[u] = load_frag(k + src);
+    qx[u] = load_frag(q + src);
+    vx[u] = load_frag(v + src);
+    lx[u] = load_frag(f.log_g + src);
+    if (HAS_B) bx[u] = load_frag(f.b + src);
+    dOx[u] = load_frag(dO + src);
   }
-  // the chunk's fp32 inverse T = (I + A)^-1 from the prep pass, 4 consecutive columns
-  // per piece (pieces past the end are clamped and not used)
-  constexpr int TP = LC * LC / 4, NTP = (TP + NT - 1) / NT;
+  constexpr int TP = LC * LC / 4, NTP = (TP + NT - 1) / NT;   // 4 consecutive columns per piece
   f32x4 tpre[NTP];
 #pragma unroll
   for (int u = 0; u < NTP; ++u)
     tpre[u] = *reinterpret_cast<const f32x4*>(f.f.Tinv + ci * LC * LC + 4 * min(tid + NT * u, TP - 1));
-  if (tid < LC) wL[tid] = (tid < n) ? f.w[row0 + min(tid, n - 1)] : 0.f;
-  {
-    constexpr int PR = D / 8;                    // 8-element pieces per token row
-    for (int idx = tid; idx < LC * PR; idx += NT) {
-      const int r = idx / PR, g = idx % PR;
-      const size_t src = (row0 + min(r, n - 1)) * D + 8 * g;
-      const bool valid = r < n;
-      const Frag<T> kx = load_frag(k + src), qx = load_frag(q + src), vx = load_frag(v + src);
-      const Frag<float> lx = load_frag(f.log_g + src);
-      Frag<float> bx = lx;
-      if (HAS_B) bx = load_frag(f.b + src);
-      *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = valid ? kx : zero_frag(T());
-      *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = valid ? qx : zero_frag(T());
-      *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? vx : zero_frag(T());
-      *reinterpret_cast<Frag<float>*>(lgS + r * LDG + 8 * g) = valid ? lx : zero_frag(float());
-      if (HAS_B) {
-        Frag<float> one;
-        one.lo = f32x4{1.f, 1.f, 1.f, 1.f};
-        one.hi = one.lo;
-        *reinterpret_cast<Frag<float>*>(bS + r * LDG + 8 * g) = valid ? bx : one;
-      }
+  // k, q, v (dtype) into the K+, Q+, V slots; log g into slots 4-5 and b from slot 6 on
+  // (fp32, row stride D+4).  Tokens past the end read as k = q = v = 0, log g = 0, b = 1.
+  if (tid < LC) wL[tid] = (tid < n) ? wv : 0.f;
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    const bool valid = r < n;
+    *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = valid ? kx[u] : zero_frag(T());
+    *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = valid ? qx[u] : zero_frag(T());
+    *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? vx[u] : zero_frag(T());
+    Frag<float> lw = lx[u];
+    lw.lo = valid ? lw.lo : f32x4{0.f, 0.f, 0.f, 0.f};
+    lw.hi = valid ? lw.hi : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<Frag<float>*>(lgS + r * LDG + 8 * g) = lw;
+    if (HAS_B) {
+      Frag<float> bw = bx[u];
+      bw.lo = valid ? bw.lo : f32x4{1.f, 1.f, 1.f, 1.f};
+      bw.hi = valid ? bw.hi : f32x4{1.f, 1.f, 1.f, 1.f};
+      *reinterpret_cast<Frag<float>*>(bS + r * LDG + 8 * g) = bw;
     }
   }
   __syncthreads();
@@ -544,8 +551,8 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 
   // ---- dO into LDS (row-major, zero for tokens past the end)
 #pragma unroll
-  for (int u = 0; u < NDO; ++u) {
-    const int idx = tid + NT * u, r = idx / (D / 8), g = idx % (D / 8);
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
     *reinterpret_cast<Frag<T>*>(dOr + r * LDD + 8 * g) = (r < n) ? dOx[u] : zero_frag(T());
   }
   __syncthreads();
