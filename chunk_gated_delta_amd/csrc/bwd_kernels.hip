@@ -12,6 +12,8 @@
 //      the coupling's dB, then the key-axis retention through a reverse cumulative
 //      sum of dlog a inside the chunk).
 // Gradients are w.r.t. log g, the erase probability b and the write strength w.
+#include <type_traits>
+
 #include "carve_chunk.h"
 
 namespace carve {
@@ -782,11 +784,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
           const int r = 16 * i + 4 * lg + ii;
           const float da = (s < r) ? -dA[u][ii] : 0.f;
           dA[u][ii] = da;
-          float rs = bacc[ii] * da;
-          rs += __shfl_xor(rs, 1);
-          rs += __shfl_xor(rs, 2);
-          rs += __shfl_xor(rs, 4);
-          rs += __shfl_xor(rs, 8);
+          const float rs = row16_sum(bacc[ii] * da);
           if (lr == 0) dwq[j * LC + r] = rs;
         }
       }
@@ -865,19 +863,12 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
         tile += tg;
       }
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int r = 16 * rt + 4 * lg + ii;
-        if (r < n) {
-          const size_t idx = row0 * D + (unsigned)(r * D + col);
-          const float dla = post + loc[ii];
-          a.dlog_g[idx] = dla;
-          if (HAS_B) a.db[idx] = dla * binv[j][rt][ii];
-        }
-      }
+      for (int ii = 0; ii < 4; ++ii) dG[rt][j][ii] = post + loc[ii];    // dlog a
       run += tile;
     }
   }
-  {
+  // gradient stores; a full chunk stores without per-element token checks
+  auto store_grads = [&](auto full) {
     T* dk = reinterpret_cast<T*>(a.dk);
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
@@ -886,9 +877,16 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
-          if (r < n) dk[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(dK[rt][j][ii]);
+          if (decltype(full)::value || r < n) {
+            const size_t idx = row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr);
+            a.dlog_g[idx] = dG[rt][j][ii];
+            if (HAS_B) a.db[idx] = dG[rt][j][ii] * binv[j][rt][ii];
+            dk[idx] = to<T>(dK[rt][j][ii]);
+          }
         }
-  }
+  };
+  if (n == LC) store_grads(std::true_type{});
+  else store_grads(std::false_type{});
   // ---- dw_r = sum_s B_rs dA_rs + sum_i T[i][r] dT'[i][r]
   if (tid < LC && tid < n) {
     float s = 0.f;
