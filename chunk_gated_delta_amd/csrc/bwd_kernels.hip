@@ -27,8 +27,7 @@ template <bool TR, typename T>
 __device__ __forceinline__ Frag<T> frag(const T* base, int ld, int row0, int k0) {
   const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
   if constexpr (!TR) return load_frag(base + (size_t)(row0 + lr) * ld + k0 + 8 * lg);
-  else if constexpr (sizeof(T) == 2) return lds_frag_tr(base, ld, row0, k0);
-  else return load_frag_strided(base + (size_t)(k0 + 8 * lg) * ld + row0 + lr, ld);
+  else return lds_frag_cols(base, ld, row0, k0);
 }
 
 // Same from an fp32 matrix in global memory, converted to the operand type,
@@ -172,8 +171,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
         const int jc = j / NVT, ct = wave * Op::SCT + jc, vt = j % NVT;
-        store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, dS[j] * cur.gl[jc], dS[j]);
+        if constexpr (kWideSlice<VS>) store_vk_group<T, D>(vk, v0 / 16 + vt, ct, dS[j] * cur.gl[jc]);
+        else store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, dS[j] * cur.gl[jc], dS[j]);
       }
+      // the plain copy's "kv" fragments come out of dSb, which holds dS in the dtype
+      if constexpr (kWideSlice<VS>) store_kv_from_lds<T, D, VS, kWaves>(kv, dSb, LDS_, v0);
     }
     // dO^T slice into LDS
 #pragma unroll

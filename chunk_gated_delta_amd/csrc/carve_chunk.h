@@ -381,12 +381,34 @@ __device__ __forceinline__ size_t frag_offset(int rt, int kb, int lane) {
 // Scatter one accumulator group (lane (lr, lg) of state tile (vt, ct): the four
 // values M[16 vt + lr][16 ct + 4 lg + i]) into both fragment layouts.
 template <typename T, int D>
-__device__ __forceinline__ void store_state_frags(T* vk, T* kv, int vt, int ct, f32x4 x_vk, f32x4 x_kv) {
+__device__ __forceinline__ void store_vk_group(T* vk, int vt, int ct, f32x4 x_vk) {
   const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
   store4(vk + frag_offset<D>(vt, ct >> 1, lr + 16 * (2 * (ct & 1) + (lg >> 1))) + 4 * (lg & 1), x_vk);
+}
+template <typename T, int D>
+__device__ __forceinline__ void store_state_frags(T* vk, T* kv, int vt, int ct, f32x4 x_vk, f32x4 x_kv) {
+  const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
+  store_vk_group<T, D>(vk, vt, ct, x_vk);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     kv[frag_offset<D>(ct, vt >> 1, (4 * lg + i) + 16 * (2 * (vt & 1) + (lr >> 3))) + (lr & 7)] = to<T>(x_kv[i]);
+}
+
+// Value slices of 32 or more rows copy whole "kv" fragments (and outputs) out of
+// their LDS copies with 16-byte stores (a fragment spans 32 rows of the slice).
+template <int VS> constexpr bool kWideSlice = VS >= 32;
+
+// "kv" fragments of a slice of rows v0..v0+VS-1 (VS a multiple of 32) of S[v][k],
+// from its row-major LDS copy Sb (row stride ld); one 16-byte store per lane each.
+template <typename T, int D, int VS, int NWAVES>
+__device__ __forceinline__ void store_kv_from_lds(T* kv, const T* Sb, int ld, int v0) {
+  const int lane = lane_id(), wave = wave_id();
+#pragma unroll
+  for (int f = wave; f < (D / 16) * (VS / 32); f += NWAVES) {
+    const int kt = f / (VS / 32), vb = f % (VS / 32);
+    const Frag<T> x = lds_frag_cols(Sb, ld, 16 * kt, 32 * vb);
+    *reinterpret_cast<Frag<T>*>(kv + frag_offset<D>(kt, v0 / 32 + vb, lane)) = x;
+  }
 }
 
 }  // namespace carve

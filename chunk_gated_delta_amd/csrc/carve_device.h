@@ -92,6 +92,14 @@ __device__ __forceinline__ Frag<bf16> lds_frag_tr(const bf16* m, int ld, int c0,
   f.v = __builtin_bit_cast(bf16x8, both);
   return f;
 }
+// The same fragment for either operand type (fp32: eight strided LDS reads).
+__device__ __forceinline__ Frag<bf16> lds_frag_cols(const bf16* m, int ld, int c0, int k0) {
+  return lds_frag_tr(m, ld, c0, k0);
+}
+__device__ __forceinline__ Frag<float> lds_frag_cols(const float* m, int ld, int c0, int k0) {
+  const int lane = lane_id();
+  return load_frag_strided(m + (k0 + 8 * (lane >> 4)) * ld + c0 + (lane & 15), ld);
+}
 __device__ __forceinline__ Frag<bf16> zero_frag(bf16) {
   Frag<bf16> f;
 #pragma unroll

@@ -44,8 +44,10 @@ struct StateLayout {
   static constexpr int LDS_ = D + Pad<T>::v;
   static constexpr int LDU = LC + Pad<T>::v;
   static constexpr int NB = LC / 16, NVT = VS / 16;
-  static constexpr size_t bytes = sizeof(T) * (VS * LDS_ + VS * LDU) + sizeof(float) * NB * VS;
+  // Sb [VS][LDS_] dtype state, UT [VS][LDU] U^T, OT [VS][LDU] O^T, colsum [NB][VS]
+  static constexpr size_t bytes = sizeof(T) * (VS * LDS_ + 2 * VS * LDU) + sizeof(float) * NB * VS;
 };
+
 
 template <typename T> struct Raw4;
 template <> struct Raw4<bf16> { bf16x4 v; };
@@ -141,8 +143,10 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
   constexpr int LDS_ = Lay::LDS_, LDU = Lay::LDU;
   T* Sb = reinterpret_cast<T*>(smem);
   T* UT = Sb + VS * LDS_;
+  T* OT = UT + VS * LDU;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
   T* o = reinterpret_cast<T*>(a.o);
+  constexpr bool WIDE = kWideSlice<VS>;
 
   const int t0 = wave * UPW;
   if (t0 < NUO) {
@@ -161,11 +165,12 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
       }
       if (HAS_O) {
         float csum = 0.f;
+        if (WIDE) store4(OT + vl * LDU + r, accO);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int t = c * LC + r + ii;
           if (FULL || t < a.T) {          // FULL: every token of the chunk exists
-            o[((size_t)bh * a.T + t) * D + vg] = to<T>(accO[ii]);
+            if (!WIDE) o[((size_t)bh * a.T + t) * D + vg] = to<T>(accO[ii]);
             csum += accO[ii];
           }
         }
@@ -179,6 +184,17 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
     }
   }
   __syncthreads();
+  if (HAS_O && WIDE) {
+    // O^T fragments: lane (lr, lg) gets 8 consecutive value rows of token 16 tt + lr
+#pragma unroll
+    for (int f = wave; f < (LC / 16) * (VS / 32); f += kWaves) {
+      const int tt = f / (VS / 32), vb = f % (VS / 32);
+      const Frag<T> x = lds_frag_cols(OT, LDU, 16 * tt, 32 * vb);
+      const int t = c * LC + 16 * tt + lr;
+      if (FULL || t < a.T)
+        *reinterpret_cast<Frag<T>*>(o + ((size_t)bh * a.T + t) * D + v0 + 32 * vb + 8 * lg) = x;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     // wave*SPW is a multiple of NVT, so the key tile index within the wave is j / NVT
@@ -207,16 +223,32 @@ __device__ void state_store(const FwdArgs& a, int bh, int v0, const f32x4 (&S)[S
 }
 
 // Store the state entering chunk ci in the two fragment layouts of the backward.
+// Wide slices copy whole fragments out of the dtype copy Sb (rows v0.., in LDS):
+// "vk" fragments are 8 consecutive k of one row, "kv" fragments 8 consecutive rows
+// of one k column; both are one 16-byte store per lane.  Narrow slices scatter
+// the registers' accumulator groups.
 template <typename T, int D, int VS>
-__device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW]) {
+__device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW],
+                                           const T* Sb) {
   using ST = StateTiles<D, VS>;
   T* vk = reinterpret_cast<T*>(a.S_vk) + ci * D * D;
   T* kv = reinterpret_cast<T*>(a.S_kv) + ci * D * D;
-  const int wave = wave_id();
+  const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+  if constexpr (kWideSlice<VS>) {
+    constexpr int LDS_ = D + Pad<T>::v;
 #pragma unroll
-  for (int jj = 0; jj < ST::SPW; ++jj) {
-    const int st = wave * ST::SPW + jj, ct = st / ST::NVT, vt = st % ST::NVT;
-    store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, S[jj], S[jj]);
+    for (int f = wave; f < (VS / 16) * (D / 32); f += kWaves) {
+      const int vt = f / (D / 32), kb = f % (D / 32);
+      const Frag<T> x = load_frag(Sb + (16 * vt + lr) * LDS_ + 32 * kb + 8 * lg);
+      *reinterpret_cast<Frag<T>*>(vk + frag_offset<D>(v0 / 16 + vt, kb, lane)) = x;
+    }
+    store_kv_from_lds<T, D, VS, kWaves>(kv, Sb, LDS_, v0);
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < ST::SPW; ++jj) {
+      const int st = wave * ST::SPW + jj, ct = st / ST::NVT, vt = st % ST::NVT;
+      store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, S[jj], S[jj]);
+    }
   }
 }
 
@@ -247,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
     for (int j = 0; j < PF; ++j) {
       const int c = c0 + j;
       buf[(j + PF - 1) % PF].load(a, c0i + min(c + PF - 1, a.NC - 1), v0);
-      if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S);
+      if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S, reinterpret_cast<const T*>(smem));
       state_chunk<T, LC, D, VS, HAS_O, true>(a, bh, c, v0, buf[j], S, smem, nullptr);
     }
   }
@@ -256,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
     const int c = nmain + j;
     if (c < a.NC) {
       if (c + PF - 1 < a.NC) buf[(j + PF - 1) % PF].load(a, c0i + c + PF - 1, v0);
-      if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S);
+      if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S, reinterpret_cast<const T*>(smem));
       state_chunk<T, LC, D, VS, HAS_O, false>(a, bh, c, v0, buf[j], S, smem, nullptr);
     }
   }

@@ -133,3 +133,35 @@ def test_saved_pair_matches_recompute_bitwise():
         for key in NAMES:
             if g1[key] is not None:
                 assert torch.equal(g1[key], g2[key]), (D, key)
+
+
+@pytest.mark.parametrize("B,H", [(8, 8), (8, 16)], ids=["slice32", "slice64"])
+def test_wide_value_slices_sampled_heads(B, H):
+    """Enough heads that the state passes split D=128 into 32- and 64-row value slices
+    (whose state copies and outputs leave through LDS), with a ragged tail, S0 and dS_T;
+    forward and gradients of sampled heads against the reference."""
+    announce(f"wide value slices B{B} H{H}")
+    T, D = 100, 128
+    inp = random_inputs(B, H, T, D, D, dtype="bf16", seed=300 + H, erase="sigmoid", dists="softplus_decay",
+                        with_dO=True)
+    rng = np.random.default_rng(11)
+    S0 = np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64)
+    dS_T = np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64)
+    d = to_device(inp, "bf16")
+    S0d = torch.from_numpy(np.asarray(S0, np.float32)).cuda()
+    dSd = torch.from_numpy(np.asarray(dS_T, np.float32)).cuda()
+    o, S_T, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=S0d)
+    g = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=d["b"], S0=S0d, dS_T=dSd)
+    torch.cuda.synchronize()
+    for (bi, hi) in [(0, 0), (B - 1, H - 1), (3, H // 2)]:
+        sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items() if not k_.endswith("_bits")}
+        s0 = S0[bi:bi + 1, hi:hi + 1]
+        ds = dS_T[bi:bi + 1, hi:hi + 1]
+        o_ref, sT_ref, _ = oracle.forward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], b=sub["b"], S0=s0)
+        ref = oracle.backward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], sub["dO"], b=sub["b"],
+                              S0=s0, dS_T=ds)
+        errs = {"o": max_rel(to_np(o[bi:bi + 1, hi:hi + 1]), o_ref),
+                "S_T": max_rel(to_np(S_T[bi:bi + 1, hi:hi + 1]), sT_ref)}
+        errs.update({key: max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key]) for key in NAMES})
+        print(f"  head ({bi},{hi}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        assert all(v_ <= 2e-2 for v_ in errs.values()), errs
