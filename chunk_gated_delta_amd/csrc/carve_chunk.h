@@ -115,17 +115,22 @@ __device__ void triangular_inverse(const float* Af, float* Tf, float* scratch) {
 // channel, in LDS).
 struct TokenGatesB {
   const float* b;
-  __device__ __forceinline__ float load(size_t idx) const { return b[idx]; }
+  __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b + idx); }
   __device__ __forceinline__ float act(float x, int) const { return x; }
 };
 struct TokenGates1 {
-  __device__ __forceinline__ float load(size_t) const { return 1.f; }
+  __device__ __forceinline__ Frag<float> load8(size_t) const {
+    Frag<float> f;
+    f.lo = f32x4{1.f, 1.f, 1.f, 1.f};
+    f.hi = f.lo;
+    return f;
+  }
   __device__ __forceinline__ float act(float x, int) const { return x; }
 };
 struct ContentGates {
   const float* b_x;
   const float* z;
-  __device__ __forceinline__ float load(size_t idx) const { return b_x[idx]; }
+  __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b_x + idx); }
   __device__ __forceinline__ float act(float x, int ch) const { return 1.f / (1.f + __expf(-(x + z[ch]))); }
 };
 
@@ -136,9 +141,85 @@ struct ContentGates {
 // bit 2 writes the layouts the backward passes need ((-W)^T, Q~^T, row-major K->).
 // -W, K->^T, Ubar^T and Gamma_L are always written.
 constexpr int kPrepFwd = 1, kPrepBwd = 2;
+
+// Raw inputs of one chunk as 16-byte pieces (8 consecutive channels of one token),
+// piece tid + NT u of thread tid.  Loaded from clamped rows (branch-free), then
+// staged in LDS: k, q, v raw in the K+, Q+ and Ubar^T regions, the per-element
+// retention a = exp(log g) * b in the Kw^T region (fp32 [LC][D]); rows past the
+// end become k = q = v = 0, a = 1.
+template <typename T, int LC, int D, int NT>
+struct PrepStage {
+  static constexpr int PR = D / 8, NP = LC * PR, NST = (NP + NT - 1) / NT;
+  Frag<T> k[NST], q[NST], v[NST];
+  Frag<float> lg[NST], g[NST];
+  float w;
+};
+
+template <typename T, int LC, int D, typename Gates, int NT>
+__device__ __forceinline__ void prep_stage_load(const FwdArgs& a, const Gates& gates, int bh, int c,
+                                                PrepStage<T, LC, D, NT>& st) {
+  using St = PrepStage<T, LC, D, NT>;
+  const int tid = threadIdx.x;
+  const int n = min(LC, a.T - c * LC);
+  const size_t row0 = (size_t)bh * a.T + (size_t)c * LC;
+  const T* kb = reinterpret_cast<const T*>(a.k) + row0 * D;
+  const T* qb = reinterpret_cast<const T*>(a.q) + row0 * D;
+  const T* vb = reinterpret_cast<const T*>(a.v) + row0 * D;
+  const float* lb = a.log_g + row0 * D;
+  st.w = a.w[row0 + min(tid, n - 1)];
+#pragma unroll
+  for (int u = 0; u < St::NST; ++u) {
+    const int idx = min(tid + NT * u, St::NP - 1), r = idx / St::PR, g = idx % St::PR;
+    const unsigned e = (unsigned)(min(r, n - 1) * D + 8 * g);
+    st.k[u] = load_frag(kb + e);
+    st.q[u] = load_frag(qb + e);
+    st.v[u] = load_frag(vb + e);
+    st.lg[u] = load_frag(lb + e);
+    st.g[u] = gates.load8(row0 * D + e);
+  }
+}
+
+template <typename T, int LC, int D, typename Gates, int NT>
+__device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& gates, int c,
+                                                 const PrepStage<T, LC, D, NT>& st, unsigned char* smem) {
+  using Lay = PrepLayout<T, LC, D, NT>;
+  using St = PrepStage<T, LC, D, NT>;
+  constexpr int LDD = Lay::LDD;
+  static_assert(sizeof(float) * LC * D <= 2 * Lay::szDL, "retention staging exceeds the Kw^T region");
+  static_assert(Lay::szLD <= Lay::szDL, "raw v staging exceeds the Ubar^T region");
+  T* Kp = reinterpret_cast<T*>(smem + Lay::R1);
+  T* Qp = reinterpret_cast<T*>(smem + Lay::R2);
+  float* aS = reinterpret_cast<float*>(smem + Lay::R3);
+  T* Vr = reinterpret_cast<T*>(smem + Lay::R6);
+  float* wL = reinterpret_cast<float*>(smem + Lay::R7);
+  const int tid = threadIdx.x;
+  const int n = min(LC, a.T - c * LC);
+  if (tid < LC) wL[tid] = (tid < n) ? st.w : 0.f;
+#pragma unroll
+  for (int u = 0; u < St::NST; ++u) {
+    const int idx = tid + NT * u;
+    if (St::NP % NT == 0 || idx < St::NP) {
+      const int r = idx / St::PR, g = idx % St::PR;
+      const bool valid = r < n;
+      *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = valid ? st.k[u] : zero_frag(T());
+      *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = valid ? st.q[u] : zero_frag(T());
+      *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? st.v[u] : zero_frag(T());
+      f32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo[e] = valid ? __expf(st.lg[u].lo[e]) * gates.act(st.g[u].lo[e], 8 * g + e) : 1.f;
+        hi[e] = valid ? __expf(st.lg[u].hi[e]) * gates.act(st.g[u].hi[e], 8 * g + 4 + e) : 1.f;
+      }
+      *reinterpret_cast<f32x4*>(aS + r * D + 8 * g) = lo;
+      *reinterpret_cast<f32x4*>(aS + r * D + 8 * g + 4) = hi;
+    }
+  }
+}
+
+// The chunk's factors from its staged inputs (LDS, after a barrier).
 template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
-__device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
-                           unsigned char* smem) {
+__device__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
+                             unsigned char* smem) {
   using Lay = PrepLayout<T, LC, D, NT>;
   constexpr int NW = NT / 64;
   constexpr int NB = LC / 16, NCT = D / 16;
@@ -163,9 +244,6 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
   const int t0 = c * LC;
   const int n = min(LC, a.T - t0);
   const size_t row0 = (size_t)bh * a.T + t0;   // global token row of the chunk's first token
-  const T* q = reinterpret_cast<const T*>(a.q);
-  const T* k = reinterpret_cast<const T*>(a.k);
-  const T* v = reinterpret_cast<const T*>(a.v);
   constexpr bool FWD = (MODE & kPrepFwd) != 0, BWD = (MODE & kPrepBwd) != 0;
   T* gWn = reinterpret_cast<T*>(a.f.Wn) + ci * LC * D;
   T* gQt = FWD ? reinterpret_cast<T*>(a.f.Qt) + ci * LC * D : nullptr;
@@ -176,33 +254,22 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
   T* gQtT = BWD ? reinterpret_cast<T*>(a.f.QtT) + ci * D * LC : nullptr;
   T* gKf = BWD ? reinterpret_cast<T*>(a.f.Kf) + ci * LC * D : nullptr;
 
-  // ---- gate pass: cumulative key-axis retention Gamma (thread = key channel x token part).
-  // All global loads are issued up front from clamped rows (n >= 1), then masked.
+  // ---- gate pass: cumulative key-axis retention Gamma (thread = key channel x token part)
+  // over the staged retention a (1 past the end); raw k, q, v are read from their slots.
   const int ch = tid % D, pid = tid / D, r0 = pid * RP;
-  if (tid < LC) wL[tid] = (tid < n) ? a.w[row0 + min(tid, n - 1)] : 0.f;
-  float lgv[RP], gv[RP];
-  T kr[RP], qr[RP], vr[RP];
-#pragma unroll
-  for (int i = 0; i < RP; ++i) {
-    const size_t idx = (row0 + min(r0 + i, n - 1)) * D + ch;
-    lgv[i] = a.log_g[idx];
-    gv[i] = gates.load(idx);
-  }
-#pragma unroll
-  for (int i = 0; i < RP; ++i) {
-    const size_t idx = (row0 + min(r0 + i, n - 1)) * D + ch;
-    kr[i] = k[idx];
-    qr[i] = q[idx];
-    vr[i] = v[idx];
-  }
+  const float* aS = reinterpret_cast<const float*>(smem + Lay::R3);
+  const T* Vraw = reinterpret_cast<const T*>(smem + Lay::R6);
   float G[RP];
+  T kr[RP], qr[RP], vr[RP];
   {
     float run = 1.f;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
-      const float av = (r0 + i < n) ? __expf(lgv[i]) * gates.act(gv[i], ch) : 1.f;
-      run *= av;
+      run *= aS[(r0 + i) * D + ch];
       G[i] = run;
+      kr[i] = Kp[(r0 + i) * LDD + ch];
+      qr[i] = Qp[(r0 + i) * LDD + ch];
+      vr[i] = Vraw[(r0 + i) * LDD + ch];
     }
     part[pid * D + ch] = run;
   }
@@ -221,10 +288,9 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
       const int r = r0 + i;
       const float gam = pre * G[i];
       const float inv = 1.f / gam;
-      const bool valid = r < n;
-      const float kv = valid ? tof(kr[i]) : 0.f;
-      const float qv = valid ? tof(qr[i]) : 0.f;
-      const float vv = valid ? tof(vr[i]) : 0.f;
+      const float kv = tof(kr[i]);       // staged as 0 past the end
+      const float qv = tof(qr[i]);
+      const float vv = tof(vr[i]);
       const float wr = wL[r];
       Kp[r * LDD + ch] = to<T>(kv * gam);
       Km[r * LDD + ch] = to<T>(kv * inv);
@@ -338,6 +404,16 @@ __device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, 
       }
     }
   }
+}
+
+// One chunk, not pipelined: load, stage, compute.
+template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
+__device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci, unsigned char* smem) {
+  PrepStage<T, LC, D, NT> st;
+  prep_stage_load<T, LC, D, Gates, NT>(a, gates, bh, c, st);
+  prep_stage_write<T, LC, D, Gates, NT>(a, gates, c, st, smem);
+  __syncthreads();
+  prep_compute<T, LC, D, Gates, MODE, NT>(a, gates, bh, c, ci, smem);
 }
 
 

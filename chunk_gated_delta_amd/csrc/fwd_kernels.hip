@@ -18,20 +18,41 @@
 // This is the token recurrence of the CARVE notes (sections 2.1-2.3) unrolled
 // over one chunk: the shared coupling is what the notes call the single WY-form
 // triangular solve that key-axis-only gating keeps valid.
+#include <algorithm>
+
 #include "carve_chunk.h"
 
 namespace carve {
 
 // threads of the chunk-prep kernel: one wave per 16 columns of the width
-template <int D> constexpr int prep_threads() { return 8 * D; }
+template <int D> constexpr int prep_threads() { return 4 * D; }
+
+// Persistent over chunks: workgroup g prepares chunks g, g + G, g + 2G, ... (G = grid
+// size, chunk index ci = bh * NC + c).  Once a chunk's raw inputs are staged in LDS
+// the registers take the next chunk's loads, which land while this chunk computes.
+template <typename T, int LC, int D, int MODE, typename Gates>
+__device__ __forceinline__ void prep_loop(const FwdArgs& a, const Gates& gates, unsigned char* smem) {
+  constexpr int NT = prep_threads<D>();
+  const int total = a.B * a.H * a.NC;
+  PrepStage<T, LC, D, NT> st;
+  int ci = blockIdx.x;
+  prep_stage_load<T, LC, D, Gates, NT>(a, gates, ci / a.NC, ci % a.NC, st);
+  for (; ci < total; ci += gridDim.x) {
+    const int bh = ci / a.NC, c = ci % a.NC;
+    prep_stage_write<T, LC, D, Gates, NT>(a, gates, c, st, smem);
+    __syncthreads();
+    const int cn = min(ci + (int)gridDim.x, total - 1);      // clamped: the last pass reloads a valid chunk
+    prep_stage_load<T, LC, D, Gates, NT>(a, gates, cn / a.NC, cn % a.NC, st);
+    prep_compute<T, LC, D, Gates, MODE, NT>(a, gates, bh, c, ci, smem);
+    __syncthreads();                                         // LDS is restaged by the next chunk
+  }
+}
 
 template <typename T, int LC, int D, int MODE>
-__global__ __launch_bounds__(8 * D) void fwd_prep_kernel(FwdArgs a) {
-  constexpr int NT = prep_threads<D>();
+__global__ __launch_bounds__(4 * D) void fwd_prep_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int c = blockIdx.x, bh = blockIdx.y;
-  if (a.b) prep_chunk<T, LC, D, TokenGatesB, MODE, NT>(a, TokenGatesB{a.b}, bh, c, (size_t)bh * a.NC + c, smem);
-  else prep_chunk<T, LC, D, TokenGates1, MODE, NT>(a, TokenGates1{}, bh, c, (size_t)bh * a.NC + c, smem);
+  if (a.b) prep_loop<T, LC, D, MODE>(a, TokenGatesB{a.b}, smem);
+  else prep_loop<T, LC, D, MODE>(a, TokenGates1{}, smem);
 }
 
 // ------------------------------------------------------------------ state step
@@ -413,6 +434,20 @@ hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream
 }
 
 // ------------------------------------------------------------------ launchers
+// Workgroups of a persistent launch: one per compute unit of the current device
+// (the prep's LDS footprint allows one resident workgroup per unit).
+static int persistent_blocks() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {  // one [chunk][LC][D] block
   const size_t es = dtype ? 2 : 4;
   return ((size_t)BH * NC * LC * D * es + 255) & ~size_t(255);
@@ -456,8 +491,8 @@ static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
-  dim3 grid(a.NC, a.B * a.H);
-  hipLaunchKernelGGL(kern, grid, dim3(prep_threads<D>()), Lay::bytes, st, a);
+  const int total = a.NC * a.B * a.H;
+  hipLaunchKernelGGL(kern, dim3(std::min(total, persistent_blocks())), dim3(prep_threads<D>()), Lay::bytes, st, a);
   return hipGetLastError();
 }
 
