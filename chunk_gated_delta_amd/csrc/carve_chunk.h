@@ -39,8 +39,8 @@ struct PrepLayout {
   static constexpr size_t R4 = R3 + al(2 * szDL);         // A (fp32), then (-W)^T
   static constexpr size_t R5 = R4 + al(cmax(szLLf, szDL)); // P (dtype)
   static constexpr size_t R6 = R5 + al(szLL);             // Ubar^T
-  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [P][D], T-solve scratch
-  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D + (NT / 64) * 16 * 20));
+  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [P][D]
+  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D));
 };
 
 // lower-triangular block index -> (i, j), j <= i
@@ -53,56 +53,59 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
 // T = (I + A)^-1 for strictly lower-triangular A (fp32 in LDS), LC = 16 * NB.
 // Diagonal 16x16 blocks by column-parallel forward substitution, then the
 // off-diagonal blocks by block forward substitution on fp32 MFMA:
-//   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj,   processed by increasing i - j.
+//   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj = -sum_{m=j}^{i-1} (T_ii A_im) T_mj,
+// with the scaled blocks T_ii A_im formed first (all in parallel) and the T_ij
+// by increasing distance i - j.  The strictly lower blocks of A are overwritten;
+// the blocks of T above the diagonal are not written.
 template <int LC, int LDF, int NT = kThreads>
-__device__ void triangular_inverse(const float* Af, float* Tf, float* scratch) {
+__device__ void triangular_inverse(float* Af, float* Tf) {
   constexpr int NB = LC / 16;
   static_assert(NT / 64 >= NB - 1, "one wave per off-diagonal block of a distance");
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   if (tid < 16 * NB) {
+    // lane (block, column j) solves (I + A_bb) x = e_j; right-looking: once x[m] is
+    // final it is subtracted from every later row, so the dependent chain is 15
+    // steps long (each row still accumulates its terms in the order m = 0, 1, ...)
     const int base = 16 * (tid / 16), j = tid % 16;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = (r == j) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s -= Af[(base + r) * LDF + base + m] * x[m];
-      x[r] = s;
-    }
+    for (int m = 0; m < 15; ++m)
+#pragma unroll
+      for (int r = m + 1; r < 16; ++r) x[r] -= Af[(base + r) * LDF + base + m] * x[m];
 #pragma unroll
     for (int r = 0; r < 16; ++r) Tf[(base + r) * LDF + base + j] = x[r];
   }
-  for (int idx = tid; idx < LC * LC; idx += NT) {
-    const int r = idx / LC, s = idx % LC;
-    if ((s >> 4) > (r >> 4)) Tf[r * LDF + s] = 0.f;
+  __syncthreads();   // blocks above the diagonal are never written: readers treat them as 0
+  const int lr = lane & 15, lg = lane >> 4;
+  // scaled coupling blocks Ahat_im = T_ii A_im (i > m), written over A_im (one wave
+  // per block; a wave reads only its own block of A before writing it)
+  constexpr int NPAIR = NB * (NB - 1) / 2;
+  float* Ah = Af;
+  for (int t = wave; t < NPAIR; t += NT / 64) {
+    int i = 1, m = t;
+    while (m >= i) { m -= i; ++i; }           // t -> (i, m), 0 <= m < i
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      mma_k4(y, Tf[(16 * i + lr) * LDF + 16 * i + 4 * s4 + lg], Af[(16 * i + 4 * s4 + lg) * LDF + 16 * m + lr]);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) Ah[(16 * i + 4 * lg + ii) * LDF + 16 * m + lr] = y[ii];
   }
   __syncthreads();
+  // off-diagonal blocks by increasing distance: T_ij = -sum_{m=j}^{i-1} Ahat_im T_mj
   for (int d = 1; d < NB; ++d) {
     if (wave < NB - d) {
       const int j = wave, i = wave + d;
-      const int lr = lane & 15, lg = lane >> 4;
       f32x4 y = {0.f, 0.f, 0.f, 0.f};
       for (int m = j; m < i; ++m) {
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const float a = Af[(16 * i + lr) * LDF + 16 * m + 4 * s4 + lg];
-          const float b = Tf[(16 * m + 4 * s4 + lg) * LDF + 16 * j + lr];
-          mma_k4(y, a, b);
-        }
-      }
-      float* Y = scratch + wave * 16 * 20;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Y[(4 * lg + ii) * 20 + lr] = y[ii];
-      wave_lds_sync();
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const float a = Tf[(16 * i + lr) * LDF + 16 * i + 4 * s4 + lg];
-        const float b = Y[(4 * s4 + lg) * 20 + lr];
-        mma_k4(x, a, b);
+        for (int s4 = 0; s4 < 4; ++s4)
+          mma_k4(y, Ah[(16 * i + lr) * LDF + 16 * m + 4 * s4 + lg], Tf[(16 * m + 4 * s4 + lg) * LDF + 16 * j + lr]);
       }
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) Tf[(16 * i + 4 * lg + ii) * LDF + 16 * j + lr] = -x[ii];
+      for (int ii = 0; ii < 4; ++ii) Tf[(16 * i + 4 * lg + ii) * LDF + 16 * j + lr] = -y[ii];
     }
     __syncthreads();
   }
@@ -237,7 +240,6 @@ __device__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c
   T* UbTs = reinterpret_cast<T*>(smem + Lay::R6);
   float* wL = reinterpret_cast<float*>(smem + Lay::R7);
   float* part = wL + LC;
-  float* scratch = part + P * D;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
@@ -339,12 +341,11 @@ __device__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c
 
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
   // modes also keep the fp32 T of the chunk
-  triangular_inverse<LC, LDF, NT>(Af, Tf, scratch);
+  triangular_inverse<LC, LDF, NT>(Af, Tf);
   for (int idx = tid; idx < LC * LC / 4; idx += NT) {
     const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
-    const f32x4 t4 = *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Tb[r * LDL + s + e] = to<T>(t4[e]);
+    const f32x4 t4 = ((s >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);
+    store4(Tb + r * LDL + s, t4);
     if (BWD) *reinterpret_cast<f32x4*>(a.f.Tinv + (ci * LC + r) * LC + s) = t4;
   }
   __syncthreads();
