@@ -63,6 +63,24 @@ def algorithmic(wl, with_bwd):
     return out
 
 
+TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "head1p3b_fwd_bwd_hbm_traffic.md")
+STAGE_KERNEL = {"fwd_prep": "fwd_prep_kernel", "fwd_state": "fwd_state_kernel",
+                "bwd_state_rev": "bwd_state_kernel", "bwd_chunk_grads": "bwd_chunk_kernel"}
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of a training-step kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a reference copy kernel), or None when
+    the kernel sources changed after the counters were taken."""
+    from chunk_gated_delta_amd.build import source_digest
+    from chunk_gated_delta_amd.prof_summary import read_traffic
+    rec = read_traffic(TRAFFIC_SUMMARY)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    b = rec["bytes_per_launch"].get(STAGE_KERNEL.get(stage, ""))
+    return None if b is None else int(b["read"] + b["write"])
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -208,6 +226,11 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                 "bytes_per_token_head": stage_bytes[dom], "launch_ms": round(dom_ms, 4)}
+    traffic = measured_traffic(dom) if with_bwd else None
+    if traffic is not None:
+        roofline["traffic"] = traffic
+        roofline["traffic_unit"] = "HBM bytes per launch (read + written)"
+        roofline["traffic_over_algorithmic"] = round(traffic / (stage_bytes[dom] * units), 3)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,0 +1,127 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the project.
+
+    python -m chunk_gated_delta_amd.prof_summary stats KERNEL_STATS_CSV --title T --command C [--bench-json J] --out F
+    python -m chunk_gated_delta_amd.prof_summary traffic FETCH_CSV WRITE_CSV --copy-mib N --title T
+                                                   --command-fetch C1 --command-write C2 --out F
+
+`stats` tabulates a --kernel-trace --stats run.  `traffic` takes one --pmc FETCH_SIZE
+run and one --pmc WRITE_SIZE run of `python -m chunk_gated_delta_amd.profile_step
+--copy-mib N` and scales each counter (KiB per dispatch) by what it reads for the
+reference kernel, which reads N MiB and writes N MiB; the per-kernel HBM bytes per
+launch are also written as a machine-readable line (with the digest of the kernel
+sources they were measured on) that bench.py reports while the sources are unchanged.
+"""
+import argparse
+import csv
+import json
+import statistics
+import sys
+
+TRAFFIC_TAG = "<!-- hbm-traffic: "
+
+
+def short_name(mangled):
+    for key in ("bwd_chunk_kernel", "bwd_state_kernel", "fwd_prep_kernel", "fwd_state_kernel",
+                "fwd_content_kernel", "copy_or_zero_kernel"):
+        if key in mangled:
+            return key
+    return mangled[:48]
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = [f"# {args.title}", "", "Command (from /tmp with TMPDIR=/tmp; repository at $R, PYTHONPATH=$R):", "",
+           "    " + args.command, "", "Durations in microseconds (rocprofv3 kernel statistics).", "",
+           "| kernel | mangled name | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| {short_name(r['Name'])} | `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / total:.1f} |")
+    if args.bench_json:
+        line = [ln for ln in open(args.bench_json) if ln.startswith("{")][-1]
+        b = json.loads(line)
+        out += ["", "The same run's bench line (HIP events on the launch stream, mean per launch):", ""]
+        for k_, v_ in b["extra"]["stage_ms"].items():
+            out.append(f"* {k_}: {1e3 * v_:.1f} us")
+        out.append(f"* step: {1e3 * b['ms_per_step']:.1f} us; roofline kernel {b['roofline']['kernel']}, "
+                   f"launch {1e3 * b['roofline']['launch_ms']:.1f} us")
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
+def _per_kernel(path, counter):
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(args):
+    from chunk_gated_delta_amd.build import source_digest
+    fetch = _per_kernel(args.fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(args.write_csv, "WRITE_SIZE")
+    ref_kib = args.copy_mib * 1024.0
+    # reference kernel: the dispatches that read (torch.neg); the fill that precedes them reads nothing
+    ref_f = [v for k_, vs in fetch.items() if "carve" not in k_ for v in vs if v > 0.25 * ref_kib]
+    ref_w = [v for k_, vs in write.items() if "carve" not in k_ for v in vs if v > 0.25 * ref_kib]
+    f_scale = ref_kib / statistics.median(ref_f)
+    w_scale = ref_kib / statistics.median(ref_w)
+    out = [f"# {args.title}", "", "Commands (from /tmp with TMPDIR=/tmp; repository at $R, PYTHONPATH=$R):", "",
+           "    " + args.command_fetch, "    " + args.command_write, "",
+           f"Reference kernel (torch.neg, {args.copy_mib} MiB read + {args.copy_mib} MiB written): FETCH_SIZE reads "
+           f"{statistics.median(ref_f):.0f} KiB, WRITE_SIZE {statistics.median(ref_w):.0f} KiB per dispatch, so the "
+           f"counters are scaled by {f_scale:.3f} (fetch) and {w_scale:.3f} (write).", "",
+           "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM written MB | total MB |",
+           "|---|---|---|---|---|---|---|"]
+    record = {"source_digest": source_digest(), "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+              "bytes_per_launch": {}}
+    for name in fetch:
+        if "carve" not in name:
+            continue
+        fk = statistics.median(fetch[name])
+        wk = statistics.median(write.get(name, [0.0]))
+        rd, wr = fk * f_scale * 1024, wk * w_scale * 1024
+        out.append(f"| {short_name(name)} `{name[:70]}` | {len(fetch[name])} | {fk:.0f} | {wk:.0f} | "
+                   f"{rd / 1e6:.1f} | {wr / 1e6:.1f} | {(rd + wr) / 1e6:.1f} |")
+        record["bytes_per_launch"][short_name(name)] = {"read": round(rd), "write": round(wr)}
+    out += ["", "Kernel sources digest at measurement: `" + record["source_digest"] + "`", "",
+            TRAFFIC_TAG + json.dumps(record) + " -->"]
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
+def read_traffic(path):
+    """The machine-readable record of a traffic summary, or None."""
+    try:
+        for line in open(path):
+            if line.startswith(TRAFFIC_TAG):
+                return json.loads(line[len(TRAFFIC_TAG):].rsplit(" -->", 1)[0])
+    except OSError:
+        return None
+    return None
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--bench-json")
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv")
+    t.add_argument("write_csv")
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--title", required=True)
+    t.add_argument("--command-fetch", required=True)
+    t.add_argument("--command-write", required=True)
+    t.add_argument("--out", required=True)
+    a = p.parse_args(argv)
+    (stats if a.cmd == "stats" else traffic)(a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
