@@ -43,6 +43,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--no-content", action="store_true")
+    p.add_argument("--no-long", action="store_true", help="skip the long-context forward")
     return p.parse_args()
 
 
@@ -176,10 +177,56 @@ def main():
     fwd_ms = f0.elapsed_time(f1) / args.steps
     fwd_stage = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in pf])) for j, name in enumerate(fwd_names)}
 
-    # content-aware forward of the same shape (separate timing, not part of the step)
+    # per-step times, hot (back to back) and cold: before each cold step a 512 MiB buffer is
+    # overwritten so the 256 MB last-level cache holds none of the step's inputs
+    def per_step(nrep, flush):
+        times = []
+        for _ in range(nrep):
+            if flush is not None:
+                flush.add_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(None, None)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return times
+    nrep = min(args.steps, 10)
+    hot = per_step(nrep, None)
+    flush = torch.zeros(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    cold = per_step(nrep, flush)
+    del flush
+
     extra = {"stage_ms": {k_: round(v_, 4) for k_, v_ in stage_mean.items()},
+             "step_ms_hot": {"median": round(float(np.median(hot)), 4), "min": round(float(np.min(hot)), 4)},
+             "step_ms_cold": {"median": round(float(np.median(cold)), 4), "min": round(float(np.min(cold)), 4)},
+             "tokens_per_s_cold_median": B * T / (float(np.median(cold)) * 1e-3),
              "fwd_ms": round(fwd_ms, 4), "fwd_stage_ms": {k_: round(v_, 4) for k_, v_ in fwd_stage.items()},
              "fwd_tokens_per_s": B * T / (fwd_ms * 1e-3)}
+
+    # long-context forward (B1 H16 T32768 d128 L64): sixteen sequential chains of 512 chunks
+    if not args.no_long:
+        wlc = WORKLOADS["long_ctx_fwd"]
+        lin = make_inputs(wlc)
+        lq, lk, lv = (torch.from_numpy(np.ascontiguousarray(lin[key + "_bits"]).view(np.int16)).to(dev)
+                      .view(torch.bfloat16) for key in ("q", "k", "v"))
+        lg_, lw_ = (torch.from_numpy(np.ascontiguousarray(lin[key], dtype=np.float32)).to(dev) for key in ("log_g", "w"))
+        lb_ = torch.from_numpy(np.ascontiguousarray(lin["b"], dtype=np.float32)).to(dev) if "b" in lin else None
+        for _ in range(2):
+            carve.fwd(lq, lk, lv, lg_, lw_, b=lb_, L=wlc.L)
+        torch.cuda.synchronize()
+        le0, le1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        le0.record()
+        for _ in range(5):
+            carve.fwd(lq, lk, lv, lg_, lw_, b=lb_, L=wlc.L)
+        le1.record()
+        torch.cuda.synchronize()
+        lms = le0.elapsed_time(le1) / 5
+        extra["long_ctx_fwd_ms"] = round(lms, 4)
+        extra["long_ctx_fwd_tokens_per_s"] = wlc.B * wlc.T / (lms * 1e-3)
+        del lq, lk, lv, lg_, lw_, lb_
+
+    # content-aware forward of the same shape (separate timing, not part of the step)
     if not args.no_content:
         wc = WORKLOADS["content_fwd"]
         cin = make_inputs(wc)
