@@ -45,8 +45,8 @@
  *     handled); B, H >= 0 (an empty batch, head or token axis is a no-op that
  *     still writes S_T = S0 and m_out = m0).  Chunk length L: any L >= 1 for
  *     token-only gates (the result does not depend on L; the kernels tile
- *     tokens in blocks of 32 when L <= 32 and of 64 otherwise); for the content
- *     path L must be a multiple of that tile (32, 64, 128, ...).
+ *     tokens in blocks of 32 when L <= 32 or dtype is float32, and of 64
+ *     otherwise); for the content path L must be a multiple of that tile.
  *   - Numerical range: the chunk kernels form products exp(G_r) and exp(-G_s)
  *     of the cumulative log-retention G inside one tile of tokens, so every
  *     key channel's retention accumulated over one tile must stay above about
