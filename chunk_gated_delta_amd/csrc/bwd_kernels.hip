@@ -85,6 +85,8 @@ struct RevOps {
   static constexpr int VEC = 8;                                   // elements per fragment-sized piece
   static constexpr int NDO = (LC * VS / VEC + kThreads - 1) / kThreads;
   static_assert(NVT % XPW == 0, "a wave's X tiles must share one row tile");
+  static constexpr bool kAllWaves = XPW * (kWaves - 1) < NX;          // every wave owns X tiles
+  static constexpr bool kFullDO = (LC * VS / VEC) % kThreads == 0;    // every thread loads NDO pieces
   Frag<T> kf[KD];
   Frag<T> wt[SCT][KL];
   Frag<T> qt[SCT][KL];
@@ -99,7 +101,7 @@ struct RevOps {
     const T* WnT = reinterpret_cast<const T*>(f.f.WnT);
     const T* QtT = reinterpret_cast<const T*>(f.f.QtT);
     const int t0 = wave * XPW;
-    if (t0 < NX) {
+    if (kAllWaves || t0 < NX) {
       const int rt = t0 / NVT;
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) kf[kk] = load_frag(Kf + (ci * LC + 16 * rt + lr) * D + 32 * kk + 8 * lg);
@@ -120,7 +122,7 @@ struct RevOps {
     for (int u = 0; u < NDO; ++u) {
       const int idx = threadIdx.x + kThreads * u;            // piece index: token r, column group g
       const int r = idx / (VS / VEC), g = idx % (VS / VEC);
-      if (idx < LC * VS / VEC) {
+      if (kFullDO || idx < LC * VS / VEC) {
         const int rr = min(r, n - 1);   // rows past the sequence end are zeroed where they are used
         dov[u] = load_frag(dO + ((size_t)bh * f.T + c * LC + rr) * D + v0 + VEC * g);
       }
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
     for (int u = 0; u < Op::NDO; ++u) {
       const int idx = threadIdx.x + kThreads * u;
-      if (idx < LC * VS / VEC) {
+      if (Op::kFullDO || idx < LC * VS / VEC) {
         const int r = idx / (VS / VEC), g = idx % (VS / VEC);
         const bool live = r < f.T - c * LC;
 #pragma unroll
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     // X^T = K-> dS^T  (tiles [s][v])
     {
       const int t0 = wave * Op::XPW;
-      if (t0 < Op::NX) {
+      if (Op::kAllWaves || t0 < Op::NX) {
         const int rt = t0 / NVT;
 #pragma unroll
         for (int u = 0; u < Op::XPW; ++u) {

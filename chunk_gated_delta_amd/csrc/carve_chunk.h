@@ -480,12 +480,11 @@ template <int VS> constexpr bool kWideSlice = VS >= 32;
 template <typename T, int D, int VS, int NWAVES>
 __device__ __forceinline__ void store_kv_from_lds(T* kv, const T* Sb, int ld, int v0) {
   const int lane = lane_id(), wave = wave_id();
-#pragma unroll
-  for (int f = wave; f < (D / 16) * (VS / 32); f += NWAVES) {
+  for_wave_items<(D / 16) * (VS / 32), NWAVES>(wave, [&](int f) {
     const int kt = f / (VS / 32), vb = f % (VS / 32);
     const Frag<T> x = lds_frag_cols(Sb, ld, 16 * kt, 32 * vb);
     *reinterpret_cast<Frag<T>*>(kv + frag_offset<D>(kt, v0 / 32 + vb, lane)) = x;
-  }
+  });
 }
 
 }  // namespace carve

@@ -39,6 +39,21 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Calls fn(f) for f = wave, wave + NW, ... < F.  When NW divides F every wave runs the
+// same iterations with no branch, so memory operations inside stay unconditional (the
+// compiler's per-wave memory counters are then exact across loop iterations).
+template <int F, int NW, typename Fn>
+__device__ __forceinline__ void for_wave_items(int wave, Fn&& fn) {
+  if constexpr (F % NW == 0) {
+#pragma unroll
+    for (int u = 0; u < F / NW; ++u) fn(wave + NW * u);
+  } else {
+#pragma unroll
+    for (int u = 0; u < (F + NW - 1) / NW; ++u)
+      if (wave + NW * u < F) fn(wave + NW * u);
+  }
+}
+
 // ------------------------------------------------------------------ fragments
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };

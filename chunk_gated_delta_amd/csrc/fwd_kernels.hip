@@ -91,6 +91,7 @@ struct ChunkOps {
   static constexpr int SCT = NCT / kWaves;
   static constexpr int KD = D / 32, KL = LC / 32;
   static_assert(NVT % UPW == 0, "a wave's U/O tiles must share one row tile");
+  static constexpr bool kAllWaves = UPW * (kWaves - 1) < NUO;   // every wave owns U/O tiles
   Frag<T> w[KD];
   Frag<T> q[HAS_O ? KD : 1];
   Raw4<T> ub[UPW];
@@ -106,7 +107,7 @@ struct ChunkOps {
     const T* UbT = reinterpret_cast<const T*>(a.f.UbT);
     const T* OiT = reinterpret_cast<const T*>(a.f.OiT);
     const int t0 = wave * UPW;
-    if (t0 < NUO) {
+    if (kAllWaves || t0 < NUO) {
       const int rt = t0 / NVT;
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) {
@@ -128,6 +129,9 @@ struct ChunkOps {
 #pragma unroll
       for (int kk = 0; kk < KL; ++kk) kf[j][kk] = load_frag(KfT + (ci * D + 16 * ct + lr) * LC + 32 * kk + 8 * lg);
     }
+    // keep the loads here: without this compiler-level fence they may be sunk to their
+    // first use, which would leave no time for them to arrive
+    asm volatile("" ::: "memory");
   }
 };
 
@@ -170,7 +174,7 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
   constexpr bool WIDE = kWideSlice<VS>;
 
   const int t0 = wave * UPW;
-  if (t0 < NUO) {
+  if (Op::kAllWaves || t0 < NUO) {
     const int rt = t0 / NVT;
 #pragma unroll
     for (int u = 0; u < UPW; ++u) {
@@ -207,14 +211,13 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
   __syncthreads();
   if (HAS_O && WIDE) {
     // O^T fragments: lane (lr, lg) gets 8 consecutive value rows of token 16 tt + lr
-#pragma unroll
-    for (int f = wave; f < (LC / 16) * (VS / 32); f += kWaves) {
+    for_wave_items<(LC / 16) * (VS / 32), kWaves>(wave, [&](int f) {
       const int tt = f / (VS / 32), vb = f % (VS / 32);
       const Frag<T> x = lds_frag_cols(OT, LDU, 16 * tt, 32 * vb);
       const int t = c * LC + 16 * tt + lr;
       if (FULL || t < a.T)
         *reinterpret_cast<Frag<T>*>(o + ((size_t)bh * a.T + t) * D + v0 + 32 * vb + 8 * lg) = x;
-    }
+    });
   }
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
@@ -257,12 +260,11 @@ __device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, 
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
   if constexpr (kWideSlice<VS>) {
     constexpr int LDS_ = D + Pad<T>::v;
-#pragma unroll
-    for (int f = wave; f < (VS / 16) * (D / 32); f += kWaves) {
+    for_wave_items<(VS / 16) * (D / 32), kWaves>(wave, [&](int f) {
       const int vt = f / (D / 32), kb = f % (D / 32);
       const Frag<T> x = load_frag(Sb + (16 * vt + lr) * LDS_ + 32 * kb + 8 * lg);
       *reinterpret_cast<Frag<T>*>(vk + frag_offset<D>(v0 / 16 + vt, kb, lane)) = x;
-    }
+    });
     store_kv_from_lds<T, D, VS, kWaves>(kv, Sb, LDS_, v0);
   } else {
 #pragma unroll
@@ -273,10 +275,11 @@ __device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, 
   }
 }
 
-// The chunk loop keeps three operand buffers, so chunk c's factors are loaded two
-// chunks ahead.  Full chunks run in a branch-free main loop (prefetch indices are
-// clamped, no token checks), so the compiler's per-wave memory counters only wait
-// for the buffer in use; the last chunks run in a checked tail.
+// The chunk loop keeps three operand buffers: chunk c is consumed from buffer c % 3,
+// which then takes the loads of chunk c + 3, so every chunk's factors are in flight
+// for two whole chunk steps and a step never waits on loads issued in the same step.
+// Full chunks run in a branch-free main loop (prefetch indices are clamped, no token
+// checks); the last chunks run in a checked tail.
 template <typename T, int LC, int D, int VS, bool HAS_O, bool SAVE>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   using ST = StateTiles<D, VS>;
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   f32x4 S[ST::SPW];
   Op buf[PF];
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, c0i + min(j, a.NC - 1), v0);
+  for (int j = 0; j < PF; ++j) buf[j].load(a, c0i + min(j, a.NC - 1), v0);
   state_init<T, D, VS>(a, bh, v0, S, reinterpret_cast<T*>(smem));
   __syncthreads();
   const int nfull = (a.T % LC == 0) ? a.NC : a.NC - 1;
@@ -299,16 +302,15 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int c = c0 + j;
-      buf[(j + PF - 1) % PF].load(a, c0i + min(c + PF - 1, a.NC - 1), v0);
       if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S, reinterpret_cast<const T*>(smem));
       state_chunk<T, LC, D, VS, HAS_O, true>(a, bh, c, v0, buf[j], S, smem, nullptr);
+      buf[j].load(a, c0i + min(c + PF, a.NC - 1), v0);
     }
   }
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
     const int c = nmain + j;
     if (c < a.NC) {
-      if (c + PF - 1 < a.NC) buf[(j + PF - 1) % PF].load(a, c0i + c + PF - 1, v0);
       if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S, reinterpret_cast<const T*>(smem));
       state_chunk<T, LC, D, VS, HAS_O, false>(a, bh, c, v0, buf[j], S, smem, nullptr);
     }
