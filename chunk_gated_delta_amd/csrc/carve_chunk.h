@@ -57,8 +57,11 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
 // with the scaled blocks T_ii A_im formed first (all in parallel) and the T_ij
 // by increasing distance i - j.  The strictly lower blocks of A are overwritten;
 // the blocks of T above the diagonal are not written.
+// Kept out of line (each instantiation is shared by its callers) with LDS-typed
+// pointers, so that every access is an LDS instruction.
+typedef __attribute__((address_space(3))) float lds_float;
 template <int LC, int LDF, int NT = kThreads>
-__device__ void triangular_inverse(float* Af, float* Tf) {
+__device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_float* Tf) {
   constexpr int NB = LC / 16;
   static_assert(NT / 64 >= NB - 1, "one wave per off-diagonal block of a distance");
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -82,7 +85,7 @@ __device__ void triangular_inverse(float* Af, float* Tf) {
   // scaled coupling blocks Ahat_im = T_ii A_im (i > m), written over A_im (one wave
   // per block; a wave reads only its own block of A before writing it)
   constexpr int NPAIR = NB * (NB - 1) / 2;
-  float* Ah = Af;
+  lds_float* Ah = Af;
   for (int t = wave; t < NPAIR; t += NT / 64) {
     int i = 1, m = t;
     while (m >= i) { m -= i; ++i; }           // t -> (i, m), 0 <= m < i
@@ -221,7 +224,7 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
 
 // The chunk's factors from its staged inputs (LDS, after a barrier).
 template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
-__device__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
+__device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
                              unsigned char* smem) {
   using Lay = PrepLayout<T, LC, D, NT>;
   constexpr int NW = NT / 64;
@@ -341,7 +344,7 @@ __device__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c
 
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
   // modes also keep the fp32 T of the chunk
-  triangular_inverse<LC, LDF, NT>(Af, Tf);
+  triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
   for (int idx = tid; idx < LC * LC / 4; idx += NT) {
     const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
     const f32x4 t4 = ((s >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);
@@ -409,7 +412,7 @@ __device__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c
 
 // One chunk, not pipelined: load, stage, compute.
 template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
-__device__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci, unsigned char* smem) {
+__device__ __forceinline__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci, unsigned char* smem) {
   PrepStage<T, LC, D, NT> st;
   prep_stage_load<T, LC, D, Gates, NT>(a, gates, bh, c, st);
   prep_stage_write<T, LC, D, Gates, NT>(a, gates, c, st, smem);
@@ -437,11 +440,15 @@ __device__ __forceinline__ void xcd_slice_map(int nslices, int BH, int& bh, int&
 // State tiles of a workgroup holding VS value rows of a D x D state: lane l of
 // tile (ct, vt) holds S[16 vt + l%16][16 ct + 4 (l/16) + i], i = 0..3
 // (accumulator layout of S^T); wave w owns tiles w*SPW .. w*SPW+SPW-1.
-template <int D, int VS>
+template <int D, int VS, int NW = kWaves>
 struct StateTiles {
   static constexpr int NVT = VS / 16, NCT = D / 16;
-  static constexpr int SPW = NCT * NVT / kWaves;   // state tiles per wave
-  static_assert(NCT * NVT % kWaves == 0, "state tiles must split evenly over waves");
+  static constexpr int SPW = NCT * NVT / NW;       // state tiles per wave
+  static_assert(NCT * NVT % NW == 0, "state tiles must split evenly over waves");
+  static_assert(SPW % NVT == 0 || NVT % SPW == 0, "a wave's tiles must cover whole key tiles or part of one");
+  static constexpr int SCT = SPW >= NVT ? SPW / NVT : 1;   // key tiles a wave touches
+  // key tile of the wave's tile j, relative to the wave's first key tile
+  static constexpr int jc(int j) { return SPW >= NVT ? j / NVT : 0; }
 };
 
 // D x D matrices handed from the state passes to the chunk-gradient kernel are

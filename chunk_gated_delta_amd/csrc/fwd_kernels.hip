@@ -80,18 +80,19 @@ __device__ __forceinline__ f32x4 widen(const Raw4<bf16>& r) {
 }
 __device__ __forceinline__ f32x4 widen(const Raw4<float>& r) { return r.v; }
 
-// The global operands one wave needs for one chunk.  Wave w owns the U/O tiles
-// tix = w*UPW + u (all in one row tile of the chunk) and the state tiles of
-// key tiles ct = w*SCT + j.  Loaded one chunk ahead of their use.
-template <typename T, int LC, int D, int VS, bool HAS_O>
+// The global operands one wave needs for one chunk.  Wave w (of NW) owns the U/O
+// tiles tix = w*UPW + u (all in one row tile of the chunk) and the state tiles
+// st = w*SPW + j (key tile st / NVT, value tile st % NVT).
+template <typename T, int LC, int D, int VS, bool HAS_O, int NW = kWaves>
 struct ChunkOps {
+  using ST = StateTiles<D, VS, NW>;
   static constexpr int NVT = VS / 16, NB = LC / 16, NCT = D / 16;
   static constexpr int NUO = NB * NVT;
-  static constexpr int UPW = (NUO + kWaves - 1) / kWaves;
-  static constexpr int SCT = NCT / kWaves;
+  static constexpr int UPW = (NUO + NW - 1) / NW;
+  static constexpr int SCT = ST::SCT;
   static constexpr int KD = D / 32, KL = LC / 32;
   static_assert(NVT % UPW == 0, "a wave's U/O tiles must share one row tile");
-  static constexpr bool kAllWaves = UPW * (kWaves - 1) < NUO;   // every wave owns U/O tiles
+  static constexpr bool kAllWaves = UPW * (NW - 1) < NUO;   // every wave owns U/O tiles
   Frag<T> w[KD];
   Frag<T> q[HAS_O ? KD : 1];
   Raw4<T> ub[UPW];
@@ -124,21 +125,18 @@ struct ChunkOps {
     }
 #pragma unroll
     for (int j = 0; j < SCT; ++j) {
-      const int ct = wave * SCT + j;
+      const int ct = (wave * ST::SPW) / NVT + j;
       gl[j] = load4f(a.f.gL + ci * D + 16 * ct + 4 * lg);
 #pragma unroll
       for (int kk = 0; kk < KL; ++kk) kf[j][kk] = load_frag(KfT + (ci * D + 16 * ct + lr) * LC + 32 * kk + 8 * lg);
     }
-    // keep the loads here: without this compiler-level fence they may be sunk to their
-    // first use, which would leave no time for them to arrive
-    asm volatile("" ::: "memory");
   }
 };
 
 // Load the state slice (S0 or zero) into registers and its dtype copy into LDS.
-template <typename T, int D, int VS>
-__device__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTiles<D, VS>::SPW], T* Sb) {
-  using ST = StateTiles<D, VS>;
+template <typename T, int D, int VS, int NW = kWaves>
+__device__ __forceinline__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTiles<D, VS, NW>::SPW], T* Sb) {
+  using ST = StateTiles<D, VS, NW>;
   constexpr int LDS_ = D + Pad<T>::v;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
 #pragma unroll
@@ -158,12 +156,12 @@ __device__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTil
 // copy of S; on exit S and Sb hold the updated state.  If colsum is given, the
 // per-row-tile column sums of the fp32 outputs (valid tokens only) are written
 // to colsum[NB][VS].
-template <typename T, int LC, int D, int VS, bool HAS_O, bool FULL = false>
-__device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const ChunkOps<T, LC, D, VS, HAS_O>& op,
-                            f32x4 (&S)[StateTiles<D, VS>::SPW], unsigned char* smem, float* colsum) {
+template <typename T, int LC, int D, int VS, bool HAS_O, bool FULL = false, int NW = kWaves>
+__device__ __forceinline__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const ChunkOps<T, LC, D, VS, HAS_O, NW>& op,
+                            f32x4 (&S)[StateTiles<D, VS, NW>::SPW], unsigned char* smem, float* colsum) {
   using Lay = StateLayout<T, LC, D, VS>;
-  using Op = ChunkOps<T, LC, D, VS, HAS_O>;
-  using ST = StateTiles<D, VS>;
+  using Op = ChunkOps<T, LC, D, VS, HAS_O, NW>;
+  using ST = StateTiles<D, VS, NW>;
   constexpr int NVT = ST::NVT, SPW = ST::SPW, UPW = Op::UPW, NUO = Op::NUO;
   constexpr int LDS_ = Lay::LDS_, LDU = Lay::LDU;
   T* Sb = reinterpret_cast<T*>(smem);
@@ -211,7 +209,7 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
   __syncthreads();
   if (HAS_O && WIDE) {
     // O^T fragments: lane (lr, lg) gets 8 consecutive value rows of token 16 tt + lr
-    for_wave_items<(LC / 16) * (VS / 32), kWaves>(wave, [&](int f) {
+    for_wave_items<(LC / 16) * (VS / 32), NW>(wave, [&](int f) {
       const int tt = f / (VS / 32), vb = f % (VS / 32);
       const Frag<T> x = lds_frag_cols(OT, LDU, 16 * tt, 32 * vb);
       const int t = c * LC + 16 * tt + lr;
@@ -221,8 +219,7 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
   }
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
-    // wave*SPW is a multiple of NVT, so the key tile index within the wave is j / NVT
-    const int jc = j / NVT, ct = wave * Op::SCT + jc, vt = j % NVT;
+    const int st = wave * SPW + j, jc = ST::jc(j), ct = st / NVT, vt = st % NVT;
     const int kc = 16 * ct + 4 * lg, vl = 16 * vt + lr;
     S[j] *= op.gl[jc];
 #pragma unroll
@@ -235,9 +232,9 @@ __device__ void state_chunk(const FwdArgs& a, int bh, int c, int v0, const Chunk
   __syncthreads();
 }
 
-template <typename T, int D, int VS>
-__device__ void state_store(const FwdArgs& a, int bh, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW], float* dst) {
-  using ST = StateTiles<D, VS>;
+template <typename T, int D, int VS, int NW = kWaves>
+__device__ __forceinline__ void state_store(const FwdArgs& a, int bh, int v0, const f32x4 (&S)[StateTiles<D, VS, NW>::SPW], float* dst) {
+  using ST = StateTiles<D, VS, NW>;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int j = 0; j < ST::SPW; ++j) {
@@ -327,18 +324,22 @@ __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
 // resident), and the state step consumes them with all Dv rows in the
 // workgroup.  The mean is accumulated from the fp32 outputs before rounding,
 // in a fixed order (deterministic).
+// eight waves per workgroup: the per-chunk work of one head is spread over the CU
+constexpr int kContentWaves = 8;
+
 template <typename T, int LC, int D>
 struct ContentLayout {
-  static constexpr size_t prep = PrepLayout<T, LC, D>::bytes;
+  static constexpr size_t prep = PrepLayout<T, LC, D, 64 * kContentWaves>::bytes;
   static constexpr size_t step = StateLayout<T, LC, D, D>::bytes;
   static constexpr size_t body = (prep > step ? prep : step);
   static constexpr size_t bytes = body + sizeof(float) * (4 * D + 64);   // z, msum, m, r
 };
 
 template <typename T, int LC, int D>
-__global__ __launch_bounds__(kThreads) void fwd_content_kernel(FwdArgs a, ContentArgs cg) {
+__global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs a, ContentArgs cg) {
+  constexpr int NW = kContentWaves, NT = 64 * NW;
   using Lay = ContentLayout<T, LC, D>;
-  using ST = StateTiles<D, D>;
+  using ST = StateTiles<D, D, NW>;
   constexpr int NB = LC / 16;
   extern __shared__ __align__(16) unsigned char smem[];
   float* zL = reinterpret_cast<float*>(smem + Lay::body);
@@ -382,10 +383,10 @@ __global__ __launch_bounds__(kThreads) void fwd_content_kernel(FwdArgs a, Conten
       __syncthreads();
     }
     // prepare this chunk's factors into the head's slot
-    prep_chunk<T, LC, D>(a, ContentGates{cg.b_x, zL}, bh, c, (size_t)bh, smem);
+    prep_chunk<T, LC, D, ContentGates, kPrepFwd, NT>(a, ContentGates{cg.b_x, zL}, bh, c, (size_t)bh, smem);
     __syncthreads();
     if (c == 0) {
-      state_init<T, D, D>(a, bh, 0, S, reinterpret_cast<T*>(smem));
+      state_init<T, D, D, NW>(a, bh, 0, S, reinterpret_cast<T*>(smem));
       __syncthreads();
     } else {
       // rebuild the LDS copy of the state (the prep pass reused that memory)
@@ -400,9 +401,9 @@ __global__ __launch_bounds__(kThreads) void fwd_content_kernel(FwdArgs a, Conten
       __syncthreads();
     }
     float* cs = reinterpret_cast<float*>(smem + StateLayout<T, LC, D, D>::bytes - sizeof(float) * NB * D);
-    ChunkOps<T, LC, D, D, true> op;
+    ChunkOps<T, LC, D, D, true, NW> op;
     op.load(a, (size_t)bh, 0);
-    state_chunk<T, LC, D, D, true>(a, bh, c, 0, op, S, smem, cs);
+    state_chunk<T, LC, D, D, true, false, NW>(a, bh, c, 0, op, S, smem, cs);
     // fold this chunk's column sums into the period sum (fixed order over row tiles)
     const int nvalid = min(LC, a.T - c * LC);
     if (tid < D) {
@@ -417,7 +418,7 @@ __global__ __launch_bounds__(kThreads) void fwd_content_kernel(FwdArgs a, Conten
     }
     __syncthreads();
   }
-  if (a.S_T) state_store<T, D, D>(a, bh, 0, S, a.S_T);
+  if (a.S_T) state_store<T, D, D, NW>(a, bh, 0, S, a.S_T);
   if (cg.m_out && tid < D) cg.m_out[(size_t)bh * D + tid] = mL[tid];
 }
 
@@ -540,7 +541,7 @@ static hipError_t content_launch(const FwdArgs& a, const ContentArgs& cg, hipStr
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(kThreads), Lay::bytes, st, a, cg);
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(64 * kContentWaves), Lay::bytes, st, a, cg);
   return hipGetLastError();
 }
 
