@@ -104,7 +104,7 @@ struct RevOps {
     if (kAllWaves || t0 < NX) {
       const int rt = t0 / NVT;
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) kf[kk] = load_frag(Kf + (ci * LC + 16 * rt + lr) * D + 32 * kk + 8 * lg);
+      for (int kk = 0; kk < KD; ++kk) kf[kk] = load_frag(Kf + ci * LC * D + frag_offset<D>(rt, kk, lane));
     }
 #pragma unroll
     for (int j = 0; j < SCT; ++j) {
@@ -112,8 +112,8 @@ struct RevOps {
       gl[j] = load4f(f.f.gL + ci * D + 16 * ct + 4 * lg);
 #pragma unroll
       for (int kk = 0; kk < KL; ++kk) {
-        wt[j][kk] = load_frag(WnT + (ci * D + 16 * ct + lr) * LC + 32 * kk + 8 * lg);
-        qt[j][kk] = load_frag(QtT + (ci * D + 16 * ct + lr) * LC + 32 * kk + 8 * lg);
+        wt[j][kk] = load_frag(WnT + ci * D * LC + frag_offset<LC>(ct, kk, lane));
+        qt[j][kk] = load_frag(QtT + ci * D * LC + frag_offset<LC>(ct, kk, lane));
       }
     }
     const T* dO = reinterpret_cast<const T*>(a.dO);

@@ -43,6 +43,22 @@ struct PrepLayout {
   static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D));
 };
 
+// ------------------------------------------------------------------ global layouts
+// MFMA fragment order of a [rows][C] matrix M (C = contraction length): fragment
+// (rt, kb) holds, for lane l, M[16 rt + l%16][32 kb + 8 (l/16) + j], j = 0..7, at
+// ((rt * C/32 + kb) * 64 + l) * 8, so one fragment is one contiguous 16-byte
+// (bf16) load per lane and 1 KB per wave.
+template <int C>
+__device__ __forceinline__ size_t frag_offset(int rt, int kb, int lane) {
+  return ((size_t)(rt * (C / 32) + kb) * 64 + lane) * 8;
+}
+// Accumulator order of a [rows][W] matrix (an MFMA output): tile (rt, ct) holds, for
+// lane l, M[16 rt + 4 (l/16) + i][16 ct + l%16], i = 0..3, at ((rt * W/16 + ct) * 64 + l) * 4.
+template <int W>
+__device__ __forceinline__ size_t acc_offset(int rt, int ct, int lane) {
+  return ((size_t)(rt * (W / 16) + ct) * 64 + lane) * 4;
+}
+
 // lower-triangular block index -> (i, j), j <= i
 __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
   i = 0;
@@ -239,6 +255,8 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   T* VwT = KwT + D * LDL;
   float* Af = reinterpret_cast<float*>(smem + Lay::R4);
   T* WnT = reinterpret_cast<T*>(smem + Lay::R4);
+  T* KfL = reinterpret_cast<T*>(smem + Lay::R4);   // row-major K-> during the gate pass (backward modes)
+  T* QtTs = KwT;                                    // Q~^T once the WY factors are done
   T* Pb = reinterpret_cast<T*>(smem + Lay::R5);
   T* UbTs = reinterpret_cast<T*>(smem + Lay::R6);
   float* wL = reinterpret_cast<float*>(smem + Lay::R7);
@@ -250,6 +268,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   const int n = min(LC, a.T - t0);
   const size_t row0 = (size_t)bh * a.T + t0;   // global token row of the chunk's first token
   constexpr bool FWD = (MODE & kPrepFwd) != 0, BWD = (MODE & kPrepBwd) != 0;
+  static_assert(Lay::szLD <= Lay::R5 - Lay::R4, "row-major K-> exceeds the coupling slot");
   T* gWn = reinterpret_cast<T*>(a.f.Wn) + ci * LC * D;
   T* gQt = FWD ? reinterpret_cast<T*>(a.f.Qt) + ci * LC * D : nullptr;
   T* gKfT = reinterpret_cast<T*>(a.f.KfT) + ci * D * LC;
@@ -265,16 +284,12 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   const float* aS = reinterpret_cast<const float*>(smem + Lay::R3);
   const T* Vraw = reinterpret_cast<const T*>(smem + Lay::R6);
   float G[RP];
-  T kr[RP], qr[RP], vr[RP];
   {
     float run = 1.f;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
       run *= aS[(r0 + i) * D + ch];
       G[i] = run;
-      kr[i] = Kp[(r0 + i) * LDD + ch];
-      qr[i] = Qp[(r0 + i) * LDD + ch];
-      vr[i] = Vraw[(r0 + i) * LDD + ch];
     }
     part[pid * D + ch] = run;
   }
@@ -293,9 +308,9 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       const int r = r0 + i;
       const float gam = pre * G[i];
       const float inv = 1.f / gam;
-      const float kv = tof(kr[i]);       // staged as 0 past the end
-      const float qv = tof(qr[i]);
-      const float vv = tof(vr[i]);
+      const float kv = tof(Kp[r * LDD + ch]);      // staged raw, 0 past the end
+      const float qv = tof(Qp[r * LDD + ch]);
+      const float vv = tof(Vraw[r * LDD + ch]);
       const float wr = wL[r];
       Kp[r * LDD + ch] = to<T>(kv * gam);
       Km[r * LDD + ch] = to<T>(kv * inv);
@@ -304,15 +319,29 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       VwT[ch * LDL + r] = to<T>(wr * vv);
       kf[i] = to<T>(kv * (tot * inv));
     }
+    // K->^T in fragment order: this thread's tokens r0.. of key channel ch, 4 at a time
+    static_assert(RP % 4 == 0, "token parts must hold whole groups of 4");
 #pragma unroll
-    for (int i = 0; i < RP; ++i) gKfT[ch * LC + r0 + i] = kf[i];
+    for (int t = 0; t < RP / 4; ++t) {
+      const int r = r0 + 4 * t;
+      T* dst = gKfT + frag_offset<LC>(ch / 16, r / 32, ch % 16 + 16 * ((r % 32) / 8)) + r % 8;
+      store4(dst, f32x4{tof(kf[4 * t]), tof(kf[4 * t + 1]), tof(kf[4 * t + 2]), tof(kf[4 * t + 3])});
+    }
     if (BWD) {
 #pragma unroll
-      for (int i = 0; i < RP; ++i) gKf[(r0 + i) * D + ch] = kf[i];
+      for (int i = 0; i < RP; ++i) KfL[(r0 + i) * LDD + ch] = kf[i];
     }
     if (pid == 0) a.f.gL[ci * D + ch] = tot;
   }
   __syncthreads();
+  if (BWD) {
+    // row-major K-> (staged in the coupling slot) to fragment order, then free the slot
+    for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
+      const int rt = f / (D / 32), kb = f % (D / 32);
+      *reinterpret_cast<Frag<T>*>(gKf + frag_offset<D>(rt, kb, lane)) = load_frag(KfL + (16 * rt + lr) * LDD + 32 * kb + 8 * lg);
+    });
+    __syncthreads();
+  }
 
   // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
   constexpr int NTRI = NB * (NB + 1) / 2;
@@ -332,13 +361,15 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
       const int r = 16 * i + 4 * lg + ii;
-      if (isA) Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
-      else Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
+      if (isA) {
+        Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
+      } else {
+        Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
+        // the products with P run over 32-token blocks: block (i, i+1) of an even row
+        // tile i is read by them and must be zero
+        if (j == i && i % 2 == 0 && i + 1 < NB) Pb[r * LDL + s + 16] = to<T>(0.f);
+      }
     }
-  }
-  for (int idx = tid; idx < LC * LC; idx += NT) {
-    const int r = idx / LC, s = idx % LC;
-    if ((s >> 4) > (r >> 4)) Pb[r * LDL + s] = to<T>(0.f);
   }
   __syncthreads();
 
@@ -367,17 +398,24 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     }
     const int col = 16 * ct + lr, r = 16 * i + 4 * lg;
     if (isW) {
-      const f32x4 neg = -acc;
-      store4(WnT + col * LDL + r, neg);
-      if (BWD) store4(gWnT + col * LC + r, neg);
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) gWn[(r + ii) * D + col] = to<T>(neg[ii]);
+      store4(WnT + col * LDL + r, -acc);
     } else {
       store4(UbTs + col * LDL + r, acc);
-      store4(gUbT + col * LC + r, acc);
+      store4(gUbT + acc_offset<D>(i, ct, lane), acc);
     }
   }
   __syncthreads();
+  // -W out of LDS in fragment order: rows = tokens (forward), rows = keys (backward)
+  for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
+    const int rt = f / (D / 32), kb = f % (D / 32);
+    *reinterpret_cast<Frag<T>*>(gWn + frag_offset<D>(rt, kb, lane)) = lds_frag_cols(WnT, LDL, 16 * rt, 32 * kb);
+  });
+  if (BWD) {
+    for_wave_items<NCT * (LC / 32), NW>(wave, [&](int f) {
+      const int kt = f / (LC / 32), kb = f % (LC / 32);
+      *reinterpret_cast<Frag<T>*>(gWnT + frag_offset<LC>(kt, kb, lane)) = load_frag(WnT + (16 * kt + lr) * LDL + 32 * kb + 8 * lg);
+    });
+  }
 
   // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
   for (int t = FWD ? wave : wave + NB * NCT; t < 2 * NB * NCT; t += NW) {
@@ -398,15 +436,22 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       const Frag<T> fb = load_frag(Bs + (16 * ct + lr) * LDL + kk + 8 * lg);
       mma(acc, fa, fb);
     }
-    if (isO) {
-      store4(gOiT + col * LC + r, acc);
-    } else {
-      if (BWD) store4(gQtT + col * LC + r, acc);
-      if (FWD) {
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) gQt[(r + ii) * D + col] = to<T>(acc[ii]);
-      }
-    }
+    if (isO) store4(gOiT + acc_offset<D>(i, ct, lane), acc);
+    else store4(QtTs + col * LDL + r, acc);
+  }
+  __syncthreads();
+  // Q~ out of LDS in fragment order (rows = tokens forward, rows = keys backward)
+  if (FWD) {
+    for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
+      const int rt = f / (D / 32), kb = f % (D / 32);
+      *reinterpret_cast<Frag<T>*>(gQt + frag_offset<D>(rt, kb, lane)) = lds_frag_cols(QtTs, LDL, 16 * rt, 32 * kb);
+    });
+  }
+  if (BWD) {
+    for_wave_items<NCT * (LC / 32), NW>(wave, [&](int f) {
+      const int kt = f / (LC / 32), kb = f % (LC / 32);
+      *reinterpret_cast<Frag<T>*>(gQtT + frag_offset<LC>(kt, kb, lane)) = load_frag(QtTs + (16 * kt + lr) * LDL + 32 * kb + 8 * lg);
+    });
   }
 }
 
@@ -451,16 +496,9 @@ struct StateTiles {
   static constexpr int jc(int j) { return SPW >= NVT ? j / NVT : 0; }
 };
 
-// D x D matrices handed from the state passes to the chunk-gradient kernel are
-// stored in MFMA fragment order: fragment (rt, kb) of a [rows][contraction]
-// matrix M holds, for lane l, M[16 rt + l%16][32 kb + 8 (l/16) + j], j = 0..7, at
-// ((rt * D/32 + kb) * 64 + l) * 8, so one fragment is one coalesced 16-byte
-// (bf16) load per lane.  Two orientations of the state S[v][k] are kept:
-//   "vk": rows v, contraction k;     "kv": rows k, contraction v.
-template <int D>
-__device__ __forceinline__ size_t frag_offset(int rt, int kb, int lane) {
-  return ((size_t)(rt * (D / 32) + kb) * 64 + lane) * 8;
-}
+// The D x D state matrices handed to the chunk-gradient kernel use the fragment
+// order of frag_offset (two orientations of S[v][k]: "vk" rows v, contraction k;
+// "kv" rows k, contraction v).
 
 // Scatter one accumulator group (lane (lr, lg) of state tile (vt, ct): the four
 // values M[16 vt + lr][16 ct + 4 lg + i]) into both fragment layouts.

@@ -6,21 +6,24 @@
 namespace carve {
 
 // Per-chunk factors produced by the chunk-parallel prep kernel and consumed by
-// the sequential state kernels.  Chunk index ci = (b*H + h) * NC + c.
-//   Wn  [ci][LC][D]  -W      with W  = T diag(w) (K .* Gamma)        (dtype)
-//   Qt  [ci][LC][D]  Q~      = (Q .* Gamma) - P W                    (dtype)
-//   KfT [ci][D][LC]  (K .* Gamma_L / Gamma)^T                        (dtype)
-//   UbT [ci][D][LC]  Ubar^T  with Ubar = T diag(w) V                 (dtype)
-//   OiT [ci][D][LC]  (P Ubar)^T, the intra-chunk output              (dtype)
-//   gL  [ci][D]      Gamma_L, the chunk's total key-axis retention   (float)
+// the sequential state kernels.  Chunk index ci = (b*H + h) * NC + c; every block
+// holds LC*D elements per chunk, in the order the state kernels load them
+// ("frag <C>": MFMA fragment order with contraction length C, frag_offset;
+// "acc": accumulator order, acc_offset):
+//   Wn  -W [LC][D], frag<D>     with W = T diag(w) (K .* Gamma)       (dtype)
+//   Qt  Q~ [LC][D], frag<D>     Q~ = (Q .* Gamma) - P W               (dtype)
+//   KfT K->^T [D][LC], frag<LC> K-> = K .* Gamma_L / Gamma            (dtype)
+//   UbT Ubar [LC][D], acc       Ubar = T diag(w) V                    (dtype)
+//   OiT P Ubar [LC][D], acc     the intra-chunk output                (dtype)
+//   gL  [ci][D]                 Gamma_L, the chunk's total retention  (float)
 // where Gamma is the inclusive cumulative product of a inside the chunk,
 // T = (I + A)^-1, A = strict_tril(diag(w) (K.*Gamma)(K./Gamma)^T) and
 // P = tril((Q.*Gamma)(K./Gamma)^T).
 // The backward layouts (written when the prep mode includes the backward):
-//   QtT [ci][D][LC]  Q~^T
-//   WnT [ci][D][LC]  (-W)^T
-//   Kf  [ci][LC][D]  K->
-//   Tinv [ci][LC][LC] T = (I + A)^-1, fp32
+//   QtT Q~^T [D][LC], frag<LC>
+//   WnT (-W)^T [D][LC], frag<LC>
+//   Kf  K-> [LC][D], frag<D>
+//   Tinv [ci][LC][LC] row-major, T = (I + A)^-1, fp32
 // Prep modes: 1 = forward only, 2 = backward only (no Qt / OiT), 3 = both.
 struct ChunkFactors {
   void* Wn;

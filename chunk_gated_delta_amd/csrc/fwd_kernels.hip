@@ -112,15 +112,14 @@ struct ChunkOps {
       const int rt = t0 / NVT;
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) {
-        w[kk] = load_frag(Wn + (ci * LC + 16 * rt + lr) * D + 32 * kk + 8 * lg);
-        if (HAS_O) q[kk] = load_frag(Qt + (ci * LC + 16 * rt + lr) * D + 32 * kk + 8 * lg);
+        w[kk] = load_frag(Wn + ci * LC * D + frag_offset<D>(rt, kk, lane));
+        if (HAS_O) q[kk] = load_frag(Qt + ci * LC * D + frag_offset<D>(rt, kk, lane));
       }
 #pragma unroll
       for (int u = 0; u < UPW; ++u) {
         const int vt = (t0 + u) % NVT;
-        const int vg = v0 + 16 * vt + lr, r = 16 * rt + 4 * lg;
-        ub[u] = load_raw4(UbT + (ci * D + vg) * LC + r);
-        if (HAS_O) oi[u] = load_raw4(OiT + (ci * D + vg) * LC + r);
+        ub[u] = load_raw4(UbT + ci * LC * D + acc_offset<D>(rt, v0 / 16 + vt, lane));
+        if (HAS_O) oi[u] = load_raw4(OiT + ci * LC * D + acc_offset<D>(rt, v0 / 16 + vt, lane));
       }
     }
 #pragma unroll
@@ -128,7 +127,7 @@ struct ChunkOps {
       const int ct = (wave * ST::SPW) / NVT + j;
       gl[j] = load4f(a.f.gL + ci * D + 16 * ct + 4 * lg);
 #pragma unroll
-      for (int kk = 0; kk < KL; ++kk) kf[j][kk] = load_frag(KfT + (ci * D + 16 * ct + lr) * LC + 32 * kk + 8 * lg);
+      for (int kk = 0; kk < KL; ++kk) kf[j][kk] = load_frag(KfT + ci * D * LC + frag_offset<LC>(ct, kk, lane));
     }
   }
 };
