@@ -497,13 +497,11 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     for (int ii = 0; ii < 4; ++ii) {
       const int r = 16 * i + 4 * lg + ii;
       Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
-    }
-  }
-  for (int idx = tid; idx < LC * LC; idx += NT) {
-    const int r = idx / LC, s = idx % LC;
-    if ((s >> 4) > (r >> 4)) {
-      Pb[r * LDL + s] = to<T>(0.f);
-      dPb[r * LDL + s] = to<T>(0.f);
+      if (j < i) {
+        // the mirrored tile above the diagonal is zero in P and in dP (written later)
+        Pb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);
+        dPb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);
+      }
     }
   }
   // state fragments for U = Ubar - W S^T
@@ -709,16 +707,14 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
       const int r = 16 * i + 4 * lg + ii;
       dTb[r * LDL + s] = to<T>(acc[ii] * wL[s]);
       cs += tof(Tb[r * LDL + s]) * acc[ii];
+      if (j < i) dTb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);   // mirrored tile: zero
     }
     cs += __shfl_xor(cs, 16);
     cs += __shfl_xor(cs, 32);
-    if (lg == 0) dwp[i * LC + s] = cs;
-  }
-  for (int idx = tid; idx < LC * LC; idx += NT) {
-    const int r = idx / LC, s = idx % LC;
-    const int it = r >> 4, jt = s >> 4;
-    if (jt > it) dTb[r * LDL + s] = to<T>(0.f);
-    if (jt > it) dwp[it * LC + s] = 0.f;      // tiles above the diagonal contribute nothing
+    if (lg == 0) {
+      dwp[i * LC + s] = cs;
+      if (j < i) dwp[j * LC + 16 * i + lr] = 0.f;      // tiles above the diagonal contribute nothing
+    }
   }
   // ---- dV = Tw^T dU (write dv); dK+ (first part) = Tw^T dW -> dK += Gamma dK+, dG += K+ dK+
   {
@@ -805,15 +801,12 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * i + 4 * lg + ii;
           dAb[r * LDL + s] = to<T>(wL[r] * dA[u][ii]);
+          if (j < i) {
+            // mirrored tile above the diagonal: zero, and no row-sum contribution
+            dAb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);
+            if (lr == 0) dwq[i * LC + 16 * j + 4 * lg + ii] = 0.f;
+          }
         }
-      }
-    }
-    for (int idx = tid; idx < LC * LC; idx += NT) {
-      const int r = idx / LC, s = idx % LC;
-      const int it = r >> 4, jt = s >> 4;
-      if (jt > it) {
-        dAb[r * LDL + s] = to<T>(0.f);
-        dwq[jt * LC + r] = 0.f;
       }
     }
   }
