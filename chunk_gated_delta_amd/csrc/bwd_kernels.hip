@@ -30,36 +30,6 @@ __device__ __forceinline__ Frag<T> frag(const T* base, int ld, int row0, int k0)
   else return lds_frag_cols(base, ld, row0, k0);
 }
 
-// Same from an fp32 matrix in global memory, converted to the operand type,
-// optionally scaled per k by kscale[k].
-template <bool TR, typename T>
-__device__ __forceinline__ Frag<T> frag32(const float* base, int ld, int row0, int k0, const float* kscale) {
-  const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
-  float x[8];
-  if (!TR) {
-    const f32x4 lo = *reinterpret_cast<const f32x4*>(base + (size_t)(row0 + lr) * ld + k0 + 8 * lg);
-    const f32x4 hi = *reinterpret_cast<const f32x4*>(base + (size_t)(row0 + lr) * ld + k0 + 8 * lg + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { x[j] = lo[j]; x[j + 4] = hi[j]; }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = base[(size_t)(k0 + 8 * lg + j) * ld + row0 + lr];
-  }
-  if (kscale) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] *= kscale[k0 + 8 * lg + j];
-  }
-  Frag<T> f;
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] = (bf16)x[j];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { f.lo[j] = x[j]; f.hi[j] = x[j + 4]; }
-  }
-  return f;
-}
-
 __device__ __forceinline__ bf16 frag_elem(const Frag<bf16>& f, int e) { return f.v[e]; }
 __device__ __forceinline__ float frag_elem(const Frag<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
 
@@ -165,19 +135,14 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   __syncthreads();
   auto step = [&](int c, const Op& cur) {
     const size_t ci = (size_t)bh * f.NC + c;
-    // gradient w.r.t. the state leaving chunk c, in fragment order: scaled by this
-    // chunk's Gamma_L (rows v) and plain (rows k)
+    // gradient w.r.t. the state leaving chunk c, in fragment order rows v
     {
-      T* vk = reinterpret_cast<T*>(a.dSg_vk) + ci * D * D;
-      T* kv = reinterpret_cast<T*>(a.dS_kv) + ci * D * D;
+      T* vk = reinterpret_cast<T*>(a.dS_vk) + ci * D * D;
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
         const int jc = j / NVT, ct = wave * Op::SCT + jc, vt = j % NVT;
-        if constexpr (kWideSlice<VS>) store_vk_group<T, D>(vk, v0 / 16 + vt, ct, dS[j] * cur.gl[jc]);
-        else store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, dS[j] * cur.gl[jc], dS[j]);
+        store_vk_group<T, D>(vk, v0 / 16 + vt, ct, dS[j]);
       }
-      // the plain copy's "kv" fragments come out of dSb, which holds dS in the dtype
-      if constexpr (kWideSlice<VS>) store_kv_from_lds<T, D, VS, kWaves>(kv, dSb, LDS_, v0);
     }
     // dO^T slice into LDS
 #pragma unroll
@@ -314,7 +279,8 @@ __device__ __forceinline__ void owned_mma(f32x4 (&acc)[NB][CPW], const ASrc& A, 
     }
   }
 }
-// fragments of a fragment-ordered D x D matrix for the wave's row tiles ct0 + j
+// fragments of a "vk"-ordered D x D matrix M[v][k] for the wave's row tiles ct0 + j:
+// rows v, contraction over k
 template <typename T, int D, int CPW>
 __device__ __forceinline__ void load_state_frags(Frag<T> (&dst)[D / 32][CPW], const T* base, int ct0) {
   const int lane = lane_id();
@@ -322,6 +288,22 @@ __device__ __forceinline__ void load_state_frags(Frag<T> (&dst)[D / 32][CPW], co
   for (int kb = 0; kb < D / 32; ++kb)
 #pragma unroll
     for (int j = 0; j < CPW; ++j) dst[kb][j] = load_frag(base + frag_offset<D>(ct0 + j, kb, lane));
+}
+// the same matrix with rows k for the wave's key tiles ct0 + j (contraction over v):
+// raw pieces, then the fragments
+template <typename T, int D, int CPW>
+__device__ __forceinline__ void load_state_kmajor(KmajorPieces<T> (&dst)[D / 32][CPW], const T* base, int ct0) {
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) dst[kb][j] = load_kmajor_pieces<D>(base, ct0 + j, kb);
+}
+template <typename T, int KB, int CPW>
+__device__ __forceinline__ void finish_kmajor(Frag<T> (&dst)[KB][CPW], const KmajorPieces<T> (&src)[KB][CPW]) {
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) dst[kb][j] = kmajor_frag(src[kb][j]);
 }
 template <int NB, int CPW>
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NB][CPW]) {
@@ -376,9 +358,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   const T* v = reinterpret_cast<const T*>(f.v);
   const T* dO = reinterpret_cast<const T*>(a.dO);
   const T* Svk = reinterpret_cast<const T*>(f.S_vk) + ci * D * D;     // state entering the chunk
-  const T* Skv = reinterpret_cast<const T*>(f.S_kv) + ci * D * D;
-  const T* dSgvk = reinterpret_cast<const T*>(a.dSg_vk) + ci * D * D; // gradient w.r.t. the state leaving it
-  const T* dSkv = reinterpret_cast<const T*>(a.dS_kv) + ci * D * D;
+  const T* dSvk = reinterpret_cast<const T*>(a.dS_vk) + ci * D * D;   // gradient w.r.t. the state leaving it
 
   // ---- stage the chunk's raw inputs in LDS with coalesced 16-byte loads:
   // k, q, v (dtype) in the K+, Q+, V slots; log g in slots 4-5 and b from slot 6 on
@@ -549,8 +529,8 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         Ur[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(accU[rt][j][ii]);
-  Frag<T> fG[KD][CPW];                       // dS' Diag(Gamma_L) fragments for dU
-  load_state_frags<T, D, CPW>(fG, dSgvk, ct0);
+  Frag<T> fG[KD][CPW];                       // dS' fragments, scaled to dS' Diag(Gamma_L) for dU
+  load_state_frags<T, D, CPW>(fG, dSvk, ct0);
   __syncthreads();   // -W no longer needed: its slot takes dO
 
   // ---- dO into LDS (row-major, zero for tokens past the end)
@@ -566,6 +546,14 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     f32x4 acc[NB][CPW];
     zero_acc(acc);
     owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, true>{Pb, LDL}, LdsSrc<T, true>{dOr, LDD}, ct0);
+    // column scaling by Gamma_L: the lane's values of block kb sit at k = 32 kb + 8 lg + e
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gLs + 32 * kb + 8 * lg);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gLs + 32 * kb + 8 * lg + 4);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) fG[kb][j] = scale_frag(fG[kb][j], g0, g1);
+    }
     owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{Km, LDD}, fG);
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
@@ -575,9 +563,9 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
         for (int ii = 0; ii < 4; ++ii)
           dUr[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(acc[rt][j][ii]);
   }
-  Frag<T> fSk[KD][CPW], fDk[KD][CPW];        // S and dS' with rows k, for the key-owned products
-  load_state_frags<T, D, CPW>(fSk, Skv, ct0);
-  load_state_frags<T, D, CPW>(fDk, dSkv, ct0);
+  KmajorPieces<T> pSk[KD][CPW], pDk[KD][CPW];   // S and dS' with rows k, for the key-owned products
+  load_state_kmajor<T, D, CPW>(pSk, Svk, ct0);
+  load_state_kmajor<T, D, CPW>(pDk, dSvk, ct0);
   // ---- dP = tril(dO U^T)
   for (int t = wave; t < NTRI; t += NW) {
     int i, j;
@@ -598,6 +586,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   //   dK = Gamma dK+ + dK- / Gamma + (Gamma_L / Gamma) dK->        (gradient w.r.t. k)
   //   dG = K+ dK+ - K- dK- + Q+ dQ+ - K-> dK->                        (gradient w.r.t. the
   //        cumulative log-retention, elementwise; K-> = K- Gamma_L)
+  Frag<T> fSk[KD][CPW], fDk[KD][CPW];
   f32x4 dK[NB][CPW], dG[NB][CPW];
   float gsum[CPW];        // sum over tokens of K-> .* dK-> per column (part of the G_L term)
   auto lds_el = [&](const T* m, int rt, int j, int ii) {
@@ -607,8 +596,10 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     // dQ+ = dO S + dP K-  -> dq = Gamma dQ+, dG = Q+ dQ+
     f32x4 acc[NB][CPW];
     zero_acc(acc);
-    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{dOr, LDD}, fSk);
     owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, false>{dPb, LDL}, LdsSrc<T, true>{Km, LDD}, ct0);
+    finish_kmajor(fSk, pSk);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{dOr, LDD}, fSk);
+    finish_kmajor(fDk, pDk);
     T* dq = reinterpret_cast<T*>(a.dq);
 #pragma unroll
     for (int j = 0; j < CPW; ++j)

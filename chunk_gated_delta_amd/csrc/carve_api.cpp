@@ -78,22 +78,22 @@ size_t states_bytes(const carve_shape* s, const Plan& p) {
 }
 
 // saved buffer of carve_fwd_save: factors (forward + backward layouts) and the
-// state entering every chunk (two fragment-order copies)
+// state entering every chunk (one fragment-order copy)
 size_t saved_bytes(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 3) + 2 * (states_bytes(s, p) + 256) + 256;
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 3) + (states_bytes(s, p) + 256) + 256;
 }
 
-// workspace of carve_bwd_saved: the state gradients (two copies)
+// workspace of carve_bwd_saved: the state gradients (one fragment-order copy)
 size_t bwd_saved_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  return 2 * (states_bytes(s, p) + 256) + 256;
+  return (states_bytes(s, p) + 256) + 256;
 }
 
 size_t bwd_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  // S and dS per chunk, two fragment-order copies each, in the operand type
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 2) + 4 * (states_bytes(s, p) + 256) + 256;
+  // S and dS per chunk, one fragment-order copy each, in the operand type
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 2) + 2 * (states_bytes(s, p) + 256) + 256;
 }
 
 carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, const void* k, const void* v,
@@ -247,9 +247,7 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
                         carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2));
   const size_t states = states_bytes(s, p);
   a.fwd.S_vk = base;
-  a.fwd.S_kv = align_up(base + states);
-  a.dSg_vk = align_up(static_cast<char*>(a.fwd.S_kv) + states);
-  a.dS_kv = align_up(static_cast<char*>(a.dSg_vk) + states);
+  a.dS_vk = align_up(base + states);
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -306,7 +304,6 @@ carve_status carve_fwd_save(const carve_shape* s, const void* q, const void* k, 
   a.f = carve::carve_factors(saved, a.dtype, p.BH, p.NC, p.LC, p.D, 3);
   char* base = align_up(static_cast<char*>(saved) + carve::factors_bytes(a.dtype, p.BH, p.NC, p.LC, p.D, 3));
   a.S_vk = base;
-  a.S_kv = align_up(base + states_bytes(s, p));
   mark(prof, 0, hs);
   hipError_t e = carve::launch_fwd_prep(a, hs);
   mark(prof, 1, hs);
@@ -350,9 +347,7 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
   char* base = align_up(static_cast<char*>(sv) + carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 3));
   const size_t states = states_bytes(s, p);
   a.fwd.S_vk = base;
-  a.fwd.S_kv = align_up(base + states);
-  a.dSg_vk = align_up(workspace);
-  a.dS_kv = align_up(static_cast<char*>(a.dSg_vk) + states);
+  a.dS_vk = align_up(workspace);
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;

@@ -496,40 +496,66 @@ struct StateTiles {
   static constexpr int jc(int j) { return SPW >= NVT ? j / NVT : 0; }
 };
 
-// The D x D state matrices handed to the chunk-gradient kernel use the fragment
-// order of frag_offset (two orientations of S[v][k]: "vk" rows v, contraction k;
-// "kv" rows k, contraction v).
+// The D x D state matrices handed to the chunk-gradient kernel, M[v][k], use the
+// fragment order of frag_offset with rows v and contraction k ("vk").
 
 // Scatter one accumulator group (lane (lr, lg) of state tile (vt, ct): the four
-// values M[16 vt + lr][16 ct + 4 lg + i]) into both fragment layouts.
+// values M[16 vt + lr][16 ct + 4 lg + i]) into the "vk" fragment order.
 template <typename T, int D>
 __device__ __forceinline__ void store_vk_group(T* vk, int vt, int ct, f32x4 x_vk) {
   const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
   store4(vk + frag_offset<D>(vt, ct >> 1, lr + 16 * (2 * (ct & 1) + (lg >> 1))) + 4 * (lg & 1), x_vk);
 }
-template <typename T, int D>
-__device__ __forceinline__ void store_state_frags(T* vk, T* kv, int vt, int ct, f32x4 x_vk, f32x4 x_kv) {
-  const int lane = lane_id(), lr = lane & 15, lg = lane >> 4;
-  store_vk_group<T, D>(vk, vt, ct, x_vk);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    kv[frag_offset<D>(ct, vt >> 1, (4 * lg + i) + 16 * (2 * (vt & 1) + (lr >> 3))) + (lr & 7)] = to<T>(x_kv[i]);
-}
 
-// Value slices of 32 or more rows copy whole "kv" fragments (and outputs) out of
-// their LDS copies with 16-byte stores (a fragment spans 32 rows of the slice).
+// Value slices of 32 or more rows copy whole fragments (and outputs) out of their
+// LDS copies with 16-byte stores (a fragment spans 32 rows of the slice).
 template <int VS> constexpr bool kWideSlice = VS >= 32;
 
-// "kv" fragments of a slice of rows v0..v0+VS-1 (VS a multiple of 32) of S[v][k],
-// from its row-major LDS copy Sb (row stride ld); one 16-byte store per lane each.
-template <typename T, int D, int VS, int NWAVES>
-__device__ __forceinline__ void store_kv_from_lds(T* kv, const T* Sb, int ld, int v0) {
-  const int lane = lane_id(), wave = wave_id();
-  for_wave_items<(D / 16) * (VS / 32), NWAVES>(wave, [&](int f) {
-    const int kt = f / (VS / 32), vb = f % (VS / 32);
-    const Frag<T> x = lds_frag_cols(Sb, ld, 16 * kt, 32 * vb);
-    *reinterpret_cast<Frag<T>*>(kv + frag_offset<D>(kt, v0 / 32 + vb, lane)) = x;
-  });
+// Operand of a contraction over v from the "vk" fragment order: the fragment for
+// rows k = 16 kc .. 16 kc + 15 and v block kb, lane c + 16 g receiving
+// M[32 kb + 8 g + e][16 kc + c], e = 0..7.  It is loaded as raw pieces (issued early)
+// and finished where it is used.
+//   bf16: two identity transposes (transpose_tile16), t = 0, 1; for transpose t, input
+//   row r carries M[32 kb + 8 (r / 4) + 4 t + r % 4][16 kc + 4 g ..], an 8-byte piece of
+//   stored lane (row % 16) + 16 (2 (kc % 2) + g / 2) at element 4 (g % 2), so that
+//   output value i of lane c + 16 g is M[32 kb + 8 g + 4 t + i][16 kc + c].
+//   fp32: eight element reads per lane, already in place.
+template <typename T> struct KmajorPieces;
+template <> struct KmajorPieces<bf16> { bf16x4 h[2]; };
+template <> struct KmajorPieces<float> { Frag<float> f; };
+
+template <int D>
+__device__ __forceinline__ KmajorPieces<bf16> load_kmajor_pieces(const bf16* vk, int kc, int kb) {
+  const int lane = lane_id(), r = lane & 15, g = lane >> 4;
+  KmajorPieces<bf16> p;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int v = 8 * (r >> 2) + 4 * t + (r & 3);          // row inside the 32-row block
+    p.h[t] = *reinterpret_cast<const bf16x4*>(
+        vk + frag_offset<D>(2 * kb + (v >> 4), kc >> 1, (v & 15) + 16 * (2 * (kc & 1) + (g >> 1))) + 4 * (g & 1));
+  }
+  return p;
 }
+template <int D>
+__device__ __forceinline__ KmajorPieces<float> load_kmajor_pieces(const float* vk, int kc, int kb) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  const int cc = 16 * (kc & 1) + c;      // column inside the 32-wide k block
+  KmajorPieces<float> p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int v = 8 * g + e;
+    const float x = vk[frag_offset<D>(2 * kb + (v >> 4), kc >> 1, (v & 15) + 16 * (cc >> 3)) + (cc & 7)];
+    if (e < 4) p.f.lo[e] = x;
+    else p.f.hi[e - 4] = x;
+  }
+  return p;
+}
+__device__ __forceinline__ Frag<bf16> kmajor_frag(const KmajorPieces<bf16>& p) {
+  const bf16x4 lo = transpose_tile16(p.h[0]), hi = transpose_tile16(p.h[1]);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ Frag<float> kmajor_frag(const KmajorPieces<float>& p) { return p.f; }
 
 }  // namespace carve

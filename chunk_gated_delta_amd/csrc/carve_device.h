@@ -138,6 +138,41 @@ __device__ __forceinline__ void mma(f32x4& c, const Frag<float>& a, const Frag<f
   for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[j], b.hi[j], c, 0, 0, 0);
 }
 
+// 16 x 16 bf16 tile transposed by one v_mfma_f32_16x16x16_bf16 against the identity.
+// That instruction takes A[r][4 g + i] from lane r + 16 g and returns C[4 g + i][c]
+// to lane c + 16 g (i = 0..3), so with B = I lane c + 16 g receives X[4 g + i][c] of
+// the tile X whose row r, columns 4 g .. 4 g + 3 lane r + 16 g passed in: four rows
+// of one column, exactly (products with 1 and 0).
+__device__ __forceinline__ bf16x4 transpose_tile16(bf16x4 x_row4) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  i16x4 eye;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? (short)0x3F80 : (short)0;   // bf16 1.0
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 t = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, x_row4), eye, z, 0, 0, 0);
+  bf16x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (bf16)t[i];
+  return r;
+}
+
+// fragment values e = 0..7 multiplied by (g0, g1)[e] (rounded once to the operand type)
+__device__ __forceinline__ Frag<bf16> scale_frag(const Frag<bf16>& f, f32x4 g0, f32x4 g1) {
+  Frag<bf16> r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r.v[e] = (bf16)((float)f.v[e] * g0[e]);
+    r.v[e + 4] = (bf16)((float)f.v[e + 4] * g1[e]);
+  }
+  return r;
+}
+__device__ __forceinline__ Frag<float> scale_frag(const Frag<float>& f, f32x4 g0, f32x4 g1) {
+  Frag<float> r;
+  r.lo = f.lo * g0;
+  r.hi = f.hi * g1;
+  return r;
+}
+
 // single fp32 MFMA step (k = 4): lane l supplies A[l%16][l/16] and B[l/16][l%16]
 __device__ __forceinline__ void mma_k4(f32x4& c, float a, float b) {
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

@@ -51,8 +51,7 @@ struct FwdArgs {
   const float* S0;        // may be null
   void* o;                // may be null (state-only pass)
   float* S_T;             // may be null
-  void* S_vk;             // may be null: state entering every chunk, fragment order, rows v (dtype)
-  void* S_kv;             // ... and rows k (both [ci][D*D], written together)
+  void* S_vk;             // may be null: state entering every chunk, [ci][D*D] dtype, fragment order rows v
   ChunkFactors f;
 };
 
@@ -67,11 +66,10 @@ struct ContentArgs {
 };
 
 struct BwdArgs {
-  FwdArgs fwd;            // forward inputs, factors and S_vk / S_kv (all required)
+  FwdArgs fwd;            // forward inputs, factors and S_vk (all required)
   const void* dO;
   const float* dS_T;      // may be null
-  void* dSg_vk;           // [ci][D*D] dtype: dS_{c+1} Diag(Gamma_L of chunk c), fragment order rows v
-  void* dS_kv;            // [ci][D*D] dtype: dS_{c+1}, fragment order rows k
+  void* dS_vk;            // [ci][D*D] dtype: dS_{c+1}, fragment order rows v
   void* dq;
   void* dk;
   void* dv;

@@ -242,17 +242,15 @@ __device__ __forceinline__ void state_store(const FwdArgs& a, int bh, int v0, co
   }
 }
 
-// Store the state entering chunk ci in the two fragment layouts of the backward.
-// Wide slices copy whole fragments out of the dtype copy Sb (rows v0.., in LDS):
-// "vk" fragments are 8 consecutive k of one row, "kv" fragments 8 consecutive rows
-// of one k column; both are one 16-byte store per lane.  Narrow slices scatter
-// the registers' accumulator groups.
+// Store the state entering chunk ci in the fragment order of the backward ("vk":
+// 8 consecutive k of one row v per lane).  Wide slices copy whole fragments out of
+// the dtype copy Sb (rows v0.., in LDS) with one 16-byte store per lane; narrow
+// slices scatter the registers' accumulator groups.
 template <typename T, int D, int VS>
 __device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW],
                                            const T* Sb) {
   using ST = StateTiles<D, VS>;
   T* vk = reinterpret_cast<T*>(a.S_vk) + ci * D * D;
-  T* kv = reinterpret_cast<T*>(a.S_kv) + ci * D * D;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
   if constexpr (kWideSlice<VS>) {
     constexpr int LDS_ = D + Pad<T>::v;
@@ -261,12 +259,11 @@ __device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, 
       const Frag<T> x = load_frag(Sb + (16 * vt + lr) * LDS_ + 32 * kb + 8 * lg);
       *reinterpret_cast<Frag<T>*>(vk + frag_offset<D>(v0 / 16 + vt, kb, lane)) = x;
     });
-    store_kv_from_lds<T, D, VS, kWaves>(kv, Sb, LDS_, v0);
   } else {
 #pragma unroll
     for (int jj = 0; jj < ST::SPW; ++jj) {
       const int st = wave * ST::SPW + jj, ct = st / ST::NVT, vt = st % ST::NVT;
-      store_state_frags<T, D>(vk, kv, v0 / 16 + vt, ct, S[jj], S[jj]);
+      store_vk_group<T, D>(vk, v0 / 16 + vt, ct, S[jj]);
     }
   }
 }
