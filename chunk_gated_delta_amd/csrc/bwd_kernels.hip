@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 //   s4 -W -> dO      s5 U             s6 dU
 //   (s4..s6 first stage the fp32 log g and b of the chunk)
 //   p0 P -> dT        p1 T (dtype)     p2 Tw = T diag(w)  p3 dP -> Z -> dA
-// T = (I + A)^-1 itself comes from the prep pass (fp32, one LC x LC block per chunk).
+// T = (I + A)^-1 itself comes from the prep pass (dtype, one LC x LC block per chunk).
 // Tiles of [token][key] and [token][value] results are owned by column: wave w
 // computes every token tile of key/value tiles ct = w*CPW .. w*CPW+CPW-1, so the
 // cumulative retention Gamma of those columns stays in that wave's registers
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   static_assert(6 * Lay::S1 + sizeof(float) * LC * LDG <= Lay::small, "b staging exceeds the slots");
   // All of the chunk's global loads are issued here, from clamped rows (n >= 1), before
   // anything waits on them: the staged inputs, dO (written to LDS once its slot is
-  // free), the chunk's fp32 inverse T = (I + A)^-1 from the prep pass, and w.
+  // free), the chunk's inverse T = (I + A)^-1 from the prep pass (dtype), and w.
   constexpr int PR = D / 8;                      // 8-element pieces per token row
   constexpr int NST = LC * PR / NT;              // pieces per thread
   static_assert(NST * NT == LC * PR, "pieces must split evenly over the threads");
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   f32x4 tpre[NTP];
 #pragma unroll
   for (int u = 0; u < NTP; ++u)
-    tpre[u] = *reinterpret_cast<const f32x4*>(f.f.Tinv + ci * LC * LC + 4 * min(tid + NT * u, TP - 1));
+    tpre[u] = load4f(reinterpret_cast<const T*>(f.f.Tt) + ci * LC * LC + 4 * min(tid + NT * u, TP - 1));
   // k, q, v (dtype) into the K+, Q+, V slots; log g into slots 4-5 and b from slot 6 on
   // (fp32, row stride D+4).  Tokens past the end read as k = q = v = 0, log g = 0, b = 1.
   if (tid < LC) wL[tid] = (tid < n) ? wv : 0.f;

@@ -374,13 +374,13 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   __syncthreads();
 
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
-  // modes also keep the fp32 T of the chunk
+  // modes also keep that copy of the chunk (row-major [LC][LC])
   triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
   for (int idx = tid; idx < LC * LC / 4; idx += NT) {
     const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
     const f32x4 t4 = ((s >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);
     store4(Tb + r * LDL + s, t4);
-    if (BWD) *reinterpret_cast<f32x4*>(a.f.Tinv + (ci * LC + r) * LC + s) = t4;
+    if (BWD) store4(reinterpret_cast<T*>(a.f.Tt) + (ci * LC + r) * LC + s, t4);
   }
   __syncthreads();
 

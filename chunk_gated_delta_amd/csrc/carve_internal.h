@@ -23,7 +23,7 @@ namespace carve {
 //   QtT Q~^T [D][LC], frag<LC>
 //   WnT (-W)^T [D][LC], frag<LC>
 //   Kf  K-> [LC][D], frag<D>
-//   Tinv [ci][LC][LC] row-major, T = (I + A)^-1, fp32
+//   Tt  [ci][LC][LC] row-major, T = (I + A)^-1 (dtype)
 // Prep modes: 1 = forward only, 2 = backward only (no Qt / OiT), 3 = both.
 struct ChunkFactors {
   void* Wn;
@@ -35,7 +35,7 @@ struct ChunkFactors {
   void* QtT;
   void* WnT;
   void* Kf;
-  float* Tinv;            // [ci][LC][LC] T = (I + A)^-1 in fp32 (backward modes)
+  void* Tt;               // [ci][LC][LC] T = (I + A)^-1 in the operand type (backward modes)
 };
 
 struct FwdArgs {

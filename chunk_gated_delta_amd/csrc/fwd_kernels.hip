@@ -454,13 +454,13 @@ static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {  // one [
 
 // Factor blocks in the workspace: -W, K->^T, Ubar^T always; Q~, P Ubar with the
 // forward mode; (-W)^T, Q~^T, K-> with the backward mode; then Gamma_L, and with the
-// backward mode the fp32 inverse T of every chunk.
+// backward mode the inverse T of every chunk (LC x LC, dtype).
 static int factor_blocks(int mode) { return 3 + ((mode & 1) ? 2 : 0) + ((mode & 2) ? 3 : 0); }
 static size_t gl_block(int BH, int NC, int D) { return ((size_t)BH * NC * D * sizeof(float) + 255) & ~size_t(255); }
 
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode) {
   return factor_blocks(mode) * factor_block(dtype, BH, NC, LC, D) + gl_block(BH, NC, D) +
-         ((mode & 2) ? (size_t)BH * NC * LC * LC * sizeof(float) : 0);
+         ((mode & 2) ? (size_t)BH * NC * LC * LC * (dtype ? 2 : 4) : 0);
 }
 
 ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode) {
@@ -477,7 +477,7 @@ ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, i
   f.QtT = (mode & 2) ? p + blk * i++ : nullptr;
   f.Kf = (mode & 2) ? p + blk * i++ : nullptr;
   f.gL = reinterpret_cast<float*>(p + blk * i);
-  f.Tinv = (mode & 2) ? reinterpret_cast<float*>(p + blk * i + gl_block(BH, NC, D)) : nullptr;
+  f.Tt = (mode & 2) ? p + blk * i + gl_block(BH, NC, D) : nullptr;
   return f;
 }
 
