@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=2048)
     p.add_argument("--no-content", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the long-context forward")
+    p.add_argument("--no-decode", action="store_true", help="skip the recurrent decode step")
     return p.parse_args()
 
 
@@ -254,6 +255,10 @@ def main():
         extra["content_fwd_tokens_per_s"] = wc.B * wc.T / (cms * 1e-3)
         del cq, ck, cv, cf, cont, ws_c, co
 
+    # recurrent decode step (one token per sequence and head, state updated in place)
+    if not args.no_decode:
+        extra["decode"] = {f"B{db}_H{H}": decode_bench(db, H, D, dev) for db in (B, 256)}
+
     # roofline of the dominant stage
     alg = algorithmic(wl, with_bwd)
     units = B * H * T
@@ -304,6 +309,41 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line))
+
+
+def decode_bench(B, H, D, dev, nrep=200):
+    """Time carve.decode_step at batch B (bf16 q/k/v, fp32 gates and state, d = D): per step,
+    one token for each of B sequences; the state (B*H*D*D fp32) is read and written once."""
+    import torch
+    from chunk_gated_delta_amd import carve
+    from chunk_gated_delta_amd.synth import random_inputs
+    inp = random_inputs(B, H, 1, D, D, dtype="bf16", seed=1006, erase="sigmoid", dists="softplus_decay")
+
+    def t_(key, bf):
+        if bf:
+            x = torch.from_numpy(np.ascontiguousarray(inp[key + "_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            x = torch.from_numpy(np.ascontiguousarray(inp[key], dtype=np.float32)).to(dev)
+        return x[:, :, 0].contiguous()
+    q, k, v = t_("q", True), t_("k", True), t_("v", True)
+    lg, b = t_("log_g", False), t_("b", False)
+    w = torch.from_numpy(np.ascontiguousarray(inp["w"][:, :, 0], dtype=np.float32)).to(dev)
+    S = torch.zeros((B, H, D, D), dtype=torch.float32, device=dev)
+    o = torch.empty_like(v)
+    for _ in range(10):
+        carve.decode_step(q, k, v, lg, w, S, b=b, o=o)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nrep):
+        carve.decode_step(q, k, v, lg, w, S, b=b, o=o)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / nrep
+    state_bytes = 2 * 4 * B * H * D * D            # the state read and written once per step
+    return {"us_per_step": round(us, 3), "tokens_per_s": B / (us * 1e-6),
+            "state_GB_per_s": round(state_bytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(state_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def es_do(wl):

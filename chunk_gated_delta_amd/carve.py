@@ -29,6 +29,12 @@ class carve_content(ctypes.Structure):
                 ("R", ctypes.c_int), ("m0", ctypes.c_void_p), ("m_out", ctypes.c_void_p)]
 
 
+class carve_decode_content(ctypes.Structure):
+    _fields_ = [("b_x", ctypes.c_void_p), ("U1", ctypes.c_void_p), ("U2", ctypes.c_void_p),
+                ("R", ctypes.c_int), ("m_in", ctypes.c_void_p), ("m_out", ctypes.c_void_p),
+                ("csum", ctypes.c_void_p), ("pos", ctypes.c_int)]
+
+
 class carve_profile(ctypes.Structure):
     _fields_ = [("events", ctypes.c_void_p * 9), ("n_events", ctypes.c_int)]
 
@@ -78,6 +84,9 @@ def load_library():
     lib.carve_bwd_saved.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                     vp, pp]
     lib.carve_bwd_saved.restype = i
+    dcp = ctypes.POINTER(carve_decode_content)
+    lib.carve_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, dcp, vp, vp]
+    lib.carve_decode_step.restype = i
     lib.carve_status_string.argtypes = [i]
     lib.carve_status_string.restype = ctypes.c_char_p
     lib.carve_abi_version.argtypes = []
@@ -294,3 +303,51 @@ def bwd_saved(q, k, v, log_g, w, dO, saved, b=None, dS_T=None, L=64, want_dS0=Tr
                                ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_bwd_saved")
     return g
+
+
+def decode_step(q, k, v, log_g, w, S, b=None, L=64, content=None, o=None):
+    """One recurrent decode token per (batch, head); S [B,H,Dv,Dk] float32 is updated in place.
+
+    q, k [B,H,Dk], v [B,H,Dv] (float32 or bfloat16); log_g, b [B,H,Dk] float32; w [B,H]
+    float32.  content is None or a dict with b_x [B,H,Dk], U1 [H,R,Dv] / U2 [H,Dk,R] (or None),
+    m_in [B,H,Dv] (or None), csum [B,H,Dv] (updated in place) and pos (tokens of the current
+    chunk of L before this one).  Returns (o [B,H,Dv], m_out [B,H,Dv] or None)."""
+    lib = load_library()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    _check(k, "k", (B, H, Dk), dt, dev)
+    _check(v, "v", (B, H, Dv), dt, dev)
+    _check(log_g, "log_g", (B, H, Dk), torch.float32, dev)
+    _check(b, "b", (B, H, Dk), torch.float32, dev)
+    _check(w, "w", (B, H), torch.float32, dev)
+    _check(S, "S", (B, H, Dv, Dk), torch.float32, dev)
+    s = carve_shape(B, H, 1, Dk, Dv, L, _dtype_code(q))
+    cs = None
+    m_out = None
+    if content is not None:
+        bx, U1, U2 = content["b_x"], content.get("U1"), content.get("U2")
+        m_in, csum = content.get("m_in"), content["csum"]
+        _check(bx, "b_x", (B, H, Dk), torch.float32, dev)
+        R = 0
+        if U1 is not None:
+            R = U1.shape[1]
+            _check(U1, "U1", (H, R, Dv), torch.float32, dev)
+            _check(U2, "U2", (H, Dk, R), torch.float32, dev)
+        _check(m_in, "m_in", (B, H, Dv), torch.float32, dev)
+        _check(csum, "csum", (B, H, Dv), torch.float32, dev)
+        m_out = content.get("m_out")
+        if m_out is None:
+            m_out = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+        _check(m_out, "m_out", (B, H, Dv), torch.float32, dev)
+        cs = carve_decode_content(bx.data_ptr(), None if U1 is None else U1.data_ptr(),
+                                  None if U2 is None else U2.data_ptr(), R,
+                                  None if m_in is None else m_in.data_ptr(), m_out.data_ptr(),
+                                  csum.data_ptr(), int(content.get("pos", 0)))
+    if o is None:
+        o = torch.empty((B, H, Dv), dtype=dt, device=dev)
+    code = lib.carve_decode_step(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w),
+                                 _ptr(S), ctypes.byref(cs) if cs is not None else None, _ptr(o), _stream(dev))
+    _raise(code, "carve_decode_step")
+    return o, m_out

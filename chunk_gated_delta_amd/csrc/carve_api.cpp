@@ -365,6 +365,55 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 
+carve_status carve_decode_step(const carve_shape* s, const void* q, const void* k, const void* v,
+                               const float* log_g, const float* b, const float* w, float* S,
+                               const carve_decode_content* content, void* o, void* stream) {
+  if (!s || s->T != 1) return CARVE_ERR_INVALID_ARG;
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  if (p.BH == 0) return CARVE_OK;
+  if (!q || !k || !v || !log_g || !w || !S || !o) return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {(const void*)q, k, (const void*)log_g, (const void*)b, (const void*)S})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const carve_decode_content* c = content;
+  if (c) {
+    if (b || !c->b_x || !c->m_out || !c->csum) return CARVE_ERR_INVALID_ARG;
+    if ((c->U1 == nullptr) != (c->U2 == nullptr)) return CARVE_ERR_INVALID_ARG;
+    if (c->U1 && (c->R < 1 || c->R > 64)) return CARVE_ERR_INVALID_ARG;
+    if (c->pos < 0 || c->pos >= s->L) return CARVE_ERR_INVALID_ARG;
+    if (c->m_in && c->m_in == c->m_out) return CARVE_ERR_INVALID_ARG;
+    if (!aligned16(c->b_x)) return CARVE_ERR_INVALID_ARG;
+  }
+  carve::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = s->B;
+  a.H = s->H;
+  a.Dk = s->Dk;
+  a.Dv = s->Dv;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.log_g = log_g;
+  a.b = b;
+  a.w = w;
+  a.S = S;
+  a.o = o;
+  if (c) {
+    a.b_x = c->b_x;
+    a.U1 = c->U1;
+    a.U2 = c->U2;
+    a.R = c->U1 ? c->R : 0;
+    a.m_in = c->m_in;
+    a.m_out = c->m_out;
+    a.csum = c->csum;
+    a.L = s->L;
+    a.pos = c->pos;
+  }
+  hipError_t e = carve::launch_decode(a, s->dtype == CARVE_BF16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
 const char* carve_status_string(carve_status st) {
   switch (st) {
     case CARVE_OK: return "CARVE_OK";

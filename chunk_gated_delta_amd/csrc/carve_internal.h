@@ -79,6 +79,28 @@ struct BwdArgs {
   float* dS0;             // may be null
 };
 
+// One recurrent decode step (one token per batch and head), state updated in place.
+struct DecodeArgs {
+  int B, H, Dk, Dv;
+  const void* q;          // [B,H,Dk] dtype
+  const void* k;          // [B,H,Dk] dtype
+  const void* v;          // [B,H,Dv] dtype
+  const float* log_g;     // [B,H,Dk]
+  const float* b;         // [B,H,Dk] or null (= 1); null on the content path
+  const float* w;         // [B,H]
+  float* S;               // [B,H,Dv,Dk] read and overwritten
+  void* o;                // [B,H,Dv] dtype
+  // content-aware erase (b_x null: token-only gates)
+  const float* b_x;       // [B,H,Dk]
+  const float* U1;        // [H,R,Dv] or null (with U2)
+  const float* U2;        // [H,Dk,R] or null
+  int R;
+  const float* m_in;      // [B,H,Dv] or null (= 0)
+  float* m_out;           // [B,H,Dv]
+  float* csum;            // [B,H,Dv] running sum of the current chunk's outputs
+  int L, pos;             // content period and the token's position inside it
+};
+
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode);
 ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode);
 
@@ -88,5 +110,6 @@ hipError_t launch_fwd_state(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_content(const FwdArgs& a, const ContentArgs& c, hipStream_t st);
 hipError_t launch_bwd_state(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
 
 }  // namespace carve

@@ -202,6 +202,47 @@ carve_status carve_bwd_saved(const carve_shape* s,
                              void* workspace, size_t workspace_bytes, void* stream,
                              const carve_profile* profile);
 
+/*
+ * Recurrent decode: one new token per (batch, head), the O(Dv Dk) per-token form
+ * of the same recurrence (comparison table of the notes, section 3), with the
+ * state updated in place.  shape->T must be 1; shape->L is the content period
+ * (ignored for token-only gates).
+ *   q, k   (device) [B,H,Dk] dtype            v (device) [B,H,Dv] dtype
+ *   log_g  (device) [B,H,Dk] float, <= 0      b (device) [B,H,Dk] float or NULL (= 1)
+ *   w      (device) [B,H]    float
+ *   S      (device) [B,H,Dv,Dk] float         state before the token; overwritten with the
+ *                                              state after it (S_T of a carve_fwd prefill
+ *                                              continues a sequence)
+ *   content NULL (token-only gates) or the content-aware erase carry below
+ *   o      (device) [B,H,Dv] dtype            output o = S q of the updated state (written)
+ * Content-aware erase (b must be NULL): this token's gate is
+ * b = sigmoid(b_x + U2 (U1 m_in)) with m_in the mean output of the previous
+ * complete chunk of L tokens; `csum` holds the sum of the current chunk's outputs
+ * so far and `pos` the number of them (0 <= pos < L; at pos = 0 csum is not read).
+ * The call writes csum (the sum including this token, or 0 when the token
+ * completes the chunk) and m_out (m_in again, or this chunk's mean when pos = L-1;
+ * m_out must not alias m_in: other workgroups of the head still read m_in).  A
+ * carve_fwd prefill of a whole number of chunks hands over with m_in = its m_out,
+ * pos = 0.  Rows of one head are updated by different workgroups: S, o, csum and
+ * m_out must not alias any input.
+ */
+typedef struct {
+  const float* b_x;   /* (device) [B,H,Dk] erase pre-activation of this token (required)   */
+  const float* U1;    /* (device) [H,R,Dv] or NULL; U1 and U2 both NULL = no projection     */
+  const float* U2;    /* (device) [H,Dk,R] or NULL                                          */
+  int R;              /* rank, 1..64 (ignored without projection)                            */
+  const float* m_in;  /* (device) [B,H,Dv] mean output of the previous chunk, or NULL (= 0)  */
+  float* m_out;       /* (device) [B,H,Dv] written (see above)                               */
+  float* csum;        /* (device) [B,H,Dv] read when pos > 0, written                        */
+  int pos;            /* tokens of the current chunk before this one                          */
+} carve_decode_content;
+
+carve_status carve_decode_step(const carve_shape* s,
+                               const void* q, const void* k, const void* v,
+                               const float* log_g, const float* b, const float* w,
+                               float* S, const carve_decode_content* content,
+                               void* o, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* carve_status_string(carve_status st);
 

@@ -134,3 +134,31 @@ def test_saved_pair_checks(lib):
     assert lib.carve_bwd_saved(*args(need - 1, wsz, None)) == WORKSPACE
     assert lib.carve_bwd_saved(*args(need, wsz - 1, None)) == WORKSPACE
     assert lib.carve_bwd_saved(*args(need, wsz, FAKE)) == INVALID
+
+
+def call_decode(lib, s, q=FAKE, k=FAKE, v=FAKE, log_g=FAKE, b=None, w=FAKE, S=FAKE, content=None, o=FAKE):
+    return lib.carve_decode_step(ctypes.byref(s), q, k, v, log_g, b, w, S,
+                                 ctypes.byref(content) if content is not None else None, o, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert call_decode(lib, shape(T=2)) == INVALID                 # one token per call
+    assert call_decode(lib, shape(T=1, D=96)) == UNSUPPORTED
+    assert call_decode(lib, shape(T=1), S=None) == INVALID
+    assert call_decode(lib, shape(T=1), S=FAKE + 8) == INVALID     # state must be 16-byte aligned
+    assert call_decode(lib, shape(T=1), o=None) == INVALID
+    assert call_decode(lib, shape(T=1, B=0), q=None, k=None, v=None, log_g=None, w=None, S=None, o=None) == OK
+    c = carve.carve_decode_content(FAKE, None, None, 0, FAKE, FAKE + 256, FAKE + 512, 0)
+    assert call_decode(lib, shape(T=1, L=4), content=c, b=FAKE) == INVALID    # b comes from the content gate
+    bad_pos = carve.carve_decode_content(FAKE, None, None, 0, FAKE, FAKE + 256, FAKE + 512, 4)
+    assert call_decode(lib, shape(T=1, L=4), content=bad_pos) == INVALID
+    alias = carve.carve_decode_content(FAKE, None, None, 0, FAKE, FAKE, FAKE + 512, 0)
+    assert call_decode(lib, shape(T=1, L=4), content=alias) == INVALID        # m_out aliases m_in
+    half = carve.carve_decode_content(FAKE, FAKE, None, 16, None, FAKE + 256, FAKE + 512, 0)
+    assert call_decode(lib, shape(T=1, L=4), content=half) == INVALID         # U1 without U2
+    rank = carve.carve_decode_content(FAKE, FAKE, FAKE, 65, None, FAKE + 256, FAKE + 512, 0)
+    assert call_decode(lib, shape(T=1, L=4), content=rank) == INVALID
+    no_sum = carve.carve_decode_content(FAKE, None, None, 0, None, FAKE + 256, None, 0)
+    assert call_decode(lib, shape(T=1, L=4), content=no_sum) == INVALID
+    assert call_decode(lib, shape(T=1), k=FAKE + 4) == INVALID                # misaligned vectors
+    assert call_decode(lib, shape(T=1), log_g=FAKE + 4) == INVALID
