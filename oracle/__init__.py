@@ -3,4 +3,4 @@
 Test infrastructure only: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library's product path.
 """
-from .carve_oracle import forward, backward  # noqa: F401
+from .carve_oracle import forward, backward, backward_content  # noqa: F401

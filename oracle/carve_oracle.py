@@ -35,6 +35,11 @@ caller L2-normalises q and k.
 
 Arrays are numpy float64 with leading [B, H] axes; the loops run over tokens
 and are vectorised over (B*H) heads only.
+
+Functions: forward (token-serial forward, token-only or content-aware gates),
+backward (reverse mode of the token-only forward), backward_content (reverse
+mode of the content-aware forward, including the projection and the carried-in
+mean).
 """
 
 import numpy as np
@@ -222,5 +227,121 @@ def backward(q, k, v, log_g, w, dO, b=None, S0=None, dS_T=None, segment=64):
         "db": None if db is None else db.reshape(B, H, T, Dk),
         "dw": dw.reshape(B, H, T),
         "dS0": dS.reshape(B, H, Dv, Dk),
+    }
+    return out
+
+
+def backward_content(q, k, v, log_g, w, dO, content, S0=None, dS_T=None, dm_out=None, L=64):
+    """Reverse-mode gradients of the content-aware forward pass.
+
+    content: dict with 'b_x' [B,H,T,Dk], 'U1' [H,R,Dv] / 'U2' [H,Dk,R] (both None:
+    no projection) and 'm0' [B,H,Dv] (None: zero), as for forward().  The loss is
+    <dO, o> + <dS_T, S_T> + <dm_out, m_out> (dS_T, dm_out None: zero).  Returns a
+    dict with dq, dk, dv, dlog_g, db_x, dw, dU1 [H,R,Dv], dU2 [H,Dk,R] (None
+    without projection; summed over the batch), dm0 [B,H,Dv] and dS0.
+
+    The chain, in the order of the pages' content-aware erase (notes section 2.2):
+    chunk c's gate is b = sigmoid(x), x = b_x + z_c, z_c = U2 r_c, r_c = U1 m_{c-1},
+    and m_{c-1} is the mean of chunk c-1's outputs.  So, going backwards, chunk c's
+    gate gradient dx_t = db_t b_t (1 - b_t) gives dz_c = sum_t dx_t, then
+    dU2 += dz_c r_c^T, dr_c = U2^T dz_c, dU1 += dr_c m_{c-1}^T and dm_{c-1} = U1^T dr_c,
+    which reaches every output of chunk c-1 as dm_{c-1} / (its token count) before
+    that chunk is swept (chunk 0's goes to m0).  Inside a chunk the per-token
+    steps are those of backward() with b_t in place of the erase input.
+    """
+    q, k, v, log_g, w, dO = map(_as64, (q, k, v, log_g, w, dO))
+    B, H, T, Dk = k.shape
+    Dv = v.shape[-1]
+    BH = B * H
+    qf, kf, vf = q.reshape(BH, T, Dk), k.reshape(BH, T, Dk), v.reshape(BH, T, Dv)
+    gf, wf, dOf = log_g.reshape(BH, T, Dk), w.reshape(BH, T), dO.reshape(BH, T, Dv)
+    bx = _as64(content["b_x"]).reshape(BH, T, Dk)
+    U1, U2 = content.get("U1"), content.get("U2")
+    if (U1 is None) != (U2 is None):
+        raise ValueError("U1 and U2 must both be given or both be None")
+    proj = U1 is not None
+    if proj:
+        R = np.shape(U1)[1]
+        U1h = np.broadcast_to(_as64(U1)[None], (B,) + np.shape(U1)).reshape(BH, R, Dv)
+        U2h = np.broadcast_to(_as64(U2)[None], (B,) + np.shape(U2)).reshape(BH, Dk, R)
+    m0 = content.get("m0")
+    m_prev = np.zeros((BH, Dv)) if m0 is None else _as64(m0).reshape(BH, Dv).copy()
+
+    # forward sweep: the state entering every chunk, each chunk's gates and the mean
+    # output m_{c-1} its gate was formed from
+    NCh = (T + L - 1) // L
+    S = np.zeros((BH, Dv, Dk)) if S0 is None else _as64(S0).reshape(BH, Dv, Dk).copy()
+    S_in, m_in, bgate = [], [], np.zeros((BH, T, Dk))
+    for c in range(NCh):
+        t0, t1 = c * L, min((c + 1) * L, T)
+        S_in.append(S.copy())
+        m_in.append(m_prev.copy())
+        z = np.einsum("nkr,nr->nk", U2h, np.einsum("nrv,nv->nr", U1h, m_prev)) if proj else np.zeros((BH, Dk))
+        csum = np.zeros((BH, Dv))
+        for t in range(t0, t1):
+            bgate[:, t] = _sigmoid(bx[:, t] + z)
+            a = np.exp(gf[:, t]) * bgate[:, t]
+            P = S * a[:, None, :]
+            e = vf[:, t] - np.einsum("nvk,nk->nv", P, kf[:, t])
+            S = P + wf[:, t][:, None, None] * e[:, :, None] * kf[:, t][:, None, :]
+            csum += np.einsum("nvk,nk->nv", S, qf[:, t])
+        m_prev = csum / (t1 - t0)
+
+    dq, dk, dv = np.zeros((BH, T, Dk)), np.zeros((BH, T, Dk)), np.zeros((BH, T, Dv))
+    dlog_g, dbx, dw = np.zeros((BH, T, Dk)), np.zeros((BH, T, Dk)), np.zeros((BH, T))
+    dU1 = np.zeros((BH, R, Dv)) if proj else None
+    dU2 = np.zeros((BH, Dk, R)) if proj else None
+    dS = np.zeros((BH, Dv, Dk)) if dS_T is None else _as64(dS_T).reshape(BH, Dv, Dk).copy()
+    # gradient w.r.t. the mean output of the chunk being swept (the last one: dm_out)
+    dm = np.zeros((BH, Dv)) if dm_out is None else _as64(dm_out).reshape(BH, Dv).copy()
+
+    for c in range(NCh - 1, -1, -1):
+        t0, t1 = c * L, min((c + 1) * L, T)
+        dOc = dOf[:, t0:t1] + (dm / (t1 - t0))[:, None, :]     # m_c's gradient reaches each output
+        # states before every token of the chunk
+        states = [S_in[c]]
+        for t in range(t0, t1):
+            a = np.exp(gf[:, t]) * bgate[:, t]
+            P = states[-1] * a[:, None, :]
+            e = vf[:, t] - np.einsum("nvk,nk->nv", P, kf[:, t])
+            states.append(P + wf[:, t][:, None, None] * e[:, :, None] * kf[:, t][:, None, :])
+        dz = np.zeros((BH, Dk))
+        for t in range(t1 - 1, t0 - 1, -1):
+            S_prev, S_t = states[t - t0], states[t - t0 + 1]
+            g = np.exp(gf[:, t])
+            bt = bgate[:, t]
+            a = g * bt
+            kt, vt, qt, wt, dot = kf[:, t], vf[:, t], qf[:, t], wf[:, t], dOc[:, t - t0]
+            P = S_prev * a[:, None, :]
+            e = vt - np.einsum("nvk,nk->nv", P, kt)
+            dS = dS + dot[:, :, None] * qt[:, None, :]
+            dq[:, t] = np.einsum("nvk,nv->nk", S_t, dot)
+            r = np.einsum("nvk,nk->nv", dS, kt)
+            dv[:, t] = wt[:, None] * r
+            dw[:, t] = np.einsum("nv,nv->n", e, r)
+            dk[:, t] = wt[:, None] * (np.einsum("nvk,nv->nk", dS, e) - np.einsum("nvk,nv->nk", P, r))
+            dP = dS - wt[:, None, None] * r[:, :, None] * kt[:, None, :]
+            da = np.einsum("nvk,nvk->nk", S_prev, dP)
+            dlog_g[:, t] = a * da
+            dx = g * da * bt * (1.0 - bt)                  # through b = sigmoid(b_x + z_c)
+            dbx[:, t] = dx
+            dz += dx
+            dS = dP * a[:, None, :]
+        # z_c = U2 U1 m_{c-1}
+        if proj:
+            rc = np.einsum("nrv,nv->nr", U1h, m_in[c])
+            dU2 += np.einsum("nk,nr->nkr", dz, rc)
+            dr = np.einsum("nkr,nk->nr", U2h, dz)
+            dU1 += np.einsum("nr,nv->nrv", dr, m_in[c])
+            dm = np.einsum("nrv,nr->nv", U1h, dr)
+        else:
+            dm = np.zeros((BH, Dv))
+
+    out = {
+        "dq": dq.reshape(B, H, T, Dk), "dk": dk.reshape(B, H, T, Dk), "dv": dv.reshape(B, H, T, Dv),
+        "dlog_g": dlog_g.reshape(B, H, T, Dk), "db_x": dbx.reshape(B, H, T, Dk), "dw": dw.reshape(B, H, T),
+        "dU1": None if not proj else dU1.reshape(B, H, R, Dv).sum(axis=0),
+        "dU2": None if not proj else dU2.reshape(B, H, Dk, R).sum(axis=0),
+        "dm0": dm.reshape(B, H, Dv), "dS0": dS.reshape(B, H, Dv, Dk),
     }
     return out

@@ -14,7 +14,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import forward, backward
+from oracle import forward, backward, backward_content
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -391,3 +391,85 @@ def test_backward_segmenting_is_invisible():
     g2 = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], segment=64)
     for key in g1:
         np.testing.assert_allclose(g1[key], g2[key], rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------- content-aware backward pins
+
+def content_case(rng, B=1, H=2, T=11, D=4, R=3, uscale=0.8):
+    c = rand_case(rng, B=B, H=H, T=T, Dk=D, Dv=D, unit_keys=False, with_b=False)
+    c["b_x"] = rng.normal(1.0, 1.0, (B, H, T, D))
+    c["U1"] = rng.standard_normal((H, R, D)) * uscale
+    c["U2"] = rng.standard_normal((H, D, R)) * uscale
+    c["m0"] = rng.standard_normal((B, H, D))
+    return c
+
+
+def _content_loss(c, dO, dS_T, dm_out, L):
+    cont = {"b_x": c["b_x"], "U1": c["U1"], "U2": c["U2"], "m0": c["m0"]}
+    o, S_T, m = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], S0=c["S0"], L=L, content=cont)
+    return np.sum(o * dO) + np.sum(S_T * dS_T) + np.sum(m * dm_out)
+
+
+@pytest.mark.parametrize("seed,T,L", [(30, 11, 4), (31, 9, 3), (32, 6, 8)])
+def test_content_backward_matches_finite_differences(seed, T, L):
+    """Every input, including the projection, the carried-in mean and S0, against
+    central differences of <dO,o> + <dS_T,S_T> + <dm_out,m_out> (ragged last chunk,
+    several chunks, and a single chunk)."""
+    rng = np.random.default_rng(seed)
+    c = content_case(rng, T=T)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+    dm_out = rng.standard_normal(c["m0"].shape)
+    g = backward_content(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO,
+                         {"b_x": c["b_x"], "U1": c["U1"], "U2": c["U2"], "m0": c["m0"]},
+                         S0=c["S0"], dS_T=dS_T, dm_out=dm_out, L=L)
+    eps = 1e-6
+    for name, gname in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_g", "dlog_g"), ("b_x", "db_x"), ("w", "dw"),
+                        ("U1", "dU1"), ("U2", "dU2"), ("m0", "dm0"), ("S0", "dS0")]:
+        x = c[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = _content_loss(c, dO, dS_T, dm_out, L)
+            x[i] = old - eps
+            lm = _content_loss(c, dO, dS_T, dm_out, L)
+            x[i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
+
+
+def test_content_backward_zero_projection_is_token_only():
+    """With U1 = U2 = 0 the gate is b = sigmoid(b_x) in every chunk: the gradients are
+    the token-only backward's with that b, db_x = db * b (1 - b), and nothing flows into
+    the projection or the carried-in mean."""
+    rng = np.random.default_rng(33)
+    c = content_case(rng, B=2, H=2, T=21, D=5)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+    bz = 1.0 / (1.0 + np.exp(-c["b_x"]))
+    ref = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=bz, S0=c["S0"], dS_T=dS_T)
+    for U1, U2 in ((np.zeros_like(c["U1"]), np.zeros_like(c["U2"])), (None, None)):
+        g = backward_content(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO,
+                             {"b_x": c["b_x"], "U1": U1, "U2": U2, "m0": c["m0"]}, S0=c["S0"], dS_T=dS_T, L=4)
+        for key in ("dq", "dk", "dv", "dlog_g", "dw", "dS0"):
+            np.testing.assert_allclose(g[key], ref[key], rtol=1e-12, atol=1e-13, err_msg=key)
+        np.testing.assert_allclose(g["db_x"], ref["db"] * bz * (1 - bz), rtol=1e-12, atol=1e-13)
+        assert np.all(g["dm0"] == 0)
+        if U1 is not None:
+            assert np.all(g["dU1"] == 0) and np.all(g["dU2"] == 0)
+
+
+def test_content_backward_first_chunk_gradient_of_m0():
+    """In a single chunk, m0 enters only through z = U2 U1 m0, so
+    dm0 = U1^T U2^T sum_t db_x,t exactly (per head, no batch sum)."""
+    rng = np.random.default_rng(34)
+    c = content_case(rng, B=2, H=2, T=5, D=4)
+    dO = rng.standard_normal(c["v"].shape)
+    g = backward_content(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO,
+                         {"b_x": c["b_x"], "U1": c["U1"], "U2": c["U2"], "m0": c["m0"]}, S0=c["S0"], L=8)
+    dz = g["db_x"].sum(axis=2)                                   # [B,H,Dk]
+    want = np.einsum("hrv,hkr,bhk->bhv", c["U1"], c["U2"], dz)
+    np.testing.assert_allclose(g["dm0"], want, rtol=1e-12, atol=1e-13)
