@@ -84,6 +84,11 @@ def load_library():
     lib.carve_bwd_saved.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                     vp, pp]
     lib.carve_bwd_saved.restype = i
+    lib.carve_bwd_content_workspace_size.argtypes = [sp, cp]
+    lib.carve_bwd_content_workspace_size.restype = sz
+    lib.carve_bwd_content.argtypes = [sp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, sz, vp]
+    lib.carve_bwd_content.restype = i
     dcp = ctypes.POINTER(carve_decode_content)
     lib.carve_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, dcp, vp, vp]
     lib.carve_decode_step.restype = i
@@ -302,6 +307,52 @@ def bwd_saved(q, k, v, log_g, w, dO, saved, b=None, dS_T=None, L=64, want_dS0=Tr
                                workspace.numel(), _stream(dev),
                                ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_bwd_saved")
+    return g
+
+
+def bwd_content(q, k, v, log_g, w, dO, content, S0=None, dS_T=None, dm_out=None, L=64, want_dS0=True,
+                want_dm0=True, workspace=None):
+    """Gradients of the content-aware forward: dict with dq, dk, dv, dlog_g, db_x, dw,
+    dU1 / dU2 (None without projection), dm0 and dS0 (None unless asked for).
+    content: dict with b_x, U1, U2 (or None) and m0 (or None), as for fwd()."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    _check(k, "k", (B, H, T, Dk), dt, dev)
+    _check(v, "v", (B, H, T, Dv), dt, dev)
+    _check(dO, "dO", (B, H, T, Dv), dt, dev)
+    _check(log_g, "log_g", (B, H, T, Dk), torch.float32, dev)
+    _check(w, "w", (B, H, T), torch.float32, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    _check(dm_out, "dm_out", (B, H, Dv), torch.float32, dev)
+    bx, U1, U2, m0 = content["b_x"], content.get("U1"), content.get("U2"), content.get("m0")
+    _check(bx, "b_x", (B, H, T, Dk), torch.float32, dev)
+    R = 0
+    if U1 is not None:
+        R = U1.shape[1]
+        _check(U1, "U1", (H, R, Dv), torch.float32, dev)
+        _check(U2, "U2", (H, Dk, R), torch.float32, dev)
+    _check(m0, "m0", (B, H, Dv), torch.float32, dev)
+    cs = carve_content(bx.data_ptr(), None if U1 is None else U1.data_ptr(), None if U2 is None else U2.data_ptr(),
+                       R, None if m0 is None else m0.data_ptr(), None)
+    s = make_shape(q, v, L)
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "dlog_g": torch.empty_like(log_g), "db_x": torch.empty_like(bx), "dw": torch.empty_like(w),
+         "dU1": None if U1 is None else torch.empty_like(U1), "dU2": None if U2 is None else torch.empty_like(U2),
+         "dm0": torch.empty((B, H, Dv), dtype=torch.float32, device=dev) if want_dm0 else None,
+         "dS0": torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev) if want_dS0 else None}
+    need = lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(cs))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_bwd_content(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(w), _ptr(S0),
+                                 ctypes.byref(cs), _ptr(dO), _ptr(dS_T), _ptr(dm_out), _ptr(g["dq"]), _ptr(g["dk"]),
+                                 _ptr(g["dv"]), _ptr(g["dlog_g"]), _ptr(g["db_x"]), _ptr(g["dw"]), _ptr(g["dU1"]),
+                                 _ptr(g["dU2"]), _ptr(g["dm0"]), _ptr(g["dS0"]), _ptr(workspace), workspace.numel(),
+                                 _stream(dev))
+    _raise(code, "carve_bwd_content")
     return g
 
 

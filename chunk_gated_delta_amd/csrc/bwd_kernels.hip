@@ -129,9 +129,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   // three operand buffers, loaded two chunks ahead (chunks run last to first);
   // chunks below the last one run in a branch-free main loop with clamped prefetch.
   constexpr int PF = 3;
+  // chunk range (all chunks unless a sub-range is asked for)
+  const int clo = a.c_lo, chi = a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1, nch = chi - clo + 1;
   Op buf[PF];
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, bh, max(f.NC - 1 - j, 0), v0);
+  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, bh, max(chi - j, clo), v0);
   __syncthreads();
   auto step = [&](int c, const Op& cur) {
     const size_t ci = (size_t)bh * f.NC + c;
@@ -188,20 +190,20 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     }
     __syncthreads();
   };
-  const int nmain = f.NC - (f.NC % PF);     // chunks NC-1 .. NC-nmain in groups of PF
+  const int nmain = nch - (nch % PF);       // chunks chi .. chi-nmain+1 in groups of PF
   for (int g = 0; g < nmain; g += PF) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int c = f.NC - 1 - (g + j);
-      buf[(j + PF - 1) % PF].load(a, bh, max(c - (PF - 1), 0), v0);
+      const int c = chi - (g + j);
+      buf[(j + PF - 1) % PF].load(a, bh, max(c - (PF - 1), clo), v0);
       step(c, buf[j]);
     }
   }
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    const int c = f.NC - 1 - (nmain + j);
-    if (c >= 0) {
-      if (c - (PF - 1) >= 0) buf[(j + PF - 1) % PF].load(a, bh, c - (PF - 1), v0);
+    const int c = chi - (nmain + j);
+    if (c >= clo) {
+      if (c - (PF - 1) >= clo) buf[(j + PF - 1) % PF].load(a, bh, c - (PF - 1), v0);
       step(c, buf[j]);
     }
   }
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   float* glt = dwq + NB * LC;      // [D] G_L term per key column
 
   const FwdArgs& f = a.fwd;
-  const int c = blockIdx.x, bh = blockIdx.y;
+  const int c = a.c_lo + blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
   const int ct0 = wave * CPW;      // first key/value tile owned by this wave
   const int n = min(LC, f.T - c * LC);
@@ -912,7 +914,7 @@ static hipError_t grad_launch(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
-  dim3 grid(a.fwd.NC, a.fwd.B * a.fwd.H);
+  dim3 grid(a.c_count ? a.c_count : a.fwd.NC, a.fwd.B * a.fwd.H);
   hipLaunchKernelGGL(kern, grid, dim3(D * 4), Lay::bytes, st, a);
   return hipGetLastError();
 }

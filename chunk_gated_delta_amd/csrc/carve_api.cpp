@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "../../include/carve.h"
@@ -183,7 +185,7 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
   hipError_t e;
   if (content) {
     a.f = carve::carve_factors(workspace, a.dtype, p.BH, 1, p.LC, p.D, 1);
-    carve::ContentArgs cg;
+    carve::ContentArgs cg = {};
     cg.b_x = content->b_x;
     cg.U1 = content->U1;
     cg.U2 = content->U2;
@@ -362,6 +364,163 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
   mark(prof, 1, hs);
   if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
   mark(prof, 2, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+// Workspace of carve_bwd_content, in order: the content forward's factor slot, its
+// output (scratch), z and m of every period, the gates b, the token-only backward's
+// workspace (factors, S and dS per chunk), dO with the mean-output term, the dS carry,
+// the period's output-gradient term g, and per-sequence dU1 / dU2 accumulators.
+struct ContentBwdLayout {
+  size_t fwd, o, z, m, bmat, bwd, dOp, carry, g, du1, du2, total;
+};
+ContentBwdLayout content_bwd_layout(const carve_shape* s, const Plan& p, const carve_content* c) {
+  const size_t es = s->dtype == CARVE_BF16 ? 2 : 4;
+  const size_t NP = ((size_t)s->T + s->L - 1) / s->L;
+  const size_t R = c && c->U1 ? (size_t)c->R : 0;
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  ContentBwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += al(bytes); return at; };
+  L.fwd = take(fwd_ws(s, p, c));
+  L.o = take((size_t)p.BH * s->T * s->Dv * es);
+  L.z = take((size_t)p.BH * NP * p.D * 4);
+  L.m = take((size_t)p.BH * NP * p.D * 4);
+  L.bmat = take((size_t)p.BH * s->T * p.D * 4);
+  L.bwd = take(bwd_ws(s, p));
+  L.dOp = take((size_t)p.BH * s->T * s->Dv * es);
+  L.carry = take((size_t)p.BH * p.D * p.D * 4);
+  L.g = take((size_t)p.BH * p.D * 4);
+  L.du1 = take((size_t)p.BH * R * p.D * 4);
+  L.du2 = take((size_t)p.BH * p.D * R * 4);
+  L.total = p.empty ? 0 : off + 256;
+  return L;
+}
+
+size_t carve_bwd_content_workspace_size(const carve_shape* s, const carve_content* content) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK) return 0;
+  return content_bwd_layout(s, p, content).total;
+}
+
+carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* k, const void* v,
+                               const float* log_g, const float* w, const float* S0, const carve_content* content,
+                               const void* dO, const float* dS_T, const float* dm_out, void* dq, void* dk,
+                               void* dv, float* dlog_g, float* db_x, float* dw, float* dU1, float* dU2,
+                               float* dm0, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  if (!content) return CARVE_ERR_INVALID_ARG;
+  st = check_content(s, p, content, nullptr);
+  if (st != CARVE_OK) return st;
+  const bool proj = content->U1 != nullptr;
+  if ((dU1 == nullptr) != !proj || (dU2 == nullptr) != !proj) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty) {
+    if (!q || !k || !v || !log_g || !w || !dO || !dq || !dk || !dv || !dlog_g || !db_x || !dw)
+      return CARVE_ERR_INVALID_ARG;
+  }
+  for (const void* ptr : {q, k, v, (const void*)log_g, (const void*)w, (const void*)S0, dO, (const void*)dS_T,
+                          (const void*)dm_out, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)dlog_g, (const void*)db_x, (const void*)dw, (const void*)dU1,
+                          (const void*)dU2, (const void*)dm0, (const void*)dS0})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const ContentBwdLayout Lw = content_bwd_layout(s, p, content);
+  if (workspace_bytes < Lw.total || (Lw.total > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int R = proj ? content->R : 0;
+  if (p.empty) {
+    // no tokens: S_T = S0 and m_out = m0, so their gradients pass straight through
+    hipError_t e = hipSuccess;
+    if (dS0) e = carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * p.D * p.D, hs);
+    if (e == hipSuccess && dm0) e = carve::launch_copy_or_zero(dm0, dm_out, (size_t)p.BH * p.D, hs);
+    if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(dU1, nullptr, (size_t)s->H * R * p.D, hs);
+    if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(dU2, nullptr, (size_t)s->H * p.D * R, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  char* ws = align_up(workspace);
+  float* z_all = reinterpret_cast<float*>(ws + Lw.z);
+  float* m_all = reinterpret_cast<float*>(ws + Lw.m);
+  float* bmat = reinterpret_cast<float*>(ws + Lw.bmat);
+
+  // 1. the content forward again, recording each period's z and the mean it used
+  carve::FwdArgs fa = fwd_args(s, p, q, k, v, log_g, nullptr, w, S0, ws + Lw.o, nullptr);
+  fa.mode = 1;
+  fa.f = carve::carve_factors(ws + Lw.fwd, fa.dtype, p.BH, 1, p.LC, p.D, 1);
+  carve::ContentArgs cg = {};
+  cg.b_x = content->b_x;
+  cg.U1 = content->U1;
+  cg.U2 = content->U2;
+  cg.R = R;
+  cg.m0 = content->m0;
+  cg.period = s->L;
+  cg.z_all = z_all;
+  cg.m_all = m_all;
+  hipError_t e = carve::launch_fwd_content(fa, cg, hs);
+
+  carve::ContentBwdArgs ca = {};
+  ca.B = s->B;
+  ca.H = s->H;
+  ca.T = s->T;
+  ca.D = p.D;
+  ca.L = s->L;
+  ca.NP = (s->T + s->L - 1) / s->L;
+  ca.R = R;
+  ca.z_all = z_all;
+  ca.m_all = m_all;
+  ca.bmat = bmat;
+  ca.dbx = db_x;
+  ca.U1 = content->U1;
+  ca.U2 = content->U2;
+  ca.dU1p = reinterpret_cast<float*>(ws + Lw.du1);
+  ca.dU2p = reinterpret_cast<float*>(ws + Lw.du2);
+  ca.g = reinterpret_cast<float*>(ws + Lw.g);
+  ca.dm0 = dm0;
+  // 2. the gates of every token
+  if (e == hipSuccess) e = carve::launch_content_gates(ca, content->b_x, bmat, hs);
+
+  // 3. the token-only backward machinery with those gates: factors and chunk states
+  carve::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fwd = fwd_args(s, p, q, k, v, log_g, bmat, w, S0, nullptr, nullptr);
+  a.fwd.mode = 2;
+  char* wb = ws + Lw.bwd;
+  a.fwd.f = carve::carve_factors(wb, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2);
+  char* base = align_up(wb + carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2));
+  a.fwd.S_vk = base;
+  a.dS_vk = align_up(base + states_bytes(s, p));
+  float* carry = reinterpret_cast<float*>(ws + Lw.carry);
+  a.dO = ws + Lw.dOp;
+  a.dS_T = carry;
+  a.dS0 = carry;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_g = dlog_g;
+  a.db = db_x;          // d/db first; the gate kernel turns it into d/db_x
+  a.dw = dw;
+  if (e == hipSuccess) e = carve::launch_fwd_prep(a.fwd, hs);
+  if (e == hipSuccess) e = carve::launch_fwd_state(a.fwd, hs);
+
+  // 4. the periods in reverse
+  if (e == hipSuccess) e = carve::launch_copy_or_zero(carry, dS_T, (size_t)p.BH * p.D * p.D, hs);
+  if (e == hipSuccess) e = carve::launch_init_grad_mean(ca, dm_out, hs);
+  if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(ca.dU1p, nullptr, (size_t)p.BH * R * p.D, hs);
+  if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(ca.dU2p, nullptr, (size_t)p.BH * p.D * R, hs);
+  const int per = s->L / p.LC;     // tiles per period
+  for (int pp = ca.NP - 1; pp >= 0 && e == hipSuccess; --pp) {
+    ca.p = pp;
+    a.c_lo = pp * per;
+    a.c_count = std::min(per, p.NC - a.c_lo);
+    e = carve::launch_add_grad_mean(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
+    if (e == hipSuccess) e = carve::launch_bwd_state(a, hs);
+    if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
+    if (e == hipSuccess) e = carve::launch_content_gate_bwd(ca, hs);
+  }
+  if (e == hipSuccess && dS0) e = carve::launch_copy_or_zero(dS0, carry, (size_t)p.BH * p.D * p.D, hs);
+  if (e == hipSuccess && proj) e = carve::launch_sum_over_batch(ca.dU1p, dU1, s->B, s->H, R * p.D, hs);
+  if (e == hipSuccess && proj) e = carve::launch_sum_over_batch(ca.dU2p, dU2, s->B, s->H, p.D * R, hs);
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 

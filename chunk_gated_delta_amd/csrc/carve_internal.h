@@ -63,6 +63,8 @@ struct ContentArgs {
   const float* m0;        // may be null
   float* m_out;           // may be null
   int period;             // content period in tokens (the chunk length L), multiple of LC
+  float* z_all;           // may be null: [B*H][periods][Dk] content signal z of every period
+  float* m_all;           // may be null: [B*H][periods][Dv] the mean output each period's z was formed from
 };
 
 struct BwdArgs {
@@ -77,6 +79,10 @@ struct BwdArgs {
   float* db;              // may be null (iff b is null)
   float* dw;
   float* dS0;             // may be null
+  // chunk range of the backward kernels: chunks c_lo .. c_lo + c_count - 1 of every
+  // head (c_count = 0: all chunks).  The reverse state pass starts from dS_T and
+  // ends in dS0 for that range.
+  int c_lo, c_count;
 };
 
 // One recurrent decode step (one token per batch and head), state updated in place.
@@ -101,6 +107,22 @@ struct DecodeArgs {
   int L, pos;             // content period and the token's position inside it
 };
 
+// Per-period pieces of the backward through the content-aware erase.
+struct ContentBwdArgs {
+  int B, H, T, D, L, NP, R;   // L = content period in tokens, NP = number of periods
+  int p;                      // the period a launch works on
+  const float* z_all;         // [B*H][NP][D] content signal of every period
+  const float* m_all;         // [B*H][NP][D] mean output each period's signal was formed from
+  const float* bmat;          // [B,H,T,D] the gate b of every token
+  float* dbx;                 // [B,H,T,D] in: d/db of period p; out: d/db_x
+  const float* U1;            // [H,R,D] or null (no projection)
+  const float* U2;            // [H,D,R]
+  float* dU1p;                // [B*H][R][D] per-sequence accumulators
+  float* dU2p;                // [B*H][D][R]
+  float* g;                   // [B*H][D] output-gradient term of the period being swept
+  float* dm0;                 // [B*H][D] or null
+};
+
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode);
 ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode);
 
@@ -111,5 +133,10 @@ hipError_t launch_fwd_content(const FwdArgs& a, const ContentArgs& c, hipStream_
 hipError_t launch_bwd_state(const BwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
+hipError_t launch_content_gates(const ContentBwdArgs& a, const float* b_x, float* bmat, hipStream_t st);
+hipError_t launch_add_grad_mean(const ContentBwdArgs& a, int dtype, const void* dO, void* dOp, hipStream_t st);
+hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, hipStream_t st);
+hipError_t launch_init_grad_mean(const ContentBwdArgs& a, const float* dm_out, hipStream_t st);
+hipError_t launch_sum_over_batch(const float* part, float* out, int B, int H, int n, hipStream_t st);
 
 }  // namespace carve

@@ -1,0 +1,166 @@
+// Backward through the content-aware erase (CARVE notes, section 2.2) on gfx950.
+//
+// Once the forward has run, every content period p (L tokens) has a fixed gate
+// b = sigmoid(b_x + z_p), z_p = U2 (U1 m_{p-1}); the chunk gradients are those of the
+// token-only rule with that b.  What couples the periods is the mean output: m_{p-1}
+// feeds z_p, so period p's gate gradient dx = db * b (1 - b) gives
+//   dz_p = sum_t dx_t,  dU2 += dz_p r_p^T (r_p = U1 m_{p-1}),  dr = U2^T dz_p,
+//   dU1 += dr m_{p-1}^T,  dm_{p-1} = U1^T dr,
+// and dm_{p-1} / L is added to the output gradient of every token of period p-1
+// (period 0's dm goes to m0).  The library runs the periods in reverse; these
+// kernels are the per-period pieces around the token-only backward kernels.
+#include "carve_device.h"
+#include "carve_internal.h"
+
+namespace carve {
+
+// b = sigmoid(b_x + z_p) for every token, the same expression as the forward's gate
+__global__ __launch_bounds__(256) void content_gates_kernel(ContentBwdArgs a, const float* b_x, float* bmat) {
+  const size_t n4 = (size_t)a.B * a.H * a.T * a.D / 4;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = 4 * i;
+    const int k = (int)(e % a.D);
+    const size_t row = e / a.D;                      // (bh, t)
+    const int t = (int)(row % a.T);
+    const size_t bh = row / a.T;
+    const float* z = a.z_all + (bh * a.NP + t / a.L) * a.D + k;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(b_x + e);
+    f32x4 b;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = 1.f / (1.f + __expf(-(x[j] + z[j])));
+    *reinterpret_cast<f32x4*>(bmat + e) = b;
+  }
+}
+
+// dO' = dO + g (g per head and value column) for the tokens of period p
+template <typename T>
+__global__ __launch_bounds__(256) void add_grad_mean_kernel(ContentBwdArgs a, const T* dO, T* dOp) {
+  const int bh = blockIdx.x;
+  const int t0 = a.p * a.L, t1 = min(t0 + a.L, a.T);
+  const size_t base = ((size_t)bh * a.T + t0) * a.D;
+  const int n4 = (t1 - t0) * a.D / 4;
+  const float* g = a.g + (size_t)bh * a.D;
+  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+    const int col = (4 * i) % a.D;
+    const f32x4 x = load4f(dO + base + 4 * i);
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(g + col);
+    store4(dOp + base + 4 * i, x + gv);
+  }
+}
+
+// Gate backward of period p for one head (one workgroup per head):
+// db (w.r.t. the gate probability, from the chunk-gradient kernel) -> db_x in place,
+// then the projection's gradients and the next period's output-gradient term g.
+__global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a) {
+  __shared__ float dzp[256];
+  __shared__ float dz[128];
+  __shared__ float rS[64], drS[64];
+  const int bh = blockIdx.x, h = bh % a.H, tid = threadIdx.x, D = a.D;
+  const int t0 = a.p * a.L, t1 = min(t0 + a.L, a.T);
+  // dx = db * b (1 - b), summed over the period's tokens per key column
+  const int k = tid % D, part = tid / D, nparts = 256 / D;
+  float acc = 0.f;
+  for (int t = t0 + part; t < t1; t += nparts) {
+    const size_t i = ((size_t)bh * a.T + t) * D + k;
+    const float b = a.bmat[i];
+    const float dx = a.dbx[i] * b * (1.f - b);
+    a.dbx[i] = dx;
+    acc += dx;
+  }
+  dzp[tid] = acc;
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int pp = 0; pp < nparts; ++pp) s += dzp[pp * D + tid];
+    dz[tid] = s;
+  }
+  if (!a.U1) {
+    // no projection: nothing reaches the previous period or m0
+    if (tid < D) {
+      if (a.p > 0) a.g[(size_t)bh * D + tid] = 0.f;
+      else if (a.dm0) a.dm0[(size_t)bh * D + tid] = 0.f;
+    }
+    return;
+  }
+  const float* m = a.m_all + ((size_t)bh * a.NP + a.p) * D;      // m_{p-1}
+  const float* U1 = a.U1 + (size_t)h * a.R * D;                  // [R][D]
+  const float* U2 = a.U2 + (size_t)h * D * a.R;                  // [D][R]
+  __syncthreads();
+  if (tid < a.R) {
+    float r = 0.f, dr = 0.f;
+    for (int v = 0; v < D; ++v) r += U1[tid * D + v] * m[v];
+    for (int kk = 0; kk < D; ++kk) dr += U2[kk * a.R + tid] * dz[kk];
+    rS[tid] = r;
+    drS[tid] = dr;
+  }
+  __syncthreads();
+  float* dU2p = a.dU2p + (size_t)bh * D * a.R;
+  float* dU1p = a.dU1p + (size_t)bh * a.R * D;
+  for (int i = tid; i < D * a.R; i += 256) {
+    dU2p[i] += dz[i / a.R] * rS[i % a.R];
+    dU1p[i] += drS[i / D] * m[i % D];
+  }
+  if (tid < D) {
+    float dm = 0.f;
+    for (int r = 0; r < a.R; ++r) dm += U1[r * D + tid] * drS[r];
+    if (a.p > 0) a.g[(size_t)bh * D + tid] = dm / (float)a.L;     // period p-1 is whole
+    else if (a.dm0) a.dm0[(size_t)bh * D + tid] = dm;
+  }
+}
+
+// g = dm_out / (tokens of the last period), or 0
+__global__ __launch_bounds__(256) void init_grad_mean_kernel(ContentBwdArgs a, const float* dm_out) {
+  const size_t n = (size_t)a.B * a.H * a.D;
+  const float inv = 1.f / (float)(a.T - (a.NP - 1) * a.L);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    a.g[i] = dm_out ? dm_out[i] * inv : 0.f;
+}
+
+// out[h][i] = sum over the batch of part[b * H + h][i]
+__global__ __launch_bounds__(256) void sum_over_batch_kernel(const float* part, float* out, int B, int H, int n) {
+  const size_t total = (size_t)H * n;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t h = i / n, j = i % n;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) s += part[((size_t)b * H + h) * n + j];
+    out[i] = s;
+  }
+}
+
+static unsigned grid_for(size_t n, unsigned cap = 4096) {
+  const size_t g = (n + 255) / 256;
+  return (unsigned)(g < cap ? (g ? g : 1) : cap);
+}
+
+hipError_t launch_content_gates(const ContentBwdArgs& a, const float* b_x, float* bmat, hipStream_t st) {
+  hipLaunchKernelGGL(content_gates_kernel, dim3(grid_for((size_t)a.B * a.H * a.T * a.D / 4)), dim3(256), 0, st, a,
+                     b_x, bmat);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_grad_mean(const ContentBwdArgs& a, int dtype, const void* dO, void* dOp, hipStream_t st) {
+  if (dtype)
+    hipLaunchKernelGGL(add_grad_mean_kernel<bf16>, dim3(a.B * a.H), dim3(256), 0, st, a,
+                       reinterpret_cast<const bf16*>(dO), reinterpret_cast<bf16*>(dOp));
+  else
+    hipLaunchKernelGGL(add_grad_mean_kernel<float>, dim3(a.B * a.H), dim3(256), 0, st, a,
+                       reinterpret_cast<const float*>(dO), reinterpret_cast<float*>(dOp));
+  return hipGetLastError();
+}
+
+hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(content_gate_bwd_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_grad_mean(const ContentBwdArgs& a, const float* dm_out, hipStream_t st) {
+  hipLaunchKernelGGL(init_grad_mean_kernel, dim3(grid_for((size_t)a.B * a.H * a.D)), dim3(256), 0, st, a, dm_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_over_batch(const float* part, float* out, int B, int H, int n, hipStream_t st) {
+  hipLaunchKernelGGL(sum_over_batch_kernel, dim3(grid_for((size_t)H * n)), dim3(256), 0, st, part, out, B, H, n);
+  return hipGetLastError();
+}
+
+}  // namespace carve

@@ -374,7 +374,15 @@ __global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs
       } else if (tid < D) {
         zL[tid] = 0.f;
       }
-      if (tid < D) msum[tid] = 0.f;
+      if (tid < D) {
+        msum[tid] = 0.f;
+        if (cg.z_all) {
+          // per-period record for the backward: z and the mean it was formed from
+          const size_t pi = (size_t)bh * ((a.NC + per - 1) / per) + c / per;
+          cg.z_all[pi * D + tid] = zL[tid];
+          cg.m_all[pi * D + tid] = mL[tid];
+        }
+      }
       count = 0;
       __syncthreads();
     }

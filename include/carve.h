@@ -115,9 +115,8 @@ carve_status carve_fwd(const carve_shape* s,
 size_t carve_bwd_workspace_size(const carve_shape* s);
 
 /*
- * Backward pass of the token-only forward (content-aware backward is not
- * provided: CARVE_ERR_UNSUPPORTED is never needed because there is no content
- * argument).  Recomputes the forward internally.
+ * Backward pass of the token-only forward (the content-aware forward has its own
+ * backward, carve_bwd_content, below).  Recomputes the forward internally.
  *   q, k, v, log_g, b, w, S0   as for carve_fwd
  *   dO     (device) [B,H,T,Dv] dtype          gradient of the loss w.r.t. o
  *   dS_T   (device) [B,H,Dv,Dk] float         gradient w.r.t. S_T, or NULL (= 0)
@@ -201,6 +200,38 @@ carve_status carve_bwd_saved(const carve_shape* s,
                              void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream,
                              const carve_profile* profile);
+
+/*
+ * Backward through the content-aware erase (notes section 2.2): gradients of the
+ * content-aware forward, including the projection and the chain through each
+ * chunk's mean output into the next chunk's gate.  Recomputes the forward.
+ *   q, k, v, log_g, w, S0, content   as for carve_fwd (content required; its
+ *                                    m_out is ignored)
+ *   dO     (device) [B,H,T,Dv] dtype   gradient w.r.t. o
+ *   dS_T   (device) [B,H,Dv,Dk] float  gradient w.r.t. S_T, or NULL (= 0)
+ *   dm_out (device) [B,H,Dv] float     gradient w.r.t. m_out (the last chunk's mean), or NULL (= 0)
+ * Outputs:
+ *   dq, dk (dtype) [B,H,T,Dk]; dv (dtype) [B,H,T,Dv]; dlog_g (float) [B,H,T,Dk];
+ *   db_x   (float) [B,H,T,Dk]  derivative w.r.t. the erase pre-activation b_x;
+ *   dw     (float) [B,H,T];
+ *   dU1    (float) [H,R,Dv], dU2 (float) [H,Dk,R]: summed over the batch; required
+ *          when the projection is given, NULL without it;
+ *   dm0    (float) [B,H,Dv] derivative w.r.t. m0, or NULL (not written);
+ *   dS0    (float) [B,H,Dv,Dk] derivative w.r.t. S0, or NULL (not written).
+ * The chunks of L tokens are swept in reverse, one sweep step per chunk (a few
+ * launches each, all heads in parallel), because chunk c-1's output gradient
+ * needs chunk c's gate gradient.
+ */
+size_t carve_bwd_content_workspace_size(const carve_shape* s, const carve_content* content);
+
+carve_status carve_bwd_content(const carve_shape* s,
+                               const void* q, const void* k, const void* v,
+                               const float* log_g, const float* w, const float* S0,
+                               const carve_content* content,
+                               const void* dO, const float* dS_T, const float* dm_out,
+                               void* dq, void* dk, void* dv, float* dlog_g, float* db_x, float* dw,
+                               float* dU1, float* dU2, float* dm0, float* dS0,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Recurrent decode: one new token per (batch, head), the O(Dv Dk) per-token form

@@ -1,0 +1,140 @@
+"""GPU parity of the backward through the content-aware erase (needs an MI355X).
+
+Compared with the float64 reverse-mode reference (itself pinned by finite
+differences in the CPU suite).  Error metric: per gradient tensor,
+max|gpu - ref| / max|ref|; bars 1e-4 (float32 inputs) and 2e-2 (bfloat16 inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunk_gated_delta_amd import carve
+from chunk_gated_delta_amd.synth import WORKLOADS, make_inputs, random_inputs
+from tests.helpers import max_rel, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dq", "dk", "dv", "dlog_g", "db_x", "dw", "dU1", "dU2", "dm0", "dS0")
+
+
+def announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def f32(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).cuda()
+
+
+def content_case(B, H, T, D, dtype, seed, scale=8.0):
+    inp = random_inputs(B, H, T, D, D, dtype=dtype, seed=seed, erase="content", dists="softplus_decay",
+                        with_dO=True)
+    inp["U1"] = inp["U1"] * scale
+    inp["U2"] = inp["U2"] * scale
+    rng = np.random.default_rng(seed + 1)
+    extra = {
+        "m0": np.asarray(rng.standard_normal((B, H, D)) * 0.5, np.float32).astype(np.float64),
+        "S0": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),
+        "dS_T": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),
+        "dm_out": np.asarray(rng.standard_normal((B, H, D)), np.float32).astype(np.float64),
+    }
+    return inp, extra
+
+
+def run_both(inp, ex, dtype, L, proj=True):
+    d = to_device(inp, dtype)
+    U1 = d["U1"] if proj else None
+    U2 = d["U2"] if proj else None
+    g = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"],
+                          {"b_x": d["b_x"], "U1": U1, "U2": U2, "m0": f32(ex["m0"])},
+                          S0=f32(ex["S0"]), dS_T=f32(ex["dS_T"]), dm_out=f32(ex["dm_out"]), L=L)
+    torch.cuda.synchronize()
+    g = {k_: (None if v_ is None else to_np(v_)) for k_, v_ in g.items()}
+    ref = oracle.backward_content(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"],
+                                  {"b_x": inp["b_x"], "U1": inp["U1"] if proj else None,
+                                   "U2": inp["U2"] if proj else None, "m0": ex["m0"]},
+                                  S0=ex["S0"], dS_T=ex["dS_T"], dm_out=ex["dm_out"], L=L)
+    return g, ref
+
+
+def check(g, ref, tol):
+    errs = {}
+    for key in NAMES:
+        if ref[key] is None:
+            assert g[key] is None, key
+            continue
+        errs[key] = max_rel(g[key], ref[key])
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= tol for v_ in errs.values()), errs
+
+
+CASES = [
+    # dtype, B, H, T, D, L
+    ("f32", 1, 2, 200, 64, 64),
+    ("bf16", 2, 2, 256, 128, 64),
+    ("bf16", 1, 2, 320, 128, 128),
+    ("bf16", 2, 1, 100, 64, 32),
+    ("f32", 1, 1, 96, 128, 32),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,T,D,L", CASES, ids=[f"{c[0]}_T{c[3]}_d{c[4]}_L{c[5]}" for c in CASES])
+def test_content_bwd_parity(dtype, B, H, T, D, L):
+    announce(f"content bwd {dtype} B{B} H{H} T{T} d{D} L{L}")
+    inp, ex = content_case(B, H, T, D, dtype, seed=200 + T + D + L)
+    g, ref = run_both(inp, ex, dtype, L)
+    check(g, ref, TOL[dtype])
+    # the chain through the mean outputs must matter here (else it pins nothing)
+    ref0 = oracle.backward_content(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"],
+                                   {"b_x": inp["b_x"], "U1": None, "U2": None, "m0": ex["m0"]},
+                                   S0=ex["S0"], dS_T=ex["dS_T"], dm_out=ex["dm_out"], L=L)
+    assert max_rel(ref0["dk"], ref["dk"]) > 0.02
+
+
+def test_content_bwd_no_projection():
+    announce("content bwd without projection")
+    inp, ex = content_case(2, 2, 150, 128, "bf16", seed=301)
+    g, ref = run_both(inp, ex, "bf16", 64, proj=False)
+    check(g, ref, TOL["bf16"])
+    assert np.all(g["dm0"] == 0)
+
+
+def test_content_bwd_zero_projection_bit_exact():
+    """U_b = 0 gives the same gradients as U_b absent, bit for bit, and zero
+    gradients for the projection and the carried-in mean."""
+    announce("content bwd zero projection bit exact")
+    inp, ex = content_case(2, 2, 192, 128, "bf16", seed=302)
+    d = to_device(inp, "bf16")
+    outs = []
+    for U1, U2 in ((torch.zeros_like(d["U1"]), torch.zeros_like(d["U2"])), (None, None)):
+        g = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"],
+                              {"b_x": d["b_x"], "U1": U1, "U2": U2, "m0": f32(ex["m0"])},
+                              S0=f32(ex["S0"]), dS_T=f32(ex["dS_T"]), L=64)
+        torch.cuda.synchronize()
+        outs.append(g)
+    for key in ("dq", "dk", "dv", "dlog_g", "db_x", "dw", "dm0", "dS0"):
+        assert torch.equal(outs[0][key], outs[1][key]), key
+    assert torch.count_nonzero(outs[0]["dU1"]) == 0 and torch.count_nonzero(outs[0]["dU2"]) == 0
+
+
+def test_content_bwd_full_size_sampled_head():
+    """The content workload's shape (B4 H16 T4096 d128 L64): one sampled head against the
+    reference (dU1 / dU2 are sums over the batch; the small cases above compare them)."""
+    wl = WORKLOADS["content_fwd"]
+    announce(f"content bwd full size {wl.name}")
+    inp = make_inputs(wl, with_dO=True)
+    d = to_device(inp, wl.dtype)
+    g = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"],
+                          {"b_x": d["b_x"], "U1": d["U1"], "U2": d["U2"]}, L=wl.L)
+    torch.cuda.synchronize()
+    bi, hi = 1, 5
+    sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items() if not k_.endswith("_bits") and np.ndim(v_) == 4}
+    sub["w"] = inp["w"][bi:bi + 1, hi:hi + 1]
+    ref = oracle.backward_content(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], sub["dO"],
+                                  {"b_x": sub["b_x"], "U1": inp["U1"][hi:hi + 1], "U2": inp["U2"][hi:hi + 1]},
+                                  L=wl.L)
+    errs = {}
+    for key in ("dq", "dk", "dv", "dlog_g", "db_x", "dw", "dm0", "dS0"):
+        errs[key] = max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key])
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL["bf16"] for v_ in errs.values()), errs
