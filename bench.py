@@ -253,7 +253,24 @@ def main():
         cms = ce0.elapsed_time(ce1) / nrep
         extra["content_fwd_ms"] = round(cms, 4)
         extra["content_fwd_tokens_per_s"] = wc.B * wc.T / (cms * 1e-3)
-        del cq, ck, cv, cf, cont, ws_c, co
+        # its backward (gradients of q, k, v, log g, b_x, w, U1, U2): a reverse sweep over the
+        # content periods, each a few launches over all heads
+        cdo = torch.from_numpy(np.ascontiguousarray(make_inputs(wc, with_dO=True)["dO_bits"]).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        ws_cb = torch.empty(carve.bwd_content_workspace_bytes(cq, cv, wc.L, R=cf["U1"].shape[1]), dtype=torch.uint8,
+                            device=dev)
+        for _ in range(2):
+            carve.bwd_content(cq, ck, cv, cf["log_g"], cf["w"], cdo, cont, L=wc.L, workspace=ws_cb)
+        torch.cuda.synchronize()
+        ce0.record()
+        for _ in range(3):
+            carve.bwd_content(cq, ck, cv, cf["log_g"], cf["w"], cdo, cont, L=wc.L, workspace=ws_cb)
+        ce1.record()
+        torch.cuda.synchronize()
+        cbms = ce0.elapsed_time(ce1) / 3
+        extra["content_bwd_ms"] = round(cbms, 4)
+        extra["content_bwd_tokens_per_s"] = wc.B * wc.T / (cbms * 1e-3)
+        del cq, ck, cv, cf, cont, ws_c, co, cdo, ws_cb
 
     # recurrent decode step (one token per sequence and head, state updated in place)
     if not args.no_decode:

@@ -310,6 +310,14 @@ def bwd_saved(q, k, v, log_g, w, dO, saved, b=None, dS_T=None, L=64, want_dS0=Tr
     return g
 
 
+def bwd_content_workspace_bytes(q, v, L=64, R=0):
+    """Workspace bytes of bwd_content for this shape (R: projection rank, 0 = none)."""
+    lib = load_library()
+    s = make_shape(q, v, L)
+    c = carve_content(None, 1 if R else None, 1 if R else None, R, None, None)
+    return lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(c))
+
+
 def bwd_content(q, k, v, log_g, w, dO, content, S0=None, dS_T=None, dm_out=None, L=64, want_dS0=True,
                 want_dm0=True, workspace=None):
     """Gradients of the content-aware forward: dict with dq, dk, dv, dlog_g, db_x, dw,

@@ -162,3 +162,27 @@ def test_decode_rejects_bad_arguments(lib):
     assert call_decode(lib, shape(T=1, L=4), content=no_sum) == INVALID
     assert call_decode(lib, shape(T=1), k=FAKE + 4) == INVALID                # misaligned vectors
     assert call_decode(lib, shape(T=1), log_g=FAKE + 4) == INVALID
+
+
+def call_bwd_content(lib, s, content, dU1=None, dU2=None, ws_bytes=1 << 40, **kw):
+    ptrs = {n: FAKE for n in ("q", "k", "v", "log_g", "w", "dO", "dq", "dk", "dv", "dlog_g", "db_x", "dw")}
+    ptrs.update(kw)
+    return lib.carve_bwd_content(ctypes.byref(s), ptrs["q"], ptrs["k"], ptrs["v"], ptrs["log_g"], ptrs["w"], None,
+                                 ctypes.byref(content) if content is not None else None, ptrs["dO"], None, None,
+                                 ptrs["dq"], ptrs["dk"], ptrs["dv"], ptrs["dlog_g"], ptrs["db_x"], ptrs["dw"],
+                                 dU1, dU2, None, None, FAKE, ws_bytes, None)
+
+
+def test_bwd_content_rejects_bad_arguments(lib):
+    s = shape()
+    plain = carve.carve_content(FAKE, None, None, 0, None, None)
+    proj = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
+    assert call_bwd_content(lib, s, None) == INVALID                       # content is required
+    assert call_bwd_content(lib, s, proj) == INVALID                       # projection needs dU1, dU2
+    assert call_bwd_content(lib, s, plain, dU1=FAKE, dU2=FAKE) == INVALID  # ... and only then
+    assert call_bwd_content(lib, s, plain, db_x=None) == INVALID
+    assert call_bwd_content(lib, s, plain, dO=FAKE + 4) == INVALID
+    assert call_bwd_content(lib, shape(L=48), plain) == UNSUPPORTED        # period not whole tiles
+    need = lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(proj))
+    assert need > lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(plain)) > 0
+    assert call_bwd_content(lib, s, proj, dU1=FAKE, dU2=FAKE, ws_bytes=need - 1) == WORKSPACE
