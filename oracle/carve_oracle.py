@@ -39,7 +39,8 @@ and are vectorised over (B*H) heads only.
 Functions: forward (token-serial forward, token-only or content-aware gates),
 backward (reverse mode of the token-only forward), backward_content (reverse
 mode of the content-aware forward, including the projection and the carried-in
-mean).
+mean), and gates_from_logits / forward_logits / backward_logits (the gates given
+as pre-activations, computed inside the operation).
 """
 
 import numpy as np
@@ -344,4 +345,51 @@ def backward_content(q, k, v, log_g, w, dO, content, S0=None, dS_T=None, dm_out=
         "dU2": None if not proj else dU2.reshape(B, H, Dk, R).sum(axis=0),
         "dm0": dm.reshape(B, H, Dv), "dS0": dS.reshape(B, H, Dv, Dk),
     }
+    return out
+
+
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def gates_from_logits(f, A, tau, w_hat, b_x=None):
+    """Gates from their pre-activations, the reading taken of the pages' fused
+    gate (notes section 2.3 legends: A the log-decay amplitude, f the decay
+    logits, tau a bias, the output log g <= 0; scalar write pre-activation w_hat):
+        log g = -A softplus(f + tau)   (A, tau per head and key channel, [H, Dk])
+        b = sigmoid(b_x)               (None: b = 1)
+        w = sigmoid(w_hat)
+    Returns (log_g, b, w)."""
+    f, A, tau, w_hat = map(_as64, (f, A, tau, w_hat))
+    log_g = -A[None, :, None, :] * _softplus(f + tau[None, :, None, :])
+    b = None if b_x is None else _sigmoid(_as64(b_x))
+    return log_g, b, _sigmoid(w_hat)
+
+
+def forward_logits(q, k, v, f, A, tau, w_hat, b_x=None, S0=None):
+    """Token-only forward pass with the gates given as pre-activations (see
+    gates_from_logits).  Returns (o, S_T)."""
+    log_g, b, w = gates_from_logits(f, A, tau, w_hat, b_x)
+    o, S_T, _ = forward(q, k, v, log_g, w, b=b, S0=S0)
+    return o, S_T
+
+
+def backward_logits(q, k, v, f, A, tau, w_hat, dO, b_x=None, S0=None, dS_T=None):
+    """Gradients of forward_logits: dict with dq, dk, dv, df, dA, dtau ([H, Dk],
+    summed over batch and tokens), db_x (None without b_x), dw_hat and dS0.
+    The chain rule through the three activations:
+        d f = d(log g) * (-A sigmoid(f + tau)),  d tau = sum d f,
+        d A = sum d(log g) * (-softplus(f + tau)),
+        d b_x = d b * b (1 - b),  d w_hat = d w * w (1 - w)."""
+    log_g, b, w = gates_from_logits(f, A, tau, w_hat, b_x)
+    g = backward(q, k, v, log_g, w, dO, b=b, S0=S0, dS_T=dS_T)
+    f, A, tau = map(_as64, (f, A, tau))
+    y = f + tau[None, :, None, :]
+    df = g["dlog_g"] * (-A[None, :, None, :] * _sigmoid(y))
+    out = {key: g[key] for key in ("dq", "dk", "dv", "dS0")}
+    out["df"] = df
+    out["dtau"] = df.sum(axis=(0, 2))
+    out["dA"] = (g["dlog_g"] * (-_softplus(y))).sum(axis=(0, 2))
+    out["db_x"] = None if b is None else g["db"] * b * (1.0 - b)
+    out["dw_hat"] = g["dw"] * w * (1.0 - w)
     return out

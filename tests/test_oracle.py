@@ -14,7 +14,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import forward, backward, backward_content
+from oracle import forward, backward, backward_content, backward_logits, forward_logits, gates_from_logits
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -473,3 +473,62 @@ def test_content_backward_first_chunk_gradient_of_m0():
     dz = g["db_x"].sum(axis=2)                                   # [B,H,Dk]
     want = np.einsum("hrv,hkr,bhk->bhv", c["U1"], c["U2"], dz)
     np.testing.assert_allclose(g["dm0"], want, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ gate pre-activations
+
+def logit_case(rng, B=1, H=2, T=9, D=3, with_bx=True):
+    c = rand_case(rng, B=B, H=H, T=T, Dk=D, Dv=D, unit_keys=False, with_b=False)
+    c["f"] = rng.standard_normal((B, H, T, D))
+    c["A"] = rng.uniform(0.05, 0.6, (H, D))
+    c["tau"] = rng.standard_normal((H, D)) * 0.5
+    c["w_hat"] = rng.standard_normal((B, H, T))
+    c["b_x"] = rng.normal(1.0, 1.0, (B, H, T, D)) if with_bx else None
+    return c
+
+
+def test_gates_from_logits_values():
+    """The activations themselves: softplus(0) = log 2, sigmoid(0) = 1/2, and log g <= 0."""
+    f = np.zeros((1, 1, 1, 2))
+    log_g, b, w = gates_from_logits(f, np.array([[1.0, 2.0]]), np.zeros((1, 2)), np.zeros((1, 1, 1)), b_x=f)
+    np.testing.assert_allclose(log_g[0, 0, 0], [-np.log(2.0), -2 * np.log(2.0)], rtol=1e-15)
+    assert np.all(b == 0.5) and np.all(w == 0.5)
+    rng = np.random.default_rng(40)
+    lg, _, _ = gates_from_logits(rng.standard_normal((2, 3, 5, 4)) * 30, rng.uniform(0, 2, (3, 4)),
+                                 rng.standard_normal((3, 4)), rng.standard_normal((2, 3, 5)))
+    assert np.all(lg <= 0) and np.all(np.isfinite(lg))
+
+
+@pytest.mark.parametrize("with_bx", [True, False])
+def test_logit_backward_matches_finite_differences(with_bx):
+    rng = np.random.default_rng(41 + with_bx)
+    c = logit_case(rng, with_bx=with_bx)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+
+    def loss():
+        o, S_T = forward_logits(c["q"], c["k"], c["v"], c["f"], c["A"], c["tau"], c["w_hat"], b_x=c["b_x"],
+                                S0=c["S0"])
+        return np.sum(o * dO) + np.sum(S_T * dS_T)
+
+    g = backward_logits(c["q"], c["k"], c["v"], c["f"], c["A"], c["tau"], c["w_hat"], dO, b_x=c["b_x"],
+                        S0=c["S0"], dS_T=dS_T)
+    eps = 1e-6
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("f", "df"), ("A", "dA"), ("tau", "dtau"),
+             ("w_hat", "dw_hat"), ("S0", "dS0")] + ([("b_x", "db_x")] if with_bx else [])
+    for name, gname in names:
+        x = c[name]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            i = it.multi_index
+            old = x[i]
+            x[i] = old + eps
+            lp = loss()
+            x[i] = old - eps
+            lm = loss()
+            x[i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
+    if not with_bx:
+        assert g["db_x"] is None
