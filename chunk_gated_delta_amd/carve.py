@@ -29,6 +29,11 @@ class carve_content(ctypes.Structure):
                 ("R", ctypes.c_int), ("m0", ctypes.c_void_p), ("m_out", ctypes.c_void_p)]
 
 
+class carve_gate_logits(ctypes.Structure):
+    _fields_ = [("f", ctypes.c_void_p), ("A", ctypes.c_void_p), ("tau", ctypes.c_void_p), ("b_x", ctypes.c_void_p),
+                ("w_hat", ctypes.c_void_p)]
+
+
 class carve_decode_content(ctypes.Structure):
     _fields_ = [("b_x", ctypes.c_void_p), ("U1", ctypes.c_void_p), ("U2", ctypes.c_void_p),
                 ("R", ctypes.c_int), ("m_in", ctypes.c_void_p), ("m_out", ctypes.c_void_p),
@@ -84,6 +89,13 @@ def load_library():
     lib.carve_bwd_saved.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                     vp, pp]
     lib.carve_bwd_saved.restype = i
+    glp = ctypes.POINTER(carve_gate_logits)
+    lib.carve_fwd_logits.argtypes = [sp, vp, vp, vp, glp, vp, vp, vp, vp, sz, vp]
+    lib.carve_fwd_logits.restype = i
+    lib.carve_bwd_logits_workspace_size.argtypes = [sp]
+    lib.carve_bwd_logits_workspace_size.restype = sz
+    lib.carve_bwd_logits.argtypes = [sp, vp, vp, vp, glp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.carve_bwd_logits.restype = i
     lib.carve_bwd_content_workspace_size.argtypes = [sp, cp]
     lib.carve_bwd_content_workspace_size.restype = sz
     lib.carve_bwd_content.argtypes = [sp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -308,6 +320,73 @@ def bwd_saved(q, k, v, log_g, w, dO, saved, b=None, dS_T=None, L=64, want_dS0=Tr
                                ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_bwd_saved")
     return g
+
+
+def _gate_logits(q, f, A, tau, w_hat, b_x):
+    B, H, T, Dk = q.shape
+    dev = q.device
+    _check(f, "f", (B, H, T, Dk), torch.float32, dev)
+    _check(A, "A", (H, Dk), torch.float32, dev)
+    _check(tau, "tau", (H, Dk), torch.float32, dev)
+    _check(w_hat, "w_hat", (B, H, T), torch.float32, dev)
+    _check(b_x, "b_x", (B, H, T, Dk), torch.float32, dev)
+    return carve_gate_logits(f.data_ptr(), A.data_ptr(), tau.data_ptr(), None if b_x is None else b_x.data_ptr(),
+                             w_hat.data_ptr())
+
+
+def fwd_logits(q, k, v, f, A, tau, w_hat, b_x=None, S0=None, L=64, o=None, S_T=None, workspace=None):
+    """o, S_T with the gates given as pre-activations: log g = -A softplus(f + tau),
+    b = sigmoid(b_x) (None: b = 1), w = sigmoid(w_hat); f, b_x [B,H,T,Dk], A, tau [H,Dk],
+    w_hat [B,H,T], all float32."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, H, T, Dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, Dv), q.dtype, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    g = _gate_logits(q, f, A, tau, w_hat, b_x)
+    s = make_shape(q, v, L)
+    if o is None:
+        o = torch.empty((B, H, T, Dv), dtype=q.dtype, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    need = lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_fwd_logits(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g), _ptr(S0), _ptr(o),
+                                _ptr(S_T), _ptr(workspace), workspace.numel(), _stream(dev))
+    _raise(code, "carve_fwd_logits")
+    return o, S_T
+
+
+def bwd_logits(q, k, v, f, A, tau, w_hat, dO, b_x=None, S0=None, dS_T=None, L=64, want_dS0=True, workspace=None):
+    """Gradients of fwd_logits: dict with dq, dk, dv, df, dA, dtau, db_x (None without
+    b_x), dw_hat and dS0 (None unless want_dS0)."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, H, T, Dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, Dv), q.dtype, dev)
+    _check(dO, "dO", (B, H, T, Dv), q.dtype, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    g = _gate_logits(q, f, A, tau, w_hat, b_x)
+    s = make_shape(q, v, L)
+    out = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v), "df": torch.empty_like(f),
+           "dA": torch.empty_like(A), "dtau": torch.empty_like(tau),
+           "db_x": None if b_x is None else torch.empty_like(b_x), "dw_hat": torch.empty_like(w_hat),
+           "dS0": torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev) if want_dS0 else None}
+    need = lib.carve_bwd_logits_workspace_size(ctypes.byref(s))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_bwd_logits(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g), _ptr(S0), _ptr(dO),
+                                _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]),
+                                _ptr(out["dA"]), _ptr(out["dtau"]), _ptr(out["db_x"]), _ptr(out["dw_hat"]),
+                                _ptr(out["dS0"]), _ptr(workspace), workspace.numel(), _stream(dev))
+    _raise(code, "carve_bwd_logits")
+    return out
 
 
 def bwd_content_workspace_bytes(q, v, L=64, R=0):

@@ -316,7 +316,10 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NB][CPW]) {
 }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-template <typename T, int LC, int D, bool HAS_B>
+// LG: the gates come as pre-activations (log_g holds f, b holds b_x, w holds w_hat);
+// they are activated when staged, and the kernel returns d/db_x and d/dw_hat in place
+// of d/db and d/dw (d/dlog g stays, for the logit pass to turn into d/df).
+template <typename T, int LC, int D, bool HAS_B, bool LG>
 __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   using Lay = GradLayout<T, LC, D>;
   // one wave per 16-column tile of the key/value width: NW = D/16 waves
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     tpre[u] = load4f(reinterpret_cast<const T*>(f.f.Tt) + ci * LC * LC + 4 * min(tid + NT * u, TP - 1));
   // k, q, v (dtype) into the K+, Q+, V slots; log g into slots 4-5 and b from slot 6 on
   // (fp32, row stride D+4).  Tokens past the end read as k = q = v = 0, log g = 0, b = 1.
-  if (tid < LC) wL[tid] = (tid < n) ? wv : 0.f;
+  if (tid < LC) wL[tid] = (tid < n) ? (LG ? sigmoidf(wv) : wv) : 0.f;
 #pragma unroll
   for (int u = 0; u < NST; ++u) {
     const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
@@ -405,6 +408,19 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = valid ? kx[u] : zero_frag(T());
     *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = valid ? qx[u] : zero_frag(T());
     *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? vx[u] : zero_frag(T());
+    if constexpr (LG) {
+      const LogitGates<D, HAS_B> gate{nullptr, f.gA, f.gtau};
+      const int h = bh % f.H;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lx[u].lo[e] = gate.logdecay(lx[u].lo[e], 8 * g + e, h);
+        lx[u].hi[e] = gate.logdecay(lx[u].hi[e], 8 * g + 4 + e, h);
+        if (HAS_B) {
+          bx[u].lo[e] = sigmoidf(bx[u].lo[e]);
+          bx[u].hi[e] = sigmoidf(bx[u].hi[e]);
+        }
+      }
+    }
     Frag<float> lw = lx[u];
     lw.lo = valid ? lw.lo : f32x4{0.f, 0.f, 0.f, 0.f};
     lw.hi = valid ? lw.hi : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -811,7 +827,9 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) binv[j][rt][ii] = rcp(binv[j][rt][ii]);
+        for (int ii = 0; ii < 4; ++ii)
+          // d/db = dlog a / b; with pre-activations d/db_x = d/db * b (1 - b) = dlog a * sigmoid(-b_x)
+          binv[j][rt][ii] = LG ? sigmoidf(-binv[j][rt][ii]) : rcp(binv[j][rt][ii]);
   }
   // ---- dK+ += dB K-, dK- += dB^T K+
   {
@@ -882,7 +900,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int t = 0; t < NB; ++t) s += dwq[t * LC + tid] + dwp[t * LC + tid];
-    a.dw[row0 + tid] = s;
+    a.dw[row0 + tid] = LG ? s * wL[tid] * (1.f - wL[tid]) : s;     // d/dw_hat = d/dw * w (1 - w)
   }
 }
 
@@ -910,7 +928,8 @@ template <typename T, int LC, int D>
 static hipError_t grad_launch(const BwdArgs& a, hipStream_t st) {
   using Lay = GradLayout<T, LC, D>;
   static_assert(Lay::bytes <= 160 * 1024, "chunk-gradient LDS exceeds 160 KB");
-  auto kern = a.fwd.b ? bwd_chunk_kernel<T, LC, D, true> : bwd_chunk_kernel<T, LC, D, false>;
+  auto kern = a.fwd.logits ? (a.fwd.b ? bwd_chunk_kernel<T, LC, D, true, true> : bwd_chunk_kernel<T, LC, D, false, true>)
+                           : (a.fwd.b ? bwd_chunk_kernel<T, LC, D, true, false> : bwd_chunk_kernel<T, LC, D, false, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;

@@ -367,6 +367,116 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 
+// ------------------------------------------------------------ gate pre-activations
+carve_status check_logits(const carve_shape* s, const Plan& p, const carve_gate_logits* g) {
+  if (!g) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!g->f || !g->A || !g->tau || !g->w_hat)) return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {(const void*)g->f, (const void*)g->b_x, (const void*)g->w_hat})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  return CARVE_OK;
+}
+
+carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k, const void* v,
+                              const carve_gate_logits* gates, const float* S0, void* o, float* S_T,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  st = check_logits(s, p, gates);
+  if (st != CARVE_OK) return st;
+  if (!p.empty && (!q || !k || !v || !o)) return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, (const void*)S0, (const void*)o, (const void*)S_T})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need = fwd_ws(s, p, nullptr);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = S_T ? carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * p.D * p.D, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::FwdArgs a = fwd_args(s, p, q, k, v, gates->f, gates->b_x, gates->w_hat, S0, o, S_T);
+  a.logits = 1;
+  a.gA = gates->A;
+  a.gtau = gates->tau;
+  a.mode = 1;
+  a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, 1);
+  hipError_t e = carve::launch_fwd_prep(a, hs);
+  if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+size_t carve_bwd_logits_workspace_size(const carve_shape* s) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK || p.empty) return 0;
+  return bwd_ws(s, p) + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) + 512;
+}
+
+carve_status carve_bwd_logits(const carve_shape* s, const void* q, const void* k, const void* v,
+                              const carve_gate_logits* gates, const float* S0, const void* dO, const float* dS_T,
+                              void* dq, void* dk, void* dv, float* df, float* dA, float* dtau, float* db_x,
+                              float* dw_hat, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  st = check_logits(s, p, gates);
+  if (st != CARVE_OK) return st;
+  if ((gates->b_x == nullptr) != (db_x == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!q || !k || !v || !dO || !dq || !dk || !dv || !df || !dA || !dtau || !dw_hat))
+    return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, (const void*)S0, dO, (const void*)dS_T, (const void*)dq, (const void*)dk,
+                          (const void*)dv, (const void*)df, (const void*)db_x, (const void*)dw_hat, (const void*)dS0})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need = carve_bwd_logits_workspace_size(s);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = dS0 ? carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * p.D * p.D, hs) : hipSuccess;
+    if (e == hipSuccess && dA && s->H > 0) e = carve::launch_copy_or_zero(dA, nullptr, (size_t)s->H * p.D, hs);
+    if (e == hipSuccess && dtau && s->H > 0) e = carve::launch_copy_or_zero(dtau, nullptr, (size_t)s->H * p.D, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fwd = fwd_args(s, p, q, k, v, gates->f, gates->b_x, gates->w_hat, S0, nullptr, nullptr);
+  a.fwd.logits = 1;
+  a.fwd.gA = gates->A;
+  a.fwd.gtau = gates->tau;
+  a.fwd.mode = 2;
+  char* ws = align_up(workspace);
+  a.fwd.f = carve::carve_factors(ws, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2);
+  char* base = align_up(ws + carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2));
+  const size_t states = states_bytes(s, p);
+  a.fwd.S_vk = base;
+  a.dS_vk = align_up(base + states);
+  float* partA = reinterpret_cast<float*>(align_up(static_cast<char*>(a.dS_vk) + states));
+  a.dO = dO;
+  a.dS_T = dS_T;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_g = df;        // d/dlog g, turned into d/df by the logit pass
+  a.db = db_x;          // the chunk kernel returns d/db_x directly
+  a.dw = dw_hat;        // ... and d/dw_hat
+  a.dS0 = dS0;
+  hipError_t e = carve::launch_fwd_prep(a.fwd, hs);
+  if (e == hipSuccess) e = carve::launch_fwd_state(a.fwd, hs);
+  if (e == hipSuccess) e = carve::launch_bwd_state(a, hs);
+  if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
+  carve::LogitGradArgs lg = {};
+  lg.B = s->B;
+  lg.H = s->H;
+  lg.T = s->T;
+  lg.D = p.D;
+  lg.f = gates->f;
+  lg.A = gates->A;
+  lg.tau = gates->tau;
+  lg.df = df;
+  lg.partA = partA;
+  lg.partT = partA + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) / (2 * sizeof(float));
+  if (e == hipSuccess) e = carve::launch_logit_grads(lg, dA, dtau, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
 // Workspace of carve_bwd_content, in order: the content forward's factor slot, its
 // output (scratch), z and m of every period, the gates b, the token-only backward's
 // workspace (factors, S and dS per chunk), dO with the mean-output term, the dS carry,

@@ -135,10 +135,15 @@ __device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_
 // and its activation: token-only with b given, token-only with b = 1, or
 // content-aware b = sigmoid(b_x + z) with the chunk's content signal z (per key
 // channel, in LDS).
+// Every source also maps the staged decay input to log g (logdecay, per key channel
+// ch of head h) and the staged write input to w (wact); both are the identity unless
+// the gates come as pre-activations.
 struct TokenGatesB {
   const float* b;
   __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b + idx); }
   __device__ __forceinline__ float act(float x, int) const { return x; }
+  __device__ __forceinline__ float logdecay(float x, int, int) const { return x; }
+  __device__ __forceinline__ float wact(float x) const { return x; }
 };
 struct TokenGates1 {
   __device__ __forceinline__ Frag<float> load8(size_t) const {
@@ -148,12 +153,38 @@ struct TokenGates1 {
     return f;
   }
   __device__ __forceinline__ float act(float x, int) const { return x; }
+  __device__ __forceinline__ float logdecay(float x, int, int) const { return x; }
+  __device__ __forceinline__ float wact(float x) const { return x; }
 };
 struct ContentGates {
   const float* b_x;
   const float* z;
   __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b_x + idx); }
   __device__ __forceinline__ float act(float x, int ch) const { return 1.f / (1.f + __expf(-(x + z[ch]))); }
+  __device__ __forceinline__ float logdecay(float x, int, int) const { return x; }
+  __device__ __forceinline__ float wact(float x) const { return x; }
+};
+
+// Gates given as pre-activations (the fused gate of the notes, section 2.3):
+// log g = -A softplus(f + tau) with A, tau per head and key channel, b = sigmoid(b_x)
+// (HAS_BX; else b = 1), w = sigmoid(w_hat).  The staged decay input is f, the staged
+// erase input b_x, the staged write input w_hat.
+__device__ __forceinline__ float softplusf(float y) { return fmaxf(y, 0.f) + log1pf(__expf(-fabsf(y))); }
+__device__ __forceinline__ float sigmoidf(float y) { return 1.f / (1.f + __expf(-y)); }
+template <int D, bool HAS_BX>
+struct LogitGates {
+  const float* b_x;
+  const float* A;     // [H][D]
+  const float* tau;   // [H][D]
+  __device__ __forceinline__ Frag<float> load8(size_t idx) const {
+    if constexpr (HAS_BX) return load_frag(b_x + idx);
+    return TokenGates1{}.load8(idx);
+  }
+  __device__ __forceinline__ float act(float x, int) const { return HAS_BX ? sigmoidf(x) : x; }
+  __device__ __forceinline__ float logdecay(float x, int ch, int h) const {
+    return -A[h * D + ch] * softplusf(x + tau[h * D + ch]);
+  }
+  __device__ __forceinline__ float wact(float x) const { return sigmoidf(x); }
 };
 
 // ------------------------------------------------------------------ per-chunk prep
@@ -175,6 +206,7 @@ struct PrepStage {
   Frag<T> k[NST], q[NST], v[NST];
   Frag<float> lg[NST], g[NST];
   float w;
+  int h;          // head of the staged chunk
 };
 
 template <typename T, int LC, int D, typename Gates, int NT>
@@ -189,6 +221,7 @@ __device__ __forceinline__ void prep_stage_load(const FwdArgs& a, const Gates& g
   const T* vb = reinterpret_cast<const T*>(a.v) + row0 * D;
   const float* lb = a.log_g + row0 * D;
   st.w = a.w[row0 + min(tid, n - 1)];
+  st.h = bh % a.H;
 #pragma unroll
   for (int u = 0; u < St::NST; ++u) {
     const int idx = min(tid + NT * u, St::NP - 1), r = idx / St::PR, g = idx % St::PR;
@@ -216,7 +249,7 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
   float* wL = reinterpret_cast<float*>(smem + Lay::R7);
   const int tid = threadIdx.x;
   const int n = min(LC, a.T - c * LC);
-  if (tid < LC) wL[tid] = (tid < n) ? st.w : 0.f;
+  if (tid < LC) wL[tid] = (tid < n) ? gates.wact(st.w) : 0.f;
 #pragma unroll
   for (int u = 0; u < St::NST; ++u) {
     const int idx = tid + NT * u;
@@ -229,8 +262,8 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
       f32x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lo[e] = valid ? __expf(st.lg[u].lo[e]) * gates.act(st.g[u].lo[e], 8 * g + e) : 1.f;
-        hi[e] = valid ? __expf(st.lg[u].hi[e]) * gates.act(st.g[u].hi[e], 8 * g + 4 + e) : 1.f;
+        lo[e] = valid ? __expf(gates.logdecay(st.lg[u].lo[e], 8 * g + e, st.h)) * gates.act(st.g[u].lo[e], 8 * g + e) : 1.f;
+        hi[e] = valid ? __expf(gates.logdecay(st.lg[u].hi[e], 8 * g + 4 + e, st.h)) * gates.act(st.g[u].hi[e], 8 * g + 4 + e) : 1.f;
       }
       *reinterpret_cast<f32x4*>(aS + r * D + 8 * g) = lo;
       *reinterpret_cast<f32x4*>(aS + r * D + 8 * g + 4) = hi;

@@ -53,6 +53,12 @@ struct FwdArgs {
   float* S_T;             // may be null
   void* S_vk;             // may be null: state entering every chunk, [ci][D*D] dtype, fragment order rows v
   ChunkFactors f;
+  // gates as pre-activations (logits != 0): log_g then holds the decay logits f, b the
+  // erase pre-activation b_x (or null), w the write pre-activation w_hat, and
+  // log g = -gA softplus(f + gtau) (gA, gtau [H][D]), b = sigmoid(b_x), w = sigmoid(w_hat)
+  int logits;
+  const float* gA;
+  const float* gtau;
 };
 
 struct ContentArgs {
@@ -123,6 +129,18 @@ struct ContentBwdArgs {
   float* dm0;                 // [B*H][D] or null
 };
 
+// Logit-space epilogue of the backward for gates given as pre-activations.
+struct LogitGradArgs {
+  int B, H, T, D;
+  const float* f;             // [B,H,T,D] decay logits
+  const float* A;             // [H,D]
+  const float* tau;           // [H,D]
+  float* df;                  // [B,H,T,D] in: d/dlog g; out: d/df
+  float* partA;               // [B*H][token blocks][D] partial sums
+  float* partT;
+};
+size_t logit_partials_bytes(int B, int H, int T, int D);
+
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode);
 ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode);
 
@@ -138,5 +156,6 @@ hipError_t launch_add_grad_mean(const ContentBwdArgs& a, int dtype, const void* 
 hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, hipStream_t st);
 hipError_t launch_init_grad_mean(const ContentBwdArgs& a, const float* dm_out, hipStream_t st);
 hipError_t launch_sum_over_batch(const float* part, float* out, int B, int H, int n, hipStream_t st);
+hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hipStream_t st);
 
 }  // namespace carve

@@ -9,8 +9,9 @@
 // and dm_{p-1} / L is added to the output gradient of every token of period p-1
 // (period 0's dm goes to m0).  The library runs the periods in reverse; these
 // kernels are the per-period pieces around the token-only backward kernels.
-#include "carve_device.h"
-#include "carve_internal.h"
+// The file also holds the logit-space epilogue of the backward for gates given as
+// pre-activations (d f, d A, d tau).
+#include "carve_chunk.h"
 
 namespace carve {
 
@@ -125,6 +126,69 @@ __global__ __launch_bounds__(256) void sum_over_batch_kernel(const float* part, 
     for (int b = 0; b < B; ++b) s += part[((size_t)b * H + h) * n + j];
     out[i] = s;
   }
+}
+
+// ------------------------------------------------------------ gate pre-activations
+// d/df = d/dlog g * (-A sigmoid(f + tau)) in place over the buffer holding d/dlog g,
+// with per-(sequence, token block) column sums of d/df (-> d tau) and of
+// d/dlog g * (-softplus(f + tau)) (-> d A).  One workgroup per (b*H + h, block of
+// kLogitBlock tokens); thread t owns column t % D and every (256 / D)-th token.
+constexpr int kLogitBlock = 256;
+__global__ __launch_bounds__(256) void logit_grads_kernel(LogitGradArgs a) {
+  __shared__ float pa[256], pt[256];
+  const int bh = blockIdx.x, tb = blockIdx.y, tid = threadIdx.x, D = a.D, h = bh % a.H;
+  const int k = tid % D, part = tid / D, nparts = 256 / D;
+  const float A = a.A[h * D + k], tau = a.tau[h * D + k];
+  const int t0 = tb * kLogitBlock, t1 = min(t0 + kLogitBlock, a.T);
+  float sa = 0.f, st = 0.f;
+  for (int t = t0 + part; t < t1; t += nparts) {
+    const size_t i = ((size_t)bh * a.T + t) * D + k;
+    const float y = a.f[i] + tau;
+    const float dlg = a.df[i];
+    const float df = -dlg * A * sigmoidf(y);
+    a.df[i] = df;
+    st += df;
+    sa -= dlg * softplusf(y);
+  }
+  pa[tid] = sa;
+  pt[tid] = st;
+  __syncthreads();
+  if (tid < D) {
+    float s1 = 0.f, s2 = 0.f;
+    for (int pp = 0; pp < nparts; ++pp) {
+      s1 += pa[pp * D + tid];
+      s2 += pt[pp * D + tid];
+    }
+    const size_t o = ((size_t)bh * gridDim.y + tb) * D + tid;
+    a.partA[o] = s1;
+    a.partT[o] = s2;
+  }
+}
+
+// out[h][k] = sum over the batch and token blocks of part[(b*H + h) * nblk + tb][k]
+__global__ __launch_bounds__(256) void sum_heads_kernel(const float* part, float* out, int B, int H, int nblk, int D) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= H * D) return;
+  const int h = i / D, k = i % D;
+  float s = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int tb = 0; tb < nblk; ++tb) s += part[(((size_t)b * H + h) * nblk + tb) * D + k];
+  out[i] = s;
+}
+
+hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hipStream_t st) {
+  const int nblk = (a.T + kLogitBlock - 1) / kLogitBlock;
+  hipLaunchKernelGGL(logit_grads_kernel, dim3(a.B * a.H, nblk), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned g = (unsigned)((a.H * a.D + 255) / 256);
+  hipLaunchKernelGGL(sum_heads_kernel, dim3(g), dim3(256), 0, st, a.partA, dA, a.B, a.H, nblk, a.D);
+  hipLaunchKernelGGL(sum_heads_kernel, dim3(g), dim3(256), 0, st, a.partT, dtau, a.B, a.H, nblk, a.D);
+  return hipGetLastError();
+}
+
+size_t logit_partials_bytes(int B, int H, int T, int D) {
+  return 2 * (size_t)B * H * ((T + kLogitBlock - 1) / kLogitBlock) * D * sizeof(float);
 }
 
 static unsigned grid_for(size_t n, unsigned cap = 4096) {

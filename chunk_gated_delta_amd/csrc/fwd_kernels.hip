@@ -48,11 +48,16 @@ __device__ __forceinline__ void prep_loop(const FwdArgs& a, const Gates& gates, 
   }
 }
 
-template <typename T, int LC, int D, int MODE>
+template <typename T, int LC, int D, int MODE, bool LOGITS>
 __global__ __launch_bounds__(4 * D) void fwd_prep_kernel(FwdArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  if (a.b) prep_loop<T, LC, D, MODE>(a, TokenGatesB{a.b}, smem);
-  else prep_loop<T, LC, D, MODE>(a, TokenGates1{}, smem);
+  if constexpr (LOGITS) {
+    if (a.b) prep_loop<T, LC, D, MODE>(a, LogitGates<D, true>{a.b, a.gA, a.gtau}, smem);
+    else prep_loop<T, LC, D, MODE>(a, LogitGates<D, false>{nullptr, a.gA, a.gtau}, smem);
+  } else {
+    if (a.b) prep_loop<T, LC, D, MODE>(a, TokenGatesB{a.b}, smem);
+    else prep_loop<T, LC, D, MODE>(a, TokenGates1{}, smem);
+  }
 }
 
 // ------------------------------------------------------------------ state step
@@ -493,8 +498,10 @@ template <typename T, int LC, int D>
 static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = PrepLayout<T, LC, D, prep_threads<D>()>;
   static_assert(Lay::bytes <= 160 * 1024, "prep LDS exceeds 160 KB");
-  auto kern = a.mode == 3 ? fwd_prep_kernel<T, LC, D, 3>
-              : (a.mode == 2 ? fwd_prep_kernel<T, LC, D, 2> : fwd_prep_kernel<T, LC, D, 1>);
+  auto kern = a.logits ? (a.mode == 3 ? fwd_prep_kernel<T, LC, D, 3, true>
+                                      : (a.mode == 2 ? fwd_prep_kernel<T, LC, D, 2, true> : fwd_prep_kernel<T, LC, D, 1, true>))
+                       : (a.mode == 3 ? fwd_prep_kernel<T, LC, D, 3, false>
+                                      : (a.mode == 2 ? fwd_prep_kernel<T, LC, D, 2, false> : fwd_prep_kernel<T, LC, D, 1, false>));
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;

@@ -202,6 +202,47 @@ carve_status carve_bwd_saved(const carve_shape* s,
                              const carve_profile* profile);
 
 /*
+ * Gates given as pre-activations, activated inside the kernels (the fused gate of
+ * the notes, section 2.3: A the log-decay amplitude, f the decay logits, tau a bias,
+ * the output log g <= 0; w_hat the scalar write pre-activation).  Reading taken:
+ *     log g = -A softplus(f + tau),   b = sigmoid(b_x) (b = 1 without b_x),
+ *     w = sigmoid(w_hat),
+ * with A (> 0 for log g <= 0) and tau per head and key channel.
+ */
+typedef struct {
+  const float* f;      /* (device) [B,H,T,Dk] decay logits                         */
+  const float* A;      /* (device) [H,Dk]     decay amplitude                      */
+  const float* tau;    /* (device) [H,Dk]     decay bias                           */
+  const float* b_x;    /* (device) [B,H,T,Dk] erase pre-activation, or NULL (b = 1) */
+  const float* w_hat;  /* (device) [B,H,T]    write pre-activation                 */
+} carve_gate_logits;
+
+/*
+ * Forward with gates given as pre-activations (token-only gates): as carve_fwd with
+ * log_g, b, w replaced by `gates`; workspace of carve_fwd_workspace_size(s, NULL).
+ */
+carve_status carve_fwd_logits(const carve_shape* s,
+                              const void* q, const void* k, const void* v,
+                              const carve_gate_logits* gates, const float* S0,
+                              void* o, float* S_T,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Its backward: as carve_bwd, with the gate gradients in the pre-activations'
+ * space: df (float) [B,H,T,Dk]; dA, dtau (float) [H,Dk], summed over batch and
+ * tokens; db_x (float) [B,H,T,Dk], required iff gates->b_x is given; dw_hat (float)
+ * [B,H,T].  Workspace of carve_bwd_logits_workspace_size() bytes.
+ */
+size_t carve_bwd_logits_workspace_size(const carve_shape* s);
+carve_status carve_bwd_logits(const carve_shape* s,
+                              const void* q, const void* k, const void* v,
+                              const carve_gate_logits* gates, const float* S0,
+                              const void* dO, const float* dS_T,
+                              void* dq, void* dk, void* dv, float* df, float* dA, float* dtau,
+                              float* db_x, float* dw_hat, float* dS0,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Backward through the content-aware erase (notes section 2.2): gradients of the
  * content-aware forward, including the projection and the chain through each
  * chunk's mean output into the next chunk's gate.  Recomputes the forward.

@@ -186,3 +186,24 @@ def test_bwd_content_rejects_bad_arguments(lib):
     need = lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(proj))
     assert need > lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(plain)) > 0
     assert call_bwd_content(lib, s, proj, dU1=FAKE, dU2=FAKE, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_logits_entry_points_reject_bad_arguments(lib):
+    s = shape()
+    g = carve.carve_gate_logits(FAKE, FAKE, FAKE, None, FAKE)
+    call = lambda gates, **kw: lib.carve_fwd_logits(ctypes.byref(s), FAKE, FAKE, FAKE,
+                                                    ctypes.byref(gates) if gates is not None else None, None,
+                                                    kw.get("o", FAKE), None, FAKE, 1 << 40, None)
+    assert call(None) == INVALID
+    assert call(carve.carve_gate_logits(FAKE, None, FAKE, None, FAKE)) == INVALID     # A required
+    assert call(carve.carve_gate_logits(FAKE + 4, FAKE, FAKE, None, FAKE)) == INVALID  # misaligned f
+    assert call(g, o=None) == INVALID
+    need = lib.carve_bwd_logits_workspace_size(ctypes.byref(s))
+    assert need > 0
+
+    def bwd(gates, db_x=None, ws_bytes=1 << 40):
+        return lib.carve_bwd_logits(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(gates), None, FAKE, None,
+                                    FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, db_x, FAKE, None, FAKE, ws_bytes, None)
+    assert bwd(g, db_x=FAKE) == INVALID                                                # db_x only with b_x
+    assert bwd(carve.carve_gate_logits(FAKE, FAKE, FAKE, FAKE, FAKE)) == INVALID       # ... and then required
+    assert bwd(g, ws_bytes=need - 1) == WORKSPACE

@@ -1,0 +1,96 @@
+"""GPU parity of the forward and backward with gates given as pre-activations
+(needs an MI355X): log g = -A softplus(f + tau), b = sigmoid(b_x), w = sigmoid(w_hat)
+activated inside the kernels, compared with the float64 reference (itself pinned by
+finite differences).  Error metric: max|gpu - ref| / max|ref| per tensor; bars 1e-4
+(float32 inputs) and 2e-2 (bfloat16 inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunk_gated_delta_amd import carve
+from chunk_gated_delta_amd.synth import random_inputs
+from tests.helpers import max_rel, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def f32np(x):
+    return np.asarray(x, np.float32).astype(np.float64)
+
+
+def logit_case(B, H, T, D, dtype, seed, with_bx=True):
+    inp = random_inputs(B, H, T, D, D, dtype=dtype, seed=seed, erase="none", with_dO=True)
+    rng = np.random.default_rng(seed + 7)
+    inp["f"] = f32np(rng.standard_normal((B, H, T, D)))
+    inp["A"] = f32np(rng.uniform(0.05, 0.5, (H, D)))
+    inp["tau"] = f32np(rng.standard_normal((H, D)) * 0.5)
+    inp["w_hat"] = f32np(rng.standard_normal((B, H, T)))
+    inp["b_x"] = f32np(rng.normal(2.0, 1.0, (B, H, T, D))) if with_bx else None
+    inp["S0"] = f32np(rng.standard_normal((B, H, D, D)) * 0.3)
+    inp["dS_T"] = f32np(rng.standard_normal((B, H, D, D)) * 0.3)
+    return inp
+
+
+def dev(x):
+    return None if x is None else torch.from_numpy(np.asarray(x, np.float32)).cuda()
+
+
+CASES = [("f32", 1, 2, 100, 64, True), ("bf16", 2, 2, 200, 128, True), ("bf16", 1, 2, 130, 128, False),
+         ("f32", 2, 1, 64, 128, False)]
+IDS = [f"{c[0]}_T{c[3]}_d{c[4]}_{'bx' if c[5] else 'nob'}" for c in CASES]
+
+
+@pytest.mark.parametrize("dtype,B,H,T,D,with_bx", CASES, ids=IDS)
+def test_fwd_logits_parity(dtype, B, H, T, D, with_bx):
+    announce(f"fwd logits {dtype} T{T} d{D} b_x={with_bx}")
+    inp = logit_case(B, H, T, D, dtype, seed=500 + T + D, with_bx=with_bx)
+    d = to_device(inp, dtype)
+    o, S_T = carve.fwd_logits(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]),
+                              dev(inp["w_hat"]), b_x=dev(inp["b_x"]), S0=dev(inp["S0"]))
+    torch.cuda.synchronize()
+    ro, rS = oracle.forward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"],
+                                   b_x=inp["b_x"], S0=inp["S0"])
+    eo, es = max_rel(to_np(o), ro), max_rel(to_np(S_T), rS)
+    print(f"  err o={eo:.2e} S_T={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,B,H,T,D,with_bx", CASES, ids=IDS)
+def test_bwd_logits_parity(dtype, B, H, T, D, with_bx):
+    announce(f"bwd logits {dtype} T{T} d{D} b_x={with_bx}")
+    inp = logit_case(B, H, T, D, dtype, seed=600 + T + D, with_bx=with_bx)
+    d = to_device(inp, dtype)
+    g = carve.bwd_logits(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]), dev(inp["w_hat"]),
+                         d["dO"], b_x=dev(inp["b_x"]), S0=dev(inp["S0"]), dS_T=dev(inp["dS_T"]))
+    torch.cuda.synchronize()
+    ref = oracle.backward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"],
+                                 inp["dO"], b_x=inp["b_x"], S0=inp["S0"], dS_T=inp["dS_T"])
+    errs = {}
+    for key in ("dq", "dk", "dv", "df", "dA", "dtau", "db_x", "dw_hat", "dS0"):
+        if ref[key] is None:
+            assert g[key] is None
+            continue
+        errs[key] = max_rel(to_np(g[key]), ref[key])
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
+
+
+def test_logits_match_activated_gates():
+    """The fused activation agrees with passing the activated gates (computed in
+    float32 on the device) to the plain entry points, within the bf16 bar."""
+    announce("logits vs activated gates")
+    inp = logit_case(2, 2, 256, 128, "bf16", seed=700)
+    d = to_device(inp, "bf16")
+    f, A, tau, wh, bx = (dev(inp[k_]) for k_ in ("f", "A", "tau", "w_hat", "b_x"))
+    log_g = -A[None, :, None, :] * torch.nn.functional.softplus(f + tau[None, :, None, :])
+    b, w = torch.sigmoid(bx), torch.sigmoid(wh)
+    o1, S1 = carve.fwd_logits(d["q"], d["k"], d["v"], f, A, tau, wh, b_x=bx)
+    o2, S2, _ = carve.fwd(d["q"], d["k"], d["v"], log_g.contiguous(), w.contiguous(), b=b.contiguous())
+    torch.cuda.synchronize()
+    assert max_rel(to_np(o1), to_np(o2)) <= 2e-2 and max_rel(to_np(S1), to_np(S2)) <= 2e-2
