@@ -45,6 +45,7 @@ def parse():
     p.add_argument("--no-content", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the long-context forward")
     p.add_argument("--no-decode", action="store_true", help="skip the recurrent decode step")
+    p.add_argument("--no-logits", action="store_true", help="skip the gate pre-activation entry points")
     return p.parse_args()
 
 
@@ -272,6 +273,11 @@ def main():
         extra["content_bwd_tokens_per_s"] = wc.B * wc.T / (cbms * 1e-3)
         del cq, ck, cv, cf, cont, ws_c, co, cdo, ws_cb
 
+    # gates given as pre-activations (activated inside the kernels), same shape; the plain
+    # backward that recomputes the forward is timed beside it
+    if not args.no_logits:
+        extra["logits"] = logits_bench(q, k, v, dO, wl, dev)
+
     # recurrent decode step (one token per sequence and head, state updated in place)
     if not args.no_decode:
         extra["decode"] = {f"B{db}_H{H}": decode_bench(db, H, D, dev) for db in (B, 256)}
@@ -326,6 +332,39 @@ def main():
         "extra": extra,
     }
     print(json.dumps(line))
+
+
+def logits_bench(q, k, v, dO, wl, dev, nrep=5):
+    """Time fwd_logits / bwd_logits and the plain recomputing backward at the workload shape."""
+    import torch
+    from chunk_gated_delta_amd import carve
+    B, H, T, D = wl.B, wl.H, wl.T, wl.Dk
+    gen = torch.Generator(device=dev).manual_seed(1007)
+    f = torch.randn((B, H, T, D), generator=gen, device=dev)
+    A = torch.rand((H, D), generator=gen, device=dev) * 0.2 + 0.02
+    tau = torch.randn((H, D), generator=gen, device=dev) * 0.5
+    w_hat = torch.randn((B, H, T), generator=gen, device=dev)
+    b_x = torch.randn((B, H, T, D), generator=gen, device=dev) + 2.0
+    ws_f = torch.empty(max(1, carve.fwd_workspace_bytes(q, v, wl.L)), dtype=torch.uint8, device=dev)
+    log_g = (-A[None, :, None, :] * torch.nn.functional.softplus(f + tau[None, :, None, :])).contiguous()
+    b, w = torch.sigmoid(b_x).contiguous(), torch.sigmoid(w_hat).contiguous()
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nrep):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) / nrep, 4)
+    out = {"fwd_logits_ms": timed(lambda: carve.fwd_logits(q, k, v, f, A, tau, w_hat, b_x=b_x, L=wl.L,
+                                                           workspace=ws_f)),
+           "bwd_logits_ms": timed(lambda: carve.bwd_logits(q, k, v, f, A, tau, w_hat, dO, b_x=b_x, L=wl.L)),
+           "bwd_plain_ms": timed(lambda: carve.bwd(q, k, v, log_g, w, dO, b=b, L=wl.L))}
+    return out
 
 
 def decode_bench(B, H, D, dev, nrep=200):

@@ -393,6 +393,14 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     if (HAS_B) bx[u] = load_frag(f.b + src);
     dOx[u] = load_frag(dO + src);
   }
+  // gates as pre-activations: amplitude and bias of the thread's 8 channels (the same
+  // for all of its pieces, as NT is a multiple of D / 8)
+  Frag<float> pA, pT;
+  if constexpr (LG) {
+    static_assert(NT % PR == 0, "pieces of a thread must share their channels");
+    pA = load_frag(f.gA + (bh % f.H) * D + 8 * (tid % PR));
+    pT = load_frag(f.gtau + (bh % f.H) * D + 8 * (tid % PR));
+  }
   constexpr int TP = LC * LC / 4, NTP = (TP + NT - 1) / NT;   // 4 consecutive columns per piece
   f32x4 tpre[NTP];
 #pragma unroll
@@ -410,11 +418,10 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? vx[u] : zero_frag(T());
     if constexpr (LG) {
       const LogitGates<D, HAS_B> gate{nullptr, f.gA, f.gtau};
-      const int h = bh % f.H;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lx[u].lo[e] = gate.logdecay(lx[u].lo[e], 8 * g + e, h);
-        lx[u].hi[e] = gate.logdecay(lx[u].hi[e], 8 * g + 4 + e, h);
+        lx[u].lo[e] = gate.logdecay_p(lx[u].lo[e], pA.lo[e], pT.lo[e]);
+        lx[u].hi[e] = gate.logdecay_p(lx[u].hi[e], pA.hi[e], pT.hi[e]);
         if (HAS_B) {
           bx[u].lo[e] = sigmoidf(bx[u].lo[e]);
           bx[u].hi[e] = sigmoidf(bx[u].hi[e]);

@@ -135,17 +135,18 @@ __device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_
 // and its activation: token-only with b given, token-only with b = 1, or
 // content-aware b = sigmoid(b_x + z) with the chunk's content signal z (per key
 // channel, in LDS).
-// Every source also maps the staged decay input to log g (logdecay, per key channel
-// ch of head h) and the staged write input to w (wact); both are the identity unless
-// the gates come as pre-activations.
+// Every source also maps the staged write input to w (wact: the identity unless the
+// gates come as pre-activations; kLogits marks that case, whose staged decay input is
+// the logit f).
 struct TokenGatesB {
+  static constexpr bool kLogits = false;
   const float* b;
   __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b + idx); }
   __device__ __forceinline__ float act(float x, int) const { return x; }
-  __device__ __forceinline__ float logdecay(float x, int, int) const { return x; }
   __device__ __forceinline__ float wact(float x) const { return x; }
 };
 struct TokenGates1 {
+  static constexpr bool kLogits = false;
   __device__ __forceinline__ Frag<float> load8(size_t) const {
     Frag<float> f;
     f.lo = f32x4{1.f, 1.f, 1.f, 1.f};
@@ -153,15 +154,14 @@ struct TokenGates1 {
     return f;
   }
   __device__ __forceinline__ float act(float x, int) const { return x; }
-  __device__ __forceinline__ float logdecay(float x, int, int) const { return x; }
   __device__ __forceinline__ float wact(float x) const { return x; }
 };
 struct ContentGates {
+  static constexpr bool kLogits = false;
   const float* b_x;
   const float* z;
   __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b_x + idx); }
   __device__ __forceinline__ float act(float x, int ch) const { return 1.f / (1.f + __expf(-(x + z[ch]))); }
-  __device__ __forceinline__ float logdecay(float x, int, int) const { return x; }
   __device__ __forceinline__ float wact(float x) const { return x; }
 };
 
@@ -169,10 +169,12 @@ struct ContentGates {
 // log g = -A softplus(f + tau) with A, tau per head and key channel, b = sigmoid(b_x)
 // (HAS_BX; else b = 1), w = sigmoid(w_hat).  The staged decay input is f, the staged
 // erase input b_x, the staged write input w_hat.
-__device__ __forceinline__ float softplusf(float y) { return fmaxf(y, 0.f) + log1pf(__expf(-fabsf(y))); }
-__device__ __forceinline__ float sigmoidf(float y) { return 1.f / (1.f + __expf(-y)); }
+// (hardware exp / log / reciprocal: softplus(y) = max(y, 0) + log(1 + exp(-|y|)))
+__device__ __forceinline__ float softplusf(float y) { return fmaxf(y, 0.f) + __logf(1.f + __expf(-fabsf(y))); }
+__device__ __forceinline__ float sigmoidf(float y) { return __builtin_amdgcn_rcpf(1.f + __expf(-y)); }
 template <int D, bool HAS_BX>
 struct LogitGates {
+  static constexpr bool kLogits = true;
   const float* b_x;
   const float* A;     // [H][D]
   const float* tau;   // [H][D]
@@ -181,9 +183,8 @@ struct LogitGates {
     return TokenGates1{}.load8(idx);
   }
   __device__ __forceinline__ float act(float x, int) const { return HAS_BX ? sigmoidf(x) : x; }
-  __device__ __forceinline__ float logdecay(float x, int ch, int h) const {
-    return -A[h * D + ch] * softplusf(x + tau[h * D + ch]);
-  }
+  // log g from the decay logit x and the channel's amplitude and bias
+  __device__ __forceinline__ float logdecay_p(float x, float a, float t) const { return -a * softplusf(x + t); }
   __device__ __forceinline__ float wact(float x) const { return sigmoidf(x); }
 };
 
@@ -206,7 +207,7 @@ struct PrepStage {
   Frag<T> k[NST], q[NST], v[NST];
   Frag<float> lg[NST], g[NST];
   float w;
-  int h;          // head of the staged chunk
+  int h;                // head of the staged chunk
 };
 
 template <typename T, int LC, int D, typename Gates, int NT>
@@ -249,6 +250,15 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
   float* wL = reinterpret_cast<float*>(smem + Lay::R7);
   const int tid = threadIdx.x;
   const int n = min(LC, a.T - c * LC);
+  // gates as pre-activations: amplitude and bias of the thread's 8 channels (every piece
+  // of a thread covers the same channels, as NT is a multiple of D / 8); [H][D] arrays
+  // small enough to stay cached, read here rather than held through the prefetch
+  Frag<float> pA, pT;
+  if constexpr (Gates::kLogits) {
+    static_assert(NT % St::PR == 0, "pieces of a thread must share their channels");
+    pA = load_frag(gates.A + st.h * D + 8 * (tid % St::PR));
+    pT = load_frag(gates.tau + st.h * D + 8 * (tid % St::PR));
+  }
   if (tid < LC) wL[tid] = (tid < n) ? gates.wact(st.w) : 0.f;
 #pragma unroll
   for (int u = 0; u < St::NST; ++u) {
@@ -262,8 +272,13 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
       f32x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        lo[e] = valid ? __expf(gates.logdecay(st.lg[u].lo[e], 8 * g + e, st.h)) * gates.act(st.g[u].lo[e], 8 * g + e) : 1.f;
-        hi[e] = valid ? __expf(gates.logdecay(st.lg[u].hi[e], 8 * g + 4 + e, st.h)) * gates.act(st.g[u].hi[e], 8 * g + 4 + e) : 1.f;
+        float llo = st.lg[u].lo[e], lhi = st.lg[u].hi[e];
+        if constexpr (Gates::kLogits) {
+          llo = gates.logdecay_p(llo, pA.lo[e], pT.lo[e]);
+          lhi = gates.logdecay_p(lhi, pA.hi[e], pT.hi[e]);
+        }
+        lo[e] = valid ? __expf(llo) * gates.act(st.g[u].lo[e], 8 * g + e) : 1.f;
+        hi[e] = valid ? __expf(lhi) * gates.act(st.g[u].hi[e], 8 * g + 4 + e) : 1.f;
       }
       *reinterpret_cast<f32x4*>(aS + r * D + 8 * g) = lo;
       *reinterpret_cast<f32x4*>(aS + r * D + 8 * g + 4) = hi;
