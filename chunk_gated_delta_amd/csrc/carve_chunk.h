@@ -73,8 +73,10 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
 // with the scaled blocks T_ii A_im formed first (all in parallel) and the T_ij
 // by increasing distance i - j.  The strictly lower blocks of A are overwritten;
 // the blocks of T above the diagonal are not written.
-// Kept out of line (each instantiation is shared by its callers) with LDS-typed
-// pointers, so that every access is an LDS instruction.
+// Kept out of line (inlined, its registers would add to the prefetched next chunk's
+// in the persistent prep loop), with LDS-typed pointers so that every access is an
+// LDS instruction.  An out-of-line function starts by waiting for all of its caller's
+// outstanding memory operations, so callers issue prefetches after this call.
 typedef __attribute__((address_space(3))) float lds_float;
 template <int LC, int LDF, int NT = kThreads>
 __device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_float* Tf) {
@@ -210,7 +212,8 @@ struct PrepStage {
   int h;                // head of the staged chunk
 };
 
-template <typename T, int LC, int D, typename Gates, int NT>
+// PART 1: log g, the erase input and w; PART 2: k, q, v; PART 0: all of them.
+template <typename T, int LC, int D, typename Gates, int NT, int PART = 0>
 __device__ __forceinline__ void prep_stage_load(const FwdArgs& a, const Gates& gates, int bh, int c,
                                                 PrepStage<T, LC, D, NT>& st) {
   using St = PrepStage<T, LC, D, NT>;
@@ -221,17 +224,24 @@ __device__ __forceinline__ void prep_stage_load(const FwdArgs& a, const Gates& g
   const T* qb = reinterpret_cast<const T*>(a.q) + row0 * D;
   const T* vb = reinterpret_cast<const T*>(a.v) + row0 * D;
   const float* lb = a.log_g + row0 * D;
-  st.w = a.w[row0 + min(tid, n - 1)];
-  st.h = bh % a.H;
+  if (PART != 2) {
+    st.w = a.w[row0 + min(tid, n - 1)];
+    st.h = bh % a.H;
+  }
+  // (the gate pieces, the larger half, are the ones issued early by the persistent loop)
 #pragma unroll
   for (int u = 0; u < St::NST; ++u) {
     const int idx = min(tid + NT * u, St::NP - 1), r = idx / St::PR, g = idx % St::PR;
     const unsigned e = (unsigned)(min(r, n - 1) * D + 8 * g);
-    st.k[u] = load_frag(kb + e);
-    st.q[u] = load_frag(qb + e);
-    st.v[u] = load_frag(vb + e);
-    st.lg[u] = load_frag(lb + e);
-    st.g[u] = gates.load8(row0 * D + e);
+    if (PART != 1) {
+      st.k[u] = load_frag(kb + e);
+      st.q[u] = load_frag(qb + e);
+      st.v[u] = load_frag(vb + e);
+    }
+    if (PART != 2) {
+      st.lg[u] = load_frag(lb + e);
+      st.g[u] = gates.load8(row0 * D + e);
+    }
   }
 }
 
@@ -287,9 +297,15 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
 }
 
 // The chunk's factors from its staged inputs (LDS, after a barrier).
-template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
+struct NoPrefetch {
+  __device__ __forceinline__ void operator()() const {}
+};
+// `after_solve` runs right after the triangular inverse (the persistent loop issues the
+// next chunk's loads there, past the out-of-line call's wait for outstanding loads).
+template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads,
+          typename AfterSolve = NoPrefetch>
 __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci,
-                             unsigned char* smem) {
+                             unsigned char* smem, const AfterSolve& after_solve = AfterSolve{}) {
   using Lay = PrepLayout<T, LC, D, NT>;
   constexpr int NW = NT / 64;
   constexpr int NB = LC / 16, NCT = D / 16;
@@ -424,6 +440,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
   // modes also keep that copy of the chunk (row-major [LC][LC])
   triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
+  after_solve();
   for (int idx = tid; idx < LC * LC / 4; idx += NT) {
     const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
     const f32x4 t4 = ((s >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);

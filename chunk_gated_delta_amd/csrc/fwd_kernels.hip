@@ -29,7 +29,10 @@ template <int D> constexpr int prep_threads() { return 4 * D; }
 
 // Persistent over chunks: workgroup g prepares chunks g, g + G, g + 2G, ... (G = grid
 // size, chunk index ci = bh * NC + c).  Once a chunk's raw inputs are staged in LDS
-// the registers take the next chunk's loads, which land while this chunk computes.
+// the registers take the next chunk's loads, which land while this chunk computes:
+// the gate pieces right away, k, q, v right after the chunk's triangular inverse (an
+// out-of-line call, which starts by waiting for every outstanding load; issuing only
+// part of the prefetch before it keeps that wait short and the live registers fewer).
 template <typename T, int LC, int D, int MODE, typename Gates>
 __device__ __forceinline__ void prep_loop(const FwdArgs& a, const Gates& gates, unsigned char* smem) {
   constexpr int NT = prep_threads<D>();
@@ -42,8 +45,10 @@ __device__ __forceinline__ void prep_loop(const FwdArgs& a, const Gates& gates, 
     prep_stage_write<T, LC, D, Gates, NT>(a, gates, c, st, smem);
     __syncthreads();
     const int cn = min(ci + (int)gridDim.x, total - 1);      // clamped: the last pass reloads a valid chunk
-    prep_stage_load<T, LC, D, Gates, NT>(a, gates, cn / a.NC, cn % a.NC, st);
-    prep_compute<T, LC, D, Gates, MODE, NT>(a, gates, bh, c, ci, smem);
+    prep_stage_load<T, LC, D, Gates, NT, 1>(a, gates, cn / a.NC, cn % a.NC, st);
+    prep_compute<T, LC, D, Gates, MODE, NT>(a, gates, bh, c, ci, smem, [&]() {
+      prep_stage_load<T, LC, D, Gates, NT, 2>(a, gates, cn / a.NC, cn % a.NC, st);
+    });
     __syncthreads();                                         // LDS is restaged by the next chunk
   }
 }
