@@ -138,3 +138,38 @@ def test_content_bwd_full_size_sampled_head():
         errs[key] = max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key])
     print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
     assert all(v_ <= TOL["bf16"] for v_ in errs.values()), errs
+
+
+@pytest.mark.parametrize("T,L,R", [(1, 64, 16), (59, 64, 1), (64, 64, 4)])
+def test_content_bwd_short_sequences(T, L, R):
+    """One token, one partial chunk, exactly one chunk (only m0 feeds a gate)."""
+    announce(f"content bwd short T{T} L{L} R{R}")
+    B, H, D = 2, 2, 128
+    inp = random_inputs(B, H, T, D, D, dtype="bf16", seed=400 + T, erase="content", dists="softplus_decay",
+                        with_dO=True, rank=R)
+    inp["U1"] = inp["U1"] * 8.0
+    inp["U2"] = inp["U2"] * 8.0
+    rng = np.random.default_rng(401)
+    ex = {"m0": np.asarray(rng.standard_normal((B, H, D)), np.float32).astype(np.float64),
+          "S0": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),
+          "dS_T": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),
+          "dm_out": np.asarray(rng.standard_normal((B, H, D)), np.float32).astype(np.float64)}
+    g, ref = run_both(inp, ex, "bf16", L)
+    check(g, ref, TOL["bf16"])
+
+
+def test_content_bwd_empty_sequence():
+    """T = 0: S_T = S0 and m_out = m0, so their gradients pass through; the rest is zero."""
+    announce("content bwd empty")
+    B, H, D = 1, 2, 64
+    z = torch.zeros((B, H, 0, D), dtype=torch.bfloat16, device="cuda")
+    zf = torch.zeros((B, H, 0, D), dtype=torch.float32, device="cuda")
+    dS_T = torch.randn((B, H, D, D), device="cuda")
+    dm_out = torch.randn((B, H, D), device="cuda")
+    U1 = torch.randn((H, 4, D), device="cuda")
+    U2 = torch.randn((H, D, 4), device="cuda")
+    g = carve.bwd_content(z, z, z, zf, torch.zeros((B, H, 0), device="cuda"), z, {"b_x": zf, "U1": U1, "U2": U2},
+                          dS_T=dS_T, dm_out=dm_out, L=64)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dS0"], dS_T) and torch.equal(g["dm0"], dm_out)
+    assert torch.count_nonzero(g["dU1"]) == 0 and torch.count_nonzero(g["dU2"]) == 0

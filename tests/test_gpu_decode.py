@@ -151,3 +151,22 @@ def test_decode_zero_projection_bit_exact():
         res.append((o, S, carry["m_in"], carry["csum"]))
     for x, y in zip(*res):
         assert torch.equal(x, y)
+
+
+def test_decode_content_rank64_d64():
+    """Largest projection rank (64) at key width 64, across a chunk boundary."""
+    announce("decode content rank 64 d64")
+    B, H, D, L, T, R = 2, 2, 64, 4, 9, 64
+    inp = random_inputs(B, H, T, D, D, dtype="bf16", seed=111, erase="content", dists="softplus_decay", rank=R)
+    inp["U1"] = inp["U1"] * 6.0
+    inp["U2"] = inp["U2"] * 6.0
+    d = to_device(inp, "bf16")
+    S = torch.zeros((B, H, D, D), dtype=torch.float32, device="cuda")
+    carry = {"U1": d["U1"], "U2": d["U2"], "m_in": None,
+             "csum": torch.zeros((B, H, D), dtype=torch.float32, device="cuda"), "pos": 0}
+    o = decode_run(d, T, S, L=L, b=False, content=carry)
+    ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L,
+                               content={"b_x": inp["b_x"], "U1": inp["U1"], "U2": inp["U2"]})
+    eo, es = max_rel(to_np(o), ro), max_rel(to_np(S), rS)
+    print(f"  err o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]

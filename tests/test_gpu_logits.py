@@ -94,3 +94,24 @@ def test_logits_match_activated_gates():
     o2, S2, _ = carve.fwd(d["q"], d["k"], d["v"], log_g.contiguous(), w.contiguous(), b=b.contiguous())
     torch.cuda.synchronize()
     assert max_rel(to_np(o1), to_np(o2)) <= 2e-2 and max_rel(to_np(S1), to_np(S2)) <= 2e-2
+
+
+def test_logits_single_token_and_empty():
+    announce("logits T1 and T0")
+    inp = logit_case(1, 2, 1, 128, "bf16", seed=801)
+    d = to_device(inp, "bf16")
+    g = carve.bwd_logits(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]), dev(inp["w_hat"]),
+                         d["dO"], b_x=dev(inp["b_x"]), S0=dev(inp["S0"]), dS_T=dev(inp["dS_T"]))
+    torch.cuda.synchronize()
+    ref = oracle.backward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"],
+                                 inp["dO"], b_x=inp["b_x"], S0=inp["S0"], dS_T=inp["dS_T"])
+    for key in ("dq", "dk", "dv", "df", "dA", "dtau", "db_x", "dw_hat", "dS0"):
+        assert max_rel(to_np(g[key]), ref[key]) <= TOL["bf16"], key
+    # no tokens: S_T = S0, and the amplitude / bias gradients are zero
+    z = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
+    zf = torch.zeros((1, 2, 0, 128), dtype=torch.float32, device="cuda")
+    S0 = dev(inp["S0"])
+    o, S_T = carve.fwd_logits(z, z, z, zf, dev(inp["A"]), dev(inp["tau"]), torch.zeros((1, 2, 0), device="cuda"),
+                              S0=S0)
+    torch.cuda.synchronize()
+    assert torch.equal(S_T, S0)
