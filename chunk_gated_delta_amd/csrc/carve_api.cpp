@@ -619,14 +619,17 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
   if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(ca.dU1p, nullptr, (size_t)p.BH * R * p.D, hs);
   if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(ca.dU2p, nullptr, (size_t)p.BH * p.D * R, hs);
   const int per = s->L / p.LC;     // tiles per period
+  // the last period's dO + dm_out / n; every other period's dO + g is written by the
+  // gate kernel of the period after it
+  ca.p = ca.NP - 1;
+  if (e == hipSuccess) e = carve::launch_add_grad_mean(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
   for (int pp = ca.NP - 1; pp >= 0 && e == hipSuccess; --pp) {
     ca.p = pp;
     a.c_lo = pp * per;
     a.c_count = std::min(per, p.NC - a.c_lo);
-    e = carve::launch_add_grad_mean(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
-    if (e == hipSuccess) e = carve::launch_bwd_state(a, hs);
+    e = carve::launch_bwd_state(a, hs);
     if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
-    if (e == hipSuccess) e = carve::launch_content_gate_bwd(ca, hs);
+    if (e == hipSuccess) e = carve::launch_content_gate_bwd(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
   }
   if (e == hipSuccess && dS0) e = carve::launch_copy_or_zero(dS0, carry, (size_t)p.BH * p.D * p.D, hs);
   if (e == hipSuccess && proj) e = carve::launch_sum_over_batch(ca.dU1p, dU1, s->B, s->H, R * p.D, hs);

@@ -125,7 +125,7 @@ struct ContentBwdArgs {
   const float* U2;            // [H,D,R]
   float* dU1p;                // [B*H][R][D] per-sequence accumulators
   float* dU2p;                // [B*H][D][R]
-  float* g;                   // [B*H][D] output-gradient term of the period being swept
+  float* g;                   // [B*H][D] output-gradient term of the last period (before the sweep)
   float* dm0;                 // [B*H][D] or null
 };
 
@@ -153,7 +153,7 @@ hipError_t launch_bwd_chunk(const BwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t st);
 hipError_t launch_content_gates(const ContentBwdArgs& a, const float* b_x, float* bmat, hipStream_t st);
 hipError_t launch_add_grad_mean(const ContentBwdArgs& a, int dtype, const void* dO, void* dOp, hipStream_t st);
-hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, hipStream_t st);
+hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, int dtype, const void* dO, void* dOp, hipStream_t st);
 hipError_t launch_init_grad_mean(const ContentBwdArgs& a, const float* dm_out, hipStream_t st);
 hipError_t launch_sum_over_batch(const float* part, float* out, int B, int H, int n, hipStream_t st);
 hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hipStream_t st);

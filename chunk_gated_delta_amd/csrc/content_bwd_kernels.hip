@@ -51,61 +51,117 @@ __global__ __launch_bounds__(256) void add_grad_mean_kernel(ContentBwdArgs a, co
 
 // Gate backward of period p for one head (one workgroup per head):
 // db (w.r.t. the gate probability, from the chunk-gradient kernel) -> db_x in place,
-// then the projection's gradients and the next period's output-gradient term g.
-__global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a) {
+// then the projection's gradients and the output-gradient term g of period p-1, which
+// is added at once to that period's dO (into dOp; period 0's dm goes to m0).
+// The rank contractions run 16 lanes per rank index with DPP row sums.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a, const T* dO, T* dOp) {
   __shared__ float dzp[256];
-  __shared__ float dz[128];
+  __shared__ float dz[D], gS[D];
   __shared__ float rS[64], drS[64];
-  const int bh = blockIdx.x, h = bh % a.H, tid = threadIdx.x, D = a.D;
+  const int bh = blockIdx.x, h = bh % a.H, tid = threadIdx.x;
   const int t0 = a.p * a.L, t1 = min(t0 + a.L, a.T);
   // dx = db * b (1 - b), summed over the period's tokens per key column
-  const int k = tid % D, part = tid / D, nparts = 256 / D;
+  constexpr int NPART = 256 / D;
+  const int k = tid % D, part = tid / D;
+  // (in batches of 8 tokens whose loads are all issued before the stores: the
+  // compiler cannot reorder a load past a store to a buffer that might alias it)
   float acc = 0.f;
-  for (int t = t0 + part; t < t1; t += nparts) {
-    const size_t i = ((size_t)bh * a.T + t) * D + k;
-    const float b = a.bmat[i];
-    const float dx = a.dbx[i] * b * (1.f - b);
-    a.dbx[i] = dx;
-    acc += dx;
+  for (int tb = t0 + part; tb < t1; tb += 8 * NPART) {
+    float bv[8], gv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = min(tb + j * NPART, t1 - 1);
+      const size_t i = ((size_t)bh * a.T + t) * D + k;
+      bv[j] = a.bmat[i];
+      gv[j] = a.dbx[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = tb + j * NPART;
+      if (t < t1) {
+        const float dx = gv[j] * bv[j] * (1.f - bv[j]);
+        a.dbx[((size_t)bh * a.T + t) * D + k] = dx;
+        acc += dx;
+      }
+    }
   }
   dzp[tid] = acc;
   __syncthreads();
   if (tid < D) {
     float s = 0.f;
-    for (int pp = 0; pp < nparts; ++pp) s += dzp[pp * D + tid];
+#pragma unroll
+    for (int pp = 0; pp < NPART; ++pp) s += dzp[pp * D + tid];
     dz[tid] = s;
   }
-  if (!a.U1) {
-    // no projection: nothing reaches the previous period or m0
-    if (tid < D) {
-      if (a.p > 0) a.g[(size_t)bh * D + tid] = 0.f;
-      else if (a.dm0) a.dm0[(size_t)bh * D + tid] = 0.f;
-    }
-    return;
-  }
+  const bool proj = a.U1 != nullptr;
   const float* m = a.m_all + ((size_t)bh * a.NP + a.p) * D;      // m_{p-1}
-  const float* U1 = a.U1 + (size_t)h * a.R * D;                  // [R][D]
-  const float* U2 = a.U2 + (size_t)h * D * a.R;                  // [D][R]
+  const float* U1 = proj ? a.U1 + (size_t)h * a.R * D : nullptr;  // [R][D]
+  const float* U2 = proj ? a.U2 + (size_t)h * D * a.R : nullptr;  // [D][R]
   __syncthreads();
-  if (tid < a.R) {
-    float r = 0.f, dr = 0.f;
-    for (int v = 0; v < D; ++v) r += U1[tid * D + v] * m[v];
-    for (int kk = 0; kk < D; ++kk) dr += U2[kk * a.R + tid] * dz[kk];
-    rS[tid] = r;
-    drS[tid] = dr;
-  }
-  __syncthreads();
-  float* dU2p = a.dU2p + (size_t)bh * D * a.R;
-  float* dU1p = a.dU1p + (size_t)bh * a.R * D;
-  for (int i = tid; i < D * a.R; i += 256) {
-    dU2p[i] += dz[i / a.R] * rS[i % a.R];
-    dU1p[i] += drS[i / D] * m[i % D];
+  if (proj) {
+    // r = U1 m and dr = U2^T dz: lanes 16 r' .. 16 r' + 15 of a row share rank index r'
+    constexpr int PER = D / 16;
+    for (int idx = tid; idx < 16 * a.R; idx += 256) {
+      const int r = idx >> 4, c = (idx & 15) * PER;
+      float x = 0.f, y = 0.f;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        x += U1[r * D + c + j] * m[c + j];
+        y += U2[(c + j) * a.R + r] * dz[c + j];
+      }
+      x = row16_sum(x);
+      y = row16_sum(y);
+      if ((idx & 15) == 0) {
+        rS[r] = x;
+        drS[r] = y;
+      }
+    }
+    __syncthreads();
+    float* dU2p = a.dU2p + (size_t)bh * D * a.R;
+    float* dU1p = a.dU1p + (size_t)bh * a.R * D;
+    for (int i0 = tid; i0 < D * a.R; i0 += 4 * 256) {
+      float u2[4], u1[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = min(i0 + 256 * j, D * a.R - 1);
+        u2[j] = dU2p[i];
+        u1[j] = dU1p[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + 256 * j;
+        if (i < D * a.R) {
+          dU2p[i] = u2[j] + dz[i / a.R] * rS[i % a.R];
+          dU1p[i] = u1[j] + drS[i / D] * m[i % D];
+        }
+      }
+    }
   }
   if (tid < D) {
     float dm = 0.f;
-    for (int r = 0; r < a.R; ++r) dm += U1[r * D + tid] * drS[r];
-    if (a.p > 0) a.g[(size_t)bh * D + tid] = dm / (float)a.L;     // period p-1 is whole
+    if (proj)
+      for (int r = 0; r < a.R; ++r) dm += U1[r * D + tid] * drS[r];
+    if (a.p > 0) gS[tid] = dm / (float)a.L;      // period p-1 is whole
     else if (a.dm0) a.dm0[(size_t)bh * D + tid] = dm;
+  }
+  if (a.p == 0) return;
+  __syncthreads();
+  // dO + g for the tokens of period p-1
+  const size_t base = ((size_t)bh * a.T + (size_t)(a.p - 1) * a.L) * D;
+  const int n4 = a.L * D / 4;
+  for (int i0 = tid; i0 < n4; i0 += 8 * 256) {
+    f32x4 x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = load4f(dO + base + 4 * min(i0 + 256 * j, n4 - 1));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 256 * j;
+      if (i < n4) {
+        const int col = (4 * i) % D;
+        store4(dOp + base + 4 * i, x[j] + f32x4{gS[col], gS[col + 1], gS[col + 2], gS[col + 3]});
+      }
+    }
   }
 }
 
@@ -212,9 +268,20 @@ hipError_t launch_add_grad_mean(const ContentBwdArgs& a, int dtype, const void* 
   return hipGetLastError();
 }
 
-hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(content_gate_bwd_kernel, dim3(a.B * a.H), dim3(256), 0, st, a);
+template <typename T>
+static hipError_t gate_bwd_launch(const ContentBwdArgs& a, const void* dO, void* dOp, hipStream_t st) {
+  const dim3 grid(a.B * a.H);
+  if (a.D == 128)
+    hipLaunchKernelGGL((content_gate_bwd_kernel<T, 128>), grid, dim3(256), 0, st, a,
+                       reinterpret_cast<const T*>(dO), reinterpret_cast<T*>(dOp));
+  else
+    hipLaunchKernelGGL((content_gate_bwd_kernel<T, 64>), grid, dim3(256), 0, st, a,
+                       reinterpret_cast<const T*>(dO), reinterpret_cast<T*>(dOp));
   return hipGetLastError();
+}
+
+hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, int dtype, const void* dO, void* dOp, hipStream_t st) {
+  return dtype ? gate_bwd_launch<bf16>(a, dO, dOp, st) : gate_bwd_launch<float>(a, dO, dOp, st);
 }
 
 hipError_t launch_init_grad_mean(const ContentBwdArgs& a, const float* dm_out, hipStream_t st) {

@@ -1,12 +1,13 @@
 """Drive the CARVE kernels for an external profiler (rocprofv3).
 
     python -m chunk_gated_delta_amd.profile_step [--steps 5] [--warmup 2]
-                                                  [--pass fwd+bwd|fwd|content|decode] [--copy-mib 0]
+                                                  [--pass fwd+bwd|fwd|content|content_bwd|decode]
+                                                  [--copy-mib 0]
                                                   [--decode-batch 256]
 
 Runs the 1.3B-head-shape workload (B4 H16 T4096 d128 L64, bf16 q/k/v, fp32 gates;
 synthetic seeded inputs) through the same entry points as bench.py: the training step
-(fwd_save + bwd_saved), the plain forward, the content-aware forward, or recurrent decode
+(fwd_save + bwd_saved), the plain forward, the content-aware forward or its backward, or recurrent decode
 steps (one token per sequence and head at batch --decode-batch).  With
 --copy-mib N it also runs a plain elementwise kernel that reads N MiB and writes N MiB
 (torch.neg), the reference against which HBM byte counters are scaled.  Prints one
@@ -21,7 +22,8 @@ def main(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--pass", dest="passes", default="fwd+bwd", choices=["fwd+bwd", "fwd", "content", "decode"])
+    p.add_argument("--pass", dest="passes", default="fwd+bwd",
+                   choices=["fwd+bwd", "fwd", "content", "content_bwd", "decode"])
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--copy-mib", type=int, default=0)
     args = p.parse_args(argv)
@@ -32,10 +34,10 @@ def main(argv=None):
     from chunk_gated_delta_amd.synth import WORKLOADS, make_inputs
 
     dev = torch.device("cuda:0")
-    wl = WORKLOADS["content_fwd" if args.passes == "content" else "head1p3b_fwd"]
+    wl = WORKLOADS["content_fwd" if args.passes in ("content", "content_bwd") else "head1p3b_fwd"]
     if args.passes == "decode":
         return decode(args, wl, dev)
-    inp = make_inputs(wl, with_dO=args.passes == "fwd+bwd")
+    inp = make_inputs(wl, with_dO=args.passes in ("fwd+bwd", "content_bwd"))
 
     def bf16(name):
         return torch.from_numpy(np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -46,9 +48,9 @@ def main(argv=None):
     q, k, v = bf16("q"), bf16("k"), bf16("v")
     log_g, w = f32("log_g"), f32("w")
     b = f32("b") if "b" in inp else None
-    dO = bf16("dO") if args.passes == "fwd+bwd" else None
+    dO = bf16("dO") if args.passes in ("fwd+bwd", "content_bwd") else None
     content = None
-    if args.passes == "content":
+    if args.passes in ("content", "content_bwd"):
         content = {"b_x": f32("b_x"), "U1": f32("U1"), "U2": f32("U2")}
     print(f"[profile_step] inputs ready: {wl.name} B{wl.B} H{wl.H} T{wl.T} d{wl.Dk} L{wl.L}", flush=True)
 
@@ -58,6 +60,8 @@ def main(argv=None):
             carve.bwd_saved(q, k, v, log_g, w, dO, saved, b=b, L=wl.L)
         elif args.passes == "fwd":
             carve.fwd(q, k, v, log_g, w, b=b, L=wl.L)
+        elif args.passes == "content_bwd":
+            carve.bwd_content(q, k, v, log_g, w, dO, content, L=wl.L)
         else:
             carve.fwd(q, k, v, log_g, w, L=wl.L, content=content)
 
