@@ -20,6 +20,8 @@ struct Plan {
   int NC;      // number of token tiles, ceil(T / LC)
   int VS;      // value rows per state workgroup
   bool empty;  // no token to process
+  int nseg;    // segments of the forward state pass (1: one sequential pass per head)
+  int seg_len; // chunks per segment
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -39,6 +41,38 @@ int value_slice(int BH, int D) {
   return 16;
 }
 
+// Segmented forward state pass: when even 16-row value slices leave compute units
+// idle (few heads) and the sequence is long, every head's chunk chain is cut into
+// segments whose affine maps are chained by a short scan, so about kSegUnits
+// (head, segment) pairs of state workgroups run at once.  Segments keep at least
+// kSegMinLen chunks.
+#ifndef CARVE_SEG_UNITS
+#define CARVE_SEG_UNITS 64
+#endif
+constexpr int kSegUnits = CARVE_SEG_UNITS;
+constexpr int kSegMinLen = 16;
+
+void seg_plan(Plan* p) {
+  p->nseg = 1;
+  p->seg_len = p->NC;
+  if (p->empty || (long long)p->BH * (p->D / 16) >= 256 || p->NC < 2 * kSegMinLen) return;
+  int want = (kSegUnits + p->BH - 1) / p->BH;
+  want = std::min(want, p->NC / kSegMinLen);
+  if (want < 2) return;
+  const int len = (p->NC + want - 1) / want;
+  const int nseg = (p->NC + len - 1) / len;
+  if (nseg < 2 || (long long)(nseg - 1) * len > p->NC - 1) return;
+  p->nseg = nseg;
+  p->seg_len = len;
+  p->VS = value_slice(p->BH * nseg, p->D);
+}
+
+// fp32 affine maps [C; Pi] and entering states of the segments
+size_t seg_bytes(const Plan& p) {
+  if (p.nseg <= 1) return 0;
+  return (size_t)p.BH * p.nseg * 3 * p.D * p.D * sizeof(float) + 512;
+}
+
 carve_status check_shape(const carve_shape* s, Plan* p) {
   if (!s) return CARVE_ERR_INVALID_ARG;
   if (s->B < 0 || s->H < 0 || s->T < 0 || s->L < 1) return CARVE_ERR_INVALID_ARG;
@@ -52,6 +86,8 @@ carve_status check_shape(const carve_shape* s, Plan* p) {
   p->NC = (s->T + p->LC - 1) / p->LC;
   p->VS = value_slice(p->BH, p->D);
   p->empty = (p->BH == 0 || s->T == 0);
+  p->nseg = 1;
+  p->seg_len = p->NC;
   return CARVE_OK;
 }
 
@@ -70,8 +106,22 @@ carve_status check_content(const carve_shape* s, const Plan& p, const carve_cont
 
 size_t fwd_ws(const carve_shape* s, const Plan& p, const carve_content* c) {
   if (p.empty) return 0;
-  const int slots = c ? 1 : p.NC;   // the content kernel reuses one factor slot per head
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, slots, p.LC, p.D, 1);
+  if (c) return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, 1, p.LC, p.D, 1);  // one slot per head
+  Plan ps = p;
+  seg_plan(&ps);
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 1) + seg_bytes(ps);
+}
+
+// carve the segment buffers after the forward factors (segmented pass only)
+void set_segments(carve::FwdArgs* a, const carve_shape* s, const Plan& p, void* workspace) {
+  if (p.nseg <= 1) return;
+  char* base = static_cast<char*>(workspace) + carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 1);
+  char* al = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(base) + 255) & ~uintptr_t(255));
+  a->nseg = p.nseg;
+  a->seg_len = p.seg_len;
+  a->VS = p.VS;
+  a->aff = reinterpret_cast<float*>(al);
+  a->S_seg = a->aff + (size_t)p.BH * p.nseg * 2 * p.D * p.D;
 }
 
 // one fragment-order copy of the D x D state for every chunk, in the operand type
@@ -198,6 +248,9 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
     mark(prof, 1, hs);
   } else {
     a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, 1);
+    Plan ps = p;
+    seg_plan(&ps);
+    set_segments(&a, s, ps, workspace);
     mark(prof, 0, hs);
     e = carve::launch_fwd_prep(a, hs);
     mark(prof, 1, hs);

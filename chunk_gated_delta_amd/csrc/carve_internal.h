@@ -59,6 +59,15 @@ struct FwdArgs {
   int logits;
   const float* gA;
   const float* gtau;
+  // Segmented state pass (long sequences with few heads; nseg <= 1: one pass from S0).
+  // The NC chunks of every head run as nseg segments of seg_len chunks.  The state
+  // step is affine in S, so segment s maps its entering state to S_in Pi_s + C_s;
+  // aff receives those maps for s = 0 .. nseg-2 as [(bh*nseg + s)][2D][D] fp32
+  // (rows 0..D-1 C_s, rows D..2D-1 Pi_s), S_seg the entering state of every
+  // segment as [(bh*nseg + s)][D][D] fp32 (S_in(0) = S0).
+  int nseg, seg_len;
+  float* aff;
+  float* S_seg;
 };
 
 struct ContentArgs {

@@ -110,7 +110,8 @@ struct ChunkOps {
   Frag<T> kf[SCT][KL];
   f32x4 gl[SCT];
 
-  __device__ __forceinline__ void load(const FwdArgs& a, size_t ci, int v0) {
+  // no_ub: the slice has no write term (Ubar = 0; the Pi rows of an affine map)
+  __device__ __forceinline__ void load(const FwdArgs& a, size_t ci, int v0, bool no_ub = false) {
     const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
     const T* Wn = reinterpret_cast<const T*>(a.f.Wn);
     const T* Qt = reinterpret_cast<const T*>(a.f.Qt);
@@ -128,7 +129,8 @@ struct ChunkOps {
 #pragma unroll
       for (int u = 0; u < UPW; ++u) {
         const int vt = (t0 + u) % NVT;
-        ub[u] = load_raw4(UbT + ci * LC * D + acc_offset<D>(rt, v0 / 16 + vt, lane));
+        if (no_ub) ub[u] = Raw4<T>{};
+        else ub[u] = load_raw4(UbT + ci * LC * D + acc_offset<D>(rt, v0 / 16 + vt, lane));
         if (HAS_O) oi[u] = load_raw4(OiT + ci * LC * D + acc_offset<D>(rt, v0 / 16 + vt, lane));
       }
     }
@@ -142,9 +144,10 @@ struct ChunkOps {
   }
 };
 
-// Load the state slice (S0 or zero) into registers and its dtype copy into LDS.
+// Load the state slice (rows v0 .. v0+VS-1 of the D x D matrix init, or zero when
+// init is null) into registers and its dtype copy into LDS.
 template <typename T, int D, int VS, int NW = kWaves>
-__device__ __forceinline__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTiles<D, VS, NW>::SPW], T* Sb) {
+__device__ __forceinline__ void state_init_from(const float* init, int v0, f32x4 (&S)[StateTiles<D, VS, NW>::SPW], T* Sb) {
   using ST = StateTiles<D, VS, NW>;
   constexpr int LDS_ = D + Pad<T>::v;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
@@ -152,10 +155,16 @@ __device__ __forceinline__ void state_init(const FwdArgs& a, int bh, int v0, f32
   for (int j = 0; j < ST::SPW; ++j) {
     const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
     const int vl = 16 * vt + lr, kc = 16 * ct + 4 * lg;
-    if (a.S0) S[j] = load4f(a.S0 + ((size_t)bh * D + v0 + vl) * D + kc);
+    if (init) S[j] = load4f(init + (size_t)(v0 + vl) * D + kc);
     else S[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     store4(Sb + vl * LDS_ + kc, S[j]);
   }
+}
+
+// The state slice from S0 (or zero).
+template <typename T, int D, int VS, int NW = kWaves>
+__device__ __forceinline__ void state_init(const FwdArgs& a, int bh, int v0, f32x4 (&S)[StateTiles<D, VS, NW>::SPW], T* Sb) {
+  state_init_from<T, D, VS, NW>(a.S0 ? a.S0 + (size_t)bh * D * D : nullptr, v0, S, Sb);
 }
 
 // One chunk of the state recurrence for a slice of VS value rows:
@@ -282,43 +291,165 @@ __device__ __forceinline__ void save_state(const FwdArgs& a, size_t ci, int v0, 
 // which then takes the loads of chunk c + 3, so every chunk's factors are in flight
 // for two whole chunk steps and a step never waits on loads issued in the same step.
 // Full chunks run in a branch-free main loop (prefetch indices are clamped, no token
-// checks); the last chunks run in a checked tail.
+// checks); the last chunks run in a checked tail.  With a segmented pass (nseg > 1)
+// the workgroup runs the chunks of one segment from that segment's entering state.
 template <typename T, int LC, int D, int VS, bool HAS_O, bool SAVE>
 __global__ __launch_bounds__(kThreads) void fwd_state_kernel(FwdArgs a) {
   using ST = StateTiles<D, VS>;
   using Op = ChunkOps<T, LC, D, VS, HAS_O>;
   constexpr int PF = 3;
   extern __shared__ __align__(16) unsigned char smem[];
-  int bh, slice;
-  xcd_slice_map(D / VS, a.B * a.H, bh, slice);
+  const int nseg = a.nseg > 1 ? a.nseg : 1;
+  int u, slice;
+  xcd_slice_map(D / VS, a.B * a.H * nseg, u, slice);
+  const int bh = u / nseg, seg = u % nseg;
   const int v0 = slice * VS;
+  const int cs = nseg > 1 ? seg * a.seg_len : 0;
+  const int ce = nseg > 1 ? min(a.NC, cs + a.seg_len) : a.NC;
   const size_t c0i = (size_t)bh * a.NC;
+  const float* init = nseg > 1 ? a.S_seg + (size_t)u * D * D : (a.S0 ? a.S0 + (size_t)bh * D * D : nullptr);
   f32x4 S[ST::SPW];
   Op buf[PF];
 #pragma unroll
-  for (int j = 0; j < PF; ++j) buf[j].load(a, c0i + min(j, a.NC - 1), v0);
-  state_init<T, D, VS>(a, bh, v0, S, reinterpret_cast<T*>(smem));
+  for (int j = 0; j < PF; ++j) buf[j].load(a, c0i + min(cs + j, ce - 1), v0);
+  state_init_from<T, D, VS>(init, v0, S, reinterpret_cast<T*>(smem));
   __syncthreads();
-  const int nfull = (a.T % LC == 0) ? a.NC : a.NC - 1;
+  const int nfull = min(ce, (a.T % LC == 0) ? a.NC : a.NC - 1) - cs;   // full chunks of the range
   const int nmain = nfull - nfull % PF;
-  for (int c0 = 0; c0 < nmain; c0 += PF) {
+  for (int l0 = 0; l0 < nmain; l0 += PF) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int c = c0 + j;
+      const int c = cs + l0 + j;
       if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S, reinterpret_cast<const T*>(smem));
       state_chunk<T, LC, D, VS, HAS_O, true>(a, bh, c, v0, buf[j], S, smem, nullptr);
-      buf[j].load(a, c0i + min(c + PF, a.NC - 1), v0);
+      buf[j].load(a, c0i + min(c + PF, ce - 1), v0);
     }
   }
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    const int c = nmain + j;
-    if (c < a.NC) {
+    const int c = cs + nmain + j;
+    if (c < ce) {
       if (SAVE) save_state<T, D, VS>(a, c0i + c, v0, S, reinterpret_cast<const T*>(smem));
       state_chunk<T, LC, D, VS, HAS_O, false>(a, bh, c, v0, buf[j], S, smem, nullptr);
     }
   }
-  if (a.S_T) state_store<T, D, VS>(a, bh, v0, S, a.S_T);
+  if (a.S_T && seg == nseg - 1) state_store<T, D, VS>(a, bh, v0, S, a.S_T);
+}
+
+// ------------------------------------------------------------------ segmented state pass
+// For long sequences with few heads the chunk chain of a head is cut into segments.
+// The state step is affine in S, so a segment maps its entering state to
+// S_out = S_in Pi + C: C is the pass over the segment from S_in = 0, and Pi, the
+// product of the chunk maps M_c = Diag(Gamma_L) - W^T K->, is the same pass with no
+// write term (Ubar = 0) started from the identity (its rows are indexed by key).
+// fwd_affine runs both at once as 2D state rows [C; Pi] per (head, segment) for every
+// segment but the last; seg_scan chains the maps (S_in(s+1) = S_in(s) Pi_s + C_s,
+// fp32); the state pass then runs every segment from its S_in, writing o.  This is
+// the chunk-level scan of the affine state maps behind the logarithmic parallel depth
+// the notes list for CARVE (complexity table), taken as two levels.
+template <typename T, int LC, int D, int VS>
+__global__ __launch_bounds__(kThreads) void fwd_affine_kernel(FwdArgs a) {
+  using ST = StateTiles<D, VS>;
+  using Op = ChunkOps<T, LC, D, VS, false>;
+  constexpr int PF = 3, LDS_ = D + Pad<T>::v;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int nsa = a.nseg - 1;                  // segments with a map: all but the last
+  int u, slice;
+  xcd_slice_map(2 * D / VS, a.B * a.H * nsa, u, slice);
+  const int bh = u / nsa, seg = u % nsa;
+  const int r0 = slice * VS;                   // first row of [C; Pi]
+  const bool pi = r0 >= D;
+  const int v0 = pi ? 0 : r0;                  // value rows of C (Pi rows load no Ubar)
+  const int cs = seg * a.seg_len, ce = cs + a.seg_len;   // whole chunks (only the last segment is ragged)
+  const size_t c0i = (size_t)bh * a.NC;
+  const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+  f32x4 S[ST::SPW];
+  Op buf[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) buf[j].load(a, c0i + min(cs + j, ce - 1), v0, pi);
+  T* Sb = reinterpret_cast<T*>(smem);
+#pragma unroll
+  for (int j = 0; j < ST::SPW; ++j) {
+    const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
+    const int row = r0 - D + 16 * vt + lr, kc = 16 * ct + 4 * lg;   // Pi row index (key) when pi
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[j][i] = (pi && kc + i == row) ? 1.f : 0.f;
+    store4(Sb + (16 * vt + lr) * LDS_ + kc, S[j]);
+  }
+  __syncthreads();
+  const int n = ce - cs, nmain = n - n % PF;
+  for (int l0 = 0; l0 < nmain; l0 += PF) {
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int c = cs + l0 + j;
+      state_chunk<T, LC, D, VS, false, true>(a, bh, c, v0, buf[j], S, smem, nullptr);
+      buf[j].load(a, c0i + min(c + PF, ce - 1), v0, pi);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int c = cs + nmain + j;
+    if (c < ce) state_chunk<T, LC, D, VS, false, true>(a, bh, c, v0, buf[j], S, smem, nullptr);
+  }
+  float* dst = a.aff + ((size_t)(bh * a.nseg + seg) * 2 * D + r0) * D;
+#pragma unroll
+  for (int j = 0; j < ST::SPW; ++j) {
+    const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
+    store4(dst + (size_t)(16 * vt + lr) * D + 16 * ct + 4 * lg, S[j]);
+  }
+}
+
+// S_in(0) = S0 (or 0), S_in(s+1) = S_in(s) Pi_s + C_s for s = 0 .. nseg-2, in fp32
+// with a fixed summation order.  Workgroup (16 rows of S, head): its rows depend only
+// on themselves, so they stay in LDS across the segments; Pi_s is staged in LDS 64
+// columns at a time, and thread (r, q) owns row r, columns 64 h + 4 q .. 64 h + 4 q + 3.
+template <int D>
+__global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
+  constexpr int LDR = D + 1, NH = D / 64;
+  __shared__ __align__(16) float Pi[D * 64];
+  __shared__ float Sr[16 * LDR];
+  const int bh = blockIdx.y, r0 = 16 * blockIdx.x;
+  const int tid = threadIdx.x, r = tid / 16, cq = 4 * (tid % 16);
+  f32x4 acc[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int col = 64 * h + cq;
+    acc[h] = a.S0 ? load4f(a.S0 + ((size_t)bh * D + r0 + r) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
+    store4(a.S_seg + ((size_t)bh * a.nseg * D + r0 + r) * D + col, acc[h]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Sr[r * LDR + col + i] = acc[h][i];
+  }
+  for (int s = 0; s + 1 < a.nseg; ++s) {
+    const float* map = a.aff + (size_t)(bh * a.nseg + s) * 2 * D * D;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) acc[h] = load4f(map + (size_t)(r0 + r) * D + 64 * h + cq);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      __syncthreads();                          // Sr complete, earlier reads of Pi done
+      for (int i = tid; i < D * 16; i += 256) {
+        const int j = i / 16, q4 = 4 * (i % 16);
+        store4(Pi + j * 64 + q4, load4f(map + (size_t)(D + j) * D + 64 * h + q4));
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int j = 0; j < D; ++j) {
+        const float sv = Sr[r * LDR + j];
+        const f32x4 p = load4f(Pi + j * 64 + cq);
+        acc[h][0] = fmaf(sv, p[0], acc[h][0]);
+        acc[h][1] = fmaf(sv, p[1], acc[h][1]);
+        acc[h][2] = fmaf(sv, p[2], acc[h][2]);
+        acc[h][3] = fmaf(sv, p[3], acc[h][3]);
+      }
+    }
+    __syncthreads();                            // every read of Sr(s) done
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int col = 64 * h + cq;
+      store4(a.S_seg + (((size_t)bh * a.nseg + s + 1) * D + r0 + r) * D + col, acc[h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Sr[r * LDR + col + i] = acc[h][i];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ content-aware forward
@@ -519,7 +650,16 @@ template <typename T, int LC, int D, int VS>
 static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = StateLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 64 * 1024, "state LDS exceeds 64 KB");
-  dim3 grid((D / VS) * a.B * a.H);
+  const int nseg = a.nseg > 1 ? a.nseg : 1;
+  if (nseg > 1) {
+    // every segment but the last holds seg_len whole chunks; the last is non-empty
+    if (a.seg_len < 1 || (long long)(nseg - 1) * a.seg_len > a.NC - 1 || !a.aff || !a.S_seg)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL((fwd_affine_kernel<T, LC, D, VS>), dim3((2 * D / VS) * a.B * a.H * (nseg - 1)),
+                       dim3(kThreads), Lay::bytes, st, a);
+    hipLaunchKernelGGL(seg_scan_kernel<D>, dim3(D / 16, a.B * a.H), dim3(256), 0, st, a);
+  }
+  dim3 grid((D / VS) * a.B * a.H * nseg);
   if (a.o && a.S_vk) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true, true>), grid, dim3(kThreads), Lay::bytes, st, a);
   else if (a.o) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true, false>), grid, dim3(kThreads), Lay::bytes, st, a);
   else if (a.S_vk) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, false, true>), grid, dim3(kThreads), Lay::bytes, st, a);

@@ -1,13 +1,14 @@
 """Drive the CARVE kernels for an external profiler (rocprofv3).
 
     python -m chunk_gated_delta_amd.profile_step [--steps 5] [--warmup 2]
-                                                  [--pass fwd+bwd|fwd|content|content_bwd|decode]
+                                                  [--pass fwd+bwd|fwd|long|content|content_bwd|decode]
                                                   [--copy-mib 0]
                                                   [--decode-batch 256]
 
 Runs the 1.3B-head-shape workload (B4 H16 T4096 d128 L64, bf16 q/k/v, fp32 gates;
 synthetic seeded inputs) through the same entry points as bench.py: the training step
-(fwd_save + bwd_saved), the plain forward, the content-aware forward or its backward, or recurrent decode
+(fwd_save + bwd_saved), the plain forward, the content-aware forward or its backward, the
+long-context forward (B1 H16 T32768, --pass long), or recurrent decode
 steps (one token per sequence and head at batch --decode-batch).  With
 --copy-mib N it also runs a plain elementwise kernel that reads N MiB and writes N MiB
 (torch.neg), the reference against which HBM byte counters are scaled.  Prints one
@@ -23,7 +24,7 @@ def main(argv=None):
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--pass", dest="passes", default="fwd+bwd",
-                   choices=["fwd+bwd", "fwd", "content", "content_bwd", "decode"])
+                   choices=["fwd+bwd", "fwd", "long", "content", "content_bwd", "decode"])
     p.add_argument("--decode-batch", type=int, default=256)
     p.add_argument("--copy-mib", type=int, default=0)
     args = p.parse_args(argv)
@@ -34,7 +35,8 @@ def main(argv=None):
     from chunk_gated_delta_amd.synth import WORKLOADS, make_inputs
 
     dev = torch.device("cuda:0")
-    wl = WORKLOADS["content_fwd" if args.passes in ("content", "content_bwd") else "head1p3b_fwd"]
+    wl = WORKLOADS["content_fwd" if args.passes in ("content", "content_bwd")
+                   else "long_ctx_fwd" if args.passes == "long" else "head1p3b_fwd"]
     if args.passes == "decode":
         return decode(args, wl, dev)
     inp = make_inputs(wl, with_dO=args.passes in ("fwd+bwd", "content_bwd"))
@@ -58,7 +60,7 @@ def main(argv=None):
         if args.passes == "fwd+bwd":
             o, _, saved = carve.fwd_save(q, k, v, log_g, w, b=b, L=wl.L)
             carve.bwd_saved(q, k, v, log_g, w, dO, saved, b=b, L=wl.L)
-        elif args.passes == "fwd":
+        elif args.passes in ("fwd", "long"):
             carve.fwd(q, k, v, log_g, w, b=b, L=wl.L)
         elif args.passes == "content_bwd":
             carve.bwd_content(q, k, v, log_g, w, dO, content, L=wl.L)

@@ -81,6 +81,21 @@ def test_fwd_workspace_checks(lib):
     assert call_fwd(lib, sb, q=None, k=None, v=None, log_g=None, w=None, o=None, ws=None, ws_bytes=0) == OK
 
 
+def test_segmented_forward_workspace(lib):
+    """Few heads and a long sequence: the forward workspace also holds the fp32 affine
+    maps [C; Pi] and entering states of the state-pass segments, so per head it is
+    larger than for a batch wide enough to run one sequential pass per head."""
+    T = 64 * 100
+    few, many = shape(B=1, H=2, T=T), shape(B=16, H=2, T=T)
+    per_head_few = lib.carve_fwd_workspace_size(ctypes.byref(few), None) / 2
+    per_head_many = lib.carve_fwd_workspace_size(ctypes.byref(many), None) / 32
+    assert per_head_few > per_head_many + 3 * 128 * 128 * 4       # at least one segment's buffers
+    # short sequences stay sequential (no segment buffers)
+    short_few, short_many = shape(B=1, H=2, T=64 * 8), shape(B=16, H=2, T=64 * 8)
+    assert abs(lib.carve_fwd_workspace_size(ctypes.byref(short_few), None) / 2 -
+               lib.carve_fwd_workspace_size(ctypes.byref(short_many), None) / 32) < 4096
+
+
 def test_fwd_content_checks(lib):
     c = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
     assert call_fwd(lib, shape(), b=FAKE, content=c) == INVALID               # b together with content

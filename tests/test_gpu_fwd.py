@@ -65,6 +65,47 @@ def test_fwd_parity(name, B, H, T, D, dtype, L, erase, dists):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+# Few heads and many chunks: the state pass runs as segments whose affine maps are
+# chained by a scan (B*H*Dk/16 < 256 compute units' worth of 16-row slices, at least
+# 32 chunks).  Ragged lengths put a partial chunk in the last segment.
+SEG_CASES = [
+    # name, B, H, T, D, dtype
+    ("seg_bf16_d128", 1, 2, 64 * 100 + 5, 128, "bf16"),
+    ("seg_f32_d64", 2, 1, 32 * 70 + 9, 64, "f32"),
+    ("seg_bf16_d64_exact", 1, 3, 64 * 48, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,B,H,T,D,dtype", SEG_CASES, ids=[c[0] for c in SEG_CASES])
+def test_segmented_state_pass_parity(name, B, H, T, D, dtype):
+    announce(f"segmented {name} T{T}")
+    inp = random_inputs(B, H, T, D, D, dtype=dtype, seed=zlib.crc32(name.encode()) % 1000, erase="sigmoid",
+                        dists="softplus_decay")
+    S0 = np.asarray(np.random.default_rng(6).standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64)
+    o, S_T, _ = run_gpu(inp, dtype, 64, S0=S0)
+    ro, rS, _ = run_ref(inp, 64, S0=S0)
+    eo, es = max_rel(o, ro), max_rel(S_T, rS)
+    print(f"  err o={eo:.2e} S_T={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_segmented_matches_sequential_pass():
+    """The same two heads run segmented (alone) and sequentially (inside a batch of
+    32 heads, which fills the compute units without segments) agree to rounding."""
+    announce("segmented vs sequential state pass")
+    D, T = 128, 64 * 64 + 30
+    inp = random_inputs(16, 2, T, D, D, dtype="bf16", seed=77, erase="sigmoid", dists="softplus_decay")
+    d = to_device(inp, "bf16")
+    o_all, S_all, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], L=64)
+    sub = {k_: v_[3:4].contiguous() for k_, v_ in d.items()}
+    o_one, S_one, _ = carve.fwd(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], b=sub["b"], L=64)
+    torch.cuda.synchronize()
+    eo = max_rel(to_np(o_one), to_np(o_all[3:4]))
+    es = max_rel(to_np(S_one), to_np(S_all[3:4]))
+    print(f"  diff o={eo:.2e} S_T={es:.2e}", flush=True)
+    assert eo <= 1e-2 and es <= 1e-2
+
+
 def test_tiny_f32_workload_zero_state():
     wl = WORKLOADS["tiny_f32"]
     announce(wl.name)
