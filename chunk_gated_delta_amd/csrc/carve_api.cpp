@@ -22,6 +22,7 @@ struct Plan {
   bool empty;  // no token to process
   int nseg;    // segments of the forward state pass (1: one sequential pass per head)
   int seg_len; // chunks per segment
+  int aff_vs;  // rows per workgroup of the segments' affine-map pass
 };
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -49,7 +50,11 @@ int value_slice(int BH, int D) {
 #ifndef CARVE_SEG_UNITS
 #define CARVE_SEG_UNITS 64
 #endif
+#ifndef CARVE_AFF_ROWS
+#define CARVE_AFF_ROWS 32
+#endif
 constexpr int kSegUnits = CARVE_SEG_UNITS;
+constexpr int kAffRows = CARVE_AFF_ROWS;   // rows of [C; Pi] per affine-pass workgroup
 constexpr int kSegMinLen = 16;
 
 void seg_plan(Plan* p) {
@@ -65,6 +70,7 @@ void seg_plan(Plan* p) {
   p->nseg = nseg;
   p->seg_len = len;
   p->VS = value_slice(p->BH * nseg, p->D);
+  p->aff_vs = std::min(kAffRows, p->D);
 }
 
 // fp32 affine maps [C; Pi] and entering states of the segments
@@ -119,6 +125,7 @@ void set_segments(carve::FwdArgs* a, const carve_shape* s, const Plan& p, void* 
   char* al = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(base) + 255) & ~uintptr_t(255));
   a->nseg = p.nseg;
   a->seg_len = p.seg_len;
+  a->aff_vs = p.aff_vs;
   a->VS = p.VS;
   a->aff = reinterpret_cast<float*>(al);
   a->S_seg = a->aff + (size_t)p.BH * p.nseg * 2 * p.D * p.D;

@@ -66,6 +66,7 @@ struct FwdArgs {
   // (rows 0..D-1 C_s, rows D..2D-1 Pi_s), S_seg the entering state of every
   // segment as [(bh*nseg + s)][D][D] fp32 (S_in(0) = S0).
   int nseg, seg_len;
+  int aff_vs;             // rows of [C; Pi] per workgroup of the affine-map pass (16, 32 or 64)
   float* aff;
   float* S_seg;
 };

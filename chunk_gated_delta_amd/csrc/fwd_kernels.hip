@@ -401,53 +401,82 @@ __global__ __launch_bounds__(kThreads) void fwd_affine_kernel(FwdArgs a) {
 
 // S_in(0) = S0 (or 0), S_in(s+1) = S_in(s) Pi_s + C_s for s = 0 .. nseg-2, in fp32
 // with a fixed summation order.  Workgroup (16 rows of S, head): its rows depend only
-// on themselves, so they stay in LDS across the segments; Pi_s is staged in LDS 64
-// columns at a time, and thread (r, q) owns row r, columns 64 h + 4 q .. 64 h + 4 q + 3.
+// on themselves, so they stay in LDS across the segments (transposed, [key][row]).
+// Pi_s is staged whole in LDS; the next segment's Pi and C rows are loaded into
+// registers while the current product runs.  Wave q owns rows 4q .. 4q+3, lane l
+// the columns CW l .. CW l + CW - 1 (CW = D / 64).
+template <int D>
+struct ScanLayout {
+  static constexpr size_t bytes = sizeof(float) * (D * D + D * 16);
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
-  constexpr int LDR = D + 1, NH = D / 64;
-  __shared__ __align__(16) float Pi[D * 64];
-  __shared__ float Sr[16 * LDR];
+  constexpr int CW = D / 64, NL = D * D / 4 / 256;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Pi = reinterpret_cast<float*>(smem);
+  float* SrT = Pi + D * D;
   const int bh = blockIdx.y, r0 = 16 * blockIdx.x;
-  const int tid = threadIdx.x, r = tid / 16, cq = 4 * (tid % 16);
-  f32x4 acc[NH];
+  const int tid = threadIdx.x, rq = tid / 64, c0 = CW * (tid % 64);
+  float acc[4][CW];
 #pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    const int col = 64 * h + cq;
-    acc[h] = a.S0 ? load4f(a.S0 + ((size_t)bh * D + r0 + r) * D + col) : f32x4{0.f, 0.f, 0.f, 0.f};
-    store4(a.S_seg + ((size_t)bh * a.nseg * D + r0 + r) * D + col, acc[h]);
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + 4 * rq + i;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Sr[r * LDR + col + i] = acc[h][i];
+    for (int c = 0; c < CW; ++c) {
+      const float x = a.S0 ? a.S0[((size_t)bh * D + row) * D + c0 + c] : 0.f;
+      acc[i][c] = x;
+      a.S_seg[((size_t)bh * a.nseg * D + row) * D + c0 + c] = x;
+      SrT[(c0 + c) * 16 + 4 * rq + i] = x;
+    }
   }
-  for (int s = 0; s + 1 < a.nseg; ++s) {
+  f32x4 pre[NL];
+  float cpre[4][CW];
+  auto fetch = [&](int s) {
     const float* map = a.aff + (size_t)(bh * a.nseg + s) * 2 * D * D;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) acc[h] = load4f(map + (size_t)(r0 + r) * D + 64 * h + cq);
+    for (int l = 0; l < NL; ++l) pre[l] = load4f(map + (size_t)D * D + 4 * (tid + 256 * l));
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      __syncthreads();                          // Sr complete, earlier reads of Pi done
-      for (int i = tid; i < D * 16; i += 256) {
-        const int j = i / 16, q4 = 4 * (i % 16);
-        store4(Pi + j * 64 + q4, load4f(map + (size_t)(D + j) * D + 64 * h + q4));
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < CW; ++c) cpre[i][c] = map[(size_t)(r0 + 4 * rq + i) * D + c0 + c];
+  };
+  if (a.nseg > 1) fetch(0);
+  for (int s = 0; s + 1 < a.nseg; ++s) {
+    // every read of the previous Pi and SrT finished before the barrier that ended the last step
+#pragma unroll
+    for (int l = 0; l < NL; ++l) store4(Pi + 4 * (tid + 256 * l), pre[l]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < CW; ++c) acc[i][c] = cpre[i][c];
+    __syncthreads();
+    if (s + 2 < a.nseg) fetch(s + 1);
+#pragma unroll 4
+    for (int j = 0; j < D; ++j) {
+      const f32x4 sv = load4f(SrT + j * 16 + 4 * rq);
+      float pv[CW];
+      if constexpr (CW == 2) {
+        const float2 p2 = *reinterpret_cast<const float2*>(Pi + j * D + c0);
+        pv[0] = p2.x;
+        pv[1] = p2.y;
+      } else {
+        pv[0] = Pi[j * D + c0];
       }
-      __syncthreads();
-#pragma unroll 8
-      for (int j = 0; j < D; ++j) {
-        const float sv = Sr[r * LDR + j];
-        const f32x4 p = load4f(Pi + j * 64 + cq);
-        acc[h][0] = fmaf(sv, p[0], acc[h][0]);
-        acc[h][1] = fmaf(sv, p[1], acc[h][1]);
-        acc[h][2] = fmaf(sv, p[2], acc[h][2]);
-        acc[h][3] = fmaf(sv, p[3], acc[h][3]);
-      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[i][c] = fmaf(sv[i], pv[c], acc[i][c]);
     }
-    __syncthreads();                            // every read of Sr(s) done
+    __syncthreads();                            // every read of Pi_s and SrT(s) done
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const int col = 64 * h + cq;
-      store4(a.S_seg + (((size_t)bh * a.nseg + s + 1) * D + r0 + r) * D + col, acc[h]);
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 4 * rq + i;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Sr[r * LDR + col + i] = acc[h][i];
+      for (int c = 0; c < CW; ++c) {
+        a.S_seg[(((size_t)bh * a.nseg + s + 1) * D + row) * D + c0 + c] = acc[i][c];
+        SrT[(c0 + c) * 16 + 4 * rq + i] = acc[i][c];
+      }
     }
   }
 }
@@ -647,6 +676,15 @@ static hipError_t prep_launch(const FwdArgs& a, hipStream_t st) {
 }
 
 template <typename T, int LC, int D, int VS>
+static hipError_t affine_launch(const FwdArgs& a, hipStream_t st) {
+  using Lay = StateLayout<T, LC, D, VS>;
+  static_assert(Lay::bytes <= 64 * 1024, "state LDS exceeds 64 KB");
+  hipLaunchKernelGGL((fwd_affine_kernel<T, LC, D, VS>), dim3((2 * D / VS) * a.B * a.H * (a.nseg - 1)),
+                     dim3(kThreads), Lay::bytes, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int LC, int D, int VS>
 static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
   using Lay = StateLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 64 * 1024, "state LDS exceeds 64 KB");
@@ -655,9 +693,19 @@ static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
     // every segment but the last holds seg_len whole chunks; the last is non-empty
     if (a.seg_len < 1 || (long long)(nseg - 1) * a.seg_len > a.NC - 1 || !a.aff || !a.S_seg)
       return hipErrorInvalidValue;
-    hipLaunchKernelGGL((fwd_affine_kernel<T, LC, D, VS>), dim3((2 * D / VS) * a.B * a.H * (nseg - 1)),
-                       dim3(kThreads), Lay::bytes, st, a);
-    hipLaunchKernelGGL(seg_scan_kernel<D>, dim3(D / 16, a.B * a.H), dim3(256), 0, st, a);
+    hipError_t e = hipSuccess;
+    switch (a.aff_vs) {
+      case 16: e = affine_launch<T, LC, D, 16>(a, st); break;
+      case 32: e = affine_launch<T, LC, D, 32>(a, st); break;
+      case 64: e = affine_launch<T, LC, D, 64>(a, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    auto scan = seg_scan_kernel<D>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)ScanLayout<D>::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scan, dim3(D / 16, a.B * a.H), dim3(256), ScanLayout<D>::bytes, st, a);
   }
   dim3 grid((D / VS) * a.B * a.H * nseg);
   if (a.o && a.S_vk) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true, true>), grid, dim3(kThreads), Lay::bytes, st, a);
