@@ -460,6 +460,9 @@ carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k
   a.gtau = gates->tau;
   a.mode = 1;
   a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, 1);
+  Plan ps = p;
+  seg_plan(&ps);
+  set_segments(&a, s, ps, workspace);
   hipError_t e = carve::launch_fwd_prep(a, hs);
   if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;

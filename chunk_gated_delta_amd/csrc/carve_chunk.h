@@ -367,6 +367,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   }
   {
     T kf[RP];
+    float kw[RP], vw[RP];
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
       const int r = r0 + i;
@@ -379,9 +380,15 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       Kp[r * LDD + ch] = to<T>(kv * gam);
       Km[r * LDD + ch] = to<T>(kv * inv);
       Qp[r * LDD + ch] = to<T>(qv * gam);
-      KwT[ch * LDL + r] = to<T>(wr * (kv * gam));
-      VwT[ch * LDL + r] = to<T>(wr * vv);
+      kw[i] = wr * (kv * gam);
+      vw[i] = wr * vv;
       kf[i] = to<T>(kv * (tot * inv));
+    }
+    // Kw^T and Vw^T rows (key channel ch) take this thread's RP consecutive tokens
+#pragma unroll
+    for (int t = 0; t < RP / 4; ++t) {
+      store4(KwT + ch * LDL + r0 + 4 * t, f32x4{kw[4 * t], kw[4 * t + 1], kw[4 * t + 2], kw[4 * t + 3]});
+      store4(VwT + ch * LDL + r0 + 4 * t, f32x4{vw[4 * t], vw[4 * t + 1], vw[4 * t + 2], vw[4 * t + 3]});
     }
     // K->^T in fragment order: this thread's tokens r0.. of key channel ch, 4 at a time
     static_assert(RP % 4 == 0, "token parts must hold whole groups of 4");
@@ -450,6 +457,35 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   __syncthreads();
 
   // ---- WY factors: W = T Kw, Ubar = T Vw  (Kw = diag(w) K+, Vw = diag(w) V)
+  if constexpr (NW == NCT) {
+    // one wave per key/value column tile: its columns of Kw and Vw are loaded once and
+    // every operand of the phase is in flight before the first product
+    constexpr int KL = LC / 32;
+    const int ct = wave, col = 16 * ct + lr;
+    Frag<T> bw[KL], bu[KL], ta[NB][KL];
+#pragma unroll
+    for (int kb = 0; kb < KL; ++kb) {
+      bw[kb] = load_frag(KwT + col * LDL + 32 * kb + 8 * lg);
+      bu[kb] = load_frag(VwT + col * LDL + 32 * kb + 8 * lg);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int kb = 0; kb <= i / 2; ++kb) ta[i][kb] = load_frag(Tb + (16 * i + lr) * LDL + 32 * kb + 8 * lg);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb <= i / 2; ++kb) {
+        mma(aw, ta[i][kb], bw[kb]);
+        mma(au, ta[i][kb], bu[kb]);
+      }
+      const int r = 16 * i + 4 * lg;
+      store4(WnT + col * LDL + r, -aw);
+      store4(UbTs + col * LDL + r, au);
+      store4(gUbT + acc_offset<D>(i, ct, lane), au);
+    }
+  } else
   for (int t = wave; t < 2 * NB * NCT; t += NW) {
     const bool isW = t < NB * NCT;
     const int tt = isW ? t : t - NB * NCT;
@@ -483,6 +519,37 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   }
 
   // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
+  if constexpr (NW == NCT) {
+    // one wave per column tile, as above: P's row blocks serve both products
+    constexpr int KL = LC / 32;
+    const int ct = wave, col = 16 * ct + lr;
+    Frag<T> bo[KL], bq[KL], pa[NB][KL];
+#pragma unroll
+    for (int kb = 0; kb < KL; ++kb) {
+      if (FWD) bo[kb] = load_frag(UbTs + col * LDL + 32 * kb + 8 * lg);
+      bq[kb] = load_frag(WnT + col * LDL + 32 * kb + 8 * lg);
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int kb = 0; kb <= i / 2; ++kb) pa[i][kb] = load_frag(Pb + (16 * i + lr) * LDL + 32 * kb + 8 * lg);
+    f32x4 aq[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) aq[i][ii] = tof(Qp[(16 * i + 4 * lg + ii) * LDD + col]);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      f32x4 ao = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb <= i / 2; ++kb) {
+        if (FWD) mma(ao, pa[i][kb], bo[kb]);
+        mma(aq[i], pa[i][kb], bq[kb]);
+      }
+      if (FWD) store4(gOiT + acc_offset<D>(i, ct, lane), ao);
+      store4(QtTs + col * LDL + 16 * i + 4 * lg, aq[i]);
+    }
+  } else
   for (int t = FWD ? wave : wave + NB * NCT; t < 2 * NB * NCT; t += NW) {
     const bool isO = t < NB * NCT;
     const int tt = isO ? t : t - NB * NCT;

@@ -81,6 +81,31 @@ def test_bwd_logits_parity(dtype, B, H, T, D, with_bx):
     assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
 
 
+def test_fwd_logits_segmented_long_memory():
+    """Few heads, many chunks: the gate pre-activation forward runs the segmented state
+    pass too.  Slow decay (A small, f + tau very negative) and a small write gate keep
+    the carried state alive across segments."""
+    announce("fwd logits segmented, long memory")
+    B, H, T, D = 1, 2, 64 * 80 + 3, 128
+    inp = logit_case(B, H, T, D, "bf16", seed=901, with_bx=False)
+    rng = np.random.default_rng(902)
+    inp["A"] = f32np(rng.uniform(0.001, 0.01, (H, D)))
+    inp["tau"] = f32np(np.full((H, D), -3.0))
+    inp["w_hat"] = f32np(rng.normal(-4.0, 0.5, (B, H, T)))
+    d = to_device(inp, "bf16")
+    o, S_T = carve.fwd_logits(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]),
+                              dev(inp["w_hat"]), S0=dev(inp["S0"]))
+    torch.cuda.synchronize()
+    ro, rS = oracle.forward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"],
+                                   S0=inp["S0"])
+    ro0, _ = oracle.forward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"])
+    carried = max_rel(ro0[:, :, -64:], ro[:, :, -64:])
+    eo, es = max_rel(to_np(o), ro), max_rel(to_np(S_T), rS)
+    print(f"  err o={eo:.2e} S_T={es:.2e}; S0's share of the last chunk's outputs {carried:.2e}", flush=True)
+    assert carried > 0.1
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_logits_match_activated_gates():
     """The fused activation agrees with passing the activated gates (computed in
     float32 on the device) to the plain entry points, within the bf16 bar."""
