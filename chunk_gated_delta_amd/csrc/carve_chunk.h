@@ -23,8 +23,7 @@ struct PrepLayout {
   static constexpr int LDD = D + Pad<T>::v;      // [LC][D] row stride (elements)
   static constexpr int LDL = LC + Pad<T>::v;     // [D][LC] and [LC][LC] row stride
   static constexpr int LDF = LC + 4;             // fp32 [LC][LC] row stride
-  static constexpr int P = NT / D;               // token parts per key channel in the gate pass
-  static constexpr int RP = LC / P;              // tokens per part
+  static constexpr int P = NT / D;               // token parts per key channel (one channel a thread)
   static constexpr size_t szLD = sizeof(T) * LC * LDD;
   static constexpr size_t szDL = sizeof(T) * D * LDL;
   static constexpr size_t szLLf = sizeof(float) * LC * LDF;
@@ -39,8 +38,8 @@ struct PrepLayout {
   static constexpr size_t R4 = R3 + al(2 * szDL);         // A (fp32), then (-W)^T
   static constexpr size_t R5 = R4 + al(cmax(szLLf, szDL)); // P (dtype)
   static constexpr size_t R6 = R5 + al(szLL);             // Ubar^T
-  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [P][D]
-  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + P * D));
+  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [<= 2P][D]
+  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + 2 * P * D));   // up to 2P parts
 };
 
 // ------------------------------------------------------------------ global layouts
@@ -57,6 +56,46 @@ __device__ __forceinline__ size_t frag_offset(int rt, int kb, int lane) {
 template <int W>
 __device__ __forceinline__ size_t acc_offset(int rt, int ct, int lane) {
   return ((size_t)(rt * (W / 16) + ct) * 64 + lane) * 4;
+}
+
+// CPT (1 or 2) adjacent elements of a row in LDS, as floats (loads) or rounded to T
+// (stores; st_row with a column index stores x[c][i]).
+template <typename T, int CPT>
+__device__ __forceinline__ void ld_row(const T* p, float (&x)[CPT]) {
+  if constexpr (CPT == 2) {
+    if constexpr (sizeof(T) == 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 v = *reinterpret_cast<const bf16x2*>(p);
+      x[0] = (float)v[0];
+      x[1] = (float)v[1];
+    } else {
+      const f32x2 v = *reinterpret_cast<const f32x2*>(p);
+      x[0] = v[0];
+      x[1] = v[1];
+    }
+  } else {
+    x[0] = tof(p[0]);
+  }
+}
+template <typename T, int CPT>
+__device__ __forceinline__ void st_row(T* p, const float (&x)[CPT]) {
+  if constexpr (CPT == 2) {
+    if constexpr (sizeof(T) == 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<bf16x2*>(p) = bf16x2{to<bf16>(x[0]), to<bf16>(x[1])};
+    } else {
+      *reinterpret_cast<f32x2*>(p) = f32x2{x[0], x[1]};
+    }
+  } else {
+    p[0] = to<T>(x[0]);
+  }
+}
+template <typename T, int CPT, int N>
+__device__ __forceinline__ void st_row(T* p, const float (&x)[CPT][N], int i) {
+  float y[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) y[c] = x[c][i];
+  st_row<T, CPT>(p, y);
 }
 
 // lower-triangular block index -> (i, j), j <= i
@@ -309,7 +348,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   using Lay = PrepLayout<T, LC, D, NT>;
   constexpr int NW = NT / 64;
   constexpr int NB = LC / 16, NCT = D / 16;
-  constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF, P = Lay::P, RP = Lay::RP;
+  constexpr int LDD = Lay::LDD, LDL = Lay::LDL, LDF = Lay::LDF, P = Lay::P;
   T* Kp = reinterpret_cast<T*>(smem + Lay::R1);
   T* Km = Kp + LC * LDD;
   float* Tf = reinterpret_cast<float*>(smem + Lay::R1);
@@ -342,67 +381,90 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   T* gQtT = BWD ? reinterpret_cast<T*>(a.f.QtT) + ci * D * LC : nullptr;
   T* gKf = BWD ? reinterpret_cast<T*>(a.f.Kf) + ci * LC * D : nullptr;
 
-  // ---- gate pass: cumulative key-axis retention Gamma (thread = key channel x token part)
-  // over the staged retention a (1 past the end); raw k, q, v are read from their slots.
-  const int ch = tid % D, pid = tid / D, r0 = pid * RP;
+  // ---- gate pass: cumulative key-axis retention Gamma over the staged retention a
+  // (1 past the end); raw k, q, v are read from their slots.  With at least four
+  // tokens per part, a thread takes two adjacent key channels so that every row-major
+  // LDS access moves both; otherwise one channel.
   const float* aS = reinterpret_cast<const float*>(smem + Lay::R3);
   const T* Vraw = reinterpret_cast<const T*>(smem + Lay::R6);
-  float G[RP];
+  constexpr int CPT = (LC * D / (2 * NT)) % 4 == 0 && LC * D / (2 * NT) >= 4 ? 2 : 1;
+  constexpr int PG = CPT * NT / D, RG = LC / PG;   // token parts, tokens per part
+  static_assert(RG % 4 == 0 && PG * D <= 2 * P * D, "token parts must hold whole groups of 4");
+  const int ch = CPT * (tid % (D / CPT)), pid = tid / (D / CPT), r0 = pid * RG;
+  float G[CPT][RG];
   {
-    float run = 1.f;
+    float run[CPT];
 #pragma unroll
-    for (int i = 0; i < RP; ++i) {
-      run *= aS[(r0 + i) * D + ch];
-      G[i] = run;
+    for (int c = 0; c < CPT; ++c) run[c] = 1.f;
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const float* ar = aS + (r0 + i) * D + ch;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        run[c] *= ar[c];
+        G[c][i] = run[c];
+      }
     }
-    part[pid * D + ch] = run;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) part[pid * D + ch + c] = run[c];
   }
   __syncthreads();
-  float pre = 1.f, tot = 1.f;
+  float pre[CPT], tot[CPT];
 #pragma unroll
-  for (int pp = 0; pp < P; ++pp) {
-    const float pt = part[pp * D + ch];
-    if (pp < pid) pre *= pt;
-    tot *= pt;
+  for (int c = 0; c < CPT; ++c) pre[c] = tot[c] = 1.f;
+#pragma unroll
+  for (int pp = 0; pp < PG; ++pp) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const float pt = part[pp * D + ch + c];
+      if (pp < pid) pre[c] *= pt;
+      tot[c] *= pt;
+    }
   }
   {
-    T kf[RP];
-    float kw[RP], vw[RP];
+    float kf[CPT][RG], kw[CPT][RG], vw[CPT][RG];
 #pragma unroll
-    for (int i = 0; i < RP; ++i) {
+    for (int i = 0; i < RG; ++i) {
       const int r = r0 + i;
-      const float gam = pre * G[i];
-      const float inv = 1.f / gam;
-      const float kv = tof(Kp[r * LDD + ch]);      // staged raw, 0 past the end
-      const float qv = tof(Qp[r * LDD + ch]);
-      const float vv = tof(Vraw[r * LDD + ch]);
+      float kv[CPT], qv[CPT], vv[CPT], gam[CPT], inv[CPT], kp[CPT], km[CPT], qp[CPT];
+      ld_row<T, CPT>(Kp + r * LDD + ch, kv);       // staged raw, 0 past the end
+      ld_row<T, CPT>(Qp + r * LDD + ch, qv);
+      ld_row<T, CPT>(Vraw + r * LDD + ch, vv);
       const float wr = wL[r];
-      Kp[r * LDD + ch] = to<T>(kv * gam);
-      Km[r * LDD + ch] = to<T>(kv * inv);
-      Qp[r * LDD + ch] = to<T>(qv * gam);
-      kw[i] = wr * (kv * gam);
-      vw[i] = wr * vv;
-      kf[i] = to<T>(kv * (tot * inv));
-    }
-    // Kw^T and Vw^T rows (key channel ch) take this thread's RP consecutive tokens
 #pragma unroll
-    for (int t = 0; t < RP / 4; ++t) {
-      store4(KwT + ch * LDL + r0 + 4 * t, f32x4{kw[4 * t], kw[4 * t + 1], kw[4 * t + 2], kw[4 * t + 3]});
-      store4(VwT + ch * LDL + r0 + 4 * t, f32x4{vw[4 * t], vw[4 * t + 1], vw[4 * t + 2], vw[4 * t + 3]});
+      for (int c = 0; c < CPT; ++c) {
+        gam[c] = pre[c] * G[c][i];
+        inv[c] = 1.f / gam[c];
+        kp[c] = kv[c] * gam[c];
+        km[c] = kv[c] * inv[c];
+        qp[c] = qv[c] * gam[c];
+        kw[c][i] = wr * kp[c];
+        vw[c][i] = wr * vv[c];
+        kf[c][i] = kv[c] * (tot[c] * inv[c]);
+      }
+      st_row<T, CPT>(Kp + r * LDD + ch, kp);
+      st_row<T, CPT>(Km + r * LDD + ch, km);
+      st_row<T, CPT>(Qp + r * LDD + ch, qp);
+      if (BWD) st_row<T, CPT>(KfL + r * LDD + ch, kf, i);
     }
-    // K->^T in fragment order: this thread's tokens r0.. of key channel ch, 4 at a time
-    static_assert(RP % 4 == 0, "token parts must hold whole groups of 4");
 #pragma unroll
-    for (int t = 0; t < RP / 4; ++t) {
-      const int r = r0 + 4 * t;
-      T* dst = gKfT + frag_offset<LC>(ch / 16, r / 32, ch % 16 + 16 * ((r % 32) / 8)) + r % 8;
-      store4(dst, f32x4{tof(kf[4 * t]), tof(kf[4 * t + 1]), tof(kf[4 * t + 2]), tof(kf[4 * t + 3])});
-    }
-    if (BWD) {
+    for (int c = 0; c < CPT; ++c) {
+      // Kw^T and Vw^T rows (key channel ch + c) take this thread's RG consecutive tokens
 #pragma unroll
-      for (int i = 0; i < RP; ++i) KfL[(r0 + i) * LDD + ch] = kf[i];
+      for (int t = 0; t < RG / 4; ++t) {
+        store4(KwT + (ch + c) * LDL + r0 + 4 * t, f32x4{kw[c][4 * t], kw[c][4 * t + 1], kw[c][4 * t + 2], kw[c][4 * t + 3]});
+        store4(VwT + (ch + c) * LDL + r0 + 4 * t, f32x4{vw[c][4 * t], vw[c][4 * t + 1], vw[c][4 * t + 2], vw[c][4 * t + 3]});
+      }
+      // K->^T in fragment order, 4 tokens at a time (rounded to the operand type)
+      const int cc = ch + c;
+#pragma unroll
+      for (int t = 0; t < RG / 4; ++t) {
+        const int r = r0 + 4 * t;
+        T* dst = gKfT + frag_offset<LC>(cc / 16, r / 32, cc % 16 + 16 * ((r % 32) / 8)) + r % 8;
+        store4(dst, f32x4{kf[c][4 * t], kf[c][4 * t + 1], kf[c][4 * t + 2], kf[c][4 * t + 3]});
+      }
+      if (pid == 0) a.f.gL[ci * D + cc] = tot[c];
     }
-    if (pid == 0) a.f.gL[ci * D + ch] = tot;
   }
   __syncthreads();
   if (BWD) {
@@ -415,30 +477,45 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   }
 
   // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
-  constexpr int NTRI = NB * (NB + 1) / 2;
-  for (int t = wave; t < 2 * NTRI; t += NW) {
-    const bool isA = t < NTRI;
-    int i, j;
-    tri_index(isA ? t : t - NTRI, i, j);
-    const T* Ar = isA ? Kp : Qp;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // Wave w takes tiles w, w + NW, ... (A tiles first, then P); all of its operand
+  // fragments are loaded before its first product (a wave past the last tile reloads
+  // that tile and skips the product).
+  constexpr int NTRI = NB * (NB + 1) / 2, NTILE = 2 * NTRI, TPW = (NTILE + NW - 1) / NW, KD = D / 32;
+  {
+    Frag<T> fa[TPW][KD], fb[TPW][KD];
+    int ti[TPW], tj[TPW];
 #pragma unroll
-    for (int kk = 0; kk < D; kk += 32) {
-      const Frag<T> fa = load_frag(Ar + (16 * i + lr) * LDD + kk + 8 * lg);
-      const Frag<T> fb = load_frag(Km + (16 * j + lr) * LDD + kk + 8 * lg);
-      mma(acc, fa, fb);
+    for (int m = 0; m < TPW; ++m) {
+      const int t = min(wave + NW * m, NTILE - 1);
+      tri_index(t < NTRI ? t : t - NTRI, ti[m], tj[m]);
+      const T* Ar = t < NTRI ? Kp : Qp;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        fa[m][kk] = load_frag(Ar + (16 * ti[m] + lr) * LDD + 32 * kk + 8 * lg);
+        fb[m][kk] = load_frag(Km + (16 * tj[m] + lr) * LDD + 32 * kk + 8 * lg);
+      }
     }
-    const int s = 16 * j + lr;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 16 * i + 4 * lg + ii;
-      if (isA) {
-        Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
-      } else {
-        Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
-        // the products with P run over 32-token blocks: block (i, i+1) of an even row
-        // tile i is read by them and must be zero
-        if (j == i && i % 2 == 0 && i + 1 < NB) Pb[r * LDL + s + 16] = to<T>(0.f);
+    for (int m = 0; m < TPW; ++m) {
+      const int t = wave + NW * m;
+      if (t >= NTILE) continue;
+      const bool isA = t < NTRI;
+      const int i = ti[m], j = tj[m];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) mma(acc, fa[m][kk], fb[m][kk]);
+      const int s = 16 * j + lr;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 16 * i + 4 * lg + ii;
+        if (isA) {
+          Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
+        } else {
+          Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
+          // the products with P run over 32-token blocks: block (i, i+1) of an even row
+          // tile i is read by them and must be zero
+          if (j == i && i % 2 == 0 && i + 1 < NB) Pb[r * LDL + s + 16] = to<T>(0.f);
+        }
       }
     }
   }
