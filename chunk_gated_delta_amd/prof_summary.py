@@ -1,6 +1,7 @@
 """Turn rocprofv3 CSV output into the short text summaries kept with the project.
 
-    python -m chunk_gated_delta_amd.prof_summary stats KERNEL_STATS_CSV --title T --command C [--bench-json J] --out F
+    python -m chunk_gated_delta_amd.prof_summary stats KERNEL_STATS_CSV --title T --command C [--bench-json J]
+                                                   [--trace KERNEL_TRACE_CSV] --out F
     python -m chunk_gated_delta_amd.prof_summary traffic FETCH_CSV WRITE_CSV --copy-mib N --title T
                                                    --command-fetch C1 --command-write C2 --out F
 
@@ -22,7 +23,10 @@ TRAFFIC_TAG = "<!-- hbm-traffic: "
 
 def short_name(mangled):
     for key in ("bwd_chunk_kernel", "bwd_state_kernel", "fwd_prep_kernel", "fwd_state_kernel",
-                "fwd_content_kernel", "copy_or_zero_kernel"):
+                "fwd_content_kernel", "fwd_affine_kernel", "seg_scan_kernel", "decode_kernel",
+                "content_gate_bwd_kernel", "content_gates_kernel", "add_grad_mean_kernel",
+                "init_grad_mean_kernel", "sum_over_batch_kernel", "logit_grads_kernel", "sum_heads_kernel",
+                "copy_or_zero_kernel"):
         if key in mangled:
             return key
     return mangled[:48]
@@ -37,6 +41,23 @@ def stats(args):
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         out.append(f"| {short_name(r['Name'])} | `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                    f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {100 * float(r['TotalDurationNs']) / total:.1f} |")
+    if args.trace:
+        # the same kernel can run at several launch shapes (the training step's chunk-gradient
+        # launch covers every chunk, the content-aware backward's one chunk per head): split
+        # the trace by (kernel, grid) so each shape's average stands on its own
+        groups = {}
+        for r in csv.DictReader(open(args.trace)):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Workgroup_Size_X"]))
+            groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        gtot = sum(sum(v) for v in groups.values())
+        out += ["", "Per launch shape (the same run's kernel trace; workgroups = grid / workgroup size):", "",
+                "| kernel | workgroups (x, y) | threads | calls | average us | min us | max us | share % |",
+                "|---|---|---|---|---|---|---|---|"]
+        for (name, gx, gy, wx), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            if 100 * sum(d) / gtot < 0.1:
+                continue
+            out.append(f"| {short_name(name)} | ({gx // max(wx, 1)}, {gy}) | {wx} | {len(d)} | "
+                       f"{statistics.mean(d):.1f} | {min(d):.1f} | {max(d):.1f} | {100 * sum(d) / gtot:.1f} |")
     if args.bench_json:
         line = [ln for ln in open(args.bench_json) if ln.startswith("{")][-1]
         b = json.loads(line)
@@ -109,6 +130,7 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--bench-json")
+    s.add_argument("--trace", help="kernel trace CSV of the same run: adds per-launch-shape statistics")
     s.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv")
