@@ -260,18 +260,29 @@ def main():
             dev).view(torch.bfloat16)
         ws_cb = torch.empty(carve.bwd_content_workspace_bytes(cq, cv, wc.L, R=cf["U1"].shape[1]), dtype=torch.uint8,
                             device=dev)
-        for _ in range(2):
-            carve.bwd_content(cq, ck, cv, cf["log_g"], cf["w"], cdo, cont, L=wc.L, workspace=ws_cb)
-        torch.cuda.synchronize()
-        ce0.record()
-        for _ in range(3):
-            carve.bwd_content(cq, ck, cv, cf["log_g"], cf["w"], cdo, cont, L=wc.L, workspace=ws_cb)
-        ce1.record()
-        torch.cuda.synchronize()
-        cbms = ce0.elapsed_time(ce1) / 3
+        # as in training: the forward records each period's signal and mean, the backward reads
+        # them; the backward that re-runs the content-aware forward instead is timed beside it
+        zr, mr = carve.content_records(wc.B, wc.H, wc.T, wc.Dk, wc.Dv, wc.L, dev)
+        carve.fwd(cq, ck, cv, cf["log_g"], cf["w"], L=wc.L, content=dict(cont, z_rec=zr, m_rec=mr), o=co,
+                  workspace=ws_c)
+        crec = dict(cont, z_rec=zr, m_rec=mr)
+
+        def time_bwd(c_):
+            for _ in range(2):
+                carve.bwd_content(cq, ck, cv, cf["log_g"], cf["w"], cdo, c_, L=wc.L, workspace=ws_cb)
+            torch.cuda.synchronize()
+            ce0.record()
+            for _ in range(3):
+                carve.bwd_content(cq, ck, cv, cf["log_g"], cf["w"], cdo, c_, L=wc.L, workspace=ws_cb)
+            ce1.record()
+            torch.cuda.synchronize()
+            return ce0.elapsed_time(ce1) / 3
+
+        cbms = time_bwd(crec)
         extra["content_bwd_ms"] = round(cbms, 4)
         extra["content_bwd_tokens_per_s"] = wc.B * wc.T / (cbms * 1e-3)
-        del cq, ck, cv, cf, cont, ws_c, co, cdo, ws_cb
+        extra["content_bwd_recompute_ms"] = round(time_bwd(cont), 4)
+        del cq, ck, cv, cf, cont, crec, zr, mr, ws_c, co, cdo, ws_cb
 
     # gates given as pre-activations (activated inside the kernels), same shape; the plain
     # backward that recomputes the forward is timed beside it

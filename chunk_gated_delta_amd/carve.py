@@ -26,7 +26,30 @@ class carve_shape(ctypes.Structure):
 
 class carve_content(ctypes.Structure):
     _fields_ = [("b_x", ctypes.c_void_p), ("U1", ctypes.c_void_p), ("U2", ctypes.c_void_p),
-                ("R", ctypes.c_int), ("m0", ctypes.c_void_p), ("m_out", ctypes.c_void_p)]
+                ("R", ctypes.c_int), ("m0", ctypes.c_void_p), ("m_out", ctypes.c_void_p),
+                ("z_rec", ctypes.c_void_p), ("m_rec", ctypes.c_void_p)]
+
+
+def content_records(B, H, T, Dk, Dv, L, device):
+    """Per-period record buffers (z_rec [B,H,P,Dk], m_rec [B,H,P,Dv], P = ceil(T / L)) for the
+    content dict of fwd (which fills them) and bwd_content (which then skips re-running the
+    content-aware forward)."""
+    P = (T + L - 1) // L
+    return (torch.empty((B, H, P, Dk), dtype=torch.float32, device=device),
+            torch.empty((B, H, P, Dv), dtype=torch.float32, device=device))
+
+
+def _records(content, B, H, T, Dk, Dv, L, dev):
+    """Pointers of the content dict's record tensors (both or neither)."""
+    zr, mr = content.get("z_rec"), content.get("m_rec")
+    if (zr is None) != (mr is None):
+        raise ValueError("z_rec and m_rec are given together")
+    if zr is None:
+        return None, None
+    P = (T + L - 1) // L
+    _check(zr, "z_rec", (B, H, P, Dk), torch.float32, dev)
+    _check(mr, "m_rec", (B, H, P, Dv), torch.float32, dev)
+    return zr.data_ptr(), mr.data_ptr()
 
 
 class carve_gate_logits(ctypes.Structure):
@@ -168,7 +191,8 @@ def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None
 
     q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, one dtype); log_g, b [B,H,T,Dk]
     float32; w [B,H,T] float32; S0 [B,H,Dv,Dk] float32 or None.  content is None or a dict
-    with b_x [B,H,T,Dk], U1 [H,R,Dv] / U2 [H,Dk,R] (or None), m0 [B,H,Dv] (or None).
+    with b_x [B,H,T,Dk], U1 [H,R,Dv] / U2 [H,Dk,R] (or None), m0 [B,H,Dv] (or None), and
+    optionally z_rec / m_rec (content_records), which the forward fills.
     Outputs may be passed preallocated (o, S_T, workspace)."""
     lib = load_library()
     B, H, T, Dk = q.shape
@@ -198,9 +222,10 @@ def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None
             _check(U2, "U2", (H, Dk, R), torch.float32, dev)
         _check(m0, "m0", (B, H, Dv), torch.float32, dev)
         m_out = torch.empty((B, H, Dv), dtype=torch.float32, device=dev)
+        zr, mr = _records(content, B, H, T, Dk, Dv, L, dev)
         cs = carve_content(bx.data_ptr(), None if U1 is None else U1.data_ptr(),
                            None if U2 is None else U2.data_ptr(), R,
-                           None if m0 is None else m0.data_ptr(), m_out.data_ptr())
+                           None if m0 is None else m0.data_ptr(), m_out.data_ptr(), zr, mr)
         keep.append(cs)
     if o is None:
         o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
@@ -389,11 +414,13 @@ def bwd_logits(q, k, v, f, A, tau, w_hat, dO, b_x=None, S0=None, dS_T=None, L=64
     return out
 
 
-def bwd_content_workspace_bytes(q, v, L=64, R=0):
-    """Workspace bytes of bwd_content for this shape (R: projection rank, 0 = none)."""
+def bwd_content_workspace_bytes(q, v, L=64, R=0, records=False):
+    """Workspace bytes of bwd_content for this shape (R: projection rank, 0 = none;
+    records: the forward's per-period records are passed, so it is not re-run)."""
     lib = load_library()
     s = make_shape(q, v, L)
-    c = carve_content(None, 1 if R else None, 1 if R else None, R, None, None)
+    c = carve_content(None, 1 if R else None, 1 if R else None, R, None, None,
+                      16 if records else None, 16 if records else None)
     return lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(c))
 
 
@@ -401,7 +428,9 @@ def bwd_content(q, k, v, log_g, w, dO, content, S0=None, dS_T=None, dm_out=None,
                 want_dm0=True, workspace=None):
     """Gradients of the content-aware forward: dict with dq, dk, dv, dlog_g, db_x, dw,
     dU1 / dU2 (None without projection), dm0 and dS0 (None unless asked for).
-    content: dict with b_x, U1, U2 (or None) and m0 (or None), as for fwd()."""
+    content: dict with b_x, U1, U2 (or None) and m0 (or None), as for fwd(), and optionally
+    the records z_rec / m_rec that fwd() filled for the same inputs (then the content-aware
+    forward is not run again)."""
     lib = load_library()
     B, H, T, Dk = q.shape
     Dv = v.shape[-1]
@@ -423,8 +452,9 @@ def bwd_content(q, k, v, log_g, w, dO, content, S0=None, dS_T=None, dm_out=None,
         _check(U1, "U1", (H, R, Dv), torch.float32, dev)
         _check(U2, "U2", (H, Dk, R), torch.float32, dev)
     _check(m0, "m0", (B, H, Dv), torch.float32, dev)
+    zr, mr = _records(content, B, H, T, Dk, Dv, L, dev)
     cs = carve_content(bx.data_ptr(), None if U1 is None else U1.data_ptr(), None if U2 is None else U2.data_ptr(),
-                       R, None if m0 is None else m0.data_ptr(), None)
+                       R, None if m0 is None else m0.data_ptr(), None, zr, mr)
     s = make_shape(q, v, L)
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
          "dlog_g": torch.empty_like(log_g), "db_x": torch.empty_like(bx), "dw": torch.empty_like(w),

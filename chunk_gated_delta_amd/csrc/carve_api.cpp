@@ -104,8 +104,9 @@ carve_status check_content(const carve_shape* s, const Plan& p, const carve_cont
   if (c->U1 && (c->R < 1 || c->R > 64)) return CARVE_ERR_INVALID_ARG;
   if (s->L % p.LC != 0) return CARVE_ERR_UNSUPPORTED;        // content period must be whole tiles
   if (!p.empty && !c->b_x) return CARVE_ERR_INVALID_ARG;
+  if ((c->z_rec == nullptr) != (c->m_rec == nullptr)) return CARVE_ERR_INVALID_ARG;   // records come in pairs
   for (const void* q : {(const void*)c->b_x, (const void*)c->U1, (const void*)c->U2, (const void*)c->m0,
-                        (const void*)c->m_out})
+                        (const void*)c->m_out, (const void*)c->z_rec, (const void*)c->m_rec})
     if (q && !aligned16(q)) return CARVE_ERR_INVALID_ARG;
   return CARVE_OK;
 }
@@ -250,6 +251,8 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
     cg.m0 = content->m0;
     cg.m_out = content->m_out;
     cg.period = s->L;
+    cg.z_all = content->z_rec;      // per-period records (may be null)
+    cg.m_all = content->m_rec;
     mark(prof, 0, hs);
     e = carve::launch_fwd_content(a, cg, hs);
     mark(prof, 1, hs);
@@ -555,10 +558,12 @@ ContentBwdLayout content_bwd_layout(const carve_shape* s, const Plan& p, const c
   ContentBwdLayout L;
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t at = off; off += al(bytes); return at; };
-  L.fwd = take(fwd_ws(s, p, c));
-  L.o = take((size_t)p.BH * s->T * s->Dv * es);
-  L.z = take((size_t)p.BH * NP * p.D * 4);
-  L.m = take((size_t)p.BH * NP * p.D * 4);
+  // with the forward's records the content-aware forward is not re-run: no room for it
+  const bool rec = c && c->z_rec && c->m_rec;
+  L.fwd = take(rec ? 0 : fwd_ws(s, p, c));
+  L.o = take(rec ? 0 : (size_t)p.BH * s->T * s->Dv * es);
+  L.z = take(rec ? 0 : (size_t)p.BH * NP * p.D * 4);
+  L.m = take(rec ? 0 : (size_t)p.BH * NP * p.D * 4);
   L.bmat = take((size_t)p.BH * s->T * p.D * 4);
   L.bwd = take(bwd_ws(s, p));
   L.dOp = take((size_t)p.BH * s->T * s->Dv * es);
@@ -613,24 +618,29 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
     return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
   }
   char* ws = align_up(workspace);
-  float* z_all = reinterpret_cast<float*>(ws + Lw.z);
-  float* m_all = reinterpret_cast<float*>(ws + Lw.m);
+  const bool rec = content->z_rec && content->m_rec;
+  const float* z_all = rec ? content->z_rec : reinterpret_cast<float*>(ws + Lw.z);
+  const float* m_all = rec ? content->m_rec : reinterpret_cast<float*>(ws + Lw.m);
   float* bmat = reinterpret_cast<float*>(ws + Lw.bmat);
 
-  // 1. the content forward again, recording each period's z and the mean it used
-  carve::FwdArgs fa = fwd_args(s, p, q, k, v, log_g, nullptr, w, S0, ws + Lw.o, nullptr);
-  fa.mode = 1;
-  fa.f = carve::carve_factors(ws + Lw.fwd, fa.dtype, p.BH, 1, p.LC, p.D, 1);
-  carve::ContentArgs cg = {};
-  cg.b_x = content->b_x;
-  cg.U1 = content->U1;
-  cg.U2 = content->U2;
-  cg.R = R;
-  cg.m0 = content->m0;
-  cg.period = s->L;
-  cg.z_all = z_all;
-  cg.m_all = m_all;
-  hipError_t e = carve::launch_fwd_content(fa, cg, hs);
+  // 1. each period's z and the mean it was formed from: the forward's records, or the
+  //    content-aware forward run again to record them
+  hipError_t e = hipSuccess;
+  if (!rec) {
+    carve::FwdArgs fa = fwd_args(s, p, q, k, v, log_g, nullptr, w, S0, ws + Lw.o, nullptr);
+    fa.mode = 1;
+    fa.f = carve::carve_factors(ws + Lw.fwd, fa.dtype, p.BH, 1, p.LC, p.D, 1);
+    carve::ContentArgs cg = {};
+    cg.b_x = content->b_x;
+    cg.U1 = content->U1;
+    cg.U2 = content->U2;
+    cg.R = R;
+    cg.m0 = content->m0;
+    cg.period = s->L;
+    cg.z_all = reinterpret_cast<float*>(ws + Lw.z);
+    cg.m_all = reinterpret_cast<float*>(ws + Lw.m);
+    e = carve::launch_fwd_content(fa, cg, hs);
+  }
 
   carve::ContentBwdArgs ca = {};
   ca.B = s->B;

@@ -7,7 +7,8 @@
 
 Runs the 1.3B-head-shape workload (B4 H16 T4096 d128 L64, bf16 q/k/v, fp32 gates;
 synthetic seeded inputs) through the same entry points as bench.py: the training step
-(fwd_save + bwd_saved), the plain forward, the content-aware forward or its backward, the
+(fwd_save + bwd_saved), the plain forward, the content-aware forward or its backward (given the forward's
+per-period records), the
 long-context forward (B1 H16 T32768, --pass long), or recurrent decode
 steps (one token per sequence and head at batch --decode-batch).  With
 --copy-mib N it also runs a plain elementwise kernel that reads N MiB and writes N MiB
@@ -54,6 +55,11 @@ def main(argv=None):
     content = None
     if args.passes in ("content", "content_bwd"):
         content = {"b_x": f32("b_x"), "U1": f32("U1"), "U2": f32("U2")}
+    if args.passes == "content_bwd":
+        # the forward's per-period records, as a training step would keep them
+        zr, mr = carve.content_records(wl.B, wl.H, wl.T, wl.Dk, wl.Dv, wl.L, dev)
+        carve.fwd(q, k, v, log_g, w, L=wl.L, content=dict(content, z_rec=zr, m_rec=mr))
+        content = dict(content, z_rec=zr, m_rec=mr)
     print(f"[profile_step] inputs ready: {wl.name} B{wl.B} H{wl.H} T{wl.T} d{wl.Dk} L{wl.L}", flush=True)
 
     def step():

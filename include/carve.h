@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define CARVE_ABI_VERSION 1
+#define CARVE_ABI_VERSION 2
 
 typedef enum {
   CARVE_OK = 0,
@@ -88,6 +88,14 @@ typedef struct {
   int R;             /* rank of the projection, 1..64 (ignored when U1 = U2 = NULL)             */
   const float* m0;   /* (device) [B,H,Dv] mean output of the chunk before this call, or NULL (= 0) */
   float* m_out;      /* (device) [B,H,Dv] mean output of this call's last chunk, or NULL         */
+  /* Per-period records, P = ceil(T / L) periods of L tokens (both NULL, or both given):
+   * z_rec [B,H,P,Dk] the content signal z = U2 (U1 m) each period's erase gate used, and
+   * m_rec [B,H,P,Dv] the mean output m it was formed from (m0 or 0 for the first period).
+   * carve_fwd writes them; carve_bwd_content reads them (the records of the forward of the
+   * same inputs) instead of re-running the content-aware forward to obtain them.  Either
+   * way the gradients are the same bits.  Caller-owned, 16-byte aligned. */
+  float* z_rec;
+  float* m_rec;
 } carve_content;
 
 /* Bytes of device workspace carve_fwd needs for this shape (0 is a valid answer). */

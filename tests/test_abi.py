@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.carve_abi_version() == 1
+    assert lib.carve_abi_version() == 2
     for code in range(5):
         assert carve.status_string(code).startswith("CARVE_")
 
@@ -105,6 +105,10 @@ def test_fwd_content_checks(lib):
     assert call_fwd(lib, shape(), content=c_rank) == INVALID                 # rank 0
     c_nobx = carve.carve_content(None, None, None, 0, None, None)
     assert call_fwd(lib, shape(), content=c_nobx) == INVALID                 # b_x required
+    c_rec = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None, FAKE, None)
+    assert call_fwd(lib, shape(), content=c_rec) == INVALID                  # z_rec without m_rec
+    c_mis = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None, FAKE, FAKE + 8)
+    assert call_fwd(lib, shape(), content=c_mis) == INVALID                  # misaligned record
     assert call_fwd(lib, shape(L=16), content=c) == UNSUPPORTED               # period not whole tiles
     assert call_fwd(lib, shape(L=96), content=c) == UNSUPPORTED
     s = shape()
@@ -201,6 +205,12 @@ def test_bwd_content_rejects_bad_arguments(lib):
     need = lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(proj))
     assert need > lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(plain)) > 0
     assert call_bwd_content(lib, s, proj, dU1=FAKE, dU2=FAKE, ws_bytes=need - 1) == WORKSPACE
+    # with the forward's per-period records the content-aware forward is not re-run: less workspace
+    rec = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None, FAKE, FAKE)
+    need_rec = lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(rec))
+    assert 0 < need_rec < need
+    half = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None, None, FAKE)
+    assert call_bwd_content(lib, s, half, dU1=FAKE, dU2=FAKE) == INVALID   # m_rec without z_rec
 
 
 def test_logits_entry_points_reject_bad_arguments(lib):

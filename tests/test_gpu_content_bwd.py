@@ -173,3 +173,47 @@ def test_content_bwd_empty_sequence():
     torch.cuda.synchronize()
     assert torch.equal(g["dS0"], dS_T) and torch.equal(g["dm0"], dm_out)
     assert torch.count_nonzero(g["dU1"]) == 0 and torch.count_nonzero(g["dU2"]) == 0
+
+
+def test_forward_records_match_reference():
+    """The forward's per-period records: m_rec[p] is the mean output of period p-1 (m0 for
+    the first), z_rec[p] = U2 U1 m_rec[p]; checked against the reference forward's outputs."""
+    announce("content forward records")
+    B, H, T, D, L = 2, 2, 200, 128, 64
+    inp, ex = content_case(B, H, T, D, "bf16", seed=131)
+    d = to_device(inp, "bf16")
+    zr, mr = carve.content_records(B, H, T, D, D, L, "cuda")
+    carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], L=L,
+              content={"b_x": d["b_x"], "U1": d["U1"], "U2": d["U2"], "m0": f32(ex["m0"]), "z_rec": zr, "m_rec": mr})
+    torch.cuda.synchronize()
+    ro, _, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L,
+                              content={"b_x": inp["b_x"], "U1": inp["U1"], "U2": inp["U2"], "m0": ex["m0"]})
+    P = (T + L - 1) // L
+    m_ref = np.empty((B, H, P, D))
+    m_ref[:, :, 0] = ex["m0"]
+    for p_ in range(1, P):
+        m_ref[:, :, p_] = ro[:, :, (p_ - 1) * L:p_ * L].mean(axis=2)
+    z_ref = np.einsum("hkr,bhpr->bhpk", inp["U2"], np.einsum("hrv,bhpv->bhpr", inp["U1"], m_ref))
+    em, ez = max_rel(to_np(mr), m_ref), max_rel(to_np(zr), z_ref)
+    print(f"  err m_rec={em:.2e} z_rec={ez:.2e}", flush=True)
+    assert em <= TOL["bf16"] and ez <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,D,T,L", [("bf16", 128, 200, 64), ("f32", 64, 130, 32)])
+def test_backward_with_records_is_bit_identical(dtype, D, T, L):
+    """Passing the forward's records skips the re-run of the content-aware forward and gives
+    the same gradients, bit for bit."""
+    announce(f"content backward with records {dtype} d{D} T{T} L{L}")
+    B, H = 2, 2
+    inp, ex = content_case(B, H, T, D, dtype, seed=141 + D)
+    d = to_device(inp, dtype)
+    cont = {"b_x": d["b_x"], "U1": d["U1"], "U2": d["U2"], "m0": f32(ex["m0"])}
+    zr, mr = carve.content_records(B, H, T, D, D, L, "cuda")
+    carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], S0=f32(ex["S0"]), L=L,
+              content=dict(cont, z_rec=zr, m_rec=mr))
+    kw = dict(S0=f32(ex["S0"]), dS_T=f32(ex["dS_T"]), dm_out=f32(ex["dm_out"]), L=L)
+    g0 = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], cont, **kw)
+    g1 = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], dict(cont, z_rec=zr, m_rec=mr), **kw)
+    torch.cuda.synchronize()
+    for key in NAMES:
+        assert torch.equal(g0[key], g1[key]), key
