@@ -49,6 +49,13 @@ def parse():
     return p.parse_args()
 
 
+def hbm_frac(bytes_per_token_head, wl, ms, extra_bytes=0):
+    """Algorithmic bytes of a whole call (per token-head figure x B*H*T, plus fixed extras such
+    as S_T) over its time, as a fraction of the HBM peak."""
+    total = bytes_per_token_head * wl.B * wl.H * wl.T + extra_bytes
+    return round(total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+
 def algorithmic(wl, with_bwd):
     """Algorithmic bytes and flops per token-head (inputs read once, outputs written once;
     triangle-aware flop count, 2 per multiply-add)."""
@@ -204,7 +211,10 @@ def main():
              "step_ms_cold": {"median": round(float(np.median(cold)), 4), "min": round(float(np.min(cold)), 4)},
              "tokens_per_s_cold_median": B * T / (float(np.median(cold)) * 1e-3),
              "fwd_ms": round(fwd_ms, 4), "fwd_stage_ms": {k_: round(v_, 4) for k_, v_ in fwd_stage.items()},
-             "fwd_tokens_per_s": B * T / (fwd_ms * 1e-3)}
+             "fwd_tokens_per_s": B * T / (fwd_ms * 1e-3),
+             # each workload's algorithmic bytes over its time, against 8 TB/s (the training step's
+             # is path_hbm_frac below)
+             "hbm_frac": {"fwd": hbm_frac(algorithmic(wl, False)["fwd"], wl, fwd_ms)}}
 
     # long-context forward (B1 H16 T32768 d128 L64): sixteen sequential chains of 512 chunks
     if not args.no_long:
@@ -226,6 +236,9 @@ def main():
         lms = le0.elapsed_time(le1) / 5
         extra["long_ctx_fwd_ms"] = round(lms, 4)
         extra["long_ctx_fwd_tokens_per_s"] = wlc.B * wlc.T / (lms * 1e-3)
+        # inputs (no erase tensor) and o, plus the final state S_T
+        extra.setdefault("hbm_frac", {})["long_ctx_fwd"] = hbm_frac(
+            algorithmic(wlc, False)["fwd"], wlc, lms, extra_bytes=wlc.B * wlc.H * wlc.Dv * wlc.Dk * 4)
         del lq, lk, lv, lg_, lw_, lb_
 
     # content-aware forward of the same shape (separate timing, not part of the step)
@@ -254,6 +267,9 @@ def main():
         cms = ce0.elapsed_time(ce1) / nrep
         extra["content_fwd_ms"] = round(cms, 4)
         extra["content_fwd_tokens_per_s"] = wc.B * wc.T / (cms * 1e-3)
+        # inputs with b_x in place of b (4 Dk bytes), and o
+        cfb = algorithmic(wc, False)["fwd"] + 4 * wc.Dk
+        extra.setdefault("hbm_frac", {})["content_fwd"] = hbm_frac(cfb, wc, cms)
         # its backward (gradients of q, k, v, log g, b_x, w, U1, U2): a reverse sweep over the
         # content periods, each a few launches over all heads
         cdo = torch.from_numpy(np.ascontiguousarray(make_inputs(wc, with_dO=True)["dO_bits"]).view(np.int16)).to(
@@ -282,12 +298,19 @@ def main():
         extra["content_bwd_ms"] = round(cbms, 4)
         extra["content_bwd_tokens_per_s"] = wc.B * wc.T / (cbms * 1e-3)
         extra["content_bwd_recompute_ms"] = round(time_bwd(cont), 4)
+        # the inputs again with dO, and dq, dk, dv, dlog g, db_x, dw (as the plain backward with b)
+        extra["hbm_frac"]["content_bwd"] = hbm_frac(cfb + (algorithmic(wl, True)["bwd"] - algorithmic(wl, False)["fwd"]),
+                                                     wc, cbms)
         del cq, ck, cv, cf, cont, crec, zr, mr, ws_c, co, cdo, ws_cb
 
     # gates given as pre-activations (activated inside the kernels), same shape; the plain
     # backward that recomputes the forward is timed beside it
     if not args.no_logits:
         extra["logits"] = logits_bench(q, k, v, dO, wl, dev)
+        # f, b_x, w_hat take the places of log g, b, w: the same bytes as the plain pair
+        alg_l = algorithmic(wl, True)
+        extra.setdefault("hbm_frac", {})["fwd_logits"] = hbm_frac(alg_l["fwd"], wl, extra["logits"]["fwd_logits_ms"])
+        extra["hbm_frac"]["bwd_logits"] = hbm_frac(alg_l["fwd"] + alg_l["bwd"], wl, extra["logits"]["bwd_logits_ms"])
 
     # recurrent decode step (one token per sequence and head, state updated in place)
     if not args.no_decode:
