@@ -94,9 +94,9 @@ def measured_traffic(stage):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: the CARVE kernels run on a single MI355X in this build "
-              f"(--gpus {args.gpus} is not supported; heads would shard across GPUs with no communication, "
-              f"see the design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU: the CARVE kernels run on a single MI355X "
+              f"(--gpus {args.gpus} is not supported; (batch, head) sequences are independent, so they "
+              f"would shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import torch
