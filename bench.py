@@ -216,7 +216,8 @@ def main():
              # is path_hbm_frac below)
              "hbm_frac": {"fwd": hbm_frac(algorithmic(wl, False)["fwd"], wl, fwd_ms)}}
 
-    # long-context forward (B1 H16 T32768 d128 L64): sixteen sequential chains of 512 chunks
+    # long-context forward (B1 H16 T32768 d128 L64): sixteen heads of 512 chunks, whose state
+    # pass runs as segments chained by a scan of their affine maps
     if not args.no_long:
         wlc = WORKLOADS["long_ctx_fwd"]
         lin = make_inputs(wlc)
