@@ -523,27 +523,46 @@ __global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs
   }
   f32x4 S[ST::SPW];
   __syncthreads();
+  // the raw inputs of the next chunk are loaded (into registers) as soon as a chunk's state
+  // step is done, so they arrive while the period's mean and signal are formed
+  const ContentGates gates{cg.b_x, zL};
+  PrepStage<T, LC, D, NT> st;
+  prep_stage_load<T, LC, D, ContentGates, NT>(a, gates, bh, 0, st);
   int count = 0;
   for (int c = 0; c < a.NC; ++c) {
     if (c % per == 0) {
-      // content signal of this period from the previous period's mean output
+      // content signal of this period from the previous period's mean output, with every
+      // thread: r = U1 m (each row of U1 over 32 lanes), then z = U2 r (each row over 4 lanes)
       if (cg.U1) {
-        if (tid < cg.R) {
-          const float* u1 = cg.U1 + ((size_t)h * cg.R + tid) * D;
+        for (int j0 = 0; j0 < cg.R; j0 += NT / 32) {
+          const int j = j0 + tid / 32, part = tid % 32;
           float acc = 0.f;
-          for (int vv = 0; vv < D; ++vv) acc += u1[vv] * mL[vv];
-          rL[tid] = acc;
+          if (j < cg.R) {
+            const float* u1 = cg.U1 + ((size_t)h * cg.R + j) * D;
+#pragma unroll
+            for (int vv = part; vv < D; vv += 32) acc += u1[vv] * mL[vv];
+          }
+#pragma unroll
+          for (int o = 16; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+          if (j < cg.R && part == 0) rL[j] = acc;
         }
         __syncthreads();
-        if (tid < D) {
-          const float* u2 = cg.U2 + ((size_t)h * D + tid) * cg.R;
+        static_assert(NT >= 4 * D, "four lanes per key channel for z = U2 r");
+        {
+          const int kk = tid / 4, part = tid % 4;
           float acc = 0.f;
-          for (int j = 0; j < cg.R; ++j) acc += u2[j] * rL[j];
-          zL[tid] = acc;
+          if (kk < D) {
+            const float* u2 = cg.U2 + ((size_t)h * D + kk) * cg.R;
+            for (int j = part; j < cg.R; j += 4) acc += u2[j] * rL[j];
+          }
+          acc += __shfl_xor(acc, 2);
+          acc += __shfl_xor(acc, 1);
+          if (kk < D && part == 0) zL[kk] = acc;
         }
       } else if (tid < D) {
         zL[tid] = 0.f;
       }
+      __syncthreads();   // z is written by other threads than the ones recording it
       if (tid < D) {
         msum[tid] = 0.f;
         if (cg.z_all) {
@@ -556,8 +575,10 @@ __global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs
       count = 0;
       __syncthreads();
     }
-    // prepare this chunk's factors into the head's slot
-    prep_chunk<T, LC, D, ContentGates, kPrepFwd, NT>(a, ContentGates{cg.b_x, zL}, bh, c, (size_t)bh, smem);
+    // prepare this chunk's factors into the head's slot (its raw inputs are in registers)
+    prep_stage_write<T, LC, D, ContentGates, NT>(a, gates, c, st, smem);
+    __syncthreads();
+    prep_compute<T, LC, D, ContentGates, kPrepFwd, NT>(a, gates, bh, c, (size_t)bh, smem);
     __syncthreads();
     if (c == 0) {
       state_init<T, D, D, NW>(a, bh, 0, S, reinterpret_cast<T*>(smem));
@@ -578,6 +599,7 @@ __global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs
     ChunkOps<T, LC, D, D, true, NW> op;
     op.load(a, (size_t)bh, 0);
     state_chunk<T, LC, D, D, true, false, NW>(a, bh, c, 0, op, S, smem, cs);
+    prep_stage_load<T, LC, D, ContentGates, NT>(a, gates, bh, min(c + 1, a.NC - 1), st);   // (the last reloads itself)
     // fold this chunk's column sums into the period sum (fixed order over row tiles)
     const int nvalid = min(LC, a.T - c * LC);
     if (tid < D) {
