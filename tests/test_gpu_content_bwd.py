@@ -91,6 +91,25 @@ def test_content_bwd_parity(dtype, B, H, T, D, L):
     assert max_rel(ref0["dk"], ref["dk"]) > 0.02
 
 
+def test_content_bwd_rank64():
+    """The largest projection rank (64) at width 64, over several periods.  (Projection scale
+    8: larger scales drive sigma(b_x + z) so low that a channel's retention over one tile
+    leaves the dynamic range the chunk products support.)"""
+    announce("content bwd rank 64 d64")
+    B, H, T, D, L = 2, 2, 150, 64, 32
+    inp = random_inputs(B, H, T, D, D, dtype="bf16", seed=321, erase="content", dists="softplus_decay",
+                        with_dO=True, rank=64)
+    inp["U1"] = inp["U1"] * 8.0
+    inp["U2"] = inp["U2"] * 8.0
+    rng = np.random.default_rng(322)
+    ex = {"m0": np.asarray(rng.standard_normal((B, H, D)) * 0.5, np.float32).astype(np.float64),
+          "S0": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),
+          "dS_T": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),
+          "dm_out": np.asarray(rng.standard_normal((B, H, D)), np.float32).astype(np.float64)}
+    g, ref = run_both(inp, ex, "bf16", L)
+    check(g, ref, TOL["bf16"])
+
+
 def test_content_bwd_no_projection():
     announce("content bwd without projection")
     inp, ex = content_case(2, 2, 150, 128, "bf16", seed=301)

@@ -246,6 +246,23 @@ def test_content_parity(dtype, D, L, T, scale):
     assert max_rel(ro0, ro) > 0.02
 
 
+@pytest.mark.parametrize("dtype,D,L,R", [("bf16", 64, 64, 64), ("f32", 128, 32, 40)])
+def test_content_parity_high_rank(dtype, D, L, R):
+    """Projection ranks above 16 (up to the largest, 64): the signal's first product runs in
+    several passes over the rows of U1."""
+    announce(f"content {dtype} D{D} L{L} rank {R}")
+    T = 3 * L + 11
+    inp = content_inputs(2, 2, T, D, dtype, seed=60 + D + R, scale=32.0, R=R)
+    d = to_device(inp, dtype)
+    o, S_T, m = run_gpu(inp, dtype, L, content={"U1": d["U1"], "U2": d["U2"]})
+    ro, rS, rm = run_ref(inp, L, content={"b_x": inp["b_x"], "U1": inp["U1"], "U2": inp["U2"]})
+    errs = (max_rel(o, ro), max_rel(S_T, rS), max_rel(m, rm))
+    ro0, _, _ = run_ref(inp, L, content={"b_x": inp["b_x"], "U1": None, "U2": None})
+    print(f"  err o={errs[0]:.2e} S_T={errs[1]:.2e} m={errs[2]:.2e}; content effect {max_rel(ro0, ro):.2e}", flush=True)
+    assert max(errs) <= TOL[dtype]
+    assert max_rel(ro0, ro) > 0.02
+
+
 def test_content_zero_projection_bit_exact():
     """U_b = 0 reproduces the U_b-absent path bit for bit (o, S_T and m_out)."""
     announce("content_zero_projection_bit_exact")
