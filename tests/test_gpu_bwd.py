@@ -114,6 +114,32 @@ def test_full_train_sampled_heads():
         assert all(v_ <= 2e-2 for v_ in errs.values()), errs
 
 
+def test_full_bench_launch_sampled_heads():
+    """Exactly what the benchmark times: fwd_save + bwd_saved at the 1.3B-head shape
+    (B4 H16 T4096 d128 L64, b = sigmoid(N(2,1))); the identity <dq, q> = <dO, o> on every head
+    and one sampled head's output and gradients against the reference."""
+    wl = WORKLOADS["head1p3b_fwd"]
+    announce(wl.name + " full size via the saved pair, sampled head")
+    inp = make_inputs(wl, with_dO=True)
+    d = to_device(inp, wl.dtype)
+    o, S_T, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], L=wl.L)
+    g = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=d["b"], L=wl.L)
+    torch.cuda.synchronize()
+    lhs = (g["dq"].float() * d["q"].float()).sum(dim=(2, 3))
+    rhs = (d["dO"].float() * o.float()).sum(dim=(2, 3))
+    rel = ((lhs - rhs).abs().max() / rhs.abs().max()).item()
+    print(f"  <dq,q> vs <dO,o>: {rel:.2e}", flush=True)
+    assert rel <= 2e-2
+    bi, hi = 2, 9
+    sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items() if not k_.endswith("_bits")}
+    ro, _, _ = oracle.forward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], b=sub["b"])
+    ref = oracle.backward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], sub["dO"], b=sub["b"])
+    errs = {key: max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key]) for key in NAMES if g[key] is not None}
+    errs["o"] = max_rel(to_np(o[bi:bi + 1, hi:hi + 1]), ro)
+    print(f"  head ({bi},{hi}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= 2e-2 for v_ in errs.values()), errs
+
+
 def test_saved_pair_matches_recompute_bitwise():
     """fwd_save gives the same o and S_T as fwd, and bwd_saved the same gradients as bwd
     (the same arithmetic, only the forward is not recomputed)."""
