@@ -664,16 +664,6 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   }
 }
 
-// One chunk, not pipelined: load, stage, compute.
-template <typename T, int LC, int D, typename Gates, int MODE = kPrepFwd, int NT = kThreads>
-__device__ __forceinline__ void prep_chunk(const FwdArgs& a, const Gates& gates, int bh, int c, size_t ci, unsigned char* smem) {
-  PrepStage<T, LC, D, NT> st;
-  prep_stage_load<T, LC, D, Gates, NT>(a, gates, bh, c, st);
-  prep_stage_write<T, LC, D, Gates, NT>(a, gates, c, st, smem);
-  __syncthreads();
-  prep_compute<T, LC, D, Gates, MODE, NT>(a, gates, bh, c, ci, smem);
-}
-
 
 // Workgroups are dispatched round-robin over the 8 XCDs (block id mod 8), each
 // with its own L2.  The value slices of one (batch, head) read the same chunk

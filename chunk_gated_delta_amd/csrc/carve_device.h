@@ -198,13 +198,6 @@ __device__ __forceinline__ f32x4 load4f(const bf16* p) {
   return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
 }
 
-// wave-local ordering of LDS traffic between lanes of one wave
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // padded leading dimensions for LDS tiles: rows shifted by 16 bytes to spread banks
 template <typename T> struct Pad;
 template <> struct Pad<bf16> { static constexpr int v = 8; };
