@@ -32,8 +32,10 @@
  *     gates, states, workspace-independent outputs marked float are float32.
  *   - The caller owns every buffer, including the workspace, which must hold at
  *     least *_workspace_size() bytes.  The library never allocates or frees
- *     device memory and keeps no mutable global state; calls on different
- *     streams may run concurrently as long as they use different workspaces.
+ *     device memory; its only global state is a per-device cache of the
+ *     compute-unit count (the size of its persistent launches).  Calls on
+ *     different streams may run concurrently as long as they use different
+ *     workspaces.
  *   - Every launch is enqueued on `stream` (a hipStream_t; NULL = default
  *     stream) and the call returns without synchronising.
  *   - Argument checks run on the host before any launch.  On a non-OK status
@@ -111,6 +113,10 @@ size_t carve_fwd_workspace_size(const carve_shape* s, const carve_content* conte
  *   content                                    NULL (token-only gates) or content-aware erase
  *   o      (device) [B,H,T,Dv] dtype          output (written)
  *   S_T    (device) [B,H,Dv,Dk] float         final state (written), or NULL
+ * With few heads and a long sequence (B*H*Dk/16 < 256 and at least 32 chunks of
+ * tokens) the token-only state pass runs as segments of chunks whose affine maps
+ * S_in -> S_in Pi + C are chained by a short scan (the workspace then also holds
+ * their float32 maps); the result agrees with the sequential pass to rounding.
  */
 carve_status carve_fwd(const carve_shape* s,
                        const void* q, const void* k, const void* v,
@@ -150,6 +156,8 @@ carve_status carve_bwd(const carve_shape* s,
  * synchronised; the caller reads the events afterwards (hipEventElapsedTime).
  *   carve_fwd  stages: 0 = chunk prep (token-only) or the content-aware
  *                      kernel (content path, single stage), 1 = state pass
+ *                      (segmented: the affine maps, their scan and the
+ *                      segments' state passes)
  *   carve_bwd  stages: 0 = chunk prep, 1 = forward state pass,
  *                      2 = reverse state pass, 3 = chunk gradients
  * With profile == NULL they are carve_fwd / carve_bwd.
