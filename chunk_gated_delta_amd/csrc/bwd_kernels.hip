@@ -465,28 +465,32 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
         tile *= tg;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gam[rt][j][i] = pre * loc[i];
+      for (int i = 0; i < 4; ++i) {
+        gam[rt][j][i] = pre * loc[i];
+        lgS[(16 * rt + 4 * lg + i) * LDG + col] = gam[rt][j][i];   // only this lane reads it
+      }
       run *= tile;
     }
     gLc[j] = run;
     if (lg == 0) gLs[col] = run;
   }
-  // operand matrices K+ (in place), K-, Q+ (in place); V stays raw
+  __syncthreads();
+  // operand matrices K+ (in place), K-, Q+ (in place) in the staging pieces, with Gamma
+  // read back from the log g slots; V stays raw
 #pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int col = 16 * (ct0 + j) + lr;
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    const Frag<float> gm = load_frag(lgS + r * LDG + 8 * g);
+    f32x4 ri0, ri1;
 #pragma unroll
-    for (int rt = 0; rt < NB; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i;
-        const float kv = tof(Kp[r * LDD + col]);
-        const float qv = tof(Qp[r * LDD + col]);
-        const float g = gam[rt][j][i];
-        Kp[r * LDD + col] = to<T>(kv * g);
-        Km[r * LDD + col] = to<T>(kv * rcp(g));
-        Qp[r * LDD + col] = to<T>(qv * g);
-      }
+    for (int e = 0; e < 4; ++e) {
+      ri0[e] = rcp(gm.lo[e]);
+      ri1[e] = rcp(gm.hi[e]);
+    }
+    const Frag<T> kf = load_frag(Kp + r * LDD + 8 * g), qf = load_frag(Qp + r * LDD + 8 * g);
+    *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = scale_frag(kf, gm.lo, gm.hi);
+    *reinterpret_cast<Frag<T>*>(Km + r * LDD + 8 * g) = scale_frag(kf, ri0, ri1);
+    *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = scale_frag(qf, gm.lo, gm.hi);
   }
   __syncthreads();
 

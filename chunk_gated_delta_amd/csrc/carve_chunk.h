@@ -121,19 +121,28 @@ template <int LC, int LDF, int NT = kThreads>
 __device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_float* Tf) {
   constexpr int NB = LC / 16;
   static_assert(NT / 64 >= NB - 1, "one wave per off-diagonal block of a distance");
+  static_assert(LDF % 4 == 0, "rows of A are read as 16-byte pieces");
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   if (tid < 16 * NB) {
-    // lane (block, column j) solves (I + A_bb) x = e_j; right-looking: once x[m] is
-    // final it is subtracted from every later row, so the dependent chain is 15
-    // steps long (each row still accumulates its terms in the order m = 0, 1, ...)
+    // lane (block, column j) solves (I + A_bb) x = e_j row by row: x[r] = e_j[r] -
+    // sum_{m<r} A[r][m] x[m], accumulated in the order m = 0, 1, ...; the rows of A
+    // are read as 4-float pieces (every lane of a block reads the same addresses), all
+    // independent of x, so only the final subtraction of each row waits on x[r-1]
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
     const int base = 16 * (tid / 16), j = tid % 16;
     float x[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == j) ? 1.f : 0.f;
+    for (int r = 0; r < 16; ++r) {
+      float xr = (r == j) ? 1.f : 0.f;
 #pragma unroll
-    for (int m = 0; m < 15; ++m)
+      for (int c4 = 0; 4 * c4 < r; ++c4) {
+        const f32x4 av = *reinterpret_cast<const lds_f32x4*>(Af + (base + r) * LDF + base + 4 * c4);
 #pragma unroll
-      for (int r = m + 1; r < 16; ++r) x[r] -= Af[(base + r) * LDF + base + m] * x[m];
+        for (int e = 0; e < 4; ++e)
+          if (4 * c4 + e < r) xr -= av[e] * x[4 * c4 + e];
+      }
+      x[r] = xr;
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Tf[(base + r) * LDF + base + j] = x[r];
   }
