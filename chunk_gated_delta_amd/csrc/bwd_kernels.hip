@@ -34,16 +34,24 @@ __device__ __forceinline__ bf16 frag_elem(const Frag<bf16>& f, int e) { return f
 __device__ __forceinline__ float frag_elem(const Frag<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
 
 // ------------------------------------------------------------------ reverse state pass
+// LDS: the dtype copy of the dS^T slice [VS][D], X^T [VS][LC], the chunk's dO slice
+// (row-major [LC][VS]) and the chunk's factors in their forward layouts, row-major:
+// -W and Q~ [LC][D] (rows = tokens), K->^T [D][LC] (rows = keys).  The products read
+// the factors and dO as transposed fragments.
 template <typename T, int LC, int D, int VS>
 struct RevLayout {
   static constexpr int LDS_ = D + Pad<T>::v;
   static constexpr int LDU = LC + Pad<T>::v;
-  static constexpr size_t bytes = sizeof(T) * (VS * LDS_ + 2 * VS * LDU);
+  static constexpr int LDV = VS + Pad<T>::v;
+  static constexpr size_t state = sizeof(T) * (VS * LDS_ + VS * LDU + LC * LDV);
+  static constexpr size_t Wl = state, Ql = Wl + sizeof(T) * LC * LDS_, Kl = Ql + sizeof(T) * LC * LDS_;
+  static constexpr size_t bytes = Kl + sizeof(T) * D * LDU;
 };
 
-// Global operands of one chunk for one wave (loaded one chunk ahead):
-//   X^T tiles [s][v] = K-> dS^T: wave w owns tiles tix = w*XPW + u (one row tile of s)
-//   dS^T tiles [k][v]: wave w owns key tiles ct = w*SCT + j
+// Global operands of one chunk (loaded two chunks ahead, chunks running last to first):
+//   the chunk's -W, Q~ and K->^T blocks as they are stored (fragment order), piece
+//   tid + kThreads u of each block, staged in LDS one chunk step ahead of their use
+//   Gamma_L of the wave's key tiles
 //   the chunk's dO slice (LC x VS), spread over all threads
 template <typename T, int LC, int D, int VS>
 struct RevOps {
@@ -54,38 +62,31 @@ struct RevOps {
   static constexpr int KD = D / 32, KL = LC / 32;
   static constexpr int VEC = 8;                                   // elements per fragment-sized piece
   static constexpr int NDO = (LC * VS / VEC + kThreads - 1) / kThreads;
+  static constexpr int NPT = LC * D / VEC / kThreads;             // pieces of each factor block per thread
   static_assert(NVT % XPW == 0, "a wave's X tiles must share one row tile");
+  static_assert(NPT * kThreads * VEC == LC * D, "factor blocks must split evenly over the threads");
   static constexpr bool kAllWaves = XPW * (kWaves - 1) < NX;          // every wave owns X tiles
   static constexpr bool kFullDO = (LC * VS / VEC) % kThreads == 0;    // every thread loads NDO pieces
-  Frag<T> kf[KD];
-  Frag<T> wt[SCT][KL];
-  Frag<T> qt[SCT][KL];
+  Frag<T> wn[NPT], qt[NPT], kt[NPT];
   f32x4 gl[SCT];
   Frag<T> dov[NDO];   // raw 16-byte pieces of dO: VEC consecutive value columns of one token
 
   __device__ __forceinline__ void load(const BwdArgs& a, int bh, int c, int v0) {
     const FwdArgs& f = a.fwd;
-    const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+    const int lg = lane_id() >> 4, wave = wave_id();
     const size_t ci = (size_t)bh * f.NC + c;
-    const T* Kf = reinterpret_cast<const T*>(f.f.Kf);
-    const T* WnT = reinterpret_cast<const T*>(f.f.WnT);
-    const T* QtT = reinterpret_cast<const T*>(f.f.QtT);
-    const int t0 = wave * XPW;
-    if (kAllWaves || t0 < NX) {
-      const int rt = t0 / NVT;
+    const T* Wn = reinterpret_cast<const T*>(f.f.Wn) + ci * LC * D;
+    const T* Qt = reinterpret_cast<const T*>(f.f.Qt) + ci * LC * D;
+    const T* KfT = reinterpret_cast<const T*>(f.f.KfT) + ci * D * LC;
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) kf[kk] = load_frag(Kf + ci * LC * D + frag_offset<D>(rt, kk, lane));
+    for (int u = 0; u < NPT; ++u) {
+      const int pc = threadIdx.x + kThreads * u;
+      wn[u] = load_frag(Wn + VEC * pc);
+      qt[u] = load_frag(Qt + VEC * pc);
+      kt[u] = load_frag(KfT + VEC * pc);
     }
 #pragma unroll
-    for (int j = 0; j < SCT; ++j) {
-      const int ct = wave * SCT + j;
-      gl[j] = load4f(f.f.gL + ci * D + 16 * ct + 4 * lg);
-#pragma unroll
-      for (int kk = 0; kk < KL; ++kk) {
-        wt[j][kk] = load_frag(WnT + ci * D * LC + frag_offset<LC>(ct, kk, lane));
-        qt[j][kk] = load_frag(QtT + ci * D * LC + frag_offset<LC>(ct, kk, lane));
-      }
-    }
+    for (int j = 0; j < SCT; ++j) gl[j] = load4f(f.f.gL + ci * D + 16 * (wave * SCT + j) + 4 * lg);
     const T* dO = reinterpret_cast<const T*>(a.dO);
     const int n = min(LC, f.T - c * LC);
 #pragma unroll
@@ -93,9 +94,25 @@ struct RevOps {
       const int idx = threadIdx.x + kThreads * u;            // piece index: token r, column group g
       const int r = idx / (VS / VEC), g = idx % (VS / VEC);
       if (kFullDO || idx < LC * VS / VEC) {
-        const int rr = min(r, n - 1);   // rows past the sequence end are zeroed where they are used
+        const int rr = min(r, n - 1);   // rows past the sequence end meet zero columns of Q~^T
         dov[u] = load_frag(dO + ((size_t)bh * f.T + c * LC + rr) * D + v0 + VEC * g);
       }
+    }
+  }
+
+  // The factor pieces into LDS, row-major: piece p of a block with C columns holds row
+  // 16 (b / (C/32)) + l % 16, columns 32 (b % (C/32)) + 8 (l / 16) .. + 7 (b = p / 64,
+  // l = p % 64; the fragment order of the prep pass).
+  __device__ __forceinline__ void stage(T* Wl, T* Ql, T* Kl) const {
+    constexpr int LDS_ = D + Pad<T>::v, LDU = LC + Pad<T>::v;
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int pc = threadIdx.x + kThreads * u, l = pc % 64, b = pc / 64;
+      const int rowd = 16 * (b / (D / 32)) + l % 16, cold = 32 * (b % (D / 32)) + 8 * (l / 16);
+      const int rowl = 16 * (b / (LC / 32)) + l % 16, coll = 32 * (b % (LC / 32)) + 8 * (l / 16);
+      *reinterpret_cast<Frag<T>*>(Wl + rowd * LDS_ + cold) = wn[u];
+      *reinterpret_cast<Frag<T>*>(Ql + rowd * LDS_ + cold) = qt[u];
+      *reinterpret_cast<Frag<T>*>(Kl + rowl * LDU + coll) = kt[u];
     }
   }
 };
@@ -105,12 +122,15 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   using Lay = RevLayout<T, LC, D, VS>;
   using Op = RevOps<T, LC, D, VS>;
   using ST = StateTiles<D, VS>;
-  constexpr int NVT = ST::NVT, SPW = ST::SPW, LDS_ = Lay::LDS_, LDU = Lay::LDU;
+  constexpr int NVT = ST::NVT, SPW = ST::SPW, LDS_ = Lay::LDS_, LDU = Lay::LDU, LDV = Lay::LDV;
   constexpr int VEC = Op::VEC;
   extern __shared__ __align__(16) unsigned char smem[];
   T* dSb = reinterpret_cast<T*>(smem);
   T* XT = dSb + VS * LDS_;
-  T* dOT = XT + VS * LDU;
+  T* dOr = XT + VS * LDU;
+  T* Wl = reinterpret_cast<T*>(smem + Lay::Wl);
+  T* Ql = reinterpret_cast<T*>(smem + Lay::Ql);
+  T* Kl = reinterpret_cast<T*>(smem + Lay::Kl);
   const FwdArgs& f = a.fwd;
   int bh, slice;
   xcd_slice_map(D / VS, f.B * f.H, bh, slice);
@@ -126,16 +146,19 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     else dS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     store4(dSb + vl * LDS_ + kc, dS[j]);
   }
-  // three operand buffers, loaded two chunks ahead (chunks run last to first);
-  // chunks below the last one run in a branch-free main loop with clamped prefetch.
+  // three operand buffers, loaded two chunks ahead (chunks run last to first); a
+  // chunk's factors are staged in LDS during the step before its own.  Chunks below
+  // the last one run in a branch-free main loop with clamped prefetch (a clamped
+  // buffer re-stages a chunk already done, which nothing reads).
   constexpr int PF = 3;
   // chunk range (all chunks unless a sub-range is asked for)
   const int clo = a.c_lo, chi = a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1, nch = chi - clo + 1;
   Op buf[PF];
 #pragma unroll
   for (int j = 0; j < PF - 1; ++j) buf[j].load(a, bh, max(chi - j, clo), v0);
+  buf[0].stage(Wl, Ql, Kl);
   __syncthreads();
-  auto step = [&](int c, const Op& cur) {
+  auto step = [&](int c, const Op& cur, const Op& nxt) {
     const size_t ci = (size_t)bh * f.NC + c;
     // gradient w.r.t. the state leaving chunk c, in fragment order rows v
     {
@@ -146,34 +169,49 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
         store_vk_group<T, D>(vk, v0 / 16 + vt, ct, dS[j]);
       }
     }
-    // dO^T slice into LDS
+    // dO slice into LDS as whole pieces (no per-element work on the loaded data, so none
+    // of it can be scheduled ahead of the step that owns the chunk).  Rows past the
+    // sequence end hold the clamped copy of the last row; they only meet columns of
+    // Q~^T that are exactly zero (q is zero past the end, so Q+, P and Q~ vanish there).
 #pragma unroll
     for (int u = 0; u < Op::NDO; ++u) {
       const int idx = threadIdx.x + kThreads * u;
       if (Op::kFullDO || idx < LC * VS / VEC) {
         const int r = idx / (VS / VEC), g = idx % (VS / VEC);
-        const bool live = r < f.T - c * LC;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) dOT[(VEC * g + e) * LDU + r] = live ? frag_elem(cur.dov[u], e) : T(0.f);
+        *reinterpret_cast<Frag<T>*>(dOr + r * LDV + VEC * g) = cur.dov[u];
       }
     }
+    // this chunk's factor fragments, transposed out of the staged blocks: K-> rows of
+    // the wave's X row tile (contraction over keys), (-W)^T and Q~^T rows of its key
+    // tiles (contraction over tokens); all are read before the barrier below, after
+    // which the next chunk's factors take the staging slots
+    Frag<T> kf[Op::KD], wt[Op::SCT][Op::KL], qt[Op::SCT][Op::KL];
+    const int t0 = wave * Op::XPW, rt = t0 / NVT;
+    if (Op::kAllWaves || t0 < Op::NX) {
+#pragma unroll
+      for (int kk = 0; kk < Op::KD; ++kk) kf[kk] = lds_frag_cols(Kl, LDU, 16 * rt, 32 * kk);
+    }
+#pragma unroll
+    for (int jc = 0; jc < Op::SCT; ++jc)
+#pragma unroll
+      for (int kk = 0; kk < Op::KL; ++kk) {
+        wt[jc][kk] = lds_frag_cols(Wl, LDS_, 16 * (wave * Op::SCT + jc), 32 * kk);
+        qt[jc][kk] = lds_frag_cols(Ql, LDS_, 16 * (wave * Op::SCT + jc), 32 * kk);
+      }
     // X^T = K-> dS^T  (tiles [s][v])
-    {
-      const int t0 = wave * Op::XPW;
-      if (Op::kAllWaves || t0 < Op::NX) {
-        const int rt = t0 / NVT;
+    if (Op::kAllWaves || t0 < Op::NX) {
 #pragma unroll
-        for (int u = 0; u < Op::XPW; ++u) {
-          const int vt = (t0 + u) % NVT;
-          const int vl = 16 * vt + lr;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < Op::XPW; ++u) {
+        const int vt = (t0 + u) % NVT;
+        const int vl = 16 * vt + lr;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kk = 0; kk < Op::KD; ++kk) mma(acc, cur.kf[kk], load_frag(dSb + vl * LDS_ + 32 * kk + 8 * lg));
-          store4(XT + vl * LDU + 16 * rt + 4 * lg, acc);
-        }
+        for (int kk = 0; kk < Op::KD; ++kk) mma(acc, kf[kk], load_frag(dSb + vl * LDS_ + 32 * kk + 8 * lg));
+        store4(XT + vl * LDU + 16 * rt + 4 * lg, acc);
       }
     }
     __syncthreads();
+    nxt.stage(Wl, Ql, Kl);
     // dS^T <- Diag(Gamma_L) dS^T + (-W)^T X^T + Q~^T dO
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {
@@ -183,8 +221,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
       dS[j] *= cur.gl[jc];
 #pragma unroll
       for (int kk = 0; kk < Op::KL; ++kk) {
-        mma(dS[j], cur.wt[jc][kk], load_frag(XT + vl * LDU + 32 * kk + 8 * lg));
-        mma(dS[j], cur.qt[jc][kk], load_frag(dOT + vl * LDU + 32 * kk + 8 * lg));
+        mma(dS[j], wt[jc][kk], load_frag(XT + vl * LDU + 32 * kk + 8 * lg));
+        mma(dS[j], qt[jc][kk], lds_frag_cols(dOr, LDV, 16 * vt, 32 * kk));
       }
       store4(dSb + vl * LDS_ + kc, dS[j]);
     }
@@ -196,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     for (int j = 0; j < PF; ++j) {
       const int c = chi - (g + j);
       buf[(j + PF - 1) % PF].load(a, bh, max(c - (PF - 1), clo), v0);
-      step(c, buf[j]);
+      step(c, buf[j], buf[(j + 1) % PF]);
     }
   }
 #pragma unroll
@@ -204,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
     const int c = chi - (nmain + j);
     if (c >= clo) {
       if (c - (PF - 1) >= clo) buf[(j + PF - 1) % PF].load(a, bh, c - (PF - 1), v0);
-      step(c, buf[j]);
+      step(c, buf[j], buf[(j + 1) % PF]);
     }
   }
   if (a.dS0) {
@@ -919,18 +957,25 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 template <typename T, int LC, int D, int VS>
 static hipError_t rev_launch(const BwdArgs& a, hipStream_t st) {
   using Lay = RevLayout<T, LC, D, VS>;
-  static_assert(Lay::bytes <= 64 * 1024, "reverse-state LDS exceeds 64 KB");
+  static_assert(Lay::bytes <= 80 * 1024, "reverse-state LDS exceeds half a compute unit's 160 KB");
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_state_kernel<T, LC, D, VS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
+  if (e != hipSuccess) return e;
   dim3 grid((D / VS) * a.fwd.B * a.fwd.H);
   hipLaunchKernelGGL((bwd_state_kernel<T, LC, D, VS>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }
 
+// The reverse pass takes at most 32 value rows per workgroup: with the staged factor
+// blocks a 64-row slice would need more than half of a compute unit's LDS, so two of
+// its workgroups could not share one (the forward pass's 64-row plans get twice as
+// many 32-row workgroups here).
 template <typename T, int LC, int D>
 static hipError_t rev_launch_vs(const BwdArgs& a, hipStream_t st) {
   switch (a.fwd.VS) {
     case 16: return rev_launch<T, LC, D, 16>(a, st);
-    case 32: return rev_launch<T, LC, D, 32>(a, st);
-    case 64: return rev_launch<T, LC, D, 64>(a, st);
+    case 32:
+    case 64: return rev_launch<T, LC, D, 32>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -241,9 +241,9 @@ struct LogitGates {
 // ------------------------------------------------------------------ per-chunk prep
 // Computes the factors of chunk c of head bh and writes them to slot `ci` of
 // the factor arrays.  Uses PrepLayout<T, LC, D>::bytes of LDS at `smem`.
-// MODE bit 1 writes the factors only the forward output uses (Q~ and P Ubar);
-// bit 2 writes the layouts the backward passes need ((-W)^T, Q~^T, row-major K->).
-// -W, K->^T, Ubar^T and Gamma_L are always written.
+// MODE bit 1 writes the factor only the forward output uses (P Ubar); bit 2 writes
+// the inverse T the chunk-gradient pass needs.  -W, Q~, K->^T, Ubar^T and Gamma_L
+// are always written.
 constexpr int kPrepFwd = 1, kPrepBwd = 2;
 
 // Raw inputs of one chunk as 16-byte pieces (8 consecutive channels of one token),
@@ -367,7 +367,6 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   T* VwT = KwT + D * LDL;
   float* Af = reinterpret_cast<float*>(smem + Lay::R4);
   T* WnT = reinterpret_cast<T*>(smem + Lay::R4);
-  T* KfL = reinterpret_cast<T*>(smem + Lay::R4);   // row-major K-> during the gate pass (backward modes)
   T* QtTs = KwT;                                    // Q~^T once the WY factors are done
   T* Pb = reinterpret_cast<T*>(smem + Lay::R5);
   T* UbTs = reinterpret_cast<T*>(smem + Lay::R6);
@@ -380,15 +379,11 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   const int n = min(LC, a.T - t0);
   const size_t row0 = (size_t)bh * a.T + t0;   // global token row of the chunk's first token
   constexpr bool FWD = (MODE & kPrepFwd) != 0, BWD = (MODE & kPrepBwd) != 0;
-  static_assert(Lay::szLD <= Lay::R5 - Lay::R4, "row-major K-> exceeds the coupling slot");
   T* gWn = reinterpret_cast<T*>(a.f.Wn) + ci * LC * D;
-  T* gQt = FWD ? reinterpret_cast<T*>(a.f.Qt) + ci * LC * D : nullptr;
+  T* gQt = reinterpret_cast<T*>(a.f.Qt) + ci * LC * D;
   T* gKfT = reinterpret_cast<T*>(a.f.KfT) + ci * D * LC;
   T* gUbT = reinterpret_cast<T*>(a.f.UbT) + ci * D * LC;
   T* gOiT = FWD ? reinterpret_cast<T*>(a.f.OiT) + ci * D * LC : nullptr;
-  T* gWnT = BWD ? reinterpret_cast<T*>(a.f.WnT) + ci * D * LC : nullptr;
-  T* gQtT = BWD ? reinterpret_cast<T*>(a.f.QtT) + ci * D * LC : nullptr;
-  T* gKf = BWD ? reinterpret_cast<T*>(a.f.Kf) + ci * LC * D : nullptr;
 
   // ---- gate pass: cumulative key-axis retention Gamma over the staged retention a
   // (1 past the end); raw k, q, v are read from their slots.  With at least four
@@ -454,7 +449,6 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       st_row<T, CPT>(Kp + r * LDD + ch, kp);
       st_row<T, CPT>(Km + r * LDD + ch, km);
       st_row<T, CPT>(Qp + r * LDD + ch, qp);
-      if (BWD) st_row<T, CPT>(KfL + r * LDD + ch, kf, i);
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -476,14 +470,6 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     }
   }
   __syncthreads();
-  if (BWD) {
-    // row-major K-> (staged in the coupling slot) to fragment order, then free the slot
-    for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
-      const int rt = f / (D / 32), kb = f % (D / 32);
-      *reinterpret_cast<Frag<T>*>(gKf + frag_offset<D>(rt, kb, lane)) = load_frag(KfL + (16 * rt + lr) * LDD + 32 * kb + 8 * lg);
-    });
-    __syncthreads();
-  }
 
   // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
   // Wave w takes tiles w, w + NW, ... (A tiles first, then P); all of its operand
@@ -592,17 +578,11 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     }
   }
   __syncthreads();
-  // -W out of LDS in fragment order: rows = tokens (forward), rows = keys (backward)
+  // -W out of LDS in fragment order, rows = tokens
   for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
     const int rt = f / (D / 32), kb = f % (D / 32);
     *reinterpret_cast<Frag<T>*>(gWn + frag_offset<D>(rt, kb, lane)) = lds_frag_cols(WnT, LDL, 16 * rt, 32 * kb);
   });
-  if (BWD) {
-    for_wave_items<NCT * (LC / 32), NW>(wave, [&](int f) {
-      const int kt = f / (LC / 32), kb = f % (LC / 32);
-      *reinterpret_cast<Frag<T>*>(gWnT + frag_offset<LC>(kt, kb, lane)) = load_frag(WnT + (16 * kt + lr) * LDL + 32 * kb + 8 * lg);
-    });
-  }
 
   // ---- intra-chunk output P Ubar and Q~ = Q+ - P W
   if constexpr (NW == NCT) {
@@ -658,19 +638,11 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     else store4(QtTs + col * LDL + r, acc);
   }
   __syncthreads();
-  // Q~ out of LDS in fragment order (rows = tokens forward, rows = keys backward)
-  if (FWD) {
-    for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
-      const int rt = f / (D / 32), kb = f % (D / 32);
-      *reinterpret_cast<Frag<T>*>(gQt + frag_offset<D>(rt, kb, lane)) = lds_frag_cols(QtTs, LDL, 16 * rt, 32 * kb);
-    });
-  }
-  if (BWD) {
-    for_wave_items<NCT * (LC / 32), NW>(wave, [&](int f) {
-      const int kt = f / (LC / 32), kb = f % (LC / 32);
-      *reinterpret_cast<Frag<T>*>(gQtT + frag_offset<LC>(kt, kb, lane)) = load_frag(QtTs + (16 * kt + lr) * LDL + 32 * kb + 8 * lg);
-    });
-  }
+  // Q~ out of LDS in fragment order, rows = tokens
+  for_wave_items<NB * (D / 32), NW>(wave, [&](int f) {
+    const int rt = f / (D / 32), kb = f % (D / 32);
+    *reinterpret_cast<Frag<T>*>(gQt + frag_offset<D>(rt, kb, lane)) = lds_frag_cols(QtTs, LDL, 16 * rt, 32 * kb);
+  });
 }
 
 

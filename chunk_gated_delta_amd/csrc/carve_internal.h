@@ -19,12 +19,10 @@ namespace carve {
 // where Gamma is the inclusive cumulative product of a inside the chunk,
 // T = (I + A)^-1, A = strict_tril(diag(w) (K.*Gamma)(K./Gamma)^T) and
 // P = tril((Q.*Gamma)(K./Gamma)^T).
-// The backward layouts (written when the prep mode includes the backward):
-//   QtT Q~^T [D][LC], frag<LC>
-//   WnT (-W)^T [D][LC], frag<LC>
-//   Kf  K-> [LC][D], frag<D>
+// The reverse state pass reads Wn, Qt and KfT too (transposed on chip); the backward
+// modes also write
 //   Tt  [ci][LC][LC] row-major, T = (I + A)^-1 (dtype)
-// Prep modes: 1 = forward only, 2 = backward only (no Qt / OiT), 3 = both.
+// Prep modes: 1 = forward only, 2 = backward only (no OiT), 3 = both.
 struct ChunkFactors {
   void* Wn;
   void* Qt;
@@ -32,9 +30,6 @@ struct ChunkFactors {
   void* UbT;
   void* OiT;
   float* gL;
-  void* QtT;
-  void* WnT;
-  void* Kf;
   void* Tt;               // [ci][LC][LC] T = (I + A)^-1 in the operand type (backward modes)
 };
 

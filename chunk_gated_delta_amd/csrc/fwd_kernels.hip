@@ -652,10 +652,10 @@ static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {  // one [
   return ((size_t)BH * NC * LC * D * es + 255) & ~size_t(255);
 }
 
-// Factor blocks in the workspace: -W, K->^T, Ubar^T always; Q~, P Ubar with the
-// forward mode; (-W)^T, Q~^T, K-> with the backward mode; then Gamma_L, and with the
-// backward mode the inverse T of every chunk (LC x LC, dtype).
-static int factor_blocks(int mode) { return 3 + ((mode & 1) ? 2 : 0) + ((mode & 2) ? 3 : 0); }
+// Factor blocks in the workspace: -W, K->^T, Ubar^T, Q~ always; P Ubar with the
+// forward mode; then Gamma_L, and with the backward mode the inverse T of every chunk
+// (LC x LC, dtype).
+static int factor_blocks(int mode) { return 4 + ((mode & 1) ? 1 : 0); }
 static size_t gl_block(int BH, int NC, int D) { return ((size_t)BH * NC * D * sizeof(float) + 255) & ~size_t(255); }
 
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode) {
@@ -671,11 +671,8 @@ ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, i
   f.Wn = p + blk * i++;
   f.KfT = p + blk * i++;
   f.UbT = p + blk * i++;
-  f.Qt = (mode & 1) ? p + blk * i++ : nullptr;
+  f.Qt = p + blk * i++;
   f.OiT = (mode & 1) ? p + blk * i++ : nullptr;
-  f.WnT = (mode & 2) ? p + blk * i++ : nullptr;
-  f.QtT = (mode & 2) ? p + blk * i++ : nullptr;
-  f.Kf = (mode & 2) ? p + blk * i++ : nullptr;
   f.gL = reinterpret_cast<float*>(p + blk * i);
   f.Tt = (mode & 2) ? p + blk * i + gl_block(BH, NC, D) : nullptr;
   return f;
