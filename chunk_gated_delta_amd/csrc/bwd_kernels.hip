@@ -656,9 +656,9 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   Frag<T> fSk[KD][CPW], fDk[KD][CPW];
   f32x4 dK[NB][CPW], dG[NB][CPW];
   float gsum[CPW];        // sum over tokens of K-> .* dK-> per column (part of the G_L term)
-  auto lds_el = [&](const T* m, int rt, int j, int ii) {
-    return tof(m[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr]);
-  };
+  // M[16 rt + 4 lg + i][16 (ct0 + j) + lr], i = 0..3: the lane's accumulator-layout
+  // elements of an operand matrix in LDS
+  auto lds_tile = [&](const T* m, int rt, int j) { return lds_acc_tile(m, LDD, 16 * rt, 16 * (ct0 + j)); };
   {
     // dQ+ = dO S + dP K-  -> dq = Gamma dQ+, dG = Q+ dQ+
     f32x4 acc[NB][CPW];
@@ -671,13 +671,15 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 qv = lds_tile(Qp, rt, j);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
-          dG[rt][j][ii] = lds_el(Qp, rt, j, ii) * acc[rt][j][ii];
+          dG[rt][j][ii] = qv[ii] * acc[rt][j][ii];
           if (r < n) dq[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(gam[rt][j][ii] * acc[rt][j][ii]);
         }
+      }
   }
   {
     // dK-> = U dS'  -> dK = (Gamma_L / Gamma) dK->, dG -= K-> dK->
@@ -688,14 +690,16 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     for (int j = 0; j < CPW; ++j) {
       float cs = 0.f;
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kmv = lds_tile(Km, rt, j);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const float kf = lds_el(Km, rt, j, ii) * gLc[j];       // K->
+          const float kf = kmv[ii] * gLc[j];       // K->
           dK[rt][j][ii] = gLc[j] * rcp(gam[rt][j][ii]) * acc[rt][j][ii];
           dG[rt][j][ii] -= kf * acc[rt][j][ii];
           cs += kf * acc[rt][j][ii];
         }
+      }
       gsum[j] = cs;
     }
     // G_L term of each column: sum_s K->_s dK->_s + Gamma_L sum_v S[v][k] dS'[v][k]
@@ -724,12 +728,14 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kmv = lds_tile(Km, rt, j);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           dK[rt][j][ii] += rcp(gam[rt][j][ii]) * acc[rt][j][ii];
-          dG[rt][j][ii] -= lds_el(Km, rt, j, ii) * acc[rt][j][ii];
+          dG[rt][j][ii] -= kmv[ii] * acc[rt][j][ii];
         }
+      }
   }
   __syncthreads();   // Q+ is dead: its slot takes dW
 
@@ -785,14 +791,16 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kpv = lds_tile(Kp, rt, j);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * rt + 4 * lg + ii;
           if (r < n) dv[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(acc[rt][j][ii]);
           dK[rt][j][ii] += gam[rt][j][ii] * acc2[rt][j][ii];
-          dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * acc2[rt][j][ii];
+          dG[rt][j][ii] += kpv[ii] * acc2[rt][j][ii];
         }
+      }
   }
   __syncthreads();   // dT complete; dP no longer needed (its slot takes Z)
 
@@ -890,13 +898,15 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < CPW; ++j)
 #pragma unroll
-      for (int rt = 0; rt < NB; ++rt)
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kpv = lds_tile(Kp, rt, j), kmv = lds_tile(Km, rt, j);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const float g = gam[rt][j][ii];
           dK[rt][j][ii] += g * accp[rt][j][ii] + rcp(g) * accm[rt][j][ii];
-          dG[rt][j][ii] += lds_el(Kp, rt, j, ii) * accp[rt][j][ii] - lds_el(Km, rt, j, ii) * accm[rt][j][ii];
+          dG[rt][j][ii] += kpv[ii] * accp[rt][j][ii] - kmv[ii] * accm[rt][j][ii];
         }
+      }
   }
   __syncthreads();   // glt, dwp, dwq complete
 

@@ -156,6 +156,27 @@ __device__ __forceinline__ bf16x4 transpose_tile16(bf16x4 x_row4) {
   return r;
 }
 
+// X[r0 + 4 g + i][c0 + c] (i = 0..3) for lane c + 16 g, of a row-major bf16 matrix in
+// LDS (row stride ld, a multiple of 4): the accumulator layout of the tile at (r0, c0),
+// from one 8-byte read of row r0 + c, columns c0 + 4 g .. + 3, and a product with the
+// identity as above (exact), in place of four 2-byte column reads.
+__device__ __forceinline__ f32x4 lds_acc_tile(const bf16* m, int ld, int r0, int c0) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  const bf16x4 x = *reinterpret_cast<const bf16x4*>(m + (r0 + c) * ld + c0 + 4 * g);
+  i16x4 eye;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) eye[i] = (4 * g + i == c) ? (short)0x3F80 : (short)0;   // bf16 1.0
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, x), eye, z, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 lds_acc_tile(const float* m, int ld, int r0, int c0) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  f32x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = m[(r0 + 4 * g + i) * ld + c0 + c];
+  return x;
+}
+
 // fragment values e = 0..7 multiplied by (g0, g1)[e] (rounded once to the operand type)
 __device__ __forceinline__ Frag<bf16> scale_frag(const Frag<bf16>& f, f32x4 g0, f32x4 g1) {
   Frag<bf16> r;
