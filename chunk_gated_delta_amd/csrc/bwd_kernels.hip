@@ -577,10 +577,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-      for (int j = 0; j < CPW; ++j)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          Wn[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(-acc[rt][j][ii]);
+      for (int j = 0; j < CPW; ++j) lds_store_acc_tile(Wn, LDD, 16 * rt, 16 * (ct0 + j), -acc[rt][j]);
   }
   f32x4 accU[NB][CPW];
   zero_acc(accU);
@@ -592,10 +589,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
   for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-    for (int j = 0; j < CPW; ++j)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        Ur[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(accU[rt][j][ii]);
+    for (int j = 0; j < CPW; ++j) lds_store_acc_tile(Ur, LDD, 16 * rt, 16 * (ct0 + j), accU[rt][j]);
   Frag<T> fG[KD][CPW];                       // dS' fragments, scaled to dS' Diag(Gamma_L) for dU
   load_state_frags<T, D, CPW>(fG, dSvk, ct0);
   __syncthreads();   // -W no longer needed: its slot takes dO
@@ -625,10 +619,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-      for (int j = 0; j < CPW; ++j)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dUr[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(acc[rt][j][ii]);
+      for (int j = 0; j < CPW; ++j) lds_store_acc_tile(dUr, LDD, 16 * rt, 16 * (ct0 + j), acc[rt][j]);
   }
   KmajorPieces<T> pSk[KD][CPW], pDk[KD][CPW];   // S and dS' with rows k, for the key-owned products
   load_state_kmajor<T, D, CPW>(pSk, Svk, ct0);
@@ -747,10 +738,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
-      for (int j = 0; j < CPW; ++j)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          dWr[(16 * rt + 4 * lg + ii) * LDD + 16 * (ct0 + j) + lr] = to<T>(-acc[rt][j][ii]);
+      for (int j = 0; j < CPW; ++j) lds_store_acc_tile(dWr, LDD, 16 * rt, 16 * (ct0 + j), -acc[rt][j]);
   }
   __syncthreads();
 

@@ -177,6 +177,23 @@ __device__ __forceinline__ f32x4 lds_acc_tile(const float* m, int ld, int r0, in
   return x;
 }
 
+// The reverse: the lane's accumulator-layout values v[i] = X[r0 + 4 g + i][c0 + c] stored
+// into a row-major matrix in LDS.  bf16: rounded, turned into the row piece X[r0 + c][c0 +
+// 4 g .. + 3] by transpose_tile16 (which, given a tile's accumulator layout, returns its
+// row pieces), and written with one 8-byte store instead of four 2-byte ones.
+__device__ __forceinline__ void lds_store_acc_tile(bf16* m, int ld, int r0, int c0, f32x4 v) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  bf16x4 x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x4*>(m + (r0 + c) * ld + c0 + 4 * g) = transpose_tile16(x);
+}
+__device__ __forceinline__ void lds_store_acc_tile(float* m, int ld, int r0, int c0, f32x4 v) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m[(r0 + 4 * g + i) * ld + c0 + c] = v[i];
+}
+
 // fragment values e = 0..7 multiplied by (g0, g1)[e] (rounded once to the operand type)
 __device__ __forceinline__ Frag<bf16> scale_frag(const Frag<bf16>& f, f32x4 g0, f32x4 g1) {
   Frag<bf16> r;
