@@ -541,14 +541,12 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     for (int kk = 0; kk < D; kk += 32) mma(acc, frag<false>(Qp, LDD, 16 * i, kk), frag<false>(Km, LDD, 16 * j, kk));
     const int s = 16 * j + lr;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 16 * i + 4 * lg + ii;
-      Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
-      if (j < i) {
-        // the mirrored tile above the diagonal is zero in P and in dP (written later)
-        Pb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);
-        dPb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);
-      }
+    for (int ii = 0; ii < 4; ++ii) acc[ii] = (s <= 16 * i + 4 * lg + ii) ? acc[ii] : 0.f;
+    lds_store_acc_tile(Pb, LDL, 16 * i, 16 * j, acc);
+    if (j < i) {
+      // the mirrored tile above the diagonal is zero in P and in dP (written later)
+      lds_zero_tile(Pb, LDL, 16 * j, 16 * i);
+      lds_zero_tile(dPb, LDL, 16 * j, 16 * i);
     }
   }
   // state fragments for U = Ubar - W S^T
@@ -633,10 +631,8 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     for (int kk = 0; kk < D; kk += 32) mma(acc, frag<false>(dOr, LDD, 16 * i, kk), frag<false>(Ur, LDD, 16 * j, kk));
     const int s = 16 * j + lr;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 16 * i + 4 * lg + ii;
-      dPb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
-    }
+    for (int ii = 0; ii < 4; ++ii) acc[ii] = (s <= 16 * i + 4 * lg + ii) ? acc[ii] : 0.f;
+    lds_store_acc_tile(dPb, LDL, 16 * i, 16 * j, acc);
   }
   __syncthreads();
 
@@ -754,13 +750,11 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     }
     const int s = 16 * j + lr;
     float cs = 0.f;
+    const f32x4 tv = lds_acc_tile(Tb, LDL, 16 * i, 16 * j);
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int r = 16 * i + 4 * lg + ii;
-      dTb[r * LDL + s] = to<T>(acc[ii] * wL[s]);
-      cs += tof(Tb[r * LDL + s]) * acc[ii];
-      if (j < i) dTb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);   // mirrored tile: zero
-    }
+    for (int ii = 0; ii < 4; ++ii) cs += tv[ii] * acc[ii];
+    lds_store_acc_tile(dTb, LDL, 16 * i, 16 * j, acc * wL[s]);
+    if (j < i) lds_zero_tile(dTb, LDL, 16 * j, 16 * i);   // mirrored tile: zero
     cs += __shfl_xor(cs, 16);
     cs += __shfl_xor(cs, 32);
     if (lg == 0) {
@@ -799,9 +793,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < LC; kk += 32) mma(acc, frag<false>(dTb, LDL, 16 * i, kk), frag<false>(Tb, LDL, 16 * j, kk));
-    const int s = 16 * j + lr;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) Zb[(16 * i + 4 * lg + ii) * LDL + s] = to<T>(acc[ii]);
+    lds_store_acc_tile(Zb, LDL, 16 * i, 16 * j, acc);
   }
   __syncthreads();
   // b at the lane's gradient positions, for db = dlog a / b; loaded here so that the
@@ -850,15 +842,16 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
       if (t < NTRI) {
         int i, j;
         tri_index(t, i, j);
-        const int s = 16 * j + lr;
+        f32x4 v;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int r = 16 * i + 4 * lg + ii;
-          dAb[r * LDL + s] = to<T>(wL[r] * dA[u][ii]);
-          if (j < i) {
-            // mirrored tile above the diagonal: zero, and no row-sum contribution
-            dAb[(16 * j + 4 * lg + ii) * LDL + 16 * i + lr] = to<T>(0.f);
-            if (lr == 0) dwq[i * LC + 16 * j + 4 * lg + ii] = 0.f;
+        for (int ii = 0; ii < 4; ++ii) v[ii] = wL[16 * i + 4 * lg + ii] * dA[u][ii];
+        lds_store_acc_tile(dAb, LDL, 16 * i, 16 * j, v);
+        if (j < i) {
+          // mirrored tile above the diagonal: zero, and no row-sum contribution
+          lds_zero_tile(dAb, LDL, 16 * j, 16 * i);
+          if (lr == 0) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) dwq[i * LC + 16 * j + 4 * lg + ii] = 0.f;
           }
         }
       }

@@ -193,6 +193,15 @@ __device__ __forceinline__ void lds_store_acc_tile(float* m, int ld, int r0, int
 #pragma unroll
   for (int i = 0; i < 4; ++i) m[(r0 + 4 * g + i) * ld + c0 + c] = v[i];
 }
+// A 16 x 16 tile of zeros at (r0, c0): every lane writes one row piece.
+__device__ __forceinline__ void lds_zero_tile(bf16* m, int ld, int r0, int c0) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  *reinterpret_cast<i16x4*>(m + (r0 + c) * ld + c0 + 4 * g) = i16x4{0, 0, 0, 0};
+}
+__device__ __forceinline__ void lds_zero_tile(float* m, int ld, int r0, int c0) {
+  const int lane = lane_id(), c = lane & 15, g = lane >> 4;
+  *reinterpret_cast<f32x4*>(m + (r0 + c) * ld + c0 + 4 * g) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
 // fragment values e = 0..7 multiplied by (g0, g1)[e] (rounded once to the operand type)
 __device__ __forceinline__ Frag<bf16> scale_frag(const Frag<bf16>& f, f32x4 g0, f32x4 g1) {
