@@ -500,17 +500,19 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) mma(acc, fa[m][kk], fb[m][kk]);
       const int s = 16 * j + lr;
+      if (isA) {
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int r = 16 * i + 4 * lg + ii;
-        if (isA) {
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * i + 4 * lg + ii;
           Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
-        } else {
-          Pb[r * LDL + s] = to<T>((s <= r) ? acc[ii] : 0.f);
-          // the products with P run over 32-token blocks: block (i, i+1) of an even row
-          // tile i is read by them and must be zero
-          if (j == i && i % 2 == 0 && i + 1 < NB) Pb[r * LDL + s + 16] = to<T>(0.f);
         }
+      } else {
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc[ii] = (s <= 16 * i + 4 * lg + ii) ? acc[ii] : 0.f;
+        lds_store_acc_tile(Pb, LDL, 16 * i, 16 * j, acc);
+        // the products with P run over 32-token blocks: block (i, i+1) of an even row
+        // tile i is read by them and must be zero
+        if (j == i && i % 2 == 0 && i + 1 < NB) lds_zero_tile(Pb, LDL, 16 * i, 16 * (i + 1));
       }
     }
   }
@@ -601,9 +603,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       for (int kb = 0; kb <= i / 2; ++kb) pa[i][kb] = load_frag(Pb + (16 * i + lr) * LDL + 32 * kb + 8 * lg);
     f32x4 aq[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) aq[i][ii] = tof(Qp[(16 * i + 4 * lg + ii) * LDD + col]);
+    for (int i = 0; i < NB; ++i) aq[i] = lds_acc_tile(Qp, LDD, 16 * i, 16 * ct);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       f32x4 ao = {0.f, 0.f, 0.f, 0.f};
@@ -625,8 +625,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     if (isO) {
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) acc[ii] = tof(Qp[(r + ii) * LDD + col]);
+      acc = lds_acc_tile(Qp, LDD, 16 * i, 16 * ct);
     }
     const T* Bs = isO ? UbTs : WnT;
     for (int kk = 0; kk < 16 * (i + 1); kk += 32) {
