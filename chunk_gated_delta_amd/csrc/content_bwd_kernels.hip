@@ -53,62 +53,113 @@ __global__ __launch_bounds__(256) void add_grad_mean_kernel(ContentBwdArgs a, co
 // db (w.r.t. the gate probability, from the chunk-gradient kernel) -> db_x in place,
 // then the projection's gradients and the output-gradient term g of period p-1, which
 // is added at once to that period's dO (into dOp; period 0's dm goes to m0).
-// The rank contractions run 16 lanes per rank index with DPP row sums.
+// Nothing this kernel loads depends on what it computes, so every load is issued at the
+// start (db and b of the first 64 tokens, U1 and U2 for LDS, m_{p-1}, the running dU
+// sums, the first 64 tokens of period p-1's dO): one round trip to memory instead of one
+// per phase.  The rank contractions run 16 lanes per rank index with DPP row sums.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a, const T* dO, T* dOp) {
-  __shared__ float dzp[256];
-  __shared__ float dz[D], gS[D];
-  __shared__ float rS[64], drS[64];
+  constexpr int NT = 256, NPART = NT / D, TPT = 64 / NPART;   // tokens per thread in a 64-token batch
+  constexpr int RMAX = 64, UPT = RMAX * D / NT;                // projection elements per thread, at most
+  constexpr int OP = 64 * D / 4 / NT;                          // 4-element dO pieces per thread, 64 tokens
+  extern __shared__ float Us[];                                // U1 [R][D], then U2 [D][R]
+  __shared__ float dzp[NT];
+  __shared__ float dz[D], gS[D], mS[D];
+  __shared__ float rS[RMAX], drS[RMAX];
   const int bh = blockIdx.x, h = bh % a.H, tid = threadIdx.x;
   const int t0 = a.p * a.L, t1 = min(t0 + a.L, a.T);
-  // dx = db * b (1 - b), summed over the period's tokens per key column
-  constexpr int NPART = 256 / D;
   const int k = tid % D, part = tid / D;
-  // (in batches of 8 tokens whose loads are all issued before the stores: the
-  // compiler cannot reorder a load past a store to a buffer that might alias it)
-  float acc = 0.f;
-  for (int tb = t0 + part; tb < t1; tb += 8 * NPART) {
-    float bv[8], gv[8];
+  const bool proj = a.U1 != nullptr;
+  const int R = proj ? a.R : 0, RD = R * D;
+  const float* m = a.m_all + ((size_t)bh * a.NP + a.p) * D;    // m_{p-1}
+  float* dU1p = a.dU1p + (size_t)bh * RD;                      // [R][D]
+  float* dU2p = a.dU2p + (size_t)bh * RD;                      // [D][R]
+  float* U1s = Us;
+  float* U2s = Us + RD;
+
+  // ---- every load
+  float bv[TPT], gv[TPT];
+  auto load_batch = [&](int tb) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = min(tb + j * NPART, t1 - 1);
+    for (int j = 0; j < TPT; ++j) {
+      const int t = min(tb + part + NPART * j, t1 - 1);
       const size_t i = ((size_t)bh * a.T + t) * D + k;
       bv[j] = a.bmat[i];
       gv[j] = a.dbx[i];
     }
+  };
+  load_batch(t0);
+  // Unconditional loads from clamped indices (without a projection, from b: any valid
+  // address; the values past RD are never used).  A branch around a load makes the
+  // compiler copy its result at the join, which waits for every load issued before it.
+  float u1[UPT], u2[UPT], du1[UPT], du2[UPT];
+  const float* U1g = proj ? a.U1 + (size_t)h * RD : a.bmat;
+  const float* U2g = proj ? a.U2 + (size_t)h * RD : a.bmat;
+  const float* dU1g = proj ? dU1p : a.bmat;
+  const float* dU2g = proj ? dU2p : a.bmat;
+  const int ilast = max(RD - 1, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = tb + j * NPART;
+  for (int j = 0; j < UPT; ++j) {
+    const int i = min(tid + NT * j, ilast);
+    u1[j] = U1g[i];
+    u2[j] = U2g[i];
+    du1[j] = dU1g[i];
+    du2[j] = dU2g[i];
+  }
+  const float mv = m[min(tid, D - 1)];
+  const bool addg = a.p > 0;
+  // period p-1 (whole) when there is one; period 0's tokens are loaded in vain otherwise
+  const size_t obase = ((size_t)bh * a.T + (size_t)(addg ? a.p - 1 : 0) * a.L) * D;
+  const int n4 = a.L * D / 4, nl4 = addg ? n4 : (t1 - t0) * D / 4;   // pieces that exist
+  f32x4 ov[OP];
+#pragma unroll
+  for (int j = 0; j < OP; ++j) ov[j] = load4f(dO + obase + 4 * min(tid + NT * j, nl4 - 1));
+#pragma unroll
+  for (int j = 0; j < UPT; ++j) {
+    const int i = tid + NT * j;
+    if (i < RD) {
+      U1s[i] = u1[j];
+      U2s[i] = u2[j];
+    }
+  }
+  if (tid < D) mS[tid] = mv;
+
+  // ---- dx = db * b (1 - b), written back as d/db_x and summed over the period's tokens
+  // per key column (each thread in token order)
+  float acc = 0.f;
+  for (int tb = t0;;) {
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      const int t = tb + part + NPART * j;
       if (t < t1) {
         const float dx = gv[j] * bv[j] * (1.f - bv[j]);
         a.dbx[((size_t)bh * a.T + t) * D + k] = dx;
         acc += dx;
       }
     }
+    tb += 64;
+    if (tb >= t1) break;
+    load_batch(tb);
   }
   dzp[tid] = acc;
   __syncthreads();
   if (tid < D) {
-    float s = 0.f;
+    float sum = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < NPART; ++pp) s += dzp[pp * D + tid];
-    dz[tid] = s;
+    for (int pp = 0; pp < NPART; ++pp) sum += dzp[pp * D + tid];
+    dz[tid] = sum;
   }
-  const bool proj = a.U1 != nullptr;
-  const float* m = a.m_all + ((size_t)bh * a.NP + a.p) * D;      // m_{p-1}
-  const float* U1 = proj ? a.U1 + (size_t)h * a.R * D : nullptr;  // [R][D]
-  const float* U2 = proj ? a.U2 + (size_t)h * D * a.R : nullptr;  // [D][R]
   __syncthreads();
   if (proj) {
     // r = U1 m and dr = U2^T dz: lanes 16 r' .. 16 r' + 15 of a row share rank index r'
     constexpr int PER = D / 16;
-    for (int idx = tid; idx < 16 * a.R; idx += 256) {
+    for (int idx = tid; idx < 16 * R; idx += NT) {
       const int r = idx >> 4, c = (idx & 15) * PER;
       float x = 0.f, y = 0.f;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        x += U1[r * D + c + j] * m[c + j];
-        y += U2[(c + j) * a.R + r] * dz[c + j];
+        x += U1s[r * D + c + j] * mS[c + j];
+        y += U2s[(c + j) * R + r] * dz[c + j];
       }
       x = row16_sum(x);
       y = row16_sum(y);
@@ -118,50 +169,35 @@ __global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a,
       }
     }
     __syncthreads();
-    float* dU2p = a.dU2p + (size_t)bh * D * a.R;
-    float* dU1p = a.dU1p + (size_t)bh * a.R * D;
-    for (int i0 = tid; i0 < D * a.R; i0 += 4 * 256) {
-      float u2[4], u1[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = min(i0 + 256 * j, D * a.R - 1);
-        u2[j] = dU2p[i];
-        u1[j] = dU1p[i];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + 256 * j;
-        if (i < D * a.R) {
-          dU2p[i] = u2[j] + dz[i / a.R] * rS[i % a.R];
-          dU1p[i] = u1[j] + drS[i / D] * m[i % D];
-        }
+    for (int j = 0; j < UPT; ++j) {
+      const int i = tid + NT * j;
+      if (i < RD) {
+        dU2p[i] = du2[j] + dz[i / R] * rS[i % R];
+        dU1p[i] = du1[j] + drS[i / D] * mS[i % D];
       }
     }
   }
   if (tid < D) {
     float dm = 0.f;
-    if (proj)
-      for (int r = 0; r < a.R; ++r) dm += U1[r * D + tid] * drS[r];
-    if (a.p > 0) gS[tid] = dm / (float)a.L;      // period p-1 is whole
+    for (int r = 0; r < R; ++r) dm += U1s[r * D + tid] * drS[r];
+    if (addg) gS[tid] = dm / (float)a.L;
     else if (a.dm0) a.dm0[(size_t)bh * D + tid] = dm;
   }
-  if (a.p == 0) return;
+  if (!addg) return;
   __syncthreads();
   // dO + g for the tokens of period p-1
-  const size_t base = ((size_t)bh * a.T + (size_t)(a.p - 1) * a.L) * D;
-  const int n4 = a.L * D / 4;
-  for (int i0 = tid; i0 < n4; i0 += 8 * 256) {
-    f32x4 x[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = load4f(dO + base + 4 * min(i0 + 256 * j, n4 - 1));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + 256 * j;
-      if (i < n4) {
-        const int col = (4 * i) % D;
-        store4(dOp + base + 4 * i, x[j] + f32x4{gS[col], gS[col + 1], gS[col + 2], gS[col + 3]});
-      }
+  for (int j = 0; j < OP; ++j) {
+    const int i = tid + NT * j;
+    if (i < n4) {
+      const int col = (4 * i) % D;
+      store4(dOp + obase + 4 * i, ov[j] + f32x4{gS[col], gS[col + 1], gS[col + 2], gS[col + 3]});
     }
+  }
+  for (int i = tid + NT * OP; i < n4; i += NT) {              // periods longer than 64 tokens
+    const int col = (4 * i) % D;
+    store4(dOp + obase + 4 * i, load4f(dO + obase + 4 * i) + f32x4{gS[col], gS[col + 1], gS[col + 2], gS[col + 3]});
   }
 }
 
@@ -268,16 +304,19 @@ hipError_t launch_add_grad_mean(const ContentBwdArgs& a, int dtype, const void* 
   return hipGetLastError();
 }
 
+template <typename T, int D>
+static hipError_t gate_bwd_launch_d(const ContentBwdArgs& a, const void* dO, void* dOp, hipStream_t st) {
+  const size_t lds = 2 * sizeof(float) * (a.U1 ? a.R : 0) * D;   // U1 and U2 of the head
+  auto kern = content_gate_bwd_kernel<T, D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)(2 * sizeof(float) * 64 * D));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(256), lds, st, a, reinterpret_cast<const T*>(dO), reinterpret_cast<T*>(dOp));
+  return hipGetLastError();
+}
 template <typename T>
 static hipError_t gate_bwd_launch(const ContentBwdArgs& a, const void* dO, void* dOp, hipStream_t st) {
-  const dim3 grid(a.B * a.H);
-  if (a.D == 128)
-    hipLaunchKernelGGL((content_gate_bwd_kernel<T, 128>), grid, dim3(256), 0, st, a,
-                       reinterpret_cast<const T*>(dO), reinterpret_cast<T*>(dOp));
-  else
-    hipLaunchKernelGGL((content_gate_bwd_kernel<T, 64>), grid, dim3(256), 0, st, a,
-                       reinterpret_cast<const T*>(dO), reinterpret_cast<T*>(dOp));
-  return hipGetLastError();
+  return a.D == 128 ? gate_bwd_launch_d<T, 128>(a, dO, dOp, st) : gate_bwd_launch_d<T, 64>(a, dO, dOp, st);
 }
 
 hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, int dtype, const void* dO, void* dOp, hipStream_t st) {
