@@ -148,8 +148,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   }
   // three operand buffers, loaded two chunks ahead (chunks run last to first); a
   // chunk's factors are staged in LDS during the step before its own.  Chunks below
-  // the last one run in a branch-free main loop with clamped prefetch (a clamped
-  // buffer re-stages a chunk already done, which nothing reads).
+  // the last one run in a main loop with clamped prefetch.
   constexpr int PF = 3;
   // chunk range (all chunks unless a sub-range is asked for)
   const int clo = a.c_lo, chi = a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1, nch = chi - clo + 1;
@@ -211,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    nxt.stage(Wl, Ql, Kl);
+    if (c > clo) nxt.stage(Wl, Ql, Kl);   // (the last chunk has no successor to stage)
     // dS^T <- Diag(Gamma_L) dS^T + (-W)^T X^T + Q~^T dO
 #pragma unroll
     for (int j = 0; j < SPW; ++j) {

@@ -75,6 +75,10 @@ CASES = [
     ("bf16", 1, 2, 320, 128, 128),
     ("bf16", 2, 1, 100, 64, 32),
     ("f32", 1, 1, 96, 128, 32),
+    # periods longer than the gate kernel's 64-token batch: a partial second batch, and
+    # three batches with a short last period
+    ("f32", 1, 2, 200, 64, 96),
+    ("bf16", 1, 1, 400, 128, 192),
 ]
 
 
