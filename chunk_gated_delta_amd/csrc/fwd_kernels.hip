@@ -580,6 +580,10 @@ __global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs
     __syncthreads();
     prep_compute<T, LC, D, ContentGates, kPrepFwd, NT>(a, gates, bh, c, (size_t)bh, smem);
     __syncthreads();
+    // the chunk's factors (just written by this workgroup) are loaded before the state's
+    // LDS copy is rebuilt, so that their round trip overlaps it
+    ChunkOps<T, LC, D, D, true, NW> op;
+    op.load(a, (size_t)bh, 0);
     if (c == 0) {
       state_init<T, D, D, NW>(a, bh, 0, S, reinterpret_cast<T*>(smem));
       __syncthreads();
@@ -596,8 +600,6 @@ __global__ __launch_bounds__(64 * kContentWaves) void fwd_content_kernel(FwdArgs
       __syncthreads();
     }
     float* cs = reinterpret_cast<float*>(smem + StateLayout<T, LC, D, D>::bytes - sizeof(float) * NB * D);
-    ChunkOps<T, LC, D, D, true, NW> op;
-    op.load(a, (size_t)bh, 0);
     state_chunk<T, LC, D, D, true, false, NW>(a, bh, c, 0, op, S, smem, cs);
     prep_stage_load<T, LC, D, ContentGates, NT>(a, gates, bh, min(c + 1, a.NC - 1), st);   // (the last reloads itself)
     // fold this chunk's column sums into the period sum (fixed order over row tiles)
