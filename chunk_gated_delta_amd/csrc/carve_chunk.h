@@ -112,13 +112,14 @@ __device__ __forceinline__ void tri_index(int t, int& i, int& j) {
 // with the scaled blocks T_ii A_im formed first (all in parallel) and the T_ij
 // by increasing distance i - j.  The strictly lower blocks of A are overwritten;
 // the blocks of T above the diagonal are not written.
-// Kept out of line (inlined, its registers would add to the prefetched next chunk's
-// in the persistent prep loop), with LDS-typed pointers so that every access is an
-// LDS instruction.  An out-of-line function starts by waiting for all of its caller's
-// outstanding memory operations, so callers issue prefetches after this call.
+// LDS-typed pointers, so that every access is an LDS instruction.  triangular_inverse
+// is the out-of-line copy (used where inlining would add its registers to those of the
+// chunk prefetched in the persistent loop, or to the content-aware kernel's, and spill);
+// an out-of-line function starts by waiting for all of its caller's outstanding memory
+// operations, so callers issue prefetches after the call.
 typedef __attribute__((address_space(3))) float lds_float;
 template <int LC, int LDF, int NT = kThreads>
-__device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_float* Tf) {
+__device__ __forceinline__ void triangular_inverse_inl(lds_float* Af, lds_float* Tf) {
   constexpr int NB = LC / 16;
   static_assert(NT / 64 >= NB - 1, "one wave per off-diagonal block of a distance");
   static_assert(LDF % 4 == 0, "rows of A are read as 16-byte pieces");
@@ -178,6 +179,10 @@ __device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_
     }
     __syncthreads();
   }
+}
+template <int LC, int LDF, int NT = kThreads>
+__device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_float* Tf) {
+  triangular_inverse_inl<LC, LDF, NT>(Af, Tf);
 }
 
 // ------------------------------------------------------------------ gate sources
@@ -520,7 +525,11 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
 
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
   // modes also keep that copy of the chunk (row-major [LC][LC])
-  triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
+  // inlined in the modes that keep T for the backward: there the out-of-line call's wait
+  // for the gate pass's K->^T stores cost more than the extra registers (measured; the
+  // forward-only and content-aware prep keep the call)
+  if constexpr (BWD) triangular_inverse_inl<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
+  else triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
   after_solve();
   for (int idx = tid; idx < LC * LC / 4; idx += NT) {
     const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
