@@ -232,15 +232,29 @@ __global__ __launch_bounds__(256) void logit_grads_kernel(LogitGradArgs a) {
   const int k = tid % D, part = tid / D, nparts = 256 / D;
   const float A = a.A[h * D + k], tau = a.tau[h * D + k];
   const int t0 = tb * kLogitBlock, t1 = min(t0 + kLogitBlock, a.T);
+  // tokens t0 + part + nparts j, eight at a time: the loads of a batch are issued before
+  // its stores (the compiler cannot move a load past a store to df, which it must assume
+  // may alias f); the sums run in token order
   float sa = 0.f, st = 0.f;
-  for (int t = t0 + part; t < t1; t += nparts) {
-    const size_t i = ((size_t)bh * a.T + t) * D + k;
-    const float y = a.f[i] + tau;
-    const float dlg = a.df[i];
-    const float df = -dlg * A * sigmoidf(y);
-    a.df[i] = df;
-    st += df;
-    sa -= dlg * softplusf(y);
+  for (int tb = t0 + part; tb < t1; tb += 8 * nparts) {
+    float fv[8], dv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t i = ((size_t)bh * a.T + min(tb + nparts * u, t1 - 1)) * D + k;
+      fv[u] = a.f[i];
+      dv[u] = a.df[i];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = tb + nparts * u;
+      if (t < t1) {
+        const float y = fv[u] + tau;
+        const float df = -dv[u] * A * sigmoidf(y);
+        a.df[((size_t)bh * a.T + t) * D + k] = df;
+        st += df;
+        sa -= dv[u] * softplusf(y);
+      }
+    }
   }
   pa[tid] = sa;
   pt[tid] = st;
@@ -257,15 +271,30 @@ __global__ __launch_bounds__(256) void logit_grads_kernel(LogitGradArgs a) {
   }
 }
 
-// out[h][k] = sum over the batch and token blocks of part[(b*H + h) * nblk + tb][k]
-__global__ __launch_bounds__(256) void sum_heads_kernel(const float* part, float* out, int B, int H, int nblk, int D) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= H * D) return;
-  const int h = i / D, k = i % D;
+// outX[h][k] = sum over the batch and token blocks of partX[(b*H + h) * nblk + tb][k], for
+// X = A (threads 0 .. H*D-1) and X = tau (the next H*D); summed in the order b, tb, with
+// the loads issued eight at a time
+__global__ __launch_bounds__(256) void sum_heads_kernel(const float* partA, const float* partT, float* outA,
+                                                        float* outT, int B, int H, int nblk, int D) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * H * D) return;
+  const bool isA = i < H * D;
+  if (!isA) i -= H * D;
+  const float* part = isA ? partA : partT;
+  const int h = i / D, k = i % D, n = B * nblk;
   float s = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int tb = 0; tb < nblk; ++tb) s += part[(((size_t)b * H + h) * nblk + tb) * D + k];
-  out[i] = s;
+  for (int j0 = 0; j0 < n; j0 += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, n - 1), b = j / nblk, tb = j % nblk;
+      x[u] = part[(((size_t)b * H + h) * nblk + tb) * D + k];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < n) s += x[u];
+  }
+  (isA ? outA : outT)[i] = s;
 }
 
 hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hipStream_t st) {
@@ -273,9 +302,8 @@ hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hi
   hipLaunchKernelGGL(logit_grads_kernel, dim3(a.B * a.H, nblk), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned g = (unsigned)((a.H * a.D + 255) / 256);
-  hipLaunchKernelGGL(sum_heads_kernel, dim3(g), dim3(256), 0, st, a.partA, dA, a.B, a.H, nblk, a.D);
-  hipLaunchKernelGGL(sum_heads_kernel, dim3(g), dim3(256), 0, st, a.partT, dtau, a.B, a.H, nblk, a.D);
+  const unsigned g = (unsigned)((2 * a.H * a.D + 255) / 256);
+  hipLaunchKernelGGL(sum_heads_kernel, dim3(g), dim3(256), 0, st, a.partA, a.partT, dA, dtau, a.B, a.H, nblk, a.D);
   return hipGetLastError();
 }
 
