@@ -12,6 +12,7 @@
 //      the coupling's dB, then the key-axis retention through a reverse cumulative
 //      sum of dlog a inside the chunk).
 // Gradients are w.r.t. log g, the erase probability b and the write strength w.
+#include <algorithm>
 #include <type_traits>
 
 #include "carve_chunk.h"
@@ -30,8 +31,6 @@ __device__ __forceinline__ Frag<T> frag(const T* base, int ld, int row0, int k0)
   else return lds_frag_cols(base, ld, row0, k0);
 }
 
-__device__ __forceinline__ bf16 frag_elem(const Frag<bf16>& f, int e) { return f.v[e]; }
-__device__ __forceinline__ float frag_elem(const Frag<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
 
 // ------------------------------------------------------------------ reverse state pass
 // LDS: the dtype copy of the dS^T slice [VS][D], X^T [VS][LC], the chunk's dO slice
@@ -255,14 +254,28 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ chunk gradients
 // LDS slots (reused as the computation proceeds; "row-major" = [token][width]):
-//   s0 K+            s1 K-            s2 Q+ -> dW        s3 V (raw)
+//   s0 K^+           s1 K^-           s2 Q^+ -> dW       s3 V (raw)
 //   s4 -W -> dO      s5 U             s6 dU
-//   (s4..s6 first stage the fp32 log g and b of the chunk)
-//   p0 P -> dT        p1 T (dtype)     p2 Tw = T diag(w)  p3 dP -> Z -> dA
-// T = (I + A)^-1 itself comes from the prep pass (dtype, one LC x LC block per chunk).
+//   (s4..s5 first stage the fp32 log-retention la of the chunk, then the block-local G)
+//   p0 P -> dT       p1 T (dtype)     p2 Tw = T diag(w) -> e^(G_L - Gb[J+1]) -> e^Gb
+//   p3 block log-retention table -> dP -> Z -> dA
+// T = (I + A)^-1, P and the coupling B come from the prep pass.  The gate algebra is
+// the prep pass's (carve_chunk.h): G is the cumulative log-retention inside the chunk,
+// Gb[I] its value at the start of 16-token block I, btot_I the block's log-retention,
+// loc = G - Gb[I] <= 0, and the operands
+//   K^+ = k e^loc, Q^+ = q e^loc, K^- = k e^(btot - loc)
+// (row operands referred to their block start, column operands to their block end).
+// A ratio-weighted product over the tokens s of blocks J <= I, such as
+//   X_r = sum_s dB_rs k_s Gamma_r/Gamma_s = e^loc_r sum_J D_IJ (dB_IJ K^-_J)_r,
+// runs one 16-token block J at a time, with the per-key-channel factor
+// D_IJ = e^(Gb[I] - Gb[J+1]) (1 for J = I - 1, <= 1 for J < I - 1, e^-btot_I on the
+// diagonal) applied to the fp32 result: every operand is rounded once.  A diagonal block
+// whose log-retention falls below -kSafeLog in some channel leaves out its 16-deep
+// product; the kernel stores that block's diagonal tiles of dP and dB, and the fix-up
+// pass (bwd_diag_fix_kernel) adds the exact elementwise terms.
 // Tiles of [token][key] and [token][value] results are owned by column: wave w
 // computes every token tile of key/value tiles ct = w*CPW .. w*CPW+CPW-1, so the
-// cumulative retention Gamma of those columns stays in that wave's registers
+// block-local log-retention of those columns stays in that wave's registers
 // (accumulator layout) for the elementwise tail and the reverse cumulative sum.
 template <typename T, int LC, int D>
 struct GradLayout {
@@ -276,8 +289,8 @@ struct GradLayout {
   static constexpr size_t S2 = al(sizeof(T) * LC * LDL);
   static constexpr size_t slot(int i) { return S1 * i; }
   static constexpr size_t pslot(int i) { return 7 * S1 + S2 * i; }
-  static constexpr size_t small = 7 * S1 + 4 * S2;                  // w, Gamma_L, dw partials, G_L term
-  static constexpr size_t bytes = small + sizeof(float) * (LC + D + 2 * NB * LC + D);
+  static constexpr size_t small = 7 * S1 + 4 * S2;   // w, Gamma_L, dw partials, G_L term, block flags
+  static constexpr size_t bytes = small + sizeof(float) * (LC + D + 2 * NB * LC + D) + 16 * sizeof(int);
 };
 
 // Operand sources for the column-owned products below: a fragment of rows
@@ -353,11 +366,153 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[NB][CPW]) {
 }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// LG: the gates come as pre-activations (log_g holds f, b holds b_x, w holds w_hat);
-// they are activated when staged, and the kernel returns d/db_x and d/dw_hat in place
-// of d/db and d/dw (d/dlog g stays, for the logit pass to turn into d/df).
+// Block-wise column-owned products, one 16-token contraction block at a time with the
+// lane's factor applied to the fp32 result (see the layout notes above):
+//   LOWER: acc[I][j] += sc(I, J, j) * (A_{I,J} B_{J,col})   for J <= I   (output rows I)
+//   UPPER: acc[J][j] += sc(I, J, j) * (A_{J,I} B_{I,col})   for I >= J   (output rows J)
+// A16(output block, contraction block) and B16(contraction block, column tile) give
+// 16-deep fragments; sc(I, J, j) is the lane's factor for its column of tile ct0 + j.
+template <typename T, int NB, int CPW, bool LOWER, typename ASrc, typename BSrc, typename Sc>
+__device__ __forceinline__ void owned_mma_blk(f32x4 (&acc)[NB][CPW], const ASrc& A16, const BSrc& B16, int ct0,
+                                              const Sc& sc) {
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+    Frag16<T> bf[CPW];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) bf[j] = B16(kb, ct0 + j);
+#pragma unroll
+    for (int ob = 0; ob < NB; ++ob) {
+      if (LOWER ? kb > ob : kb < ob) continue;
+      const Frag16<T> af = A16(ob, kb);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        mma16(t, af, bf[j]);
+        acc[ob][j] += (LOWER ? sc(ob, kb, j) : sc(kb, ob, j)) * t;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ within-block terms
+// Exact within-block terms for the 16-token blocks (bits of mask) of a range-safe chunk
+// whose log-retention left the fast tiles' range (the chunk's 16-deep products left them
+// out and stored the blocks' diagonal tiles of dP and dB = diag(w) dA).  For block I, key
+// column ch and r, s in the block, with R_rs = prod_{t=s+1..r} a_t formed as running
+// products of the retention:
+//   x2_r = sum_{s<=r} dP_rs k_s R_rs,   x1_r = sum_{s<r} dB_rs k_s R_rs,
+//   x3_s = sum_{r>=s} (dP_rs q_r + dB_rs k_r) R_rs,
+// dq_r += x2_r and dk_r += x1_r + x3_r; the gradient w.r.t. the cumulative
+// log-retention gains q_r x2_r + k_r x1_r - k_r x3_r, whose reverse cumulative sum over
+// the chunk's tokens is added to dlog g (and, through the erase factor, to db).  k, q and
+// the retention come from global memory with the staging's gate arithmetic; the chunk's
+// own gradients are read back (same workgroup, after a barrier).  Every thread of the
+// workgroup (NT) takes part in the barriers and the staging; threads 0 .. D-1 take one
+// key column each.  tl: 2 x 16 x 17 + 3 x 16 x (D + 1) floats of free LDS.
+template <typename T, int LC, int D, bool HAS_B, bool LG, int NT>
+__device__ __forceinline__ void diag_fix_chunk(const BwdArgs& a, int bh, int c, int mask, float* tl) {
+  constexpr int NB = LC / 16, LDC = D + 1;
+  static_assert(NT >= D, "one thread per key column");
+  const FwdArgs& f = a.fwd;
+  const int ch = threadIdx.x;
+  const bool col = ch < D;
+  const size_t ci = (size_t)bh * f.NC + c;
+  const T* kg = reinterpret_cast<const T*>(f.k);
+  const T* qg = reinterpret_cast<const T*>(f.q);
+  T* dq = reinterpret_cast<T*>(a.dq);
+  T* dk = reinterpret_cast<T*>(a.dk);
+  float* aS = tl + 2 * 16 * 17;     // [16][LDC] retention a of the block, per column
+  float* kS = aS + 16 * LDC;        // [16][LDC] k
+  float* qS = kS + 16 * LDC;        // [16][LDC] q
+  const int n = min(LC, f.T - c * LC);
+  const size_t row0 = (size_t)bh * f.T + (size_t)c * LC;
+  const int chc = min(ch, D - 1);
+  float gA = 0.f, gt = 0.f;
+  if constexpr (LG) {
+    gA = f.gA[(bh % f.H) * D + chc];
+    gt = f.gtau[(bh % f.H) * D + chc];
+  }
+  // the erase factor of dlog g in the erase gradient at token r (as in the chunk kernels)
+  auto efac = [&](size_t idx) -> float {
+    if constexpr (!HAS_B) return 0.f;
+    const float bvv = f.b[idx];
+    return LG ? sigmoidf(-bvv) : (a.db_mode ? 1.f - bvv : __builtin_amdgcn_rcpf(bvv));
+  };
+  float carry = 0.f;   // sum of the corrections of the later tokens
+  for (int I = NB - 1; I >= 0; --I) {
+    if (mask & (1 << I)) {
+      // the block's tiles, row-major [2][16][17], and a, k, q of every column
+      for (int e = threadIdx.x; e < 2 * 256; e += NT) {
+        const int which = e / 256, l = (e % 256) / 4, ii = e % 4;
+        tl[(which * 16 + 4 * (l / 16) + ii) * 17 + l % 16] =
+            tof(reinterpret_cast<const T*>(a.diag)[((ci * NB + I) * 2 + which) * 256 + e % 256]);
+      }
+      for (int e = threadIdx.x; e < 16 * D; e += NT) {
+        const int t = e / D, cc = e % D, r = 16 * I + t;
+        const bool valid = r < n;
+        const size_t idx = (row0 + (size_t)min(r, n - 1)) * D + cc;
+        const float lgv = f.log_g[idx];
+        float la = lgv;
+        if constexpr (LG) la = -f.gA[(bh % f.H) * D + cc] * softplusf(lgv + f.gtau[(bh % f.H) * D + cc]);
+        if constexpr (HAS_B) la += LG ? -softplusf(-f.b[idx]) : flog(f.b[idx]);
+        aS[t * LDC + cc] = valid ? fexp(clamp_la(la)) : 1.f;
+        kS[t * LDC + cc] = valid ? tof(kg[idx]) : 0.f;
+        qS[t * LDC + cc] = valid ? tof(qg[idx]) : 0.f;
+      }
+      __syncthreads();
+      if (col) {
+#pragma unroll 1
+        for (int r = 15; r >= 0; --r) {
+          // row role of row r (s <= r, running product downwards) and column role of
+          // column r (rows r' >= r, running product upwards)
+          float rho = 1.f, x1 = 0.f, x2 = 0.f;
+#pragma unroll 1
+          for (int s = r; s >= 0; --s) {
+            const float ks = kS[s * LDC + ch];
+            x2 += tl[r * 17 + s] * ks * rho;
+            x1 += tl[(16 + r) * 17 + s] * ks * rho;
+            rho *= aS[s * LDC + ch];
+          }
+          float x3 = 0.f;
+          rho = 1.f;
+#pragma unroll 1
+          for (int rr = r; rr < 16; ++rr) {
+            if (rr > r) rho *= aS[rr * LDC + ch];
+            x3 += (tl[rr * 17 + r] * qS[rr * LDC + ch] + tl[(16 + rr) * 17 + r] * kS[rr * LDC + ch]) * rho;
+          }
+          const float kr = kS[r * LDC + ch];
+          carry += qS[r * LDC + ch] * x2 + kr * (x1 - x3);
+          const int tok = 16 * I + r;
+          if (tok < n) {
+            const size_t idx = row0 * D + (size_t)tok * D + ch;
+            dq[idx] = to<T>(tof(dq[idx]) + x2);
+            dk[idx] = to<T>(tof(dk[idx]) + x1 + x3);
+            a.dlog_g[idx] += carry;
+            if (HAS_B) a.db[idx] += carry * efac(idx);
+          }
+        }
+      }
+      __syncthreads();   // every read of this block's staging is done
+    } else if (col && carry != 0.f) {
+      for (int r = 15; r >= 0; --r) {
+        const int tok = 16 * I + r;
+        if (tok < n) {
+          const size_t idx = row0 * D + (size_t)tok * D + ch;
+          a.dlog_g[idx] += carry;
+          if (HAS_B) a.db[idx] += carry * efac(idx);
+        }
+      }
+    }
+  }
+  (void)gA;
+  (void)gt;
+}
+
+// Fast path of the chunk gradients (chunks whose log-retention stays within the fast
+// range, -kChunkSafe, in every key channel): the retention referred to the chunk start,
+// Gamma = running product of a inside the chunk, K+ = K Gamma, K- = K / Gamma, Q+ = Q Gamma.
 template <typename T, int LC, int D, bool HAS_B, bool LG>
-__global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_chunk_fast(const BwdArgs& a, unsigned char* smem) {
   using Lay = GradLayout<T, LC, D>;
   // one wave per 16-column tile of the key/value width: NW = D/16 waves
   constexpr int NW = D / 16, NT = 64 * NW;
@@ -365,7 +520,6 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int LDD = Lay::LDD, LDL = Lay::LDL;
   constexpr int NTRI = NB * (NB + 1) / 2;
   static_assert(NCT % NW == 0, "key tiles must split evenly over waves");
-  extern __shared__ __align__(16) unsigned char smem[];
   T* Kp = reinterpret_cast<T*>(smem + Lay::slot(0));
   T* Km = reinterpret_cast<T*>(smem + Lay::slot(1));
   T* Qp = reinterpret_cast<T*>(smem + Lay::slot(2));
@@ -490,7 +644,7 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * rt + 4 * lg + i;
-        const float av = __expf(lgS[r * LDG + col]) * (HAS_B ? bS[r * LDG + col] : 1.f);
+        const float av = fexp(lgS[r * LDG + col]) * (HAS_B ? bS[r * LDG + col] : 1.f);
         loc[i] = (i == 0) ? av : loc[i - 1] * av;
       }
       // product of the 4-row groups of this row tile held by lanes with smaller lg
@@ -865,8 +1019,9 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
       for (int rt = 0; rt < NB; ++rt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-          // d/db = dlog a / b; with pre-activations d/db_x = d/db * b (1 - b) = dlog a * sigmoid(-b_x)
-          binv[j][rt][ii] = LG ? sigmoidf(-binv[j][rt][ii]) : rcp(binv[j][rt][ii]);
+          // d/db = dlog a / b; with pre-activations d/db_x = d/db * b (1 - b) = dlog a * sigmoid(-b_x);
+          // for b = sigmoid(x) given as b (db_mode 1), d/dx = dlog a (1 - b)
+          binv[j][rt][ii] = LG ? sigmoidf(-binv[j][rt][ii]) : (a.db_mode ? 1.f - binv[j][rt][ii] : rcp(binv[j][rt][ii]));
   }
   // ---- dK+ += dB K-, dK- += dB^T K+
   {
@@ -941,6 +1096,686 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
     for (int t = 0; t < NB; ++t) s += dwq[t * LC + tid] + dwp[t * LC + tid];
     a.dw[row0 + tid] = LG ? s * wL[tid] * (1.f - wL[tid]) : s;     // d/dw_hat = d/dw * w (1 - w)
   }
+}
+
+// Range-safe path of the chunk gradients (chunks whose log-retention over the chunk
+// falls below -kChunkSafe in some key channel): operands referred to their 16-token
+// blocks, as described with the layout above.
+template <typename T, int LC, int D, bool HAS_B, bool LG>
+__device__ __forceinline__ void bwd_chunk_range(const BwdArgs& a, unsigned char* smem) {
+  using Lay = GradLayout<T, LC, D>;
+  // one wave per 16-column tile of the key/value width: NW = D/16 waves
+  constexpr int NW = D / 16, NT = 64 * NW;
+  constexpr int NB = LC / 16, NCT = D / 16, CPW = NCT / NW, KD = D / 32, KL = LC / 32;
+  constexpr int LDD = Lay::LDD, LDL = Lay::LDL;
+  constexpr int NTRI = NB * (NB + 1) / 2;
+  static_assert(NCT % NW == 0, "key tiles must split evenly over waves");
+  T* Kp = reinterpret_cast<T*>(smem + Lay::slot(0));
+  T* Km = reinterpret_cast<T*>(smem + Lay::slot(1));
+  T* Qp = reinterpret_cast<T*>(smem + Lay::slot(2));
+  T* dWr = Qp;
+  T* Vr = reinterpret_cast<T*>(smem + Lay::slot(3));
+  T* Wn = reinterpret_cast<T*>(smem + Lay::slot(4));
+  T* dOr = Wn;
+  T* Ur = reinterpret_cast<T*>(smem + Lay::slot(5));
+  T* dUr = reinterpret_cast<T*>(smem + Lay::slot(6));
+  T* Pb = reinterpret_cast<T*>(smem + Lay::pslot(0));
+  T* dTb = Pb;
+  T* Tb = reinterpret_cast<T*>(smem + Lay::pslot(1));
+  T* Twb = reinterpret_cast<T*>(smem + Lay::pslot(2));
+  float* cKT = reinterpret_cast<float*>(smem + Lay::pslot(2));   // [NB][D] e^(G_L - Gb[J+1]) once Tw is done
+  float* gbeT = cKT;                                               // [NB][D] e^Gb[J] for dT'
+  T* dPb = reinterpret_cast<T*>(smem + Lay::pslot(3));
+  float* btT = reinterpret_cast<float*>(smem + Lay::pslot(3));   // [NB][D] block log-retention (gate pass)
+  T* Zb = dPb;
+  T* dAb = dPb;
+  float* wL = reinterpret_cast<float*>(smem + Lay::small);
+  float* gLs = wL + LC;
+  float* dwp = gLs + D;            // [NB][LC] column sums of T .* dT' per token-tile row
+  float* dwq = dwp + NB * LC;      // [NB][LC] row sums of B .* dA per token-tile column
+  float* glt = dwq + NB * LC;      // [D] G_L term per key column
+  int* flags = reinterpret_cast<int*>(glt + D);   // [NB] block needs the exact within-block terms
+  static_assert(sizeof(float) * NB * D * 2 <= Lay::S2, "gate tables exceed a tile slot");
+
+  const FwdArgs& f = a.fwd;
+  const int c = a.c_lo + blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+  const int ct0 = wave * CPW;      // first key/value tile owned by this wave
+  const int n = min(LC, f.T - c * LC);
+  const size_t ci = (size_t)bh * f.NC + c;
+  const size_t row0 = (size_t)bh * f.T + (size_t)c * LC;
+  const T* q = reinterpret_cast<const T*>(f.q);
+  const T* k = reinterpret_cast<const T*>(f.k);
+  const T* v = reinterpret_cast<const T*>(f.v);
+  const T* dO = reinterpret_cast<const T*>(a.dO);
+  const T* Svk = reinterpret_cast<const T*>(f.S_vk) + ci * D * D;     // state entering the chunk
+  const T* dSvk = reinterpret_cast<const T*>(a.dS_vk) + ci * D * D;   // gradient w.r.t. the state leaving it
+
+  // ---- stage the chunk's raw inputs in LDS with coalesced 16-byte loads: k, q, v (dtype)
+  // in the K^+, Q^+, V slots; the per-token log-retention la = log g + log b (clamped as
+  // in the prep pass) in slots 4-5 (fp32, row stride D+4); P from the prep pass.  Tokens
+  // past the end read as k = q = v = 0, la = 0.
+  constexpr int LDG = D + 4;
+  float* lgS = reinterpret_cast<float*>(smem + Lay::slot(4));
+  static_assert(sizeof(float) * LC * LDG <= 2 * Lay::S1, "log-retention staging exceeds two slots");
+  // All of the chunk's global loads are issued here, from clamped rows (n >= 1), before
+  // anything waits on them: the staged inputs, dO (written to LDS once its slot is
+  // free), the chunk's inverse T = (I + A)^-1 and P from the prep pass (dtype), and w.
+  constexpr int PR = D / 8;                      // 8-element pieces per token row
+  constexpr int NST = LC * PR / NT;              // pieces per thread
+  static_assert(NST * NT == LC * PR, "pieces must split evenly over the threads");
+  const float wv = f.w[row0 + min(tid, n - 1)];
+  Frag<T> kx[NST], qx[NST], vx[NST], dOx[NST];
+  Frag<float> lx[NST], bx[NST];
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    const size_t src = row0 * D + (unsigned)(min(r, n - 1) * D + 8 * g);
+    kx[u] = load_frag(k + src);
+    qx[u] = load_frag(q + src);
+    vx[u] = load_frag(v + src);
+    lx[u] = load_frag(f.log_g + src);
+    if (HAS_B) bx[u] = load_frag(f.b + src);
+    dOx[u] = load_frag(dO + src);
+  }
+  // gates as pre-activations: amplitude and bias of the thread's 8 channels (the same
+  // for all of its pieces, as NT is a multiple of D / 8)
+  Frag<float> pA, pT;
+  if constexpr (LG) {
+    static_assert(NT % PR == 0, "pieces of a thread must share their channels");
+    pA = load_frag(f.gA + (bh % f.H) * D + 8 * (tid % PR));
+    pT = load_frag(f.gtau + (bh % f.H) * D + 8 * (tid % PR));
+  }
+  constexpr int TP = LC * LC / 4, NTP = (TP + NT - 1) / NT;   // 4 consecutive columns per piece
+  f32x4 tpre[NTP], ppre[NTP];
+#pragma unroll
+  for (int u = 0; u < NTP; ++u) {
+    const size_t o = ci * LC * LC + 4 * min(tid + NT * u, TP - 1);
+    tpre[u] = load4f(reinterpret_cast<const T*>(f.f.Tt) + o);
+    ppre[u] = load4f(reinterpret_cast<const T*>(f.f.Pt) + o);
+  }
+  if (tid < LC) wL[tid] = (tid < n) ? (LG ? sigmoidf(wv) : wv) : 0.f;
+  if (tid < 16) flags[tid] = 0;
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    const bool valid = r < n;
+    *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = valid ? kx[u] : zero_frag(T());
+    *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = valid ? qx[u] : zero_frag(T());
+    *reinterpret_cast<Frag<T>*>(Vr + r * LDD + 8 * g) = valid ? vx[u] : zero_frag(T());
+    Frag<float> lw;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float la = frag_elem(lx[u], e);
+      if constexpr (LG) la = -(e < 4 ? pA.lo[e] : pA.hi[e - 4]) * softplusf(la + (e < 4 ? pT.lo[e] : pT.hi[e - 4]));
+      if constexpr (HAS_B) la += LG ? -softplusf(-frag_elem(bx[u], e)) : flog(frag_elem(bx[u], e));
+      la = valid ? clamp_la(la) : 0.f;
+      if (e < 4) lw.lo[e] = la;
+      else lw.hi[e - 4] = la;
+    }
+    *reinterpret_cast<Frag<float>*>(lgS + r * LDG + 8 * g) = lw;
+  }
+#pragma unroll
+  for (int u = 0; u < NTP; ++u) {
+    const int idx = tid + NT * u;
+    if (idx < TP) store4(Pb + (idx / (LC / 4)) * LDL + 4 * (idx % (LC / 4)), ppre[u]);
+  }
+  __syncthreads();
+  // ---- gate pass in accumulator layout: lane holds rows 16 rt + 4 lg + i of column
+  // 16 (ct0 + j) + lr.  Inclusive sums of la inside each 16-token block (loc = G - Gb),
+  // the block log-retention btot and the block starts Gb; loc goes back over the staged
+  // la (each lane overwrites only what it read)
+  f32x4 loc[NB][CPW];
+  float gbs[NB][CPW], bto[NB][CPW], GLs[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int col = 16 * (ct0 + j) + lr;
+    float run = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt) {
+      float cs[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cs[i] = (i == 0 ? 0.f : cs[i - 1]) + lgS[(16 * rt + 4 * lg + i) * LDG + col];
+      // sum of the 4-row groups of this block held by lanes with smaller lg
+      float pre = 0.f, tile = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float tg = __shfl(cs[3], lr + 16 * g);
+        if (g < lg) pre += tg;
+        tile += tg;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        loc[rt][j][i] = pre + cs[i];
+        lgS[(16 * rt + 4 * lg + i) * LDG + col] = loc[rt][j][i];
+      }
+      gbs[rt][j] = run;
+      bto[rt][j] = tile;
+      run += tile;
+    }
+    GLs[j] = run;
+    if (lg == 0) {
+      gLs[col] = fexp(run);
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        btT[rt * D + col] = bto[rt][j];
+        if (-bto[rt][j] > kSafeLog) flags[rt] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  bool unsafe[NB];
+  int mask = 0;
+#pragma unroll
+  for (int I = 0; I < NB; ++I) {
+    unsafe[I] = flags[I] != 0;
+    mask |= unsafe[I] ? 1 << I : 0;
+  }
+
+  // the lane's factor of block pair (I, J), J <= I: e^(Gb[I] - Gb[J+1]); on the diagonal
+  // e^-btot_I, or 0 where the exact terms replace the block's product
+  auto dfac = [&](int I, int J, int j) -> float {
+    if (I == J) return unsafe[I] ? 0.f : fexp(-bto[I][j]);
+    float s = 0.f;
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+      if (m > J && m < I) s += bto[m][j];
+    return I == J + 1 ? 1.f : fexp(s);
+  };
+  // operand matrices K^+ (in place), K^-, Q^+ (in place) in the staging pieces, with loc
+  // read back from the staging slots and btot from the table; V stays raw
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    const Frag<float> lc = load_frag(lgS + r * LDG + 8 * g);
+    const Frag<float> bt = load_frag(btT + (r / 16) * D + 8 * g);
+    f32x4 eo0, eo1, ee0, ee1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      eo0[e] = fexp(lc.lo[e]);
+      eo1[e] = fexp(lc.hi[e]);
+      ee0[e] = fexp(bt.lo[e] - lc.lo[e]);
+      ee1[e] = fexp(bt.hi[e] - lc.hi[e]);
+    }
+    const Frag<T> kf = load_frag(Kp + r * LDD + 8 * g), qf = load_frag(Qp + r * LDD + 8 * g);
+    *reinterpret_cast<Frag<T>*>(Kp + r * LDD + 8 * g) = scale_frag(kf, eo0, eo1);
+    *reinterpret_cast<Frag<T>*>(Km + r * LDD + 8 * g) = scale_frag(kf, ee0, ee1);
+    *reinterpret_cast<Frag<T>*>(Qp + r * LDD + 8 * g) = scale_frag(qf, eo0, eo1);
+  }
+  // state fragments for U = Ubar - W S^T
+  Frag<T> fS[KD][CPW];
+  load_state_frags<T, D, CPW>(fS, Svk, ct0);
+  // dtype copies of T and Tw = T diag(w)
+#pragma unroll
+  for (int u = 0; u < NTP; ++u) {
+    const int idx = tid + NT * u;
+    if (idx < TP) {
+      const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Tb[r * LDL + s + e] = to<T>(tpre[u][e]);
+        Twb[r * LDL + s + e] = to<T>(tpre[u][e] * wL[s + e]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- W = Tw K+ with K+ = K^+ e^Gb (chunk reference: block J's factor on the lane's
+  // column), stored negated; Ubar = Tw V (kept as U's accumulator)
+  {
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma_blk<T, NB, CPW, true>(
+        acc, [&](int ob, int kb) { return lds_frag16_rows(Twb, LDL, 16 * ob, 16 * kb); },
+        [&](int kb, int ct) { return lds_frag16_cols(Kp, LDD, 16 * ct, 16 * kb); }, ct0,
+        [&](int, int J, int j) { return fexp(gbs[J][j]); });
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) lds_store_acc_tile(Wn, LDD, 16 * rt, 16 * (ct0 + j), -acc[rt][j]);
+  }
+  f32x4 accU[NB][CPW];
+  zero_acc(accU);
+  owned_mma<T, NB, CPW, KL>(accU, LdsSrc<T, false>{Twb, LDL}, LdsSrc<T, true>{Vr, LDD}, ct0);
+  __syncthreads();
+
+  // ---- U = Ubar + (-W) S^T  -> row-major U
+  owned_mma<T, NB, CPW, KD>(accU, LdsSrc<T, false>{Wn, LDD}, fS);
+#pragma unroll
+  for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) lds_store_acc_tile(Ur, LDD, 16 * rt, 16 * (ct0 + j), accU[rt][j]);
+  Frag<T> fG[KD][CPW];                       // dS' fragments
+  load_state_frags<T, D, CPW>(fG, dSvk, ct0);
+  __syncthreads();   // -W and Tw no longer needed: their slots take dO and the K-> factors
+
+  // ---- dO into LDS (row-major, zero for tokens past the end); e^(G_L - Gb[J+1]) of the
+  // lane's column (the suffix of the block log-retentions) into the table
+#pragma unroll
+  for (int u = 0; u < NST; ++u) {
+    const int idx = tid + NT * u, r = idx / PR, g = idx % PR;
+    *reinterpret_cast<Frag<T>*>(dOr + r * LDD + 8 * g) = (r < n) ? dOx[u] : zero_frag(T());
+  }
+  if (lg == 0) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      float sfx = 0.f;
+#pragma unroll
+      for (int rt = NB - 1; rt >= 0; --rt) {
+        cKT[rt * D + 16 * (ct0 + j) + lr] = fexp(sfx);
+        sfx += bto[rt][j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- dU = P^T dO + K-> dS'^T, K->_s = K^-_s e^(G_L - Gb[J+1]) for s in block J (the
+  // factor of the contraction's key channels, applied to the dS' fragment per row block)
+  {
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, true>{Pb, LDL}, LdsSrc<T, true>{dOr, LDD}, ct0);
+#pragma unroll
+    for (int kb = 0; kb < KD; ++kb) {
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(cKT + rt * D + 32 * kb + 8 * lg);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(cKT + rt * D + 32 * kb + 8 * lg + 4);
+        const Frag<T> af = frag<false>(Km, LDD, 16 * rt, 32 * kb);
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) mma(acc[rt][j], af, scale_frag(fG[kb][j], g0, g1));
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) lds_store_acc_tile(dUr, LDD, 16 * rt, 16 * (ct0 + j), acc[rt][j]);
+  }
+  KmajorPieces<T> pSk[KD][CPW], pDk[KD][CPW];   // S and dS' with rows k, for the key-owned products
+  load_state_kmajor<T, D, CPW>(pSk, Svk, ct0);
+  load_state_kmajor<T, D, CPW>(pDk, dSvk, ct0);
+  // ---- dP = tril(dO U^T) (the mirrored tiles above the diagonal are zero)
+  for (int t = wave; t < NTRI; t += NW) {
+    int i, j;
+    tri_index(t, i, j);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D; kk += 32) mma(acc, frag<false>(dOr, LDD, 16 * i, kk), frag<false>(Ur, LDD, 16 * j, kk));
+    const int s = 16 * j + lr;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) acc[ii] = (s <= 16 * i + 4 * lg + ii) ? acc[ii] : 0.f;
+    lds_store_acc_tile(dPb, LDL, 16 * i, 16 * j, acc);
+    if (j < i) lds_zero_tile(dPb, LDL, 16 * j, 16 * i);
+    if (i == j && unsafe[i]) store4(reinterpret_cast<T*>(a.diag) + ((ci * NB + i) * 2 * 64 + lane) * 4, acc);
+  }
+  __syncthreads();
+
+  // ---- token x key gradients of this wave's columns, folded as they are produced into
+  //   dk (gradient w.r.t. k) and dG (gradient w.r.t. the cumulative log-retention G,
+  //   elementwise): per term, the row role of a ratio-weighted product adds
+  //   e^loc X to dk and K^+ X to dG, the column role e^(btot - loc) X to dk and -K^- X
+  //   to dG (X before the element's own factor)
+  Frag<T> fSk[KD][CPW], fDk[KD][CPW];
+  f32x4 dK[NB][CPW], dG[NB][CPW];
+  zero_acc(dK);
+  float gsum[CPW];        // sum over tokens of K-> .* dK-> per column (part of the G_L term)
+  // M[16 rt + 4 lg + i][16 (ct0 + j) + lr], i = 0..3: the lane's accumulator-layout
+  // elements of an operand matrix in LDS
+  auto lds_tile = [&](const T* m, int rt, int j) { return lds_acc_tile(m, LDD, 16 * rt, 16 * (ct0 + j)); };
+  {
+    // dQ+ = (dO S) e^Gb + X2 with X2 = sum_J D_IJ (dP_IJ K^-_J): dq = e^loc dQ+, dG = Q^+ dQ+
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    finish_kmajor(fSk, pSk);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{dOr, LDD}, fSk);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) acc[rt][j] *= fexp(gbs[rt][j]);
+    owned_mma_blk<T, NB, CPW, true>(
+        acc, [&](int ob, int kb) { return lds_frag16_rows(dPb, LDL, 16 * ob, 16 * kb); },
+        [&](int kb, int ct) { return lds_frag16_cols(Km, LDD, 16 * ct, 16 * kb); }, ct0, dfac);
+    finish_kmajor(fDk, pDk);
+    T* dq = reinterpret_cast<T*>(a.dq);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 qv = lds_tile(Qp, rt, j);
+        f32x4 dqv;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float y = acc[rt][j][ii];
+          dG[rt][j][ii] = qv[ii] * y;
+          dqv[ii] = fexp(loc[rt][j][ii]) * y;
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * rt + 4 * lg + ii;
+          if (r < n) dq[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(dqv[ii]);
+        }
+      }
+  }
+  {
+    // dK-> = U dS'  -> dk += e^(G_L - G) dK->, dG -= K-> dK->
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{Ur, LDD}, fDk);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      float cs = 0.f, tail = 0.f;
+#pragma unroll
+      for (int rt = NB - 1; rt >= 0; --rt) {
+        const float eK = fexp(tail);             // e^(G_L - Gb[rt+1])
+        const f32x4 kmv = lds_tile(Km, rt, j);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float kf = kmv[ii] * eK;           // K->
+          dK[rt][j][ii] += fexp(bto[rt][j] - loc[rt][j][ii]) * eK * acc[rt][j][ii];
+          dG[rt][j][ii] -= kf * acc[rt][j][ii];
+          cs += kf * acc[rt][j][ii];
+        }
+        tail += bto[rt][j];
+      }
+      gsum[j] = cs;
+    }
+    // G_L term of each column: sum_s K->_s dK->_s + Gamma_L sum_v S[v][k] dS'[v][k]
+    // (the lane's fragments hold S and dS' at v = 32 kb + 8 lg + e of column 16 (ct0 + j) + lr)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      float sd = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KD; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sd += tof(frag_elem(fSk[kb][j], e)) * tof(frag_elem(fDk[kb][j], e));
+      float tot = fexp(GLs[j]) * sd;
+      tot += __shfl_xor(tot, 16);
+      tot += __shfl_xor(tot, 32);
+      float gs = gsum[j];
+      gs += __shfl_xor(gs, 16);
+      gs += __shfl_xor(gs, 32);
+      if (lg == 0) glt[16 * (ct0 + j) + lr] = tot + gs;
+    }
+  }
+  {
+    // column role of the dP product: X3 = sum_I D_IJ (dP_IJ^T Q^+_I)
+    //   -> dk += e^(btot - loc) X3, dG -= K^- X3
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma_blk<T, NB, CPW, false>(
+        acc, [&](int ob, int kb) { return lds_frag16_cols(dPb, LDL, 16 * ob, 16 * kb); },
+        [&](int kb, int ct) { return lds_frag16_cols(Qp, LDD, 16 * ct, 16 * kb); }, ct0, dfac);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kmv = lds_tile(Km, rt, j);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          dK[rt][j][ii] += fexp(bto[rt][j] - loc[rt][j][ii]) * acc[rt][j][ii];
+          dG[rt][j][ii] -= kmv[ii] * acc[rt][j][ii];
+        }
+      }
+  }
+  __syncthreads();   // Q^+ is dead: its slot takes dW; the K-> table's slot takes e^Gb
+
+  // ---- dW = -dU S  -> row-major dW; e^Gb of the lane's column into the table for dT'
+  {
+    f32x4 acc[NB][CPW];
+    zero_acc(acc);
+    owned_mma<T, NB, CPW, KD>(acc, LdsSrc<T, false>{dUr, LDD}, fSk);
+#pragma unroll
+    for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) lds_store_acc_tile(dWr, LDD, 16 * rt, 16 * (ct0 + j), -acc[rt][j]);
+    if (lg == 0) {
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int rt = 0; rt < NB; ++rt) gbeT[rt * D + 16 * (ct0 + j) + lr] = fexp(gbs[rt][j]);
+    }
+  }
+  __syncthreads();
+
+  // ---- dT' = dW K+^T + dU V^T (lower tiles; K+ = K^+ e^Gb, the factor of the key channels
+  // of block j applied to the fragment); dT = dT' diag(w); dw term sum_i T[i][r] dT'[i][r]
+  for (int t = wave; t < NTRI; t += NW) {
+    int i, j;
+    tri_index(t, i, j);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D; kk += 32) {
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(gbeT + j * D + kk + 8 * lg);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(gbeT + j * D + kk + 8 * lg + 4);
+      mma(acc, frag<false>(dWr, LDD, 16 * i, kk), scale_frag(frag<false>(Kp, LDD, 16 * j, kk), g0, g1));
+      mma(acc, frag<false>(dUr, LDD, 16 * i, kk), frag<false>(Vr, LDD, 16 * j, kk));
+    }
+    const int s = 16 * j + lr;
+    float cs = 0.f;
+    const f32x4 tv = lds_acc_tile(Tb, LDL, 16 * i, 16 * j);
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) cs += tv[ii] * acc[ii];
+    lds_store_acc_tile(dTb, LDL, 16 * i, 16 * j, acc * wL[s]);
+    if (j < i) lds_zero_tile(dTb, LDL, 16 * j, 16 * i);   // mirrored tile: zero
+    cs += __shfl_xor(cs, 16);
+    cs += __shfl_xor(cs, 32);
+    if (lg == 0) {
+      dwp[i * LC + s] = cs;
+      if (j < i) dwp[j * LC + 16 * i + lr] = 0.f;      // tiles above the diagonal contribute nothing
+    }
+  }
+  // ---- dV = Tw^T dU = diag(w) T^T dU (write dv); dK+ (first part) = diag(w) T^T dW
+  //   -> dk += Gamma dK+, dG += K+ dK+ (Gamma = e^(Gb + loc), K+ = K^+ e^Gb)
+  {
+    f32x4 acc[NB][CPW], acc2[NB][CPW];
+    zero_acc(acc);
+    zero_acc(acc2);
+    owned_mma<T, NB, CPW, KL>(acc, LdsSrc<T, true>{Tb, LDL}, LdsSrc<T, true>{dUr, LDD}, ct0);
+    owned_mma<T, NB, CPW, KL>(acc2, LdsSrc<T, true>{Tb, LDL}, LdsSrc<T, true>{dWr, LDD}, ct0);
+    T* dv = reinterpret_cast<T*>(a.dv);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kpv = lds_tile(Kp, rt, j);
+        const float egb = fexp(gbs[rt][j]);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * rt + 4 * lg + ii;
+          const float wr = wL[r];
+          if (r < n) dv[row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr)] = to<T>(wr * acc[rt][j][ii]);
+          const float x = egb * wr * acc2[rt][j][ii];
+          dK[rt][j][ii] += fexp(loc[rt][j][ii]) * x;
+          dG[rt][j][ii] += kpv[ii] * x;
+        }
+      }
+  }
+  __syncthreads();   // dT complete; dP no longer needed (its slot takes Z)
+
+  // ---- Z = dT T^T (lower tiles)
+  for (int t = wave; t < NTRI; t += NW) {
+    int i, j;
+    tri_index(t, i, j);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < LC; kk += 32) mma(acc, frag<false>(dTb, LDL, 16 * i, kk), frag<false>(Tb, LDL, 16 * j, kk));
+    lds_store_acc_tile(Zb, LDL, 16 * i, 16 * j, acc);
+  }
+  __syncthreads();
+  // b (or b_x) at the lane's gradient positions, for the erase gradient; loaded here so
+  // that the loads are consumed before the chunk's gradient stores are issued
+  float binv[CPW][NB][4];
+  if (HAS_B) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+          binv[j][rt][ii] = f.b[row0 * D + (unsigned)(min(16 * rt + 4 * lg + ii, n - 1) * D + 16 * (ct0 + j) + lr)];
+  }
+  // ---- dA = -T^T Z (strictly lower), dB = diag(w) dA; dw term sum_s B_rs dA_rs with B
+  // (the coupling before the row scaling by w) from the prep pass
+  {
+    constexpr int MAXT = (NTRI + NW - 1) / NW;
+    f32x4 dA[MAXT];
+    const T* gB = reinterpret_cast<const T*>(f.f.Bt) + ci * LC * LC;
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int t = wave + NW * u;
+      dA[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < NTRI) {
+        int i, j;
+        tri_index(t, i, j);
+        const f32x4 bacc = load4f(gB + ((size_t)t * 64 + lane) * 4);
+#pragma unroll
+        for (int kk = 0; kk < LC; kk += 32) mma(dA[u], frag<true>(Tb, LDL, 16 * i, kk), frag<true>(Zb, LDL, 16 * j, kk));
+        const int s = 16 * j + lr;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * i + 4 * lg + ii;
+          const float da = (s < r) ? -dA[u][ii] : 0.f;
+          dA[u][ii] = da;
+          const float rs = row16_sum(bacc[ii] * da);
+          if (lr == 0) dwq[j * LC + r] = rs;
+        }
+      }
+    }
+    __syncthreads();   // every read of Z is done
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+      const int t = wave + NW * u;
+      if (t < NTRI) {
+        int i, j;
+        tri_index(t, i, j);
+        f32x4 v;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) v[ii] = wL[16 * i + 4 * lg + ii] * dA[u][ii];
+        lds_store_acc_tile(dAb, LDL, 16 * i, 16 * j, v);
+        if (i == j && unsafe[i]) store4(reinterpret_cast<T*>(a.diag) + (((ci * NB + i) * 2 + 1) * 64 + lane) * 4, v);
+        if (j < i) {
+          // mirrored tile above the diagonal: zero, and no row-sum contribution
+          lds_zero_tile(dAb, LDL, 16 * j, 16 * i);
+          if (lr == 0) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) dwq[i * LC + 16 * j + 4 * lg + ii] = 0.f;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  if (HAS_B) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          // the erase gradient from d log a: d/db = dlog a / b; with pre-activations
+          // d/db_x = dlog a * sigmoid(-b_x); for b = sigmoid(x) given as b (db_mode 1)
+          // d/dx = dlog a * (1 - b)
+          const float bvv = binv[j][rt][ii];
+          binv[j][rt][ii] = LG ? sigmoidf(-bvv) : (a.db_mode ? 1.f - bvv : rcp(bvv));
+        }
+  }
+  // ---- the coupling's row and column roles: X1 = sum_J D_IJ (dB_IJ K^-_J) and
+  // X3 = sum_I D_IJ (dB_IJ^T K^+_I)
+  {
+    f32x4 accp[NB][CPW], accm[NB][CPW];
+    zero_acc(accp);
+    zero_acc(accm);
+    owned_mma_blk<T, NB, CPW, true>(
+        accp, [&](int ob, int kb) { return lds_frag16_rows(dAb, LDL, 16 * ob, 16 * kb); },
+        [&](int kb, int ct) { return lds_frag16_cols(Km, LDD, 16 * ct, 16 * kb); }, ct0, dfac);
+    owned_mma_blk<T, NB, CPW, false>(
+        accm, [&](int ob, int kb) { return lds_frag16_cols(dAb, LDL, 16 * ob, 16 * kb); },
+        [&](int kb, int ct) { return lds_frag16_cols(Kp, LDD, 16 * ct, 16 * kb); }, ct0, dfac);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt) {
+        const f32x4 kpv = lds_tile(Kp, rt, j), kmv = lds_tile(Km, rt, j);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float lo = loc[rt][j][ii];
+          dK[rt][j][ii] += fexp(lo) * accp[rt][j][ii] + fexp(bto[rt][j] - lo) * accm[rt][j][ii];
+          dG[rt][j][ii] += kpv[ii] * accp[rt][j][ii] - kmv[ii] * accm[rt][j][ii];
+        }
+      }
+  }
+  __syncthreads();   // glt, dwp, dwq complete
+
+  // ---- dlog a = reverse cumulative sum of dG over the chunk's tokens + G_L term
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int col = 16 * (ct0 + j) + lr;
+    float run = glt[col];
+#pragma unroll
+    for (int rt = NB - 1; rt >= 0; --rt) {
+      float l4[4];
+      l4[3] = dG[rt][j][3];
+      l4[2] = l4[3] + dG[rt][j][2];
+      l4[1] = l4[2] + dG[rt][j][1];
+      l4[0] = l4[1] + dG[rt][j][0];
+      float post = run, tile = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float tg = __shfl(l4[0], lr + 16 * g);
+        if (g > lg) post += tg;
+        tile += tg;
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) dG[rt][j][ii] = post + l4[ii];    // dlog a
+      run += tile;
+    }
+  }
+  // gradient stores; a full chunk stores without per-element token checks
+  auto store_grads = [&](auto full) {
+    T* dk = reinterpret_cast<T*>(a.dk);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int rt = 0; rt < NB; ++rt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int r = 16 * rt + 4 * lg + ii;
+          if (decltype(full)::value || r < n) {
+            const size_t idx = row0 * D + (unsigned)(r * D + 16 * (ct0 + j) + lr);
+            a.dlog_g[idx] = dG[rt][j][ii];
+            if (HAS_B) a.db[idx] = dG[rt][j][ii] * binv[j][rt][ii];
+            dk[idx] = to<T>(dK[rt][j][ii]);
+          }
+        }
+  };
+  if (n == LC) store_grads(std::true_type{});
+  else store_grads(std::false_type{});
+  // ---- dw_r = sum_s B_rs dA_rs + sum_i T[i][r] dT'[i][r]
+  if (tid < LC && tid < n) {
+    float s = 0.f;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) s += dwq[t * LC + tid] + dwp[t * LC + tid];
+    a.dw[row0 + tid] = LG ? s * wL[tid] * (1.f - wL[tid]) : s;     // d/dw_hat = d/dw * w (1 - w)
+  }
+  // ---- exact within-block terms of the blocks beyond the fast tiles' range, by this
+  // workgroup once its gradient stores are done
+  if (mask) {
+    __syncthreads();
+    diag_fix_chunk<T, LC, D, HAS_B, LG, NT>(a, bh, c, mask, reinterpret_cast<float*>(smem));
+  }
+}
+
+template <typename T, int LC, int D, bool HAS_B, bool LG>
+__global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const size_t ci = (size_t)blockIdx.y * a.fwd.NC + a.c_lo + blockIdx.x;
+  if (a.fwd.f.cflag[ci]) bwd_chunk_range<T, LC, D, HAS_B, LG>(a, smem);
+  else bwd_chunk_fast<T, LC, D, HAS_B, LG>(a, smem);
+}
+
+size_t diag_fix_bytes(int dtype, int BH, int NC, int LC) {
+  return ((size_t)BH * NC * (LC / 16) * 512 * (dtype ? 2 : 4) + 255) & ~size_t(255);
 }
 
 // ------------------------------------------------------------------ launchers

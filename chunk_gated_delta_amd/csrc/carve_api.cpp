@@ -144,16 +144,30 @@ size_t saved_bytes(const carve_shape* s, const Plan& p) {
   return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 3) + (states_bytes(s, p) + 256) + 256;
 }
 
-// workspace of carve_bwd_saved: the state gradients (one fragment-order copy)
+// diagonal tiles of the blocks whose exact within-block terms the range-safe chunk
+// gradients add
+size_t diag_bytes(const carve_shape* s, const Plan& p) {
+  return carve::diag_fix_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC) + 256;
+}
+void set_diag(carve::BwdArgs* a, const carve_shape* s, const Plan& p, void* base) {
+  a->diag = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(base) + 255) & ~uintptr_t(255));
+  (void)s;
+  (void)p;
+}
+
+// workspace of carve_bwd_saved: the state gradients (one fragment-order copy), then the
+// fix-up flags and tiles
 size_t bwd_saved_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  return (states_bytes(s, p) + 256) + 256;
+  return (states_bytes(s, p) + 256) + 256 + diag_bytes(s, p);
 }
 
 size_t bwd_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  // S and dS per chunk, one fragment-order copy each, in the operand type
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 2) + 2 * (states_bytes(s, p) + 256) + 256;
+  // S and dS per chunk, one fragment-order copy each, in the operand type; the fix-up
+  // flags and tiles
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 2) + 2 * (states_bytes(s, p) + 256) + 256 +
+         diag_bytes(s, p);
 }
 
 carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, const void* k, const void* v,
@@ -313,6 +327,7 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
   const size_t states = states_bytes(s, p);
   a.fwd.S_vk = base;
   a.dS_vk = align_up(base + states);
+  set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states);
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -413,6 +428,7 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
   const size_t states = states_bytes(s, p);
   a.fwd.S_vk = base;
   a.dS_vk = align_up(workspace);
+  set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states);
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -474,7 +490,7 @@ carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k
 size_t carve_bwd_logits_workspace_size(const carve_shape* s) {
   Plan p;
   if (check_shape(s, &p) != CARVE_OK || p.empty) return 0;
-  return bwd_ws(s, p) + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) + 512;
+  return bwd_ws(s, p) + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) + 1024;
 }
 
 carve_status carve_bwd_logits(const carve_shape* s, const void* q, const void* k, const void* v,
@@ -514,7 +530,8 @@ carve_status carve_bwd_logits(const carve_shape* s, const void* q, const void* k
   const size_t states = states_bytes(s, p);
   a.fwd.S_vk = base;
   a.dS_vk = align_up(base + states);
-  float* partA = reinterpret_cast<float*>(align_up(static_cast<char*>(a.dS_vk) + states));
+  set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states);
+  float* partA = reinterpret_cast<float*>(align_up(static_cast<char*>(a.dS_vk) + states + 256 + diag_bytes(s, p)));
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -673,6 +690,7 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
   char* base = align_up(wb + carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 2));
   a.fwd.S_vk = base;
   a.dS_vk = align_up(base + states_bytes(s, p));
+  set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states_bytes(s, p));
   float* carry = reinterpret_cast<float*>(ws + Lw.carry);
   a.dO = ws + Lw.dOp;
   a.dS_T = carry;
@@ -681,7 +699,8 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
   a.dk = dk;
   a.dv = dv;
   a.dlog_g = dlog_g;
-  a.db = db_x;          // d/db first; the gate kernel turns it into d/db_x
+  a.db = db_x;          // d/db_x for b = sigmoid(b_x + z) directly (dlog a (1 - b))
+  a.db_mode = 1;
   a.dw = dw;
   if (e == hipSuccess) e = carve::launch_fwd_prep(a.fwd, hs);
   if (e == hipSuccess) e = carve::launch_fwd_state(a.fwd, hs);
@@ -702,7 +721,7 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
     a.c_count = std::min(per, p.NC - a.c_lo);
     e = carve::launch_bwd_state(a, hs);
     if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
-    if (e == hipSuccess) e = carve::launch_content_gate_bwd(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
+      if (e == hipSuccess) e = carve::launch_content_gate_bwd(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
   }
   if (e == hipSuccess && dS0) e = carve::launch_copy_or_zero(dS0, carry, (size_t)p.BH * p.D * p.D, hs);
   if (e == hipSuccess && proj) e = carve::launch_sum_over_batch(ca.dU1p, dU1, s->B, s->H, R * p.D, hs);

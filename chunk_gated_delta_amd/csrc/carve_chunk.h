@@ -37,10 +37,37 @@ struct PrepLayout {
   static constexpr size_t R3 = R2 + al(szLD);             // Kw^T, Vw^T   (gate pass .. WY factors)
   static constexpr size_t R4 = R3 + al(2 * szDL);         // A (fp32), then (-W)^T
   static constexpr size_t R5 = R4 + al(cmax(szLLf, szDL)); // P (dtype)
-  static constexpr size_t R6 = R5 + al(szLL);             // Ubar^T
-  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part products [<= 2P][D]
-  static constexpr size_t bytes = R7 + al(sizeof(float) * (LC + 2 * P * D));   // up to 2P parts
+  static constexpr size_t R6 = R5 + al(szLL);             // raw V, then the diagonal-tile K operand, then Ubar^T
+  static constexpr size_t R7 = R6 + al(szDL);             // w [LC], part sums of log a [<= 2P][D]
+  // R8: per-chunk gate tables: flags [16] int (1 = block needs the exact diagonal
+  // tiles) and exp of the log-retention at each block start [NB][D]
+  static constexpr int NB = LC / 16;
+  static constexpr int NFAR = (NB - 1) * (NB - 2) / 2;
+  static constexpr size_t R8 = R7 + al(sizeof(float) * (LC + 2 * P * D));   // up to 2P parts
+  // R9: column operands of the far coupling tiles (blocks I >= J + 2), [NFAR][16][LDD]:
+  // K^-_J times the retention between the end of block J and the start of block I
+  static constexpr size_t R9 = R8 + al(sizeof(int) * 16 + sizeof(float) * NB * D);
+  static constexpr size_t bytes = R9 + al(sizeof(T) * NFAR * 16 * LDD);
 };
+
+// Range of the gate algebra.  The per-token log-retention la = log g + log b is taken
+// in [kLaFloor, 0] (a retention below e^kLaFloor is zero in float32; NaN passes
+// through).  Inside a 16-token block the diagonal coupling tiles use one operand scaled
+// by exp(-(decay since the block start)); that is finite while the block's decay stays
+// below kSafeLog in every key channel.  Blocks beyond that take the exact elementwise
+// tiles (running products of the retention).
+constexpr float kLaFloor = -1.0e4f;
+constexpr float kSafeLog = 64.f;
+// A chunk whose log-retention stays above -kChunkSafe in every key channel takes the
+// fast path: operands referred to the chunk start, K- = k / Gamma at most e^kChunkSafe.
+constexpr float kChunkSafe = 80.f;
+constexpr float kMinOwn = 1.6038109e-28f;   // exp(-64)
+__device__ __forceinline__ float clamp_la(float la) {
+  la = la > 0.f ? 0.f : la;
+  return la < kLaFloor ? kLaFloor : la;
+}
+// blocks I >= J + 2 of a chunk -> index into the far-pair table
+__device__ __forceinline__ constexpr int far_index(int I, int J) { return (I - 2) * (I - 1) / 2 + J; }
 
 // ------------------------------------------------------------------ global layouts
 // MFMA fragment order of a [rows][C] matrix M (C = contraction length): fragment
@@ -186,18 +213,24 @@ __device__ __attribute__((noinline)) void triangular_inverse(lds_float* Af, lds_
 }
 
 // ------------------------------------------------------------------ gate sources
-// Erase gate of one element, split into a raw load (issued early, branch-free)
-// and its activation: token-only with b given, token-only with b = 1, or
-// content-aware b = sigmoid(b_x + z) with the chunk's content signal z (per key
-// channel, in LDS).
+// Erase gate of one element, split into a raw load (issued early, branch-free) and the
+// log-retention it contributes: token-only with b given, token-only with b = 1, or
+// content-aware b = sigmoid(b_x + z) with the chunk's content signal z (per key channel,
+// in LDS).  la(lg, x, ch, A, tau) is the per-token log-retention log g + log b of key
+// channel ch from the staged decay input lg and erase input x (A, tau: the channel's
+// amplitude and bias when the gates come as pre-activations).
 // Every source also maps the staged write input to w (wact: the identity unless the
 // gates come as pre-activations; kLogits marks that case, whose staged decay input is
 // the logit f).
+// (hardware exp / log / reciprocal: softplus(y) = max(y, 0) + log(1 + exp(-|y|)),
+// log sigmoid(y) = -softplus(-y))
+__device__ __forceinline__ float softplusf(float y) { return fmaxf(y, 0.f) + flog(1.f + fexp(-fabsf(y))); }
+__device__ __forceinline__ float sigmoidf(float y) { return __builtin_amdgcn_rcpf(1.f + fexp(-y)); }
 struct TokenGatesB {
   static constexpr bool kLogits = false;
   const float* b;
   __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b + idx); }
-  __device__ __forceinline__ float act(float x, int) const { return x; }
+  __device__ __forceinline__ float la(float lg, float x, int, float, float) const { return clamp_la(lg + flog(x)); }
   __device__ __forceinline__ float wact(float x) const { return x; }
 };
 struct TokenGates1 {
@@ -208,7 +241,7 @@ struct TokenGates1 {
     f.hi = f.lo;
     return f;
   }
-  __device__ __forceinline__ float act(float x, int) const { return x; }
+  __device__ __forceinline__ float la(float lg, float, int, float, float) const { return clamp_la(lg); }
   __device__ __forceinline__ float wact(float x) const { return x; }
 };
 struct ContentGates {
@@ -216,7 +249,9 @@ struct ContentGates {
   const float* b_x;
   const float* z;
   __device__ __forceinline__ Frag<float> load8(size_t idx) const { return load_frag(b_x + idx); }
-  __device__ __forceinline__ float act(float x, int ch) const { return 1.f / (1.f + __expf(-(x + z[ch]))); }
+  __device__ __forceinline__ float la(float lg, float x, int ch, float, float) const {
+    return clamp_la(lg - softplusf(-(x + z[ch])));
+  }
   __device__ __forceinline__ float wact(float x) const { return x; }
 };
 
@@ -224,9 +259,6 @@ struct ContentGates {
 // log g = -A softplus(f + tau) with A, tau per head and key channel, b = sigmoid(b_x)
 // (HAS_BX; else b = 1), w = sigmoid(w_hat).  The staged decay input is f, the staged
 // erase input b_x, the staged write input w_hat.
-// (hardware exp / log / reciprocal: softplus(y) = max(y, 0) + log(1 + exp(-|y|)))
-__device__ __forceinline__ float softplusf(float y) { return fmaxf(y, 0.f) + __logf(1.f + __expf(-fabsf(y))); }
-__device__ __forceinline__ float sigmoidf(float y) { return __builtin_amdgcn_rcpf(1.f + __expf(-y)); }
 template <int D, bool HAS_BX>
 struct LogitGates {
   static constexpr bool kLogits = true;
@@ -237,9 +269,12 @@ struct LogitGates {
     if constexpr (HAS_BX) return load_frag(b_x + idx);
     return TokenGates1{}.load8(idx);
   }
-  __device__ __forceinline__ float act(float x, int) const { return HAS_BX ? sigmoidf(x) : x; }
   // log g from the decay logit x and the channel's amplitude and bias
   __device__ __forceinline__ float logdecay_p(float x, float a, float t) const { return -a * softplusf(x + t); }
+  __device__ __forceinline__ float la(float lg, float x, int, float a, float t) const {
+    const float l = logdecay_p(lg, a, t);
+    return clamp_la(HAS_BX ? l - softplusf(-x) : l);
+  }
   __device__ __forceinline__ float wact(float x) const { return sigmoidf(x); }
 };
 
@@ -254,8 +289,8 @@ constexpr int kPrepFwd = 1, kPrepBwd = 2;
 // Raw inputs of one chunk as 16-byte pieces (8 consecutive channels of one token),
 // piece tid + NT u of thread tid.  Loaded from clamped rows (branch-free), then
 // staged in LDS: k, q, v raw in the K+, Q+ and Ubar^T regions, the per-element
-// retention a = exp(log g) * b in the Kw^T region (fp32 [LC][D]); rows past the
-// end become k = q = v = 0, a = 1.
+// log-retention la = log g + log b (clamped, see clamp_la) in the Kw^T region
+// (fp32 [LC][D]); rows past the end become k = q = v = 0, la = 0.
 template <typename T, int LC, int D, int NT>
 struct PrepStage {
   static constexpr int PR = D / 8, NP = LC * PR, NST = (NP + NT - 1) / NT;
@@ -323,6 +358,7 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
     pT = load_frag(gates.tau + st.h * D + 8 * (tid % St::PR));
   }
   if (tid < LC) wL[tid] = (tid < n) ? gates.wact(st.w) : 0.f;
+  if (tid < 16) reinterpret_cast<int*>(smem + Lay::R8)[tid] = 0;   // exact-diagonal flags of the chunk
 #pragma unroll
   for (int u = 0; u < St::NST; ++u) {
     const int idx = tid + NT * u;
@@ -335,18 +371,124 @@ __device__ __forceinline__ void prep_stage_write(const FwdArgs& a, const Gates& 
       f32x4 lo, hi;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float llo = st.lg[u].lo[e], lhi = st.lg[u].hi[e];
+        float alo = 0.f, tlo = 0.f, ahi = 0.f, thi = 0.f;
         if constexpr (Gates::kLogits) {
-          llo = gates.logdecay_p(llo, pA.lo[e], pT.lo[e]);
-          lhi = gates.logdecay_p(lhi, pA.hi[e], pT.hi[e]);
+          alo = pA.lo[e];
+          tlo = pT.lo[e];
+          ahi = pA.hi[e];
+          thi = pT.hi[e];
         }
-        lo[e] = valid ? __expf(llo) * gates.act(st.g[u].lo[e], 8 * g + e) : 1.f;
-        hi[e] = valid ? __expf(lhi) * gates.act(st.g[u].hi[e], 8 * g + 4 + e) : 1.f;
+        lo[e] = valid ? gates.la(st.lg[u].lo[e], st.g[u].lo[e], 8 * g + e, alo, tlo) : 0.f;
+        hi[e] = valid ? gates.la(st.lg[u].hi[e], st.g[u].hi[e], 8 * g + 4 + e, ahi, thi) : 0.f;
       }
       *reinterpret_cast<f32x4*>(aS + r * D + 8 * g) = lo;
       *reinterpret_cast<f32x4*>(aS + r * D + 8 * g + 4) = hi;
     }
   }
+}
+
+// Sum over the G lanes g = 0..G-1 of a lane group (G a power of two, the groups aligned);
+// every lane of the group receives the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Exact diagonal coupling tiles of a 16-token block I whose log-retention falls below
+// -kSafeLog in some key channel (the fast tiles would need factors beyond float range):
+// for r >= s inside the block
+//   B_rs = sum_ch k_r k_s R_rs,   P_rs = sum_ch q_r k_s R_rs,   R_rs = prod_{t=s+1..r} a_t,
+// the retention ratio as a running product of a = e^la (no exponent range issue; a
+// product that underflows is one whose true value is below float range).  The block's
+// raw k, q and la are read again from global memory (the same gate arithmetic as the
+// staging) into the scratch region R1, which is free after the coupling phase.  Thread
+// (s, channel group g of 8 channels) runs r = 0..15, contributing for r >= s, and the
+// groups of one s are summed with shuffles.  Overwrites the block's diagonal tiles of A
+// (= w_r B_rs for s < r, fp32) and P, and with gB (backward modes) stores B in the
+// accumulator order of the coupling phase.  Starts and ends with a barrier-separated
+// phase (callers reach it from a workgroup-uniform branch).  Inlined: as an out-of-line
+// call it would make the whole kernel address memory through generic pointers.
+template <typename T, int LC, int D, typename Gates, int NT>
+__device__ __forceinline__ void prep_diag_exact(const FwdArgs& a, const Gates& gates, int bh, int c, int I,
+                                                          unsigned char* smem, float* Af, T* Pb, T* gB) {
+  using Lay = PrepLayout<T, LC, D, NT>;
+  constexpr int LDF = Lay::LDF, LDL = Lay::LDL, LDD = Lay::LDD, LDA = D + 4;
+  constexpr int PR = D / 8, G = D / 8;
+  static_assert(16 * G <= NT && (16 * G) % 64 == 0, "one thread per (column, channel group), whole waves");
+  static_assert(sizeof(float) * 16 * LDA + 2 * sizeof(T) * 16 * LDD <= Lay::R1sz, "exact-tile scratch exceeds R1");
+  float* aS = reinterpret_cast<float*>(smem + Lay::R1);                         // [16][LDA] a
+  T* kS = reinterpret_cast<T*>(smem + Lay::R1 + sizeof(float) * 16 * LDA);      // [16][LDD] raw k
+  T* qS = kS + 16 * LDD;                                                         // [16][LDD] raw q
+  const float* wL = reinterpret_cast<const float*>(smem + Lay::R7);
+  const int tid = threadIdx.x, lane = lane_id();
+  const int n = min(LC, a.T - c * LC);
+  const size_t row0 = (size_t)bh * a.T + (size_t)c * LC;
+  const T* kg = reinterpret_cast<const T*>(a.k);
+  const T* qg = reinterpret_cast<const T*>(a.q);
+  for (int idx = tid; idx < 16 * PR; idx += NT) {
+    const int rr = idx / PR, g = idx % PR, r = 16 * I + rr;
+    const bool valid = r < n;
+    const size_t e = (row0 + (size_t)min(r, n - 1)) * D + 8 * g;
+    const Frag<T> kf = load_frag(kg + e), qf = load_frag(qg + e);
+    const Frag<float> lf = load_frag(a.log_g + e), gf = gates.load8(e);
+    Frag<float> pA = zero_frag(0.f), pT = zero_frag(0.f);
+    if constexpr (Gates::kLogits) {
+      pA = load_frag(gates.A + (bh % a.H) * D + 8 * g);
+      pT = load_frag(gates.tau + (bh % a.H) * D + 8 * g);
+    }
+    f32x4 lo, hi;
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      lo[e4] = valid ? fexp(gates.la(lf.lo[e4], gf.lo[e4], 8 * g + e4, pA.lo[e4], pT.lo[e4])) : 1.f;
+      hi[e4] = valid ? fexp(gates.la(lf.hi[e4], gf.hi[e4], 8 * g + 4 + e4, pA.hi[e4], pT.hi[e4])) : 1.f;
+    }
+    *reinterpret_cast<f32x4*>(aS + rr * LDA + 8 * g) = lo;
+    *reinterpret_cast<f32x4*>(aS + rr * LDA + 8 * g + 4) = hi;
+    *reinterpret_cast<Frag<T>*>(kS + rr * LDD + 8 * g) = valid ? kf : zero_frag(T());
+    *reinterpret_cast<Frag<T>*>(qS + rr * LDD + 8 * g) = valid ? qf : zero_frag(T());
+  }
+  __syncthreads();
+  if (tid < 16 * G) {
+    const int s = tid / G, g = tid % G;
+    float ks[8], rho[8];
+    {
+      const Frag<T> f = load_frag(kS + s * LDD + 8 * g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ks[j] = tof(frag_elem(f, j));
+        rho[j] = 1.f;
+      }
+    }
+    const int t = I * (I + 1) / 2 + I;             // tri index of the diagonal tile
+#pragma unroll 1
+    for (int r = 0; r < 16; ++r) {
+      const Frag<T> kr = load_frag(kS + r * LDD + 8 * g), qr = load_frag(qS + r * LDD + 8 * g);
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(aS + r * LDA + 8 * g);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(aS + r * LDA + 8 * g + 4);
+      float sb = 0.f, sp = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ar = j < 4 ? a0[j] : a1[j - 4];
+        rho[j] = r > s ? rho[j] * ar : rho[j];
+        const float x = ks[j] * rho[j];
+        sb += tof(frag_elem(kr, j)) * x;
+        sp += tof(frag_elem(qr, j)) * x;
+      }
+      sb = group_sum<G>(r >= s ? sb : 0.f);
+      sp = group_sum<G>(r >= s ? sp : 0.f);
+      if (g == 0) {
+        const int row = 16 * I + r, col = 16 * I + s;
+        const float bv = s < r ? sb : 0.f;
+        Af[row * LDF + col] = wL[row] * bv;
+        Pb[row * LDL + col] = to<T>(s <= r ? sp : 0.f);
+        if (gB) gB[((size_t)t * 64 + s + 16 * (r / 4)) * 4 + r % 4] = to<T>(bv);
+      }
+    }
+  }
+  (void)lane;
+  __syncthreads();
 }
 
 // The chunk's factors from its staged inputs (LDS, after a barrier).
@@ -390,70 +532,194 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
   T* gUbT = reinterpret_cast<T*>(a.f.UbT) + ci * D * LC;
   T* gOiT = FWD ? reinterpret_cast<T*>(a.f.OiT) + ci * D * LC : nullptr;
 
-  // ---- gate pass: cumulative key-axis retention Gamma over the staged retention a
-  // (1 past the end); raw k, q, v are read from their slots.  With at least four
-  // tokens per part, a thread takes two adjacent key channels so that every row-major
-  // LDS access moves both; otherwise one channel.
-  const float* aS = reinterpret_cast<const float*>(smem + Lay::R3);
+  // ---- gate pass, in log space.  G_r = sum_{t<=r} la_t inside the chunk (la <= 0).  A
+  // chunk whose G_L stays above -kChunkSafe in every key channel refers its operands to
+  // the chunk start (fast path below).  Otherwise (range-safe path): Gb[I] is G at
+  // the start of 16-token block I (Gb[0] = 0) and btot_I = Gb[I+1] - Gb[I] <= 0 the
+  // block's log-retention.  Per element, with loc = G_r - Gb[I(r)] in [btot, 0]:
+  //   K^+ = k e^loc, Q^+ = q e^loc        row operands of the coupling tiles (<= |k|, |q|)
+  //   K^- = k e^(btot - loc)              column operand, referred to the block end (<= |k|)
+  //   K^d = k e^-loc                      column operand of the diagonal tiles (>= |k|,
+  //                                       finite while -btot <= kSafeLog)
+  //   Kw = w k e^(Gb + loc), K-> = k e^(G_L - Gb[I+1]) e^(btot - loc)   (chunk references)
+  // so a tile (I, J) of the coupling is K^+_I D_IJ K^-_J^T with D_IJ = 1 for J = I - 1,
+  // the retention between the end of block J and the start of block I (<= 1) for
+  // J <= I - 2, and K^+_I K^d_I^T on the diagonal: every retention ratio Gamma_r/Gamma_s
+  // is a product of factors <= 1, except inside a diagonal block, which the exact path
+  // below takes over when its decay leaves the safe range.  Raw k, q, v are read from
+  // their slots; with at least four tokens per part a thread takes two adjacent key
+  // channels so that every row-major LDS access moves both.
+  const float* laS = reinterpret_cast<const float*>(smem + Lay::R3);
   const T* Vraw = reinterpret_cast<const T*>(smem + Lay::R6);
+  T* Kd = reinterpret_cast<T*>(smem + Lay::R6);       // diagonal-tile operand, written over raw v
+  int* flags = reinterpret_cast<int*>(smem + Lay::R8);
+  float* gbeT = reinterpret_cast<float*>(smem + Lay::R8 + 16 * sizeof(int));   // [NB][D] e^Gb
+  T* Kfar = reinterpret_cast<T*>(smem + Lay::R9);                                // [NFAR][16][LDD]
   constexpr int CPT = (LC * D / (2 * NT)) % 4 == 0 && LC * D / (2 * NT) >= 4 ? 2 : 1;
   constexpr int PG = CPT * NT / D, RG = LC / PG;   // token parts, tokens per part
   static_assert(RG % 4 == 0 && PG * D <= 2 * P * D, "token parts must hold whole groups of 4");
+  static_assert(RG <= 16 && 16 % RG == 0, "a token part must lie inside one 16-token block");
+  constexpr int PB = 16 / RG;                      // parts per block
   const int ch = CPT * (tid % (D / CPT)), pid = tid / (D / CPT), r0 = pid * RG;
-  float G[CPT][RG];
+  const int blk = pid / PB, pf = blk * PB;         // the part's block and that block's first part
+  float gl[CPT][RG];                               // inclusive sums of la inside the part
   {
     float run[CPT];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) run[c] = 1.f;
+    for (int c = 0; c < CPT; ++c) run[c] = 0.f;
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
-      const float* ar = aS + (r0 + i) * D + ch;
+      const float* ar = laS + (r0 + i) * D + ch;
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        run[c] *= ar[c];
-        G[c][i] = run[c];
+        run[c] += ar[c];
+        gl[c][i] = run[c];
       }
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) part[pid * D + ch + c] = run[c];
   }
   __syncthreads();
-  float pre[CPT], tot[CPT];
+  // per channel: the parts before the block (gst = Gb), the block's parts before this
+  // one (bpre), the whole block (btot) and the parts after it (gaf = G_L - Gb[I+1])
+  float bpre[CPT], btot[CPT], gst[CPT], gaf[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) pre[c] = tot[c] = 1.f;
+  for (int c = 0; c < CPT; ++c) bpre[c] = btot[c] = gst[c] = gaf[c] = 0.f;
 #pragma unroll
   for (int pp = 0; pp < PG; ++pp) {
+    const bool before = pp < pf, inblk = !before && pp < pf + PB, mine = inblk && pp < pid;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const float pt = part[pp * D + ch + c];
-      if (pp < pid) pre[c] *= pt;
-      tot[c] *= pt;
+      gst[c] += before ? pt : 0.f;
+      btot[c] += inblk ? pt : 0.f;
+      bpre[c] += mine ? pt : 0.f;
+      gaf[c] += (!before && !inblk) ? pt : 0.f;
     }
   }
-  {
+  // the chunk's path: a key channel whose log-retention over the whole chunk falls
+  // below -kChunkSafe sends the chunk down the range-safe path (flag word 15)
+  if (pid == 0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c)
+      if (-(btot[c] + gaf[c]) > kChunkSafe) flags[15] = 1;
+  }
+  __syncthreads();
+  const bool wide = flags[15] != 0;
+  if (BWD && tid == 0) a.f.cflag[ci] = wide ? 1 : 0;
+  if (!wide) {
+    // ---- fast path: the retention referred to the chunk start, Gamma_r = e^G_r >= e^-kChunkSafe,
+    //   K+ = k Gamma, K- = k / Gamma, Q+ = q Gamma, K-> = k Gamma_L / Gamma
+    // (every coupling tile is K+_I K-_J^T, each product of a ratio Gamma_r / Gamma_s <= 1
+    // formed from two factors inside float range)
+    float egl[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) egl[c] = fexp(gst[c] + btot[c] + gaf[c]);
     float kf[CPT][RG], kw[CPT][RG], vw[CPT][RG];
 #pragma unroll
     for (int i = 0; i < RG; ++i) {
       const int r = r0 + i;
-      float kv[CPT], qv[CPT], vv[CPT], gam[CPT], inv[CPT], kp[CPT], km[CPT], qp[CPT];
+      float kv[CPT], qv[CPT], vv[CPT], kp[CPT], km[CPT], qp[CPT];
       ld_row<T, CPT>(Kp + r * LDD + ch, kv);       // staged raw, 0 past the end
       ld_row<T, CPT>(Qp + r * LDD + ch, qv);
       ld_row<T, CPT>(Vraw + r * LDD + ch, vv);
       const float wr = wL[r];
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        gam[c] = pre[c] * G[c][i];
-        inv[c] = 1.f / gam[c];
-        kp[c] = kv[c] * gam[c];
-        km[c] = kv[c] * inv[c];
-        qp[c] = qv[c] * gam[c];
+        const float gam = fexp(gst[c] + bpre[c] + gl[c][i]);
+        const float inv = __builtin_amdgcn_rcpf(gam);
+        kp[c] = kv[c] * gam;
+        km[c] = kv[c] * inv;
+        qp[c] = qv[c] * gam;
         kw[c][i] = wr * kp[c];
         vw[c][i] = wr * vv[c];
-        kf[c][i] = kv[c] * (tot[c] * inv[c]);
+        kf[c][i] = kv[c] * (egl[c] * inv);
       }
       st_row<T, CPT>(Kp + r * LDD + ch, kp);
       st_row<T, CPT>(Km + r * LDD + ch, km);
       st_row<T, CPT>(Qp + r * LDD + ch, qp);
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+#pragma unroll
+      for (int t = 0; t < RG / 4; ++t) {
+        store4(KwT + (ch + c) * LDL + r0 + 4 * t, f32x4{kw[c][4 * t], kw[c][4 * t + 1], kw[c][4 * t + 2], kw[c][4 * t + 3]});
+        store4(VwT + (ch + c) * LDL + r0 + 4 * t, f32x4{vw[c][4 * t], vw[c][4 * t + 1], vw[c][4 * t + 2], vw[c][4 * t + 3]});
+      }
+      const int cc = ch + c;
+#pragma unroll
+      for (int t = 0; t < RG / 4; ++t) {
+        const int r = r0 + 4 * t;
+        T* dst = gKfT + frag_offset<LC>(cc / 16, r / 32, cc % 16 + 16 * ((r % 32) / 8)) + r % 8;
+        store4(dst, f32x4{kf[c][4 * t], kf[c][4 * t + 1], kf[c][4 * t + 2], kf[c][4 * t + 3]});
+      }
+      if (pid == 0) a.f.gL[ci * D + cc] = egl[c];
+    }
+  } else {
+  // ---- range-safe path
+  if (pid == pf) {
+    // one part per block: the block's flag and its start retention e^Gb
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (-btot[c] > kSafeLog) flags[blk] = 1;
+      gbeT[blk * D + ch + c] = fexp(gst[c]);
+    }
+  }
+  // far-pair factors of this block as column block J: the retention from its end to the
+  // start of block I = J + 2 + d
+  constexpr int NFD = NB > 2 ? NB - 2 : 1;
+  float dfar[CPT][NFD];
+#pragma unroll
+  for (int d = 0; d < NFD; ++d)
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      float sm = 0.f;
+#pragma unroll
+      for (int pp = 0; pp < PG; ++pp) sm += (pp >= pf + PB && pp < (blk + 2 + d) * PB) ? part[pp * D + ch + c] : 0.f;
+      dfar[c][d] = fexp(sm);
+    }
+  {
+    float egs[CPT], ega[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      egs[c] = fexp(gst[c]);
+      ega[c] = fexp(gaf[c]);
+    }
+    float kf[CPT][RG], kw[CPT][RG], vw[CPT][RG];
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int r = r0 + i;
+      float kv[CPT], qv[CPT], vv[CPT], kp[CPT], km[CPT], kd[CPT], qp[CPT];
+      ld_row<T, CPT>(Kp + r * LDD + ch, kv);       // staged raw, 0 past the end
+      ld_row<T, CPT>(Qp + r * LDD + ch, qv);
+      ld_row<T, CPT>(Vraw + r * LDD + ch, vv);
+      const float wr = wL[r];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const float loc = bpre[c] + gl[c][i];
+        const float eo = fexp(loc), ee = fexp(btot[c] - loc);
+        const float ed = __builtin_amdgcn_rcpf(fmaxf(eo, kMinOwn));
+        kp[c] = kv[c] * eo;
+        qp[c] = qv[c] * eo;
+        km[c] = kv[c] * ee;
+        kd[c] = kv[c] * ed;
+        kw[c][i] = wr * kv[c] * (eo * egs[c]);
+        vw[c][i] = wr * vv[c];
+        kf[c][i] = kv[c] * (ee * ega[c]);
+      }
+      st_row<T, CPT>(Kp + r * LDD + ch, kp);
+      st_row<T, CPT>(Km + r * LDD + ch, km);
+      st_row<T, CPT>(Qp + r * LDD + ch, qp);
+      st_row<T, CPT>(Kd + r * LDD + ch, kd);       // over the raw v this thread just read
+#pragma unroll
+      for (int d = 0; d < NB - 2; ++d) {
+        if (blk + 2 + d < NB) {                    // far tile (blk + 2 + d, blk)
+          float kx[CPT];
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) kx[c] = km[c] * dfar[c][d];
+          st_row<T, CPT>(Kfar + (far_index(blk + 2 + d, blk) * 16 + r % 16) * LDD + ch, kx);
+        }
+      }
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -471,16 +737,20 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
         T* dst = gKfT + frag_offset<LC>(cc / 16, r / 32, cc % 16 + 16 * ((r % 32) / 8)) + r % 8;
         store4(dst, f32x4{kf[c][4 * t], kf[c][4 * t + 1], kf[c][4 * t + 2], kf[c][4 * t + 3]});
       }
-      if (pid == 0) a.f.gL[ci * D + cc] = tot[c];
+      if (pid == 0) a.f.gL[ci * D + cc] = fexp(btot[c] + gaf[c]);   // Gamma_L = e^(G_L)
     }
   }
+  }   // range-safe path
   __syncthreads();
 
-  // ---- coupling A = strict_tril(diag(w) K+ K-^T) (fp32) and P = tril(Q+ K-^T)
+  // ---- coupling A = strict_tril(diag(w) B), B_rs = sum_ch k_r k_s Gamma_r/Gamma_s (fp32),
+  // and P = tril(sum_ch q_r k_s Gamma_r/Gamma_s), tile (I, J) from K^+_I (A) or Q^+_I (P)
+  // against K^d_I (J = I), K^-_J (J = I - 1) or K^-_J scaled by the far-pair factor.
   // Wave w takes tiles w, w + NW, ... (A tiles first, then P); all of its operand
   // fragments are loaded before its first product (a wave past the last tile reloads
-  // that tile and skips the product).
+  // that tile and skips the product).  The backward modes also keep B (acc order).
   constexpr int NTRI = NB * (NB + 1) / 2, NTILE = 2 * NTRI, TPW = (NTILE + NW - 1) / NW, KD = D / 32;
+  T* gB = BWD ? reinterpret_cast<T*>(a.f.Bt) + ci * LC * LC : nullptr;
   {
     Frag<T> fa[TPW][KD], fb[TPW][KD];
     int ti[TPW], tj[TPW];
@@ -488,11 +758,14 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     for (int m = 0; m < TPW; ++m) {
       const int t = min(wave + NW * m, NTILE - 1);
       tri_index(t < NTRI ? t : t - NTRI, ti[m], tj[m]);
-      const T* Ar = t < NTRI ? Kp : Qp;
+      const T* Ar = (t < NTRI ? Kp : Qp) + 16 * ti[m] * LDD;
+      const T* Br = !wide || ti[m] == tj[m] + 1 ? Km + 16 * tj[m] * LDD
+                  : ti[m] == tj[m] ? Kd + 16 * tj[m] * LDD
+                  : Kfar + far_index(ti[m], tj[m]) * 16 * LDD;
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) {
-        fa[m][kk] = load_frag(Ar + (16 * ti[m] + lr) * LDD + 32 * kk + 8 * lg);
-        fb[m][kk] = load_frag(Km + (16 * tj[m] + lr) * LDD + 32 * kk + 8 * lg);
+        fa[m][kk] = load_frag(Ar + lr * LDD + 32 * kk + 8 * lg);
+        fb[m][kk] = load_frag(Br + lr * LDD + 32 * kk + 8 * lg);
       }
     }
 #pragma unroll
@@ -506,11 +779,14 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       for (int kk = 0; kk < KD; ++kk) mma(acc, fa[m][kk], fb[m][kk]);
       const int s = 16 * j + lr;
       if (isA) {
+        f32x4 bm;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int r = 16 * i + 4 * lg + ii;
-          Af[r * LDF + s] = (s < r) ? wL[r] * acc[ii] : 0.f;
+          bm[ii] = (s < r) ? acc[ii] : 0.f;
+          Af[r * LDF + s] = wL[r] * bm[ii];
         }
+        if (BWD && wide && !(i == j && flags[i])) store4(gB + ((size_t)t * 64 + lane) * 4, bm);
       } else {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) acc[ii] = (s <= 16 * i + 4 * lg + ii) ? acc[ii] : 0.f;
@@ -522,20 +798,30 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
     }
   }
   __syncthreads();
+  // exact diagonal tiles of the blocks beyond the fast tiles' range (range-safe path only)
+  if (wide) {
+#pragma unroll
+    for (int I = 0; I < NB; ++I)
+      if (flags[I]) prep_diag_exact<T, LC, D, Gates, NT>(a, gates, bh, c, I, smem, Af, Pb, gB);
+  }
 
   // ---- T = (I + A)^-1 (fp32), then a dtype copy for the WY products; the backward
-  // modes also keep that copy of the chunk (row-major [LC][LC])
-  // inlined in the modes that keep T for the backward: there the out-of-line call's wait
-  // for the gate pass's K->^T stores cost more than the extra registers (measured; the
-  // forward-only and content-aware prep keep the call)
-  if constexpr (BWD) triangular_inverse_inl<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
-  else triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
+  // modes also keep that copy and P of the chunk (row-major [LC][LC]).  The solve is an
+  // out-of-line call in every mode (inlined, its registers add to the persistent loop's
+  // prefetch and spill)
+  triangular_inverse<LC, LDF, NT>((lds_float*)Af, (lds_float*)Tf);
   after_solve();
   for (int idx = tid; idx < LC * LC / 4; idx += NT) {
     const int r = idx / (LC / 4), s = 4 * (idx % (LC / 4));
     const f32x4 t4 = ((s >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(Tf + r * LDF + s);
     store4(Tb + r * LDL + s, t4);
-    if (BWD) store4(reinterpret_cast<T*>(a.f.Tt) + (ci * LC + r) * LC + s, t4);
+    if (BWD) {
+      store4(reinterpret_cast<T*>(a.f.Tt) + (ci * LC + r) * LC + s, t4);
+      if (wide) {   // the range-safe backward takes P from here
+        const f32x4 p4 = ((s >> 4) > (r >> 4)) ? f32x4{0.f, 0.f, 0.f, 0.f} : load4f(Pb + r * LDL + s);
+        store4(reinterpret_cast<T*>(a.f.Pt) + (ci * LC + r) * LC + s, p4);
+      }
+    }
   }
   __syncthreads();
 
@@ -612,7 +898,10 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       for (int kb = 0; kb <= i / 2; ++kb) pa[i][kb] = load_frag(Pb + (16 * i + lr) * LDL + 32 * kb + 8 * lg);
     f32x4 aq[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) aq[i] = lds_acc_tile(Qp, LDD, 16 * i, 16 * ct);
+    for (int i = 0; i < NB; ++i) {
+      aq[i] = lds_acc_tile(Qp, LDD, 16 * i, 16 * ct);
+      if (wide) aq[i] *= gbeT[i * D + col];   // Q+ = Q^+ e^Gb
+    }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       f32x4 ao = {0.f, 0.f, 0.f, 0.f};
@@ -635,6 +924,7 @@ __device__ __forceinline__ void prep_compute(const FwdArgs& a, const Gates& gate
       acc = f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
       acc = lds_acc_tile(Qp, LDD, 16 * i, 16 * ct);
+      if (wide) acc *= gbeT[i * D + col];   // Q+ = Q^+ e^Gb
     }
     const T* Bs = isO ? UbTs : WnT;
     for (int kk = 0; kk < 16 * (i + 1); kk += 32) {

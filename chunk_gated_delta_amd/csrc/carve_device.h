@@ -54,6 +54,12 @@ __device__ __forceinline__ void for_wave_items(int wave, Fn&& fn) {
   }
 }
 
+// Hardware exponential and logarithm (v_exp_f32 / v_log_f32, base 2, about 1 ulp): no
+// range reduction or denormal fix-up around them.  Results below float range flush to 0,
+// log of 0 (or of a flushed denormal) is -inf; the callers' range logic expects exactly that.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
+
 // ------------------------------------------------------------------ fragments
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { bf16x8 v; };
@@ -115,6 +121,9 @@ __device__ __forceinline__ Frag<float> lds_frag_cols(const float* m, int ld, int
   const int lane = lane_id();
   return load_frag_strided(m + (k0 + 8 * (lane >> 4)) * ld + c0 + (lane & 15), ld);
 }
+// element e (0..7) of a fragment
+__device__ __forceinline__ bf16 frag_elem(const Frag<bf16>& f, int e) { return f.v[e]; }
+__device__ __forceinline__ float frag_elem(const Frag<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
 __device__ __forceinline__ Frag<bf16> zero_frag(bf16) {
   Frag<bf16> f;
 #pragma unroll
@@ -243,6 +252,57 @@ __device__ __forceinline__ f32x4 load4f(const float* p) { return *reinterpret_ca
 __device__ __forceinline__ f32x4 load4f(const bf16* p) {
   bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
   return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+
+// ------------------------------------------------------------------ 16-deep products
+// One 16-token block of a contraction: v_mfma_f32_16x16x16_bf16 (bf16) or four
+// v_mfma_f32_16x16x4_f32 steps (fp32).  Operand layouts:
+//   bf16  A: lane l holds A[l % 16][4 (l / 16) + j]        B: B[4 (l / 16) + j][l % 16], j = 0..3
+//   fp32  A: lane l holds A[l % 16][4 s + l / 16] (step s) B: B[4 s + l / 16][l % 16]
+// (A and B share the k permutation, so the sum is unchanged); C as the 32-deep form.
+template <typename T> struct Frag16;
+template <> struct Frag16<bf16> { bf16x4 v; };
+template <> struct Frag16<float> { f32x4 v; };
+
+__device__ __forceinline__ void mma16(f32x4& c, const Frag16<bf16>& a, const Frag16<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a.v), __builtin_bit_cast(i16x4, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& c, const Frag16<float>& a, const Frag16<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+// Fragment whose 16 rows are rows r0.. of a row-major LDS matrix M (stride ld) and whose
+// 16-deep k block starts at column k0 (the A operand of a matrix stored [row][k]).
+__device__ __forceinline__ Frag16<bf16> lds_frag16_rows(const bf16* m, int ld, int r0, int k0) {
+  const int lane = lane_id();
+  Frag16<bf16> f;
+  f.v = *reinterpret_cast<const bf16x4*>(m + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+  return f;
+}
+__device__ __forceinline__ Frag16<float> lds_frag16_rows(const float* m, int ld, int r0, int k0) {
+  const int lane = lane_id();
+  Frag16<float> f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f.v[s] = m[(r0 + (lane & 15)) * ld + k0 + 4 * s + (lane >> 4)];
+  return f;
+}
+// Fragment whose 16 rows are columns c0.. of a row-major LDS matrix M and whose k block
+// is rows k0 .. k0 + 15 (the B operand of a matrix stored [k][column], or the A operand
+// of one stored transposed).  bf16: one LDS transpose read, lane s of each 16-lane group
+// g pointing at row k0 + 4 g + s / 4, columns c0 + 4 (s % 4) (see lds_frag_tr).
+__device__ __forceinline__ Frag16<bf16> lds_frag16_cols(const bf16* m, int ld, int c0, int k0) {
+  const int lane = lane_id(), s = lane & 15, g = lane >> 4;
+  bf16* p = const_cast<bf16*>(m) + (k0 + 4 * g + (s >> 2)) * ld + c0 + 4 * (s & 3);
+  Frag16<bf16> f;
+  f.v = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
+  return f;
+}
+__device__ __forceinline__ Frag16<float> lds_frag16_cols(const float* m, int ld, int c0, int k0) {
+  const int lane = lane_id();
+  Frag16<float> f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) f.v[s] = m[(k0 + 4 * s + (lane >> 4)) * ld + c0 + (lane & 15)];
+  return f;
 }
 
 // padded leading dimensions for LDS tiles: rows shifted by 16 bytes to spread banks

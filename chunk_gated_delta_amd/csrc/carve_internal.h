@@ -22,6 +22,11 @@ namespace carve {
 // The reverse state pass reads Wn, Qt and KfT too (transposed on chip); the backward
 // modes also write
 //   Tt  [ci][LC][LC] row-major, T = (I + A)^-1 (dtype)
+//   cflag [ci] the chunk's path (1: range-safe, whose log-retention over the chunk
+//       fell below the fast path's range in some key channel), and for those chunks
+//   Pt  [ci][LC][LC] row-major, P (dtype)
+//   Bt  [ci][NTRI][64][4], B = A before the row scaling by w (strictly lower
+//       coupling), the lower 16x16 tiles (tri index) in accumulator order (dtype)
 // Prep modes: 1 = forward only, 2 = backward only (no OiT), 3 = both.
 struct ChunkFactors {
   void* Wn;
@@ -31,6 +36,9 @@ struct ChunkFactors {
   void* OiT;
   float* gL;
   void* Tt;               // [ci][LC][LC] T = (I + A)^-1 in the operand type (backward modes)
+  void* Pt;               // [ci][LC][LC] P (backward modes, range-safe chunks)
+  void* Bt;               // [ci][LC*LC] B tiles in accumulator order (backward modes, range-safe chunks)
+  int* cflag;             // [ci] 1 = the chunk took the range-safe path (backward modes)
 };
 
 struct FwdArgs {
@@ -88,13 +96,19 @@ struct BwdArgs {
   void* dv;
   float* dlog_g;
   float* db;              // may be null (iff b is null)
+  int db_mode;            // what db receives: 0 d/db; 1 d/dx for b = sigmoid(x) given as b, i.e. dlog a (1 - b)
   float* dw;
   float* dS0;             // may be null
   // chunk range of the backward kernels: chunks c_lo .. c_lo + c_count - 1 of every
   // head (c_count = 0: all chunks).  The reverse state pass starts from dS_T and
   // ends in dS0 for that range.
   int c_lo, c_count;
+  // Range-safe chunks: diag [ci][NB][2][64][4] (dtype) receives the diagonal tiles of
+  // dP and dB of the blocks whose log-retention leaves the fast tiles' range (accumulator
+  // order); the same workgroup reads them back for those blocks' exact terms.
+  void* diag;
 };
+size_t diag_fix_bytes(int dtype, int BH, int NC, int LC);
 
 // One recurrent decode step (one token per batch and head), state updated in place.
 struct DecodeArgs {

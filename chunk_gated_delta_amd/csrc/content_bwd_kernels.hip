@@ -2,8 +2,9 @@
 //
 // Once the forward has run, every content period p (L tokens) has a fixed gate
 // b = sigmoid(b_x + z_p), z_p = U2 (U1 m_{p-1}); the chunk gradients are those of the
-// token-only rule with that b.  What couples the periods is the mean output: m_{p-1}
-// feeds z_p, so period p's gate gradient dx = db * b (1 - b) gives
+// token-only rule with that b, the erase gradient taken directly w.r.t. the gate's
+// pre-activation (dx = dlog a (1 - b) = db b (1 - b)).  What couples the periods is the
+// mean output: m_{p-1} feeds z_p, so period p's gate gradient dx gives
 //   dz_p = sum_t dx_t,  dU2 += dz_p r_p^T (r_p = U1 m_{p-1}),  dr = U2^T dz_p,
 //   dU1 += dr m_{p-1}^T,  dm_{p-1} = U1^T dr,
 // and dm_{p-1} / L is added to the output gradient of every token of period p-1
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void content_gates_kernel(ContentBwdArgs a, co
     const f32x4 x = *reinterpret_cast<const f32x4*>(b_x + e);
     f32x4 b;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = 1.f / (1.f + __expf(-(x[j] + z[j])));
+    for (int j = 0; j < 4; ++j) b[j] = 1.f / (1.f + fexp(-(x[j] + z[j])));
     *reinterpret_cast<f32x4*>(bmat + e) = b;
   }
 }
@@ -49,12 +50,12 @@ __global__ __launch_bounds__(256) void add_grad_mean_kernel(ContentBwdArgs a, co
   }
 }
 
-// Gate backward of period p for one head (one workgroup per head):
-// db (w.r.t. the gate probability, from the chunk-gradient kernel) -> db_x in place,
-// then the projection's gradients and the output-gradient term g of period p-1, which
+// Gate backward of period p for one head (one workgroup per head): the sum of the
+// period's d/db_x (from the chunk-gradient kernel) per key channel, then the projection's
+// gradients and the output-gradient term g of period p-1, which
 // is added at once to that period's dO (into dOp; period 0's dm goes to m0).
 // Nothing this kernel loads depends on what it computes, so every load is issued at the
-// start (db and b of the first 64 tokens, U1 and U2 for LDS, m_{p-1}, the running dU
+// start (d/db_x of the first 64 tokens, U1 and U2 for LDS, m_{p-1}, the running dU
 // sums, the first 64 tokens of period p-1's dO): one round trip to memory instead of one
 // per phase.  The rank contractions run 16 lanes per rank index with DPP row sums.
 template <typename T, int D>
@@ -78,14 +79,12 @@ __global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a,
   float* U2s = Us + RD;
 
   // ---- every load
-  float bv[TPT], gv[TPT];
+  float gv[TPT];
   auto load_batch = [&](int tb) {
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int t = min(tb + part + NPART * j, t1 - 1);
-      const size_t i = ((size_t)bh * a.T + t) * D + k;
-      bv[j] = a.bmat[i];
-      gv[j] = a.dbx[i];
+      gv[j] = a.dbx[((size_t)bh * a.T + t) * D + k];
     }
   };
   load_batch(t0);
@@ -124,18 +123,14 @@ __global__ __launch_bounds__(256) void content_gate_bwd_kernel(ContentBwdArgs a,
   }
   if (tid < D) mS[tid] = mv;
 
-  // ---- dx = db * b (1 - b), written back as d/db_x and summed over the period's tokens
-  // per key column (each thread in token order)
+  // ---- dx = d/db_x (the chunk-gradient kernel already wrote dlog a (1 - b)), summed over
+  // the period's tokens per key column (each thread in token order)
   float acc = 0.f;
   for (int tb = t0;;) {
 #pragma unroll
     for (int j = 0; j < TPT; ++j) {
       const int t = tb + part + NPART * j;
-      if (t < t1) {
-        const float dx = gv[j] * bv[j] * (1.f - bv[j]);
-        a.dbx[((size_t)bh * a.T + t) * D + k] = dx;
-        acc += dx;
-      }
+      if (t < t1) acc += gv[j];
     }
     tb += 64;
     if (tb >= t1) break;

@@ -655,14 +655,21 @@ static size_t factor_block(int dtype, int BH, int NC, int LC, int D) {  // one [
 }
 
 // Factor blocks in the workspace: -W, K->^T, Ubar^T, Q~ always; P Ubar with the
-// forward mode; then Gamma_L, and with the backward mode the inverse T of every chunk
-// (LC x LC, dtype).
+// forward mode; then Gamma_L, and with the backward mode the inverse T, the intra-chunk
+// weights P and the coupling B of every chunk (LC x LC each, dtype; P and B written for
+// range-safe chunks only) and the chunks' path flags.
 static int factor_blocks(int mode) { return 4 + ((mode & 1) ? 1 : 0); }
 static size_t gl_block(int BH, int NC, int D) { return ((size_t)BH * NC * D * sizeof(float) + 255) & ~size_t(255); }
 
+static size_t tile_block(int dtype, int BH, int NC, int LC) {   // one [chunk][LC][LC] block
+  return ((size_t)BH * NC * LC * LC * (dtype ? 2 : 4) + 255) & ~size_t(255);
+}
+
+static size_t flag_block(int BH, int NC) { return ((size_t)BH * NC * sizeof(int) + 255) & ~size_t(255); }
+
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode) {
   return factor_blocks(mode) * factor_block(dtype, BH, NC, LC, D) + gl_block(BH, NC, D) +
-         ((mode & 2) ? (size_t)BH * NC * LC * LC * (dtype ? 2 : 4) : 0);
+         ((mode & 2) ? 3 * tile_block(dtype, BH, NC, LC) + flag_block(BH, NC) : 0);
 }
 
 ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode) {
@@ -676,7 +683,12 @@ ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, i
   f.Qt = p + blk * i++;
   f.OiT = (mode & 1) ? p + blk * i++ : nullptr;
   f.gL = reinterpret_cast<float*>(p + blk * i);
-  f.Tt = (mode & 2) ? p + blk * i + gl_block(BH, NC, D) : nullptr;
+  char* tiles = p + blk * i + gl_block(BH, NC, D);
+  const size_t tb = tile_block(dtype, BH, NC, LC);
+  f.Tt = (mode & 2) ? tiles : nullptr;
+  f.Pt = (mode & 2) ? tiles + tb : nullptr;
+  f.Bt = (mode & 2) ? tiles + 2 * tb : nullptr;
+  f.cflag = (mode & 2) ? reinterpret_cast<int*>(tiles + 3 * tb) : nullptr;
   return f;
 }
 

@@ -49,10 +49,20 @@
  *     token-only gates (the result does not depend on L; the kernels tile
  *     tokens in blocks of 32 when L <= 32 or dtype is float32, and of 64
  *     otherwise); for the content path L must be a multiple of that tile.
- *   - Numerical range: the chunk kernels form products exp(G_r) and exp(-G_s)
- *     of the cumulative log-retention G inside one tile of tokens, so every
- *     key channel's retention accumulated over one tile must stay above about
- *     1e-30 (|sum of log a| < ~69 per 64 tokens); beyond that outputs are NaN.
+ *   - Numerical range: any retention a = exp(log g) * b in [0, 1] is handled
+ *     (the pages put no floor on the decay, notes section 2.3, and take the
+ *     erase as a factor in (0, 1], section 2.1).  The kernels carry the
+ *     cumulative log-retention inside each tile of tokens: a tile whose
+ *     log-retention stays above -80 in every key channel refers its operands
+ *     to the tile start; a stronger tile refers them to 16-token blocks, and a
+ *     block beyond -64 computes its within-block ratios as running products of
+ *     the retention.  Per-token log-retention is taken in [-1e4, 0] (values above
+ *     0 count as 0, a retention below e^-1e4 as e^-1e4, zero in float32).
+ *   - Conditioning of the erase gradient: d/db = d/dlog a / b carries the
+ *     absolute error of d/dlog a (a reverse cumulative sum over the tile)
+ *     divided by b, so it is ill-conditioned where b is small; d/dlog g (which
+ *     equals b * d/db) and the pre-activation gradients d/db_x = d/dlog a (1 - b)
+ *     of carve_bwd_logits and carve_bwd_content are well conditioned.
  */
 #ifndef CARVE_H
 #define CARVE_H

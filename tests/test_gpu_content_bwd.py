@@ -96,15 +96,15 @@ def test_content_bwd_parity(dtype, B, H, T, D, L):
 
 
 def test_content_bwd_rank64():
-    """The largest projection rank (64) at width 64, over several periods.  (Projection scale
-    8: larger scales drive sigma(b_x + z) so low that a channel's retention over one tile
-    leaves the dynamic range the chunk products support.)"""
+    """The largest projection rank (64) at width 64, over several periods, with the
+    projection scaled by 64: sigma(b_x + z) then reaches hard erase on many channels,
+    so tiles of tokens take the range-safe path as well as the fast one."""
     announce("content bwd rank 64 d64")
     B, H, T, D, L = 2, 2, 150, 64, 32
     inp = random_inputs(B, H, T, D, D, dtype="bf16", seed=321, erase="content", dists="softplus_decay",
                         with_dO=True, rank=64)
-    inp["U1"] = inp["U1"] * 8.0
-    inp["U2"] = inp["U2"] * 8.0
+    inp["U1"] = inp["U1"] * 64.0
+    inp["U2"] = inp["U2"] * 64.0
     rng = np.random.default_rng(322)
     ex = {"m0": np.asarray(rng.standard_normal((B, H, D)) * 0.5, np.float32).astype(np.float64),
           "S0": np.asarray(rng.standard_normal((B, H, D, D)) * 0.3, np.float32).astype(np.float64),

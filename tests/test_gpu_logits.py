@@ -28,7 +28,7 @@ def logit_case(B, H, T, D, dtype, seed, with_bx=True):
     inp = random_inputs(B, H, T, D, D, dtype=dtype, seed=seed, erase="none", with_dO=True)
     rng = np.random.default_rng(seed + 7)
     inp["f"] = f32np(rng.standard_normal((B, H, T, D)))
-    inp["A"] = f32np(rng.uniform(0.05, 0.5, (H, D)))
+    inp["A"] = f32np(rng.uniform(0.05, 10.0, (H, D)))   # amplitudes up to 10: strong decay included
     inp["tau"] = f32np(rng.standard_normal((H, D)) * 0.5)
     inp["w_hat"] = f32np(rng.standard_normal((B, H, T)))
     inp["b_x"] = f32np(rng.normal(2.0, 1.0, (B, H, T, D))) if with_bx else None
