@@ -99,6 +99,8 @@ def load_library():
     pp = ctypes.POINTER(carve_profile)
     lib.carve_fwd_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, sz, vp, pp]
     lib.carve_fwd_ex.restype = i
+    lib.carve_fwd_noalloc.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp]
+    lib.carve_fwd_noalloc.restype = i
     lib.carve_bwd_ex.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, pp]
     lib.carve_bwd_ex.restype = i
     lib.carve_bwd.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -185,15 +187,9 @@ def fwd_workspace_bytes(q, v, L=64, content=False):
     return lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(c) if c is not None else None)
 
 
-def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None, workspace=None,
-        want_state=True, profile=None):
-    """o, S_T, m_out = fwd(...).
-
-    q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, one dtype); log_g, b [B,H,T,Dk]
-    float32; w [B,H,T] float32; S0 [B,H,Dv,Dk] float32 or None.  content is None or a dict
-    with b_x [B,H,T,Dk], U1 [H,R,Dv] / U2 [H,Dk,R] (or None), m0 [B,H,Dv] (or None), and
-    optionally z_rec / m_rec (content_records), which the forward fills.
-    Outputs may be passed preallocated (o, S_T, workspace)."""
+def _fwd_args(q, k, v, log_g, w, b, S0, L, content, o, S_T, want_state):
+    """Checks and marshalling shared by fwd and fwd_noalloc: (lib, shape, content struct or
+    None, o, S_T, m_out, objects to keep alive during the call)."""
     lib = load_library()
     B, H, T, Dk = q.shape
     Dv = v.shape[-1]
@@ -231,6 +227,20 @@ def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None
         o = torch.empty((B, H, T, Dv), dtype=dt, device=dev)
     if S_T is None and want_state:
         S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    return lib, s, cs, o, S_T, m_out, keep
+
+
+def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None, workspace=None,
+        want_state=True, profile=None):
+    """o, S_T, m_out = fwd(...).
+
+    q, k [B,H,T,Dk], v [B,H,T,Dv] (float32 or bfloat16, one dtype); log_g, b [B,H,T,Dk]
+    float32; w [B,H,T] float32; S0 [B,H,Dv,Dk] float32 or None.  content is None or a dict
+    with b_x [B,H,T,Dk], U1 [H,R,Dv] / U2 [H,Dk,R] (or None), m0 [B,H,Dv] (or None), and
+    optionally z_rec / m_rec (content_records), which the forward fills.
+    Outputs may be passed preallocated (o, S_T, workspace)."""
+    lib, s, cs, o, S_T, m_out, keep = _fwd_args(q, k, v, log_g, w, b, S0, L, content, o, S_T, want_state)
+    dev = q.device
     need = lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(cs) if cs is not None else None)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -239,6 +249,18 @@ def fwd(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None
                             _ptr(workspace), workspace.numel(), _stream(dev),
                             ctypes.byref(profile) if profile is not None else None)
     _raise(code, "carve_fwd")
+    return o, S_T, m_out
+
+
+def fwd_noalloc(q, k, v, log_g, w, b=None, S0=None, L=64, content=None, o=None, S_T=None, want_state=True):
+    """fwd() through carve_fwd_noalloc: no workspace, the library's fixed device scratch
+    instead (outputs may be passed preallocated; the C entry point itself allocates
+    nothing).  Raises RuntimeError (CARVE_ERR_WORKSPACE) for shapes beyond the scratch."""
+    lib, s, cs, o, S_T, m_out, keep = _fwd_args(q, k, v, log_g, w, b, S0, L, content, o, S_T, want_state)
+    code = lib.carve_fwd_noalloc(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(b), _ptr(w),
+                                 _ptr(S0), ctypes.byref(cs) if cs is not None else None, _ptr(o), _ptr(S_T),
+                                 _stream(q.device))
+    _raise(code, "carve_fwd_noalloc")
     return o, S_T, m_out
 
 

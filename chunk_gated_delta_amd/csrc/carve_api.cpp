@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -204,6 +205,32 @@ char* align_up(void* p) {
   return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255));
 }
 
+// Library-owned scratch of carve_fwd_noalloc: one copy of this array on every device the
+// library runs on (held until the process ends).  Its name is a host-side stand-in;
+// the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[CARVE_NOALLOC_SCRATCH_BYTES];
+
+void* scratch_address(carve_status* st) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *st = CARVE_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      *st = CARVE_ERR_HIP;
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  *st = CARVE_OK;
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +309,21 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
     mark(prof, 2, hs);
   }
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+carve_status carve_fwd_noalloc(const carve_shape* s, const void* q, const void* k, const void* v,
+                               const float* log_g, const float* b, const float* w, const float* S0,
+                               const carve_content* content, void* o, float* S_T, void* stream) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  st = check_content(s, p, content, b);
+  if (st != CARVE_OK) return st;
+  if (fwd_ws(s, p, content) > CARVE_NOALLOC_SCRATCH_BYTES) return CARVE_ERR_WORKSPACE;
+  void* ws = scratch_address(&st);
+  if (st != CARVE_OK) return st;
+  return carve_fwd_ex(s, q, k, v, log_g, b, w, S0, content, o, S_T, ws, CARVE_NOALLOC_SCRATCH_BYTES, stream,
+                      nullptr);
 }
 
 carve_status carve_bwd(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,

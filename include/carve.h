@@ -32,8 +32,9 @@
  *     gates, states, workspace-independent outputs marked float are float32.
  *   - The caller owns every buffer, including the workspace, which must hold at
  *     least *_workspace_size() bytes.  The library never allocates or frees
- *     device memory; its only global state is a per-device cache of the
- *     compute-unit count (the size of its persistent launches).  Calls on
+ *     device memory; its global state is a per-device cache of the compute-unit
+ *     count (the size of its persistent launches) and, for carve_fwd_noalloc
+ *     only, a fixed device array with its per-device address.  Calls on
  *     different streams may run concurrently as long as they use different
  *     workspaces.
  *   - Every launch is enqueued on `stream` (a hipStream_t; NULL = default
@@ -73,7 +74,7 @@
 extern "C" {
 #endif
 
-#define CARVE_ABI_VERSION 2
+#define CARVE_ABI_VERSION 3
 
 typedef enum {
   CARVE_OK = 0,
@@ -134,6 +135,26 @@ carve_status carve_fwd(const carve_shape* s,
                        const float* S0, const carve_content* content,
                        void* o, float* S_T,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): carve_fwd with the same
+ * arguments minus the workspace, which is instead a library-owned device array of
+ * CARVE_NOALLOC_SCRATCH_BYTES on each device (held until the process ends; its address
+ * is looked up once per device on the first call there).  The call allocates and frees
+ * nothing.  A shape whose carve_fwd_workspace_size() exceeds the array returns
+ * CARVE_ERR_WORKSPACE before any launch.  Every call on one device shares that device's
+ * array: calls that overlap in time on one device (different streams, or host threads
+ * with unsynchronised streams) race on it and must be serialised by the caller.  No part
+ * of the array needs to start at zero: every byte a call reads is written earlier in the
+ * same call.
+ */
+#define CARVE_NOALLOC_SCRATCH_BYTES (64u << 20)
+carve_status carve_fwd_noalloc(const carve_shape* s,
+                               const void* q, const void* k, const void* v,
+                               const float* log_g, const float* b, const float* w,
+                               const float* S0, const carve_content* content,
+                               void* o, float* S_T, void* stream);
 
 /* Bytes of device workspace carve_bwd needs for this shape. */
 size_t carve_bwd_workspace_size(const carve_shape* s);

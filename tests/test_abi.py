@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.carve_abi_version() == 2
+    assert lib.carve_abi_version() == 3
     for code in range(5):
         assert carve.status_string(code).startswith("CARVE_")
 
@@ -232,3 +232,16 @@ def test_logits_entry_points_reject_bad_arguments(lib):
     assert bwd(g, db_x=FAKE) == INVALID                                                # db_x only with b_x
     assert bwd(carve.carve_gate_logits(FAKE, FAKE, FAKE, FAKE, FAKE)) == INVALID       # ... and then required
     assert bwd(g, ws_bytes=need - 1) == WORKSPACE
+
+
+def test_noalloc_rejects_beyond_scratch_on_host(lib):
+    """carve_fwd_noalloc checks the shape's workspace against its fixed scratch before it
+    touches the device (B2 H16 T2048 d128 bf16 needs more than 64 MiB)."""
+    s = shape(B=2, H=16, T=2048)
+    need = lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+    assert need > (64 << 20)
+    assert lib.carve_fwd_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None,
+                                 None) == WORKSPACE
+    # argument errors come first, as for carve_fwd
+    assert lib.carve_fwd_noalloc(ctypes.byref(shape(Dv=64)), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                                 FAKE, None, None) == UNSUPPORTED
