@@ -16,11 +16,15 @@ Roofline: every stage is bracketed with HIP events on the stream it runs on
 largest mean duration is the dominant kernel, and its achieved bandwidth is
 its algorithmic bytes (inputs it must read plus outputs it must write, per
 token-head, times the token-heads of one launch) over that mean duration.
+That figure is set against the published 8 TB/s and against the copy bandwidth
+measured in the same run (the library's streaming copy kernel and torch's copy
+over 1 GiB); the MFMA-busy fraction and MFMA flop rate of the dominant kernel
+come from the committed rocprofv3 counter summary while the kernel sources are
+unchanged since it was taken.
 """
 import argparse
 import json
 import os
-import platform
 import sys
 import time
 
@@ -41,7 +45,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--pass", dest="passes", default="fwd+bwd", choices=["fwd+bwd", "fwd"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    p.add_argument("--cpu-sample-heads", type=int, default=64,
+                   help="(batch, head) sequences of the workload the CPU oracle runs (full length)")
     p.add_argument("--no-content", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the long-context forward")
     p.add_argument("--no-decode", action="store_true", help="skip the recurrent decode step")
@@ -74,6 +79,7 @@ def algorithmic(wl, with_bwd):
 
 
 TRAFFIC_SUMMARY = os.path.join(HERE, "profiles", "head1p3b_fwd_bwd_hbm_traffic.md")
+MFMA_SUMMARY = os.path.join(HERE, "profiles", "head1p3b_fwd_bwd_mfma.md")
 STAGE_KERNEL = {"fwd_prep": "fwd_prep_kernel", "fwd_state": "fwd_state_kernel",
                 "bwd_state_rev": "bwd_state_kernel", "bwd_chunk_grads": "bwd_chunk_kernel"}
 
@@ -89,6 +95,41 @@ def measured_traffic(stage):
         return None
     b = rec["bytes_per_launch"].get(STAGE_KERNEL.get(stage, ""))
     return None if b is None else int(b["read"] + b["write"])
+
+
+def measured_mfma(stage):
+    """MFMA-busy fraction and MFMA flops of a training-step kernel from the committed rocprofv3
+    counter summary, or None when the kernel sources changed after the counters were taken."""
+    from chunk_gated_delta_amd.build import source_digest
+    from chunk_gated_delta_amd.prof_summary import read_mfma
+    rec = read_mfma(MFMA_SUMMARY)
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec["kernels"].get(STAGE_KERNEL.get(stage, ""))
+
+
+def copy_bandwidth(dev, mib=1024, nrep=10):
+    """Achievable device copy bandwidth (GB/s, bytes read + written over time), measured live
+    with the library's streaming copy kernel and with torch's copy on a `mib` MiB buffer."""
+    import torch
+    from chunk_gated_delta_amd import carve
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    nbytes = 2 * src.numel() * 4
+    out = {}
+    for name, fn in (("stream_copy", lambda: carve.stream_copy(dst, src)), ("torch_copy", lambda: dst.copy_(src))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(nrep):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(nbytes / (e0.elapsed_time(e1) / nrep * 1e-3) / 1e9, 1)
+    del src, dst
+    return out
 
 
 def main():
@@ -336,6 +377,16 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
                 "bytes_per_token_head": stage_bytes[dom], "launch_ms": round(dom_ms, 4)}
+    copy_gbs = copy_bandwidth(dev)
+    measured_peak = max(copy_gbs.values())
+    roofline["measured_copy_GBs"] = copy_gbs
+    roofline["measured_peak"] = measured_peak
+    roofline["frac_of_measured"] = round(ach / measured_peak, 4)
+    mf = measured_mfma(dom) if with_bwd else None
+    if mf is not None:
+        roofline["mfma_busy_frac"] = mf["busy_frac"]
+        roofline["mfma_tflops"] = mf["tflops"]
+        roofline["mfma_frac_of_bf16_peak"] = None if mf["tflops"] is None else round(mf["tflops"] / BF16_PEAK_TFLOPS, 4)
     traffic = measured_traffic(dom) if with_bwd else None
     if traffic is not None:
         roofline["traffic"] = traffic
@@ -344,7 +395,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, wl, args.cpu_sample_tokens, with_bwd)
+        cpu = cpu_baseline(inp, wl, args.cpu_sample_heads, with_bwd)
 
     tokens = B * T
     line = {
@@ -442,20 +493,28 @@ def es_do(wl):
     return (2 if wl.dtype == "bf16" else 4) * wl.Dv
 
 
-def cpu_baseline(inp, wl, t_sample, with_bwd):
-    """The float64 reference timed on the host on the first t_sample tokens of every head."""
-    import oracle
-    sl = {k_: v_[:, :, :t_sample] for k_, v_ in inp.items() if not k_.endswith("_bits") and np.ndim(v_) >= 3}
-    t0 = time.perf_counter()
-    oracle.forward(sl["q"], sl["k"], sl["v"], sl["log_g"], sl["w"], b=sl.get("b"), L=wl.L)
-    if with_bwd:
-        oracle.backward(sl["q"], sl["k"], sl["v"], sl["log_g"], sl["w"], sl["dO"], b=sl.get("b"))
-    dt = time.perf_counter() - t0
-    return {"value": wl.B * t_sample / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"all {wl.B}x{wl.H} heads, first {t_sample} of {wl.T} tokens, "
-                      f"{'forward+backward' if with_bwd else 'forward'}, float64 numpy, single process",
-            "seconds": round(dt, 2), "cpu": platform.processor() or platform.machine(),
-            "numpy": np.__version__}
+def cpu_baseline(inp, wl, n_heads, with_bwd):
+    """The float64 reference timed on the host: the first n_heads (batch, head) sequences of
+    the workload over the full sequence length, split over a pool of host processes (one per
+    core this process may use, at most 16), scaled to the workload's tokens."""
+    from oracle.head_pool import HeadPool, cpu_model, host_workers
+    BH = wl.B * wl.H
+    n_heads = max(1, min(n_heads, BH))
+    sl = {k_: v_.reshape((1, BH) + v_.shape[2:])[:, :n_heads]
+          for k_, v_ in inp.items() if not k_.endswith("_bits") and np.ndim(v_) >= 3}
+    kw = dict(q=sl["q"], k=sl["k"], v=sl["v"], log_g=sl["log_g"], w=sl["w"], b=sl.get("b"))
+    workers = host_workers()
+    with HeadPool(workers) as pool:
+        t0 = time.perf_counter()
+        pool.run("forward", 1, n_heads, groups=workers, L=wl.L, **kw)
+        if with_bwd:
+            pool.run("backward", 1, n_heads, groups=workers, dO=sl["dO"], **kw)
+        dt = time.perf_counter() - t0
+    return {"value": wl.B * wl.T * (n_heads / BH) / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{n_heads} of the {wl.B}x{wl.H} (batch, head) sequences, all {wl.T} tokens, "
+                      f"{'forward+backward' if with_bwd else 'forward'}, float64 numpy, {workers} processes "
+                      f"of one thread; tokens/s scaled by {n_heads}/{BH} of the workload",
+            "seconds": round(dt, 2), "cpu": cpu_model(), "numpy": np.__version__}
 
 
 if __name__ == "__main__":

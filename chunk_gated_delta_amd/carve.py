@@ -129,6 +129,8 @@ def load_library():
     dcp = ctypes.POINTER(carve_decode_content)
     lib.carve_decode_step.argtypes = [sp, vp, vp, vp, vp, vp, vp, vp, dcp, vp, vp]
     lib.carve_decode_step.restype = i
+    lib.carve_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.carve_stream_copy.restype = i
     lib.carve_status_string.argtypes = [i]
     lib.carve_status_string.restype = ctypes.c_char_p
     lib.carve_abi_version.argtypes = []
@@ -541,3 +543,17 @@ def decode_step(q, k, v, log_g, w, S, b=None, L=64, content=None, o=None):
                                  _ptr(S), ctypes.byref(cs) if cs is not None else None, _ptr(o), _stream(dev))
     _raise(code, "carve_decode_step")
     return o, m_out
+
+
+def stream_copy(dst, src):
+    """Copy src into dst (same number of bytes, contiguous device tensors) with the library's
+    streaming copy kernel on the current stream; a measurement helper for the achievable
+    copy bandwidth, not part of the CARVE operation."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("stream_copy: dst and src differ in size")
+    if not (dst.is_contiguous() and src.is_contiguous()) or dst.device != src.device:
+        raise ValueError("stream_copy: contiguous tensors on one device required")
+    code = load_library().carve_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(src.device))
+    _raise(code, "carve_stream_copy")
+    return dst

@@ -820,6 +820,19 @@ carve_status carve_decode_step(const carve_shape* s, const void* q, const void* 
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 
+carve_status carve_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (bytes == 0) return CARVE_OK;
+  if (!dst || !src || bytes % 16 || ((uintptr_t)dst | (uintptr_t)src) % 16) return CARVE_ERR_INVALID_ARG;
+  const uintptr_t d0 = (uintptr_t)dst, s0 = (uintptr_t)src;
+  if (d0 < s0 + bytes && s0 < d0 + bytes) return CARVE_ERR_INVALID_ARG;      // overlapping ranges
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return CARVE_ERR_HIP;
+  return carve::launch_stream_copy(dst, src, bytes / 16, cus, (hipStream_t)stream) == hipSuccess ? CARVE_OK
+                                                                                                  : CARVE_ERR_HIP;
+}
+
 const char* carve_status_string(carve_status st) {
   switch (st) {
     case CARVE_OK: return "CARVE_OK";

@@ -176,5 +176,7 @@ hipError_t launch_content_gate_bwd(const ContentBwdArgs& a, int dtype, const voi
 hipError_t launch_init_grad_mean(const ContentBwdArgs& a, const float* dm_out, hipStream_t st);
 hipError_t launch_sum_over_batch(const float* part, float* out, int B, int H, int n, hipStream_t st);
 hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hipStream_t st);
+// n16 16-byte vectors; cus = compute units of the current device (sizes the grid)
+hipError_t launch_stream_copy(void* dst, const void* src, size_t n16, int cus, hipStream_t st);
 
 }  // namespace carve

@@ -5,7 +5,15 @@
     python -m chunk_gated_delta_amd.prof_summary traffic FETCH_CSV WRITE_CSV --copy-mib N --title T
                                                    --command-fetch C1 --command-write C2 --out F
 
-`stats` tabulates a --kernel-trace --stats run.  `traffic` takes one --pmc FETCH_SIZE
+    python -m chunk_gated_delta_amd.prof_summary mfma COUNTER_CSV --stats-csv KERNEL_STATS_CSV --simds N
+                                                   --title T --command C --command-stats C2 --out F
+
+`stats` tabulates a --kernel-trace --stats run.  `mfma` takes one --pmc run of the MFMA
+counters (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, the derived MfmaUtil, and the
+bf16 / fp32 MFMA op counts SQ_INSTS_VALU_MFMA_MOPS_*, each 512 flops) and the kernel
+statistics of a trace run of the same program, and writes per kernel the fraction of
+SIMD cycles the matrix cores were busy and the MFMA flops per launch and per second,
+again with a machine-readable line for bench.py.  `traffic` takes one --pmc FETCH_SIZE
 run and one --pmc WRITE_SIZE run of `python -m chunk_gated_delta_amd.profile_step
 --copy-mib N` and scales each counter (KiB per dispatch) by what it reads for the
 reference kernel, which reads N MiB and writes N MiB; the per-kernel HBM bytes per
@@ -19,6 +27,7 @@ import statistics
 import sys
 
 TRAFFIC_TAG = "<!-- hbm-traffic: "
+MFMA_TAG = "<!-- mfma: "
 
 
 def short_name(mangled):
@@ -26,7 +35,7 @@ def short_name(mangled):
                 "fwd_content_kernel", "fwd_affine_kernel", "seg_scan_kernel", "decode_kernel",
                 "content_gate_bwd_kernel", "content_gates_kernel", "add_grad_mean_kernel",
                 "init_grad_mean_kernel", "sum_over_batch_kernel", "logit_grads_kernel", "sum_heads_kernel",
-                "copy_or_zero_kernel"):
+                "copy_or_zero_kernel", "stream_copy_kernel"):
         if key in mangled:
             return key
     return mangled[:48]
@@ -111,15 +120,72 @@ def traffic(args):
     open(args.out, "w").write("\n".join(out) + "\n")
 
 
-def read_traffic(path):
-    """The machine-readable record of a traffic summary, or None."""
+def _counters(path):
+    per = {}
+    for r in csv.DictReader(open(path)):
+        per.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def mfma(args):
+    from chunk_gated_delta_amd.build import source_digest
+    per = _counters(args.csv)
+    avg_ns = {r["Name"]: float(r["AverageNs"]) for r in csv.DictReader(open(args.stats_csv))}
+    out = [f"# {args.title}", "", "Commands (from /tmp with TMPDIR=/tmp; repository at $R, PYTHONPATH=$R):", "",
+           "    " + args.command, "    " + args.command_stats, "",
+           "MFMA busy = the share of SIMD cycles in which the matrix core was busy during the dispatch "
+           f"(rocprofv3's MfmaUtil: summed SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x {args.simds} SIMDs; "
+           f"the last column recomputes it from the raw counters, the CSV's GRBM_GUI_ACTIVE being the sum over "
+           f"{args.xcc} XCDs). MFMA flops = "
+           "SQ_INSTS_VALU_MFMA_MOPS_* x 512 per dispatch; TFLOP/s divides them by the kernel's average duration "
+           "in the trace run. Medians over dispatches.", "",
+           "| kernel | dispatches | average us | MFMA busy % | bf16 MFMA GFLOP | fp32 MFMA GFLOP | MFMA TFLOP/s | "
+           "busy / (GUI x SIMDs) % |", "|---|---|---|---|---|---|---|---|"]
+    record = {"source_digest": source_digest(), "simds": args.simds, "kernels": {}}
+    for name, c in per.items():
+        if "carve" not in name:
+            continue
+        med = {k_: statistics.median(v_) for k_, v_ in c.items()}
+        n = max(len(v_) for v_ in c.values())
+        util = med.get("MfmaUtil")
+        raw = None
+        if med.get("GRBM_GUI_ACTIVE"):
+            # the CSV sums GRBM_GUI_ACTIVE over the XCDs, each of which counts the dispatch's cycles
+            raw = med.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (med["GRBM_GUI_ACTIVE"] / args.xcc * args.simds)
+        busy = util / 100.0 if util is not None else raw
+        fb = med.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        ff = med.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512
+        ns = avg_ns.get(name)
+        tf = (fb + ff) / (ns * 1e-9) / 1e12 if ns else None
+        out.append(f"| {short_name(name)} | {n} | {ns / 1e3 if ns else float('nan'):.1f} | "
+                   f"{100 * busy if busy is not None else float('nan'):.1f} | {fb / 1e9:.2f} | {ff / 1e9:.2f} | "
+                   f"{tf if tf is not None else float('nan'):.1f} | {100 * raw if raw is not None else float('nan'):.1f} |")
+        record["kernels"][short_name(name)] = {
+            "busy_frac": None if busy is None else round(busy, 4), "bf16_flops": fb, "f32_flops": ff,
+            "tflops": None if tf is None else round(tf, 2), "avg_us": None if not ns else round(ns / 1e3, 1)}
+    out += ["", "Kernel sources digest at measurement: `" + record["source_digest"] + "`", "",
+            MFMA_TAG + json.dumps(record) + " -->"]
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
+def _read_tagged(path, tag):
     try:
         for line in open(path):
-            if line.startswith(TRAFFIC_TAG):
-                return json.loads(line[len(TRAFFIC_TAG):].rsplit(" -->", 1)[0])
+            if line.startswith(tag):
+                return json.loads(line[len(tag):].rsplit(" -->", 1)[0])
     except OSError:
         return None
     return None
+
+
+def read_mfma(path):
+    """The machine-readable record of an MFMA counter summary, or None."""
+    return _read_tagged(path, MFMA_TAG)
+
+
+def read_traffic(path):
+    """The machine-readable record of a traffic summary, or None."""
+    return _read_tagged(path, TRAFFIC_TAG)
 
 
 def main(argv=None):
@@ -140,8 +206,17 @@ def main(argv=None):
     t.add_argument("--command-fetch", required=True)
     t.add_argument("--command-write", required=True)
     t.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--stats-csv", required=True)
+    m.add_argument("--simds", type=int, default=1024, help="SIMDs of the device (compute units x 4)")
+    m.add_argument("--xcc", type=int, default=8, help="XCDs of the device")
+    m.add_argument("--title", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--command-stats", required=True)
+    m.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    (stats if a.cmd == "stats" else traffic)(a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.cmd](a)
     return 0
 
 

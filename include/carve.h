@@ -362,6 +362,17 @@ carve_status carve_decode_step(const carve_shape* s,
                                float* S, const carve_decode_content* content,
                                void* o, void* stream);
 
+/*
+ * Measurement helper, not part of the CARVE operation: copies `bytes` from src to dst
+ * (both device pointers, 16-byte aligned, non-overlapping; bytes a multiple of 16) with a
+ * plain streaming kernel (each byte read once and written once by 16-byte vector accesses,
+ * no reuse), asynchronously on `stream`.  Its rate is the device's achievable copy
+ * bandwidth, the measured denominator set beside the published HBM peak when the kernels'
+ * algorithmic bytes are put against the memory roofline.  bytes = 0 launches nothing;
+ * misaligned, odd-sized or overlapping arguments return CARVE_ERR_INVALID_ARG.
+ */
+carve_status carve_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* carve_status_string(carve_status st);
 

@@ -32,3 +32,13 @@ def max_rel(gpu, ref):
     gpu = np.asarray(gpu, np.float64)
     den = np.max(np.abs(ref))
     return float(np.max(np.abs(gpu - ref)) / (den if den > 0 else 1.0))
+
+
+def per_head_rel(gpu, ref):
+    """[B, H] array: max |gpu - ref| / max |ref| within each (batch, head) sequence."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    ax = tuple(range(2, ref.ndim))
+    den = np.max(np.abs(ref), axis=ax) if ax else np.abs(ref)
+    num = np.max(np.abs(gpu - ref), axis=ax) if ax else np.abs(gpu - ref)
+    return num / np.where(den > 0, den, 1.0)

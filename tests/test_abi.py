@@ -245,3 +245,15 @@ def test_noalloc_rejects_beyond_scratch_on_host(lib):
     # argument errors come first, as for carve_fwd
     assert lib.carve_fwd_noalloc(ctypes.byref(shape(Dv=64)), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
                                  FAKE, None, None) == UNSUPPORTED
+
+
+def test_stream_copy_rejects_bad_arguments_on_host(lib):
+    """The copy helper checks sizes, alignment and overlap before it touches the device;
+    zero bytes is a no-op."""
+    lib.carve_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    a, b = 1 << 20, 1 << 24
+    assert lib.carve_stream_copy(None, None, 0, None) == 0
+    assert lib.carve_stream_copy(a, b, 24, None) == INVALID        # not a multiple of 16
+    assert lib.carve_stream_copy(a + 8, b, 32, None) == INVALID    # misaligned destination
+    assert lib.carve_stream_copy(a, None, 32, None) == INVALID     # missing source
+    assert lib.carve_stream_copy(a, a + 16, 64, None) == INVALID   # overlapping ranges

@@ -12,8 +12,8 @@ import torch
 
 import oracle
 from chunk_gated_delta_amd import carve
-from chunk_gated_delta_amd.synth import WORKLOADS, make_inputs, random_inputs
-from tests.helpers import max_rel, to_device, to_np
+from chunk_gated_delta_amd.synth import random_inputs
+from tests.helpers import max_rel, per_head_rel, to_device, to_np
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -90,56 +90,6 @@ def test_bwd_empty():
     assert torch.equal(g["dS0"], dS_T)
 
 
-def test_full_train_sampled_heads():
-    """Training workload at full size (B8 H16 T2048 d128 L64, b = ones); gradients of two sampled
-    heads against the reference, plus the homogeneity identity <dq, q> = <dO, o> on every head."""
-    wl = WORKLOADS["train_fwd_bwd"]
-    announce(wl.name + " full size, sampled heads")
-    inp = make_inputs(wl)
-    d = to_device(inp, wl.dtype)
-    g = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=d["b"], L=wl.L, want_dS0=True)
-    o, _, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], L=wl.L)
-    torch.cuda.synchronize()
-    # identity: o is linear in q, so sum(dq * q) = sum(dO * o) per head
-    lhs = (g["dq"].float() * d["q"].float()).sum(dim=(2, 3))
-    rhs = (d["dO"].float() * o.float()).sum(dim=(2, 3))
-    rel = ((lhs - rhs).abs().max() / rhs.abs().max()).item()
-    print(f"  <dq,q> vs <dO,o>: {rel:.2e}", flush=True)
-    assert rel <= 2e-2
-    for (bi, hi) in [(0, 0), (7, 13)]:
-        sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items() if not k_.endswith("_bits")}
-        ref = oracle.backward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], sub["dO"], b=sub["b"])
-        errs = {key: max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key]) for key in NAMES}
-        print(f"  head ({bi},{hi}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
-        assert all(v_ <= 2e-2 for v_ in errs.values()), errs
-
-
-def test_full_bench_launch_sampled_heads():
-    """Exactly what the benchmark times: fwd_save + bwd_saved at the 1.3B-head shape
-    (B4 H16 T4096 d128 L64, b = sigmoid(N(2,1))); the identity <dq, q> = <dO, o> on every head
-    and one sampled head's output and gradients against the reference."""
-    wl = WORKLOADS["head1p3b_fwd"]
-    announce(wl.name + " full size via the saved pair, sampled head")
-    inp = make_inputs(wl, with_dO=True)
-    d = to_device(inp, wl.dtype)
-    o, S_T, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], L=wl.L)
-    g = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=d["b"], L=wl.L)
-    torch.cuda.synchronize()
-    lhs = (g["dq"].float() * d["q"].float()).sum(dim=(2, 3))
-    rhs = (d["dO"].float() * o.float()).sum(dim=(2, 3))
-    rel = ((lhs - rhs).abs().max() / rhs.abs().max()).item()
-    print(f"  <dq,q> vs <dO,o>: {rel:.2e}", flush=True)
-    assert rel <= 2e-2
-    bi, hi = 2, 9
-    sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items() if not k_.endswith("_bits")}
-    ro, _, _ = oracle.forward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], b=sub["b"])
-    ref = oracle.backward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], sub["dO"], b=sub["b"])
-    errs = {key: max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key]) for key in NAMES if g[key] is not None}
-    errs["o"] = max_rel(to_np(o[bi:bi + 1, hi:hi + 1]), ro)
-    print(f"  head ({bi},{hi}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
-    assert all(v_ <= 2e-2 for v_ in errs.values()), errs
-
-
 def test_saved_pair_matches_recompute_bitwise():
     """fwd_save gives the same o and S_T as fwd, and bwd_saved the same gradients as bwd
     (the same arithmetic, only the forward is not recomputed)."""
@@ -162,10 +112,10 @@ def test_saved_pair_matches_recompute_bitwise():
 
 
 @pytest.mark.parametrize("B,H", [(8, 8), (8, 16)], ids=["slice32", "slice64"])
-def test_wide_value_slices_sampled_heads(B, H):
+def test_wide_value_slices_every_head(B, H):
     """Enough heads that the state passes split D=128 into 32- and 64-row value slices
     (whose state copies and outputs leave through LDS), with a ragged tail, S0 and dS_T;
-    forward and gradients of sampled heads against the reference."""
+    forward and gradients of every head against the reference, normalised per head."""
     announce(f"wide value slices B{B} H{H}")
     T, D = 100, 128
     inp = random_inputs(B, H, T, D, D, dtype="bf16", seed=300 + H, erase="sigmoid", dists="softplus_decay",
@@ -179,15 +129,10 @@ def test_wide_value_slices_sampled_heads(B, H):
     o, S_T, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=S0d)
     g = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=d["b"], S0=S0d, dS_T=dSd)
     torch.cuda.synchronize()
-    for (bi, hi) in [(0, 0), (B - 1, H - 1), (3, H // 2)]:
-        sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items() if not k_.endswith("_bits")}
-        s0 = S0[bi:bi + 1, hi:hi + 1]
-        ds = dS_T[bi:bi + 1, hi:hi + 1]
-        o_ref, sT_ref, _ = oracle.forward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], b=sub["b"], S0=s0)
-        ref = oracle.backward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], sub["dO"], b=sub["b"],
-                              S0=s0, dS_T=ds)
-        errs = {"o": max_rel(to_np(o[bi:bi + 1, hi:hi + 1]), o_ref),
-                "S_T": max_rel(to_np(S_T[bi:bi + 1, hi:hi + 1]), sT_ref)}
-        errs.update({key: max_rel(to_np(g[key][bi:bi + 1, hi:hi + 1]), ref[key]) for key in NAMES})
-        print(f"  head ({bi},{hi}) " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
-        assert all(v_ <= 2e-2 for v_ in errs.values()), errs
+    o_ref, sT_ref, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], b=inp["b"], S0=S0)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"], b=inp["b"],
+                          S0=S0, dS_T=dS_T)
+    errs = {"o": per_head_rel(to_np(o), o_ref).max(), "S_T": per_head_rel(to_np(S_T), sT_ref).max()}
+    errs.update({key: per_head_rel(to_np(g[key]), ref[key]).max() for key in NAMES})
+    print("  worst head " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= 2e-2 for v_ in errs.values()), errs

@@ -280,43 +280,3 @@ def test_content_zero_projection_bit_exact():
     ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"],
                                b=1 / (1 + np.exp(-inp["b_x"])))
     assert max_rel(to_np(oz), ro) <= 2e-2 and max_rel(to_np(sz), rS) <= 2e-2
-
-
-# ------------------------------------------------------- full-size workloads (sampled heads)
-
-def sampled_heads_check(wl, heads, content=False):
-    inp = make_inputs(wl)
-    d = to_device(inp, wl.dtype)
-    cont = None
-    if content:
-        cont = {"b_x": d["b_x"], "U1": d["U1"], "U2": d["U2"]}
-    o, S_T, m = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d.get("b"), L=wl.L, content=cont)
-    torch.cuda.synchronize()
-    o, S_T = to_np(o), to_np(S_T)
-    for (bi, hi) in heads:
-        sub = {k_: v_[bi:bi + 1, hi:hi + 1] for k_, v_ in inp.items()
-               if not k_.endswith("_bits") and k_ not in ("U1", "U2")}
-        rc = None
-        if content:
-            rc = {"b_x": sub["b_x"], "U1": inp["U1"][hi:hi + 1], "U2": inp["U2"][hi:hi + 1]}
-        ro, rS, _ = oracle.forward(sub["q"], sub["k"], sub["v"], sub["log_g"], sub["w"], b=sub.get("b"), L=wl.L,
-                                   content=rc)
-        eo = max_rel(o[bi:bi + 1, hi:hi + 1], ro)
-        es = max_rel(S_T[bi:bi + 1, hi:hi + 1], rS)
-        print(f"  head ({bi},{hi}) err o={eo:.2e} S_T={es:.2e}", flush=True)
-        assert eo <= 2e-2 and es <= 2e-2
-
-
-def test_full_head1p3b_sampled():
-    announce("head1p3b_fwd full size, sampled heads")
-    sampled_heads_check(WORKLOADS["head1p3b_fwd"], [(0, 0), (3, 15), (2, 7)])
-
-
-def test_full_long_ctx_sampled():
-    announce("long_ctx_fwd full size, sampled heads (S_T compared)")
-    sampled_heads_check(WORKLOADS["long_ctx_fwd"], [(0, 5)])
-
-
-def test_full_content_sampled():
-    announce("content_fwd full size, sampled heads")
-    sampled_heads_check(WORKLOADS["content_fwd"], [(1, 3)], content=True)

@@ -499,6 +499,28 @@ def test_gates_from_logits_values():
     assert np.all(lg <= 0) and np.all(np.isfinite(lg))
 
 
+def test_gates_from_logits_bias_inside_softplus():
+    """Nonzero logits and bias, per head and key channel (notes section 2.3, fused-gate legend:
+    the bias shifts the decay logit before the softplus).  f = 1, tau = -1 gives softplus(0) =
+    log 2; f = 2, tau = log(e - 1) - 2 gives softplus(log(e - 1)) = 1; f = -1, tau = 1 + log 3
+    gives log 4.  A misplaced bias (softplus(f) + tau) or a head/channel mix-up of A or tau
+    changes every one of these.  b_x = log 3 gives b = 3/4; w_hat = -log 3 gives w = 1/4."""
+    A = np.array([[0.7, 1.9, 3.0], [5.0, 0.25, 10.0]])                 # [H=2, Dk=3]
+    tau = np.array([[-1.0, np.log(np.e - 1.0) - 2.0, 1.0 + np.log(3.0)],
+                    [1.0 + np.log(3.0), -1.0, np.log(np.e - 1.0) - 2.0]])
+    f = np.empty((1, 2, 2, 3))
+    f[0, 0, :] = [1.0, 2.0, -1.0]
+    f[0, 1, :] = [-1.0, 1.0, 2.0]
+    b_x = np.full((1, 2, 2, 3), np.log(3.0))
+    w_hat = np.full((1, 2, 2), -np.log(3.0))
+    log_g, b, w = gates_from_logits(f, A, tau, w_hat, b_x=b_x)
+    sp = np.array([[np.log(2.0), 1.0, np.log(4.0)], [np.log(4.0), np.log(2.0), 1.0]])
+    for t in range(2):
+        np.testing.assert_allclose(log_g[0, :, t], -A * sp, rtol=1e-14)
+    np.testing.assert_allclose(b, 0.75, rtol=1e-15)
+    np.testing.assert_allclose(w, 0.25, rtol=1e-15)
+
+
 @pytest.mark.parametrize("with_bx", [True, False])
 def test_logit_backward_matches_finite_differences(with_bx):
     rng = np.random.default_rng(41 + with_bx)
