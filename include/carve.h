@@ -161,7 +161,14 @@ size_t carve_bwd_workspace_size(const carve_shape* s);
 
 /*
  * Backward pass of the token-only forward (the content-aware forward has its own
- * backward, carve_bwd_content, below).  Recomputes the forward internally.
+ * backward, carve_bwd_content, below): the reverse-mode derivative of the chunked
+ * forward, whose fused forward/backward pair and "backward scan" over chunks the notes
+ * report in section 3.1 (Table 2, forward and backward error against the reference)
+ * and section 4 (summary).  The pages print no backward formula; this is the exact
+ * gradient of the forward defined above, reached by a reverse state pass
+ * dS_c = dS_{c+1} M_c^T + (terms of chunk c's outputs), M_c the chunk's state map, and
+ * per chunk back through the output, the WY factors, the inverse of (I + A) and the
+ * cumulative retention.  Recomputes the forward internally.
  *   q, k, v, log_g, b, w, S0   as for carve_fwd
  *   dO     (device) [B,H,T,Dv] dtype          gradient of the loss w.r.t. o
  *   dS_T   (device) [B,H,Dv,Dk] float         gradient w.r.t. S_T, or NULL (= 0)

@@ -554,3 +554,42 @@ def test_logit_backward_matches_finite_differences(with_bx):
         np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-7, err_msg=gname)
     if not with_bx:
         assert g["db_x"] is None
+
+
+@pytest.mark.parametrize("Dk,Dv", [(6, 3), (3, 6)])
+def test_unequal_widths_reduce_to_padded_equal_widths(Dk, Dv):
+    """The state is d_v x d_k with independent widths (notes section 1).  Each value row of
+    the recurrence evolves on its own, and a key channel with k = q = 0 and a = 1 neither
+    feeds nor is fed by the others, so zero-padding the narrower axis to the wider one
+    reproduces the unequal-width result on the true rows and columns: forward outputs, the
+    final state and every gradient."""
+    rng = np.random.default_rng(90 + Dk)
+    c = rand_case(rng, B=1, H=2, T=11, Dk=Dk, Dv=Dv)
+    dO = rng.standard_normal(c["v"].shape)
+    dS_T = rng.standard_normal(c["S0"].shape)
+    D = max(Dk, Dv)
+
+    def pad(x, axis_len, fill=0.0):
+        out = np.full(x.shape[:-1] + (axis_len,), fill)
+        out[..., :x.shape[-1]] = x
+        return out
+
+    p = dict(c)
+    p["q"], p["k"] = pad(c["q"], D), pad(c["k"], D)
+    p["log_g"], p["b"] = pad(c["log_g"], D, 0.0), pad(c["b"], D, 1.0)
+    p["v"] = pad(c["v"], D)
+    p["S0"] = np.zeros(c["S0"].shape[:2] + (D, D))
+    p["S0"][..., :Dv, :Dk] = c["S0"]
+    pdS = np.zeros_like(p["S0"])
+    pdS[..., :Dv, :Dk] = dS_T
+    o, S_T, _ = forward(c["q"], c["k"], c["v"], c["log_g"], c["w"], b=c["b"], S0=c["S0"])
+    po, pS, _ = forward(p["q"], p["k"], p["v"], p["log_g"], p["w"], b=p["b"], S0=p["S0"])
+    np.testing.assert_allclose(po[..., :Dv], o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(pS[..., :Dv, :Dk], S_T, rtol=1e-12, atol=1e-12)
+    assert np.all(po[..., Dv:] == 0) and np.all(pS[..., Dv:, :] == 0) and np.all(pS[..., :, Dk:] == 0)
+    g = backward(c["q"], c["k"], c["v"], c["log_g"], c["w"], dO, b=c["b"], S0=c["S0"], dS_T=dS_T)
+    pg = backward(p["q"], p["k"], p["v"], p["log_g"], p["w"], pad(dO, D), b=p["b"], S0=p["S0"], dS_T=pdS)
+    for key, width in (("dq", Dk), ("dk", Dk), ("dlog_g", Dk), ("db", Dk), ("dv", Dv)):
+        np.testing.assert_allclose(pg[key][..., :width], g[key], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(pg["dw"], g["dw"], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(pg["dS0"][..., :Dv, :Dk], g["dS0"], rtol=1e-10, atol=1e-12)
