@@ -70,7 +70,9 @@ struct RevOps {
   f32x4 gl[SCT];
   Frag<T> dov[NDO];   // raw 16-byte pieces of dO: VEC consecutive value columns of one token
 
-  __device__ __forceinline__ void load(const BwdArgs& a, int bh, int c, int v0) {
+  // with_do = false: the output term is left out (dO read as zero; the rows of the linear
+  // part of a segment's reverse map)
+  __device__ __forceinline__ void load(const BwdArgs& a, int bh, int c, int v0, bool with_do = true) {
     const FwdArgs& f = a.fwd;
     const int lg = lane_id() >> 4, wave = wave_id();
     const size_t ci = (size_t)bh * f.NC + c;
@@ -94,7 +96,7 @@ struct RevOps {
       const int r = idx / (VS / VEC), g = idx % (VS / VEC);
       if (kFullDO || idx < LC * VS / VEC) {
         const int rr = min(r, n - 1);   // rows past the sequence end meet zero columns of Q~^T
-        dov[u] = load_frag(dO + ((size_t)bh * f.T + c * LC + rr) * D + v0 + VEC * g);
+        dov[u] = with_do ? load_frag(dO + ((size_t)bh * f.T + c * LC + rr) * D + v0 + VEC * g) : zero_frag(T());
       }
     }
   }
@@ -116,14 +118,24 @@ struct RevOps {
   }
 };
 
-template <typename T, int LC, int D, int VS>
-__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
+// One reverse pass over chunks chi down to clo for a slice of VS rows of the state
+// gradient, held as accumulator tiles of dS^T (lane of tile (ct, vt) holds
+// dS[v0 + 16 vt + lr][16 ct + 4 lg + i]):
+//   dS^T <- Diag(Gamma_L) dS^T + (-W)^T (K-> dS^T) + Q~^T dO.
+// The rows start from rows v0 .. of `init` (a D x D matrix; null: zero) or, with
+// eye_row >= 0, from the identity rows eye_row .. (the linear part of a segment's map).
+// with_do = false leaves out the output term.  STORE: the gradient w.r.t. the state
+// leaving every chunk goes to dS_vk (fragment order).  On return dS holds the gradient
+// w.r.t. the state entering chunk clo.
+template <typename T, int LC, int D, int VS, bool STORE>
+__device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int clo, int chi, const float* init,
+                                         int eye_row, bool with_do, f32x4 (&dS)[StateTiles<D, VS>::SPW],
+                                         unsigned char* smem) {
   using Lay = RevLayout<T, LC, D, VS>;
   using Op = RevOps<T, LC, D, VS>;
   using ST = StateTiles<D, VS>;
   constexpr int NVT = ST::NVT, SPW = ST::SPW, LDS_ = Lay::LDS_, LDU = Lay::LDU, LDV = Lay::LDV;
   constexpr int VEC = Op::VEC;
-  extern __shared__ __align__(16) unsigned char smem[];
   T* dSb = reinterpret_cast<T*>(smem);
   T* XT = dSb + VS * LDS_;
   T* dOr = XT + VS * LDU;
@@ -131,35 +143,36 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   T* Ql = reinterpret_cast<T*>(smem + Lay::Ql);
   T* Kl = reinterpret_cast<T*>(smem + Lay::Kl);
   const FwdArgs& f = a.fwd;
-  int bh, slice;
-  xcd_slice_map(D / VS, f.B * f.H, bh, slice);
-  const int v0 = slice * VS;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
 
-  f32x4 dS[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int st = wave * SPW + j, ct = st / NVT, vt = st % NVT;
     const int vl = 16 * vt + lr, kc = 16 * ct + 4 * lg;
-    if (a.dS_T) dS[j] = load4f(a.dS_T + ((size_t)bh * D + v0 + vl) * D + kc);
-    else dS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (eye_row >= 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dS[j][i] = (eye_row + vl == kc + i) ? 1.f : 0.f;
+    } else if (init) {
+      dS[j] = load4f(init + (size_t)(v0 + vl) * D + kc);
+    } else {
+      dS[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     store4(dSb + vl * LDS_ + kc, dS[j]);
   }
   // three operand buffers, loaded two chunks ahead (chunks run last to first); a
   // chunk's factors are staged in LDS during the step before its own.  Chunks below
   // the last one run in a main loop with clamped prefetch.
   constexpr int PF = 3;
-  // chunk range (all chunks unless a sub-range is asked for)
-  const int clo = a.c_lo, chi = a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1, nch = chi - clo + 1;
+  const int nch = chi - clo + 1;
   Op buf[PF];
 #pragma unroll
-  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, bh, max(chi - j, clo), v0);
+  for (int j = 0; j < PF - 1; ++j) buf[j].load(a, bh, max(chi - j, clo), v0, with_do);
   buf[0].stage(Wl, Ql, Kl);
   __syncthreads();
   auto step = [&](int c, const Op& cur, const Op& nxt) {
-    const size_t ci = (size_t)bh * f.NC + c;
-    // gradient w.r.t. the state leaving chunk c, in fragment order rows v
-    {
+    if constexpr (STORE) {
+      // gradient w.r.t. the state leaving chunk c, in fragment order rows v
+      const size_t ci = (size_t)bh * f.NC + c;
       T* vk = reinterpret_cast<T*>(a.dS_vk) + ci * D * D;
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
@@ -231,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
       const int c = chi - (g + j);
-      buf[(j + PF - 1) % PF].load(a, bh, max(c - (PF - 1), clo), v0);
+      buf[(j + PF - 1) % PF].load(a, bh, max(c - (PF - 1), clo), v0, with_do);
       step(c, buf[j], buf[(j + 1) % PF]);
     }
   }
@@ -239,17 +252,77 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   for (int j = 0; j < PF; ++j) {
     const int c = chi - (nmain + j);
     if (c >= clo) {
-      if (c - (PF - 1) >= clo) buf[(j + PF - 1) % PF].load(a, bh, c - (PF - 1), v0);
+      if (c - (PF - 1) >= clo) buf[(j + PF - 1) % PF].load(a, bh, c - (PF - 1), v0, with_do);
       step(c, buf[j], buf[(j + 1) % PF]);
     }
   }
-  if (a.dS0) {
+}
+
+// Rows v0 .. v0 + VS - 1 of a D x D matrix (row stride D) from the accumulator tiles.
+template <int D, int VS>
+__device__ __forceinline__ void store_rows(float* dst, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW]) {
+  using ST = StateTiles<D, VS>;
+  const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < SPW; ++j) {
-      const int st = wave * SPW + j, ct = st / NVT, vt = st % NVT;
-      store4(a.dS0 + ((size_t)bh * D + v0 + 16 * vt + lr) * D + 16 * ct + 4 * lg, dS[j]);
-    }
+  for (int j = 0; j < ST::SPW; ++j) {
+    const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
+    store4(dst + (size_t)(v0 + 16 * vt + lr) * D + 16 * ct + 4 * lg, S[j]);
   }
+}
+
+// Workgroup = (slice of VS value rows, batch*head[, segment]).  Unsegmented: chunks
+// c_lo .. (all by default) from dS_T, ending in dS0.  Segmented (fwd.nseg > 1): segment
+// s runs its chunks from dS_seg[s], the gradient w.r.t. the state leaving it, and the
+// first segment ends in dS0.
+template <typename T, int LC, int D, int VS>
+__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const FwdArgs& f = a.fwd;
+  const int nseg = f.nseg > 1 ? f.nseg : 1;
+  int u, slice;
+  xcd_slice_map(D / VS, f.B * f.H * nseg, u, slice);
+  const int bh = u / nseg, seg = u % nseg, v0 = slice * VS;
+  int clo, chi;
+  const float* init;
+  if (nseg > 1) {
+    clo = seg * f.seg_len;
+    chi = min(f.NC, clo + f.seg_len) - 1;
+    init = a.dS_seg + (size_t)u * D * D;
+  } else {
+    clo = a.c_lo;
+    chi = a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1;
+    init = a.dS_T ? a.dS_T + (size_t)bh * D * D : nullptr;
+  }
+  f32x4 dS[StateTiles<D, VS>::SPW];
+  rev_pass<T, LC, D, VS, true>(a, bh, v0, clo, chi, init, -1, true, dS, smem);
+  if (a.dS0 && seg == 0) store_rows<D, VS>(a.dS0 + (size_t)bh * D * D, v0, dS);
+}
+
+// ------------------------------------------------------------------ segmented reverse pass
+// The reverse step is affine in dS, so a segment maps the gradient w.r.t. the state
+// leaving it to the gradient w.r.t. the state entering it as dS_in = dS_out Pi + C: C is
+// the segment's reverse pass from dS_out = 0, and Pi, the product of the transposed
+// chunk maps, is the pass with no output term started from the identity (its rows are
+// indexed by key).  bwd_affine computes [C; Pi] as 2D rows per (head, segment) for every
+// segment but the first; the reverse scan of seg_scan chains them from dS_T down
+// (dS_out(s - 1) = dS_out(s) Pi_s + C_s); then every segment runs its reverse pass from
+// its dS_out, storing the chunk-level gradients.  The reverse side of the chunk-level
+// scan of affine state maps behind the logarithmic parallel depth the notes list for
+// CARVE (complexity table), taken as two levels like the forward.
+template <typename T, int LC, int D, int VS>
+__global__ __launch_bounds__(kThreads) void bwd_affine_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const FwdArgs& f = a.fwd;
+  const int nsa = f.nseg - 1;                  // segments with a reverse map: all but the first
+  int u, slice;
+  xcd_slice_map(2 * D / VS, f.B * f.H * nsa, u, slice);
+  const int bh = u / nsa, seg = 1 + u % nsa;
+  const int r0 = slice * VS;                   // first row of [C; Pi]
+  const bool pi = r0 >= D;
+  const int clo = seg * f.seg_len, chi = min(f.NC, clo + f.seg_len) - 1;
+  f32x4 dS[StateTiles<D, VS>::SPW];
+  rev_pass<T, LC, D, VS, false>(a, bh, pi ? 0 : r0, clo, chi, nullptr, pi ? r0 - D : -1, !pi, dS, smem);
+  store_rows<D, VS>(a.raff + (size_t)(bh * f.nseg + seg) * 2 * D * D, r0, dS);
 }
 
 // ------------------------------------------------------------------ chunk gradients
@@ -1780,13 +1853,36 @@ size_t diag_fix_bytes(int dtype, int BH, int NC, int LC) {
 
 // ------------------------------------------------------------------ launchers
 template <typename T, int LC, int D, int VS>
+static hipError_t rev_affine_launch(const BwdArgs& a, hipStream_t st) {
+  using Lay = RevLayout<T, LC, D, VS>;
+  static_assert(Lay::bytes <= 80 * 1024, "reverse-state LDS exceeds half a compute unit's 160 KB");
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_affine_kernel<T, LC, D, VS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
+  if (e != hipSuccess) return e;
+  dim3 grid((2 * D / VS) * a.fwd.B * a.fwd.H * (a.fwd.nseg - 1));
+  hipLaunchKernelGGL((bwd_affine_kernel<T, LC, D, VS>), grid, dim3(kThreads), Lay::bytes, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int LC, int D, int VS>
 static hipError_t rev_launch(const BwdArgs& a, hipStream_t st) {
   using Lay = RevLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 80 * 1024, "reverse-state LDS exceeds half a compute unit's 160 KB");
+  const FwdArgs& f = a.fwd;
+  const int nseg = f.nseg > 1 ? f.nseg : 1;
+  if (nseg > 1) {
+    // every segment but the last holds seg_len whole chunks; the last is non-empty
+    if (f.seg_len < 1 || (long long)(nseg - 1) * f.seg_len > f.NC - 1 || !a.raff || !a.dS_seg || a.c_count)
+      return hipErrorInvalidValue;
+    hipError_t e = f.aff_vs == 16 ? rev_affine_launch<T, LC, D, 16>(a, st) : rev_affine_launch<T, LC, D, 32>(a, st);
+    if (e != hipSuccess) return e;
+    e = launch_seg_scan(ScanArgs{a.dS_T, a.dS_seg, a.raff, nseg}, D, f.B * f.H, true, st);
+    if (e != hipSuccess) return e;
+  }
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_state_kernel<T, LC, D, VS>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
-  dim3 grid((D / VS) * a.fwd.B * a.fwd.H);
+  dim3 grid((D / VS) * f.B * f.H * nseg);
   hipLaunchKernelGGL((bwd_state_kernel<T, LC, D, VS>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }

@@ -120,10 +120,9 @@ size_t fwd_ws(const carve_shape* s, const Plan& p, const carve_content* c) {
   return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 1) + seg_bytes(ps);
 }
 
-// carve the segment buffers after the forward factors (segmented pass only)
-void set_segments(carve::FwdArgs* a, const carve_shape* s, const Plan& p, void* workspace) {
+// carve the segment buffers (segmented pass only) from `base` (seg_bytes of space)
+void set_segments(carve::FwdArgs* a, const Plan& p, void* base) {
   if (p.nseg <= 1) return;
-  char* base = static_cast<char*>(workspace) + carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 1);
   char* al = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(base) + 255) & ~uintptr_t(255));
   a->nseg = p.nseg;
   a->seg_len = p.seg_len;
@@ -131,6 +130,15 @@ void set_segments(carve::FwdArgs* a, const carve_shape* s, const Plan& p, void* 
   a->VS = p.VS;
   a->aff = reinterpret_cast<float*>(al);
   a->S_seg = a->aff + (size_t)p.BH * p.nseg * 2 * p.D * p.D;
+}
+void* after_factors(void* workspace, const carve_shape* s, const Plan& p, int mode) {
+  return static_cast<char*>(workspace) + carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, mode);
+}
+// the plan with the segmented state passes (long sequences, few heads)
+Plan seg_planned(const Plan& p) {
+  Plan ps = p;
+  seg_plan(&ps);
+  return ps;
 }
 
 // one fragment-order copy of the D x D state for every chunk, in the operand type
@@ -142,7 +150,9 @@ size_t states_bytes(const carve_shape* s, const Plan& p) {
 // state entering every chunk (one fragment-order copy)
 size_t saved_bytes(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 3) + (states_bytes(s, p) + 256) + 256;
+  // (+ the segmented forward pass's maps and entering states, when it is segmented)
+  return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 3) + (states_bytes(s, p) + 256) + 256 +
+         seg_bytes(seg_planned(p));
 }
 
 // diagonal tiles of the blocks whose exact within-block terms the range-safe chunk
@@ -160,15 +170,17 @@ void set_diag(carve::BwdArgs* a, const carve_shape* s, const Plan& p, void* base
 // fix-up flags and tiles
 size_t bwd_saved_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
-  return (states_bytes(s, p) + 256) + 256 + diag_bytes(s, p);
+  // (+ the segmented reverse pass's maps and segment gradients, when it is segmented)
+  return (states_bytes(s, p) + 256) + 256 + diag_bytes(s, p) + seg_bytes(seg_planned(p));
 }
 
 size_t bwd_ws(const carve_shape* s, const Plan& p) {
   if (p.empty) return 0;
   // S and dS per chunk, one fragment-order copy each, in the operand type; the fix-up
   // flags and tiles
+  // (+ the segment maps, used by the forward pass and then by the reverse pass)
   return carve::factors_bytes(s->dtype == CARVE_BF16, p.BH, p.NC, p.LC, p.D, 2) + 2 * (states_bytes(s, p) + 256) + 256 +
-         diag_bytes(s, p);
+         diag_bytes(s, p) + seg_bytes(seg_planned(p));
 }
 
 carve::FwdArgs fwd_args(const carve_shape* s, const Plan& p, const void* q, const void* k, const void* v,
@@ -299,9 +311,7 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
     mark(prof, 1, hs);
   } else {
     a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, 1);
-    Plan ps = p;
-    seg_plan(&ps);
-    set_segments(&a, s, ps, workspace);
+    set_segments(&a, seg_planned(p), after_factors(workspace, s, p, 1));
     mark(prof, 0, hs);
     e = carve::launch_fwd_prep(a, hs);
     mark(prof, 1, hs);
@@ -370,6 +380,11 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
   a.fwd.S_vk = base;
   a.dS_vk = align_up(base + states);
   set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states);
+  // segmented state passes: the forward's maps, then (the same memory) the reverse maps
+  set_segments(&a.fwd, seg_planned(p),
+               static_cast<char*>(a.diag) + carve::diag_fix_bytes(a.fwd.dtype, p.BH, p.NC, p.LC));
+  a.raff = a.fwd.aff;
+  a.dS_seg = a.fwd.S_seg;
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -426,6 +441,7 @@ carve_status carve_fwd_save(const carve_shape* s, const void* q, const void* k, 
   a.f = carve::carve_factors(saved, a.dtype, p.BH, p.NC, p.LC, p.D, 3);
   char* base = align_up(static_cast<char*>(saved) + carve::factors_bytes(a.dtype, p.BH, p.NC, p.LC, p.D, 3));
   a.S_vk = base;
+  set_segments(&a, seg_planned(p), base + states_bytes(s, p) + 256);
   mark(prof, 0, hs);
   hipError_t e = carve::launch_fwd_prep(a, hs);
   mark(prof, 1, hs);
@@ -471,6 +487,11 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
   a.fwd.S_vk = base;
   a.dS_vk = align_up(workspace);
   set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states);
+  // segmented reverse pass: the reverse maps and segment gradients
+  set_segments(&a.fwd, seg_planned(p),
+               static_cast<char*>(a.diag) + carve::diag_fix_bytes(a.fwd.dtype, p.BH, p.NC, p.LC));
+  a.raff = a.fwd.aff;
+  a.dS_seg = a.fwd.S_seg;
   a.dO = dO;
   a.dS_T = dS_T;
   a.dq = dq;
@@ -521,9 +542,7 @@ carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k
   a.gtau = gates->tau;
   a.mode = 1;
   a.f = carve::carve_factors(workspace, a.dtype, p.BH, p.NC, p.LC, p.D, 1);
-  Plan ps = p;
-  seg_plan(&ps);
-  set_segments(&a, s, ps, workspace);
+  set_segments(&a, seg_planned(p), after_factors(workspace, s, p, 1));
   hipError_t e = carve::launch_fwd_prep(a, hs);
   if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;

@@ -103,6 +103,13 @@ struct BwdArgs {
   // head (c_count = 0: all chunks).  The reverse state pass starts from dS_T and
   // ends in dS0 for that range.
   int c_lo, c_count;
+  // Segmented reverse pass (fwd.nseg > 1, the forward's segments of fwd.seg_len chunks):
+  // raff receives the reverse maps of segments s = 1 .. nseg-1 as [(bh*nseg + s)][2D][D]
+  // fp32 (rows 0..D-1 C_s, the segment's pass from a zero gradient; rows D..2D-1 Pi_s,
+  // the pass with no output term from the identity), dS_seg the gradient w.r.t. the
+  // state leaving every segment as [(bh*nseg + s)][D][D] fp32 (segment nseg-1: dS_T).
+  float* raff;
+  float* dS_seg;
   // Range-safe chunks: diag [ci][NB][2][64][4] (dtype) receives the diagonal tiles of
   // dP and dB of the blocks whose log-retention leaves the fast tiles' range (accumulator
   // order); the same workgroup reads them back for those blocks' exact terms.
@@ -163,6 +170,15 @@ size_t logit_partials_bytes(int B, int H, int T, int D);
 size_t factors_bytes(int dtype, int BH, int NC, int LC, int D, int mode);
 ChunkFactors carve_factors(void* ws, int dtype, int BH, int NC, int LC, int D, int mode);
 
+// Chain of the segments' affine maps (seg_scan_kernel): init [B*H][D][D] (null: zero),
+// seg [(bh*nseg + s)][D][D] the chained rows, aff [(bh*nseg + s)][2D][D] the maps [C; Pi].
+struct ScanArgs {
+  const float* init;
+  float* seg;
+  const float* aff;
+  int nseg;
+};
+hipError_t launch_seg_scan(const ScanArgs& a, int D, int BH, bool rev, hipStream_t st);
 hipError_t launch_copy_or_zero(float* dst, const float* src, size_t n, hipStream_t st);
 hipError_t launch_fwd_prep(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_state(const FwdArgs& a, hipStream_t st);

@@ -399,41 +399,45 @@ __global__ __launch_bounds__(kThreads) void fwd_affine_kernel(FwdArgs a) {
   }
 }
 
-// S_in(0) = S0 (or 0), S_in(s+1) = S_in(s) Pi_s + C_s for s = 0 .. nseg-2, in fp32
-// with a fixed summation order.  Workgroup (16 rows of S, head): its rows depend only
-// on themselves, so they stay in LDS across the segments (transposed, [key][row]).
-// Pi_s is staged whole in LDS; the next segment's Pi and C rows are loaded into
-// registers while the current product runs.  Wave q owns rows 4q .. 4q+3, lane l
-// the columns CW l .. CW l + CW - 1 (CW = D / 64).
+// Forward: S_in(0) = S0 (or 0), S_in(s+1) = S_in(s) Pi_s + C_s for s = 0 .. nseg-2.
+// Reverse (REV): the gradient w.r.t. the state leaving segment nseg-1 is dS_T (or 0), and
+// dS_out(s-1) = dS_out(s) Pi_s + C_s for s = nseg-1 .. 1.  Both in fp32 with a fixed
+// summation order.  Workgroup (16 rows, head): its rows depend only on themselves, so they
+// stay in LDS across the segments (transposed, [key][row]).  Pi_s is staged whole in
+// LDS; the next map's Pi and C rows are loaded into registers while the current product
+// runs.  Wave q owns rows 4q .. 4q+3, lane l the columns CW l .. CW l + CW - 1 (CW = D / 64).
 template <int D>
 struct ScanLayout {
   static constexpr size_t bytes = sizeof(float) * (D * D + D * 16);
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
+template <int D, bool REV>
+__global__ __launch_bounds__(256) void seg_scan_kernel(ScanArgs a) {
   constexpr int CW = D / 64, NL = D * D / 4 / 256;
   extern __shared__ __align__(16) unsigned char smem[];
   float* Pi = reinterpret_cast<float*>(smem);
   float* SrT = Pi + D * D;
   const int bh = blockIdx.y, r0 = 16 * blockIdx.x;
   const int tid = threadIdx.x, rq = tid / 64, c0 = CW * (tid % 64);
+  // step k (k = 0 .. nseg-2) reads the rows of segment slot(k) and map slot(k) and
+  // writes slot(k + 1)
+  auto slot = [&](int k) { return REV ? a.nseg - 1 - k : k; };
   float acc[4][CW];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = r0 + 4 * rq + i;
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
-      const float x = a.S0 ? a.S0[((size_t)bh * D + row) * D + c0 + c] : 0.f;
+      const float x = a.init ? a.init[((size_t)bh * D + row) * D + c0 + c] : 0.f;
       acc[i][c] = x;
-      a.S_seg[((size_t)bh * a.nseg * D + row) * D + c0 + c] = x;
+      a.seg[(((size_t)bh * a.nseg + slot(0)) * D + row) * D + c0 + c] = x;
       SrT[(c0 + c) * 16 + 4 * rq + i] = x;
     }
   }
   f32x4 pre[NL];
   float cpre[4][CW];
-  auto fetch = [&](int s) {
-    const float* map = a.aff + (size_t)(bh * a.nseg + s) * 2 * D * D;
+  auto fetch = [&](int k) {
+    const float* map = a.aff + (size_t)(bh * a.nseg + slot(k)) * 2 * D * D;
 #pragma unroll
     for (int l = 0; l < NL; ++l) pre[l] = load4f(map + (size_t)D * D + 4 * (tid + 256 * l));
 #pragma unroll
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
       for (int c = 0; c < CW; ++c) cpre[i][c] = map[(size_t)(r0 + 4 * rq + i) * D + c0 + c];
   };
   if (a.nseg > 1) fetch(0);
-  for (int s = 0; s + 1 < a.nseg; ++s) {
+  for (int k = 0; k + 1 < a.nseg; ++k) {
     // every read of the previous Pi and SrT finished before the barrier that ended the last step
 #pragma unroll
     for (int l = 0; l < NL; ++l) store4(Pi + 4 * (tid + 256 * l), pre[l]);
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < CW; ++c) acc[i][c] = cpre[i][c];
     __syncthreads();
-    if (s + 2 < a.nseg) fetch(s + 1);
+    if (k + 2 < a.nseg) fetch(k + 1);
 #pragma unroll 4
     for (int j = 0; j < D; ++j) {
       const f32x4 sv = load4f(SrT + j * 16 + 4 * rq);
@@ -474,11 +478,28 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(FwdArgs a) {
       const int row = r0 + 4 * rq + i;
 #pragma unroll
       for (int c = 0; c < CW; ++c) {
-        a.S_seg[(((size_t)bh * a.nseg + s + 1) * D + row) * D + c0 + c] = acc[i][c];
+        a.seg[(((size_t)bh * a.nseg + slot(k + 1)) * D + row) * D + c0 + c] = acc[i][c];
         SrT[(c0 + c) * 16 + 4 * rq + i] = acc[i][c];
       }
     }
   }
+}
+
+template <int D, bool REV>
+static hipError_t scan_launch(const ScanArgs& a, int BH, hipStream_t st) {
+  auto scan = seg_scan_kernel<D, REV>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)ScanLayout<D>::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(scan, dim3(D / 16, BH), dim3(256), ScanLayout<D>::bytes, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_scan(const ScanArgs& a, int D, int BH, bool rev, hipStream_t st) {
+  if (a.nseg < 2 || !a.aff || !a.seg) return hipErrorInvalidValue;
+  if (D == 128) return rev ? scan_launch<128, true>(a, BH, st) : scan_launch<128, false>(a, BH, st);
+  if (D == 64) return rev ? scan_launch<64, true>(a, BH, st) : scan_launch<64, false>(a, BH, st);
+  return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------ content-aware forward
@@ -734,11 +755,8 @@ static hipError_t state_launch(const FwdArgs& a, hipStream_t st) {
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    auto scan = seg_scan_kernel<D>;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)ScanLayout<D>::bytes);
+    e = launch_seg_scan(ScanArgs{a.S0, a.S_seg, a.aff, nseg}, D, a.B * a.H, false, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(scan, dim3(D / 16, a.B * a.H), dim3(256), ScanLayout<D>::bytes, st, a);
   }
   dim3 grid((D / VS) * a.B * a.H * nseg);
   if (a.o && a.S_vk) hipLaunchKernelGGL((fwd_state_kernel<T, LC, D, VS, true, true>), grid, dim3(kThreads), Lay::bytes, st, a);
