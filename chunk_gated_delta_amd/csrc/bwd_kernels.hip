@@ -118,24 +118,27 @@ struct RevOps {
   }
 };
 
-// One reverse pass over chunks chi down to clo for a slice of VS rows of the state
-// gradient, held as accumulator tiles of dS^T (lane of tile (ct, vt) holds
-// dS[v0 + 16 vt + lr][16 ct + 4 lg + i]):
+// Reverse state pass.  A slice of VS rows of the state gradient is held as accumulator
+// tiles of dS^T (lane of tile (ct, vt) holds dS[v0 + 16 vt + lr][16 ct + 4 lg + i]) and
+// stepped over chunks chi down to clo:
 //   dS^T <- Diag(Gamma_L) dS^T + (-W)^T (K-> dS^T) + Q~^T dO.
-// The rows start from rows v0 .. of `init` (a D x D matrix; null: zero) or, with
-// eye_row >= 0, from the identity rows eye_row .. (the linear part of a segment's map).
-// with_do = false leaves out the output term.  STORE: the gradient w.r.t. the state
-// leaving every chunk goes to dS_vk (fragment order).  On return dS holds the gradient
-// w.r.t. the state entering chunk clo.
-template <typename T, int LC, int D, int VS, bool STORE>
-__device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int clo, int chi, const float* init,
-                                         int eye_row, bool with_do, f32x4 (&dS)[StateTiles<D, VS>::SPW],
-                                         unsigned char* smem) {
+// AFF = false: workgroup = (slice of VS value rows, batch*head[, segment]).  Unsegmented:
+// chunks c_lo .. (all by default) from dS_T, ending in dS0.  Segmented (fwd.nseg > 1):
+// segment s runs its chunks from dS_seg[s], the gradient w.r.t. the state leaving it, and
+// the first segment ends in dS0.  The gradient w.r.t. the state leaving every chunk goes
+// to dS_vk (fragment order).
+// AFF = true: the segments' reverse maps (see the segmented reverse pass below):
+// workgroup = (VS rows of [C; Pi], batch*head, segment s >= 1); C rows start from zero
+// with the output term, Pi rows from the identity rows without it; nothing is stored
+// per chunk, and the rows end in raff.
+template <typename T, int LC, int D, int VS, bool AFF>
+__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   using Lay = RevLayout<T, LC, D, VS>;
   using Op = RevOps<T, LC, D, VS>;
   using ST = StateTiles<D, VS>;
   constexpr int NVT = ST::NVT, SPW = ST::SPW, LDS_ = Lay::LDS_, LDU = Lay::LDU, LDV = Lay::LDV;
   constexpr int VEC = Op::VEC;
+  extern __shared__ __align__(16) unsigned char smem[];
   T* dSb = reinterpret_cast<T*>(smem);
   T* XT = dSb + VS * LDS_;
   T* dOr = XT + VS * LDU;
@@ -143,13 +146,36 @@ __device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int c
   T* Ql = reinterpret_cast<T*>(smem + Lay::Ql);
   T* Kl = reinterpret_cast<T*>(smem + Lay::Kl);
   const FwdArgs& f = a.fwd;
+  const int nseg = f.nseg > 1 ? f.nseg : 1;
   const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+  int u, slice, bh, seg, v0, eye_row = -1;
+  bool with_do = true;
+  const float* init = nullptr;
+  if constexpr (AFF) {
+    const int nsa = nseg - 1;                  // segments with a reverse map: all but the first
+    xcd_slice_map(2 * D / VS, f.B * f.H * nsa, u, slice);
+    bh = u / nsa;
+    seg = 1 + u % nsa;
+    const int r0 = slice * VS;                 // first row of [C; Pi]
+    v0 = r0 < D ? r0 : 0;                      // value rows of C (Pi rows read no dO)
+    if (r0 >= D) {
+      eye_row = r0 - D;
+      with_do = false;
+    }
+  } else {
+    xcd_slice_map(D / VS, f.B * f.H * nseg, u, slice);
+    bh = u / nseg;
+    seg = u % nseg;
+    v0 = slice * VS;
+    init = nseg > 1 ? a.dS_seg + (size_t)u * D * D : (a.dS_T ? a.dS_T + (size_t)bh * D * D : nullptr);
+  }
 
+  f32x4 dS[SPW];
 #pragma unroll
   for (int j = 0; j < SPW; ++j) {
     const int st = wave * SPW + j, ct = st / NVT, vt = st % NVT;
     const int vl = 16 * vt + lr, kc = 16 * ct + 4 * lg;
-    if (eye_row >= 0) {
+    if (AFF && eye_row >= 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) dS[j][i] = (eye_row + vl == kc + i) ? 1.f : 0.f;
     } else if (init) {
@@ -163,6 +189,9 @@ __device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int c
   // chunk's factors are staged in LDS during the step before its own.  Chunks below
   // the last one run in a main loop with clamped prefetch.
   constexpr int PF = 3;
+  // chunk range: the segment's chunks, or (unsegmented) c_lo .. (all by default)
+  const int clo = nseg > 1 ? seg * f.seg_len : a.c_lo;
+  const int chi = nseg > 1 ? min(f.NC, clo + f.seg_len) - 1 : (a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1);
   const int nch = chi - clo + 1;
   Op buf[PF];
 #pragma unroll
@@ -170,9 +199,9 @@ __device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int c
   buf[0].stage(Wl, Ql, Kl);
   __syncthreads();
   auto step = [&](int c, const Op& cur, const Op& nxt) {
-    if constexpr (STORE) {
+    const size_t ci = (size_t)bh * f.NC + c;
+    if constexpr (!AFF) {
       // gradient w.r.t. the state leaving chunk c, in fragment order rows v
-      const size_t ci = (size_t)bh * f.NC + c;
       T* vk = reinterpret_cast<T*>(a.dS_vk) + ci * D * D;
 #pragma unroll
       for (int j = 0; j < SPW; ++j) {
@@ -185,11 +214,11 @@ __device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int c
     // sequence end hold the clamped copy of the last row; they only meet columns of
     // Q~^T that are exactly zero (q is zero past the end, so Q+, P and Q~ vanish there).
 #pragma unroll
-    for (int u = 0; u < Op::NDO; ++u) {
-      const int idx = threadIdx.x + kThreads * u;
+    for (int u2 = 0; u2 < Op::NDO; ++u2) {
+      const int idx = threadIdx.x + kThreads * u2;
       if (Op::kFullDO || idx < LC * VS / VEC) {
         const int r = idx / (VS / VEC), g = idx % (VS / VEC);
-        *reinterpret_cast<Frag<T>*>(dOr + r * LDV + VEC * g) = cur.dov[u];
+        *reinterpret_cast<Frag<T>*>(dOr + r * LDV + VEC * g) = cur.dov[u2];
       }
     }
     // this chunk's factor fragments, transposed out of the staged blocks: K-> rows of
@@ -212,8 +241,8 @@ __device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int c
     // X^T = K-> dS^T  (tiles [s][v])
     if (Op::kAllWaves || t0 < Op::NX) {
 #pragma unroll
-      for (int u = 0; u < Op::XPW; ++u) {
-        const int vt = (t0 + u) % NVT;
+      for (int x = 0; x < Op::XPW; ++x) {
+        const int vt = (t0 + x) % NVT;
         const int vl = 16 * vt + lr;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -256,46 +285,16 @@ __device__ __forceinline__ void rev_pass(const BwdArgs& a, int bh, int v0, int c
       step(c, buf[j], buf[(j + 1) % PF]);
     }
   }
-}
-
-// Rows v0 .. v0 + VS - 1 of a D x D matrix (row stride D) from the accumulator tiles.
-template <int D, int VS>
-__device__ __forceinline__ void store_rows(float* dst, int v0, const f32x4 (&S)[StateTiles<D, VS>::SPW]) {
-  using ST = StateTiles<D, VS>;
-  const int lane = lane_id(), wave = wave_id(), lr = lane & 15, lg = lane >> 4;
+  // AFF: the rows of [C; Pi]; otherwise dS0 from the first segment
+  float* dst = AFF ? a.raff + (size_t)(bh * f.nseg + seg) * 2 * D * D + (size_t)(slice * VS) * D
+                   : (a.dS0 && seg == 0 ? a.dS0 + ((size_t)bh * D + v0) * D : nullptr);
+  if (dst) {
 #pragma unroll
-  for (int j = 0; j < ST::SPW; ++j) {
-    const int st = wave * ST::SPW + j, ct = st / ST::NVT, vt = st % ST::NVT;
-    store4(dst + (size_t)(v0 + 16 * vt + lr) * D + 16 * ct + 4 * lg, S[j]);
+    for (int j = 0; j < SPW; ++j) {
+      const int st = wave * SPW + j, ct = st / NVT, vt = st % NVT;
+      store4(dst + (size_t)(16 * vt + lr) * D + 16 * ct + 4 * lg, dS[j]);
+    }
   }
-}
-
-// Workgroup = (slice of VS value rows, batch*head[, segment]).  Unsegmented: chunks
-// c_lo .. (all by default) from dS_T, ending in dS0.  Segmented (fwd.nseg > 1): segment
-// s runs its chunks from dS_seg[s], the gradient w.r.t. the state leaving it, and the
-// first segment ends in dS0.
-template <typename T, int LC, int D, int VS>
-__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const FwdArgs& f = a.fwd;
-  const int nseg = f.nseg > 1 ? f.nseg : 1;
-  int u, slice;
-  xcd_slice_map(D / VS, f.B * f.H * nseg, u, slice);
-  const int bh = u / nseg, seg = u % nseg, v0 = slice * VS;
-  int clo, chi;
-  const float* init;
-  if (nseg > 1) {
-    clo = seg * f.seg_len;
-    chi = min(f.NC, clo + f.seg_len) - 1;
-    init = a.dS_seg + (size_t)u * D * D;
-  } else {
-    clo = a.c_lo;
-    chi = a.c_count ? a.c_lo + a.c_count - 1 : f.NC - 1;
-    init = a.dS_T ? a.dS_T + (size_t)bh * D * D : nullptr;
-  }
-  f32x4 dS[StateTiles<D, VS>::SPW];
-  rev_pass<T, LC, D, VS, true>(a, bh, v0, clo, chi, init, -1, true, dS, smem);
-  if (a.dS0 && seg == 0) store_rows<D, VS>(a.dS0 + (size_t)bh * D * D, v0, dS);
 }
 
 // ------------------------------------------------------------------ segmented reverse pass
@@ -303,27 +302,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 // leaving it to the gradient w.r.t. the state entering it as dS_in = dS_out Pi + C: C is
 // the segment's reverse pass from dS_out = 0, and Pi, the product of the transposed
 // chunk maps, is the pass with no output term started from the identity (its rows are
-// indexed by key).  bwd_affine computes [C; Pi] as 2D rows per (head, segment) for every
-// segment but the first; the reverse scan of seg_scan chains them from dS_T down
-// (dS_out(s - 1) = dS_out(s) Pi_s + C_s); then every segment runs its reverse pass from
-// its dS_out, storing the chunk-level gradients.  The reverse side of the chunk-level
-// scan of affine state maps behind the logarithmic parallel depth the notes list for
-// CARVE (complexity table), taken as two levels like the forward.
-template <typename T, int LC, int D, int VS>
-__global__ __launch_bounds__(kThreads) void bwd_affine_kernel(BwdArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const FwdArgs& f = a.fwd;
-  const int nsa = f.nseg - 1;                  // segments with a reverse map: all but the first
-  int u, slice;
-  xcd_slice_map(2 * D / VS, f.B * f.H * nsa, u, slice);
-  const int bh = u / nsa, seg = 1 + u % nsa;
-  const int r0 = slice * VS;                   // first row of [C; Pi]
-  const bool pi = r0 >= D;
-  const int clo = seg * f.seg_len, chi = min(f.NC, clo + f.seg_len) - 1;
-  f32x4 dS[StateTiles<D, VS>::SPW];
-  rev_pass<T, LC, D, VS, false>(a, bh, pi ? 0 : r0, clo, chi, nullptr, pi ? r0 - D : -1, !pi, dS, smem);
-  store_rows<D, VS>(a.raff + (size_t)(bh * f.nseg + seg) * 2 * D * D, r0, dS);
-}
+// indexed by key).  bwd_state_kernel<AFF = true> computes [C; Pi] as 2D rows per (head,
+// segment) for every segment but the first; the reverse scan of seg_scan chains them from
+// dS_T down (dS_out(s - 1) = dS_out(s) Pi_s + C_s); then every segment runs its reverse
+// pass from its dS_out, storing the chunk-level gradients.  The reverse side of the
+// chunk-level scan of affine state maps behind the logarithmic parallel depth the notes
+// list for CARVE (complexity table), taken as two levels like the forward.
 
 // ------------------------------------------------------------------ chunk gradients
 // LDS slots (reused as the computation proceeds; "row-major" = [token][width]):
@@ -1856,11 +1840,11 @@ template <typename T, int LC, int D, int VS>
 static hipError_t rev_affine_launch(const BwdArgs& a, hipStream_t st) {
   using Lay = RevLayout<T, LC, D, VS>;
   static_assert(Lay::bytes <= 80 * 1024, "reverse-state LDS exceeds half a compute unit's 160 KB");
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_affine_kernel<T, LC, D, VS>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_state_kernel<T, LC, D, VS, true>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
   dim3 grid((2 * D / VS) * a.fwd.B * a.fwd.H * (a.fwd.nseg - 1));
-  hipLaunchKernelGGL((bwd_affine_kernel<T, LC, D, VS>), grid, dim3(kThreads), Lay::bytes, st, a);
+  hipLaunchKernelGGL((bwd_state_kernel<T, LC, D, VS, true>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }
 
@@ -1879,11 +1863,11 @@ static hipError_t rev_launch(const BwdArgs& a, hipStream_t st) {
     e = launch_seg_scan(ScanArgs{a.dS_T, a.dS_seg, a.raff, nseg}, D, f.B * f.H, true, st);
     if (e != hipSuccess) return e;
   }
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_state_kernel<T, LC, D, VS>),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_state_kernel<T, LC, D, VS, false>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lay::bytes);
   if (e != hipSuccess) return e;
   dim3 grid((D / VS) * f.B * f.H * nseg);
-  hipLaunchKernelGGL((bwd_state_kernel<T, LC, D, VS>), grid, dim3(kThreads), Lay::bytes, st, a);
+  hipLaunchKernelGGL((bwd_state_kernel<T, LC, D, VS, false>), grid, dim3(kThreads), Lay::bytes, st, a);
   return hipGetLastError();
 }
 
