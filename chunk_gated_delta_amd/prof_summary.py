@@ -7,6 +7,7 @@
 
     python -m chunk_gated_delta_amd.prof_summary mfma COUNTER_CSV --stats-csv KERNEL_STATS_CSV --simds N
                                                    --title T --command C --command-stats C2 --out F
+    python -m chunk_gated_delta_amd.prof_summary lds COUNTER_CSV --title T --command C --out F
 
 `stats` tabulates a --kernel-trace --stats run.  `mfma` takes one --pmc run of the MFMA
 counters (SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, the derived MfmaUtil, and the
@@ -168,6 +169,28 @@ def mfma(args):
     open(args.out, "w").write("\n".join(out) + "\n")
 
 
+def lds(args):
+    """LDS counters (SQ_INSTS_LDS, SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT) averaged per kernel."""
+    from chunk_gated_delta_amd.build import source_digest
+    per = _counters(args.csv)
+    out = [f"# {args.title}", "", "Command (from /tmp with TMPDIR=/tmp; repository at $R, PYTHONPATH=$R):", "",
+           "    " + args.command, "",
+           "Counter values averaged over the dispatches of each kernel (cycles summed over the chip as the SQ "
+           "counters report them).", "",
+           "| kernel | dispatches | SQ_INSTS_LDS | SQ_LDS_IDX_ACTIVE | SQ_LDS_BANK_CONFLICT | conflict / active |",
+           "|---|---|---|---|---|---|"]
+    for name, c in per.items():
+        if "carve" not in name:
+            continue
+        mean = {k_: statistics.mean(v_) for k_, v_ in c.items()}
+        act = mean.get("SQ_LDS_IDX_ACTIVE", 0.0)
+        con = mean.get("SQ_LDS_BANK_CONFLICT", 0.0)
+        out.append(f"| {short_name(name)} `{name[:70]}` | {len(c.get('SQ_LDS_IDX_ACTIVE', []))} | "
+                   f"{mean.get('SQ_INSTS_LDS', 0.0):.0f} | {act:.0f} | {con:.0f} | {con / act if act else 0.0:.2f} |")
+    out += ["", "Kernel sources digest at measurement: `" + source_digest() + "`"]
+    open(args.out, "w").write("\n".join(out) + "\n")
+
+
 def _read_tagged(path, tag):
     try:
         for line in open(path):
@@ -215,8 +238,13 @@ def main(argv=None):
     m.add_argument("--command", required=True)
     m.add_argument("--command-stats", required=True)
     m.add_argument("--out", required=True)
+    d = sub.add_parser("lds")
+    d.add_argument("csv")
+    d.add_argument("--title", required=True)
+    d.add_argument("--command", required=True)
+    d.add_argument("--out", required=True)
     a = p.parse_args(argv)
-    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.cmd](a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "lds": lds}[a.cmd](a)
     return 0
 
 
