@@ -446,10 +446,17 @@ def logits_bench(q, k, v, dO, wl, dev, nrep=5):
         e1.record()
         torch.cuda.synchronize()
         return round(e0.elapsed_time(e1) / nrep, 4)
+    saved = carve.fwd_logits_save(q, k, v, f, A, tau, w_hat, b_x=b_x, L=wl.L)[2]
     out = {"fwd_logits_ms": timed(lambda: carve.fwd_logits(q, k, v, f, A, tau, w_hat, b_x=b_x, L=wl.L,
                                                            workspace=ws_f)),
            "bwd_logits_ms": timed(lambda: carve.bwd_logits(q, k, v, f, A, tau, w_hat, dO, b_x=b_x, L=wl.L)),
-           "bwd_plain_ms": timed(lambda: carve.bwd(q, k, v, log_g, w, dO, b=b, L=wl.L))}
+           "bwd_plain_ms": timed(lambda: carve.bwd(q, k, v, log_g, w, dO, b=b, L=wl.L)),
+           # the training pair: the forward keeps its factors, the backward does not recompute it
+           "fwd_logits_save_ms": timed(lambda: carve.fwd_logits_save(q, k, v, f, A, tau, w_hat, b_x=b_x, L=wl.L,
+                                                                     saved=saved)),
+           "bwd_logits_saved_ms": timed(lambda: carve.bwd_logits_saved(q, k, v, f, A, tau, w_hat, dO, saved,
+                                                                       b_x=b_x, L=wl.L))}
+    out["train_pair_ms"] = round(out["fwd_logits_save_ms"] + out["bwd_logits_saved_ms"], 4)
     return out
 
 

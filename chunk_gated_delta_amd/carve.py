@@ -121,6 +121,13 @@ def load_library():
     lib.carve_bwd_logits_workspace_size.restype = sz
     lib.carve_bwd_logits.argtypes = [sp, vp, vp, vp, glp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.carve_bwd_logits.restype = i
+    lib.carve_bwd_logits_saved_workspace_size.argtypes = [sp]
+    lib.carve_bwd_logits_saved_workspace_size.restype = sz
+    lib.carve_fwd_logits_save.argtypes = [sp, vp, vp, vp, glp, vp, vp, vp, vp, sz, vp, pp]
+    lib.carve_fwd_logits_save.restype = i
+    lib.carve_bwd_logits_saved.argtypes = [sp, vp, vp, vp, glp, vp, vp, vp, sz, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           vp, sz, vp, pp]
+    lib.carve_bwd_logits_saved.restype = i
     lib.carve_bwd_content_workspace_size.argtypes = [sp, cp]
     lib.carve_bwd_content_workspace_size.restype = sz
     lib.carve_bwd_content.argtypes = [sp, vp, vp, vp, vp, vp, vp, cp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -436,6 +443,62 @@ def bwd_logits(q, k, v, f, A, tau, w_hat, dO, b_x=None, S0=None, dS_T=None, L=64
                                 _ptr(out["dS0"]), _ptr(workspace), workspace.numel(), _stream(dev))
     _raise(code, "carve_bwd_logits")
     return out
+
+
+def fwd_logits_save(q, k, v, f, A, tau, w_hat, b_x=None, S0=None, L=64, o=None, S_T=None, saved=None, profile=None):
+    """fwd_logits that also keeps what bwd_logits_saved needs: (o, S_T, saved)."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, H, T, Dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, Dv), q.dtype, dev)
+    _check(S0, "S0", (B, H, Dv, Dk), torch.float32, dev)
+    g = _gate_logits(q, f, A, tau, w_hat, b_x)
+    s = make_shape(q, v, L)
+    if o is None:
+        o = torch.empty((B, H, T, Dv), dtype=q.dtype, device=dev)
+    if S_T is None:
+        S_T = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    need = lib.carve_saved_size(ctypes.byref(s))
+    if saved is None or saved.numel() < need:
+        saved = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_fwd_logits_save(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g), _ptr(S0), _ptr(o),
+                                     _ptr(S_T), _ptr(saved), saved.numel(), _stream(dev),
+                                     ctypes.byref(profile) if profile is not None else None)
+    _raise(code, "carve_fwd_logits_save")
+    return o, S_T, saved
+
+
+def bwd_logits_saved(q, k, v, f, A, tau, w_hat, dO, saved, b_x=None, dS_T=None, L=64, want_dS0=True,
+                     workspace=None, out=None, profile=None):
+    """Backward from the buffer of fwd_logits_save (same inputs): dict as bwd_logits()."""
+    lib = load_library()
+    B, H, T, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", (B, H, T, Dk), q.dtype, dev)
+    _check(v, "v", (B, H, T, Dv), q.dtype, dev)
+    _check(dO, "dO", (B, H, T, Dv), q.dtype, dev)
+    _check(dS_T, "dS_T", (B, H, Dv, Dk), torch.float32, dev)
+    g = _gate_logits(q, f, A, tau, w_hat, b_x)
+    s = make_shape(q, v, L)
+    res = out if out is not None else {
+        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v), "df": torch.empty_like(f),
+        "dA": torch.empty_like(A), "dtau": torch.empty_like(tau),
+        "db_x": None if b_x is None else torch.empty_like(b_x), "dw_hat": torch.empty_like(w_hat),
+        "dS0": torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev) if want_dS0 else None}
+    need = lib.carve_bwd_logits_saved_workspace_size(ctypes.byref(s))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    code = lib.carve_bwd_logits_saved(ctypes.byref(s), _ptr(q), _ptr(k), _ptr(v), ctypes.byref(g), _ptr(dO),
+                                      _ptr(dS_T), _ptr(saved), saved.numel(), _ptr(res["dq"]), _ptr(res["dk"]),
+                                      _ptr(res["dv"]), _ptr(res["df"]), _ptr(res["dA"]), _ptr(res["dtau"]),
+                                      _ptr(res["db_x"]), _ptr(res["dw_hat"]), _ptr(res["dS0"]), _ptr(workspace),
+                                      workspace.numel(), _stream(dev),
+                                      ctypes.byref(profile) if profile is not None else None)
+    _raise(code, "carve_bwd_logits_saved")
+    return res
 
 
 def bwd_content_workspace_bytes(q, v, L=64, R=0, records=False):

@@ -518,6 +518,23 @@ carve_status check_logits(const carve_shape* s, const Plan& p, const carve_gate_
   return CARVE_OK;
 }
 
+// arguments of the logit-space epilogue (df in place, dA and dtau from per-block partial sums)
+carve::LogitGradArgs logit_grad_args(const carve_shape* s, const Plan& p, const carve_gate_logits* gates, float* df,
+                                     float* partA) {
+  carve::LogitGradArgs lg = {};
+  lg.B = s->B;
+  lg.H = s->H;
+  lg.T = s->T;
+  lg.D = p.D;
+  lg.f = gates->f;
+  lg.A = gates->A;
+  lg.tau = gates->tau;
+  lg.df = df;
+  lg.partA = partA;
+  lg.partT = partA + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) / (2 * sizeof(float));
+  return lg;
+}
+
 carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k, const void* v,
                               const carve_gate_logits* gates, const float* S0, void* o, float* S_T,
                               void* workspace, size_t workspace_bytes, void* stream) {
@@ -606,18 +623,121 @@ carve_status carve_bwd_logits(const carve_shape* s, const void* q, const void* k
   if (e == hipSuccess) e = carve::launch_fwd_state(a.fwd, hs);
   if (e == hipSuccess) e = carve::launch_bwd_state(a, hs);
   if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
-  carve::LogitGradArgs lg = {};
-  lg.B = s->B;
-  lg.H = s->H;
-  lg.T = s->T;
-  lg.D = p.D;
-  lg.f = gates->f;
-  lg.A = gates->A;
-  lg.tau = gates->tau;
-  lg.df = df;
-  lg.partA = partA;
-  lg.partT = partA + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) / (2 * sizeof(float));
-  if (e == hipSuccess) e = carve::launch_logit_grads(lg, dA, dtau, hs);
+  if (e == hipSuccess) e = carve::launch_logit_grads(logit_grad_args(s, p, gates, df, partA), dA, dtau, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+// ------------------------------------------------------------ training pair, gates as pre-activations
+size_t bwd_logits_saved_ws(const carve_shape* s, const Plan& p) {
+  if (p.empty) return 0;
+  return bwd_saved_ws(s, p) + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) + 512;
+}
+
+size_t carve_bwd_logits_saved_workspace_size(const carve_shape* s) {
+  Plan p;
+  if (check_shape(s, &p) != CARVE_OK) return 0;
+  return bwd_logits_saved_ws(s, p);
+}
+
+carve_status carve_fwd_logits_save(const carve_shape* s, const void* q, const void* k, const void* v,
+                                   const carve_gate_logits* gates, const float* S0, void* o, float* S_T,
+                                   void* saved, size_t saved_bytes_given, void* stream, const carve_profile* prof) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  st = check_logits(s, p, gates);
+  if (st != CARVE_OK) return st;
+  if (!p.empty && (!q || !k || !v || !o)) return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, (const void*)S0, (const void*)o, (const void*)S_T, (const void*)saved})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need = saved_bytes(s, p);
+  if (saved_bytes_given < need || (need > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = S_T ? carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * p.D * p.D, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::FwdArgs a = fwd_args(s, p, q, k, v, gates->f, gates->b_x, gates->w_hat, S0, o, S_T);
+  a.logits = 1;
+  a.gA = gates->A;
+  a.gtau = gates->tau;
+  a.mode = 3;
+  a.f = carve::carve_factors(saved, a.dtype, p.BH, p.NC, p.LC, p.D, 3);
+  char* base = align_up(static_cast<char*>(saved) + carve::factors_bytes(a.dtype, p.BH, p.NC, p.LC, p.D, 3));
+  a.S_vk = base;
+  set_segments(&a, seg_planned(p), base + states_bytes(s, p) + 256);
+  mark(prof, 0, hs);
+  hipError_t e = carve::launch_fwd_prep(a, hs);
+  mark(prof, 1, hs);
+  if (e == hipSuccess) e = carve::launch_fwd_state(a, hs);
+  mark(prof, 2, hs);
+  return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+carve_status carve_bwd_logits_saved(const carve_shape* s, const void* q, const void* k, const void* v,
+                                    const carve_gate_logits* gates, const void* dO, const float* dS_T,
+                                    const void* saved, size_t saved_bytes_given, void* dq, void* dk, void* dv,
+                                    float* df, float* dA, float* dtau, float* db_x, float* dw_hat, float* dS0,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    const carve_profile* prof) {
+  Plan p;
+  carve_status st = check_shape(s, &p);
+  if (st != CARVE_OK) return st;
+  st = check_logits(s, p, gates);
+  if (st != CARVE_OK) return st;
+  if ((gates->b_x == nullptr) != (db_x == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!q || !k || !v || !dO || !dq || !dk || !dv || !df || !dA || !dtau || !dw_hat))
+    return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, dO, (const void*)dS_T, saved, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)df, (const void*)db_x, (const void*)dw_hat, (const void*)dS0})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  const size_t need_saved = saved_bytes(s, p);
+  if (saved_bytes_given < need_saved || (need_saved > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  const size_t need = bwd_logits_saved_ws(s, p);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = dS0 ? carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * p.D * p.D, hs) : hipSuccess;
+    if (e == hipSuccess && dA && s->H > 0) e = carve::launch_copy_or_zero(dA, nullptr, (size_t)s->H * p.D, hs);
+    if (e == hipSuccess && dtau && s->H > 0) e = carve::launch_copy_or_zero(dtau, nullptr, (size_t)s->H * p.D, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  carve::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.fwd = fwd_args(s, p, q, k, v, gates->f, gates->b_x, gates->w_hat, nullptr, nullptr, nullptr);
+  a.fwd.logits = 1;
+  a.fwd.gA = gates->A;
+  a.fwd.gtau = gates->tau;
+  a.fwd.mode = 3;
+  void* sv = const_cast<void*>(saved);
+  a.fwd.f = carve::carve_factors(sv, a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 3);
+  char* base = align_up(static_cast<char*>(sv) + carve::factors_bytes(a.fwd.dtype, p.BH, p.NC, p.LC, p.D, 3));
+  const size_t states = states_bytes(s, p);
+  a.fwd.S_vk = base;
+  a.dS_vk = align_up(workspace);
+  set_diag(&a, s, p, static_cast<char*>(a.dS_vk) + states);
+  set_segments(&a.fwd, seg_planned(p),
+               static_cast<char*>(a.diag) + carve::diag_fix_bytes(a.fwd.dtype, p.BH, p.NC, p.LC));
+  a.raff = a.fwd.aff;
+  a.dS_seg = a.fwd.S_seg;
+  // the logit epilogue's partial sums after everything the saved backward uses
+  float* partA = reinterpret_cast<float*>(align_up(static_cast<char*>(workspace) + bwd_saved_ws(s, p)));
+  a.dO = dO;
+  a.dS_T = dS_T;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlog_g = df;        // d/dlog g, turned into d/df by the logit pass
+  a.db = db_x;          // the chunk kernel returns d/db_x directly
+  a.dw = dw_hat;        // ... and d/dw_hat
+  a.dS0 = dS0;
+  mark(prof, 0, hs);
+  hipError_t e = carve::launch_bwd_state(a, hs);
+  mark(prof, 1, hs);
+  if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
+  mark(prof, 2, hs);
+  if (e == hipSuccess) e = carve::launch_logit_grads(logit_grad_args(s, p, gates, df, partA), dA, dtau, hs);
+  mark(prof, 3, hs);
   return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 

@@ -297,6 +297,31 @@ carve_status carve_bwd_logits(const carve_shape* s,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Training pair with the gates given as pre-activations: carve_fwd_logits that also fills
+ * `saved` (at least carve_saved_size() bytes, the same layout as carve_fwd_save's), and
+ * a backward that uses it instead of recomputing the forward: inputs as
+ * carve_bwd_logits without S0 (it is in `saved`), the `saved` buffer of a
+ * carve_fwd_logits_save call with the same shape and inputs (not checked), a workspace
+ * of carve_bwd_logits_saved_workspace_size() bytes; outputs as carve_bwd_logits.
+ * Profile stages: carve_fwd_logits_save 0 = chunk prep, 1 = state pass;
+ * carve_bwd_logits_saved 0 = reverse state pass, 1 = chunk gradients, 2 = logit epilogue.
+ */
+size_t carve_bwd_logits_saved_workspace_size(const carve_shape* s);
+carve_status carve_fwd_logits_save(const carve_shape* s,
+                                   const void* q, const void* k, const void* v,
+                                   const carve_gate_logits* gates, const float* S0,
+                                   void* o, float* S_T, void* saved, size_t saved_bytes,
+                                   void* stream, const carve_profile* profile);
+carve_status carve_bwd_logits_saved(const carve_shape* s,
+                                    const void* q, const void* k, const void* v,
+                                    const carve_gate_logits* gates, const void* dO, const float* dS_T,
+                                    const void* saved, size_t saved_bytes,
+                                    void* dq, void* dk, void* dv, float* df, float* dA, float* dtau,
+                                    float* db_x, float* dw_hat, float* dS0,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    const carve_profile* profile);
+
+/*
  * Backward through the content-aware erase (notes section 2.2): gradients of the
  * content-aware forward, including the projection and the chain through each
  * chunk's mean output into the next chunk's gate.  Recomputes the forward.

@@ -140,3 +140,54 @@ def test_logits_single_token_and_empty():
                               S0=S0)
     torch.cuda.synchronize()
     assert torch.equal(S_T, S0)
+
+
+# ---------------------------------------------------------------- training pair
+def saved_pair(d, inp):
+    o, S_T, saved = carve.fwd_logits_save(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]),
+                                          dev(inp["w_hat"]), b_x=dev(inp["b_x"]), S0=dev(inp["S0"]))
+    g = carve.bwd_logits_saved(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]),
+                               dev(inp["w_hat"]), d["dO"], saved, b_x=dev(inp["b_x"]), dS_T=dev(inp["dS_T"]))
+    return o, S_T, g
+
+
+GRADS = ("dq", "dk", "dv", "df", "dA", "dtau", "db_x", "dw_hat", "dS0")
+
+
+@pytest.mark.parametrize("dtype,B,H,T,D,with_bx", CASES, ids=IDS)
+def test_logits_saved_pair_matches_recompute_bitwise(dtype, B, H, T, D, with_bx):
+    """fwd_logits_save gives the bits of fwd_logits, and bwd_logits_saved those of
+    bwd_logits (the same arithmetic; only the forward is not recomputed)."""
+    announce(f"logits saved pair vs recompute {dtype} T{T} d{D} b_x={with_bx}")
+    inp = logit_case(B, H, T, D, dtype, seed=700 + T + D, with_bx=with_bx)
+    d = to_device(inp, dtype)
+    o1, s1 = carve.fwd_logits(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]),
+                              dev(inp["w_hat"]), b_x=dev(inp["b_x"]), S0=dev(inp["S0"]))
+    g1 = carve.bwd_logits(d["q"], d["k"], d["v"], dev(inp["f"]), dev(inp["A"]), dev(inp["tau"]), dev(inp["w_hat"]),
+                          d["dO"], b_x=dev(inp["b_x"]), S0=dev(inp["S0"]), dS_T=dev(inp["dS_T"]))
+    o2, s2, g2 = saved_pair(d, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    for key in GRADS:
+        if g1[key] is None:
+            assert g2[key] is None
+            continue
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_logits_saved_pair_segmented_parity():
+    """Few heads, 40 chunks: the saved pair runs its forward and reverse state passes as
+    segments; every output and gradient against the reference."""
+    announce("logits saved pair, segmented, bf16 B1 H2 T2560 d128")
+    inp = logit_case(1, 2, 64 * 40, 128, "bf16", seed=720, with_bx=True)
+    d = to_device(inp, "bf16")
+    o, S_T, g = saved_pair(d, inp)
+    torch.cuda.synchronize()
+    ro, rS = oracle.forward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"],
+                                   b_x=inp["b_x"], S0=inp["S0"])
+    ref = oracle.backward_logits(inp["q"], inp["k"], inp["v"], inp["f"], inp["A"], inp["tau"], inp["w_hat"],
+                                 inp["dO"], b_x=inp["b_x"], S0=inp["S0"], dS_T=inp["dS_T"])
+    errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS)}
+    errs.update({key: max_rel(to_np(g[key]), ref[key]) for key in GRADS})
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL["bf16"] for v_ in errs.values()), errs
