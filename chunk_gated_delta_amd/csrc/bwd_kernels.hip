@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "carve_chunk.h"
+#include "content_gate.h"
 
 namespace carve {
 
@@ -1829,6 +1830,13 @@ __global__ __launch_bounds__(D * 4) void bwd_chunk_kernel(BwdArgs a) {
   const size_t ci = (size_t)blockIdx.y * a.fwd.NC + a.c_lo + blockIdx.x;
   if (a.fwd.f.cflag[ci]) bwd_chunk_range<T, LC, D, HAS_B, LG>(a, smem);
   else bwd_chunk_fast<T, LC, D, HAS_B, LG>(a, smem);
+  if (a.cg_on) {
+    // the chunk's d/db_x stores are visible to the whole workgroup and every LDS read of
+    // the gradient phases is done: the gate backward of the chunk's period follows
+    __syncthreads();
+    content_gate_body<T, D, D * 4>(a.cg, (int)blockIdx.y, reinterpret_cast<const T*>(a.cg_dO),
+                                   reinterpret_cast<T*>(const_cast<void*>(a.dO)), reinterpret_cast<float*>(smem));
+  }
 }
 
 size_t diag_fix_bytes(int dtype, int BH, int NC, int LC) {

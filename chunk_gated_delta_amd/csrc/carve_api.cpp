@@ -896,13 +896,19 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
   // gate kernel of the period after it
   ca.p = ca.NP - 1;
   if (e == hipSuccess) e = carve::launch_add_grad_mean(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
+  // with one token tile per period the chunk-gradient workgroup of each head runs its
+  // period's gate backward itself; otherwise a gate kernel per period follows
+  const bool fused_gate = per == 1;
+  a.cg_on = fused_gate ? 1 : 0;
+  a.cg_dO = dO;
   for (int pp = ca.NP - 1; pp >= 0 && e == hipSuccess; --pp) {
     ca.p = pp;
     a.c_lo = pp * per;
     a.c_count = std::min(per, p.NC - a.c_lo);
+    a.cg = ca;
     e = carve::launch_bwd_state(a, hs);
     if (e == hipSuccess) e = carve::launch_bwd_chunk(a, hs);
-      if (e == hipSuccess) e = carve::launch_content_gate_bwd(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
+    if (e == hipSuccess && !fused_gate) e = carve::launch_content_gate_bwd(ca, a.fwd.dtype, dO, ws + Lw.dOp, hs);
   }
   if (e == hipSuccess && dS0) e = carve::launch_copy_or_zero(dS0, carry, (size_t)p.BH * p.D * p.D, hs);
   if (e == hipSuccess && proj) e = carve::launch_sum_over_batch(ca.dU1p, dU1, s->B, s->H, R * p.D, hs);

@@ -86,6 +86,22 @@ struct ContentArgs {
   float* m_all;           // may be null: [B*H][periods][Dv] the mean output each period's z was formed from
 };
 
+// Per-period pieces of the backward through the content-aware erase.
+struct ContentBwdArgs {
+  int B, H, T, D, L, NP, R;   // L = content period in tokens, NP = number of periods
+  int p;                      // the period a launch works on
+  const float* z_all;         // [B*H][NP][D] content signal of every period
+  const float* m_all;         // [B*H][NP][D] mean output each period's signal was formed from
+  const float* bmat;          // [B,H,T,D] the gate b of every token
+  float* dbx;                 // [B,H,T,D] in: d/db of period p; out: d/db_x
+  const float* U1;            // [H,R,D] or null (no projection)
+  const float* U2;            // [H,D,R]
+  float* dU1p;                // [B*H][R][D] per-sequence accumulators
+  float* dU2p;                // [B*H][D][R]
+  float* g;                   // [B*H][D] output-gradient term of the last period (before the sweep)
+  float* dm0;                 // [B*H][D] or null
+};
+
 struct BwdArgs {
   FwdArgs fwd;            // forward inputs, factors and S_vk (all required)
   const void* dO;
@@ -110,6 +126,13 @@ struct BwdArgs {
   // state leaving every segment as [(bh*nseg + s)][D][D] fp32 (segment nseg-1: dS_T).
   float* raff;
   float* dS_seg;
+  // Content-aware backward with one token tile per content period (cg_on != 0): the
+  // chunk-gradient workgroup of each head runs the gate backward of its period
+  // (content_gate_body) after its stores; cg holds the period's arguments, cg_dO the raw
+  // output gradient, and dO (above) receives dO + g for the period before.
+  int cg_on;
+  ContentBwdArgs cg;
+  const void* cg_dO;
   // Range-safe chunks: diag [ci][NB][2][64][4] (dtype) receives the diagonal tiles of
   // dP and dB of the blocks whose log-retention leaves the fast tiles' range (accumulator
   // order); the same workgroup reads them back for those blocks' exact terms.
@@ -139,21 +162,6 @@ struct DecodeArgs {
   int L, pos;             // content period and the token's position inside it
 };
 
-// Per-period pieces of the backward through the content-aware erase.
-struct ContentBwdArgs {
-  int B, H, T, D, L, NP, R;   // L = content period in tokens, NP = number of periods
-  int p;                      // the period a launch works on
-  const float* z_all;         // [B*H][NP][D] content signal of every period
-  const float* m_all;         // [B*H][NP][D] mean output each period's signal was formed from
-  const float* bmat;          // [B,H,T,D] the gate b of every token
-  float* dbx;                 // [B,H,T,D] in: d/db of period p; out: d/db_x
-  const float* U1;            // [H,R,D] or null (no projection)
-  const float* U2;            // [H,D,R]
-  float* dU1p;                // [B*H][R][D] per-sequence accumulators
-  float* dU2p;                // [B*H][D][R]
-  float* g;                   // [B*H][D] output-gradient term of the last period (before the sweep)
-  float* dm0;                 // [B*H][D] or null
-};
 
 // Logit-space epilogue of the backward for gates given as pre-activations.
 struct LogitGradArgs {
