@@ -281,7 +281,26 @@ def main():
         # inputs (no erase tensor) and o, plus the final state S_T
         extra.setdefault("hbm_frac", {})["long_ctx_fwd"] = hbm_frac(
             algorithmic(wlc, False)["fwd"], wlc, lms, extra_bytes=wlc.B * wlc.H * wlc.Dv * wlc.Dk * 4)
-        del lq, lk, lv, lg_, lw_, lb_
+        # the training pair at the same shape: both state passes run as segments
+        ldO = torch.from_numpy(np.ascontiguousarray(make_inputs(wlc, with_dO=True)["dO_bits"]).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+        lsaved = carve.fwd_save(lq, lk, lv, lg_, lw_, b=lb_, L=wlc.L)[2]
+
+        def long_pair():
+            carve.fwd_save(lq, lk, lv, lg_, lw_, b=lb_, L=wlc.L, saved=lsaved)
+            carve.bwd_saved(lq, lk, lv, lg_, lw_, ldO, lsaved, b=lb_, L=wlc.L, want_dS0=False)
+        for _ in range(2):
+            long_pair()
+        torch.cuda.synchronize()
+        le0.record()
+        for _ in range(3):
+            long_pair()
+        le1.record()
+        torch.cuda.synchronize()
+        ltms = le0.elapsed_time(le1) / 3
+        extra["long_ctx_train_ms"] = round(ltms, 4)
+        extra["long_ctx_train_tokens_per_s"] = wlc.B * wlc.T / (ltms * 1e-3)
+        del lq, lk, lv, lg_, lw_, lb_, ldO, lsaved
 
     # content-aware forward of the same shape (separate timing, not part of the step)
     if not args.no_content:

@@ -257,3 +257,16 @@ def test_stream_copy_rejects_bad_arguments_on_host(lib):
     assert lib.carve_stream_copy(a + 8, b, 32, None) == INVALID    # misaligned destination
     assert lib.carve_stream_copy(a, None, 32, None) == INVALID     # missing source
     assert lib.carve_stream_copy(a, a + 16, 64, None) == INVALID   # overlapping ranges
+
+
+def test_size_limits_on_host(lib):
+    """The largest accepted shapes and the first rejected ones: B*H is a launch grid's y
+    extent (at most 65535), T at most 2^30; the workspace size of the largest head count
+    is finite and nonzero."""
+    assert call_fwd(lib, shape(B=5, H=13108, T=65, D=64)) == UNSUPPORTED          # B*H = 65540
+    assert call_fwd(lib, shape(B=1, H=65536, T=1, D=64)) == UNSUPPORTED
+    assert call_fwd(lib, shape(B=1, H=1, T=(1 << 30) + 1, D=64)) == UNSUPPORTED
+    s = shape(B=5, H=13107, T=65, D=64)                                          # B*H = 65535
+    ws = lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+    assert 0 < ws < (1 << 40)
+    assert 0 < lib.carve_saved_size(ctypes.byref(s)) < (1 << 40)
