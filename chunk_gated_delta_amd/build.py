@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcarve.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["carve_api.cpp", "fwd_kernels.hip", "bwd_kernels.hip", "decode_kernels.hip", "content_bwd_kernels.hip",
-           "stream_kernels.hip"]
+           "stream_kernels.hip", "width_kernels.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

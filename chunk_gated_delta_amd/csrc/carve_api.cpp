@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <mutex>
 
 #include <hip/hip_runtime.h>
@@ -243,17 +244,359 @@ void* scratch_address(carve_status* st) {
   return addr[dev];
 }
 
+// ------------------------------------------------------------ unequal key and value widths
+// The state is d_v x d_k with independent widths (CARVE notes, section 1).  A call with
+// Dk != Dv (each 64 or 128) runs the equal-width path at D = max(Dk, Dv) on padded copies
+// of its operands.  Padded key channels get k = q = 0, log g = 0 and b = 1 (retention 1):
+// the state columns they own stay zero and add nothing to S k or S q.  Padded value rows
+// get v = 0 and dO = 0: the state rows they own stay zero and change no other row.  Every
+// padded term is therefore an exact zero, and the outputs restricted to the true widths
+// are the result of the unequal-width recurrence.  The padded copies sit in front of the
+// workspace (for the training pair, the padded inputs sit in front of the saved buffer,
+// where the backward finds them again).
+bool width_ok(int d) { return d == 64 || d == 128; }
+bool unequal_widths(const carve_shape* s) {
+  return s && s->Dk != s->Dv && width_ok(s->Dk) && width_ok(s->Dv);
+}
+carve_shape widened(const carve_shape* s) {
+  carve_shape w = *s;
+  w.Dk = w.Dv = std::max(s->Dk, s->Dv);
+  return w;
+}
+
+enum class PadUse { Fwd, Bwd, Saved, BwdSaved };
+constexpr size_t kNone = ~size_t(0);
+
+// Byte offsets of the padded operands of one call (kNone: not used), each 256-byte aligned.
+struct PadLayout {
+  size_t q = kNone, k = kNone, v = kNone, lg = kNone, b = kNone;           // inputs
+  size_t S0 = kNone, S_T = kNone, o = kNone;                               // forward
+  size_t dO = kNone, dS_T = kNone, dq = kNone, dk = kNone, dv = kNone;     // backward
+  size_t dlg = kNone, db = kNone, dS0 = kNone;
+  size_t total = 0;
+};
+
+PadLayout pad_layout(const carve_shape* s, PadUse use) {
+  PadLayout L;
+  const size_t D = std::max(s->Dk, s->Dv), BH = (size_t)s->B * s->H, T = (size_t)s->T;
+  const size_t es = s->dtype == CARVE_BF16 ? 2 : 4;
+  const size_t tok = BH * T * D, st = BH * D * D * sizeof(float);
+  const bool kn = s->Dk < s->Dv;   // the key axis is the narrow one
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t at = off; off += (bytes + 255) & ~size_t(255); return at; };
+  // inputs of the forward first: for the training pair they persist in the saved buffer
+  if (use != PadUse::BwdSaved) {
+    if (kn) {
+      L.q = take(tok * es);
+      L.k = take(tok * es);
+      L.lg = take(tok * 4);
+      L.b = take(tok * 4);
+    } else {
+      L.v = take(tok * es);
+    }
+  }
+  if (use == PadUse::Fwd || use == PadUse::Saved) {
+    L.S0 = take(st);
+    L.S_T = take(st);
+    if (!kn) L.o = take(tok * es);
+  }
+  if (use == PadUse::Bwd) L.S0 = take(st);
+  if (use == PadUse::Bwd || use == PadUse::BwdSaved) {
+    L.dS_T = take(st);
+    L.dS0 = take(st);
+    if (kn) {
+      L.dq = take(tok * es);
+      L.dk = take(tok * es);
+      L.dlg = take(tok * 4);
+      L.db = take(tok * 4);
+    } else {
+      L.dO = take(tok * es);
+      L.dv = take(tok * es);
+    }
+  }
+  L.total = off;
+  return L;
+}
+
+// Moves operands between the caller's widths and the padded width D.
+struct Widen {
+  const carve_shape* s;
+  size_t D, BH, T, es;
+  bool kn;
+  char* base;
+  hipStream_t st;
+  hipError_t e = hipSuccess;
+  Widen(const carve_shape* s_, char* base_, hipStream_t st_)
+      : s(s_), D(std::max(s_->Dk, s_->Dv)), BH((size_t)s_->B * s_->H), T((size_t)s_->T),
+        es(s_->dtype == CARVE_BF16 ? 2 : 4), kn(s_->Dk < s_->Dv), base(base_), st(st_) {}
+  void* at(size_t off) const { return off == kNone ? nullptr : base + off; }
+  // [BH*T][narrow] <-> [BH*T][D] of the narrow axis (elements of `eb` bytes)
+  void* pad_tok(size_t off, const void* src, size_t eb, unsigned fill) {
+    if (!src || off == kNone) return nullptr;
+    const size_t nw = kn ? s->Dk : s->Dv;
+    if (e == hipSuccess) e = carve::launch_resize_rows(at(off), src, BH * T, nw, D, (int)eb, fill, st);
+    return at(off);
+  }
+  void unpad_tok(void* dst, size_t off, size_t eb) {
+    if (!dst || off == kNone) return;
+    const size_t nw = kn ? s->Dk : s->Dv;
+    if (e == hipSuccess) e = carve::launch_resize_rows(dst, at(off), BH * T, D, nw, (int)eb, 0u, st);
+  }
+  // state [BH][Dv][Dk] <-> [BH][D][D]: padded key columns, or padded value rows
+  float* pad_state(size_t off, const float* src) {
+    if (!src || off == kNone) return nullptr;
+    if (e == hipSuccess)
+      e = kn ? carve::launch_resize_rows(at(off), src, BH * D, s->Dk, D, 4, 0u, st)
+             : carve::launch_resize_rows(at(off), src, BH, (size_t)s->Dv * D, D * D, 4, 0u, st);
+    return static_cast<float*>(at(off));
+  }
+  void unpad_state(float* dst, size_t off) {
+    if (!dst || off == kNone) return;
+    if (e == hipSuccess)
+      e = kn ? carve::launch_resize_rows(dst, at(off), BH * D, D, s->Dk, 4, 0u, st)
+             : carve::launch_resize_rows(dst, at(off), BH, D * D, (size_t)s->Dv * D, 4, 0u, st);
+  }
+};
+constexpr unsigned kOneBits = 0x3f800000u;   // 1.0f
+
+bool all_aligned(std::initializer_list<const void*> ptrs) {
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return false;
+  return true;
+}
+size_t unequal_need(const Plan& p, const PadLayout& L, size_t inner) { return p.empty ? 0 : L.total + inner + 512; }
+
+carve_status fwd_unequal(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                         const float* b, const float* w, const float* S0, const carve_content* content, void* o,
+                         float* S_T, void* workspace, size_t workspace_bytes, void* stream,
+                         const carve_profile* prof) {
+  if (content) return CARVE_ERR_UNSUPPORTED;
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  if (!p.empty && (!q || !k || !v || !log_g || !w || !o)) return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, log_g, b, w, S0, o, S_T})) return CARVE_ERR_INVALID_ARG;
+  const PadLayout L = pad_layout(s, PadUse::Fwd);
+  const size_t need = unequal_need(p, L, fwd_ws(&ws, p, nullptr));
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = S_T ? carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  Widen W(s, align_up(workspace), hs);
+  const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
+  const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
+  const float* lgp = W.kn ? static_cast<const float*>(W.pad_tok(L.lg, log_g, 4, 0u)) : log_g;
+  const float* bp = W.kn ? static_cast<const float*>(W.pad_tok(L.b, b, 4, kOneBits)) : b;
+  const void* vp = W.kn ? v : W.pad_tok(L.v, v, W.es, 0u);
+  const float* S0p = W.pad_state(L.S0, S0);
+  void* op = W.kn ? o : W.at(L.o);
+  float* STp = S_T ? static_cast<float*>(W.at(L.S_T)) : nullptr;
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  st = carve_fwd_ex(&ws, qp, kp, vp, lgp, bp, w, S0p, nullptr, op, STp, inner,
+                    workspace_bytes - (size_t)(inner - static_cast<char*>(workspace)), stream, prof);
+  if (st != CARVE_OK) return st;
+  if (!W.kn) W.unpad_tok(o, L.o, W.es);
+  W.unpad_state(S_T, L.S_T);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+// outputs of a backward at the padded width: the narrow axis's gradients go to padded
+// buffers and come back cut to the caller's width
+struct BwdOut {
+  void *dq, *dk, *dv;
+  float *dlog_g, *db, *dS0;
+};
+BwdOut bwd_outputs(Widen& W, const PadLayout& L, void* dq, void* dk, void* dv, float* dlog_g, float* db,
+                   float* dS0) {
+  BwdOut r{dq, dk, dv, dlog_g, db, dS0 ? static_cast<float*>(W.at(L.dS0)) : nullptr};
+  if (W.kn) {
+    r.dq = W.at(L.dq);
+    r.dk = W.at(L.dk);
+    r.dlog_g = static_cast<float*>(W.at(L.dlg));
+    r.db = db ? static_cast<float*>(W.at(L.db)) : nullptr;
+  } else {
+    r.dv = W.at(L.dv);
+  }
+  return r;
+}
+void bwd_unpad(Widen& W, const PadLayout& L, void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dS0) {
+  if (W.kn) {
+    W.unpad_tok(dq, L.dq, W.es);
+    W.unpad_tok(dk, L.dk, W.es);
+    W.unpad_tok(dlog_g, L.dlg, 4);
+    W.unpad_tok(db, L.db, 4);
+  } else {
+    W.unpad_tok(dv, L.dv, W.es);
+  }
+  W.unpad_state(dS0, L.dS0);
+}
+
+carve_status bwd_unequal(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
+                         const float* b, const float* w, const float* S0, const void* dO, const float* dS_T,
+                         void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
+                         void* workspace, size_t workspace_bytes, void* stream, const carve_profile* prof) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  if ((b == nullptr) != (db == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!q || !k || !v || !log_g || !w || !dO || !dq || !dk || !dv || !dlog_g || !dw))
+    return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, log_g, b, w, S0, dO, dS_T, dq, dk, dv, dlog_g, db, dw, dS0}))
+    return CARVE_ERR_INVALID_ARG;
+  const PadLayout L = pad_layout(s, PadUse::Bwd);
+  const size_t need = unequal_need(p, L, bwd_ws(&ws, p));
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = dS0 ? carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  Widen W(s, align_up(workspace), hs);
+  const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
+  const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
+  const float* lgp = W.kn ? static_cast<const float*>(W.pad_tok(L.lg, log_g, 4, 0u)) : log_g;
+  const float* bp = W.kn ? static_cast<const float*>(W.pad_tok(L.b, b, 4, kOneBits)) : b;
+  const void* vp = W.kn ? v : W.pad_tok(L.v, v, W.es, 0u);
+  const void* dOp = W.kn ? dO : W.pad_tok(L.dO, dO, W.es, 0u);
+  const float* S0p = W.pad_state(L.S0, S0);
+  const float* dSTp = W.pad_state(L.dS_T, dS_T);
+  const BwdOut r = bwd_outputs(W, L, dq, dk, dv, dlog_g, db, dS0);
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  st = carve_bwd_ex(&ws, qp, kp, vp, lgp, bp, w, S0p, dOp, dSTp, r.dq, r.dk, r.dv, r.dlog_g, r.db, dw, r.dS0,
+                    inner, workspace_bytes - (size_t)(inner - static_cast<char*>(workspace)), stream, prof);
+  if (st != CARVE_OK) return st;
+  bwd_unpad(W, L, dq, dk, dv, dlog_g, db, dS0);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+size_t saved_unequal_bytes(const carve_shape* s) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  if (check_shape(&ws, &p) != CARVE_OK) return 0;
+  return unequal_need(p, pad_layout(s, PadUse::Saved), saved_bytes(&ws, p));
+}
+size_t bwd_saved_unequal_ws(const carve_shape* s) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  if (check_shape(&ws, &p) != CARVE_OK) return 0;
+  return unequal_need(p, pad_layout(s, PadUse::BwdSaved), bwd_saved_ws(&ws, p));
+}
+
+carve_status fwd_save_unequal(const carve_shape* s, const void* q, const void* k, const void* v,
+                              const float* log_g, const float* b, const float* w, const float* S0, void* o,
+                              float* S_T, void* saved, size_t saved_bytes_given, void* stream,
+                              const carve_profile* prof) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  if (!p.empty && (!q || !k || !v || !log_g || !w || !o)) return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, log_g, b, w, S0, o, S_T, saved})) return CARVE_ERR_INVALID_ARG;
+  const PadLayout L = pad_layout(s, PadUse::Saved);
+  const size_t need = unequal_need(p, L, saved_bytes(&ws, p));
+  if (saved_bytes_given < need || (need > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = S_T ? carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  // the padded inputs stay in the saved buffer for carve_bwd_saved
+  Widen W(s, align_up(saved), hs);
+  const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
+  const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
+  const float* lgp = W.kn ? static_cast<const float*>(W.pad_tok(L.lg, log_g, 4, 0u)) : log_g;
+  const float* bp = W.kn ? static_cast<const float*>(W.pad_tok(L.b, b, 4, kOneBits)) : b;
+  const void* vp = W.kn ? v : W.pad_tok(L.v, v, W.es, 0u);
+  const float* S0p = W.pad_state(L.S0, S0);
+  void* op = W.kn ? o : W.at(L.o);
+  float* STp = S_T ? static_cast<float*>(W.at(L.S_T)) : nullptr;
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  st = carve_fwd_save(&ws, qp, kp, vp, lgp, bp, w, S0p, op, STp, inner,
+                      saved_bytes_given - (size_t)(inner - static_cast<char*>(saved)), stream, prof);
+  if (st != CARVE_OK) return st;
+  if (!W.kn) W.unpad_tok(o, L.o, W.es);
+  W.unpad_state(S_T, L.S_T);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+carve_status bwd_saved_unequal(const carve_shape* s, const void* q, const void* k, const void* v,
+                               const float* log_g, const float* b, const float* w, const void* dO,
+                               const float* dS_T, const void* saved, size_t saved_bytes_given, void* dq, void* dk,
+                               void* dv, float* dlog_g, float* db, float* dw, float* dS0, void* workspace,
+                               size_t workspace_bytes, void* stream, const carve_profile* prof) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  if ((b == nullptr) != (db == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!q || !k || !v || !log_g || !w || !dO || !dq || !dk || !dv || !dlog_g || !dw))
+    return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, log_g, b, w, dO, dS_T, saved, dq, dk, dv, dlog_g, db, dw, dS0}))
+    return CARVE_ERR_INVALID_ARG;
+  const PadLayout Ls = pad_layout(s, PadUse::Saved);
+  const size_t need_saved = unequal_need(p, Ls, saved_bytes(&ws, p));
+  if (saved_bytes_given < need_saved || (need_saved > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  const PadLayout L = pad_layout(s, PadUse::BwdSaved);
+  const size_t need = unequal_need(p, L, bwd_saved_ws(&ws, p));
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = dS0 ? carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  // the forward's padded inputs, from the saved buffer (same layout as carve_fwd_save wrote)
+  Widen Ws(s, align_up(const_cast<void*>(saved)), hs);
+  const void* qp = Ws.kn ? Ws.at(Ls.q) : q;
+  const void* kp = Ws.kn ? Ws.at(Ls.k) : k;
+  const float* lgp = Ws.kn ? static_cast<const float*>(Ws.at(Ls.lg)) : log_g;
+  const float* bp = Ws.kn ? (b ? static_cast<const float*>(Ws.at(Ls.b)) : nullptr) : b;
+  const void* vp = Ws.kn ? v : Ws.at(Ls.v);
+  char* inner_saved = align_up(Ws.base + Ls.total);
+  Widen W(s, align_up(workspace), hs);
+  const void* dOp = W.kn ? dO : W.pad_tok(L.dO, dO, W.es, 0u);
+  const float* dSTp = W.pad_state(L.dS_T, dS_T);
+  const BwdOut r = bwd_outputs(W, L, dq, dk, dv, dlog_g, db, dS0);
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  st = carve_bwd_saved(&ws, qp, kp, vp, lgp, bp, w, dOp, dSTp, inner_saved,
+                       saved_bytes_given - (size_t)(inner_saved - static_cast<const char*>(saved)), r.dq, r.dk, r.dv,
+                       r.dlog_g, r.db, dw, r.dS0, inner,
+                       workspace_bytes - (size_t)(inner - static_cast<char*>(workspace)), stream, prof);
+  if (st != CARVE_OK) return st;
+  bwd_unpad(W, L, dq, dk, dv, dlog_g, db, dS0);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t carve_fwd_workspace_size(const carve_shape* s, const carve_content* content) {
+  if (unequal_widths(s)) {
+    const carve_shape ws = widened(s);
+    Plan p;
+    if (content || check_shape(&ws, &p) != CARVE_OK) return 0;
+    return unequal_need(p, pad_layout(s, PadUse::Fwd), fwd_ws(&ws, p, nullptr));
+  }
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
   return fwd_ws(s, p, content);
 }
 
 size_t carve_bwd_workspace_size(const carve_shape* s) {
+  if (unequal_widths(s)) {
+    const carve_shape ws = widened(s);
+    Plan p;
+    if (check_shape(&ws, &p) != CARVE_OK) return 0;
+    return unequal_need(p, pad_layout(s, PadUse::Bwd), bwd_ws(&ws, p));
+  }
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
   return bwd_ws(s, p);
@@ -269,6 +612,8 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
                           const float* b, const float* w, const float* S0, const carve_content* content, void* o,
                           float* S_T, void* workspace, size_t workspace_bytes, void* stream,
                           const carve_profile* prof) {
+  if (unequal_widths(s))
+    return fwd_unequal(s, q, k, v, log_g, b, w, S0, content, o, S_T, workspace, workspace_bytes, stream, prof);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -324,8 +669,21 @@ carve_status carve_fwd_ex(const carve_shape* s, const void* q, const void* k, co
 carve_status carve_fwd_noalloc(const carve_shape* s, const void* q, const void* k, const void* v,
                                const float* log_g, const float* b, const float* w, const float* S0,
                                const carve_content* content, void* o, float* S_T, void* stream) {
+  carve_status st;
+  if (unequal_widths(s)) {
+    if (content) return CARVE_ERR_UNSUPPORTED;
+    const carve_shape wide = widened(s);
+    Plan p;
+    st = check_shape(&wide, &p);
+    if (st != CARVE_OK) return st;
+    if (carve_fwd_workspace_size(s, nullptr) > CARVE_NOALLOC_SCRATCH_BYTES) return CARVE_ERR_WORKSPACE;
+    void* ws = scratch_address(&st);
+    if (st != CARVE_OK) return st;
+    return carve_fwd_ex(s, q, k, v, log_g, b, w, S0, nullptr, o, S_T, ws, CARVE_NOALLOC_SCRATCH_BYTES, stream,
+                        nullptr);
+  }
   Plan p;
-  carve_status st = check_shape(s, &p);
+  st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
   st = check_content(s, p, content, b);
   if (st != CARVE_OK) return st;
@@ -348,6 +706,9 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
                           const float* b, const float* w, const float* S0, const void* dO, const float* dS_T,
                           void* dq, void* dk, void* dv, float* dlog_g, float* db, float* dw, float* dS0,
                           void* workspace, size_t workspace_bytes, void* stream, const carve_profile* prof) {
+  if (unequal_widths(s))
+    return bwd_unequal(s, q, k, v, log_g, b, w, S0, dO, dS_T, dq, dk, dv, dlog_g, db, dw, dS0, workspace,
+                       workspace_bytes, stream, prof);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -407,12 +768,14 @@ carve_status carve_bwd_ex(const carve_shape* s, const void* q, const void* k, co
 }
 
 size_t carve_saved_size(const carve_shape* s) {
+  if (unequal_widths(s)) return saved_unequal_bytes(s);
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
   return saved_bytes(s, p);
 }
 
 size_t carve_bwd_saved_workspace_size(const carve_shape* s) {
+  if (unequal_widths(s)) return bwd_saved_unequal_ws(s);
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
   return bwd_saved_ws(s, p);
@@ -421,6 +784,8 @@ size_t carve_bwd_saved_workspace_size(const carve_shape* s) {
 carve_status carve_fwd_save(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
                             const float* b, const float* w, const float* S0, void* o, float* S_T, void* saved,
                             size_t saved_bytes_given, void* stream, const carve_profile* prof) {
+  if (unequal_widths(s))
+    return fwd_save_unequal(s, q, k, v, log_g, b, w, S0, o, S_T, saved, saved_bytes_given, stream, prof);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -455,6 +820,9 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
                              const float* dS_T, const void* saved, size_t saved_bytes_given, void* dq, void* dk,
                              void* dv, float* dlog_g, float* db, float* dw, float* dS0, void* workspace,
                              size_t workspace_bytes, void* stream, const carve_profile* prof) {
+  if (unequal_widths(s))
+    return bwd_saved_unequal(s, q, k, v, log_g, b, w, dO, dS_T, saved, saved_bytes_given, dq, dk, dv, dlog_g, db,
+                             dw, dS0, workspace, workspace_bytes, stream, prof);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -920,8 +1288,10 @@ carve_status carve_decode_step(const carve_shape* s, const void* q, const void* 
                                const float* log_g, const float* b, const float* w, float* S,
                                const carve_decode_content* content, void* o, void* stream) {
   if (!s || s->T != 1) return CARVE_ERR_INVALID_ARG;
+  // the decode kernel takes the key and value widths separately
+  const carve_shape sc = unequal_widths(s) ? widened(s) : *s;
   Plan p;
-  carve_status st = check_shape(s, &p);
+  carve_status st = check_shape(&sc, &p);
   if (st != CARVE_OK) return st;
   if (p.BH == 0) return CARVE_OK;
   if (!q || !k || !v || !log_g || !w || !S || !o) return CARVE_ERR_INVALID_ARG;

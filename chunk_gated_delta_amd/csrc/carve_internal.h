@@ -202,5 +202,9 @@ hipError_t launch_sum_over_batch(const float* part, float* out, int B, int H, in
 hipError_t launch_logit_grads(const LogitGradArgs& a, float* dA, float* dtau, hipStream_t st);
 // n16 16-byte vectors; cus = compute units of the current device (sizes the grid)
 hipError_t launch_stream_copy(void* dst, const void* src, size_t n16, int cus, hipStream_t st);
+// dst[r][c] = c < w_in ? src[r][c] : fill for r < rows, c < w_out; elements of 2 or 4
+// bytes, fill given as the element's bit pattern (unequal key and value widths)
+hipError_t launch_resize_rows(void* dst, const void* src, size_t rows, size_t w_in, size_t w_out, int elem_bytes,
+                              unsigned fill_bits, hipStream_t st);
 
 }  // namespace carve

@@ -44,12 +44,23 @@
  *     CARVE_ERR_HIP, which reports a launch error (hipGetLastError) after the
  *     launches were issued.  Device faults surface at the caller's next
  *     synchronisation.  NaN/Inf inputs propagate unchecked.
- *   - Supported: Dk == Dv in {64, 128}; any T >= 0 (a final partial chunk is
+ *   - Supported: Dk, Dv in {64, 128}; any T >= 0 (a final partial chunk is
  *     handled); B, H >= 0 (an empty batch, head or token axis is a no-op that
  *     still writes S_T = S0 and m_out = m0).  Chunk length L: any L >= 1 for
  *     token-only gates (the result does not depend on L; the kernels tile
  *     tokens in blocks of 32 when L <= 32 or dtype is float32, and of 64
  *     otherwise); for the content path L must be a multiple of that tile.
+ *   - Unequal widths (Dk != Dv; the pages write the state as Dv x Dk with
+ *     independent widths, notes section 1): carve_fwd, carve_fwd_ex,
+ *     carve_fwd_noalloc (token-only gates), carve_bwd, carve_bwd_ex, the training
+ *     pair and carve_decode_step accept them.  Except for the decode step, which
+ *     takes both widths directly, such a call runs at D = max(Dk, Dv) on padded
+ *     copies of its operands held in front of its workspace (for the training pair,
+ *     the padded inputs in front of the saved buffer, where carve_bwd_saved reads
+ *     them).  Padded key channels carry k = q = 0 and retention 1, padded value
+ *     rows v = 0, so every padded term is an exact zero; the size functions count
+ *     the copies.  The content-aware forward and backward and the gate
+ *     pre-activation calls return CARVE_ERR_UNSUPPORTED for Dk != Dv.
  *   - Numerical range: any retention a = exp(log g) * b in [0, 1] is handled
  *     (the pages put no floor on the decay, notes section 2.3, and take the
  *     erase as a factor in (0, 1], section 2.1).  The kernels carry the
@@ -88,7 +99,7 @@ typedef enum { CARVE_F32 = 0, CARVE_BF16 = 1 } carve_dtype;   /* dtype of q, k, 
 
 typedef struct {
   int B, H, T;     /* batch, heads, tokens                         */
-  int Dk, Dv;      /* key and value widths (equal, 64 or 128)      */
+  int Dk, Dv;      /* key and value widths, each 64 or 128         */
   int L;           /* chunk length                                  */
   carve_dtype dtype;
 } carve_shape;

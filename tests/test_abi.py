@@ -53,7 +53,8 @@ def call_fwd(lib, s, q=FAKE, k=FAKE, v=FAKE, log_g=FAKE, b=None, w=FAKE, S0=None
 
 def test_fwd_rejects_bad_shapes(lib):
     assert call_fwd(lib, shape(D=96)) == UNSUPPORTED
-    assert call_fwd(lib, shape(D=128, Dv=64)) == UNSUPPORTED
+    assert call_fwd(lib, shape(D=128, Dv=96)) == UNSUPPORTED
+    assert call_fwd(lib, shape(D=64, Dv=32)) == UNSUPPORTED
     assert call_fwd(lib, shape(B=-1)) == INVALID
     assert call_fwd(lib, shape(T=-5)) == INVALID
     assert call_fwd(lib, shape(L=0)) == INVALID
@@ -243,8 +244,16 @@ def test_noalloc_rejects_beyond_scratch_on_host(lib):
     assert lib.carve_fwd_noalloc(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None,
                                  None) == WORKSPACE
     # argument errors come first, as for carve_fwd
-    assert lib.carve_fwd_noalloc(ctypes.byref(shape(Dv=64)), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+    assert lib.carve_fwd_noalloc(ctypes.byref(shape(Dv=96)), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
                                  FAKE, None, None) == UNSUPPORTED
+    # unequal widths: the padded operands count against the scratch too
+    su = shape(B=2, H=16, T=1024, D=64, Dv=128)
+    assert lib.carve_fwd_workspace_size(ctypes.byref(su), None) > (64 << 20)
+    assert lib.carve_fwd_noalloc(ctypes.byref(su), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None,
+                                 None) == WORKSPACE
+    c = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
+    assert lib.carve_fwd_noalloc(ctypes.byref(shape(D=64, Dv=128)), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                                 ctypes.byref(c), FAKE, None, None) == UNSUPPORTED
 
 
 def test_stream_copy_rejects_bad_arguments_on_host(lib):
@@ -270,3 +279,30 @@ def test_size_limits_on_host(lib):
     ws = lib.carve_fwd_workspace_size(ctypes.byref(s), None)
     assert 0 < ws < (1 << 40)
     assert 0 < lib.carve_saved_size(ctypes.byref(s)) < (1 << 40)
+
+
+def test_unequal_widths_on_host(lib):
+    """Key and value widths 64 and 128 in either order run at the wider width on padded
+    copies held in front of the workspace (or the saved buffer): every size grows by the
+    padded operands, the checks are those of the equal-width calls, and the paths with no
+    padded variant (content-aware, gate pre-activations) are rejected before any launch."""
+    for dk, dv in ((64, 128), (128, 64)):
+        s, wide = shape(D=dk, Dv=dv), shape(D=128)
+        for fn in ("carve_bwd_workspace_size", "carve_saved_size", "carve_bwd_saved_workspace_size"):
+            assert getattr(lib, fn)(ctypes.byref(s)) > getattr(lib, fn)(ctypes.byref(wide)), fn
+        need = lib.carve_fwd_workspace_size(ctypes.byref(s), None)
+        assert need > lib.carve_fwd_workspace_size(ctypes.byref(wide), None)
+        assert call_fwd(lib, s, ws_bytes=need - 1) == WORKSPACE
+        assert call_fwd(lib, s, o=None) == INVALID
+        assert call_fwd(lib, s, k=FAKE + 4) == INVALID
+        assert call_bwd(lib, s, b=FAKE, db=None) == INVALID
+        assert call_bwd(lib, s, ws_bytes=lib.carve_bwd_workspace_size(ctypes.byref(s)) - 1) == WORKSPACE
+        c = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
+        assert lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(c)) == 0
+        assert call_fwd(lib, s, content=c) == UNSUPPORTED
+        assert lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(c)) == 0
+        assert lib.carve_bwd_logits_workspace_size(ctypes.byref(s)) == 0
+        # an empty problem needs no workspace and launches nothing
+        s0 = shape(T=0, D=dk, Dv=dv)
+        assert lib.carve_fwd_workspace_size(ctypes.byref(s0), None) == 0
+        assert call_fwd(lib, s0, q=None, k=None, v=None, log_g=None, w=None, o=None, ws=None, ws_bytes=0) == OK

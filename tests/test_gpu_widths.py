@@ -1,0 +1,143 @@
+"""Unequal key and value widths (needs an MI355X).  The state is d_v x d_k with independent
+widths; the library runs such calls at the wider width on padded copies (the decode step
+takes both widths directly).  Checked against the float64 oracle, which computes at the
+true widths: forward outputs and final state, every gradient of the recomputing backward
+and of the training pair (which must also match the recomputing backward bit for bit, as
+at equal widths), the no-allocation forward (bit for bit against carve_fwd), and the
+decode step, token-only and content-aware.  Ragged token counts, both orders of the
+widths, float32 and bfloat16."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunk_gated_delta_amd import carve
+from chunk_gated_delta_amd.synth import random_inputs
+from tests.helpers import max_rel, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+NAMES = ("dq", "dk", "dv", "dlog_g", "db", "dw", "dS0")
+
+
+def announce(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def f32(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).cuda()
+
+
+CASES = [
+    # dtype, B, H, T, Dk, Dv: several tiles and a ragged tail (bf16: 64-token tiles, f32: 32)
+    ("bf16", 2, 2, 64 * 3 + 17, 64, 128),
+    ("bf16", 1, 3, 64 * 2 + 40, 128, 64),
+    ("f32", 1, 2, 32 * 4 + 9, 64, 128),
+    ("f32", 2, 1, 32 * 3 + 21, 128, 64),
+]
+IDS = [f"{c[0]}_k{c[4]}_v{c[5]}_T{c[3]}" for c in CASES]
+
+
+def setup(dtype, B, H, T, Dk, Dv, seed):
+    inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=seed, erase="sigmoid", dists="softplus_decay",
+                        with_dO=True)
+    rng = np.random.default_rng(seed + 1)
+    S0 = np.asarray(rng.standard_normal((B, H, Dv, Dk)) * 0.3, np.float32).astype(np.float64)
+    dS_T = np.asarray(rng.standard_normal((B, H, Dv, Dk)) * 0.3, np.float32).astype(np.float64)
+    return inp, S0, dS_T
+
+
+@pytest.mark.parametrize("dtype,B,H,T,Dk,Dv", CASES, ids=IDS)
+def test_unequal_widths_forward_and_backward(dtype, B, H, T, Dk, Dv):
+    announce(f"unequal widths {dtype} B{B} H{H} T{T} Dk{Dk} Dv{Dv}")
+    inp, S0, dS_T = setup(dtype, B, H, T, Dk, Dv, seed=300 + Dk + T)
+    d = to_device(inp, dtype)
+    S0d, dSd = f32(S0), f32(dS_T)
+    o, S_T, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=S0d)
+    g = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=d["b"], S0=S0d, dS_T=dSd)
+    o2, S_T2, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=S0d)
+    g2 = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=d["b"], dS_T=dSd)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (B, H, T, Dv) and tuple(S_T.shape) == (B, H, Dv, Dk)
+    ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], b=inp["b"], S0=S0)
+    ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"], b=inp["b"], S0=S0,
+                          dS_T=dS_T)
+    errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS)}
+    errs.update({k_: max_rel(to_np(g[k_]), ref[k_]) for k_ in NAMES})
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
+    # the training pair runs the same arithmetic as the recomputing calls
+    assert torch.equal(o2, o) and torch.equal(S_T2, S_T)
+    for k_ in NAMES:
+        assert torch.equal(g2[k_], g[k_]), k_
+
+
+def test_unequal_widths_noalloc_and_empty():
+    announce("unequal widths: no-allocation forward, empty inputs")
+    dtype, B, H, T, Dk, Dv = "bf16", 2, 2, 100, 64, 128
+    inp, S0, _ = setup(dtype, B, H, T, Dk, Dv, seed=321)
+    d = to_device(inp, dtype)
+    S0d = f32(S0)
+    for _ in range(2):   # twice in a row: the scratch holds the previous call's contents
+        o, S_T, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=S0d)
+        on, S_Tn, _ = carve.fwd_noalloc(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=S0d)
+        torch.cuda.synchronize()
+        assert torch.equal(on, o) and torch.equal(S_Tn, S_T)
+    # T = 0: the final state is the initial one, the state gradient passes through
+    e = {k_: v_[:, :, :0].contiguous() for k_, v_ in d.items() if v_.dim() >= 3}
+    o0, S_T0, _ = carve.fwd(e["q"], e["k"], e["v"], e["log_g"], e["w"], b=e["b"], S0=S0d)
+    dS_T = torch.randn((B, H, Dv, Dk), device="cuda")
+    g0 = carve.bwd(e["q"], e["k"], e["v"], e["log_g"], e["w"], e["dO"], b=e["b"], S0=S0d, dS_T=dS_T)
+    torch.cuda.synchronize()
+    assert o0.numel() == 0 and torch.equal(S_T0, S0d) and torch.equal(g0["dS0"], dS_T)
+
+
+def decode_tokens(d, T, S, L, b=True, content=None):
+    outs = []
+    for t in range(T):
+        tok = {k_: d[k_][:, :, t].contiguous() for k_ in ("q", "k", "v", "log_g", "w") if k_ in d}
+        cont = None
+        if content is not None:
+            cont = dict(content, b_x=d["b_x"][:, :, t].contiguous())
+        o, m_out = carve.decode_step(tok["q"], tok["k"], tok["v"], tok["log_g"], tok["w"], S,
+                                     b=d["b"][:, :, t].contiguous() if b else None, L=L, content=cont)
+        outs.append(o)
+        if content is not None:
+            content["m_in"] = m_out
+            content["pos"] = (content["pos"] + 1) % L
+    torch.cuda.synchronize()
+    return torch.stack(outs, dim=2)
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("bf16", 64, 128), ("f32", 128, 64)])
+def test_unequal_widths_decode(dtype, Dk, Dv):
+    announce(f"unequal widths decode {dtype} Dk{Dk} Dv{Dv}")
+    B, H, T = 2, 2, 37
+    inp, S0, _ = setup(dtype, B, H, T, Dk, Dv, seed=340 + Dk)
+    d = to_device(inp, dtype)
+    S = f32(S0)
+    o = decode_tokens(d, T, S, L=64)
+    ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], b=inp["b"], S0=S0)
+    eo, es = max_rel(to_np(o), ro), max_rel(to_np(S), rS)
+    print(f"  err o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [("f32", 64, 128), ("bf16", 128, 64)])
+def test_unequal_widths_content_decode(dtype, Dk, Dv):
+    """Content-aware decode across chunk boundaries: U1 is [H, R, Dv], U2 [H, Dk, R]."""
+    announce(f"unequal widths content decode {dtype} Dk{Dk} Dv{Dv}")
+    B, H, T, L = 2, 2, 41, 16
+    inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=360 + Dk, erase="content", dists="softplus_decay")
+    inp["U1"] = inp["U1"] * 8.0
+    inp["U2"] = inp["U2"] * 8.0
+    d = to_device(inp, dtype)
+    S = torch.zeros((B, H, Dv, Dk), dtype=torch.float32, device="cuda")
+    carry = {"U1": d["U1"], "U2": d["U2"], "m_in": None,
+             "csum": torch.zeros((B, H, Dv), dtype=torch.float32, device="cuda"), "pos": 0}
+    o = decode_tokens(d, T, S, L=L, b=False, content=carry)
+    ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L,
+                               content={"b_x": inp["b_x"], "U1": inp["U1"], "U2": inp["U2"]})
+    eo, es = max_rel(to_np(o), ro), max_rel(to_np(S), rS)
+    print(f"  err o={eo:.2e} S={es:.2e}", flush=True)
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
