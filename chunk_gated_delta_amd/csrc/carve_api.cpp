@@ -264,7 +264,8 @@ carve_shape widened(const carve_shape* s) {
   return w;
 }
 
-enum class PadUse { Fwd, Bwd, Saved, BwdSaved };
+enum class PadUse { Fwd, FwdContent, Bwd, Saved, BwdSaved };
+constexpr int kMaxRank = 64;   // content projection rank bound (sizes do not depend on the rank given)
 constexpr size_t kNone = ~size_t(0);
 
 // Byte offsets of the padded operands of one call (kNone: not used), each 256-byte aligned.
@@ -273,6 +274,7 @@ struct PadLayout {
   size_t S0 = kNone, S_T = kNone, o = kNone;                               // forward
   size_t dO = kNone, dS_T = kNone, dq = kNone, dk = kNone, dv = kNone;     // backward
   size_t dlg = kNone, db = kNone, dS0 = kNone;
+  size_t bx = kNone, U1 = kNone, U2 = kNone, m0 = kNone, m_out = kNone, z_rec = kNone, m_rec = kNone;  // content
   size_t total = 0;
 };
 
@@ -295,10 +297,24 @@ PadLayout pad_layout(const carve_shape* s, PadUse use) {
       L.v = take(tok * es);
     }
   }
-  if (use == PadUse::Fwd || use == PadUse::Saved) {
+  if (use == PadUse::Fwd || use == PadUse::FwdContent || use == PadUse::Saved) {
     L.S0 = take(st);
     L.S_T = take(st);
     if (!kn) L.o = take(tok * es);
+  }
+  if (use == PadUse::FwdContent) {
+    // the content gate's operands on the narrow axis: b_x, U2 and z (key), or U1 and m (value)
+    const size_t per = ((size_t)s->T + s->L - 1) / s->L;   // content periods
+    if (kn) {
+      L.bx = take(tok * 4);
+      L.U2 = take((size_t)s->H * D * kMaxRank * 4);
+      L.z_rec = take(BH * per * D * 4);
+    } else {
+      L.U1 = take((size_t)s->H * kMaxRank * D * 4);
+      L.m0 = take(BH * D * 4);
+      L.m_out = take(BH * D * 4);
+      L.m_rec = take(BH * per * D * 4);
+    }
   }
   if (use == PadUse::Bwd) L.S0 = take(st);
   if (use == PadUse::Bwd || use == PadUse::BwdSaved) {
@@ -358,6 +374,9 @@ struct Widen {
   }
 };
 constexpr unsigned kOneBits = 0x3f800000u;   // 1.0f
+// erase pre-activation of a padded key channel: sigmoid(1e30 + z) = 1 and its
+// log-sigmoid is exactly 0 in float32, with no infinity in the arithmetic
+constexpr unsigned kBigBits = 0x7149f2cau;   // 1.0e30f
 
 bool all_aligned(std::initializer_list<const void*> ptrs) {
   for (const void* ptr : ptrs)
@@ -370,22 +389,49 @@ carve_status fwd_unequal(const carve_shape* s, const void* q, const void* k, con
                          const float* b, const float* w, const float* S0, const carve_content* content, void* o,
                          float* S_T, void* workspace, size_t workspace_bytes, void* stream,
                          const carve_profile* prof) {
-  if (content) return CARVE_ERR_UNSUPPORTED;
   const carve_shape ws = widened(s);
   Plan p;
   carve_status st = check_shape(&ws, &p);
   if (st != CARVE_OK) return st;
+  st = check_content(&ws, p, content, b);
+  if (st != CARVE_OK) return st;
   if (!p.empty && (!q || !k || !v || !log_g || !w || !o)) return CARVE_ERR_INVALID_ARG;
   if (!all_aligned({q, k, v, log_g, b, w, S0, o, S_T})) return CARVE_ERR_INVALID_ARG;
-  const PadLayout L = pad_layout(s, PadUse::Fwd);
-  const size_t need = unequal_need(p, L, fwd_ws(&ws, p, nullptr));
+  const PadLayout L = pad_layout(s, content ? PadUse::FwdContent : PadUse::Fwd);
+  const size_t need = unequal_need(p, L, fwd_ws(&ws, p, content));
   if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (p.empty) {
     hipError_t e = S_T ? carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    if (e == hipSuccess && content && content->m_out)
+      e = carve::launch_copy_or_zero(content->m_out, content->m0, (size_t)p.BH * s->Dv, hs);
     return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
   }
   Widen W(s, align_up(workspace), hs);
+  carve_content cp{};
+  if (content) {
+    // b_x, U2 and z on the key axis; U1, m0, m_out and the mean records on the value axis
+    const int R = content->U1 ? content->R : 0;
+    const size_t H = (size_t)s->H, per = ((size_t)s->T + s->L - 1) / s->L;
+    cp = *content;
+    if (W.kn) {
+      cp.b_x = static_cast<const float*>(W.pad_tok(L.bx, content->b_x, 4, kBigBits));
+      if (content->U2 && W.e == hipSuccess)
+        W.e = carve::launch_resize_rows(W.at(L.U2), content->U2, H, (size_t)s->Dk * R, W.D * R, 4, 0u, hs);
+      if (content->U2) cp.U2 = static_cast<const float*>(W.at(L.U2));
+      if (content->z_rec) cp.z_rec = static_cast<float*>(W.at(L.z_rec));
+    } else {
+      if (content->U1 && W.e == hipSuccess)
+        W.e = carve::launch_resize_rows(W.at(L.U1), content->U1, H * R, s->Dv, W.D, 4, 0u, hs);
+      if (content->U1) cp.U1 = static_cast<const float*>(W.at(L.U1));
+      if (content->m0 && W.e == hipSuccess)
+        W.e = carve::launch_resize_rows(W.at(L.m0), content->m0, W.BH, s->Dv, W.D, 4, 0u, hs);
+      if (content->m0) cp.m0 = static_cast<const float*>(W.at(L.m0));
+      if (content->m_out) cp.m_out = static_cast<float*>(W.at(L.m_out));
+      if (content->m_rec) cp.m_rec = static_cast<float*>(W.at(L.m_rec));
+    }
+    (void)per;
+  }
   const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
   const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
   const float* lgp = W.kn ? static_cast<const float*>(W.pad_tok(L.lg, log_g, 4, 0u)) : log_g;
@@ -396,11 +442,20 @@ carve_status fwd_unequal(const carve_shape* s, const void* q, const void* k, con
   float* STp = S_T ? static_cast<float*>(W.at(L.S_T)) : nullptr;
   if (W.e != hipSuccess) return CARVE_ERR_HIP;
   char* inner = align_up(W.base + L.total);
-  st = carve_fwd_ex(&ws, qp, kp, vp, lgp, bp, w, S0p, nullptr, op, STp, inner,
+  st = carve_fwd_ex(&ws, qp, kp, vp, lgp, bp, w, S0p, content ? &cp : nullptr, op, STp, inner,
                     workspace_bytes - (size_t)(inner - static_cast<char*>(workspace)), stream, prof);
   if (st != CARVE_OK) return st;
   if (!W.kn) W.unpad_tok(o, L.o, W.es);
   W.unpad_state(S_T, L.S_T);
+  if (content && W.e == hipSuccess) {
+    const size_t per = ((size_t)s->T + s->L - 1) / s->L;
+    if (W.kn && content->z_rec)
+      W.e = carve::launch_resize_rows(content->z_rec, W.at(L.z_rec), W.BH * per, W.D, s->Dk, 4, 0u, hs);
+    if (!W.kn && content->m_out && W.e == hipSuccess)
+      W.e = carve::launch_resize_rows(content->m_out, W.at(L.m_out), W.BH, W.D, s->Dv, 4, 0u, hs);
+    if (!W.kn && content->m_rec && W.e == hipSuccess)
+      W.e = carve::launch_resize_rows(content->m_rec, W.at(L.m_rec), W.BH * per, W.D, s->Dv, 4, 0u, hs);
+  }
   return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 
@@ -582,8 +637,8 @@ size_t carve_fwd_workspace_size(const carve_shape* s, const carve_content* conte
   if (unequal_widths(s)) {
     const carve_shape ws = widened(s);
     Plan p;
-    if (content || check_shape(&ws, &p) != CARVE_OK) return 0;
-    return unequal_need(p, pad_layout(s, PadUse::Fwd), fwd_ws(&ws, p, nullptr));
+    if (check_shape(&ws, &p) != CARVE_OK) return 0;
+    return unequal_need(p, pad_layout(s, content ? PadUse::FwdContent : PadUse::Fwd), fwd_ws(&ws, p, content));
   }
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
@@ -671,15 +726,16 @@ carve_status carve_fwd_noalloc(const carve_shape* s, const void* q, const void* 
                                const carve_content* content, void* o, float* S_T, void* stream) {
   carve_status st;
   if (unequal_widths(s)) {
-    if (content) return CARVE_ERR_UNSUPPORTED;
     const carve_shape wide = widened(s);
     Plan p;
     st = check_shape(&wide, &p);
     if (st != CARVE_OK) return st;
-    if (carve_fwd_workspace_size(s, nullptr) > CARVE_NOALLOC_SCRATCH_BYTES) return CARVE_ERR_WORKSPACE;
+    st = check_content(&wide, p, content, b);
+    if (st != CARVE_OK) return st;
+    if (carve_fwd_workspace_size(s, content) > CARVE_NOALLOC_SCRATCH_BYTES) return CARVE_ERR_WORKSPACE;
     void* ws = scratch_address(&st);
     if (st != CARVE_OK) return st;
-    return carve_fwd_ex(s, q, k, v, log_g, b, w, S0, nullptr, o, S_T, ws, CARVE_NOALLOC_SCRATCH_BYTES, stream,
+    return carve_fwd_ex(s, q, k, v, log_g, b, w, S0, content, o, S_T, ws, CARVE_NOALLOC_SCRATCH_BYTES, stream,
                         nullptr);
   }
   Plan p;

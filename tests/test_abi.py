@@ -252,8 +252,8 @@ def test_noalloc_rejects_beyond_scratch_on_host(lib):
     assert lib.carve_fwd_noalloc(ctypes.byref(su), FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None,
                                  None) == WORKSPACE
     c = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
-    assert lib.carve_fwd_noalloc(ctypes.byref(shape(D=64, Dv=128)), FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
-                                 ctypes.byref(c), FAKE, None, None) == UNSUPPORTED
+    assert lib.carve_fwd_noalloc(ctypes.byref(shape(D=64, Dv=128)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                 ctypes.byref(c), FAKE, None, None) == INVALID     # b together with content
 
 
 def test_stream_copy_rejects_bad_arguments_on_host(lib):
@@ -285,7 +285,8 @@ def test_unequal_widths_on_host(lib):
     """Key and value widths 64 and 128 in either order run at the wider width on padded
     copies held in front of the workspace (or the saved buffer): every size grows by the
     padded operands, the checks are those of the equal-width calls, and the paths with no
-    padded variant (content-aware, gate pre-activations) are rejected before any launch."""
+    padded variant (content-aware backward, gate pre-activations) are rejected before any
+    launch."""
     for dk, dv in ((64, 128), (128, 64)):
         s, wide = shape(D=dk, Dv=dv), shape(D=128)
         for fn in ("carve_bwd_workspace_size", "carve_saved_size", "carve_bwd_saved_workspace_size"):
@@ -298,8 +299,11 @@ def test_unequal_widths_on_host(lib):
         assert call_bwd(lib, s, b=FAKE, db=None) == INVALID
         assert call_bwd(lib, s, ws_bytes=lib.carve_bwd_workspace_size(ctypes.byref(s)) - 1) == WORKSPACE
         c = carve.carve_content(FAKE, FAKE, FAKE, 16, None, None)
-        assert lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(c)) == 0
-        assert call_fwd(lib, s, content=c) == UNSUPPORTED
+        cw = lib.carve_fwd_workspace_size(ctypes.byref(wide), ctypes.byref(c))
+        assert lib.carve_fwd_workspace_size(ctypes.byref(s), ctypes.byref(c)) > cw    # content operands padded too
+        assert call_fwd(lib, s, content=c, ws_bytes=cw) == WORKSPACE
+        assert call_fwd(lib, s, b=FAKE, content=c) == INVALID                         # b together with content
+        assert call_fwd(lib, shape(D=dk, Dv=dv, L=16), content=c) == UNSUPPORTED      # period not whole tiles
         assert lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(c)) == 0
         assert lib.carve_bwd_logits_workspace_size(ctypes.byref(s)) == 0
         # an empty problem needs no workspace and launches nothing

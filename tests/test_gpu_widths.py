@@ -3,8 +3,9 @@ widths; the library runs such calls at the wider width on padded copies (the dec
 takes both widths directly).  Checked against the float64 oracle, which computes at the
 true widths: forward outputs and final state, every gradient of the recomputing backward
 and of the training pair (which must also match the recomputing backward bit for bit, as
-at equal widths), the no-allocation forward (bit for bit against carve_fwd), and the
-decode step, token-only and content-aware.  Ragged token counts, both orders of the
+at equal widths), the content-aware forward with its per-period records, the
+no-allocation forward (bit for bit against carve_fwd), and the decode step, token-only
+and content-aware.  Ragged token counts, both orders of the
 widths, float32 and bfloat16."""
 import numpy as np
 import pytest
@@ -141,3 +142,40 @@ def test_unequal_widths_content_decode(dtype, Dk, Dv):
     eo, es = max_rel(to_np(o), ro), max_rel(to_np(S), rS)
     print(f"  err o={eo:.2e} S={es:.2e}", flush=True)
     assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,T,L", [("bf16", 64, 128, 64 * 3 + 30, 64), ("f32", 128, 64, 32 * 5 + 7, 32)])
+def test_unequal_widths_content_forward(dtype, Dk, Dv, T, L):
+    """Content-aware erase at unequal widths: U1 [H, R, Dv] reads the mean output, U2 [H, Dk, R]
+    feeds the key-axis gate.  Outputs, final state, the last chunk's mean, and the per-period
+    records z [B, H, P, Dk] and m [B, H, P, Dv]; the no-allocation forward gives the same bits."""
+    announce(f"unequal widths content forward {dtype} Dk{Dk} Dv{Dv} T{T} L{L}")
+    B, H = 2, 2
+    inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=380 + Dk, erase="content", dists="softplus_decay")
+    inp["U1"] = inp["U1"] * 8.0
+    inp["U2"] = inp["U2"] * 8.0
+    d = to_device(inp, dtype)
+    m0 = np.asarray(np.random.default_rng(381).standard_normal((B, H, Dv)) * 0.5, np.float32)
+    cont = {"b_x": d["b_x"], "U1": d["U1"], "U2": d["U2"], "m0": f32(m0)}
+    zr, mr = carve.content_records(B, H, T, Dk, Dv, L, torch.device("cuda"))
+    o, S_T, m_out = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], L=L, content=dict(cont, z_rec=zr, m_rec=mr))
+    on, S_Tn, m_outn = carve.fwd_noalloc(d["q"], d["k"], d["v"], d["log_g"], d["w"], L=L, content=cont)
+    torch.cuda.synchronize()
+    assert torch.equal(on, o) and torch.equal(S_Tn, S_T) and torch.equal(m_outn, m_out)
+    ro, rS, rm = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L,
+                                content={"b_x": inp["b_x"], "U1": inp["U1"], "U2": inp["U2"],
+                                         "m0": m0.astype(np.float64)})
+    errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS), "m_out": max_rel(to_np(m_out), rm)}
+    # records: period p's z is U2 U1 m_{p-1}, with m_{p-1} the previous period's mean (m0 first)
+    P = zr.shape[2]
+    ref_m = np.concatenate([m0.astype(np.float64)[:, :, None],
+                            np.stack([ro[:, :, L * j:min(L * (j + 1), T)].mean(axis=2) for j in range(P - 1)], 2)
+                            if P > 1 else np.zeros((B, H, 0, Dv))], axis=2)
+    ref_z = np.einsum("hkr,hrv,bhpv->bhpk", inp["U2"], inp["U1"], ref_m)
+    errs["m_rec"] = max_rel(to_np(mr), ref_m)
+    errs["z_rec"] = max_rel(to_np(zr), ref_z)
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
+    ro0, _, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L,
+                               content={"b_x": inp["b_x"], "U1": None, "U2": None})
+    assert max_rel(ro0, ro) > 0.02       # the content signal matters at this scale
