@@ -264,7 +264,7 @@ carve_shape widened(const carve_shape* s) {
   return w;
 }
 
-enum class PadUse { Fwd, FwdContent, Bwd, Saved, BwdSaved };
+enum class PadUse { Fwd, FwdContent, Bwd, BwdContent, Saved, BwdSaved };
 constexpr int kMaxRank = 64;   // content projection rank bound (sizes do not depend on the rank given)
 constexpr size_t kNone = ~size_t(0);
 
@@ -275,6 +275,8 @@ struct PadLayout {
   size_t dO = kNone, dS_T = kNone, dq = kNone, dk = kNone, dv = kNone;     // backward
   size_t dlg = kNone, db = kNone, dS0 = kNone;
   size_t bx = kNone, U1 = kNone, U2 = kNone, m0 = kNone, m_out = kNone, z_rec = kNone, m_rec = kNone;  // content
+  size_t gA = kNone, gtau = kNone, dgA = kNone, dgtau = kNone;   // gate pre-activations: A, tau and their gradients
+  size_t dm_out = kNone, dU1 = kNone, dU2 = kNone, dm0 = kNone;   // content backward
   size_t total = 0;
 };
 
@@ -291,8 +293,10 @@ PadLayout pad_layout(const carve_shape* s, PadUse use) {
     if (kn) {
       L.q = take(tok * es);
       L.k = take(tok * es);
-      L.lg = take(tok * 4);
-      L.b = take(tok * 4);
+      L.lg = take(tok * 4);   // log g, or the decay logits f
+      L.b = take(tok * 4);    // b, or the erase pre-activation b_x
+      L.gA = take((size_t)s->H * D * 4);
+      L.gtau = take((size_t)s->H * D * 4);
     } else {
       L.v = take(tok * es);
     }
@@ -302,7 +306,7 @@ PadLayout pad_layout(const carve_shape* s, PadUse use) {
     L.S_T = take(st);
     if (!kn) L.o = take(tok * es);
   }
-  if (use == PadUse::FwdContent) {
+  if (use == PadUse::FwdContent || use == PadUse::BwdContent) {
     // the content gate's operands on the narrow axis: b_x, U2 and z (key), or U1 and m (value)
     const size_t per = ((size_t)s->T + s->L - 1) / s->L;   // content periods
     if (kn) {
@@ -316,8 +320,17 @@ PadLayout pad_layout(const carve_shape* s, PadUse use) {
       L.m_rec = take(BH * per * D * 4);
     }
   }
-  if (use == PadUse::Bwd) L.S0 = take(st);
-  if (use == PadUse::Bwd || use == PadUse::BwdSaved) {
+  if (use == PadUse::BwdContent) {
+    if (kn) {
+      L.dU2 = take((size_t)s->H * D * kMaxRank * 4);
+    } else {
+      L.dm_out = take(BH * D * 4);
+      L.dU1 = take((size_t)s->H * kMaxRank * D * 4);
+      L.dm0 = take(BH * D * 4);
+    }
+  }
+  if (use == PadUse::Bwd || use == PadUse::BwdContent) L.S0 = take(st);
+  if (use == PadUse::Bwd || use == PadUse::BwdContent || use == PadUse::BwdSaved) {
     L.dS_T = take(st);
     L.dS0 = take(st);
     if (kn) {
@@ -325,6 +338,8 @@ PadLayout pad_layout(const carve_shape* s, PadUse use) {
       L.dk = take(tok * es);
       L.dlg = take(tok * 4);
       L.db = take(tok * 4);
+      L.dgA = take((size_t)s->H * D * 4);
+      L.dgtau = take((size_t)s->H * D * 4);
     } else {
       L.dO = take(tok * es);
       L.dv = take(tok * es);
@@ -366,6 +381,16 @@ struct Widen {
              : carve::launch_resize_rows(at(off), src, BH, (size_t)s->Dv * D, D * D, 4, 0u, st);
     return static_cast<float*>(at(off));
   }
+  // per head and key channel [H][Dk] <-> [H][D] (narrow key axis only)
+  const float* pad_head(size_t off, const float* src) {
+    if (!src || off == kNone) return src;
+    if (e == hipSuccess) e = carve::launch_resize_rows(at(off), src, s->H, s->Dk, D, 4, 0u, st);
+    return static_cast<const float*>(at(off));
+  }
+  void unpad_head(float* dst, size_t off) {
+    if (!dst || off == kNone) return;
+    if (e == hipSuccess) e = carve::launch_resize_rows(dst, at(off), s->H, D, s->Dk, 4, 0u, st);
+  }
   void unpad_state(float* dst, size_t off) {
     if (!dst || off == kNone) return;
     if (e == hipSuccess)
@@ -384,6 +409,41 @@ bool all_aligned(std::initializer_list<const void*> ptrs) {
   return true;
 }
 size_t unequal_need(const Plan& p, const PadLayout& L, size_t inner) { return p.empty ? 0 : L.total + inner + 512; }
+
+// The content gate's operands padded for the wider width (b_x = 1e30 with zero rows of U2
+// on a narrow key axis; zero columns of U1 and zero means on a narrow value axis); the
+// records, when given, are read (backward) or written (forward) through padded buffers.
+carve_content pad_content(Widen& W, const PadLayout& L, const carve_content* c, bool records_in) {
+  carve_content cp = *c;
+  const int R = c->U1 ? c->R : 0;
+  const size_t H = (size_t)W.s->H, per = ((size_t)W.s->T + W.s->L - 1) / W.s->L;
+  hipStream_t hs = W.st;
+  if (W.kn) {
+    cp.b_x = static_cast<const float*>(W.pad_tok(L.bx, c->b_x, 4, kBigBits));
+    if (c->U2 && W.e == hipSuccess)
+      W.e = carve::launch_resize_rows(W.at(L.U2), c->U2, H, (size_t)W.s->Dk * R, W.D * R, 4, 0u, hs);
+    if (c->U2) cp.U2 = static_cast<const float*>(W.at(L.U2));
+    if (c->z_rec) {
+      if (records_in && W.e == hipSuccess)
+        W.e = carve::launch_resize_rows(W.at(L.z_rec), c->z_rec, W.BH * per, W.s->Dk, W.D, 4, 0u, hs);
+      cp.z_rec = static_cast<float*>(W.at(L.z_rec));
+    }
+  } else {
+    if (c->U1 && W.e == hipSuccess)
+      W.e = carve::launch_resize_rows(W.at(L.U1), c->U1, H * R, W.s->Dv, W.D, 4, 0u, hs);
+    if (c->U1) cp.U1 = static_cast<const float*>(W.at(L.U1));
+    if (c->m0 && W.e == hipSuccess)
+      W.e = carve::launch_resize_rows(W.at(L.m0), c->m0, W.BH, W.s->Dv, W.D, 4, 0u, hs);
+    if (c->m0) cp.m0 = static_cast<const float*>(W.at(L.m0));
+    if (c->m_out) cp.m_out = static_cast<float*>(W.at(L.m_out));
+    if (c->m_rec) {
+      if (records_in && W.e == hipSuccess)
+        W.e = carve::launch_resize_rows(W.at(L.m_rec), c->m_rec, W.BH * per, W.s->Dv, W.D, 4, 0u, hs);
+      cp.m_rec = static_cast<float*>(W.at(L.m_rec));
+    }
+  }
+  return cp;
+}
 
 carve_status fwd_unequal(const carve_shape* s, const void* q, const void* k, const void* v, const float* log_g,
                          const float* b, const float* w, const float* S0, const carve_content* content, void* o,
@@ -409,29 +469,7 @@ carve_status fwd_unequal(const carve_shape* s, const void* q, const void* k, con
   }
   Widen W(s, align_up(workspace), hs);
   carve_content cp{};
-  if (content) {
-    // b_x, U2 and z on the key axis; U1, m0, m_out and the mean records on the value axis
-    const int R = content->U1 ? content->R : 0;
-    const size_t H = (size_t)s->H, per = ((size_t)s->T + s->L - 1) / s->L;
-    cp = *content;
-    if (W.kn) {
-      cp.b_x = static_cast<const float*>(W.pad_tok(L.bx, content->b_x, 4, kBigBits));
-      if (content->U2 && W.e == hipSuccess)
-        W.e = carve::launch_resize_rows(W.at(L.U2), content->U2, H, (size_t)s->Dk * R, W.D * R, 4, 0u, hs);
-      if (content->U2) cp.U2 = static_cast<const float*>(W.at(L.U2));
-      if (content->z_rec) cp.z_rec = static_cast<float*>(W.at(L.z_rec));
-    } else {
-      if (content->U1 && W.e == hipSuccess)
-        W.e = carve::launch_resize_rows(W.at(L.U1), content->U1, H * R, s->Dv, W.D, 4, 0u, hs);
-      if (content->U1) cp.U1 = static_cast<const float*>(W.at(L.U1));
-      if (content->m0 && W.e == hipSuccess)
-        W.e = carve::launch_resize_rows(W.at(L.m0), content->m0, W.BH, s->Dv, W.D, 4, 0u, hs);
-      if (content->m0) cp.m0 = static_cast<const float*>(W.at(L.m0));
-      if (content->m_out) cp.m_out = static_cast<float*>(W.at(L.m_out));
-      if (content->m_rec) cp.m_rec = static_cast<float*>(W.at(L.m_rec));
-    }
-    (void)per;
-  }
+  if (content) cp = pad_content(W, L, content, false);
   const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
   const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
   const float* lgp = W.kn ? static_cast<const float*>(W.pad_tok(L.lg, log_g, 4, 0u)) : log_g;
@@ -626,6 +664,214 @@ carve_status bwd_saved_unequal(const carve_shape* s, const void* q, const void* 
                        workspace_bytes - (size_t)(inner - static_cast<char*>(workspace)), stream, prof);
   if (st != CARVE_OK) return st;
   bwd_unpad(W, L, dq, dk, dv, dlog_g, db, dS0);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+carve_status bwd_content_unequal(const carve_shape* s, const void* q, const void* k, const void* v,
+                                 const float* log_g, const float* w, const float* S0, const carve_content* content,
+                                 const void* dO, const float* dS_T, const float* dm_out, void* dq, void* dk, void* dv,
+                                 float* dlog_g, float* db_x, float* dw, float* dU1, float* dU2, float* dm0,
+                                 float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  if (!content) return CARVE_ERR_INVALID_ARG;
+  st = check_content(&ws, p, content, nullptr);
+  if (st != CARVE_OK) return st;
+  const bool proj = content->U1 != nullptr;
+  if ((dU1 == nullptr) != !proj || (dU2 == nullptr) != !proj) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!q || !k || !v || !log_g || !w || !dO || !dq || !dk || !dv || !dlog_g || !db_x || !dw))
+    return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, log_g, w, S0, dO, dS_T, dm_out, dq, dk, dv, dlog_g, db_x, dw, dU1, dU2, dm0, dS0}))
+    return CARVE_ERR_INVALID_ARG;
+  const PadLayout L = pad_layout(s, PadUse::BwdContent);
+  const size_t need = unequal_need(p, L, carve_bwd_content_workspace_size(&ws, content));
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int R = proj ? content->R : 0;
+  if (p.empty) {
+    hipError_t e = dS0 ? carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    if (e == hipSuccess && dm0) e = carve::launch_copy_or_zero(dm0, dm_out, (size_t)p.BH * s->Dv, hs);
+    if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(dU1, nullptr, (size_t)s->H * R * s->Dv, hs);
+    if (e == hipSuccess && proj) e = carve::launch_copy_or_zero(dU2, nullptr, (size_t)s->H * s->Dk * R, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  Widen W(s, align_up(workspace), hs);
+  const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
+  const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
+  const float* lgp = W.kn ? static_cast<const float*>(W.pad_tok(L.lg, log_g, 4, 0u)) : log_g;
+  const void* vp = W.kn ? v : W.pad_tok(L.v, v, W.es, 0u);
+  const void* dOp = W.kn ? dO : W.pad_tok(L.dO, dO, W.es, 0u);
+  const carve_content cp = pad_content(W, L, content, true);
+  const float* S0p = W.pad_state(L.S0, S0);
+  const float* dSTp = W.pad_state(L.dS_T, dS_T);
+  const float* dmop = dm_out;
+  if (!W.kn && dm_out && W.e == hipSuccess)
+    W.e = carve::launch_resize_rows(W.at(L.dm_out), dm_out, W.BH, s->Dv, W.D, 4, 0u, hs);
+  if (!W.kn && dm_out) dmop = static_cast<const float*>(W.at(L.dm_out));
+  const BwdOut r = bwd_outputs(W, L, dq, dk, dv, dlog_g, db_x, dS0);
+  float* dU1p = (!W.kn && dU1) ? static_cast<float*>(W.at(L.dU1)) : dU1;
+  float* dU2p = (W.kn && dU2) ? static_cast<float*>(W.at(L.dU2)) : dU2;
+  float* dm0p = (!W.kn && dm0) ? static_cast<float*>(W.at(L.dm0)) : dm0;
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  st = carve_bwd_content(&ws, qp, kp, vp, lgp, w, S0p, &cp, dOp, dSTp, dmop, r.dq, r.dk, r.dv, r.dlog_g, r.db, dw,
+                         dU1p, dU2p, dm0p, r.dS0, inner, workspace_bytes - (size_t)(inner - static_cast<char*>(workspace)),
+                         stream);
+  if (st != CARVE_OK) return st;
+  bwd_unpad(W, L, dq, dk, dv, dlog_g, db_x, dS0);
+  if (W.e == hipSuccess && !W.kn && dU1)
+    W.e = carve::launch_resize_rows(dU1, dU1p, (size_t)s->H * R, W.D, s->Dv, 4, 0u, hs);
+  if (W.e == hipSuccess && W.kn && dU2)
+    W.e = carve::launch_resize_rows(dU2, dU2p, (size_t)s->H, W.D * R, (size_t)s->Dk * R, 4, 0u, hs);
+  if (W.e == hipSuccess && !W.kn && dm0)
+    W.e = carve::launch_resize_rows(dm0, dm0p, W.BH, W.D, s->Dv, 4, 0u, hs);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+// gate pre-activations on a narrow key axis: f, A and tau padded with 0 (log g = -0 * softplus
+// = 0), b_x with 1e30 (b = 1); w_hat is per token and needs nothing
+carve_gate_logits pad_logits(Widen& W, const PadLayout& L, const carve_gate_logits* g) {
+  carve_gate_logits r = *g;
+  if (!W.kn) return r;
+  r.f = static_cast<const float*>(W.pad_tok(L.lg, g->f, 4, 0u));
+  r.b_x = static_cast<const float*>(W.pad_tok(L.b, g->b_x, 4, kBigBits));
+  r.A = W.pad_head(L.gA, g->A);
+  r.tau = W.pad_head(L.gtau, g->tau);
+  return r;
+}
+// the same padded gates, as carve_fwd_logits_save left them in the saved buffer
+carve_gate_logits saved_logits(const Widen& W, const PadLayout& L, const carve_gate_logits* g) {
+  carve_gate_logits r = *g;
+  if (!W.kn) return r;
+  r.f = static_cast<const float*>(W.at(L.lg));
+  r.b_x = g->b_x ? static_cast<const float*>(W.at(L.b)) : nullptr;
+  r.A = static_cast<const float*>(W.at(L.gA));
+  r.tau = static_cast<const float*>(W.at(L.gtau));
+  return r;
+}
+carve_status check_logits(const carve_shape* s, const Plan& p, const carve_gate_logits* g) {
+  if (!g) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!g->f || !g->A || !g->tau || !g->w_hat)) return CARVE_ERR_INVALID_ARG;
+  for (const void* ptr : {(const void*)g->f, (const void*)g->b_x, (const void*)g->w_hat})
+    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
+  return CARVE_OK;
+}
+
+carve_status fwd_logits_unequal(const carve_shape* s, const void* q, const void* k, const void* v,
+                                const carve_gate_logits* gates, const float* S0, void* o, float* S_T,
+                                void* saved_or_ws, size_t bytes, void* stream, const carve_profile* prof,
+                                bool save) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  st = check_logits(&ws, p, gates);
+  if (st != CARVE_OK) return st;
+  if (!p.empty && (!q || !k || !v || !o)) return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, S0, o, S_T, save ? saved_or_ws : nullptr})) return CARVE_ERR_INVALID_ARG;
+  const PadLayout L = pad_layout(s, save ? PadUse::Saved : PadUse::Fwd);
+  const size_t need = unequal_need(p, L, save ? saved_bytes(&ws, p) : fwd_ws(&ws, p, nullptr));
+  if (bytes < need || (need > 0 && !saved_or_ws)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = S_T ? carve::launch_copy_or_zero(S_T, S0, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  // for the training pair the padded inputs stay in the saved buffer for the backward
+  Widen W(s, align_up(saved_or_ws), hs);
+  const void* qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
+  const void* kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
+  const void* vp = W.kn ? v : W.pad_tok(L.v, v, W.es, 0u);
+  const carve_gate_logits gp = pad_logits(W, L, gates);
+  const float* S0p = W.pad_state(L.S0, S0);
+  void* op = W.kn ? o : W.at(L.o);
+  float* STp = S_T ? static_cast<float*>(W.at(L.S_T)) : nullptr;
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  const size_t left = bytes - (size_t)(inner - static_cast<char*>(saved_or_ws));
+  st = save ? carve_fwd_logits_save(&ws, qp, kp, vp, &gp, S0p, op, STp, inner, left, stream, prof)
+            : carve_fwd_logits(&ws, qp, kp, vp, &gp, S0p, op, STp, inner, left, stream);
+  if (st != CARVE_OK) return st;
+  if (!W.kn) W.unpad_tok(o, L.o, W.es);
+  W.unpad_state(S_T, L.S_T);
+  return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+}
+
+// the recomputing backward (saved == nullptr) or the saved one
+carve_status bwd_logits_unequal(const carve_shape* s, const void* q, const void* k, const void* v,
+                                const carve_gate_logits* gates, const float* S0, const void* dO, const float* dS_T,
+                                const void* saved, size_t saved_bytes_given, void* dq, void* dk, void* dv,
+                                float* df, float* dA, float* dtau, float* db_x, float* dw_hat, float* dS0,
+                                void* workspace, size_t workspace_bytes, void* stream, const carve_profile* prof,
+                                bool use_saved) {
+  const carve_shape ws = widened(s);
+  Plan p;
+  carve_status st = check_shape(&ws, &p);
+  if (st != CARVE_OK) return st;
+  st = check_logits(&ws, p, gates);
+  if (st != CARVE_OK) return st;
+  if ((gates->b_x == nullptr) != (db_x == nullptr)) return CARVE_ERR_INVALID_ARG;
+  if (!p.empty && (!q || !k || !v || !dO || !dq || !dk || !dv || !df || !dA || !dtau || !dw_hat))
+    return CARVE_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, S0, dO, dS_T, use_saved ? saved : nullptr, dq, dk, dv, df, db_x, dw_hat, dS0}))
+    return CARVE_ERR_INVALID_ARG;
+  const PadLayout Ls = pad_layout(s, PadUse::Saved);
+  if (use_saved) {
+    const size_t need_saved = unequal_need(p, Ls, saved_bytes(&ws, p));
+    if (saved_bytes_given < need_saved || (need_saved > 0 && !saved)) return CARVE_ERR_WORKSPACE;
+  }
+  const PadLayout L = pad_layout(s, use_saved ? PadUse::BwdSaved : PadUse::Bwd);
+  const size_t inner_need = use_saved ? carve_bwd_logits_saved_workspace_size(&ws) : carve_bwd_logits_workspace_size(&ws);
+  const size_t need = unequal_need(p, L, inner_need);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return CARVE_ERR_WORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (p.empty) {
+    hipError_t e = dS0 ? carve::launch_copy_or_zero(dS0, dS_T, (size_t)p.BH * s->Dv * s->Dk, hs) : hipSuccess;
+    if (e == hipSuccess && dA && s->H > 0) e = carve::launch_copy_or_zero(dA, nullptr, (size_t)s->H * s->Dk, hs);
+    if (e == hipSuccess && dtau && s->H > 0) e = carve::launch_copy_or_zero(dtau, nullptr, (size_t)s->H * s->Dk, hs);
+    return e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
+  }
+  Widen W(s, align_up(workspace), hs);
+  const void *qp, *kp, *vp;
+  carve_gate_logits gp;
+  char* inner_saved = nullptr;
+  if (use_saved) {
+    // the forward's padded inputs, from the saved buffer (same layout as carve_fwd_logits_save wrote)
+    Widen Ws(s, align_up(const_cast<void*>(saved)), hs);
+    qp = Ws.kn ? Ws.at(Ls.q) : q;
+    kp = Ws.kn ? Ws.at(Ls.k) : k;
+    vp = Ws.kn ? v : Ws.at(Ls.v);
+    gp = saved_logits(Ws, Ls, gates);
+    inner_saved = align_up(Ws.base + Ls.total);
+  } else {
+    qp = W.kn ? W.pad_tok(L.q, q, W.es, 0u) : q;
+    kp = W.kn ? W.pad_tok(L.k, k, W.es, 0u) : k;
+    vp = W.kn ? v : W.pad_tok(L.v, v, W.es, 0u);
+    gp = pad_logits(W, L, gates);
+  }
+  const void* dOp = W.kn ? dO : W.pad_tok(L.dO, dO, W.es, 0u);
+  const float* S0p = use_saved ? nullptr : W.pad_state(L.S0, S0);
+  const float* dSTp = W.pad_state(L.dS_T, dS_T);
+  const BwdOut r = bwd_outputs(W, L, dq, dk, dv, df, db_x, dS0);
+  float* dAp = W.kn ? static_cast<float*>(W.at(L.dgA)) : dA;
+  float* dtaup = W.kn ? static_cast<float*>(W.at(L.dgtau)) : dtau;
+  if (W.e != hipSuccess) return CARVE_ERR_HIP;
+  char* inner = align_up(W.base + L.total);
+  const size_t left = workspace_bytes - (size_t)(inner - static_cast<char*>(workspace));
+  st = use_saved
+           ? carve_bwd_logits_saved(&ws, qp, kp, vp, &gp, dOp, dSTp, inner_saved,
+                                    saved_bytes_given - (size_t)(inner_saved - static_cast<const char*>(saved)), r.dq,
+                                    r.dk, r.dv, r.dlog_g, dAp, dtaup, r.db, dw_hat, r.dS0, inner, left, stream, prof)
+           : carve_bwd_logits(&ws, qp, kp, vp, &gp, S0p, dOp, dSTp, r.dq, r.dk, r.dv, r.dlog_g, dAp, dtaup, r.db,
+                              dw_hat, r.dS0, inner, left, stream);
+  if (st != CARVE_OK) return st;
+  bwd_unpad(W, L, dq, dk, dv, df, db_x, dS0);
+  if (W.kn) {
+    W.unpad_head(dA, L.dgA);
+    W.unpad_head(dtau, L.dgtau);
+  }
   return W.e == hipSuccess ? CARVE_OK : CARVE_ERR_HIP;
 }
 
@@ -934,13 +1180,6 @@ carve_status carve_bwd_saved(const carve_shape* s, const void* q, const void* k,
 }
 
 // ------------------------------------------------------------ gate pre-activations
-carve_status check_logits(const carve_shape* s, const Plan& p, const carve_gate_logits* g) {
-  if (!g) return CARVE_ERR_INVALID_ARG;
-  if (!p.empty && (!g->f || !g->A || !g->tau || !g->w_hat)) return CARVE_ERR_INVALID_ARG;
-  for (const void* ptr : {(const void*)g->f, (const void*)g->b_x, (const void*)g->w_hat})
-    if (ptr && !aligned16(ptr)) return CARVE_ERR_INVALID_ARG;
-  return CARVE_OK;
-}
 
 // arguments of the logit-space epilogue (df in place, dA and dtau from per-block partial sums)
 carve::LogitGradArgs logit_grad_args(const carve_shape* s, const Plan& p, const carve_gate_logits* gates, float* df,
@@ -962,6 +1201,8 @@ carve::LogitGradArgs logit_grad_args(const carve_shape* s, const Plan& p, const 
 carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k, const void* v,
                               const carve_gate_logits* gates, const float* S0, void* o, float* S_T,
                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (unequal_widths(s))
+    return fwd_logits_unequal(s, q, k, v, gates, S0, o, S_T, workspace, workspace_bytes, stream, nullptr, false);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -990,6 +1231,12 @@ carve_status carve_fwd_logits(const carve_shape* s, const void* q, const void* k
 }
 
 size_t carve_bwd_logits_workspace_size(const carve_shape* s) {
+  if (unequal_widths(s)) {
+    const carve_shape ws = widened(s);
+    Plan p;
+    if (check_shape(&ws, &p) != CARVE_OK) return 0;
+    return unequal_need(p, pad_layout(s, PadUse::Bwd), carve_bwd_logits_workspace_size(&ws));
+  }
   Plan p;
   if (check_shape(s, &p) != CARVE_OK || p.empty) return 0;
   return bwd_ws(s, p) + carve::logit_partials_bytes(s->B, s->H, s->T, p.D) + 1024;
@@ -999,6 +1246,9 @@ carve_status carve_bwd_logits(const carve_shape* s, const void* q, const void* k
                               const carve_gate_logits* gates, const float* S0, const void* dO, const float* dS_T,
                               void* dq, void* dk, void* dv, float* df, float* dA, float* dtau, float* db_x,
                               float* dw_hat, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  if (unequal_widths(s))
+    return bwd_logits_unequal(s, q, k, v, gates, S0, dO, dS_T, nullptr, 0, dq, dk, dv, df, dA, dtau, db_x, dw_hat,
+                              dS0, workspace, workspace_bytes, stream, nullptr, false);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -1058,6 +1308,12 @@ size_t bwd_logits_saved_ws(const carve_shape* s, const Plan& p) {
 }
 
 size_t carve_bwd_logits_saved_workspace_size(const carve_shape* s) {
+  if (unequal_widths(s)) {
+    const carve_shape ws = widened(s);
+    Plan p;
+    if (check_shape(&ws, &p) != CARVE_OK) return 0;
+    return unequal_need(p, pad_layout(s, PadUse::BwdSaved), carve_bwd_logits_saved_workspace_size(&ws));
+  }
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
   return bwd_logits_saved_ws(s, p);
@@ -1066,6 +1322,8 @@ size_t carve_bwd_logits_saved_workspace_size(const carve_shape* s) {
 carve_status carve_fwd_logits_save(const carve_shape* s, const void* q, const void* k, const void* v,
                                    const carve_gate_logits* gates, const float* S0, void* o, float* S_T,
                                    void* saved, size_t saved_bytes_given, void* stream, const carve_profile* prof) {
+  if (unequal_widths(s))
+    return fwd_logits_unequal(s, q, k, v, gates, S0, o, S_T, saved, saved_bytes_given, stream, prof, true);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -1104,6 +1362,9 @@ carve_status carve_bwd_logits_saved(const carve_shape* s, const void* q, const v
                                     float* df, float* dA, float* dtau, float* db_x, float* dw_hat, float* dS0,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     const carve_profile* prof) {
+  if (unequal_widths(s))
+    return bwd_logits_unequal(s, q, k, v, gates, nullptr, dO, dS_T, saved, saved_bytes_given, dq, dk, dv, df, dA, dtau,
+                              db_x, dw_hat, dS0, workspace, workspace_bytes, stream, prof, true);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;
@@ -1198,6 +1459,12 @@ ContentBwdLayout content_bwd_layout(const carve_shape* s, const Plan& p, const c
 }
 
 size_t carve_bwd_content_workspace_size(const carve_shape* s, const carve_content* content) {
+  if (unequal_widths(s)) {
+    const carve_shape ws = widened(s);
+    Plan p;
+    if (check_shape(&ws, &p) != CARVE_OK) return 0;
+    return unequal_need(p, pad_layout(s, PadUse::BwdContent), carve_bwd_content_workspace_size(&ws, content));
+  }
   Plan p;
   if (check_shape(s, &p) != CARVE_OK) return 0;
   return content_bwd_layout(s, p, content).total;
@@ -1208,6 +1475,9 @@ carve_status carve_bwd_content(const carve_shape* s, const void* q, const void* 
                                const void* dO, const float* dS_T, const float* dm_out, void* dq, void* dk,
                                void* dv, float* dlog_g, float* db_x, float* dw, float* dU1, float* dU2,
                                float* dm0, float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+  if (unequal_widths(s))
+    return bwd_content_unequal(s, q, k, v, log_g, w, S0, content, dO, dS_T, dm_out, dq, dk, dv, dlog_g, db_x, dw, dU1,
+                               dU2, dm0, dS0, workspace, workspace_bytes, stream);
   Plan p;
   carve_status st = check_shape(s, &p);
   if (st != CARVE_OK) return st;

@@ -51,19 +51,17 @@
  *     tokens in blocks of 32 when L <= 32 or dtype is float32, and of 64
  *     otherwise); for the content path L must be a multiple of that tile.
  *   - Unequal widths (Dk != Dv; the pages write the state as Dv x Dk with
- *     independent widths, notes section 1): carve_fwd, carve_fwd_ex and
- *     carve_fwd_noalloc (token-only or content-aware), carve_bwd, carve_bwd_ex,
- *     the training pair and carve_decode_step accept them.  Except for the decode
- *     step, which takes both widths directly, such a call runs at D = max(Dk, Dv)
- *     on padded copies of its operands held in front of its workspace (for the
- *     training pair, the padded inputs in front of the saved buffer, where
- *     carve_bwd_saved reads them).  Padded key channels carry k = q = 0 and
- *     retention 1 (log g = 0 and b = 1, or b_x = 1e30 with zero rows of U2 on the
- *     content path), padded value rows v = 0 (and zero columns of U1), so every
- *     padded term is an exact zero; the size functions count the copies (for the
- *     content path, for any rank up to 64 and with room for the records).
- *     carve_bwd_content and the gate pre-activation calls return
- *     CARVE_ERR_UNSUPPORTED for Dk != Dv.
+ *     independent widths, notes section 1) are accepted by every entry point.
+ *     Except for the decode step, which takes both widths directly, such a call
+ *     runs at D = max(Dk, Dv) on padded copies of its operands held in front of
+ *     its workspace (for the training pairs, the padded inputs in front of the
+ *     saved buffer, where the saved backward reads them).  Padded key channels
+ *     carry k = q = 0 and retention 1 (log g = 0 and b = 1; A = 0 and
+ *     b_x = 1e30 for gates given as pre-activations; b_x = 1e30 with zero rows of
+ *     U2 on the content path), padded value rows v = dO = 0 (and zero columns of
+ *     U1), so every padded term is an exact zero, and the outputs are cut back to
+ *     the caller's widths.  The size functions count the copies (on the content
+ *     path for any rank up to 64, with room for the records).
  *   - Numerical range: any retention a = exp(log g) * b in [0, 1] is handled
  *     (the pages put no floor on the decay, notes section 2.3, and take the
  *     erase as a factor in (0, 1], section 2.1).  The kernels carry the

@@ -284,9 +284,7 @@ def test_size_limits_on_host(lib):
 def test_unequal_widths_on_host(lib):
     """Key and value widths 64 and 128 in either order run at the wider width on padded
     copies held in front of the workspace (or the saved buffer): every size grows by the
-    padded operands, the checks are those of the equal-width calls, and the paths with no
-    padded variant (content-aware backward, gate pre-activations) are rejected before any
-    launch."""
+    padded operands and the checks are those of the equal-width calls."""
     for dk, dv in ((64, 128), (128, 64)):
         s, wide = shape(D=dk, Dv=dv), shape(D=128)
         for fn in ("carve_bwd_workspace_size", "carve_saved_size", "carve_bwd_saved_workspace_size"):
@@ -304,8 +302,10 @@ def test_unequal_widths_on_host(lib):
         assert call_fwd(lib, s, content=c, ws_bytes=cw) == WORKSPACE
         assert call_fwd(lib, s, b=FAKE, content=c) == INVALID                         # b together with content
         assert call_fwd(lib, shape(D=dk, Dv=dv, L=16), content=c) == UNSUPPORTED      # period not whole tiles
-        assert lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(c)) == 0
-        assert lib.carve_bwd_logits_workspace_size(ctypes.byref(s)) == 0
+        assert lib.carve_bwd_content_workspace_size(ctypes.byref(s), ctypes.byref(c)) > \
+            lib.carve_bwd_content_workspace_size(ctypes.byref(wide), ctypes.byref(c))
+        for fn in ("carve_bwd_logits_workspace_size", "carve_bwd_logits_saved_workspace_size"):
+            assert getattr(lib, fn)(ctypes.byref(s)) > getattr(lib, fn)(ctypes.byref(wide)), fn
         # an empty problem needs no workspace and launches nothing
         s0 = shape(T=0, D=dk, Dv=dv)
         assert lib.carve_fwd_workspace_size(ctypes.byref(s0), None) == 0

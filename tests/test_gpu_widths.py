@@ -3,9 +3,9 @@ widths; the library runs such calls at the wider width on padded copies (the dec
 takes both widths directly).  Checked against the float64 oracle, which computes at the
 true widths: forward outputs and final state, every gradient of the recomputing backward
 and of the training pair (which must also match the recomputing backward bit for bit, as
-at equal widths), the content-aware forward with its per-period records, the
-no-allocation forward (bit for bit against carve_fwd), and the decode step, token-only
-and content-aware.  Ragged token counts, both orders of the
+at equal widths), the gates as pre-activations (both pairs), the content-aware forward
+with its per-period records and its backward (with and without the records), the no-allocation forward (bit for bit against carve_fwd),
+and the decode step, token-only and content-aware.  Ragged token counts, both orders of the
 widths, float32 and bfloat16."""
 import numpy as np
 import pytest
@@ -179,3 +179,76 @@ def test_unequal_widths_content_forward(dtype, Dk, Dv, T, L):
     ro0, _, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L,
                                content={"b_x": inp["b_x"], "U1": None, "U2": None})
     assert max_rel(ro0, ro) > 0.02       # the content signal matters at this scale
+
+
+LOGIT_GRADS = ("dq", "dk", "dv", "df", "dA", "dtau", "db_x", "dw_hat", "dS0")
+
+
+@pytest.mark.parametrize("dtype,B,H,T,Dk,Dv", [CASES[0], CASES[3]], ids=[IDS[0], IDS[3]])
+def test_unequal_widths_gate_logits(dtype, B, H, T, Dk, Dv):
+    """Gates given as pre-activations at unequal widths (A and tau per head and key channel):
+    the recomputing pair against the oracle, and the saved pair bit for bit against it."""
+    announce(f"unequal widths gate logits {dtype} B{B} H{H} T{T} Dk{Dk} Dv{Dv}")
+    inp, S0, dS_T = setup(dtype, B, H, T, Dk, Dv, seed=400 + Dk + T)
+    rng = np.random.default_rng(401)
+    f64 = lambda x: np.asarray(x, np.float32).astype(np.float64)
+    gl = {"f": f64(rng.standard_normal((B, H, T, Dk))), "A": f64(rng.uniform(0.05, 10.0, (H, Dk))),
+          "tau": f64(rng.standard_normal((H, Dk)) * 0.5), "w_hat": f64(rng.standard_normal((B, H, T))),
+          "b_x": f64(rng.normal(2.0, 1.0, (B, H, T, Dk)))}
+    d = to_device(inp, dtype)
+    gd = {k_: f32(v_) for k_, v_ in gl.items()}
+    S0d, dSd = f32(S0), f32(dS_T)
+    args = (d["q"], d["k"], d["v"], gd["f"], gd["A"], gd["tau"], gd["w_hat"])
+    o, S_T = carve.fwd_logits(*args, b_x=gd["b_x"], S0=S0d)
+    g = carve.bwd_logits(*args, d["dO"], b_x=gd["b_x"], S0=S0d, dS_T=dSd)
+    o2, S_T2, saved = carve.fwd_logits_save(*args, b_x=gd["b_x"], S0=S0d)
+    g2 = carve.bwd_logits_saved(*args, d["dO"], saved, b_x=gd["b_x"], dS_T=dSd)
+    torch.cuda.synchronize()
+    ro, rS = oracle.forward_logits(inp["q"], inp["k"], inp["v"], gl["f"], gl["A"], gl["tau"], gl["w_hat"],
+                                   b_x=gl["b_x"], S0=S0)
+    ref = oracle.backward_logits(inp["q"], inp["k"], inp["v"], gl["f"], gl["A"], gl["tau"], gl["w_hat"], inp["dO"],
+                                 b_x=gl["b_x"], S0=S0, dS_T=dS_T)
+    errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS)}
+    errs.update({k_: max_rel(to_np(g[k_]), ref[k_]) for k_ in LOGIT_GRADS})
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
+    assert torch.equal(o2, o) and torch.equal(S_T2, S_T)
+    for k_ in LOGIT_GRADS:
+        assert torch.equal(g2[k_], g[k_]), k_
+
+
+CONTENT_GRADS = ("dq", "dk", "dv", "dlog_g", "db_x", "dw", "dU1", "dU2", "dm0", "dS0")
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv,T,L", [("bf16", 64, 128, 64 * 3 + 30, 64), ("f32", 128, 64, 32 * 5 + 7, 32)])
+def test_unequal_widths_content_backward(dtype, Dk, Dv, T, L):
+    """Backward through the content-aware erase at unequal widths: every gradient (dU1
+    [H, R, Dv], dU2 [H, Dk, R], dm0 [B, H, Dv]) against the oracle; given the forward's
+    records, the same bits without re-running the forward."""
+    announce(f"unequal widths content backward {dtype} Dk{Dk} Dv{Dv} T{T} L{L}")
+    B, H = 2, 2
+    inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=420 + Dk, erase="content", dists="softplus_decay",
+                        with_dO=True)
+    inp["U1"] = inp["U1"] * 8.0
+    inp["U2"] = inp["U2"] * 8.0
+    rng = np.random.default_rng(421)
+    f64 = lambda x: np.asarray(x, np.float32).astype(np.float64)
+    m0, S0 = f64(rng.standard_normal((B, H, Dv)) * 0.5), f64(rng.standard_normal((B, H, Dv, Dk)) * 0.3)
+    dS_T, dm_out = f64(rng.standard_normal((B, H, Dv, Dk)) * 0.3), f64(rng.standard_normal((B, H, Dv)))
+    d = to_device(inp, dtype)
+    cont = {"b_x": d["b_x"], "U1": d["U1"], "U2": d["U2"], "m0": f32(m0)}
+    kw = dict(S0=f32(S0), dS_T=f32(dS_T), dm_out=f32(dm_out), L=L)
+    g = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], cont, **kw)
+    zr, mr = carve.content_records(B, H, T, Dk, Dv, L, torch.device("cuda"))
+    carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], S0=f32(S0), L=L, content=dict(cont, z_rec=zr, m_rec=mr))
+    g1 = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], dict(cont, z_rec=zr, m_rec=mr),
+                           **kw)
+    torch.cuda.synchronize()
+    ref = oracle.backward_content(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"],
+                                  {"b_x": inp["b_x"], "U1": inp["U1"], "U2": inp["U2"], "m0": m0},
+                                  S0=S0, dS_T=dS_T, dm_out=dm_out, L=L)
+    errs = {k_: max_rel(to_np(g[k_]), ref[k_]) for k_ in CONTENT_GRADS}
+    print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+    assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
+    for k_ in CONTENT_GRADS:
+        assert torch.equal(g1[k_], g[k_]), k_
