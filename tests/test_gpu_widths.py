@@ -6,7 +6,8 @@ and of the training pair (which must also match the recomputing backward bit for
 at equal widths), the gates as pre-activations (both pairs), the content-aware forward
 with its per-period records and its backward (with and without the records), the no-allocation forward (bit for bit against carve_fwd),
 and the decode step, token-only and content-aware.  Ragged token counts, both orders of the
-widths, float32 and bfloat16."""
+widths, float32 and bfloat16; and at full length (T = 4096) the training pair on every
+head, each head normalised by its own reference."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +15,8 @@ import torch
 import oracle
 from chunk_gated_delta_amd import carve
 from chunk_gated_delta_amd.synth import random_inputs
-from tests.helpers import max_rel, to_device, to_np
+from oracle.head_pool import HeadPool
+from tests.helpers import max_rel, per_head_rel, to_device, to_np
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -252,3 +254,32 @@ def test_unequal_widths_content_backward(dtype, Dk, Dv, T, L):
     assert all(v_ <= TOL[dtype] for v_ in errs.values()), errs
     for k_ in CONTENT_GRADS:
         assert torch.equal(g1[k_], g[k_]), k_
+
+
+@pytest.mark.parametrize("Dk,Dv", [(64, 128), (128, 64)])
+def test_unequal_widths_full_length_every_head(Dk, Dv):
+    """B2 H16 T4096 bf16 with the benchmark's gate distributions: fwd_save + bwd_saved,
+    o, S_T and every gradient of all 32 heads against the oracle, per head."""
+    B, H, T = 2, 16, 4096
+    announce(f"unequal widths full length every head Dk{Dk} Dv{Dv}")
+    inp = random_inputs(B, H, T, Dk, Dv, dtype="bf16", seed=440 + Dk, erase="sigmoid", dists="softplus_decay",
+                        with_dO=True)
+    d = to_device(inp, "bf16")
+    o, S_T, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"])
+    g = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=d["b"], want_dS0=False)
+    torch.cuda.synchronize()
+    gpu = {"o": to_np(o), "S_T": to_np(S_T)}
+    gpu.update({k_: to_np(g[k_]) for k_ in ("dq", "dk", "dv", "dlog_g", "db", "dw")})
+    del d, o, S_T, saved, g
+    kw = dict(q=inp["q"], k=inp["k"], v=inp["v"], log_g=inp["log_g"], w=inp["w"], b=inp["b"])
+    with HeadPool() as pool:
+        ro, rS, _ = pool.run("forward", B, H, **kw)
+        ref = pool.run("backward", B, H, dO=inp["dO"], **kw)
+    ref.update(o=ro, S_T=rS)
+    bad = {}
+    for k_, x in gpu.items():
+        e = per_head_rel(x, ref[k_])
+        print(f"  {k_}: worst head {e.max():.2e}, median {np.median(e):.2e}", flush=True)
+        if e.max() > TOL["bf16"]:
+            bad[k_] = float(e.max())
+    assert not bad, bad
