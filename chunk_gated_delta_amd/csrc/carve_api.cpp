@@ -29,6 +29,10 @@ struct Plan {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// largest rank of the content projection U_b = U2 U1 (the content kernels hold U1 m in a
+// 64-float buffer); padded copies of U1 and U2 are sized for it
+constexpr int kMaxRank = 64;
+
 // token tile of the chunk kernels: 32 for short chunks and for float32 inputs
 // (LDS budget of the backward chunk kernel), else 64
 int tile_for(int L, int dtype, int D) {
@@ -103,7 +107,7 @@ carve_status check_content(const carve_shape* s, const Plan& p, const carve_cont
   if (!c) return CARVE_OK;
   if (b) return CARVE_ERR_INVALID_ARG;                       // erase comes from the content gate
   if ((c->U1 == nullptr) != (c->U2 == nullptr)) return CARVE_ERR_INVALID_ARG;
-  if (c->U1 && (c->R < 1 || c->R > 64)) return CARVE_ERR_INVALID_ARG;
+  if (c->U1 && (c->R < 1 || c->R > kMaxRank)) return CARVE_ERR_INVALID_ARG;
   if (s->L % p.LC != 0) return CARVE_ERR_UNSUPPORTED;        // content period must be whole tiles
   if (!p.empty && !c->b_x) return CARVE_ERR_INVALID_ARG;
   if ((c->z_rec == nullptr) != (c->m_rec == nullptr)) return CARVE_ERR_INVALID_ARG;   // records come in pairs
@@ -265,7 +269,6 @@ carve_shape widened(const carve_shape* s) {
 }
 
 enum class PadUse { Fwd, FwdContent, Bwd, BwdContent, Saved, BwdSaved };
-constexpr int kMaxRank = 64;   // content projection rank bound (sizes do not depend on the rank given)
 constexpr size_t kNone = ~size_t(0);
 
 // Byte offsets of the padded operands of one call (kNone: not used), each 256-byte aligned.
@@ -1627,7 +1630,7 @@ carve_status carve_decode_step(const carve_shape* s, const void* q, const void* 
   if (c) {
     if (b || !c->b_x || !c->m_out || !c->csum) return CARVE_ERR_INVALID_ARG;
     if ((c->U1 == nullptr) != (c->U2 == nullptr)) return CARVE_ERR_INVALID_ARG;
-    if (c->U1 && (c->R < 1 || c->R > 64)) return CARVE_ERR_INVALID_ARG;
+    if (c->U1 && (c->R < 1 || c->R > kMaxRank)) return CARVE_ERR_INVALID_ARG;
     if (c->pos < 0 || c->pos >= s->L) return CARVE_ERR_INVALID_ARG;
     if (c->m_in && c->m_in == c->m_out) return CARVE_ERR_INVALID_ARG;
     if (!aligned16(c->b_x)) return CARVE_ERR_INVALID_ARG;
