@@ -1,0 +1,105 @@
+"""Seeded random configurations against the float64 oracle (needs an MI355X).  Each case
+draws batch, heads, token count, both head widths, dtype, chunk length, erase mode, gate
+distribution, an initial state and the call pair at random, so combinations that no
+hand-written case names (a ragged tail with unequal widths and L = 16, a one-token
+sequence with a content projection of rank 64, ...) meet the same bars: 1e-4 for float32
+inputs, 2e-2 for bfloat16, max-normalised per tensor.  The configurations are printed
+before each call."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunk_gated_delta_amd import carve
+from chunk_gated_delta_amd.synth import random_inputs
+from tests.helpers import max_rel, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def f32(x):
+    return None if x is None else torch.from_numpy(np.asarray(x, np.float32)).cuda()
+
+
+def draw_case(rng):
+    c = dict(B=int(rng.integers(1, 4)), H=int(rng.integers(1, 4)), T=int(rng.integers(1, 301)),
+             Dk=int(rng.choice([64, 128])), Dv=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])),
+             L=int(rng.choice([16, 32, 64, 128])), erase=str(rng.choice(["none", "ones", "sigmoid"])),
+             dists=str(rng.choice(["softplus_decay", "uniform_decay"])), state=bool(rng.integers(0, 2)),
+             pair=str(rng.choice(["recompute", "saved"])))
+    return c
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_token_configs(seed):
+    rng = np.random.default_rng(5000 + seed)
+    for i in range(10):
+        c = draw_case(rng)
+        print(f"\n[case] seed {seed} #{i}: {c}", flush=True)
+        B, H, T, Dk, Dv, dtype = c["B"], c["H"], c["T"], c["Dk"], c["Dv"], c["dtype"]
+        inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=int(rng.integers(1 << 30)), erase=c["erase"],
+                            dists=c["dists"], with_dO=True)
+        S0 = dS_T = None
+        if c["state"]:
+            S0 = np.asarray(rng.standard_normal((B, H, Dv, Dk)) * 0.3, np.float32).astype(np.float64)
+            dS_T = np.asarray(rng.standard_normal((B, H, Dv, Dk)) * 0.3, np.float32).astype(np.float64)
+        d = to_device(inp, dtype)
+        b = d.get("b")
+        if c["pair"] == "saved":
+            o, S_T, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=b, S0=f32(S0), L=c["L"])
+            g = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=b, dS_T=f32(dS_T),
+                                L=c["L"])
+        else:
+            o, S_T, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=b, S0=f32(S0), L=c["L"])
+            g = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=b, S0=f32(S0), dS_T=f32(dS_T),
+                          L=c["L"])
+        torch.cuda.synchronize()
+        ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], b=inp.get("b"), S0=S0)
+        ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"], b=inp.get("b"),
+                              S0=S0, dS_T=dS_T)
+        errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS)}
+        for key in ("dq", "dk", "dv", "dlog_g", "db", "dw", "dS0"):
+            if ref[key] is None or g[key] is None:
+                assert (ref[key] is None) == (g[key] is None), key
+                continue
+            errs[key] = max_rel(to_np(g[key]), ref[key])
+        print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        assert all(v_ <= TOL[dtype] for v_ in errs.values()), (c, errs)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_content_configs(seed):
+    rng = np.random.default_rng(6000 + seed)
+    for i in range(8):
+        dtype = str(rng.choice(["bf16", "f32"]))
+        L = int(rng.choice([32, 64, 128]))
+        c = dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), T=int(rng.integers(1, 301)),
+                 Dk=int(rng.choice([64, 128])), Dv=int(rng.choice([64, 128])), dtype=dtype, L=L,
+                 R=int(rng.choice([1, 16, 64])), proj=bool(rng.integers(0, 4) > 0), m0=bool(rng.integers(0, 2)))
+        print(f"\n[case] content seed {seed} #{i}: {c}", flush=True)
+        B, H, T, Dk, Dv = c["B"], c["H"], c["T"], c["Dk"], c["Dv"]
+        inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=int(rng.integers(1 << 30)), erase="content",
+                            dists="softplus_decay", with_dO=True, rank=c["R"])
+        inp["U1"] = inp["U1"] * 8.0
+        inp["U2"] = inp["U2"] * 8.0
+        m0 = np.asarray(rng.standard_normal((B, H, Dv)) * 0.5, np.float32).astype(np.float64) if c["m0"] else None
+        dm_out = np.asarray(rng.standard_normal((B, H, Dv)), np.float32).astype(np.float64)
+        d = to_device(inp, dtype)
+        U1, U2 = (d["U1"], d["U2"]) if c["proj"] else (None, None)
+        cont = {"b_x": d["b_x"], "U1": U1, "U2": U2, "m0": f32(m0)}
+        o, S_T, m_out = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], L=L, content=cont)
+        g = carve.bwd_content(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], cont, dm_out=f32(dm_out), L=L)
+        torch.cuda.synchronize()
+        rc = {"b_x": inp["b_x"], "U1": inp["U1"] if c["proj"] else None, "U2": inp["U2"] if c["proj"] else None,
+              "m0": m0}
+        ro, rS, rm = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], L=L, content=rc)
+        ref = oracle.backward_content(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"], rc,
+                                      dm_out=dm_out, L=L)
+        errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS), "m_out": max_rel(to_np(m_out), rm)}
+        for key in ("dq", "dk", "dv", "dlog_g", "db_x", "dw", "dU1", "dU2", "dm0"):
+            if ref.get(key) is None or g.get(key) is None:
+                continue
+            errs[key] = max_rel(to_np(g[key]), ref[key])
+        print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        assert all(v_ <= TOL[dtype] for v_ in errs.values()), (c, errs)
