@@ -1,4 +1,5 @@
-"""Shared test helpers: move seeded synthetic inputs to the device and compare."""
+"""Shared test helpers: move seeded synthetic inputs to the device, compare, and draw hard
+gate runs (strong decay, hard erase) for the range tests."""
 import numpy as np
 import torch
 
@@ -42,3 +43,20 @@ def per_head_rel(gpu, ref):
     den = np.max(np.abs(ref), axis=ax) if ax else np.abs(ref)
     num = np.max(np.abs(gpu - ref), axis=ax) if ax else np.abs(gpu - ref)
     return num / np.where(den > 0, den, 1.0)
+
+
+def hard_runs(rng, B, H, T, D, frac, lo, hi, run=(4, 24)):
+    """Mask of runs of tokens (lengths in `run`) on a random fraction of key channels,
+    and log-uniform values in [lo, hi] for them."""
+    mask = np.zeros((B, H, T, D), bool)
+    for b in range(B):
+        for h in range(H):
+            chans = rng.choice(D, int(frac * D), replace=False)
+            for c in chans:
+                t = int(rng.integers(0, max(T // 8, 1)))
+                while t < T:
+                    n = int(rng.integers(run[0], run[1] + 1))
+                    mask[b, h, t:t + n, c] = True
+                    t += n + int(rng.integers(8, 64))
+    vals = np.exp(rng.uniform(np.log(lo), np.log(hi), (B, H, T, D)))
+    return mask, vals

@@ -12,7 +12,7 @@ import torch
 import oracle
 from chunk_gated_delta_amd import carve
 from chunk_gated_delta_amd.synth import random_inputs
-from tests.helpers import max_rel, to_device, to_np
+from tests.helpers import hard_runs, max_rel, to_device, to_np
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -102,4 +102,49 @@ def test_random_content_configs(seed):
                 continue
             errs[key] = max_rel(to_np(g[key]), ref[key])
         print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        assert all(v_ <= TOL[dtype] for v_ in errs.values()), (c, errs)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_random_hard_range_configs(seed):
+    """Random shapes over the whole retention range: runs of hard erase (b down to 1e-6) and
+    bursts of strong decay (log g down to -40 per token) on a random share of key channels,
+    so tiles take the range-safe path and blocks beyond -64 the exact fix-up.  The erase
+    gradient is compared where b >= 0.25 (it is ill-conditioned below), d/dlog g everywhere."""
+    rng = np.random.default_rng(7000 + seed)
+    for i in range(8):
+        c = dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 3)), T=int(rng.integers(20, 301)),
+                 Dk=int(rng.choice([64, 128])), Dv=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])),
+                 L=int(rng.choice([32, 64])), frac=float(rng.uniform(0.05, 0.5)),
+                 pair=str(rng.choice(["recompute", "saved"])))
+        print(f"\n[case] hard seed {seed} #{i}: {c}", flush=True)
+        B, H, T, Dk, Dv, dtype = c["B"], c["H"], c["T"], c["Dk"], c["Dv"], c["dtype"]
+        inp = random_inputs(B, H, T, Dk, Dv, dtype=dtype, seed=int(rng.integers(1 << 30)), erase="sigmoid",
+                            dists="softplus_decay", with_dO=True)
+        m1, burst = hard_runs(rng, B, H, T, Dk, c["frac"], 2.0, 40.0)
+        m2, tiny = hard_runs(rng, B, H, T, Dk, c["frac"], 1e-6, 1e-2)
+        inp["log_g"] = np.asarray(np.where(m1, -burst, inp["log_g"]), np.float32).astype(np.float64)
+        inp["b"] = np.asarray(np.where(m2, tiny, inp["b"]), np.float32).astype(np.float64)
+        S0 = np.asarray(rng.standard_normal((B, H, Dv, Dk)) * 0.3, np.float32).astype(np.float64)
+        dS_T = np.asarray(rng.standard_normal((B, H, Dv, Dk)) * 0.3, np.float32).astype(np.float64)
+        d = to_device(inp, dtype)
+        if c["pair"] == "saved":
+            o, S_T, saved = carve.fwd_save(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=f32(S0), L=c["L"])
+            g = carve.bwd_saved(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], saved, b=d["b"],
+                                dS_T=f32(dS_T), L=c["L"])
+        else:
+            o, S_T, _ = carve.fwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], b=d["b"], S0=f32(S0), L=c["L"])
+            g = carve.bwd(d["q"], d["k"], d["v"], d["log_g"], d["w"], d["dO"], b=d["b"], S0=f32(S0),
+                          dS_T=f32(dS_T), L=c["L"])
+        torch.cuda.synchronize()
+        ro, rS, _ = oracle.forward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], b=inp["b"], S0=S0)
+        ref = oracle.backward(inp["q"], inp["k"], inp["v"], inp["log_g"], inp["w"], inp["dO"], b=inp["b"], S0=S0,
+                              dS_T=dS_T)
+        errs = {"o": max_rel(to_np(o), ro), "S_T": max_rel(to_np(S_T), rS)}
+        errs.update({key: max_rel(to_np(g[key]), ref[key]) for key in ("dq", "dk", "dv", "dlog_g", "dw", "dS0")})
+        sel = inp["b"] >= 0.25
+        errs["db(b>=0.25)"] = max_rel(to_np(g["db"])[sel], ref["db"][sel])
+        print("  " + " ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()), flush=True)
+        for key in ("dq", "dk", "dv", "dlog_g", "db", "dw"):
+            assert torch.isfinite(g[key]).all().item(), key
         assert all(v_ <= TOL[dtype] for v_ in errs.values()), (c, errs)

@@ -23,7 +23,7 @@ import torch
 import oracle
 from chunk_gated_delta_amd import carve
 from chunk_gated_delta_amd.synth import random_inputs
-from tests.helpers import max_rel, to_device, to_np
+from tests.helpers import hard_runs, max_rel, to_device, to_np
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-4, "bf16": 2e-2}
@@ -39,23 +39,6 @@ def f32np(x):
 
 def dev(x):
     return None if x is None else torch.from_numpy(np.asarray(x, np.float32)).cuda()
-
-
-def hard_runs(rng, B, H, T, D, frac, lo, hi, run=(4, 24)):
-    """Mask of runs of tokens (lengths in `run`) on a random fraction of key channels,
-    and log-uniform values in [lo, hi] for them."""
-    mask = np.zeros((B, H, T, D), bool)
-    for b in range(B):
-        for h in range(H):
-            chans = rng.choice(D, int(frac * D), replace=False)
-            for c in chans:
-                t = int(rng.integers(0, max(T // 8, 1)))
-                while t < T:
-                    n = int(rng.integers(run[0], run[1] + 1))
-                    mask[b, h, t:t + n, c] = True
-                    t += n + int(rng.integers(8, 64))
-    vals = np.exp(rng.uniform(np.log(lo), np.log(hi), (B, H, T, D)))
-    return mask, vals
 
 
 def hard_case(B, H, T, D, dtype, seed, erase=True):
