@@ -412,6 +412,19 @@ def main():
         roofline["traffic_unit"] = "HBM bytes per launch (read + written)"
         roofline["traffic_over_algorithmic"] = round(traffic / (stage_bytes[dom] * units), 3)
 
+    # every stage against the same roofline: its algorithmic bytes, and (while the counter
+    # summary matches the kernel sources) its measured HBM traffic, per launch time
+    stage_rl = {}
+    for st_name, st_ms in stage_mean.items():
+        rec = {"launch_ms": round(st_ms, 4), "bytes_per_token_head": stage_bytes.get(st_name),
+               "algorithmic_GBs": round(stage_bytes.get(st_name, 0) * units / (st_ms * 1e-3) / 1e9, 1)}
+        tr = measured_traffic(st_name) if with_bwd else None
+        if tr is not None:
+            rec["traffic_GBs"] = round(tr / (st_ms * 1e-3) / 1e9, 1)
+            rec["traffic_frac_of_measured_copy"] = round(tr / (st_ms * 1e-3) / 1e9 / measured_peak, 3)
+        stage_rl[st_name] = rec
+    extra["stage_roofline"] = stage_rl
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, wl, args.cpu_sample_heads, with_bwd)
